@@ -1,0 +1,149 @@
+"""TEST INFRASTRUCTURE ONLY: the fp64 CPU oracle for the complex diagonal scan.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library and its Python
+binding never import it, and the two share no code: the only module both sides
+use is the seeded input generator ``cssd_workloads``, which holds none of the
+method's arithmetic.
+
+The arithmetic lives in ``cssd_oracle.c`` (plain C, fp64, serial in time,
+OpenMP over independent (batch, head) sequences).  This file only compiles it
+with gcc, loads it with ctypes, and converts numpy arrays to the planar fp64
+layout the C code reads.  What is computed, and from which passages, is written
+at the top of ``cssd_oracle.c``:
+
+    a_t = exp(softplus(dt_t) * A)            (Mamba-3-Lite docs, "Complex-Valued
+                                              State Spaces", Discretization)
+    h_t = a_t h_{t-1} + B_t (x) x_t          (Mamba-3-Lite docs, "SSD Theory",
+    y_t = sum_n C_t[n] h_t[n,:] + D x_t       section 2; skip term from the
+                                              burn-mamba step_constant module)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "cssd_oracle.c")
+_LIB = os.path.join(_HERE, "libcssd_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_d = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math).  Returns the path."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Wextra", "-o", out + ".tmp", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load(path: str | None = None, rebuild: bool = False):
+    """Load (building first if needed) the oracle shared library."""
+    global _lib
+    with _lock:
+        if path is not None:
+            return _bind(ctypes.CDLL(path))
+        if _lib is None or rebuild:
+            if rebuild or not os.path.exists(_LIB) or (
+                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB))
+        return _lib
+
+
+def _bind(lib):
+    lib.oracle_forward_f64.restype = ctypes.c_int
+    lib.oracle_forward_f64.argtypes = [_i64] * 5 + [_d] * 10 + [_d] * 2 + [_d] * 4 + [ctypes.c_int]
+    lib.oracle_step_f64.restype = ctypes.c_int
+    lib.oracle_step_f64.argtypes = [_i64] * 4 + [_d] * 10 + [_d] * 4 + [ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    return lib
+
+
+def _planes(z, shape=None):
+    z = np.asarray(z)
+    if shape is not None and z.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {z.shape}")
+    re = np.ascontiguousarray(z.real, dtype=np.float64)
+    im = np.ascontiguousarray(z.imag if np.iscomplexobj(z) else np.zeros(z.shape), dtype=np.float64)
+    return re, im
+
+
+def _real(a, shape):
+    a = np.ascontiguousarray(np.asarray(a), dtype=np.float64)
+    if a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _p(a):
+    return a.ctypes.data_as(_d) if a is not None else None
+
+
+def forward(x, Bm, Cm, dt, A, Dskip=None, h0=None, nthreads: int = 0, lib=None):
+    """Sequential fp64 recurrence over the whole sequence.
+
+    x: (B,T,H,D) complex; Bm, Cm: (B,T,H,N) complex; dt: (B,T,H) real;
+    A: (H,) complex; Dskip: (H,) real or None; h0: (B,H,N,D) complex or None.
+    Returns (y (B,T,H,D) complex128, hT (B,H,N,D) complex128).
+    """
+    lib = lib or load()
+    x = np.asarray(x)
+    Bsz, T, H, D = x.shape
+    N = np.asarray(Bm).shape[-1]
+    xr, xi = _planes(x)
+    br, bi = _planes(Bm, (Bsz, T, H, N))
+    cr, ci = _planes(Cm, (Bsz, T, H, N))
+    dtv = _real(dt, (Bsz, T, H))
+    ar, ai = _planes(np.asarray(A, dtype=np.complex128), (H,))
+    ds = _real(Dskip, (H,)) if Dskip is not None else None
+    if h0 is not None:
+        h0r, h0i = _planes(h0, (Bsz, H, N, D))
+    else:
+        h0r = h0i = None
+    yr = np.empty((Bsz, T, H, D)); yi = np.empty_like(yr)
+    hr = np.empty((Bsz, H, N, D)); hi = np.empty_like(hr)
+    rc = lib.oracle_forward_f64(Bsz, T, H, D, N, _p(xr), _p(xi), _p(br), _p(bi), _p(cr), _p(ci),
+                                _p(dtv), _p(ar), _p(ai), _p(ds), _p(h0r), _p(h0i),
+                                _p(yr), _p(yi), _p(hr), _p(hi), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_forward_f64 failed")
+    return yr + 1j * yi, hr + 1j * hi
+
+
+def step(x, Bm, Cm, dt, A, Dskip, h, nthreads: int = 0, lib=None):
+    """One decode step for all (batch, head).  h (B,H,N,D) complex is NOT modified;
+    returns (y (B,H,D) complex128, h_new (B,H,N,D) complex128)."""
+    lib = lib or load()
+    x = np.asarray(x)
+    Bsz, H, D = x.shape
+    N = np.asarray(Bm).shape[-1]
+    xr, xi = _planes(x)
+    br, bi = _planes(Bm, (Bsz, H, N))
+    cr, ci = _planes(Cm, (Bsz, H, N))
+    dtv = _real(dt, (Bsz, H))
+    ar, ai = _planes(np.asarray(A, dtype=np.complex128), (H,))
+    ds = _real(Dskip, (H,)) if Dskip is not None else None
+    hr, hi = _planes(h, (Bsz, H, N, D))
+    hr = hr.copy(); hi = hi.copy()
+    yr = np.empty((Bsz, H, D)); yi = np.empty_like(yr)
+    rc = lib.oracle_step_f64(Bsz, H, D, N, _p(xr), _p(xi), _p(br), _p(bi), _p(cr), _p(ci),
+                             _p(dtv), _p(ar), _p(ai), _p(ds), _p(hr), _p(hi), _p(yr), _p(yi),
+                             int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_step_f64 failed")
+    return yr + 1j * yi, hr + 1j * hi
+
+
+def max_threads(lib=None) -> int:
+    return (lib or load()).oracle_max_threads()

@@ -1,0 +1,207 @@
+/*
+ * TEST INFRASTRUCTURE ONLY.  This is the fp64 CPU reference ("oracle") for the
+ * complex-valued diagonal selective state-space scan.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it; the
+ * product library never links, includes or calls anything in this directory,
+ * and shares no source with it.
+ *
+ * What it computes is the literal sequential recurrence, one time step after
+ * another, with no chunking, no blocking and no reordering:
+ *
+ *   s_t   = softplus(dt_t)                      real step, softplus on the real dt
+ *   a_t   = exp(s_t * A)                        A is one complex scalar per head
+ *         = exp(s_t Re A) (cos(s_t Im A) + i sin(s_t Im A))
+ *   h_t   = a_t h_{t-1} + B_t (x) x_t           h_t is N x D complex, B_t in C^N, x_t in C^D
+ *   y_t   = sum_n C_t[n] h_t[n,:] + Dskip x_t   C_t is NOT conjugated
+ *
+ * Sources (the pages this follows):
+ *  - Mamba-3-Lite docs, "SSD Theory -- Complex States & the Chunkwise Algorithm",
+ *    section 2 "Why it exists: the sequential scan is the bottleneck": the naive
+ *    loop that multiplies the whole state by the per-head factor, adds the
+ *    outer product of B_t and x_t, and reads out by summing C_t times the state
+ *    over the state index.
+ *  - Mamba-3-Lite docs, "Complex-Valued State Spaces", subsections "The
+ *    recurrence", "Discretization" (softplus is applied to the real dt and the
+ *    result then multiplies the complex A; the order is deliberate) and the
+ *    walkthrough of the discretise helper and the naive scan (state layout
+ *    (B,H,N,D), zero initial state).
+ *  - burn-mamba docs, module "step_constant": the readout adds a skip term
+ *    D x to C^T h.
+ *
+ * Readings where the pages leave a step open (each is listed in the design
+ * notes): y is returned as a complex value (both planes); softplus is the exact
+ * log(1+e^dt), evaluated in the overflow-free form max(dt,0)+log1p(e^-|dt|);
+ * a NULL Dskip means D = 0; a NULL initial state means h_{-1} = 0.
+ *
+ * Parallelism: OpenMP over the independent (batch, head) sequences only; the
+ * loop over time inside one sequence is the plain serial recurrence.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double softplus(double v)
+{
+    /* log(1 + e^v), written so that neither branch overflows */
+    return fmax(v, 0.0) + log1p(exp(-fabs(v)));
+}
+
+/* a = exp(softplus(dt) * A), A = (are, aim): scale e^{s Re A}, rotation s Im A */
+static void discretise(double dt, double are, double aim, double *ar, double *ai)
+{
+    double s = softplus(dt);
+    double mag = exp(s * are);
+    *ar = mag * cos(s * aim);
+    *ai = mag * sin(s * aim);
+}
+
+/*
+ * One time step for one (batch, head) state of N x D complex values:
+ *   h <- a h + B (x) x ;  y = sum_n C[n] h[n,:] + d x
+ */
+static void one_step(int64_t D, int64_t N, double ar, double ai,
+                     const double *xr, const double *xi,
+                     const double *br, const double *bi,
+                     const double *cr, const double *ci, double d,
+                     double *hr, double *hi, double *yr, double *yi)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t p = 0; p < D; ++p) {
+            double orr = hr[n * D + p], oii = hi[n * D + p];
+            /* a * h_old */
+            double nr = ar * orr - ai * oii;
+            double ni = ar * oii + ai * orr;
+            /* + B[n] * x[p] */
+            nr += br[n] * xr[p] - bi[n] * xi[p];
+            ni += br[n] * xi[p] + bi[n] * xr[p];
+            hr[n * D + p] = nr;
+            hi[n * D + p] = ni;
+        }
+    }
+    for (int64_t p = 0; p < D; ++p) {
+        double sr = 0.0, si = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double vr = hr[n * D + p], vi = hi[n * D + p];
+            sr += cr[n] * vr - ci[n] * vi;
+            si += cr[n] * vi + ci[n] * vr;
+        }
+        yr[p] = sr + d * xr[p];
+        yi[p] = si + d * xi[p];
+    }
+}
+
+/*
+ * Full forward over T steps.  Layouts (row-major, planar re/im):
+ *   x  [B,T,H,D]   Bm, Cm [B,T,H,N]   dt [B,T,H]   A [H]   Dskip [H] or NULL
+ *   h0 [B,H,N,D] or NULL (zero)       y [B,T,H,D]  hT [B,H,N,D] or NULL
+ * nthreads <= 0 uses the OpenMP default.  Returns 0, or -1 on a bad argument
+ * or allocation failure.
+ */
+int oracle_forward_f64(int64_t Bsz, int64_t T, int64_t H, int64_t D, int64_t N,
+                       const double *x_re, const double *x_im,
+                       const double *b_re, const double *b_im,
+                       const double *c_re, const double *c_im,
+                       const double *dt, const double *a_re, const double *a_im,
+                       const double *dskip,
+                       const double *h0_re, const double *h0_im,
+                       double *y_re, double *y_im,
+                       double *hT_re, double *hT_im, int nthreads)
+{
+    if (Bsz <= 0 || T < 0 || H <= 0 || D <= 0 || N <= 0)
+        return -1;
+    if (!x_re || !x_im || !b_re || !b_im || !c_re || !c_im || !dt || !a_re ||
+        !a_im || !y_re || !y_im)
+        return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t bh = 0; bh < Bsz * H; ++bh) {
+        int64_t b = bh / H, h = bh % H;
+        double *hr = (double *)calloc((size_t)(N * D), sizeof(double));
+        double *hi = (double *)calloc((size_t)(N * D), sizeof(double));
+        if (!hr || !hi) {
+            free(hr);
+            free(hi);
+            failed |= 1;
+            continue;
+        }
+        if (h0_re && h0_im) {
+            memcpy(hr, h0_re + bh * N * D, sizeof(double) * (size_t)(N * D));
+            memcpy(hi, h0_im + bh * N * D, sizeof(double) * (size_t)(N * D));
+        }
+        double d = dskip ? dskip[h] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t row = (b * T + t) * H + h; /* (b, t, h) */
+            double ar, ai;
+            discretise(dt[row], a_re[h], a_im[h], &ar, &ai);
+            one_step(D, N, ar, ai, x_re + row * D, x_im + row * D,
+                     b_re + row * N, b_im + row * N, c_re + row * N,
+                     c_im + row * N, d, hr, hi, y_re + row * D, y_im + row * D);
+        }
+        if (hT_re && hT_im) {
+            memcpy(hT_re + bh * N * D, hr, sizeof(double) * (size_t)(N * D));
+            memcpy(hT_im + bh * N * D, hi, sizeof(double) * (size_t)(N * D));
+        }
+        free(hr);
+        free(hi);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * One decode step for every (batch, head): the same loop body as above applied
+ * once to a persistent state, updated in place.
+ *   x [B,H,D]  Bm, Cm [B,H,N]  dt [B,H]  A [H]  Dskip [H] or NULL
+ *   h [B,H,N,D] in/out          y [B,H,D]
+ */
+int oracle_step_f64(int64_t Bsz, int64_t H, int64_t D, int64_t N,
+                    const double *x_re, const double *x_im,
+                    const double *b_re, const double *b_im,
+                    const double *c_re, const double *c_im,
+                    const double *dt, const double *a_re, const double *a_im,
+                    const double *dskip, double *h_re, double *h_im,
+                    double *y_re, double *y_im, int nthreads)
+{
+    if (Bsz <= 0 || H <= 0 || D <= 0 || N <= 0)
+        return -1;
+    if (!x_re || !x_im || !b_re || !b_im || !c_re || !c_im || !dt || !a_re ||
+        !a_im || !h_re || !h_im || !y_re || !y_im)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < Bsz * H; ++bh) {
+        int64_t h = bh % H;
+        double ar, ai;
+        discretise(dt[bh], a_re[h], a_im[h], &ar, &ai);
+        one_step(D, N, ar, ai, x_re + bh * D, x_im + bh * D, b_re + bh * N,
+                 b_im + bh * N, c_re + bh * N, c_im + bh * N,
+                 dskip ? dskip[h] : 0.0, h_re + bh * N * D, h_im + bh * N * D,
+                 y_re + bh * D, y_im + bh * D);
+    }
+    return 0;
+}
+
+/* Threads OpenMP would use for a parallel region (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,366 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+None of these re-type the oracle's loop.  Each computes the expected value by a
+different route -- an unrolled double sum with explicit products, a geometric
+series, an exponential of a summed log-decay, the PAM page's quadratic dual
+form, or a number the pages print -- so that a plausible slip in the oracle
+(dropped term, wrong sign, conjugated operand, off-by-one in the decay, wrong
+index) makes at least one of them fail.  ``test_oracle_mutants.py`` plants such
+slips in copies of the oracle source and checks exactly that.
+
+The discretisation a = exp(softplus(dt) A) is evaluated here with library
+routines only: ``numpy.logaddexp(0, dt)`` for softplus and complex ``numpy.exp``.
+
+Every pin takes the loaded oracle library (``lib``) and raises AssertionError
+on failure.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def disc(dt, A):
+    """exp(softplus(dt) * A) via library routines (broadcasting)."""
+    return np.exp(np.logaddexp(0.0, np.asarray(dt, dtype=np.float64)) * A)
+
+
+def crandn(rng, *shape, scale=math.sqrt(0.5)):
+    return scale * (rng.standard_normal(shape) + 1j * rng.standard_normal(shape))
+
+
+def rel_err(got, ref):
+    got = np.asarray(got); ref = np.asarray(ref)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+# ---------------------------------------------------------------------------
+# p1: brute-force unrolled double sum (T <= 8)
+# ---------------------------------------------------------------------------
+def bruteforce(x, Bm, Cm, dt, A, Dskip=None, h0=None):
+    """Unrolled form of the recurrence (Mamba-3-Lite docs, "The Chunkwise Complex
+    SSD Algorithm", section 3: with zero initial state the output is a sum over
+    all earlier inputs, each weighted by the product of the decays after it and
+    by the score C_t . B_s; the empty product is 1).  The initial-state term
+    carries the product of all decays up to t.  Products are formed by explicit
+    multiplication of the per-step factors, one pair (t, s) at a time."""
+    Bsz, T, H, D = x.shape
+    N = Bm.shape[-1]
+    y = np.zeros((Bsz, T, H, D), dtype=np.complex128)
+    hT = np.zeros((Bsz, H, N, D), dtype=np.complex128)
+    for b in range(Bsz):
+        for h in range(H):
+            a = [complex(disc(dt[b, u, h], A[h])) for u in range(T)]
+
+            def prod(lo, hi):
+                p = 1.0 + 0.0j
+                for u in range(lo, hi + 1):
+                    p *= a[u]
+                return p
+
+            for t in range(T):
+                acc = np.zeros(D, dtype=np.complex128)
+                for s in range(t + 1):
+                    score = np.sum(Cm[b, t, h, :] * Bm[b, s, h, :])
+                    acc += prod(s + 1, t) * score * x[b, s, h, :]
+                if h0 is not None:
+                    acc += prod(0, t) * (Cm[b, t, h, :] @ h0[b, h])
+                if Dskip is not None:
+                    acc += Dskip[h] * x[b, t, h, :]
+                y[b, t, h] = acc
+            st = np.zeros((N, D), dtype=np.complex128)
+            for s in range(T):
+                st += prod(s + 1, T - 1) * np.outer(Bm[b, s, h], x[b, s, h])
+            if h0 is not None:
+                st += prod(0, T - 1) * h0[b, h]
+            hT[b, h] = st
+    return y, hT
+
+
+def _rand_problem(rng, Bsz, T, H, D, N, with_h0=True, with_d=True):
+    x = crandn(rng, Bsz, T, H, D)
+    Bm = crandn(rng, Bsz, T, H, N)
+    Cm = crandn(rng, Bsz, T, H, N)
+    dt = rng.standard_normal((Bsz, T, H))
+    A = -rng.uniform(0.1, 1.0, H) + 1j * rng.uniform(-math.pi, math.pi, H)
+    Dk = rng.standard_normal(H) if with_d else None
+    h0 = crandn(rng, Bsz, H, N, D) if with_h0 else None
+    return x, Bm, Cm, dt, A, Dk, h0
+
+
+def pin_bruteforce(lib):
+    rng = np.random.default_rng(101)
+    for (Bsz, T, H, D, N) in [(1, 1, 1, 1, 1), (2, 3, 2, 3, 2), (1, 5, 3, 2, 4), (2, 8, 2, 3, 5)]:
+        for with_h0 in (False, True):
+            prob = _rand_problem(rng, Bsz, T, H, D, N, with_h0=with_h0)
+            y, hT = oracle.forward(*prob, lib=lib)
+            yb, hb = bruteforce(*prob)
+            assert rel_err(y, yb) < 1e-12, ("y", Bsz, T, H, D, N, with_h0, rel_err(y, yb))
+            assert rel_err(hT, hb) < 1e-12, ("hT", Bsz, T, H, D, N, with_h0, rel_err(hT, hb))
+
+
+# ---------------------------------------------------------------------------
+# p2: impulse enumeration of the segment matrix
+# ---------------------------------------------------------------------------
+def pin_impulse(lib):
+    """x one-hot at (s, p), B_t = C_t = e_n for all t, no skip, zero state:
+    y_t[q] = exp(sum_{u=s+1}^{t} softplus(dt_u) A) if t >= s and q = p, else 0
+    (Mamba-3-Lite docs, "SSD Theory" 4.3: the causal segment matrix with an
+    inclusive diagonal of exactly 1).  Every (s, p) runs as one batch row."""
+    rng = np.random.default_rng(202)
+    T, D, N, n_hot = 7, 3, 2, 1
+    A = np.array([-0.4 + 1.3j])
+    dt_row = rng.standard_normal(T)
+    Bsz = T * D
+    x = np.zeros((Bsz, T, 1, D), dtype=np.complex128)
+    for s in range(T):
+        for p in range(D):
+            x[s * D + p, s, 0, p] = 1.0
+    Bm = np.zeros((Bsz, T, 1, N), dtype=np.complex128); Bm[..., n_hot] = 1.0
+    Cm = Bm.copy()
+    dt = np.broadcast_to(dt_row[None, :, None], (Bsz, T, 1)).copy()
+    y, _ = oracle.forward(x, Bm, Cm, dt, A, None, None, lib=lib)
+    logdec = np.logaddexp(0.0, dt_row) * A[0]
+    for s in range(T):
+        for p in range(D):
+            got = y[s * D + p, :, 0, :]
+            want = np.zeros((T, D), dtype=np.complex128)
+            for t in range(s, T):
+                want[t, p] = np.exp(np.sum(logdec[s + 1:t + 1]))
+            assert np.max(np.abs(got - want)) < 1e-13, (s, p)
+
+
+# ---------------------------------------------------------------------------
+# p4/p5: constant input -- geometric series and its fixed point
+# ---------------------------------------------------------------------------
+def constant_closed_form(n, a, Bv, xv, Cv, d, h0):
+    """State and output after n identical steps (burn-mamba step_constant: the
+    n-step geometric series, here with no rotation operator, beta = 0, gamma = 1):
+    h_n = a^n h0 + (1 - a^n)/(1 - a) B (x) x ;  y_n = C . h_n + d x."""
+    an = np.exp(n * np.log(a))
+    hn = an * h0 + (1.0 - an) / (1.0 - a) * np.outer(Bv, xv)
+    return Cv @ hn + d * xv, hn
+
+
+def _const_problem(rng, T, D, N, dt0, A0):
+    Bv, Cv, xv = crandn(rng, N), crandn(rng, N), crandn(rng, D)
+    h0 = crandn(rng, 1, 1, N, D)
+    x = np.broadcast_to(xv, (1, T, 1, D)).copy()
+    Bm = np.broadcast_to(Bv, (1, T, 1, N)).copy()
+    Cm = np.broadcast_to(Cv, (1, T, 1, N)).copy()
+    dt = np.full((1, T, 1), dt0)
+    return x, Bm, Cm, dt, np.array([A0]), np.array([0.7]), h0, Bv, Cv, xv
+
+
+def pin_constant_input(lib):
+    rng = np.random.default_rng(303)
+    T, D, N = 600, 3, 2
+    x, Bm, Cm, dt, A, Dk, h0, Bv, Cv, xv = _const_problem(rng, T, D, N, 0.3, -0.05 + 2.1j)
+    y, hT = oracle.forward(x, Bm, Cm, dt, A, Dk, h0, lib=lib)
+    a = complex(disc(0.3, A[0]))
+    for n in (1, 2, 3, 17, 256, T):
+        yn, hn = constant_closed_form(n, a, Bv, xv, Cv, Dk[0], h0[0, 0])
+        assert rel_err(y[0, n - 1, 0], yn) < 1e-10, ("y", n, rel_err(y[0, n - 1, 0], yn))
+    _, hn = constant_closed_form(T, a, Bv, xv, Cv, Dk[0], h0[0, 0])
+    assert rel_err(hT[0, 0], hn) < 1e-10
+
+
+def pin_fixed_point(lib):
+    """n -> infinity: y_inf = (C . B) x / (1 - a) + d x, independent of h0."""
+    rng = np.random.default_rng(404)
+    T, D, N = 4096, 2, 3
+    x, Bm, Cm, dt, A, Dk, h0, Bv, Cv, xv = _const_problem(rng, T, D, N, -0.2, -0.06 - 0.8j)
+    y, _ = oracle.forward(x, Bm, Cm, dt, A, Dk, h0, lib=lib)
+    a = complex(disc(-0.2, A[0]))
+    assert abs(a) ** T < 1e-20
+    yinf = (Cv @ Bv) * xv / (1.0 - a) + Dk[0] * xv
+    assert rel_err(y[0, -1, 0], yinf) < 1e-10
+
+
+def pin_step_constant_input(lib):
+    """The single-step entry point, iterated, against the same geometric series."""
+    rng = np.random.default_rng(505)
+    Bsz, H, D, N, n = 2, 2, 3, 2, 150
+    Bv, Cv, xv = crandn(rng, Bsz, H, N), crandn(rng, Bsz, H, N), crandn(rng, Bsz, H, D)
+    dt = rng.standard_normal((Bsz, H))
+    A = np.array([-0.3 + 0.9j, -0.05 - 2.0j])
+    Dk = np.array([0.4, -1.1])
+    h = crandn(rng, Bsz, H, N, D)
+    h_init = h.copy()
+    for _ in range(n):
+        y, h = oracle.step(xv, Bv, Cv, dt, A, Dk, h, lib=lib)
+    for b in range(Bsz):
+        for k in range(H):
+            a = complex(disc(dt[b, k], A[k]))
+            yn, hn = constant_closed_form(n, a, Bv[b, k], xv[b, k], Cv[b, k], Dk[k], h_init[b, k])
+            assert rel_err(y[b, k], yn) < 1e-10, (b, k)
+            assert rel_err(h[b, k], hn) < 1e-10, (b, k)
+
+
+# ---------------------------------------------------------------------------
+# p6: decay zero -- the scan reduces to per-step outer products
+# ---------------------------------------------------------------------------
+def pin_decay_zero(lib):
+    rng = np.random.default_rng(606)
+    Bsz, T, H, D, N = 2, 9, 2, 3, 4
+    x, Bm, Cm, _, _, Dk, h0 = _rand_problem(rng, Bsz, T, H, D, N)
+    A = np.array([-1e4 + 0.5j, -1e4 - 2.0j])
+    dt = np.zeros((Bsz, T, H))
+    assert np.all(disc(0.0, A) == 0)
+    y, hT = oracle.forward(x, Bm, Cm, dt, A, Dk, h0, lib=lib)
+    score = np.einsum("bthn,bthn->bth", Cm, Bm)
+    want = score[..., None] * x + Dk[None, None, :, None] * x
+    assert rel_err(y, want) < 1e-13
+    want_h = np.einsum("bhn,bhd->bhnd", Bm[:, -1], x[:, -1])
+    assert rel_err(hT, want_h) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# p7: homogeneous recurrence -- exact transport of phase (Lemma 6.2)
+# ---------------------------------------------------------------------------
+def pin_homogeneous(lib):
+    """x = 0, h0 != 0: h_T = (prod a_u) h0, so |h_T| = |h0| prod |a_u| and
+    arg h_T = arg h0 + sum_u s_u Im A (mod 2 pi) ("Complex Phase-State Dynamics
+    Reduce the Optimization Steps of Sequence Models", Lemma 6.2 / eq. 7,
+    specialised to one coordinate); y_t = (prod_{u<=t} a_u) C_t . h0."""
+    rng = np.random.default_rng(707)
+    T, D, N = 4096, 2, 2
+    A = np.array([-0.002 + 2.7j])
+    dt = rng.standard_normal((1, T, 1)) * 0.5 - 1.0
+    h0 = crandn(rng, 1, 1, N, D)
+    Cm = crandn(rng, 1, T, 1, N)
+    x = np.zeros((1, T, 1, D), dtype=np.complex128)
+    Bm = crandn(rng, 1, T, 1, N)
+    y, hT = oracle.forward(x, Bm, Cm, dt, A, None, h0, lib=lib)
+    s = np.logaddexp(0.0, dt[0, :, 0])
+    log_mag = math.fsum(s * A[0].real)
+    phase = math.fsum(s * A[0].imag)
+    got = hT[0, 0] / h0[0, 0]
+    assert np.max(np.abs(np.log(np.abs(got)) - log_mag)) < 1e-9
+    dphi = np.angle(got * np.exp(-1j * phase))
+    assert np.max(np.abs(dphi)) < 1e-8
+    cum = np.cumsum(s * A[0])
+    for t in (0, 1, 100, T - 1):
+        want = np.exp(cum[t]) * (Cm[0, t, 0] @ h0[0, 0])
+        assert rel_err(y[0, t, 0], want) < 1e-8, t
+
+
+# ---------------------------------------------------------------------------
+# p9: linearity and the skip term
+# ---------------------------------------------------------------------------
+def pin_linearity_and_skip(lib):
+    rng = np.random.default_rng(909)
+    Bsz, T, H, D, N = 2, 12, 3, 4, 3
+    x1, Bm, Cm, dt, A, Dk, _ = _rand_problem(rng, Bsz, T, H, D, N, with_h0=False)
+    x2 = crandn(rng, Bsz, T, H, D)
+    al, be = 0.3 - 1.2j, -0.7 + 0.4j
+    y1, _ = oracle.forward(x1, Bm, Cm, dt, A, Dk, None, lib=lib)
+    y2, _ = oracle.forward(x2, Bm, Cm, dt, A, Dk, None, lib=lib)
+    y12, _ = oracle.forward(al * x1 + be * x2, Bm, Cm, dt, A, Dk, None, lib=lib)
+    assert rel_err(y12, al * y1 + be * y2) < 1e-12
+    y0, h0 = oracle.forward(x1, np.zeros_like(Bm), Cm, dt, A, Dk, None, lib=lib)
+    assert np.array_equal(y0, Dk[None, None, :, None] * x1)
+    assert np.all(h0 == 0)
+
+
+# ---------------------------------------------------------------------------
+# p10: PAM -- quadratic dual form and lossless retrieval with orthogonal keys
+# ---------------------------------------------------------------------------
+def pam_dual(K, Q, V, gamma, score):
+    """Phase-Associative Memory eq. 7 evaluated in the page's O(T^2) dual form:
+    decay matrix D[t,i] = gamma^(t-i) for i <= t (0 above the diagonal), score
+    W = Q~ K^*T with Q~ = Q/sqrt(d), output Y = (W * D) V.  score="re" keeps
+    Re(W) (the configuration's Re<K|Q>/sqrt(d) readout)."""
+    Bsz, T, H, d = K.shape
+    Y = np.zeros_like(V)
+    t_idx = np.arange(T)
+    expo = (t_idx[:, None] - t_idx[None, :]).astype(np.float64)
+    for b in range(Bsz):
+        for h in range(H):
+            Dm = np.where(expo >= 0, gamma[h] ** np.maximum(expo, 0), 0.0)
+            W = (Q[b, :, h, :] / math.sqrt(d)) @ np.conj(K[b, :, h, :]).T
+            if score == "re":
+                W = W.real
+            Y[b, :, h, :] = (W * Dm) @ V[b, :, h, :]
+    return Y
+
+
+def pin_pam_dual_form(lib):
+    import cssd_workloads as wl
+    p = wl.pam_draw(77, 2, 40, 2, 8)
+    for score in ("complex", "re"):
+        inp = wl.pam_to_scan(p, chunk=16, score=score)
+        x, Bm, Cm, dt, A, Dk, h0 = inp.complex()
+        y, _ = oracle.forward(x, Bm, Cm, dt, A, Dk, h0, lib=lib)
+        # the scan runs on fp32-rounded inputs; the dual form on the exact draws
+        want = pam_dual(p.K, p.Q, p.V, p.gamma.astype(np.float32).astype(np.float64), score)
+        assert rel_err(y, want) < 2e-6, (score, rel_err(y, want))
+
+
+def pin_pam_orthogonal_keys(lib):
+    """Orthonormal unit-phase keys (DFT rows / sqrt(d)), gamma = 1, queries
+    Q_t = sqrt(d) K_{j(t)} with j(t) <= t: retrieval returns V_{j(t)} exactly
+    (Phase-Associative Memory, the lossless-retrieval statement after eq. 7)."""
+    import cssd_workloads as wl
+    rng = np.random.default_rng(1010)
+    d = T = 8
+    k = np.arange(d)
+    K = np.exp(2j * np.pi * np.outer(np.arange(T), k) / d) / math.sqrt(d)
+    j = np.array([rng.integers(0, t + 1) for t in range(T)])
+    Q = math.sqrt(d) * K[j]
+    V = crandn(rng, T, d)
+    p = wl.PamInputs(K[None, :, None, :], Q[None, :, None, :], V[None, :, None, :], np.array([1.0]))
+    for score in ("complex", "re"):
+        N = d if score == "complex" else 2 * d
+        rs = 1.0 / math.sqrt(d)
+        if score == "complex":
+            Bm, Cm = np.conj(p.K), p.Q * rs
+        else:
+            Bm = np.concatenate([np.conj(p.K), p.K], -1)
+            Cm = np.concatenate([p.Q, np.conj(p.Q)], -1) * (0.5 * rs)
+        assert Bm.shape[-1] == N
+        y, _ = oracle.forward(p.V, Bm, Cm, np.zeros((1, T, 1)), np.array([0.0 + 0.0j]), None, None,
+                              lib=lib)
+        assert np.max(np.abs(y[0, :, 0, :] - V[j])) < 1e-12, score
+
+
+# ---------------------------------------------------------------------------
+# golden values printed on the pages
+# ---------------------------------------------------------------------------
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def pin_golden_modulus_drift(lib):
+    """|h_T| / |h_0| after T homogeneous steps of modulus rho, rounded as printed."""
+    g = _golden("modulus_drift.json")
+
+    def drift(rho, T):
+        # |a| = rho with dt = 0 (softplus(0) = ln 2): Re A = ln(rho) / ln 2
+        A = np.array([math.log(rho) / math.log(2.0) + 0.37j])
+        h0 = np.ones((1, 1, 1, 1), dtype=np.complex128)
+        z = np.zeros((1, T, 1, 1), dtype=np.complex128)
+        _, hT = oracle.forward(z, z, z, np.zeros((1, T, 1)), A, None, h0, lib=lib)
+        return abs(hT[0, 0, 0, 0])
+
+    for case in g["cases"]:
+        got = drift(case["rho"], case["steps"])
+        sig = case["printed_significant_digits"]
+        assert float(f"{got:.{sig}g}") == case["printed"], (case, got)
+    for case in g["bounds"]:
+        got = drift(case["rho"], case["steps"])
+        assert got < case["upper"], (case, got)
+
+
+ALL_PINS = [pin_bruteforce, pin_impulse, pin_constant_input, pin_fixed_point,
+            pin_step_constant_input, pin_decay_zero, pin_homogeneous, pin_linearity_and_skip,
+            pin_pam_dual_form, pin_pam_orthogonal_keys, pin_golden_modulus_drift]

@@ -1,0 +1,80 @@
+"""The pins have teeth: plant plausible slips in copies of the oracle source (on
+the CPU, never in the GPU path), build each copy with gcc, and require that at
+least one pin fails for every one of them.  A slip whose target text is no
+longer in the source fails the test, so the list stays in step with the oracle.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "cssd_oracle.c")
+
+MUTANTS = {
+    "conjugated_C_readout": [
+        ("sr += cr[n] * vr - ci[n] * vi;", "sr += cr[n] * vr + ci[n] * vi;"),
+        ("si += cr[n] * vi + ci[n] * vr;", "si += cr[n] * vi - ci[n] * vr;"),
+    ],
+    "skip_term_dropped": [
+        ("yr[p] = sr + d * xr[p];", "yr[p] = sr;"),
+        ("yi[p] = si + d * xi[p];", "yi[p] = si;"),
+    ],
+    "softplus_dropped": [("double s = softplus(dt);", "double s = dt;")],
+    "conjugated_A": [("*ai = mag * sin(s * aim);", "*ai = -mag * sin(s * aim);")],
+    "rotation_not_scaled_by_step": [("*ar = mag * cos(s * aim);", "*ar = mag * cos(aim);"),
+                                    ("*ai = mag * sin(s * aim);", "*ai = mag * sin(aim);")],
+    "sign_in_complex_decay": [("double ni = ar * oii + ai * orr;", "double ni = ar * oii - ai * orr;")],
+    "imag_x_ignored_in_outer_product": [("nr += br[n] * xr[p] - bi[n] * xi[p];", "nr += br[n] * xr[p];")],
+    "outer_product_conjugates_B": [("ni += br[n] * xi[p] + bi[n] * xr[p];", "ni += br[n] * xi[p] - bi[n] * xr[p];")],
+    "initial_state_ignored": [("if (h0_re && h0_im) {", "if (0) {")],
+    "wrong_row_index": [("int64_t row = (b * T + t) * H + h; /* (b, t, h) */",
+                         "int64_t row = (h * T + t) * Bsz + b;")],
+    "skip_from_head_0": [("double d = dskip ? dskip[h] : 0.0;", "double d = dskip ? dskip[0] : 0.0;")],
+    "decay_applied_after_input": [
+        ("double orr = hr[n * D + p], oii = hi[n * D + p];",
+         "double orr = hr[n * D + p] + (br[n] * xr[p] - bi[n] * xi[p]), "
+         "oii = hi[n * D + p] + (br[n] * xi[p] + bi[n] * xr[p]);"),
+        ("nr += br[n] * xr[p] - bi[n] * xi[p];", "nr += 0.0;"),
+        ("ni += br[n] * xi[p] + bi[n] * xr[p];", "ni += 0.0;"),
+    ],
+    "readout_before_update": [
+        # read out h_{t-1} (decayed nothing, no new input) instead of h_t
+        ("double vr = hr[n * D + p], vi = hi[n * D + p];",
+         "double vr = hr[n * D + p] - (br[n] * xr[p] - bi[n] * xi[p]), "
+         "vi = hi[n * D + p] - (br[n] * xi[p] + bi[n] * xr[p]);"),
+    ],
+}
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mut_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, workdir):
+    text = open(SRC).read()
+    for old, new in MUTANTS[name]:
+        assert old in text, f"mutation target not found in oracle source: {old!r}"
+        text = text.replace(old, new)
+    src = os.path.join(workdir, f"{name}.c")
+    with open(src, "w") as f:
+        f.write(text)
+    so = os.path.join(workdir, f"lib_{name}.so")
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-w", "-o", so, src,
+                    "-lm"], check=True)
+    lib = oracle.load(path=so)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
