@@ -1,0 +1,249 @@
+"""ctypes binding of libcssd.so (include/cssd.h).
+
+Argument marshalling only: shapes, dtypes, devices and contiguity are checked,
+outputs and the workspace are allocated with torch (device memory plumbing),
+raw pointers and the current HIP stream are handed to the C ABI, and a status
+other than CSSD_OK raises CSSDError.  Every step of the computation runs in the
+library's HIP kernels; there is no other code path.  If the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcssd.so")
+
+CSSD_OK, CSSD_ERR_INVALID_ARG, CSSD_ERR_UNSUPPORTED, CSSD_ERR_WORKSPACE, CSSD_ERR_HIP = range(5)
+CSSD_F32, CSSD_BF16 = 0, 1
+KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step")
+
+_lock = threading.Lock()
+_lib = None
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+
+class CSSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load_library(path: Optional[str] = None):
+    """Load libcssd.so and declare its C signatures.  Raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is not built: run `python -m complex_valued_state_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(p)
+        lib.cssd_version.restype = ctypes.c_int
+        lib.cssd_version.argtypes = []
+        lib.cssd_status_string.restype = ctypes.c_char_p
+        lib.cssd_status_string.argtypes = [ctypes.c_int]
+        lib.cssd_forward_workspace_size.restype = ctypes.c_int
+        lib.cssd_forward_workspace_size.argtypes = [_i64] * 6 + [ctypes.POINTER(_sz)]
+        lib.cssd_forward.restype = ctypes.c_int
+        lib.cssd_forward.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 \
+            + [_vp] * 4 + [_vp, _sz, _vp]
+        lib.cssd_step.restype = ctypes.c_int
+        lib.cssd_step.argtypes = [_i64] * 4 + [_vp] * 10 + [_vp] * 4 + [_vp]
+        lib.cssd_profile_enable.restype = ctypes.c_int
+        lib.cssd_profile_enable.argtypes = [ctypes.c_int]
+        lib.cssd_profile_read.restype = ctypes.c_int
+        lib.cssd_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+        lib.cssd_kernel_name.restype = ctypes.c_char_p
+        lib.cssd_kernel_name.argtypes = [ctypes.c_int]
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().cssd_status_string(int(status)).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def cssd_version() -> int:
+    return load_library().cssd_version()
+
+
+def cssd_forward_workspace_size(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                chunk: int) -> int:
+    out = _sz(0)
+    st = load_library().cssd_forward_workspace_size(batch, seqlen, nheads, headdim, dstate, chunk,
+                                                    ctypes.byref(out))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_forward_workspace_size")
+    return int(out.value)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers (torch is plumbing: device memory and streams)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, shape: Sequence[int], dtypes, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must live on the GPU device {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def cssd_forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None, h0=None, *,
+                 chunk: int, return_state: bool = True, out=None, workspace=None, stream=None):
+    """Chunkwise complex scan over a whole sequence (see include/cssd.h).
+
+    x_*: (B,T,H,D); B_*, C_*: (B,T,H,N) -- float32, or all six bfloat16 for the
+    bf16-input variant; dt: (B,T,H) float32; A_*: (H,) float32; Dskip: (H,)
+    float32 or None; h0: (h0_re, h0_im) each (B,H,N,D) float32, or None.
+    out: optional (y_re, y_im[, hT_re, hT_im]) preallocated outputs.
+    Returns (y_re, y_im, hT_re, hT_im) (the last two None if not return_state).
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = x_re.device
+    Bsz, T, H, D = x_re.shape
+    N = B_re.shape[-1]
+    in_dt = x_re.dtype
+    if in_dt == torch.float32:
+        code, okd = CSSD_F32, (torch.float32,)
+    elif in_dt == torch.bfloat16:
+        code, okd = CSSD_BF16, (torch.bfloat16,)
+    else:
+        raise TypeError("x/B/C planes must be float32 or bfloat16")
+    f32 = (torch.float32,)
+    p = {}
+    for name, t, shp, dts in (("x_re", x_re, (Bsz, T, H, D), okd), ("x_im", x_im, (Bsz, T, H, D), okd),
+                              ("B_re", B_re, (Bsz, T, H, N), okd), ("B_im", B_im, (Bsz, T, H, N), okd),
+                              ("C_re", C_re, (Bsz, T, H, N), okd), ("C_im", C_im, (Bsz, T, H, N), okd),
+                              ("dt", dt, (Bsz, T, H), f32), ("A_re", A_re, (H,), f32),
+                              ("A_im", A_im, (H,), f32)):
+        p[name] = _check(t, name, shp, dts, dev)
+    p["Dskip"] = None if Dskip is None else _check(Dskip, "Dskip", (H,), f32, dev)
+    if h0 is not None:
+        p["h0_re"] = _check(h0[0], "h0_re", (Bsz, H, N, D), f32, dev)
+        p["h0_im"] = _check(h0[1], "h0_im", (Bsz, H, N, D), f32, dev)
+    else:
+        p["h0_re"] = p["h0_im"] = None
+    if out is not None:
+        y_re, y_im = out[0], out[1]
+        hT_re, hT_im = (out[2], out[3]) if (return_state and len(out) >= 4) else (None, None)
+    else:
+        y_re = torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev)
+        y_im = torch.empty_like(y_re)
+        hT_re = hT_im = None
+    if return_state and hT_re is None:
+        hT_re = torch.empty((Bsz, H, N, D), dtype=torch.float32, device=dev)
+        hT_im = torch.empty_like(hT_re)
+    p["y_re"] = _check(y_re, "y_re", (Bsz, T, H, D), f32, dev)
+    p["y_im"] = _check(y_im, "y_im", (Bsz, T, H, D), f32, dev)
+    p["hT_re"] = None if hT_re is None else _check(hT_re, "hT_re", (Bsz, H, N, D), f32, dev)
+    p["hT_im"] = None if hT_im is None else _check(hT_im, "hT_im", (Bsz, H, N, D), f32, dev)
+    need = cssd_forward_workspace_size(Bsz, T, H, D, N, chunk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.cssd_forward(Bsz, T, H, D, N, int(chunk), code,
+                          p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
+                          p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"],
+                          p["y_re"], p["y_im"], p["hT_re"], p["hT_im"],
+                          workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_forward")
+    return y_re, y_im, hT_re, hT_im
+
+
+def cssd_step(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h_im, *,
+              out=None, stream=None):
+    """One decode token for all (batch, head); the state (h_re, h_im) is updated
+    in place.  x_*: (B,H,D); B_*, C_*: (B,H,N); dt: (B,H); A_*: (H,); Dskip: (H,)
+    or None; h_*: (B,H,N,D).  All float32.  Returns (y_re, y_im), each (B,H,D)."""
+    torch = _torch()
+    lib = load_library()
+    dev = h_re.device
+    Bsz, H, N, D = h_re.shape
+    f32 = (torch.float32,)
+    p = {}
+    for name, t, shp in (("x_re", x_re, (Bsz, H, D)), ("x_im", x_im, (Bsz, H, D)),
+                         ("B_re", B_re, (Bsz, H, N)), ("B_im", B_im, (Bsz, H, N)),
+                         ("C_re", C_re, (Bsz, H, N)), ("C_im", C_im, (Bsz, H, N)),
+                         ("dt", dt, (Bsz, H)), ("A_re", A_re, (H,)), ("A_im", A_im, (H,)),
+                         ("h_re", h_re, (Bsz, H, N, D)), ("h_im", h_im, (Bsz, H, N, D))):
+        p[name] = _check(t, name, shp, f32, dev)
+    p["Dskip"] = None if Dskip is None else _check(Dskip, "Dskip", (H,), f32, dev)
+    if out is None:
+        y_re = torch.empty((Bsz, H, D), dtype=torch.float32, device=dev)
+        y_im = torch.empty_like(y_re)
+    else:
+        y_re, y_im = out
+    p["y_re"] = _check(y_re, "y_re", (Bsz, H, D), f32, dev)
+    p["y_im"] = _check(y_im, "y_im", (Bsz, H, D), f32, dev)
+    st = lib.cssd_step(Bsz, H, D, N, p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"],
+                       p["C_im"], p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h_re"],
+                       p["h_im"], p["y_re"], p["y_im"], _stream_ptr(stream, dev))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_step")
+    return y_re, y_im
+
+
+class profile:
+    """Context manager around the library's per-kernel event timing.
+
+    with profile() as prof: ...;  prof.ms[name], prof.launches[name]
+    (the events are recorded on the stream each kernel is launched on)."""
+
+    def __enter__(self):
+        lib = load_library()
+        lib.cssd_profile_read(None, None, 0)  # drop anything pending
+        lib.cssd_profile_enable(1)
+        self.ms, self.launches = {}, {}
+        return self
+
+    def read(self):
+        lib = load_library()
+        n = len(KERNEL_NAMES)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        k = lib.cssd_profile_read(ms, cnt, n)
+        if k < 0:
+            raise CSSDError(-k, "cssd_profile_read")
+        for i, name in enumerate(KERNEL_NAMES):
+            self.ms[name] = self.ms.get(name, 0.0) + ms[i]
+            self.launches[name] = self.launches.get(name, 0) + cnt[i]
+        return self
+
+    def __exit__(self, *exc):
+        self.read()
+        load_library().cssd_profile_enable(0)
+        return False

@@ -1,0 +1,291 @@
+// C ABI of libcssd.so (declared in include/cssd.h): host-side validation,
+// workspace layout, kernel sequencing and the optional per-kernel profiler.
+// Nothing here allocates device memory, synchronises a stream or reads device
+// memory; every kernel is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/cssd.h"
+#include "cssd_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool pow2_16_128(int64_t v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------- profiler
+struct Pending {
+    int kernel;
+    hipEvent_t start, stop;
+};
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> pool;
+    double ms[cssd::K_COUNT] = {0};
+    int64_t launches[cssd::K_COUNT] = {0};
+};
+
+Profiler& prof() {
+    static Profiler p;
+    return p;
+}
+
+hipEvent_t take_event(Profiler& p) {
+    if (!p.pool.empty()) {
+        hipEvent_t e = p.pool.back();
+        p.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs one launcher, bracketed by events while profiling is on.
+template <typename F>
+hipError_t timed(int kernel, hipStream_t stream, F&& launch) {
+    Profiler& p = prof();
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    {
+        std::lock_guard<std::mutex> g(p.mu);
+        if (p.on) {
+            e0 = take_event(p);
+            e1 = take_event(p);
+        }
+    }
+    if (e0 && e1 && hipEventRecord(e0, stream) != hipSuccess) return hipGetLastError();
+    hipError_t err = launch();
+    if (err != hipSuccess) return err;
+    if (e0 && e1) {
+        if (hipEventRecord(e1, stream) != hipSuccess) return hipGetLastError();
+        std::lock_guard<std::mutex> g(p.mu);
+        p.pending.push_back(Pending{kernel, e0, e1});
+    }
+    return hipSuccess;
+}
+
+struct Layout {
+    size_t acs_re, acs_im, e_re, e_im, w_re, w_im, cd_re, cd_im, st_re, st_im, total;
+};
+
+Layout layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C) {
+    const int64_t nC = (T + C - 1) / C;
+    const size_t P = (size_t)(B * H * nC * C);
+    const size_t S = (size_t)(B * H * nC) * (size_t)(N * D);
+    Layout l;
+    size_t off = 0;
+    auto put = [&](size_t bytes) {
+        const size_t at = off;
+        off = round_up(off + bytes);
+        return at;
+    };
+    l.acs_re = put(P * sizeof(double));
+    l.acs_im = put(P * sizeof(double));
+    l.e_re = put(P * sizeof(float));
+    l.e_im = put(P * sizeof(float));
+    l.w_re = put(P * sizeof(float));
+    l.w_im = put(P * sizeof(float));
+    l.cd_re = put((size_t)(B * H * nC) * sizeof(float));
+    l.cd_im = put((size_t)(B * H * nC) * sizeof(float));
+    l.st_re = put(S * sizeof(float));
+    l.st_im = put(S * sizeof(float));
+    l.total = off;
+    return l;
+}
+
+int check_shape(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C) {
+    if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || N <= 0 || C <= 0) return CSSD_ERR_INVALID_ARG;
+    if (!pow2_16_128(D) || !pow2_16_128(N) || !pow2_16_128(C)) return CSSD_ERR_UNSUPPORTED;
+    const int64_t nC = (T + C - 1) / C;
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t m = D > N ? D : N;
+    if (B > lim || T > lim || H > lim) return CSSD_ERR_UNSUPPORTED;
+    if (B * H > lim / (nC * C) || B * nC * C * H > lim / m) return CSSD_ERR_UNSUPPORTED;
+    if (B * H * nC > lim / (N * D)) return CSSD_ERR_UNSUPPORTED;
+    return CSSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cssd_version(void) { return CSSD_VERSION; }
+
+const char* cssd_status_string(int status) {
+    switch (status) {
+        case CSSD_OK: return "CSSD_OK";
+        case CSSD_ERR_INVALID_ARG: return "CSSD_ERR_INVALID_ARG: bad pointer, size, alignment or aliasing";
+        case CSSD_ERR_UNSUPPORTED: return "CSSD_ERR_UNSUPPORTED: sizes outside the supported set";
+        case CSSD_ERR_WORKSPACE: return "CSSD_ERR_WORKSPACE: workspace missing, too small or misaligned";
+        case CSSD_ERR_HIP: return "CSSD_ERR_HIP: a HIP launch or runtime call failed";
+        default: return "unknown cssd status";
+    }
+}
+
+int cssd_forward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                int64_t dstate, int64_t chunk, size_t* bytes) {
+    if (bytes == nullptr) return CSSD_ERR_INVALID_ARG;
+    const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
+    if (st != CSSD_OK) return st;
+    *bytes = layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
+    return CSSD_OK;
+}
+
+int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int64_t chunk, int32_t in_dtype, const void* x_re, const void* x_im,
+                 const void* B_re, const void* B_im, const void* C_re, const void* C_im,
+                 const float* dt, const float* A_re, const float* A_im, const float* Dskip,
+                 const float* h0_re, const float* h0_im, float* y_re, float* y_im, float* hT_re,
+                 float* hT_im, void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
+    if (st != CSSD_OK) return st;
+    if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
+    const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, y_re, y_im};
+    for (const void* p : req)
+        if (p == nullptr || !aligned16(p)) return CSSD_ERR_INVALID_ARG;
+    if ((h0_re == nullptr) != (h0_im == nullptr)) return CSSD_ERR_INVALID_ARG;
+    if ((hT_re == nullptr) != (hT_im == nullptr)) return CSSD_ERR_INVALID_ARG;
+    const void* opt[] = {Dskip, h0_re, h0_im, hT_re, hT_im};
+    for (const void* p : opt)
+        if (p != nullptr && !aligned16(p)) return CSSD_ERR_INVALID_ARG;
+    const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im};
+    const void* outs[] = {y_re, y_im, hT_re, hT_im};
+    for (const void* o : outs) {
+        if (o == nullptr) continue;
+        for (const void* i : ins)
+            if (o == i) return CSSD_ERR_INVALID_ARG;
+    }
+    if (y_re == y_im || (hT_re != nullptr && (hT_re == hT_im || hT_re == y_re || hT_re == y_im)))
+        return CSSD_ERR_INVALID_ARG;
+
+    const Layout L = layout(batch, seqlen, nheads, headdim, dstate, chunk);
+    if (workspace == nullptr || workspace_bytes < L.total ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return CSSD_ERR_WORKSPACE;
+
+    char* ws = static_cast<char*>(workspace);
+    cssd::FwdArgs a;
+    a.B = batch;
+    a.T = seqlen;
+    a.H = nheads;
+    a.D = headdim;
+    a.N = dstate;
+    a.C = chunk;
+    a.nC = (seqlen + chunk - 1) / chunk;
+    a.in_dtype = in_dtype;
+    a.x_re = x_re; a.x_im = x_im;
+    a.b_re = B_re; a.b_im = B_im;
+    a.c_re = C_re; a.c_im = C_im;
+    a.dt = dt; a.a_re = A_re; a.a_im = A_im; a.dskip = Dskip;
+    a.h0_re = h0_re; a.h0_im = h0_im;
+    a.y_re = y_re; a.y_im = y_im; a.hT_re = hT_re; a.hT_im = hT_im;
+    a.acs_re = reinterpret_cast<double*>(ws + L.acs_re);
+    a.acs_im = reinterpret_cast<double*>(ws + L.acs_im);
+    a.e_re = reinterpret_cast<float*>(ws + L.e_re);
+    a.e_im = reinterpret_cast<float*>(ws + L.e_im);
+    a.w_re = reinterpret_cast<float*>(ws + L.w_re);
+    a.w_im = reinterpret_cast<float*>(ws + L.w_im);
+    a.cd_re = reinterpret_cast<float*>(ws + L.cd_re);
+    a.cd_im = reinterpret_cast<float*>(ws + L.cd_im);
+    a.st_re = reinterpret_cast<float*>(ws + L.st_re);
+    a.st_im = reinterpret_cast<float*>(ws + L.st_im);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_CHUNK_STATE, s, [&] { return cssd::launch_chunk_state(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_STATE_PASS, s, [&] { return cssd::launch_state_pass(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_CHUNK_SCAN, s, [&] { return cssd::launch_chunk_scan(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    return CSSD_OK;
+}
+
+int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, const float* x_re,
+              const float* x_im, const float* B_re, const float* B_im, const float* C_re,
+              const float* C_im, const float* dt, const float* A_re, const float* A_im,
+              const float* Dskip, float* h_re, float* h_im, float* y_re, float* y_im,
+              void* stream) {
+    if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0) return CSSD_ERR_INVALID_ARG;
+    if (!pow2_16_128(headdim) || !pow2_16_128(dstate)) return CSSD_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 31;
+    if (batch > lim || nheads > lim || batch * nheads > lim / (headdim * dstate))
+        return CSSD_ERR_UNSUPPORTED;
+    const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, h_re, h_im, y_re, y_im};
+    for (const void* p : req)
+        if (p == nullptr || !aligned16(p)) return CSSD_ERR_INVALID_ARG;
+    if (Dskip != nullptr && !aligned16(Dskip)) return CSSD_ERR_INVALID_ARG;
+    const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip};
+    const void* outs[] = {h_re, h_im, y_re, y_im};
+    for (const void* o : outs)
+        for (const void* i : ins)
+            if (o == i) return CSSD_ERR_INVALID_ARG;
+    if (h_re == h_im || y_re == y_im || y_re == h_re || y_re == h_im || y_im == h_re ||
+        y_im == h_im)
+        return CSSD_ERR_INVALID_ARG;
+
+    cssd::StepArgs a;
+    a.B = batch; a.H = nheads; a.D = headdim; a.N = dstate;
+    a.x_re = x_re; a.x_im = x_im; a.b_re = B_re; a.b_im = B_im; a.c_re = C_re; a.c_im = C_im;
+    a.dt = dt; a.a_re = A_re; a.a_im = A_im; a.dskip = Dskip;
+    a.h_re = h_re; a.h_im = h_im; a.y_re = y_re; a.y_im = y_im;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (timed(cssd::K_STEP, s, [&] { return cssd::launch_step(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    return CSSD_OK;
+}
+
+int cssd_profile_enable(int on) {
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.on = on != 0;
+    return CSSD_OK;
+}
+
+int cssd_profile_read(double* ms, int64_t* launches, int capacity) {
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    int status = CSSD_OK;
+    for (const Pending& q : p.pending) {
+        float t = 0.f;
+        if (hipEventSynchronize(q.stop) != hipSuccess ||
+            hipEventElapsedTime(&t, q.start, q.stop) != hipSuccess) {
+            status = CSSD_ERR_HIP;
+        } else {
+            p.ms[q.kernel] += t;
+            p.launches[q.kernel] += 1;
+        }
+        p.pool.push_back(q.start);
+        p.pool.push_back(q.stop);
+    }
+    p.pending.clear();
+    for (int k = 0; k < cssd::K_COUNT && k < capacity; ++k) {
+        if (ms) ms[k] = p.ms[k];
+        if (launches) launches[k] = p.launches[k];
+    }
+    for (int k = 0; k < cssd::K_COUNT; ++k) {
+        p.ms[k] = 0;
+        p.launches[k] = 0;
+    }
+    return status == CSSD_OK ? (int)cssd::K_COUNT : -status;
+}
+
+const char* cssd_kernel_name(int kernel_id) {
+    static const char* names[cssd::K_COUNT] = {"k_cumsum", "k_chunk_state", "k_state_pass",
+                                                "k_chunk_scan", "k_step"};
+    if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
+    return names[kernel_id];
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// K1: discretisation and chunk-local inclusive cumulative log-decay.
+//
+// For every (batch b, head h, chunk c) and intra-chunk position l:
+//   A_log[l]  = softplus(dt[b, cC+l, h]) * A[h]        (0 on padded positions l >= T - cC)
+//   acs[l]    = sum_{u <= l} A_log[u]                  (inclusive, restarts at every chunk)
+//   e[l]      = exp(acs[l])                            readout decay from the chunk start
+//   w[l]      = exp(acs[C-1] - acs[l])                 decay from l to the chunk end
+//   cd        = exp(acs[C-1])                          whole-chunk decay
+// Passages: Mamba-3-Lite docs, "SSD Theory" 4.3 (within-chunk cumulative sum,
+// inclusive so the segment matrix has a unit diagonal), 4.5 (chunk total and
+// the decay to the chunk end), and "The Chunkwise Complex SSD Algorithm" 4.2
+// (log-decay A_log = softplus(dt) A and its cumsum over the chunk axis).
+//
+// One wave per (b, h, c); lane l holds position l (two positions per lane for
+// C = 128).  The scan runs in fp64 with wave shuffles: the imaginary part of a
+// 128-step chunk reaches thousands of radians, and every consumer later takes
+// differences of these sums, so they are kept exact to fp64 and stored as
+// fp64.  Exponentials are evaluated in fp64 and rounded once to fp32.
+// Padded positions get a zero increment, so a partial last chunk's total equals
+// the sum over its valid positions and the final state never decays through
+// padding.
+#include "cssd_device.h"
+#include "cssd_launch.h"
+
+namespace cssd {
+
+template <int PER>  // positions per lane: 1 (C <= 64) or 2 (C = 128)
+__global__ __launch_bounds__(256) void k_cumsum(const float* __restrict__ dt,
+                                                const float* __restrict__ a_re,
+                                                const float* __restrict__ a_im, int64_t T, int H,
+                                                int nC, int C, int64_t units,
+                                                double* __restrict__ acs_re,
+                                                double* __restrict__ acs_im,
+                                                float* __restrict__ e_re, float* __restrict__ e_im,
+                                                float* __restrict__ w_re, float* __restrict__ w_im,
+                                                float* __restrict__ cd_re,
+                                                float* __restrict__ cd_im) {
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= units) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int c = (int)(unit % nC);
+    const int64_t bh = unit / nC;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const double are = a_re[h], aim = a_im[h];
+    const int64_t t0 = (int64_t)c * C;
+
+    double vr[PER], vi[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int l = lane * PER + j;
+        const int64_t t = t0 + l;
+        vr[j] = 0.0;
+        vi[j] = 0.0;
+        if (l < C && t < T) {
+            const double s = softplus_f64((double)dt[(b * T + t) * H + h]);
+            vr[j] = s * are;
+            vi[j] = s * aim;
+        }
+    }
+    // in-lane prefix, then an inclusive wave scan of the lane totals
+#pragma unroll
+    for (int j = 1; j < PER; ++j) {
+        vr[j] += vr[j - 1];
+        vi[j] += vi[j - 1];
+    }
+    double sr = vr[PER - 1], si = vi[PER - 1];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double ur = __shfl_up(sr, off, 64);
+        const double ui = __shfl_up(si, off, 64);
+        if (lane >= off) {
+            sr += ur;
+            si += ui;
+        }
+    }
+    const double exr = sr - vr[PER - 1], exi = si - vi[PER - 1];  // exclusive prefix of the lane
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        vr[j] += exr;
+        vi[j] += exi;
+    }
+    // chunk total acs[C-1] lives in lane (C-1)/PER, slot (C-1)%PER
+    const int last_lane = (C - 1) / PER;
+    double tot_r = vr[PER - 1], tot_i = vi[PER - 1];
+    if (PER == 2 && ((C - 1) % PER) == 0) {
+        tot_r = vr[0];
+        tot_i = vi[0];
+    }
+    tot_r = __shfl(tot_r, last_lane, 64);
+    tot_i = __shfl(tot_i, last_lane, 64);
+
+    const int64_t base = bh * (int64_t)nC * C + t0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int l = lane * PER + j;
+        if (l < C) {
+            acs_re[base + l] = vr[j];
+            acs_im[base + l] = vi[j];
+            double sn, cs;
+            sincos(vi[j], &sn, &cs);
+            const double m = exp(vr[j]);
+            e_re[base + l] = (float)(m * cs);
+            e_im[base + l] = (float)(m * sn);
+            sincos(tot_i - vi[j], &sn, &cs);
+            const double mw = exp(tot_r - vr[j]);
+            w_re[base + l] = (float)(mw * cs);
+            w_im[base + l] = (float)(mw * sn);
+        }
+    }
+    if (lane == 0) {
+        double sn, cs;
+        sincos(tot_i, &sn, &cs);
+        const double m = exp(tot_r);
+        cd_re[bh * nC + c] = (float)(m * cs);
+        cd_im[bh * nC + c] = (float)(m * sn);
+    }
+}
+
+hipError_t launch_cumsum(const FwdArgs& a, hipStream_t stream) {
+    const int64_t units = a.B * a.H * a.nC;
+    const dim3 grid((unsigned)((units + 3) / 4)), block(256);
+    if (a.C <= 64)
+        hipLaunchKernelGGL(k_cumsum<1>, grid, block, 0, stream, a.dt, a.a_re, a.a_im, a.T,
+                           (int)a.H, (int)a.nC, (int)a.C, units, a.acs_re, a.acs_im, a.e_re,
+                           a.e_im, a.w_re, a.w_im, a.cd_re, a.cd_im);
+    else
+        hipLaunchKernelGGL(k_cumsum<2>, grid, block, 0, stream, a.dt, a.a_re, a.a_im, a.T,
+                           (int)a.H, (int)a.nC, (int)a.C, units, a.acs_re, a.acs_im, a.e_re,
+                           a.e_im, a.w_re, a.w_im, a.cd_re, a.cd_im);
+    return hipGetLastError();
+}
+
+}  // namespace cssd

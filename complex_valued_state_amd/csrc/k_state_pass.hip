@@ -1,0 +1,93 @@
+// K4: the chunk-level scan that carries the state from chunk to chunk.
+//
+//   H_0 = h0 (or 0);   H_{c+1} = cd[c] * H_c + S_c;   hT = H_{nC}
+//
+// where cd[c] = exp(acs[C-1]) is the decay across chunk c and S_c its end
+// state from zero.  This is the recurrence over T/C steps that the SSD
+// decomposition leaves between chunks (Mamba-3-Lite docs, "SSD Theory" 4.5:
+// the state entering chunk c is every earlier chunk's end state decayed across
+// the chunks in between; "The Chunkwise Complex SSD Algorithm" 4.5 writes it as
+// H_c = Phi_{c-1} H_{c-1} + S_{c-1}).  It is evaluated in exactly that
+// sequential form: the einsum variant on the page aligns the decay one chunk
+// late when chunk totals differ (its own "Pitfalls" section).
+//
+// The state buffer holds S_c on entry and is overwritten in place with H_c,
+// the carry-in state chunk c's output combine reads.  Memory-bound: one thread
+// owns four consecutive (n, p) elements of one (b, h) and walks the chunks,
+// issuing the loads of U chunks before their dependent updates so that several
+// loads are in flight per thread.
+#include "cssd_device.h"
+#include "cssd_launch.h"
+
+namespace cssd {
+
+__global__ __launch_bounds__(256) void k_state_pass(float4* __restrict__ st_re,
+                                                    float4* __restrict__ st_im,
+                                                    const float* __restrict__ cd_re,
+                                                    const float* __restrict__ cd_im,
+                                                    const float4* __restrict__ h0_re,
+                                                    const float4* __restrict__ h0_im,
+                                                    float4* __restrict__ hT_re,
+                                                    float4* __restrict__ hT_im, int64_t total,
+                                                    int nd4, int nC) {
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (tid >= total) return;
+    const int64_t bh = tid / nd4;
+    const int e = (int)(tid % nd4);
+    float4 hr = make_float4(0.f, 0.f, 0.f, 0.f), hi = hr;
+    if (h0_re != nullptr) {
+        hr = h0_re[tid];
+        hi = h0_im[tid];
+    }
+    const int64_t base = bh * (int64_t)nC * nd4 + e;
+    constexpr int U = 8;
+    for (int c0 = 0; c0 < nC; c0 += U) {
+        float4 sr[U], si[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 + u < nC) {
+                sr[u] = nt_load4(&st_re[base + (int64_t)(c0 + u) * nd4]);
+                si[u] = nt_load4(&st_im[base + (int64_t)(c0 + u) * nd4]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u;
+            if (c < nC) {
+                st_re[base + (int64_t)c * nd4] = hr;
+                st_im[base + (int64_t)c * nd4] = hi;
+                const float dr = cd_re[bh * nC + c], di = cd_im[bh * nC + c];
+                float4 nr, ni;
+                nr.x = dr * hr.x - di * hi.x + sr[u].x;
+                nr.y = dr * hr.y - di * hi.y + sr[u].y;
+                nr.z = dr * hr.z - di * hi.z + sr[u].z;
+                nr.w = dr * hr.w - di * hi.w + sr[u].w;
+                ni.x = dr * hi.x + di * hr.x + si[u].x;
+                ni.y = dr * hi.y + di * hr.y + si[u].y;
+                ni.z = dr * hi.z + di * hr.z + si[u].z;
+                ni.w = dr * hi.w + di * hr.w + si[u].w;
+                hr = nr;
+                hi = ni;
+            }
+        }
+    }
+    if (hT_re != nullptr) {
+        hT_re[tid] = hr;
+        hT_im[tid] = hi;
+    }
+}
+
+hipError_t launch_state_pass(const FwdArgs& a, hipStream_t stream) {
+    const int nd4 = (int)(a.N * a.D / 4);
+    const int64_t total = a.B * a.H * nd4;
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    hipLaunchKernelGGL(k_state_pass, grid, block, 0, stream, reinterpret_cast<float4*>(a.st_re),
+                       reinterpret_cast<float4*>(a.st_im), a.cd_re, a.cd_im,
+                       reinterpret_cast<const float4*>(a.h0_re),
+                       reinterpret_cast<const float4*>(a.h0_im),
+                       reinterpret_cast<float4*>(a.hT_re), reinterpret_cast<float4*>(a.hT_im),
+                       total, nd4, (int)a.nC);
+    return hipGetLastError();
+}
+
+}  // namespace cssd

@@ -1,0 +1,184 @@
+/*
+ * cssd.h -- C ABI of libcssd.so: the complex-valued diagonal selective
+ * state-space scan, computed in chunkwise form on AMD MI355X (gfx950), plus its
+ * single-token recurrent decode step.
+ *
+ * The operation (Mamba-3-Lite docs, "SSD Theory -- Complex States & the
+ * Chunkwise Algorithm", section 2, and "Complex-Valued State Spaces", "The
+ * recurrence" and "Discretization"; the skip term D x follows the burn-mamba
+ * "step_constant" module's readout):
+ *
+ *     abar_t = exp(softplus(dt_t) * A)          A: one complex scalar per head
+ *     h_t    = abar_t * h_{t-1} + B_t (x) x_t   h_t: N x D complex per (batch, head)
+ *     y_t    = sum_n C_t[n] * h_t[n, :] + D * x_t
+ *
+ * softplus acts on the real dt before the product with the complex A; C_t is
+ * not conjugated; the outer product puts B_t on the state axis (N) and x_t on
+ * the channel axis (D).  y is complex: both planes are returned.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Complex tensors are PLANAR: two separate, contiguous, row-major arrays
+ *    (real plane, imaginary plane) of identical shape.  No interleaved data.
+ *  - Every array pointer is a DEVICE pointer owned by the caller, 16-byte
+ *    aligned, C-contiguous with the shape given in its comment.  The library
+ *    never allocates, frees or synchronises; all work is enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL = the legacy default stream) and is
+ *    complete when that stream is.  Outputs are valid only after that point.
+ *  - Validation is synchronous and host-side: bad arguments return an error
+ *    status before anything is enqueued, and the library never reads device
+ *    memory from the host.  Launch failures return CSSD_ERR_HIP.  No C++
+ *    exception crosses this boundary.
+ *  - Supported sizes: headdim D and dstate N in {16, 32, 64, 128}; chunk in
+ *    {16, 32, 64, 128}; any seqlen >= 1 (a partial last chunk is masked inside
+ *    the kernels, nothing is padded in memory); batch, nheads >= 1, with
+ *    batch*seqlen*nheads*max(D,N) < 2^31 elements per plane.  Other sizes
+ *    return CSSD_ERR_UNSUPPORTED.  There is one kernel path and no fallback.
+ *  - Outputs must not alias inputs (except the decode state, updated in place).
+ *  - The library keeps no per-call state and is safe to call from several host
+ *    threads on different streams.  The optional profiler (cssd_profile_*)
+ *    is process-wide and guarded by a lock.
+ */
+#ifndef CSSD_H
+#define CSSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSSD_VERSION 100 /* major*100 + minor */
+
+typedef enum cssd_status {
+    CSSD_OK = 0,
+    CSSD_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, misalignment, aliasing */
+    CSSD_ERR_UNSUPPORTED = 2, /* sizes outside the supported set */
+    CSSD_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned */
+    CSSD_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} cssd_status;
+
+typedef enum cssd_dtype {
+    CSSD_F32 = 0,  /* x, B, C planes are float32 */
+    CSSD_BF16 = 1  /* x, B, C planes are bfloat16 bit patterns (uint16); all else float32 */
+} cssd_dtype;
+
+/* Library version, CSSD_VERSION of the build. */
+int cssd_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *cssd_status_string(int status);
+
+/*
+ * Bytes of device workspace cssd_forward needs for this shape (written to
+ * *bytes).  Passage: the chunk states and the chunk-level scan of the SSD
+ * decomposition (Mamba-3-Lite docs, "SSD Theory" 4.5): the workspace holds one
+ * N x D complex state per chunk and the chunk-local cumulative log-decay; the
+ * C x C segment matrix L is never materialised (it lives in registers), so no
+ * term grows like 8*B*T*H*C bytes ("SSD Theory" section 5).
+ *
+ * Layout (nC = ceil(T/C), P = nC*C padded positions, every region 256-byte
+ * aligned, in this order; a caller may read it after the stream completes):
+ *   acs_re, acs_im : double [B][H][P]     inclusive chunk-local cumsum of
+ *                                         softplus(dt)*A (0 increments on
+ *                                         padded positions)
+ *   e_re,  e_im    : float  [B][H][P]     exp(acs[l])
+ *   w_re,  w_im    : float  [B][H][P]     exp(acs[C-1] - acs[l])
+ *   cd_re, cd_im   : float  [B][H][nC]    exp(acs[C-1]) (chunk decay)
+ *   st_re, st_im   : float  [B][H][nC][N][D]  chunk end states S_c, replaced
+ *                                         in place by the carry-in states H_c
+ * Returns CSSD_OK, CSSD_ERR_INVALID_ARG (null bytes / non-positive size) or
+ * CSSD_ERR_UNSUPPORTED.
+ */
+int cssd_forward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                int64_t headdim, int64_t dstate, int64_t chunk,
+                                size_t *bytes);
+
+/*
+ * Chunkwise forward over a whole sequence (Mamba-3-Lite docs, "SSD Theory"
+ * section 4 and "The Chunkwise Complex SSD Algorithm" section 4): per chunk,
+ * the cumulative log-decay, the causal segment matrix
+ * L[l,s] = exp(acs[l]-acs[s]) 1[l>=s], the intra-chunk term (C B^T . L) X, the
+ * chunk end state, a T/C-step pass carrying the state between chunks, and the
+ * output combine Y_diag + exp(acs) C H_c + D x.  The result equals the
+ * sequential recurrence above (the SSD decomposition is exact; only rounding
+ * order differs).
+ *
+ *   in_dtype         CSSD_F32 or CSSD_BF16 (applies to x, B, C planes only)
+ *   x_re, x_im       [B,T,H,D]   input channels
+ *   B_re, B_im       [B,T,H,N]   input coupling B_t
+ *   C_re, C_im       [B,T,H,N]   readout C_t
+ *   dt               [B,T,H]     float32 raw step; softplus is applied inside
+ *   A_re, A_im       [H]         float32 per-head complex rate
+ *   Dskip            [H]         float32 skip weight, or NULL for D = 0
+ *   h0_re, h0_im     [B,H,N,D]   float32 initial state, or both NULL for zero
+ *   y_re, y_im       [B,T,H,D]   float32 output (written)
+ *   hT_re, hT_im     [B,H,N,D]   float32 state after step T-1 (written), or
+ *                                both NULL.  Same layout as cssd_step's state,
+ *                                so a prefill hands over to decode directly.
+ *   workspace        device buffer of >= cssd_forward_workspace_size bytes,
+ *                    256-byte aligned; contents on entry are ignored.
+ *   stream           hipStream_t (as void*), or NULL.
+ * Padded positions of a partial last chunk contribute nothing and do not
+ * decay hT.  Returns CSSD_OK or an error status (nothing enqueued on error,
+ * except CSSD_ERR_HIP, which may leave earlier kernels of the call enqueued).
+ */
+int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                 int64_t dstate, int64_t chunk, int32_t in_dtype,
+                 const void *x_re, const void *x_im,
+                 const void *B_re, const void *B_im,
+                 const void *C_re, const void *C_im,
+                 const float *dt, const float *A_re, const float *A_im,
+                 const float *Dskip,
+                 const float *h0_re, const float *h0_im,
+                 float *y_re, float *y_im,
+                 float *hT_re, float *hT_im,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for every (batch, head), state updated in place
+ * (the loop body of the sequential scan, Mamba-3-Lite docs, "Complex-Valued
+ * State Spaces", walkthrough of the naive scan; fixed-size state, no cache of
+ * past tokens):
+ *     h <- exp(softplus(dt) A) h + B (x) x ;   y = sum_n C[n] h[n,:] + D x
+ *
+ *   x_re, x_im   [B,H,D]     float32
+ *   B_re, B_im   [B,H,N]     float32
+ *   C_re, C_im   [B,H,N]     float32
+ *   dt           [B,H]       float32 raw step
+ *   A_re, A_im   [H]         float32
+ *   Dskip        [H] or NULL
+ *   h_re, h_im   [B,H,N,D]   float32 state, read and overwritten
+ *   y_re, y_im   [B,H,D]     float32 output
+ * Returns CSSD_OK or an error status.
+ */
+int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+              const float *x_re, const float *x_im,
+              const float *B_re, const float *B_im,
+              const float *C_re, const float *C_im,
+              const float *dt, const float *A_re, const float *A_im,
+              const float *Dskip,
+              float *h_re, float *h_im,
+              float *y_re, float *y_im, void *stream);
+
+/*
+ * Optional per-kernel timing (a measurement aid, not part of the operation).
+ * While enabled, every kernel launch of cssd_forward/cssd_step is bracketed by
+ * two hipEvents recorded on the caller's stream.  cssd_profile_read waits for
+ * the recorded events, writes the accumulated milliseconds and launch counts
+ * per kernel id into ms[k] and launches[k] for k < min(capacity, number of
+ * kernels), resets the accumulators and returns the number of kernel ids (or a
+ * negative status on error).  Kernel ids: 0 cumsum, 1 chunk_state,
+ * 2 state_pass, 3 chunk_scan, 4 step.  cssd_kernel_name(k) gives the device
+ * symbol stem of each id (NULL if out of range).
+ */
+int cssd_profile_enable(int on);
+int cssd_profile_read(double *ms, int64_t *launches, int capacity);
+const char *cssd_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSSD_H */

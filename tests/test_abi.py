@@ -1,0 +1,143 @@
+"""The C ABI of libcssd.so on the host (no GPU needed, no kernel launched).
+
+Every call here fails validation before anything is enqueued, so none of them
+touches a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cssd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import complex_valued_state_amd as cssd
+    if not os.path.exists(cssd.LIB_PATH):
+        from complex_valued_state_amd.build import build_library
+        build_library()
+    return cssd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cssd_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("cssd_forward", "cssd_step", "cssd_forward_workspace_size",
+                     "cssd_status_string", "cssd_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {lib._name}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.cssd_version() == 100
+    for st in range(5):
+        assert lib.cssd_status_string(st)
+    assert b"unknown" in lib.cssd_status_string(99)
+
+
+def _ws(lib, *shape):
+    n = ctypes.c_size_t(0)
+    st = lib.cssd_forward_workspace_size(*shape, ctypes.byref(n))
+    return st, n.value
+
+
+def _align(v):
+    return (v + 255) // 256 * 256
+
+
+def test_workspace_size_layout(lib):
+    # B, T, H, D, N, C with a partial last chunk
+    B, T, H, D, N, C = 2, 100, 3, 32, 64, 16
+    st, got = _ws(lib, B, T, H, D, N, C)
+    assert st == 0
+    nC = -(-T // C)
+    P = B * H * nC * C
+    want = 0
+    for nbytes in (8 * P, 8 * P, 4 * P, 4 * P, 4 * P, 4 * P, 4 * B * H * nC, 4 * B * H * nC,
+                   4 * B * H * nC * N * D, 4 * B * H * nC * N * D):
+        want = _align(want + nbytes)
+    assert got == want
+
+
+def test_workspace_never_holds_the_segment_matrix(lib):
+    """A materialised C x C segment matrix would cost 8*B*T*H*C bytes and grow
+    with C ("SSD Theory", section 5: 268 MB at B16 T2048 H16 C64); the
+    workspace instead shrinks as C grows (one state per chunk)."""
+    assert 8 * 16 * 2048 * 16 * 64 == 268435456
+    sizes = [_ws(lib, 16, 2048, 16, 64, 64, c)[1] for c in (16, 32, 64, 128)]
+    assert sizes == sorted(sizes, reverse=True)
+
+
+@pytest.mark.parametrize("shape,status", [
+    ((0, 64, 2, 16, 16, 16), 1), ((1, 0, 2, 16, 16, 16), 1), ((1, 64, -1, 16, 16, 16), 1),
+    ((1, 64, 2, 24, 16, 16), 2), ((1, 64, 2, 16, 256, 16), 2), ((1, 64, 2, 16, 16, 48), 2),
+    ((1, 64, 2, 16, 16, 8), 2), ((1 << 20, 1 << 20, 64, 128, 128, 64), 2),
+])
+def test_workspace_size_rejects(lib, shape, status):
+    assert _ws(lib, *shape)[0] == status
+
+
+def _fwd(lib, shape=(1, 64, 2, 16, 16, 16), dtype=0, ptrs=None, ws=None, ws_bytes=1 << 30):
+    # fake, aligned, never-dereferenced addresses; validation fails before any launch
+    base = 0x10000000
+    p = {k: base + 0x100000 * i for i, k in enumerate(
+        ["x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt", "A_re", "A_im", "D",
+         "h0_re", "h0_im", "y_re", "y_im", "hT_re", "hT_im"])}
+    p.update(ptrs or {})
+    return lib.cssd_forward(*shape, dtype, p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"],
+                            p["C_im"], p["dt"], p["A_re"], p["A_im"], p["D"], p["h0_re"],
+                            p["h0_im"], p["y_re"], p["y_im"], p["hT_re"], p["hT_im"],
+                            ws, ws_bytes, None)
+
+
+def test_forward_validation(lib):
+    # missing workspace (all pointers otherwise plausible) -> workspace error, no launch
+    assert _fwd(lib, ws=None) == 3
+    assert _fwd(lib, ws=0x20000000, ws_bytes=16) == 3
+    assert _fwd(lib, ws=0x20000010) == 3                      # misaligned workspace
+    assert _fwd(lib, ptrs={"x_re": None}, ws=0x20000000) == 1
+    assert _fwd(lib, ptrs={"y_im": None}, ws=0x20000000) == 1
+    assert _fwd(lib, ptrs={"dt": 0x10000004}, ws=0x20000000) == 1  # misaligned
+    assert _fwd(lib, ptrs={"h0_im": None}, ws=0x20000000) == 1     # half an initial state
+    assert _fwd(lib, ptrs={"hT_re": None}, ws=0x20000000) == 1     # half a final state
+    assert _fwd(lib, ptrs={"y_re": 0x10000000}, ws=0x20000000) == 1  # y aliases x
+    assert _fwd(lib, dtype=7, ws=0x20000000) == 1
+    assert _fwd(lib, shape=(1, 64, 2, 16, 16, 48), ws=0x20000000) == 2
+    assert _fwd(lib, shape=(1, 64, 2, 0, 16, 16), ws=0x20000000) == 1
+
+
+def test_step_validation(lib):
+    base = 0x10000000
+    ptrs = [base + 0x100000 * i for i in range(14)]
+    args = ptrs[:10] + ptrs[10:14]
+    assert lib.cssd_step(0, 2, 16, 16, *args, None) == 1
+    assert lib.cssd_step(1, 2, 20, 16, *args, None) == 2
+    bad = list(args); bad[0] = None
+    assert lib.cssd_step(1, 2, 16, 16, *bad, None) == 1
+    bad = list(args); bad[12] = bad[10]      # y_re aliases h_re
+    assert lib.cssd_step(1, 2, 16, 16, *bad, None) == 1
+    bad = list(args); bad[10] = bad[0]       # state aliases x
+    assert lib.cssd_step(1, 2, 16, 16, *bad, None) == 1
+
+
+def test_profiler_without_launches(lib):
+    import complex_valued_state_amd as cssd
+    with cssd.profile() as prof:
+        pass
+    assert set(prof.ms) == set(cssd.KERNEL_NAMES)
+    assert all(v == 0 for v in prof.launches.values())
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(9) is None

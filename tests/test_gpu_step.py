@@ -1,0 +1,178 @@
+"""GPU parity of cssd_step (the recurrent decode step) against the oracle and
+the constant-input closed forms (needs an MI355X)."""
+import math
+
+import numpy as np
+import pytest
+
+import cssd_workloads as wl
+from gpu_util import dev_inputs, gpu_forward, log, oracle_forward, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _run_steps(steps: wl.StepInputs, A_re, A_im, Dskip, h0=None):
+    """Drive cssd_step over the leading (token) axis; returns (y (S,B,H,D), h) complex."""
+    import torch
+    import complex_valued_state_amd as cssd
+    S, B, H, D = steps.x_re.shape
+    N = steps.B_re.shape[-1]
+    d = {f: _dev(getattr(steps, f)) for f in ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt")}
+    a_re, a_im = _dev(A_re), _dev(A_im)
+    dk = None if Dskip is None else _dev(Dskip)
+    if h0 is None:
+        h_re = torch.zeros((B, H, N, D), dtype=torch.float32, device="cuda:0")
+        h_im = torch.zeros_like(h_re)
+    else:
+        h_re, h_im = _dev(h0.real.astype(np.float32)), _dev(h0.imag.astype(np.float32))
+    ys_re = torch.empty((S, B, H, D), dtype=torch.float32, device="cuda:0")
+    ys_im = torch.empty_like(ys_re)
+    for s in range(S):
+        cssd.cssd_step(d["x_re"][s], d["x_im"][s], d["B_re"][s], d["B_im"][s], d["C_re"][s],
+                       d["C_im"][s], d["dt"][s], a_re, a_im, dk, h_re, h_im,
+                       out=(ys_re[s], ys_im[s]))
+    torch.cuda.synchronize()
+    c = lambda r, i: r.double().cpu().numpy() + 1j * i.double().cpu().numpy()
+    return c(ys_re, ys_im), c(h_re, h_im)
+
+
+def _as_sequence(steps: wl.StepInputs, A_re, A_im, Dskip, chunk=16):
+    """The same tokens as one (B, T=S, H, .) sequence for the oracle."""
+    t = lambda a: np.ascontiguousarray(np.moveaxis(a, 0, 1))
+    return wl.ForwardInputs(t(steps.x_re), t(steps.x_im), t(steps.B_re), t(steps.B_im),
+                            t(steps.C_re), t(steps.C_im), t(steps.dt), A_re, A_im, Dskip, chunk)
+
+
+@pytest.mark.parametrize("B,H,D,N", [(2, 3, 16, 32), (1, 2, 128, 16), (3, 2, 32, 128), (2, 2, 64, 64)])
+def test_step_small_vs_oracle(B, H, D, N):
+    S = 20
+    steps = wl.decode_steps(40 + D + N, S, B, H, D, N)
+    A_re, A_im, Dk = wl.decode_params(40, H)
+    log(f"  step B{B} H{H} D{D} N{N} x{S}")
+    y, h = _run_steps(steps, A_re, A_im, Dk)
+    yr, hr = oracle_forward(_as_sequence(steps, A_re, A_im, Dk))
+    assert rel_err(np.moveaxis(y, 0, 1), yr) <= TOL
+    assert rel_err(h, hr) <= TOL
+
+
+def test_step_decay_zero():
+    B, H, D, N = 2, 3, 64, 128
+    steps = wl.decode_steps(41, 3, B, H, D, N)
+    steps.dt[:] = 0
+    A_re = np.full(H, -1e4, dtype=np.float32)
+    A_im = np.array([0.3, -1.0, 2.0], dtype=np.float32)
+    Dk = np.array([0.5, -1.5, 2.0], dtype=np.float32)
+    y, h = _run_steps(steps, A_re, A_im, Dk)
+    x, Bm, Cm, _ = steps.complex()
+    want = np.einsum("sbhn,sbhn->sbh", Cm, Bm)[..., None] * x + Dk[None, None, :, None] * x
+    assert rel_err(y, want) <= TOL
+    assert rel_err(h, np.einsum("bhn,bhd->bhnd", Bm[-1], x[-1])) <= TOL
+
+
+def test_step_512_tokens_vs_oracle():
+    """512 consecutive tokens at the decode shape's H, N, D (batch 4)."""
+    B, H, D, N, S = 4, 48, 64, 128, 512
+    steps = wl.decode_steps(4, S, B, H, D, N)
+    A_re, A_im, Dk = wl.decode_params(4, H)
+    log(f"  step 512 tokens B{B} H{H}")
+    y, h = _run_steps(steps, A_re, A_im, Dk)
+    yr, hr = oracle_forward(_as_sequence(steps, A_re, A_im, Dk))
+    ey, eh = rel_err(np.moveaxis(y, 0, 1), yr), rel_err(h, hr)
+    log(f"    rel err y={ey:.3e} h={eh:.3e}")
+    assert ey <= TOL and eh <= TOL
+
+
+def test_step_full_decode_shape_sampled():
+    """B256 H48 N128 D64 for 16 tokens; sampled sequences against the oracle."""
+    s = wl.CONFIG_SHAPES[4]
+    B, H, D, N, S = s["B"], s["H"], s["D"], s["N"], 16
+    steps = wl.decode_steps(4, S, B, H, D, N)
+    A_re, A_im, Dk = wl.decode_params(4, H)
+    log(f"  step full shape x{S}")
+    y, h = _run_steps(steps, A_re, A_im, Dk)
+    import oracle
+    for (b, hh) in [(0, 0), (17, 5), (130, 47), (255, 20), (64, 33)]:
+        sub = wl.StepInputs(*[np.ascontiguousarray(getattr(steps, f)[:, b:b + 1, hh:hh + 1])
+                              for f in ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt")])
+        seq = _as_sequence(sub, A_re[hh:hh + 1], A_im[hh:hh + 1], Dk[hh:hh + 1])
+        x, Bm, Cm, dt, A, Dd, _ = seq.complex()
+        yr, hr = oracle.forward(x, Bm, Cm, dt, A, Dd, None)
+        assert rel_err(y[:, b, hh], yr[0, :, 0]) <= TOL, (b, hh)
+        assert rel_err(h[b, hh], hr[0, 0]) <= TOL, (b, hh)
+
+
+def test_step_constant_input_closed_form():
+    """One draw of (x, B, C, dt) held for n = 4096 tokens at the full decode
+    shape, from a zero state: y_n = (1 - a^n)/(1 - a) (C . B) x + D x, and at
+    n = 4096 the stationary value (C . B) x / (1 - a) + D x (burn-mamba
+    step_constant: the n-step geometric series and its n -> infinity limit, with
+    no rotation operator)."""
+    import torch
+    import complex_valued_state_amd as cssd
+    s = wl.CONFIG_SHAPES[4]
+    B, H, D, N = s["B"], s["H"], s["D"], s["N"]
+    one = wl.decode_step(4, 10_000, B, H, D, N)
+    A_re, A_im, Dk = wl.decode_params(4, H)
+    d = {f: _dev(getattr(one, f)) for f in ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt")}
+    a_re, a_im, dk = _dev(A_re), _dev(A_im), _dev(Dk)
+    h_re = torch.zeros((B, H, N, D), dtype=torch.float32, device="cuda:0")
+    h_im = torch.zeros_like(h_re)
+    x, Bm, Cm, dt = one.complex()
+    A = A_re.astype(np.float64) + 1j * A_im.astype(np.float64)
+    logdec = np.logaddexp(0.0, dt) * A[None, :]                      # (B, H)
+    a = np.exp(logdec)
+    score = np.einsum("bhn,bhn->bh", Cm, Bm)
+    checkpoints = {1, 2, 64, 1000, 4096}
+    log("  constant-input run, 4096 tokens")
+    y_re = y_im = None
+    for n in range(1, 4097):
+        y_re, y_im = cssd.cssd_step(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"],
+                                    d["C_im"], d["dt"], a_re, a_im, dk, h_re, h_im)
+        if n in checkpoints:
+            torch.cuda.synchronize()
+            y = y_re.double().cpu().numpy() + 1j * y_im.double().cpu().numpy()
+            geo = (1.0 - np.exp(n * logdec)) / (1.0 - a)
+            want = (geo * score)[..., None] * x + Dk[None, :, None] * x
+            e = rel_err(y, want)
+            log(f"    n={n} rel err {e:.3e}")
+            assert e <= TOL, n
+    yinf = (score / (1.0 - a))[..., None] * x + Dk[None, :, None] * x
+    assert np.max(np.abs(a)) ** 4096 < 1e-6
+    assert rel_err(y, yinf) <= TOL
+
+
+def test_prefill_then_decode():
+    """forward over T1 tokens hands its final state to cssd_step, which continues
+    the sequence; both match one forward over all T tokens."""
+    import torch
+    import complex_valued_state_amd as cssd
+    B, T, T1, H, D, N = 2, 96, 70, 3, 32, 64
+    inp = wl.random_forward(321, B, T, H, D, N, 32, with_h0=True, name="prefill")
+    y_all, h_all = gpu_forward(inp)
+    pre = wl.ForwardInputs(*[np.ascontiguousarray(getattr(inp, f)[:, :T1]) for f in
+                             ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt")],
+                           inp.A_re, inp.A_im, inp.Dskip, inp.chunk, inp.h0_re, inp.h0_im)
+    d = dev_inputs(pre)
+    _, _, h_re, h_im = cssd.cssd_forward(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"],
+                                         d["C_im"], d["dt"], d["A_re"], d["A_im"], d["Dskip"],
+                                         d["h0"], chunk=32)
+    full = dev_inputs(inp)
+    ys = []
+    for t in range(T1, T):
+        yr_, yi_ = cssd.cssd_step(*(full[k][:, t].contiguous() for k in
+                                    ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt")),
+                                  full["A_re"], full["A_im"], full["Dskip"], h_re, h_im)
+        ys.append(yr_.double().cpu().numpy() + 1j * yi_.double().cpu().numpy())
+    torch.cuda.synchronize()
+    y_dec = np.stack(ys, axis=1)
+    h_dec = h_re.double().cpu().numpy() + 1j * h_im.double().cpu().numpy()
+    yr, hr = oracle_forward(inp)
+    assert rel_err(y_dec, yr[:, T1:]) <= TOL and rel_err(h_dec, hr) <= TOL
+    assert rel_err(y_dec, y_all[:, T1:]) <= TOL and rel_err(h_dec, h_all) <= TOL
