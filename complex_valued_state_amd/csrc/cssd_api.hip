@@ -18,7 +18,9 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool pow2_16_128(int64_t v) { return v == 16 || v == 32 || v == 64 || v == 128; }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t bytes) {
+    return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
 
 // ---------------------------------------------------------------- profiler
 struct Pending {
@@ -150,14 +152,19 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
     if (st != CSSD_OK) return st;
     if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
+    // B and C rows are read as 16-byte (f32) / 8-byte (bf16) vectors, states as
+    // float4; everything else only needs its element alignment.
+    const uintptr_t in_el = in_dtype == CSSD_BF16 ? 2 : 4, in_vec = 4 * in_el;
     const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, y_re, y_im};
-    for (const void* p : req)
-        if (p == nullptr || !aligned16(p)) return CSSD_ERR_INVALID_ARG;
+    const uintptr_t req_al[] = {in_el, in_el, in_vec, in_vec, in_vec, in_vec, 4, 4, 4, 4, 4};
+    for (int i = 0; i < 11; ++i)
+        if (req[i] == nullptr || !aligned(req[i], req_al[i])) return CSSD_ERR_INVALID_ARG;
     if ((h0_re == nullptr) != (h0_im == nullptr)) return CSSD_ERR_INVALID_ARG;
     if ((hT_re == nullptr) != (hT_im == nullptr)) return CSSD_ERR_INVALID_ARG;
     const void* opt[] = {Dskip, h0_re, h0_im, hT_re, hT_im};
-    for (const void* p : opt)
-        if (p != nullptr && !aligned16(p)) return CSSD_ERR_INVALID_ARG;
+    const uintptr_t opt_al[] = {4, 16, 16, 16, 16};
+    for (int i = 0; i < 5; ++i)
+        if (opt[i] != nullptr && !aligned(opt[i], opt_al[i])) return CSSD_ERR_INVALID_ARG;
     const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im};
     const void* outs[] = {y_re, y_im, hT_re, hT_im};
     for (const void* o : outs) {
@@ -222,10 +229,12 @@ int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, co
     const int64_t lim = (int64_t)1 << 31;
     if (batch > lim || nheads > lim || batch * nheads > lim / (headdim * dstate))
         return CSSD_ERR_UNSUPPORTED;
+    // x, the state and y are accessed as float4; B, C, dt, A, Dskip as scalars
     const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, h_re, h_im, y_re, y_im};
-    for (const void* p : req)
-        if (p == nullptr || !aligned16(p)) return CSSD_ERR_INVALID_ARG;
-    if (Dskip != nullptr && !aligned16(Dskip)) return CSSD_ERR_INVALID_ARG;
+    const uintptr_t req_al[] = {16, 16, 4, 4, 4, 4, 4, 4, 4, 16, 16, 16, 16};
+    for (int i = 0; i < 13; ++i)
+        if (req[i] == nullptr || !aligned(req[i], req_al[i])) return CSSD_ERR_INVALID_ARG;
+    if (Dskip != nullptr && !aligned(Dskip, 4)) return CSSD_ERR_INVALID_ARG;
     const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip};
     const void* outs[] = {h_re, h_im, y_re, y_im};
     for (const void* o : outs)

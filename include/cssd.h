@@ -20,8 +20,11 @@
  * ---------------------------------------
  *  - Complex tensors are PLANAR: two separate, contiguous, row-major arrays
  *    (real plane, imaginary plane) of identical shape.  No interleaved data.
- *  - Every array pointer is a DEVICE pointer owned by the caller, 16-byte
- *    aligned, C-contiguous with the shape given in its comment.  The library
+ *  - Every array pointer is a DEVICE pointer owned by the caller, C-contiguous
+ *    with the shape given in its comment, and aligned as follows: arrays read
+ *    or written as vectors (cssd_forward: B_*, C_*, h0_*, hT_*; cssd_step: x_*,
+ *    h_*, y_*) to 16 bytes (8 bytes for bf16 B_*, C_*), every other array to
+ *    its element size.  The library
  *    never allocates, frees or synchronises; all work is enqueued on `stream`
  *    (a hipStream_t passed as void*; NULL = the legacy default stream) and is
  *    complete when that stream is.  Outputs are valid only after that point.

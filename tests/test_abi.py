@@ -111,7 +111,9 @@ def test_forward_validation(lib):
     assert _fwd(lib, ws=0x20000010) == 3                      # misaligned workspace
     assert _fwd(lib, ptrs={"x_re": None}, ws=0x20000000) == 1
     assert _fwd(lib, ptrs={"y_im": None}, ws=0x20000000) == 1
-    assert _fwd(lib, ptrs={"dt": 0x10000004}, ws=0x20000000) == 1  # misaligned
+    assert _fwd(lib, ptrs={"B_im": 0x10000004}, ws=0x20000000) == 1  # misaligned vector operand
+    assert _fwd(lib, ptrs={"dt": 0x10000002}, ws=0x20000000) == 1    # misaligned scalar operand
+    assert _fwd(lib, ptrs={"h0_re": 0x10000008}, ws=0x20000000) == 1
     assert _fwd(lib, ptrs={"h0_im": None}, ws=0x20000000) == 1     # half an initial state
     assert _fwd(lib, ptrs={"hT_re": None}, ws=0x20000000) == 1     # half a final state
     assert _fwd(lib, ptrs={"y_re": 0x10000000}, ws=0x20000000) == 1  # y aliases x
