@@ -31,7 +31,8 @@ METRIC = "complex SSD fwd tokens/s at B8 T2048 H48; % of MFMA/HBM roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
 KERNEL_SRC = {"k_chunk_scan": "k_chunk_scan.hip", "k_chunk_state": "k_chunk_state.hip",
-              "k_state_pass": "k_state_pass.hip", "k_cumsum": "k_cumsum.hip", "k_step": "k_step.hip"}
+              "k_state_pass": "k_state_pass.hip", "k_cumsum": "k_cumsum.hip",
+              "k_step": "k_step.hip"}
 
 
 # ---------------------------------------------------------------------------

@@ -26,7 +26,8 @@
 //  * s-tiles strictly below the diagonal need no mask (s < l0 <= l); only the
 //    diagonal tile applies the causal mask and the padding mask;
 //  * Y_off uses A = exp(acs[l]) C[l, n] (the C rows already in registers) and
-//    B-operand = H_c[n, p] rows.
+//    B-operand = H_c[n, p]; the chunk-state kernel stores H_c in MFMA-fragment
+//    order, so each 16x16 operand tile is one contiguous 1 KB float4 load.
 // A complex product is four real MFMAs: re += ar br - ai bi, im += ar bi + ai br.
 #include "cssd_device.h"
 #include "cssd_launch.h"
@@ -43,8 +44,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
     const float* __restrict__ e_im, const float* __restrict__ hc_re,
     const float* __restrict__ hc_im, float* __restrict__ y_re, float* __restrict__ y_im,
     int64_t T, int H, int nC, int C) {
-    constexpr int NK = N / 16;  // float4 groups of the n axis per lane
-    constexpr int PT = D / 16;  // p column tiles
+    constexpr int NK = N / 16;  // 16-wide tiles of the n axis
+    constexpr int PT = D / 16;  // 16-wide tiles of the p axis
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
     const int lt = threadIdx.x >> 6;
@@ -58,26 +59,39 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
     const int l0 = lt * 16;
     if (l0 >= valid) return;  // tile entirely in the padding: nothing to write
 
+    // wave-uniform bases; per-lane offsets below are 32-bit
     const int64_t row0 = (b * T + t0) * H + h;  // row (b, t0, h); time t0+s is row0 + s*H
+    const typename In::T* __restrict__ xb_r = x_re + row0 * D;
+    const typename In::T* __restrict__ xb_i = x_im + row0 * D;
+    const typename In::T* __restrict__ bb_r = b_re + row0 * N;
+    const typename In::T* __restrict__ bb_i = b_im + row0 * N;
+    const typename In::T* __restrict__ cb_r = c_re + row0 * N;
+    const typename In::T* __restrict__ cb_i = c_im + row0 * N;
+    const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
     const int64_t pbase = bh * (int64_t)nC * C + t0;  // per-position workspace base
+    const double* __restrict__ ab_r = acs_re + pbase;
+    const double* __restrict__ ab_i = acs_im + pbase;
 
     // ---- this lane's readout row l = l0 + li (zero when it is padding)
     const int lrow = l0 + li;
     const bool lok = lrow < valid;
     float4 cre[NK], cim[NK];
     {
-        const int64_t off = (row0 + (int64_t)(lok ? lrow : valid - 1) * H) * N + 4 * g;
+        const uint32_t off = (uint32_t)(lok ? lrow : valid - 1) * sN + 4 * g;
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
-            cre[k] = In::load4(c_re + off + 16 * k);
-            cim[k] = In::load4(c_im + off + 16 * k);
-            if (!lok) {
+            cre[k] = In::load4(cb_r + off + 16 * k);
+            cim[k] = In::load4(cb_i + off + 16 * k);
+        }
+        if (!lok) {
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
                 cre[k] = make_float4(0.f, 0.f, 0.f, 0.f);
                 cim[k] = cre[k];
             }
         }
     }
-    const double alr = acs_re[pbase + lrow], ali = acs_im[pbase + lrow];
+    const double alr = ab_r[lrow], ali = ab_i[lrow];
     const float er = e_re[pbase + lrow], ei = e_im[pbase + lrow];
 
     floatx4 yr[PT], yi[PT];
@@ -87,26 +101,31 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
         yi[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- Y_off = diag(exp(acs)) C H_c : contraction over n
+    // ---- Y_off = diag(exp(acs)) C H_c : contraction over n.  H_c is stored in
+    // MFMA-fragment order: tile (k, pt) is 256 contiguous floats, lane-major.
     {
-        const int64_t hbase = (bh * nC + c) * (int64_t)N * D + li;
+        const float* __restrict__ hb_r = hc_re + (bh * nC + c) * (int64_t)N * D + 4 * lane;
+        const float* __restrict__ hb_i = hc_im + (bh * nC + c) * (int64_t)N * D + 4 * lane;
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
+            floatx4 hr[PT], hi[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                hr[pt] = *reinterpret_cast<const floatx4*>(hb_r + (k * PT + pt) * 256);
+                hi[pt] = *reinterpret_cast<const floatx4*>(hb_i + (k * PT + pt) * 256);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = 16 * k + 4 * g + q;
                 const float cr = f4get(cre[k], q), ci = f4get(cim[k], q);
                 const float ar = er * cr - ei * ci;
                 const float ai = er * ci + ei * cr;
                 const float nai = -ai;
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    const float hr = hc_re[hbase + (int64_t)n * D + pt * 16];
-                    const float hi = hc_im[hbase + (int64_t)n * D + pt * 16];
-                    yr[pt] = mfma4(ar, hr, yr[pt]);
-                    yr[pt] = mfma4(nai, hi, yr[pt]);
-                    yi[pt] = mfma4(ar, hi, yi[pt]);
-                    yi[pt] = mfma4(ai, hr, yi[pt]);
+                    yr[pt] = mfma4(ar, hr[pt][q], yr[pt]);
+                    yr[pt] = mfma4(nai, hi[pt][q], yr[pt]);
+                    yi[pt] = mfma4(ar, hi[pt][q], yi[pt]);
+                    yi[pt] = mfma4(ai, hr[pt][q], yi[pt]);
                 }
             }
         }
@@ -121,24 +140,44 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
         {
             const int srow = s0 + li;
             const bool sok = srow < valid;  // always true off the diagonal
-            const int64_t off = (row0 + (int64_t)(sok ? srow : valid - 1) * H) * N + 4 * g;
+            const uint32_t off = (uint32_t)(sok ? srow : valid - 1) * sN + 4 * g;
+            float4 bre[NK], bim[NK];
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
-                float4 bre = In::load4(b_re + off + 16 * k);
-                float4 bim = In::load4(b_im + off + 16 * k);
-                if (!sok) {
-                    bre = make_float4(0.f, 0.f, 0.f, 0.f);
-                    bim = bre;
+                bre[k] = In::load4(bb_r + off + 16 * k);
+                bim[k] = In::load4(bb_i + off + 16 * k);
+            }
+            if (!sok) {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
+                    bre[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    bim[k] = bre[k];
                 }
+            }
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float br = f4get(bre, q), bi = f4get(bim, q);
+                    const float br = f4get(bre[k], q), bi = f4get(bim[k], q);
                     const float cr = f4get(cre[k], q), ci = f4get(cim[k], q);
                     gr = mfma4(br, cr, gr);
                     gr = mfma4(-bi, ci, gr);
                     gi = mfma4(br, ci, gi);
                     gi = mfma4(bi, cr, gi);
                 }
+            }
+        }
+        // X rows of this s-tile: step r contracts s = s0 + 4g + r
+        float xr[4][PT], xi[4][PT];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = s0 + 4 * g + r;
+            const bool xok = s < valid;
+            const uint32_t xoff = (uint32_t)(xok ? s : valid - 1) * sD + li;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                xr[r][pt] = xok ? In::load1(xb_r + xoff + pt * 16) : 0.f;
+                xi[r][pt] = xok ? In::load1(xb_i + xoff + pt * 16) : 0.f;
             }
         }
         // M = G . L, register r <-> s = s0 + 4g + r, lane row l = lrow
@@ -149,8 +188,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
             const bool keep = !diag || (s <= lrow);
             float lr = 0.f, lim = 0.f;
             if (keep) {
-                const double dre = alr - acs_re[pbase + s];
-                const double dim = wrap_phase(ali - acs_im[pbase + s]);
+                const double dre = alr - ab_r[s];
+                const double dim = wrap_phase(ali - ab_i[s]);
                 const float mag = expf((float)dre);
                 float sn, cs;
                 sincosf((float)dim, &sn, &cs);
@@ -160,42 +199,35 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
             mr[r] = gr[r] * lr - gi[r] * lim;
             mi[r] = gr[r] * lim + gi[r] * lr;
         }
-        // Y += M X : step r contracts s = s0 + 4g + r
+        // Y += M X
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int s = s0 + 4 * g + r;
-            const bool xok = s < valid;
-            const int64_t xoff = (row0 + (int64_t)(xok ? s : valid - 1) * H) * D + li;
             const float nmi = -mi[r];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                float xr = In::load1(x_re + xoff + pt * 16);
-                float xi = In::load1(x_im + xoff + pt * 16);
-                if (!xok) {
-                    xr = 0.f;
-                    xi = 0.f;
-                }
-                yr[pt] = mfma4(mr[r], xr, yr[pt]);
-                yr[pt] = mfma4(nmi, xi, yr[pt]);
-                yi[pt] = mfma4(mr[r], xi, yi[pt]);
-                yi[pt] = mfma4(mi[r], xr, yi[pt]);
+                yr[pt] = mfma4(mr[r], xr[r][pt], yr[pt]);
+                yr[pt] = mfma4(nmi, xi[r][pt], yr[pt]);
+                yi[pt] = mfma4(mr[r], xi[r][pt], yi[pt]);
+                yi[pt] = mfma4(mi[r], xr[r][pt], yi[pt]);
             }
         }
     }
 
     // ---- epilogue: skip term and store; register r <-> row l = l0 + 4g + r
     const float dk = dskip != nullptr ? dskip[h] : 0.f;
+    float* __restrict__ yb_r = y_re + row0 * D;
+    float* __restrict__ yb_i = y_im + row0 * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int l = l0 + 4 * g + r;
         if (l < valid) {
-            const int64_t off = (row0 + (int64_t)l * H) * D + li;
+            const uint32_t off = (uint32_t)l * sD + li;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const float xr = In::load1(x_re + off + pt * 16);
-                const float xi = In::load1(x_im + off + pt * 16);
-                y_re[off + pt * 16] = yr[pt][r] + dk * xr;
-                y_im[off + pt * 16] = yi[pt][r] + dk * xi;
+                const float xv = In::load1(xb_r + off + pt * 16);
+                const float xw = In::load1(xb_i + off + pt * 16);
+                yb_r[off + pt * 16] = yr[pt][r] + dk * xv;
+                yb_i[off + pt * 16] = yi[pt][r] + dk * xw;
             }
         }
     }

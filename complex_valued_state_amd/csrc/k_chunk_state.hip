@@ -1,30 +1,36 @@
 // K3: per-chunk end states, as a complex GEMM on the fp32 matrix cores.
 //
-//   S_c[n, p] = sum_l  B[l, n] * w[l] * X[l, p],   w[l] = exp(acs[C-1] - acs[l])
+//   S_c[n, p] = sum_l  w[l] B[l, n] X[l, p],   w[l] = exp(acs[C-1] - acs[l])
 //
-// i.e. S_c = (diag(w) B)^T X, the state a chunk would leave behind if it
+// i.e. S_c = (diag(w) B)^T X, the state chunk c would leave behind if it
 // started from zero (Mamba-3-Lite docs, "SSD Theory" 4.5, and "The Chunkwise
-// Complex SSD Algorithm" 4.5, first einsum).  Padded positions contribute
-// nothing.
+// Complex SSD Algorithm" 4.5, the per-chunk states einsum).  Padded positions
+// of a partial last chunk contribute nothing.
 //
-// Mapping: one workgroup per chunk, one wave per 16-row tile of n; each wave
-// owns all D/16 column tiles of p.  The contraction index is time l: step j of
-// the 16x16x4 MFMA contracts l = 4j + g, where g = lane/16.  A complex product
-// is four real MFMAs (re*re - im*im, re*im + im*re); the weight w is folded into
-// B on the vector ALU before the MFMA.  Both operands are read with lane%16
-// running along the contiguous axis (n for B, p for X), so every load of a
-// 16-lane group is one contiguous 64-byte row segment.
+// Mapping: one workgroup per chunk, one wave per 16-row tile nt of n; each wave
+// owns all D/16 column tiles of p (accumulators).  Step j of the 16x16x4 MFMA
+// contracts time l = (C/4) g + j (g = lane/16), so each lane's C/4 weights w are
+// contiguous and load as float4; B and X operands are read with lane%16 along
+// their contiguous axis (one 64-byte row segment per 16-lane group).  A complex
+// product is four real MFMAs; w is folded into B on the vector ALU.
+//
+// S_c is written in MFMA-fragment order: within the N x D block of one
+// (b, h, c), element (n, p) sits at
+//   (((n/16) * (D/16) + p/16) * 4 + (n%16)/4) * 64 + (p%16) * 4 + n%4
+// so each accumulator tile is one contiguous 1 KB float4 store, and the output
+// kernel later reads the carry-in states back the same way.
 #include "cssd_device.h"
 #include "cssd_launch.h"
 
 namespace cssd {
 
-template <typename In, int N, int D>
-__global__ __launch_bounds__(4 * N) void k_chunk_state(
+template <typename In, int C, int D>
+__global__ __launch_bounds__(512) void k_chunk_state(
     const typename In::T* __restrict__ x_re, const typename In::T* __restrict__ x_im,
     const typename In::T* __restrict__ b_re, const typename In::T* __restrict__ b_im,
     const float* __restrict__ w_re, const float* __restrict__ w_im, float* __restrict__ st_re,
-    float* __restrict__ st_im, int64_t T, int H, int nC, int C) {
+    float* __restrict__ st_im, int64_t T, int H, int N, int nC) {
+    constexpr int KJ = C / 4;   // MFMA k-steps per chunk
     constexpr int PT = D / 16;  // column tiles (p)
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
@@ -37,11 +43,26 @@ __global__ __launch_bounds__(4 * N) void k_chunk_state(
     const int64_t t0 = (int64_t)c * C;
     const int valid = (int)min<int64_t>((int64_t)C, T - t0);
 
-    // row (b, t0, h) bases; consecutive time steps are H*N (H*D) elements apart
-    const int64_t rowB = ((b * T + t0) * H + h) * (int64_t)N + nt * 16 + li;
-    const int64_t rowX = ((b * T + t0) * H + h) * (int64_t)D + li;
-    const int64_t strideB = (int64_t)H * N, strideX = (int64_t)H * D;
-    const int64_t wbase = bh * (int64_t)nC * C + t0;
+    // wave-uniform bases; consecutive time steps are H*N (H*D) elements apart
+    const int64_t row0 = (b * T + t0) * H + h;
+    const typename In::T* __restrict__ bb_r = b_re + row0 * N + nt * 16 + li;
+    const typename In::T* __restrict__ bb_i = b_im + row0 * N + nt * 16 + li;
+    const typename In::T* __restrict__ xb_r = x_re + row0 * D + li;
+    const typename In::T* __restrict__ xb_i = x_im + row0 * D + li;
+    const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
+
+    float wr[KJ], wi[KJ];
+    {
+        const float* wpr = w_re + bh * (int64_t)nC * C + t0 + KJ * g;
+        const float* wpi = w_im + bh * (int64_t)nC * C + t0 + KJ * g;
+#pragma unroll
+        for (int j = 0; j < KJ; j += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(wpr + j);
+            const float4 e = *reinterpret_cast<const float4*>(wpi + j);
+            wr[j] = a.x; wr[j + 1] = a.y; wr[j + 2] = a.z; wr[j + 3] = a.w;
+            wi[j] = e.x; wi[j + 1] = e.y; wi[j + 2] = e.z; wi[j + 3] = e.w;
+        }
+    }
 
     floatx4 sr[PT], si[PT];
 #pragma unroll
@@ -50,21 +71,28 @@ __global__ __launch_bounds__(4 * N) void k_chunk_state(
         si[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-#pragma unroll 4
-    for (int j = 0; j < C / 4; ++j) {
-        const int l = 4 * j + g;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+        const int l = KJ * g + j;
         const bool ok = l < valid;
-        const int lc = ok ? l : valid - 1;  // clamped row: always in bounds
-        const float br = ok ? In::load1(b_re + rowB + lc * strideB) : 0.f;
-        const float bi = ok ? In::load1(b_im + rowB + lc * strideB) : 0.f;
-        const float wr = w_re[wbase + l], wi = w_im[wbase + l];
-        const float pr = wr * br - wi * bi;  // (w B)[l, n]
-        const float pi = wr * bi + wi * br;
+        const uint32_t lc = (uint32_t)(ok ? l : valid - 1);  // clamped row: in bounds
+        float br = In::load1(bb_r + lc * sN);
+        float bi = In::load1(bb_i + lc * sN);
+        if (!ok) {
+            br = 0.f;
+            bi = 0.f;
+        }
+        const float pr = wr[j] * br - wi[j] * bi;  // (w B)[l, n]
+        const float pi = wr[j] * bi + wi[j] * br;
         const float npi = -pi;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const float xr = ok ? In::load1(x_re + rowX + lc * strideX + pt * 16) : 0.f;
-            const float xi = ok ? In::load1(x_im + rowX + lc * strideX + pt * 16) : 0.f;
+            float xr = In::load1(xb_r + lc * sD + pt * 16);
+            float xi = In::load1(xb_i + lc * sD + pt * 16);
+            if (!ok) {
+                xr = 0.f;
+                xi = 0.f;
+            }
             sr[pt] = mfma4(pr, xr, sr[pt]);
             sr[pt] = mfma4(npi, xi, sr[pt]);
             si[pt] = mfma4(pr, xi, si[pt]);
@@ -72,29 +100,26 @@ __global__ __launch_bounds__(4 * N) void k_chunk_state(
         }
     }
 
-    // accumulator register r of lane (li + 16 g) is S[n = nt*16 + 4g + r][p = pt*16 + li]
-    const int64_t sbase = (bh * nC + c) * (int64_t)N * D;
+    // accumulator tile (nt, pt) -> 256 contiguous floats, lane-major
+    const int64_t blk = (bh * nC + c) * (int64_t)N * D + 4 * lane;
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t off = sbase + (int64_t)(nt * 16 + 4 * g + r) * D + pt * 16 + li;
-            st_re[off] = sr[pt][r];
-            st_im[off] = si[pt][r];
-        }
+        const int64_t off = blk + (int64_t)(nt * PT + pt) * 256;
+        *reinterpret_cast<floatx4*>(st_re + off) = sr[pt];
+        *reinterpret_cast<floatx4*>(st_im + off) = si[pt];
     }
 }
 
-template <typename In, int N>
-static void dispatch_d(const FwdArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.B * a.H * a.nC)), block(4 * N);
+template <typename In, int C>
+static void launch_d(const FwdArgs& a, hipStream_t s) {
     const auto* xr = static_cast<const typename In::T*>(a.x_re);
     const auto* xi = static_cast<const typename In::T*>(a.x_im);
     const auto* br = static_cast<const typename In::T*>(a.b_re);
     const auto* bi = static_cast<const typename In::T*>(a.b_im);
+    const dim3 grid((unsigned)(a.B * a.H * a.nC)), block((unsigned)(4 * a.N));
 #define CSSD_K3(DD)                                                                            \
-    hipLaunchKernelGGL((k_chunk_state<In, N, DD>), grid, block, 0, s, xr, xi, br, bi, a.w_re,  \
-                       a.w_im, a.st_re, a.st_im, a.T, (int)a.H, (int)a.nC, (int)a.C)
+    hipLaunchKernelGGL((k_chunk_state<In, C, DD>), grid, block, 0, s, xr, xi, br, bi, a.w_re,  \
+                       a.w_im, a.st_re, a.st_im, a.T, (int)a.H, (int)a.N, (int)a.nC)
     switch (a.D) {
         case 16: CSSD_K3(16); break;
         case 32: CSSD_K3(32); break;
@@ -105,20 +130,20 @@ static void dispatch_d(const FwdArgs& a, hipStream_t s) {
 }
 
 template <typename In>
-static void dispatch_n(const FwdArgs& a, hipStream_t s) {
-    switch (a.N) {
-        case 16: dispatch_d<In, 16>(a, s); break;
-        case 32: dispatch_d<In, 32>(a, s); break;
-        case 64: dispatch_d<In, 64>(a, s); break;
-        default: dispatch_d<In, 128>(a, s); break;
+static void launch_c(const FwdArgs& a, hipStream_t s) {
+    switch (a.C) {
+        case 16: launch_d<In, 16>(a, s); break;
+        case 32: launch_d<In, 32>(a, s); break;
+        case 64: launch_d<In, 64>(a, s); break;
+        default: launch_d<In, 128>(a, s); break;
     }
 }
 
 hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t stream) {
     if (a.in_dtype == 1)
-        dispatch_n<InBF16>(a, stream);
+        launch_c<InBF16>(a, stream);
     else
-        dispatch_n<InF32>(a, stream);
+        launch_c<InF32>(a, stream);
     return hipGetLastError();
 }
 

@@ -11,9 +11,11 @@
 // sequential form: the einsum variant on the page aligns the decay one chunk
 // late when chunk totals differ (its own "Pitfalls" section).
 //
-// The state buffer holds S_c on entry and is overwritten in place with H_c,
-// the carry-in state chunk c's output combine reads.  Memory-bound: one thread
-// owns four consecutive (n, p) elements of one (b, h) and walks the chunks,
+// The state buffer holds S_c on entry (MFMA-fragment order, see the
+// chunk-state kernel) and is overwritten in place with H_c, the carry-in state
+// the output kernel reads; the pass is elementwise, so it walks the buffer in
+// that order.  Only h0 and hT use the caller's (B,H,N,D) layout.  Memory-bound:
+// one thread owns four state elements of one (b, h) and walks the chunks,
 // issuing the loads of U chunks before their dependent updates so that several
 // loads are in flight per thread.
 #include "cssd_device.h"
@@ -25,19 +27,28 @@ __global__ __launch_bounds__(256) void k_state_pass(float4* __restrict__ st_re,
                                                     float4* __restrict__ st_im,
                                                     const float* __restrict__ cd_re,
                                                     const float* __restrict__ cd_im,
-                                                    const float4* __restrict__ h0_re,
-                                                    const float4* __restrict__ h0_im,
-                                                    float4* __restrict__ hT_re,
-                                                    float4* __restrict__ hT_im, int64_t total,
-                                                    int nd4, int nC) {
+                                                    const float* __restrict__ h0_re,
+                                                    const float* __restrict__ h0_im,
+                                                    float* __restrict__ hT_re,
+                                                    float* __restrict__ hT_im, int64_t total,
+                                                    int N, int D, int nC) {
     const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (tid >= total) return;
+    const int nd4 = N * D / 4;
     const int64_t bh = tid / nd4;
     const int e = (int)(tid % nd4);
+    // fragment coordinates of this float4: rows n = 16 nt + 4 g + q (q = 0..3), column p
+    const int li = e & 15, g = (e >> 4) & 3, tile = e >> 6;
+    const int PT = D / 16;
+    const int nt = tile / PT, pt = tile % PT;
+    const int64_t sbase = (bh * N + nt * 16 + 4 * g) * (int64_t)D + pt * 16 + li;
+
     float4 hr = make_float4(0.f, 0.f, 0.f, 0.f), hi = hr;
     if (h0_re != nullptr) {
-        hr = h0_re[tid];
-        hi = h0_im[tid];
+        hr = make_float4(h0_re[sbase], h0_re[sbase + D], h0_re[sbase + 2 * D],
+                         h0_re[sbase + 3 * D]);
+        hi = make_float4(h0_im[sbase], h0_im[sbase + D], h0_im[sbase + 2 * D],
+                         h0_im[sbase + 3 * D]);
     }
     const int64_t base = bh * (int64_t)nC * nd4 + e;
     constexpr int U = 8;
@@ -72,21 +83,19 @@ __global__ __launch_bounds__(256) void k_state_pass(float4* __restrict__ st_re,
         }
     }
     if (hT_re != nullptr) {
-        hT_re[tid] = hr;
-        hT_im[tid] = hi;
+        hT_re[sbase] = hr.x; hT_re[sbase + D] = hr.y;
+        hT_re[sbase + 2 * D] = hr.z; hT_re[sbase + 3 * D] = hr.w;
+        hT_im[sbase] = hi.x; hT_im[sbase + D] = hi.y;
+        hT_im[sbase + 2 * D] = hi.z; hT_im[sbase + 3 * D] = hi.w;
     }
 }
 
 hipError_t launch_state_pass(const FwdArgs& a, hipStream_t stream) {
-    const int nd4 = (int)(a.N * a.D / 4);
-    const int64_t total = a.B * a.H * nd4;
+    const int64_t total = a.B * a.H * (a.N * a.D / 4);
     const dim3 grid((unsigned)((total + 255) / 256)), block(256);
     hipLaunchKernelGGL(k_state_pass, grid, block, 0, stream, reinterpret_cast<float4*>(a.st_re),
-                       reinterpret_cast<float4*>(a.st_im), a.cd_re, a.cd_im,
-                       reinterpret_cast<const float4*>(a.h0_re),
-                       reinterpret_cast<const float4*>(a.h0_im),
-                       reinterpret_cast<float4*>(a.hT_re), reinterpret_cast<float4*>(a.hT_im),
-                       total, nd4, (int)a.nC);
+                       reinterpret_cast<float4*>(a.st_im), a.cd_re, a.cd_im, a.h0_re, a.h0_im,
+                       a.hT_re, a.hT_im, total, (int)a.N, (int)a.D, (int)a.nC);
     return hipGetLastError();
 }
 

@@ -89,8 +89,13 @@ const char *cssd_status_string(int status);
  *   e_re,  e_im    : float  [B][H][P]     exp(acs[l])
  *   w_re,  w_im    : float  [B][H][P]     exp(acs[C-1] - acs[l])
  *   cd_re, cd_im   : float  [B][H][nC]    exp(acs[C-1]) (chunk decay)
- *   st_re, st_im   : float  [B][H][nC][N][D]  chunk end states S_c, replaced
+ *   st_re, st_im   : float  [B][H][nC][N*D]  chunk end states S_c, replaced
  *                                         in place by the carry-in states H_c
+ *                                         (the state after step cC-1); each
+ *                                         N x D block in MFMA-fragment order:
+ *                                         element (n, p) at
+ *                                         (((n/16)(D/16) + p/16)*4 + (n%16)/4)*64
+ *                                         + (p%16)*4 + n%4
  * Returns CSSD_OK, CSSD_ERR_INVALID_ARG (null bytes / non-positive size) or
  * CSSD_ERR_UNSUPPORTED.
  */

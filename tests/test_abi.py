@@ -68,7 +68,7 @@ def test_workspace_size_layout(lib):
     P = B * H * nC * C
     want = 0
     for nbytes in (8 * P, 8 * P, 4 * P, 4 * P, 4 * P, 4 * P, 4 * B * H * nC, 4 * B * H * nC,
-                   4 * B * H * nC * N * D, 4 * B * H * nC * N * D):
+                   4 * B * H * nC * N * D, 4 * B * H * nC * N * D):  # acs, e, w, cd, S_c/H_c
         want = _align(want + nbytes)
     assert got == want
 
