@@ -7,7 +7,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/cssd.h"
+#include "cssd.h"
 #include "cssd_launch.h"
 
 namespace {

@@ -8,8 +8,8 @@ namespace cssd {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+constexpr double kLog2e = 1.4426950408889634073599246810019;
 
 // One 16x16x4 fp32 matrix-core step: acc += A(16x4) * B(4x16).
 // Lane layout (wave64): lane = i + 16*k holds A[i][k] and B[k][j=i];
@@ -18,13 +18,65 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// Complex multiply-accumulate of 16x16 tiles with three real MFMA products
+// (Gauss): t1 += ar br, t2 += ai bi, t3 += (ar + ai)(br + bi); then
+// re = t1 - t2 and im = t3 - t1 - t2.  The caller passes the operand sums.
+struct CTile {
+    floatx4 t1, t2, t3;
+};
+__device__ __forceinline__ void ctile_zero(CTile& a) {
+    a.t1 = floatx4{0.f, 0.f, 0.f, 0.f};
+    a.t2 = a.t1;
+    a.t3 = a.t1;
+}
+__device__ __forceinline__ void ctile_mac(CTile& a, float ar, float ai, float as, float br,
+                                          float bi, float bs) {
+    a.t1 = mfma4(ar, br, a.t1);
+    a.t2 = mfma4(ai, bi, a.t2);
+    a.t3 = mfma4(as, bs, a.t3);
+}
+__device__ __forceinline__ float ctile_re(const CTile& a, int r) { return a.t1[r] - a.t2[r]; }
+__device__ __forceinline__ float ctile_im(const CTile& a, int r) {
+    return a.t3[r] - a.t1[r] - a.t2[r];
+}
+
+// exp(re + i im) for an increment given in log2 units (re2 = re / ln 2) and in
+// turns (rev = im / 2 pi, already reduced to [-1/2, 1/2]), on the hardware
+// transcendental units: v_exp_f32 computes 2^x, v_sin_f32 / v_cos_f32 take turns.
+__device__ __forceinline__ void cexp_scaled(float re2, float rev, float& out_re, float& out_im) {
+    const float mag = __builtin_amdgcn_exp2f(re2);
+    out_re = mag * __builtin_amdgcn_cosf(rev);
+    out_im = mag * __builtin_amdgcn_sinf(rev);
+}
+
+// Index of this wave in its workgroup, as a value the compiler knows is
+// wave-uniform (so that everything derived from it lives in scalar registers).
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ double softplus_f64(double v) {
     return fmax(v, 0.0) + log1p(exp(-fabs(v)));
 }
 
-// Wrap a phase (radians) into [-pi, pi] in fp64 before it is narrowed to fp32.
-__device__ __forceinline__ double wrap_phase(double v) {
-    return v - kTwoPi * rint(v * kInvTwoPi);
+// ----------------------------------------------------------------------------
+// Raw buffer accesses: a wave-uniform base and extent in SGPRs, 32-bit per-lane
+// element offsets.  A read at or beyond the extent returns 0 and a write there
+// is dropped, which is how the kernels mask the padded rows of a partial chunk.
+// ----------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ __forceinline__ BufRes make_buf(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ float buf_f32(BufRes r, uint32_t elem) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, elem * 4u, 0, 0));
+}
+__device__ __forceinline__ floatx4 buf_f32x4(BufRes r, uint32_t elem) {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4u, 0, 0));
+}
+__device__ __forceinline__ void buf_store_f32(float v, BufRes r, uint32_t elem) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, elem * 4u, 0, 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -35,6 +87,11 @@ struct InF32 {
     __device__ __forceinline__ static float load1(const float* p) { return *p; }
     __device__ __forceinline__ static float4 load4(const float* p) {
         return *reinterpret_cast<const float4*>(p);
+    }
+    // buffer forms (element offsets), see make_buf
+    __device__ __forceinline__ static float bload1(BufRes r, uint32_t e) { return buf_f32(r, e); }
+    __device__ __forceinline__ static floatx4 bload4(BufRes r, uint32_t e) {
+        return buf_f32x4(r, e);
     }
 };
 
@@ -48,6 +105,15 @@ struct InBF16 {
         uint2 v = *reinterpret_cast<const uint2*>(p);
         return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    }
+    __device__ __forceinline__ static float bload1(BufRes r, uint32_t e) {
+        return cvt(__builtin_amdgcn_raw_buffer_load_b16(r, e * 2u, 0, 0));
+    }
+    __device__ __forceinline__ static floatx4 bload4(BufRes r, uint32_t e) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, e * 2u, 0, 0));
+        return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                       __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
     }
 };
 

@@ -11,8 +11,10 @@
 // owns all D/16 column tiles of p (accumulators).  Step j of the 16x16x4 MFMA
 // contracts time l = (C/4) g + j (g = lane/16), so each lane's C/4 weights w are
 // contiguous and load as float4; B and X operands are read with lane%16 along
-// their contiguous axis (one 64-byte row segment per 16-lane group).  A complex
-// product is four real MFMAs; w is folded into B on the vector ALU.
+// their contiguous axis (one 64-byte row segment per 16-lane group), and the
+// operands of the next DIST k-steps are loaded into a register ring before the
+// current step's MFMAs are issued, so memory latency overlaps the matrix work.
+// A complex product is four real MFMAs; w is folded into B on the vector ALU.
 //
 // S_c is written in MFMA-fragment order: within the N x D block of one
 // (b, h, c), element (n, p) sits at
@@ -32,9 +34,15 @@ __global__ __launch_bounds__(512) void k_chunk_state(
     float* __restrict__ st_im, int64_t T, int H, int N, int nC) {
     constexpr int KJ = C / 4;   // MFMA k-steps per chunk
     constexpr int PT = D / 16;  // column tiles (p)
+    // operands of DIST future k-steps are kept in flight (register ring)
+#ifndef CSSD_K3_DIST
+#define CSSD_K3_DIST 4
+#endif
+    constexpr int DW = PT <= 4 ? CSSD_K3_DIST : CSSD_K3_DIST / 2;
+    constexpr int DIST = DW < KJ ? DW : KJ;
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
-    const int nt = threadIdx.x >> 6;  // n tile of this wave
+    const int nt = wave_id();  // n tile of this wave
     const int64_t chunk = blockIdx.x;
     const int c = (int)(chunk % nC);
     const int64_t bh = chunk / nC;
@@ -50,6 +58,26 @@ __global__ __launch_bounds__(512) void k_chunk_state(
     const typename In::T* __restrict__ xb_r = x_re + row0 * D + li;
     const typename In::T* __restrict__ xb_i = x_im + row0 * D + li;
     const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
+
+    struct Ops {
+        float br, bi, xr[PT], xi[PT];
+    };
+    // rows past the end of a partial chunk are clamped (in bounds) and zeroed later
+    auto load = [&](int j, Ops& o) {
+        const int l = KJ * g + j;
+        const uint32_t lc = (uint32_t)(l < valid ? l : valid - 1);
+        o.br = In::load1(bb_r + lc * sN);
+        o.bi = In::load1(bb_i + lc * sN);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            o.xr[pt] = In::load1(xb_r + lc * sD + pt * 16);
+            o.xi[pt] = In::load1(xb_i + lc * sD + pt * 16);
+        }
+    };
+
+    Ops ring[DIST];
+#pragma unroll
+    for (int j = 0; j < DIST; ++j) load(j, ring[j]);
 
     float wr[KJ], wi[KJ];
     {
@@ -68,31 +96,22 @@ __global__ __launch_bounds__(512) void k_chunk_state(
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
         sr[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        si[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        si[pt] = sr[pt];
     }
 
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
-        const int l = KJ * g + j;
-        const bool ok = l < valid;
-        const uint32_t lc = (uint32_t)(ok ? l : valid - 1);  // clamped row: in bounds
-        float br = In::load1(bb_r + lc * sN);
-        float bi = In::load1(bb_i + lc * sN);
-        if (!ok) {
-            br = 0.f;
-            bi = 0.f;
-        }
+        Ops o = ring[j % DIST];
+        if (j + DIST < KJ) load(j + DIST, ring[j % DIST]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool ok = KJ * g + j < valid;
+        const float br = ok ? o.br : 0.f, bi = ok ? o.bi : 0.f;
         const float pr = wr[j] * br - wi[j] * bi;  // (w B)[l, n]
         const float pi = wr[j] * bi + wi[j] * br;
         const float npi = -pi;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            float xr = In::load1(xb_r + lc * sD + pt * 16);
-            float xi = In::load1(xb_i + lc * sD + pt * 16);
-            if (!ok) {
-                xr = 0.f;
-                xi = 0.f;
-            }
+            const float xr = ok ? o.xr[pt] : 0.f, xi = ok ? o.xi[pt] : 0.f;
             sr[pt] = mfma4(pr, xr, sr[pt]);
             sr[pt] = mfma4(npi, xi, sr[pt]);
             si[pt] = mfma4(pr, xi, si[pt]);

@@ -2,7 +2,10 @@
 //
 // For every (batch b, head h, chunk c) and intra-chunk position l:
 //   A_log[l]  = softplus(dt[b, cC+l, h]) * A[h]        (0 on padded positions l >= T - cC)
-//   acs[l]    = sum_{u <= l} A_log[u]                  (inclusive, restarts at every chunk)
+//   acs[l]    = sum_{u <= l} A_log[u]                  (inclusive, restarts at every chunk;
+//                                                      stored as Re/ln2 and Im/2pi: log2 units
+//                                                      and turns, ready for exp2 and sin/cos
+//                                                      of turns in the output kernel)
 //   e[l]      = exp(acs[l])                            readout decay from the chunk start
 //   w[l]      = exp(acs[C-1] - acs[l])                 decay from l to the chunk end
 //   cd        = exp(acs[C-1])                          whole-chunk decay
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(256) void k_cumsum(const float* __restrict__ dt,
                                                 float* __restrict__ w_re, float* __restrict__ w_im,
                                                 float* __restrict__ cd_re,
                                                 float* __restrict__ cd_im) {
-    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t unit = (int64_t)blockIdx.x * 4 + wave_id();
     if (unit >= units) return;  // wave-uniform
     const int lane = threadIdx.x & 63;
     const int c = (int)(unit % nC);
@@ -95,8 +98,8 @@ __global__ __launch_bounds__(256) void k_cumsum(const float* __restrict__ dt,
     for (int j = 0; j < PER; ++j) {
         const int l = lane * PER + j;
         if (l < C) {
-            acs_re[base + l] = vr[j];
-            acs_im[base + l] = vi[j];
+            acs_re[base + l] = vr[j] * kLog2e;
+            acs_im[base + l] = vi[j] * kInvTwoPi;
             double sn, cs;
             sincos(vi[j], &sn, &cs);
             const double m = exp(vr[j]);

@@ -85,7 +85,8 @@ const char *cssd_status_string(int status);
  * aligned, in this order; a caller may read it after the stream completes):
  *   acs_re, acs_im : double [B][H][P]     inclusive chunk-local cumsum of
  *                                         softplus(dt)*A (0 increments on
- *                                         padded positions)
+ *                                         padded positions), real part in log2
+ *                                         units (/ln 2), imaginary in turns (/2pi)
  *   e_re,  e_im    : float  [B][H][P]     exp(acs[l])
  *   w_re,  w_im    : float  [B][H][P]     exp(acs[C-1] - acs[l])
  *   cd_re, cd_im   : float  [B][H][nC]    exp(acs[C-1]) (chunk decay)
