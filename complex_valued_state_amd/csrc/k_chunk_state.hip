@@ -11,10 +11,12 @@
 // owns all D/16 column tiles of p (accumulators).  Step j of the 16x16x4 MFMA
 // contracts time l = (C/4) g + j (g = lane/16), so each lane's C/4 weights w are
 // contiguous and load as float4; B and X operands are read with lane%16 along
-// their contiguous axis (one 64-byte row segment per 16-lane group), and the
-// operands of the next DIST k-steps are loaded into a register ring before the
-// current step's MFMAs are issued, so memory latency overlaps the matrix work.
-// A complex product is four real MFMAs; w is folded into B on the vector ALU.
+// their contiguous axis (one 64-byte row segment per 16-lane group), through
+// raw buffer descriptors whose extent ends at the chunk's last real row (padded
+// rows read as zero, no masks); the operands of the next DIST k-steps are loaded
+// into a register ring before the current step's MFMAs are issued, so memory
+// latency overlaps the matrix work.  w is folded into B on the vector ALU.  A
+// complex product is three real MFMAs (Gauss: ar br, ai bi, (ar + ai)(br + bi)).
 //
 // S_c is written in MFMA-fragment order: within the N x D block of one
 // (b, h, c), element (n, p) sits at
@@ -32,6 +34,7 @@ __global__ __launch_bounds__(512) void k_chunk_state(
     const typename In::T* __restrict__ b_re, const typename In::T* __restrict__ b_im,
     const float* __restrict__ w_re, const float* __restrict__ w_im, float* __restrict__ st_re,
     float* __restrict__ st_im, int64_t T, int H, int N, int nC) {
+    typedef typename In::T TI;
     constexpr int KJ = C / 4;   // MFMA k-steps per chunk
     constexpr int PT = D / 16;  // column tiles (p)
     // operands of DIST future k-steps are kept in flight (register ring)
@@ -51,27 +54,28 @@ __global__ __launch_bounds__(512) void k_chunk_state(
     const int64_t t0 = (int64_t)c * C;
     const int valid = (int)min<int64_t>((int64_t)C, T - t0);
 
-    // wave-uniform bases; consecutive time steps are H*N (H*D) elements apart
+    // per-chunk buffer views whose extent ends at the last real row: rows of a
+    // partial chunk past it read as zero.  Consecutive time steps are H*N (H*D)
+    // elements apart.
     const int64_t row0 = (b * T + t0) * H + h;
-    const typename In::T* __restrict__ bb_r = b_re + row0 * N + nt * 16 + li;
-    const typename In::T* __restrict__ bb_i = b_im + row0 * N + nt * 16 + li;
-    const typename In::T* __restrict__ xb_r = x_re + row0 * D + li;
-    const typename In::T* __restrict__ xb_i = x_im + row0 * D + li;
     const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
+    const uint32_t extN = (uint32_t)(valid - 1) * sN + N, extD = (uint32_t)(valid - 1) * sD + D;
+    const BufRes rb_r = make_buf(b_re + row0 * N, extN * sizeof(TI));
+    const BufRes rb_i = make_buf(b_im + row0 * N, extN * sizeof(TI));
+    const BufRes rx_r = make_buf(x_re + row0 * D, extD * sizeof(TI));
+    const BufRes rx_i = make_buf(x_im + row0 * D, extD * sizeof(TI));
 
     struct Ops {
         float br, bi, xr[PT], xi[PT];
     };
-    // rows past the end of a partial chunk are clamped (in bounds) and zeroed later
     auto load = [&](int j, Ops& o) {
-        const int l = KJ * g + j;
-        const uint32_t lc = (uint32_t)(l < valid ? l : valid - 1);
-        o.br = In::load1(bb_r + lc * sN);
-        o.bi = In::load1(bb_i + lc * sN);
+        const uint32_t l = (uint32_t)(KJ * g + j);
+        o.br = In::bload1(rb_r, l * sN + nt * 16 + li);
+        o.bi = In::bload1(rb_i, l * sN + nt * 16 + li);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            o.xr[pt] = In::load1(xb_r + lc * sD + pt * 16);
-            o.xi[pt] = In::load1(xb_i + lc * sD + pt * 16);
+            o.xr[pt] = In::bload1(rx_r, l * sD + pt * 16 + li);
+            o.xi[pt] = In::bload1(rx_i, l * sD + pt * 16 + li);
         }
     };
 
@@ -92,31 +96,21 @@ __global__ __launch_bounds__(512) void k_chunk_state(
         }
     }
 
-    floatx4 sr[PT], si[PT];
+    CTile acc[PT];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-        sr[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        si[pt] = sr[pt];
-    }
+    for (int pt = 0; pt < PT; ++pt) ctile_zero(acc[pt]);
 
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
         Ops o = ring[j % DIST];
         if (j + DIST < KJ) load(j + DIST, ring[j % DIST]);
         __builtin_amdgcn_sched_barrier(0);
-        const bool ok = KJ * g + j < valid;
-        const float br = ok ? o.br : 0.f, bi = ok ? o.bi : 0.f;
-        const float pr = wr[j] * br - wi[j] * bi;  // (w B)[l, n]
-        const float pi = wr[j] * bi + wi[j] * br;
-        const float npi = -pi;
+        const float pr = wr[j] * o.br - wi[j] * o.bi;  // (w B)[l, n]
+        const float pi = wr[j] * o.bi + wi[j] * o.br;
+        const float ps = pr + pi;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const float xr = ok ? o.xr[pt] : 0.f, xi = ok ? o.xi[pt] : 0.f;
-            sr[pt] = mfma4(pr, xr, sr[pt]);
-            sr[pt] = mfma4(npi, xi, sr[pt]);
-            si[pt] = mfma4(pr, xi, si[pt]);
-            si[pt] = mfma4(pi, xr, si[pt]);
-        }
+        for (int pt = 0; pt < PT; ++pt)
+            ctile_mac(acc[pt], pr, pi, ps, o.xr[pt], o.xi[pt], o.xr[pt] + o.xi[pt]);
     }
 
     // accumulator tile (nt, pt) -> 256 contiguous floats, lane-major
@@ -124,8 +118,14 @@ __global__ __launch_bounds__(512) void k_chunk_state(
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
         const int64_t off = blk + (int64_t)(nt * PT + pt) * 256;
-        *reinterpret_cast<floatx4*>(st_re + off) = sr[pt];
-        *reinterpret_cast<floatx4*>(st_im + off) = si[pt];
+        floatx4 vr, vi;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vr[r] = ctile_re(acc[pt], r);
+            vi[r] = ctile_im(acc[pt], r);
+        }
+        *reinterpret_cast<floatx4*>(st_re + off) = vr;
+        *reinterpret_cast<floatx4*>(st_im + off) = vi;
     }
 }
 
