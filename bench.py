@@ -30,13 +30,16 @@ sys.path.insert(0, ROOT)
 METRIC = "complex SSD fwd tokens/s at B8 T2048 H48; % of MFMA/HBM roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
-KERNEL_SRC = {"k_chunk_scan": "k_chunk_scan.hip", "k_chunk_state": "k_chunk_state.hip",
-              "k_state_pass": "k_state_pass.hip", "k_cumsum": "k_cumsum.hip",
-              "k_step": "k_step.hip"}
+# source files that make up each kernel (besides the shared device/launch headers)
+KERNEL_SRC = {"k_chunk_scan": ("k_chunk_scan.h", "k_chunk_scan.hip", "k_chunk_scan_c16.hip",
+                               "k_chunk_scan_c32.hip", "k_chunk_scan_c64.hip",
+                               "k_chunk_scan_c128.hip"),
+              "k_chunk_state": ("k_chunk_state.hip",), "k_state_pass": ("k_state_pass.hip",),
+              "k_cumsum": ("k_cumsum.hip",), "k_step": ("k_step.hip",)}
 
 
 # ---------------------------------------------------------------------------
-# algorithmic work ("Measurement")
+# algorithmic work: what the method must read, write and multiply, not what the kernels do
 # ---------------------------------------------------------------------------
 def chunk_scan_flops(B, T, H, D, N, C):
     """Real flops one k_chunk_scan launch must do: per chunk, the causal score
@@ -65,10 +68,10 @@ def decode_hbm_bytes(B, H, D, N):
 
 
 def src_hash(name):
-    p = os.path.join(ROOT, "complex_valued_state_amd", "csrc", KERNEL_SRC[name])
+    d = os.path.join(ROOT, "complex_valued_state_amd", "csrc")
     h = hashlib.sha256()
-    for f in (p, os.path.join(ROOT, "complex_valued_state_amd", "csrc", "cssd_device.h")):
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SRC[name] + ("cssd_device.h", "cssd_launch.h"):
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -219,8 +222,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
-              "multi-GPU sharding is described in DESIGN.md but not implemented", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -28,8 +28,7 @@
  *  - burn-mamba docs, module "step_constant": the readout adds a skip term
  *    D x to C^T h.
  *
- * Readings where the pages leave a step open (each is listed in the design
- * notes): y is returned as a complex value (both planes); softplus is the exact
+ * Readings where the pages leave a step open: y is returned as a complex value (both planes); softplus is the exact
  * log(1+e^dt), evaluated in the overflow-free form max(dt,0)+log1p(e^-|dt|);
  * a NULL Dskip means D = 0; a NULL initial state means h_{-1} = 0.
  *
