@@ -26,6 +26,9 @@ struct StepArgs {
     float *h_re, *h_im, *y_re, *y_im;
 };
 
+// Number of compute units of the current device (queried once per device).
+hipError_t device_cu_count(int* cus);
+
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_cumsum(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t stream);

@@ -328,8 +328,9 @@ __attribute__((amdgpu_waves_per_eu(N * D > 64 * 128 ? 1 : CSSD_K2_WAVES))) void 
     if (NLT - 1 - t != t) chunk_scan_tile<In, C, N, D>(a, chunk, NLT - 1 - t);
 }
 
+// Launch of the register-operand kernel above (any supported shape and dtype).
 template <int C>
-hipError_t launch_chunk_scan_c(const FwdArgs& f, hipStream_t s) {
+hipError_t launch_chunk_scan_regs(const FwdArgs& f, hipStream_t s) {
     ScanArgs a;
     a.x_re = f.x_re; a.x_im = f.x_im; a.b_re = f.b_re; a.b_im = f.b_im;
     a.c_re = f.c_re; a.c_im = f.c_im; a.dskip = f.dskip;

@@ -46,6 +46,7 @@ SMALL = [
     (2, 50, 2, 128, 16, 32, False, True),    # largest D
     (1, 190, 1, 128, 128, 128, True, True),  # largest everything, partial chunk
     (3, 128, 2, 64, 64, 32, True, True),
+    (2, 130, 2, 32, 64, 64, True, True),     # two waves, five score tiles each, ragged tail
 ]
 
 
