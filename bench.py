@@ -31,7 +31,8 @@ METRIC = "complex SSD fwd tokens/s at B8 T2048 H48; % of MFMA/HBM roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
 # source files that make up each kernel (besides the shared device/launch headers)
-KERNEL_SRC = {"k_chunk_scan": ("k_chunk_scan.h", "k_chunk_scan.hip", "k_chunk_scan_c16.hip",
+KERNEL_SRC = {"k_chunk_scan": ("k_chunk_scan.h", "k_chunk_scan_lds.h", "k_chunk_scan.hip",
+                               "k_chunk_scan_c16.hip",
                                "k_chunk_scan_c32.hip", "k_chunk_scan_c64.hip",
                                "k_chunk_scan_c128.hip"),
               "k_chunk_state": ("k_chunk_state.hip",), "k_state_pass": ("k_state_pass.hip",),
@@ -65,6 +66,15 @@ def forward_hbm_bytes(B, T, H, D, N, in_bytes=4):
 def decode_hbm_bytes(B, H, D, N):
     """Per token: read and write the state, read x, B, C, dt, write y."""
     return B * H * N * D * 2 * 4 * 2 + B * H * (2 * D + 2 * N) * 2 * 4 + B * H * 4
+
+
+def chunk_scan_symbol(N, D, C, dtype):
+    """The kernel the library launches for the chunk-scan step at this shape (the
+    rule of launch_chunk_scan_c: the LDS-staged kernel for fp32 inputs with
+    C <= 64, C*N <= 4096, D <= 64 and not (C = 64, D = 16)), as rocprofv3 names it."""
+    if dtype == "f32" and C <= 64 and C * N <= 4096 and D <= 64 and not (C == 64 and D == 16):
+        return f"k_chunk_scan_lds<{C}, {N}, {D}>"
+    return f"k_chunk_scan<cssd::In{'F32' if dtype == 'f32' else 'BF16'}, {C}, {N}, {D}>"
 
 
 def src_hash(name):
@@ -256,7 +266,8 @@ def main():
                                "48 heads, head dim 64, state 64, chunk 64, fp32 complex planes",
                    "batch": B, "seqlen": T, "heads": H, "headdim": D, "dstate": N, "chunk": C,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "k_chunk_scan", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "k_chunk_scan",
+                     "symbol": chunk_scan_symbol(N, D, C, "f32"), "achieved": round(achieved, 2),
                      "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
                      "traffic": traffic, "algorithmic_flops_per_launch": k2_flops,
