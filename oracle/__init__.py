@@ -65,6 +65,10 @@ def _bind(lib):
     lib.oracle_forward_f64.argtypes = [_i64] * 5 + [_d] * 10 + [_d] * 2 + [_d] * 4 + [ctypes.c_int]
     lib.oracle_step_f64.restype = ctypes.c_int
     lib.oracle_step_f64.argtypes = [_i64] * 4 + [_d] * 10 + [_d] * 4 + [ctypes.c_int]
+    lib.oracle_step_n_f64.restype = ctypes.c_int
+    lib.oracle_step_n_f64.argtypes = [_i64] * 5 + [_d] * 10 + [_d] * 4 + [ctypes.c_int]
+    lib.oracle_step_infinite_f64.restype = ctypes.c_int
+    lib.oracle_step_infinite_f64.argtypes = [_i64] * 4 + [_d] * 10 + [_d] * 2 + [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -143,6 +147,51 @@ def step(x, Bm, Cm, dt, A, Dskip, h, nthreads: int = 0, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_step_f64 failed")
     return yr + 1j * yi, hr + 1j * hi
+
+
+def step_n(x, Bm, Cm, dt, A, Dskip, h, n: int, nthreads: int = 0, lib=None):
+    """The same input held for n steps, in closed form.  h (B,H,N,D) complex is
+    NOT modified; returns (y_n (B,H,D) complex128, h_n (B,H,N,D) complex128)."""
+    lib = lib or load()
+    x = np.asarray(x)
+    Bsz, H, D = x.shape
+    N = np.asarray(Bm).shape[-1]
+    xr, xi = _planes(x)
+    br, bi = _planes(Bm, (Bsz, H, N))
+    cr, ci = _planes(Cm, (Bsz, H, N))
+    dtv = _real(dt, (Bsz, H))
+    ar, ai = _planes(np.asarray(A, dtype=np.complex128), (H,))
+    ds = _real(Dskip, (H,)) if Dskip is not None else None
+    hr, hi = _planes(h, (Bsz, H, N, D))
+    hr = hr.copy(); hi = hi.copy()
+    yr = np.empty((Bsz, H, D)); yi = np.empty_like(yr)
+    rc = lib.oracle_step_n_f64(Bsz, H, D, N, int(n), _p(xr), _p(xi), _p(br), _p(bi), _p(cr),
+                               _p(ci), _p(dtv), _p(ar), _p(ai), _p(ds), _p(hr), _p(hi), _p(yr),
+                               _p(yi), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_step_n_f64 failed")
+    return yr + 1j * yi, hr + 1j * hi
+
+
+def step_infinite(x, Bm, Cm, dt, A, Dskip, nthreads: int = 0, lib=None):
+    """The stationary output of an endless constant input; returns y (B,H,D) complex128."""
+    lib = lib or load()
+    x = np.asarray(x)
+    Bsz, H, D = x.shape
+    N = np.asarray(Bm).shape[-1]
+    xr, xi = _planes(x)
+    br, bi = _planes(Bm, (Bsz, H, N))
+    cr, ci = _planes(Cm, (Bsz, H, N))
+    dtv = _real(dt, (Bsz, H))
+    ar, ai = _planes(np.asarray(A, dtype=np.complex128), (H,))
+    ds = _real(Dskip, (H,)) if Dskip is not None else None
+    yr = np.empty((Bsz, H, D)); yi = np.empty_like(yr)
+    rc = lib.oracle_step_infinite_f64(Bsz, H, D, N, _p(xr), _p(xi), _p(br), _p(bi), _p(cr),
+                                      _p(ci), _p(dtv), _p(ar), _p(ai), _p(ds), _p(yr), _p(yi),
+                                      int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_step_infinite_f64 failed")
+    return yr + 1j * yi
 
 
 def max_threads(lib=None) -> int:

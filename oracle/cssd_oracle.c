@@ -37,6 +37,7 @@
  */
 #include <math.h>
 #include <stddef.h>
+#include <complex.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -191,6 +192,117 @@ int oracle_step_f64(int64_t Bsz, int64_t H, int64_t D, int64_t N,
                  b_im + bh * N, c_re + bh * N, c_im + bh * N,
                  dskip ? dskip[h] : 0.0, h_re + bh * N * D, h_im + bh * N * D,
                  y_re + bh * D, y_im + bh * D);
+    }
+    return 0;
+}
+
+/*
+ * A constant input held for n steps, in closed form (burn-mamba docs, module
+ * step_constant: when the same token is fed again and again, the n unrolled
+ * steps collapse to a geometric series in the per-step factor; here there is no
+ * rotation operator between steps and the input enters with unit weight, so the
+ * series is in the scalar decay a itself):
+ *   a   = exp(softplus(dt) A),   a^n = exp(n softplus(dt) A)
+ *   h_n = a^n h_0 + (1 - a^n) / (1 - a) * B (x) x      the ratio is n when a = 1
+ *   y_n = sum_k C[k] h_n[k,:] + Dskip x                 the output of the n-th step
+ * Same layouts as oracle_step_f64; h is replaced by h_n.  n >= 1.
+ */
+int oracle_step_n_f64(int64_t Bsz, int64_t H, int64_t D, int64_t N, int64_t n,
+                      const double *x_re, const double *x_im,
+                      const double *b_re, const double *b_im,
+                      const double *c_re, const double *c_im,
+                      const double *dt, const double *a_re, const double *a_im,
+                      const double *dskip, double *h_re, double *h_im,
+                      double *y_re, double *y_im, int nthreads)
+{
+    if (Bsz <= 0 || H <= 0 || D <= 0 || N <= 0 || n < 1)
+        return -1;
+    if (!x_re || !x_im || !b_re || !b_im || !c_re || !c_im || !dt || !a_re ||
+        !a_im || !h_re || !h_im || !y_re || !y_im)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < Bsz * H; ++bh) {
+        int64_t h = bh % H;
+        double s = softplus(dt[bh]);
+        double complex z = s * (a_re[h] + a_im[h] * I);
+        double complex a = cexp(z);
+        double complex an = cexp((double)n * z);
+        double complex ratio = (a == 1.0) ? (double complex)(double)n : (1.0 - an) / (1.0 - a);
+        double d = dskip ? dskip[h] : 0.0;
+        const double *xr = x_re + bh * D, *xi = x_im + bh * D;
+        double *hr = h_re + bh * N * D, *hi = h_im + bh * N * D;
+        for (int64_t k = 0; k < N; ++k) {
+            double complex bk = b_re[bh * N + k] + b_im[bh * N + k] * I;
+            for (int64_t p = 0; p < D; ++p) {
+                double complex xp = xr[p] + xi[p] * I;
+                double complex hv = hr[k * D + p] + hi[k * D + p] * I;
+                double complex hn = an * hv + ratio * bk * xp;
+                hr[k * D + p] = creal(hn);
+                hi[k * D + p] = cimag(hn);
+            }
+        }
+        for (int64_t p = 0; p < D; ++p) {
+            double complex acc = 0.0;
+            for (int64_t k = 0; k < N; ++k) {
+                double complex ck = c_re[bh * N + k] + c_im[bh * N + k] * I;
+                acc += ck * (hr[k * D + p] + hi[k * D + p] * I);
+            }
+            acc += d * (xr[p] + xi[p] * I);
+            y_re[bh * D + p] = creal(acc);
+            y_im[bh * D + p] = cimag(acc);
+        }
+    }
+    return 0;
+}
+
+/*
+ * The output of an endless constant input (same page: the stationary fixed
+ * point, which no starting state influences).  For |a| < 1 the series of
+ * decays sums to 1 / (1 - a), so
+ *   y_inf = (sum_k C[k] B[k]) / (1 - a) * x + Dskip x
+ * Layouts as oracle_step_f64, without a state.
+ */
+int oracle_step_infinite_f64(int64_t Bsz, int64_t H, int64_t D, int64_t N,
+                             const double *x_re, const double *x_im,
+                             const double *b_re, const double *b_im,
+                             const double *c_re, const double *c_im,
+                             const double *dt, const double *a_re, const double *a_im,
+                             const double *dskip, double *y_re, double *y_im, int nthreads)
+{
+    if (Bsz <= 0 || H <= 0 || D <= 0 || N <= 0)
+        return -1;
+    if (!x_re || !x_im || !b_re || !b_im || !c_re || !c_im || !dt || !a_re ||
+        !a_im || !y_re || !y_im)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < Bsz * H; ++bh) {
+        int64_t h = bh % H;
+        double s = softplus(dt[bh]);
+        double complex a = cexp(s * (a_re[h] + a_im[h] * I));
+        double complex score = 0.0;
+        for (int64_t k = 0; k < N; ++k)
+            score += (c_re[bh * N + k] + c_im[bh * N + k] * I) *
+                     (b_re[bh * N + k] + b_im[bh * N + k] * I);
+        double complex gain = score / (1.0 - a);
+        double d = dskip ? dskip[h] : 0.0;
+        for (int64_t p = 0; p < D; ++p) {
+            double complex xp = x_re[bh * D + p] + x_im[bh * D + p] * I;
+            double complex yv = gain * xp + d * xp;
+            y_re[bh * D + p] = creal(yv);
+            y_im[bh * D + p] = cimag(yv);
+        }
     }
     return 0;
 }

@@ -205,6 +205,52 @@ def pin_step_constant_input(lib):
             assert rel_err(h[b, k], hn) < 1e-10, (b, k)
 
 
+def pin_step_n_against_recurrence(lib):
+    """The closed-form n-step entry point is the state and output after n calls
+    of the one-step recurrence with the same input (burn-mamba step_constant).
+    The heads cover |a| < 1, a pure rotation (|a| = 1, a != 1), a = 1 exactly
+    (A = 0: h_n = h0 + n B (x) x) and a vanishing decay (h_n -> B (x) x)."""
+    rng = np.random.default_rng(707)
+    Bsz, H, D, N = 2, 4, 3, 5
+    xv, Bv, Cv = crandn(rng, Bsz, H, D), crandn(rng, Bsz, H, N), crandn(rng, Bsz, H, N)
+    dt = rng.uniform(-1.0, 1.0, (Bsz, H))
+    A = np.array([-0.4 + 1.3j, 0.0 + 0.7j, 0.0 + 0.0j, -1e4 + 0.3j])
+    Dk = np.array([0.5, -0.8, 1.2, 0.3])
+    h0 = crandn(rng, Bsz, H, N, D)
+    for n in (1, 2, 7, 40):
+        h = h0.copy()
+        for _ in range(n):
+            y, h = oracle.step(xv, Bv, Cv, dt, A, Dk, h, lib=lib)
+        yn, hn = oracle.step_n(xv, Bv, Cv, dt, A, Dk, h0, n, lib=lib)
+        assert rel_err(hn, h) < 1e-12, ("h", n, rel_err(hn, h))
+        assert rel_err(yn, y) < 1e-12, ("y", n, rel_err(yn, y))
+    _, hn = oracle.step_n(xv, Bv, Cv, dt, A, Dk, h0, 9, lib=lib)
+    outer = np.einsum("bhn,bhd->bhnd", Bv, xv)
+    assert rel_err(hn[:, 2], h0[:, 2] + 9 * outer[:, 2]) < 1e-14   # a = 1
+    assert rel_err(hn[:, 3], outer[:, 3]) < 1e-14                   # a -> 0
+
+
+def pin_step_infinite_against_recurrence(lib):
+    """The stationary output is what the recurrence settles to under an endless
+    constant input, whatever the start state: iterate until |a|^n < 1e-18.  With a
+    vanishing decay it is (C . B) x + D x."""
+    rng = np.random.default_rng(808)
+    Bsz, H, D, N = 2, 3, 4, 3
+    xv, Bv, Cv = crandn(rng, Bsz, H, D), crandn(rng, Bsz, H, N), crandn(rng, Bsz, H, N)
+    dt = rng.uniform(-1.0, 1.0, (Bsz, H))
+    A = np.array([-0.5 + 2.0j, -0.2 - 0.6j, -1e4 + 1.0j])
+    Dk = np.array([0.9, -0.4, 1.7])
+    h = crandn(rng, Bsz, H, N, D)
+    amax = float(np.max(np.abs(disc(dt, A[None, :]))))
+    n = int(np.ceil(np.log(1e-18) / np.log(amax)))
+    for _ in range(n):
+        y, h = oracle.step(xv, Bv, Cv, dt, A, Dk, h, lib=lib)
+    yinf = oracle.step_infinite(xv, Bv, Cv, dt, A, Dk, lib=lib)
+    assert rel_err(yinf, y) < 1e-12, rel_err(yinf, y)
+    score = np.einsum("bhn,bhn->bh", Cv, Bv)
+    assert rel_err(yinf[:, 2], (score[:, 2, None] + Dk[2]) * xv[:, 2]) < 1e-14
+
+
 # ---------------------------------------------------------------------------
 # p6: decay zero -- the scan reduces to per-step outer products
 # ---------------------------------------------------------------------------
@@ -362,5 +408,6 @@ def pin_golden_modulus_drift(lib):
 
 
 ALL_PINS = [pin_bruteforce, pin_impulse, pin_constant_input, pin_fixed_point,
+            pin_step_n_against_recurrence, pin_step_infinite_against_recurrence,
             pin_step_constant_input, pin_decay_zero, pin_homogeneous, pin_linearity_and_skip,
             pin_pam_dual_form, pin_pam_orthogonal_keys, pin_golden_modulus_drift]

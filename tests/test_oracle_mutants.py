@@ -48,6 +48,18 @@ MUTANTS = {
          "double vr = hr[n * D + p] - (br[n] * xr[p] - bi[n] * xi[p]), "
          "vi = hi[n * D + p] - (br[n] * xi[p] + bi[n] * xr[p]);"),
     ],
+    "step_n_power_off_by_one": [("double complex an = cexp((double)n * z);",
+                                 "double complex an = cexp((double)(n - 1) * z);")],
+    "step_n_series_dropped": [("double complex hn = an * hv + ratio * bk * xp;",
+                               "double complex hn = an * hv + bk * xp;")],
+    "step_n_wrong_limit_at_unit_decay": [("(a == 1.0) ? (double complex)(double)n :",
+                                          "(a == 1.0) ? (double complex)1.0 :")],
+    "step_infinite_conjugated_score": [("score += (c_re[bh * N + k] + c_im[bh * N + k] * I) *",
+                                        "score += (c_re[bh * N + k] - c_im[bh * N + k] * I) *")],
+    "step_infinite_skip_dropped": [("double complex yv = gain * xp + d * xp;",
+                                    "double complex yv = gain * xp;")],
+    "step_infinite_gain_inverted": [("double complex gain = score / (1.0 - a);",
+                                     "double complex gain = score * (1.0 - a);")],
 }
 
 
