@@ -145,6 +145,39 @@ def time_forward(inp, steps, warmup, dev):
     return total_ms / steps, kern
 
 
+def time_constant_input(B, H, D, N, nsteps, reps, warmup, dev, seed=4):
+    """cssd_step_n (nsteps at once) and cssd_step_infinite on one seeded token;
+    returns per-call ms of each (HIP events on the launch stream)."""
+    import torch
+    import complex_valued_state_amd as cssd
+    import cssd_workloads as wl
+    g = torch.Generator(device=dev).manual_seed(seed)
+    r = math.sqrt(0.5)
+    x = [torch.randn((B, H, D), generator=g, device=dev) * r for _ in range(2)]
+    bm = [torch.randn((B, H, N), generator=g, device=dev) * r for _ in range(2)]
+    cm = [torch.randn((B, H, N), generator=g, device=dev) * r for _ in range(2)]
+    dt = torch.randn((B, H), generator=g, device=dev)
+    a_re, a_im, dk = (torch.from_numpy(v).to(dev) for v in wl.decode_params(seed, H))
+    h_re = torch.zeros((B, H, N, D), dtype=torch.float32, device=dev)
+    h_im = torch.zeros_like(h_re)
+    args = (x[0], x[1], bm[0], bm[1], cm[0], cm[1], dt, a_re, a_im, dk)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, call in (("step_n", lambda: cssd.cssd_step_n(*args, h_re, h_im, nsteps, stream=stream)),
+                       ("step_infinite", lambda: cssd.cssd_step_infinite(*args, stream=stream))):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        res[name] = e0.elapsed_time(e1) / reps
+    return res
+
+
 def time_decode(B, H, D, N, tokens, warmup, dev, seed=4):
     """cssd_step over `tokens` pre-staged tokens (seeded device-side draws)."""
     import torch
@@ -301,6 +334,15 @@ def main():
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(dbytes / (dkms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes_per_launch": dbytes, "avg_launch_ms": round(dkms, 5)}}
+        progress("timing the constant-input entry points")
+        nconst = 4096
+        cms = time_constant_input(d4["B"], d4["H"], d4["D"], d4["N"], nconst, 20, 3, dev)
+        extra["constant_input_B256_H48_N128_D64"] = {
+            "step_n": {"nsteps": nconst, "ms_per_call": round(cms["step_n"], 5),
+                       "tokens_per_s": round(d4["B"] * nconst / (cms["step_n"] * 1e-3), 1),
+                       "hbm_GBs": round(dbytes / (cms["step_n"] * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(dbytes / (cms["step_n"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "step_infinite": {"ms_per_call": round(cms["step_infinite"], 5)}}
         if args.all:
             for name, mk in (("cfg2_long_B1_T16384_H48_N128_C128", wl.config2),
                              ("cfg3_pam_B16_T1024_H12_N128_C64", lambda: wl.config3("re"))):

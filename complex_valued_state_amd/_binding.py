@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libcssd.so")
 
 CSSD_OK, CSSD_ERR_INVALID_ARG, CSSD_ERR_UNSUPPORTED, CSSD_ERR_WORKSPACE, CSSD_ERR_HIP = range(5)
 CSSD_F32, CSSD_BF16 = 0, 1
-KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step")
+KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
+                "k_step_infinite")
 
 _lock = threading.Lock()
 _lib = None
@@ -55,6 +56,10 @@ def load_library(path: Optional[str] = None):
             + [_vp] * 4 + [_vp, _sz, _vp]
         lib.cssd_step.restype = ctypes.c_int
         lib.cssd_step.argtypes = [_i64] * 4 + [_vp] * 10 + [_vp] * 4 + [_vp]
+        lib.cssd_step_n.restype = ctypes.c_int
+        lib.cssd_step_n.argtypes = [_i64] * 5 + [_vp] * 10 + [_vp] * 4 + [_vp]
+        lib.cssd_step_infinite.restype = ctypes.c_int
+        lib.cssd_step_infinite.argtypes = [_i64] * 4 + [_vp] * 10 + [_vp] * 2 + [_vp]
         lib.cssd_profile_enable.restype = ctypes.c_int
         lib.cssd_profile_enable.argtypes = [ctypes.c_int]
         lib.cssd_profile_read.restype = ctypes.c_int
@@ -184,22 +189,19 @@ def cssd_forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None,
     return y_re, y_im, hT_re, hT_im
 
 
-def cssd_step(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h_im, *,
-              out=None, stream=None):
-    """One decode token for all (batch, head); the state (h_re, h_im) is updated
-    in place.  x_*: (B,H,D); B_*, C_*: (B,H,N); dt: (B,H); A_*: (H,); Dskip: (H,)
-    or None; h_*: (B,H,N,D).  All float32.  Returns (y_re, y_im), each (B,H,D)."""
+def _step_ptrs(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h, Bsz, H, N, D, out):
+    """Checked pointers of the decode entry points (h = (h_re, h_im) or None)."""
     torch = _torch()
-    lib = load_library()
-    dev = h_re.device
-    Bsz, H, N, D = h_re.shape
+    dev = x_re.device
     f32 = (torch.float32,)
     p = {}
-    for name, t, shp in (("x_re", x_re, (Bsz, H, D)), ("x_im", x_im, (Bsz, H, D)),
-                         ("B_re", B_re, (Bsz, H, N)), ("B_im", B_im, (Bsz, H, N)),
-                         ("C_re", C_re, (Bsz, H, N)), ("C_im", C_im, (Bsz, H, N)),
-                         ("dt", dt, (Bsz, H)), ("A_re", A_re, (H,)), ("A_im", A_im, (H,)),
-                         ("h_re", h_re, (Bsz, H, N, D)), ("h_im", h_im, (Bsz, H, N, D))):
+    items = [("x_re", x_re, (Bsz, H, D)), ("x_im", x_im, (Bsz, H, D)),
+             ("B_re", B_re, (Bsz, H, N)), ("B_im", B_im, (Bsz, H, N)),
+             ("C_re", C_re, (Bsz, H, N)), ("C_im", C_im, (Bsz, H, N)),
+             ("dt", dt, (Bsz, H)), ("A_re", A_re, (H,)), ("A_im", A_im, (H,))]
+    if h is not None:
+        items += [("h_re", h[0], (Bsz, H, N, D)), ("h_im", h[1], (Bsz, H, N, D))]
+    for name, t, shp in items:
         p[name] = _check(t, name, shp, f32, dev)
     p["Dskip"] = None if Dskip is None else _check(Dskip, "Dskip", (H,), f32, dev)
     if out is None:
@@ -209,12 +211,58 @@ def cssd_step(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h
         y_re, y_im = out
     p["y_re"] = _check(y_re, "y_re", (Bsz, H, D), f32, dev)
     p["y_im"] = _check(y_im, "y_im", (Bsz, H, D), f32, dev)
+    return p, (y_re, y_im), dev
+
+
+def cssd_step(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h_im, *,
+              out=None, stream=None):
+    """One decode token for all (batch, head); the state (h_re, h_im) is updated
+    in place.  x_*: (B,H,D); B_*, C_*: (B,H,N); dt: (B,H); A_*: (H,); Dskip: (H,)
+    or None; h_*: (B,H,N,D).  All float32.  Returns (y_re, y_im), each (B,H,D)."""
+    lib = load_library()
+    Bsz, H, N, D = h_re.shape
+    p, y, dev = _step_ptrs(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip,
+                           (h_re, h_im), Bsz, H, N, D, out)
     st = lib.cssd_step(Bsz, H, D, N, p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"],
                        p["C_im"], p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h_re"],
                        p["h_im"], p["y_re"], p["y_im"], _stream_ptr(stream, dev))
     if st != CSSD_OK:
         raise CSSDError(st, "cssd_step")
-    return y_re, y_im
+    return y
+
+
+def cssd_step_n(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h_im, nsteps,
+                *, out=None, stream=None):
+    """nsteps decode steps that all receive the same input, applied at once; the
+    state is updated in place and the nsteps-th output is returned.  Arguments
+    as cssd_step, plus nsteps >= 1."""
+    lib = load_library()
+    Bsz, H, N, D = h_re.shape
+    p, y, dev = _step_ptrs(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip,
+                           (h_re, h_im), Bsz, H, N, D, out)
+    st = lib.cssd_step_n(Bsz, H, D, N, int(nsteps), p["x_re"], p["x_im"], p["B_re"], p["B_im"],
+                         p["C_re"], p["C_im"], p["dt"], p["A_re"], p["A_im"], p["Dskip"],
+                         p["h_re"], p["h_im"], p["y_re"], p["y_im"], _stream_ptr(stream, dev))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_step_n")
+    return y
+
+
+def cssd_step_infinite(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, *,
+                       out=None, stream=None):
+    """The stationary output of an endless constant input (no state).  Arguments
+    as cssd_step without the state; returns (y_re, y_im), each (B,H,D)."""
+    lib = load_library()
+    Bsz, H, D = x_re.shape
+    N = B_re.shape[-1]
+    p, y, dev = _step_ptrs(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, None,
+                           Bsz, H, N, D, out)
+    st = lib.cssd_step_infinite(Bsz, H, D, N, p["x_re"], p["x_im"], p["B_re"], p["B_im"],
+                                p["C_re"], p["C_im"], p["dt"], p["A_re"], p["A_im"], p["Dskip"],
+                                p["y_re"], p["y_im"], _stream_ptr(stream, dev))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_step_infinite")
+    return y
 
 
 class profile:

@@ -219,38 +219,94 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     return CSSD_OK;
 }
 
-int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, const float* x_re,
-              const float* x_im, const float* B_re, const float* B_im, const float* C_re,
-              const float* C_im, const float* dt, const float* A_re, const float* A_im,
-              const float* Dskip, float* h_re, float* h_im, float* y_re, float* y_im,
-              void* stream) {
+namespace {
+
+// Host-side checks shared by the decode entry points.  h_re/h_im may be NULL
+// (the stationary-output entry point has no state).
+int check_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, const float* x_re,
+               const float* x_im, const float* B_re, const float* B_im, const float* C_re,
+               const float* C_im, const float* dt, const float* A_re, const float* A_im,
+               const float* Dskip, const float* h_re, const float* h_im, const float* y_re,
+               const float* y_im, bool with_state) {
     if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0) return CSSD_ERR_INVALID_ARG;
     if (!pow2_16_128(headdim) || !pow2_16_128(dstate)) return CSSD_ERR_UNSUPPORTED;
     const int64_t lim = (int64_t)1 << 31;
     if (batch > lim || nheads > lim || batch * nheads > lim / (headdim * dstate))
         return CSSD_ERR_UNSUPPORTED;
     // x, the state and y are accessed as float4; B, C, dt, A, Dskip as scalars
-    const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, h_re, h_im, y_re, y_im};
-    const uintptr_t req_al[] = {16, 16, 4, 4, 4, 4, 4, 4, 4, 16, 16, 16, 16};
-    for (int i = 0; i < 13; ++i)
+    const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, y_re, y_im};
+    const uintptr_t req_al[] = {16, 16, 4, 4, 4, 4, 4, 4, 4, 16, 16};
+    for (int i = 0; i < 11; ++i)
         if (req[i] == nullptr || !aligned(req[i], req_al[i])) return CSSD_ERR_INVALID_ARG;
+    if (with_state && (h_re == nullptr || h_im == nullptr || !aligned(h_re, 16) || !aligned(h_im, 16)))
+        return CSSD_ERR_INVALID_ARG;
     if (Dskip != nullptr && !aligned(Dskip, 4)) return CSSD_ERR_INVALID_ARG;
     const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip};
     const void* outs[] = {h_re, h_im, y_re, y_im};
     for (const void* o : outs)
         for (const void* i : ins)
-            if (o == i) return CSSD_ERR_INVALID_ARG;
-    if (h_re == h_im || y_re == y_im || y_re == h_re || y_re == h_im || y_im == h_re ||
-        y_im == h_im)
+            if (o != nullptr && o == i) return CSSD_ERR_INVALID_ARG;
+    if (y_re == y_im) return CSSD_ERR_INVALID_ARG;
+    if (with_state && (h_re == h_im || y_re == h_re || y_re == h_im || y_im == h_re || y_im == h_im))
         return CSSD_ERR_INVALID_ARG;
+    return CSSD_OK;
+}
 
+cssd::StepArgs step_args(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                         const float* x_re, const float* x_im, const float* B_re,
+                         const float* B_im, const float* C_re, const float* C_im, const float* dt,
+                         const float* A_re, const float* A_im, const float* Dskip, float* h_re,
+                         float* h_im, float* y_re, float* y_im) {
     cssd::StepArgs a;
     a.B = batch; a.H = nheads; a.D = headdim; a.N = dstate;
     a.x_re = x_re; a.x_im = x_im; a.b_re = B_re; a.b_im = B_im; a.c_re = C_re; a.c_im = C_im;
     a.dt = dt; a.a_re = A_re; a.a_im = A_im; a.dskip = Dskip;
     a.h_re = h_re; a.h_im = h_im; a.y_re = y_re; a.y_im = y_im;
+    return a;
+}
+
+}  // namespace
+
+int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, const float* x_re,
+              const float* x_im, const float* B_re, const float* B_im, const float* C_re,
+              const float* C_im, const float* dt, const float* A_re, const float* A_im,
+              const float* Dskip, float* h_re, float* h_im, float* y_re, float* y_im,
+              void* stream) {
+    return cssd_step_n(batch, nheads, headdim, dstate, 1, x_re, x_im, B_re, B_im, C_re, C_im, dt,
+                       A_re, A_im, Dskip, h_re, h_im, y_re, y_im, stream);
+}
+
+int cssd_step_n(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int64_t nsteps,
+                const float* x_re, const float* x_im, const float* B_re, const float* B_im,
+                const float* C_re, const float* C_im, const float* dt, const float* A_re,
+                const float* A_im, const float* Dskip, float* h_re, float* h_im, float* y_re,
+                float* y_im, void* stream) {
+    if (nsteps < 1) return CSSD_ERR_INVALID_ARG;
+    const int st = check_step(batch, nheads, headdim, dstate, x_re, x_im, B_re, B_im, C_re, C_im,
+                              dt, A_re, A_im, Dskip, h_re, h_im, y_re, y_im, true);
+    if (st != CSSD_OK) return st;
+    cssd::StepArgs a = step_args(batch, nheads, headdim, dstate, x_re, x_im, B_re, B_im, C_re,
+                                 C_im, dt, A_re, A_im, Dskip, h_re, h_im, y_re, y_im);
+    a.nsteps = nsteps;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (timed(cssd::K_STEP, s, [&] { return cssd::launch_step(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    return CSSD_OK;
+}
+
+int cssd_step_infinite(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                       const float* x_re, const float* x_im, const float* B_re, const float* B_im,
+                       const float* C_re, const float* C_im, const float* dt, const float* A_re,
+                       const float* A_im, const float* Dskip, float* y_re, float* y_im,
+                       void* stream) {
+    const int st = check_step(batch, nheads, headdim, dstate, x_re, x_im, B_re, B_im, C_re, C_im,
+                              dt, A_re, A_im, Dskip, nullptr, nullptr, y_re, y_im, false);
+    if (st != CSSD_OK) return st;
+    cssd::StepArgs a = step_args(batch, nheads, headdim, dstate, x_re, x_im, B_re, B_im, C_re,
+                                 C_im, dt, A_re, A_im, Dskip, nullptr, nullptr, y_re, y_im);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (timed(cssd::K_STEP_INFINITE, s, [&] { return cssd::launch_step_infinite(a, s); }) !=
+        hipSuccess)
         return CSSD_ERR_HIP;
     return CSSD_OK;
 }
@@ -291,8 +347,8 @@ int cssd_profile_read(double* ms, int64_t* launches, int capacity) {
 }
 
 const char* cssd_kernel_name(int kernel_id) {
-    static const char* names[cssd::K_COUNT] = {"k_cumsum", "k_chunk_state", "k_state_pass",
-                                                "k_chunk_scan", "k_step"};
+    static const char* names[cssd::K_COUNT] = {"k_cumsum",     "k_chunk_state", "k_state_pass",
+                                                "k_chunk_scan", "k_step",        "k_step_infinite"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

@@ -7,7 +7,7 @@
 namespace cssd {
 
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
-                K_COUNT = 5 };
+                K_STEP_INFINITE = 5, K_COUNT = 6 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -22,6 +22,7 @@ struct FwdArgs {
 
 struct StepArgs {
     int64_t B, H, D, N;
+    int64_t nsteps = 1;  // constant-input steps applied at once (1: one decode step)
     const float *x_re, *x_im, *b_re, *b_im, *c_re, *c_im, *dt, *a_re, *a_im, *dskip;
     float *h_re, *h_im, *y_re, *y_im;
 };
@@ -35,5 +36,6 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_state_pass(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+hipError_t launch_step_infinite(const StepArgs& a, hipStream_t stream);
 
 }  // namespace cssd

@@ -8,6 +8,15 @@
 // bound by memory bandwidth).  The skip term follows the burn-mamba
 // step_constant readout.
 //
+// The same kernel applies n steps of one constant input at once (burn-mamba
+// docs, module step_constant: the unrolled steps form a geometric series; here
+// with no rotation between steps and unit input weight):
+//   h <- abar^n h + q B (x) x,   q = (1 - abar^n) / (1 - abar)   (q = n at abar = 1)
+// abar^n = exp(n z) and q = expm1(n z) / expm1(z), z = softplus(dt) A, are formed
+// per (b, h) in fp64 with the phases reduced mod 2 pi; q is folded into the B
+// row, so the streaming body is the single step's.  For n = 1, q is 1 exactly
+// and the arithmetic is that of one step.
+//
 // Mapping: one 256-thread workgroup per (b, h).  The N x D state is streamed as
 // float4 rows: D/4 threads cover one row of p, 1024/D rows per pass.  Each
 // thread issues all its state loads (non-temporal: the state is touched once
@@ -19,6 +28,19 @@
 
 namespace cssd {
 
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kPi = 3.1415926535897932384626433832795;
+
+// expm1(x + i y) = e^x e^{iy} - 1, accurate for small |x + i y|:
+// re = expm1(x) cos y - 2 sin^2(y/2), im = e^x sin y (angles reduced first).
+__device__ __forceinline__ void cexpm1_f64(double x, double y, double& re, double& im) {
+    double sn, cs;
+    sincos(remainder(y, kTwoPi), &sn, &cs);
+    const double sh = sin(remainder(0.5 * y, kPi));
+    re = expm1(x) * cs - 2.0 * sh * sh;
+    im = exp(x) * sn;
+}
+
 template <int N, int D>
 __global__ __launch_bounds__(256) void k_step(
     const float* __restrict__ x_re, const float* __restrict__ x_im,
@@ -26,7 +48,7 @@ __global__ __launch_bounds__(256) void k_step(
     const float* __restrict__ c_re, const float* __restrict__ c_im, const float* __restrict__ dt,
     const float* __restrict__ a_re, const float* __restrict__ a_im,
     const float* __restrict__ dskip, float4* __restrict__ h_re, float4* __restrict__ h_im,
-    float* __restrict__ y_re, float* __restrict__ y_im, int H) {
+    float* __restrict__ y_re, float* __restrict__ y_im, int H, int64_t nsteps) {
     constexpr int TPR = D / 4;                  // threads per state row
     constexpr int RPP = 256 / TPR;              // rows per pass
     constexpr int PASSES = (N + RPP - 1) / RPP;
@@ -36,10 +58,32 @@ __global__ __launch_bounds__(256) void k_step(
     const int h = (int)(bh % H);
 
     const double s = softplus_f64((double)dt[bh]);
-    const double mag = exp(s * (double)a_re[h]);
-    double sn, cs;
-    sincos(s * (double)a_im[h], &sn, &cs);
-    const float ar = (float)(mag * cs), ai = (float)(mag * sn);
+    const double zr = s * (double)a_re[h], zi = s * (double)a_im[h];
+    float ar, ai, qr = 1.f, qi = 0.f;  // decay factor and input weight
+    if (nsteps == 1) {
+        const double mag = exp(zr);
+        double sn, cs;
+        sincos(zi, &sn, &cs);
+        ar = (float)(mag * cs);
+        ai = (float)(mag * sn);
+    } else {
+        const double nd = (double)nsteps;
+        const double mag = exp(nd * zr);
+        double sn, cs;
+        sincos(remainder(nd * zi, kTwoPi), &sn, &cs);
+        ar = (float)(mag * cs);
+        ai = (float)(mag * sn);
+        double e1r, e1i, enr, eni;
+        cexpm1_f64(zr, zi, e1r, e1i);
+        cexpm1_f64(nd * zr, nd * zi, enr, eni);
+        const double den = e1r * e1r + e1i * e1i;
+        if (den == 0.0) {
+            qr = (float)nd;
+        } else {
+            qr = (float)((enr * e1r + eni * e1i) / den);
+            qi = (float)((eni * e1r - enr * e1i) / den);
+        }
+    }
 
     const float4 xr = reinterpret_cast<const float4*>(x_re + bh * D)[pc];
     const float4 xi = reinterpret_cast<const float4*>(x_im + bh * D)[pc];
@@ -59,7 +103,8 @@ __global__ __launch_bounds__(256) void k_step(
     for (int k = 0; k < PASSES; ++k) {
         const int n = rg + k * RPP;
         if (n < N) {
-            const float br = b_re[bh * N + n], bi = b_im[bh * N + n];
+            const float b0r = b_re[bh * N + n], b0i = b_im[bh * N + n];
+            const float br = qr * b0r - qi * b0i, bi = qr * b0i + qi * b0r;
             const float cr = c_re[bh * N + n], ci = c_im[bh * N + n];
             float4 nr, ni;
 #define CSSD_UPD(f)                                                           \
@@ -103,7 +148,7 @@ static void dispatch_d(const StepArgs& a, hipStream_t s) {
 #define CSSD_K5(DD)                                                                         \
     hipLaunchKernelGGL((k_step<N, DD>), grid, block, 0, s, a.x_re, a.x_im, a.b_re, a.b_im,  \
                        a.c_re, a.c_im, a.dt, a.a_re, a.a_im, a.dskip, hr, hi, a.y_re, a.y_im, \
-                       (int)a.H)
+                       (int)a.H, a.nsteps)
     switch (a.D) {
         case 16: CSSD_K5(16); break;
         case 32: CSSD_K5(32); break;
@@ -120,6 +165,58 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
         case 64: dispatch_d<64>(a, stream); break;
         default: dispatch_d<128>(a, stream); break;
     }
+    return hipGetLastError();
+}
+
+// The stationary output of an endless constant input (burn-mamba docs, module
+// step_constant: the fixed point, which no starting state influences):
+//   y = (sum_n C[n] B[n]) / (1 - abar) x + D x
+// One wave per (b, h): the score sum_n C[n] B[n] in fp64 over the lanes, the
+// gain score / (1 - abar) with 1 - abar = -expm1(z) in fp64, then y per column.
+__global__ __launch_bounds__(256) void k_step_infinite(
+    const float* __restrict__ x_re, const float* __restrict__ x_im,
+    const float* __restrict__ b_re, const float* __restrict__ b_im,
+    const float* __restrict__ c_re, const float* __restrict__ c_im, const float* __restrict__ dt,
+    const float* __restrict__ a_re, const float* __restrict__ a_im,
+    const float* __restrict__ dskip, float* __restrict__ y_re, float* __restrict__ y_im,
+    int64_t units, int H, int N, int D) {
+    const int64_t bh = (int64_t)blockIdx.x * 4 + wave_id();
+    if (bh >= units) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int h = (int)(bh % H);
+    double sr = 0.0, si = 0.0;
+    for (int n = lane; n < N; n += 64) {
+        const double cr = c_re[bh * N + n], ci = c_im[bh * N + n];
+        const double br = b_re[bh * N + n], bi = b_im[bh * N + n];
+        sr += cr * br - ci * bi;
+        si += cr * bi + ci * br;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        sr += __shfl_xor(sr, off, 64);
+        si += __shfl_xor(si, off, 64);
+    }
+    const double s = softplus_f64((double)dt[bh]);
+    double e1r, e1i;
+    cexpm1_f64(s * (double)a_re[h], s * (double)a_im[h], e1r, e1i);
+    // gain = score / (1 - abar) = -score / expm1(z)
+    const double den = e1r * e1r + e1i * e1i;
+    const double gr = -(sr * e1r + si * e1i) / den;
+    const double gi = -(si * e1r - sr * e1i) / den;
+    const float kr = (float)gr + (dskip != nullptr ? dskip[h] : 0.f), ki = (float)gi;
+    for (int p = lane; p < D; p += 64) {
+        const float xr = x_re[bh * D + p], xi = x_im[bh * D + p];
+        y_re[bh * D + p] = kr * xr - ki * xi;
+        y_im[bh * D + p] = kr * xi + ki * xr;
+    }
+}
+
+hipError_t launch_step_infinite(const StepArgs& a, hipStream_t stream) {
+    const int64_t units = a.B * a.H;
+    const dim3 grid((unsigned)((units + 3) / 4)), block(256);
+    hipLaunchKernelGGL(k_step_infinite, grid, block, 0, stream, a.x_re, a.x_im, a.b_re, a.b_im,
+                       a.c_re, a.c_im, a.dt, a.a_re, a.a_im, a.dskip, a.y_re, a.y_im, units,
+                       (int)a.H, (int)a.N, (int)a.D);
     return hipGetLastError();
 }
 

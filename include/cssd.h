@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 100 /* major*100 + minor */
+#define CSSD_VERSION 101 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
@@ -172,6 +172,48 @@ int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
               float *y_re, float *y_im, void *stream);
 
 /*
+ * n recurrent steps that all receive the same input, applied at once in O(1)
+ * work per state element (burn-mamba docs, module step_constant: the unrolled
+ * constant-input steps form a geometric series; this is its case with no
+ * rotation between steps and unit input weight):
+ *     a = exp(softplus(dt) A)
+ *     h <- a^n h + (1 - a^n) / (1 - a) * B (x) x      (the ratio is n when a = 1)
+ *     y  = sum_n C[n] h[n,:] + D x                    (the n-th step's output)
+ * Arguments and layouts as cssd_step, plus nsteps >= 1 (else
+ * CSSD_ERR_INVALID_ARG); nsteps = 1 is exactly cssd_step.  a^n and the ratio are
+ * formed per (batch, head) in fp64, the ratio as expm1(n z) / expm1(z) with
+ * z = softplus(dt) A (accurate as a -> 1), the phases reduced mod 2 pi (so
+ * rotation angles stay exact to about 1e-16 * n |z| radians).
+ */
+int cssd_step_n(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                int64_t nsteps,
+                const float *x_re, const float *x_im,
+                const float *B_re, const float *B_im,
+                const float *C_re, const float *C_im,
+                const float *dt, const float *A_re, const float *A_im,
+                const float *Dskip,
+                float *h_re, float *h_im,
+                float *y_re, float *y_im, void *stream);
+
+/*
+ * The stationary output of an endless constant input, the limit of
+ * cssd_step_n's y as n grows (burn-mamba docs, module step_constant: the
+ * fixed point, which no starting state influences):
+ *     y = (sum_n C[n] B[n]) / (1 - a) * x + D x
+ * Meaningful for |a| < 1, i.e. softplus(dt) Re A < 0; otherwise the series
+ * does not converge and the formula's value is returned (inf or NaN where
+ * a = 1).  No state is read or written.  Arguments and layouts as cssd_step
+ * without h_re, h_im.
+ */
+int cssd_step_infinite(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                       const float *x_re, const float *x_im,
+                       const float *B_re, const float *B_im,
+                       const float *C_re, const float *C_im,
+                       const float *dt, const float *A_re, const float *A_im,
+                       const float *Dskip,
+                       float *y_re, float *y_im, void *stream);
+
+/*
  * Optional per-kernel timing (a measurement aid, not part of the operation).
  * While enabled, every kernel launch of cssd_forward/cssd_step is bracketed by
  * two hipEvents recorded on the caller's stream.  cssd_profile_read waits for
@@ -179,8 +221,9 @@ int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
  * per kernel id into ms[k] and launches[k] for k < min(capacity, number of
  * kernels), resets the accumulators and returns the number of kernel ids (or a
  * negative status on error).  Kernel ids: 0 cumsum, 1 chunk_state,
- * 2 state_pass, 3 chunk_scan, 4 step.  cssd_kernel_name(k) gives the device
- * symbol stem of each id (NULL if out of range).
+ * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite.
+ * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
+ * range).
  */
 int cssd_profile_enable(int on);
 int cssd_profile_read(double *ms, int64_t *launches, int capacity);

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("cssd_forward", "cssd_step", "cssd_forward_workspace_size",
-                     "cssd_status_string", "cssd_version"):
+    for required in ("cssd_forward", "cssd_step", "cssd_step_n", "cssd_step_infinite",
+                     "cssd_forward_workspace_size", "cssd_status_string", "cssd_version"):
         assert required in names
 
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 100
+    assert lib.cssd_version() == 101
     for st in range(5):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -136,6 +136,24 @@ def test_step_validation(lib):
     assert lib.cssd_step(1, 2, 16, 16, *bad, None) == 1
 
 
+def test_step_n_and_infinite_validation(lib):
+    base = 0x10000000
+    ptrs = [base + 0x100000 * i for i in range(14)]
+    ins, h, y = ptrs[:10], ptrs[10:12], ptrs[12:14]
+    assert lib.cssd_step_n(1, 2, 16, 16, 0, *ins, *h, *y, None) == 1      # nsteps < 1
+    assert lib.cssd_step_n(1, 2, 16, 16, -5, *ins, *h, *y, None) == 1
+    assert lib.cssd_step_n(1, 2, 16, 24, 3, *ins, *h, *y, None) == 2      # N not supported
+    assert lib.cssd_step_n(1, 2, 16, 16, 3, *ins, None, h[1], *y, None) == 1
+    assert lib.cssd_step_infinite(0, 2, 16, 16, *ins, *y, None) == 1
+    assert lib.cssd_step_infinite(1, 2, 16, 48, *ins, *y, None) == 2
+    bad = list(ins); bad[6] = None                                         # dt missing
+    assert lib.cssd_step_infinite(1, 2, 16, 16, *bad, *y, None) == 1
+    assert lib.cssd_step_infinite(1, 2, 16, 16, *ins, y[0], y[0], None) == 1  # y_re is y_im
+    assert lib.cssd_step_infinite(1, 2, 16, 16, *ins, ins[0], y[1], None) == 1  # y aliases x
+    misaligned = list(y); misaligned[0] = y[0] + 4
+    assert lib.cssd_step_infinite(1, 2, 16, 16, *ins, *misaligned, None) == 1
+
+
 def test_profiler_without_launches(lib):
     import complex_valued_state_amd as cssd
     with cssd.profile() as prof:
@@ -143,3 +161,4 @@ def test_profiler_without_launches(lib):
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
     assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(9) is None
+    assert lib.cssd_kernel_name(5) == b"k_step_infinite"
