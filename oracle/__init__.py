@@ -69,6 +69,9 @@ def _bind(lib):
     lib.oracle_step_n_f64.argtypes = [_i64] * 5 + [_d] * 10 + [_d] * 4 + [ctypes.c_int]
     lib.oracle_step_infinite_f64.restype = ctypes.c_int
     lib.oracle_step_infinite_f64.argtypes = [_i64] * 4 + [_d] * 10 + [_d] * 2 + [ctypes.c_int]
+    lib.oracle_backward_f64.restype = ctypes.c_int
+    lib.oracle_backward_f64.argtypes = [_i64] * 5 + [_d] * 10 + [_d] * 2 + [_d] * 4 + [_d] * 6 \
+        + [_d] * 1 + [_d] * 3 + [_d] * 2 + [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -192,6 +195,44 @@ def step_infinite(x, Bm, Cm, dt, A, Dskip, nthreads: int = 0, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_step_infinite_f64 failed")
     return yr + 1j * yi
+
+
+def backward(x, Bm, Cm, dt, A, Dskip, h0, dy, dhT=None, nthreads: int = 0, lib=None):
+    """Gradients of the forward recurrence for upstream dy (B,T,H,D) complex and
+    dhT (B,H,N,D) complex or None, as complex numbers dL/dRe + i dL/dIm.
+    Returns a dict with dx, dB, dC (input shapes, complex128), ddt (B,T,H),
+    dA (H,) complex, dD (H,) real and dh0 (B,H,N,D) complex."""
+    lib = lib or load()
+    x = np.asarray(x)
+    Bsz, T, H, D = x.shape
+    N = np.asarray(Bm).shape[-1]
+    xr, xi = _planes(x)
+    br, bi = _planes(Bm, (Bsz, T, H, N))
+    cr, ci = _planes(Cm, (Bsz, T, H, N))
+    dtv = _real(dt, (Bsz, T, H))
+    ar, ai = _planes(np.asarray(A, dtype=np.complex128), (H,))
+    ds = _real(Dskip, (H,)) if Dskip is not None else None
+    h0r, h0i = _planes(h0, (Bsz, H, N, D)) if h0 is not None else (None, None)
+    gyr, gyi = _planes(dy, (Bsz, T, H, D))
+    ghr, ghi = _planes(dhT, (Bsz, H, N, D)) if dhT is not None else (None, None)
+    out = {k: np.empty(shp) for k, shp in (("dxr", (Bsz, T, H, D)), ("dxi", (Bsz, T, H, D)),
+                                            ("dbr", (Bsz, T, H, N)), ("dbi", (Bsz, T, H, N)),
+                                            ("dcr", (Bsz, T, H, N)), ("dci", (Bsz, T, H, N)),
+                                            ("ddt", (Bsz, T, H)), ("dar", (H,)), ("dai", (H,)),
+                                            ("dd", (H,)), ("dh0r", (Bsz, H, N, D)),
+                                            ("dh0i", (Bsz, H, N, D)))}
+    rc = lib.oracle_backward_f64(Bsz, T, H, D, N, _p(xr), _p(xi), _p(br), _p(bi), _p(cr), _p(ci),
+                                 _p(dtv), _p(ar), _p(ai), _p(ds), _p(h0r), _p(h0i), _p(gyr),
+                                 _p(gyi), _p(ghr), _p(ghi), _p(out["dxr"]), _p(out["dxi"]),
+                                 _p(out["dbr"]), _p(out["dbi"]), _p(out["dcr"]), _p(out["dci"]),
+                                 _p(out["ddt"]), _p(out["dar"]), _p(out["dai"]), _p(out["dd"]),
+                                 _p(out["dh0r"]), _p(out["dh0i"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_backward_f64 failed")
+    return {"dx": out["dxr"] + 1j * out["dxi"], "dB": out["dbr"] + 1j * out["dbi"],
+            "dC": out["dcr"] + 1j * out["dci"], "ddt": out["ddt"],
+            "dA": out["dar"] + 1j * out["dai"], "dD": out["dd"],
+            "dh0": out["dh0r"] + 1j * out["dh0i"]}
 
 
 def max_threads(lib=None) -> int:

@@ -307,6 +307,165 @@ int oracle_step_infinite_f64(int64_t Bsz, int64_t H, int64_t D, int64_t N,
     return 0;
 }
 
+/*
+ * Gradients of the forward recurrence (reverse mode, one (batch, head) at a
+ * time).  The pages train this scan with automatic differentiation of complex
+ * tensors (Mamba-3-Lite docs, "SSD Theory", the autograd notes, and "The
+ * Chunkwise Complex SSD Algorithm", the complex-dtype requirement); the
+ * gradient of a real loss L with respect to a complex value u + i v is taken as
+ * the pair (dL/du, dL/dv), written as the complex number dL/du + i dL/dv.
+ * With that convention, for a product w = c z the gradient reaching z is
+ * conj(c) times the gradient of w, and the one reaching c is the gradient of w
+ * times conj(z).  Walking the recurrence backwards with G = dL/dh_t:
+ *   G      += conj(C_t) (x) dy_t                      readout of step t
+ *   dC_t[n] = sum_p dy_t[p] conj(h_t[n,p])
+ *   dx_t[p] = sum_n conj(B_t[n]) G[n,p] + Dskip dy_t[p]
+ *   dB_t[n] = sum_p G[n,p] conj(x_t[p])
+ *   dz_t    = conj(a_t) sum_{n,p} G[n,p] conj(h_{t-1}[n,p])   z_t = s_t A, a_t = exp(z_t)
+ *   ddt_t   = sigmoid(dt_t) Re(dz_t conj(A)),  dA += s_t dz_t,
+ *   dDskip += Re(sum_p dy_t[p] conj(x_t[p]))
+ *   G       = conj(a_t) G                              back to h_{t-1}
+ * starting from G = dL/dh_T (dhT, or zero) and ending with dh0 = G.
+ * Inputs as oracle_forward_f64 plus dy [B,T,H,D] and dhT [B,H,N,D] (or NULL);
+ * outputs dx, dB, dC (input layouts), ddt [B,T,H], dA [H] and dDskip [H]
+ * (summed over batch and time; dDskip may be NULL), dh0 [B,H,N,D] (or NULL).
+ */
+int oracle_backward_f64(int64_t Bsz, int64_t T, int64_t H, int64_t D, int64_t N,
+                        const double *x_re, const double *x_im,
+                        const double *b_re, const double *b_im,
+                        const double *c_re, const double *c_im,
+                        const double *dt, const double *a_re, const double *a_im,
+                        const double *dskip,
+                        const double *h0_re, const double *h0_im,
+                        const double *dy_re, const double *dy_im,
+                        const double *dhT_re, const double *dhT_im,
+                        double *dx_re, double *dx_im, double *db_re, double *db_im,
+                        double *dc_re, double *dc_im, double *ddt,
+                        double *da_re, double *da_im, double *dd,
+                        double *dh0_re, double *dh0_im, int nthreads)
+{
+    if (Bsz <= 0 || T < 1 || H <= 0 || D <= 0 || N <= 0)
+        return -1;
+    if (!x_re || !x_im || !b_re || !b_im || !c_re || !c_im || !dt || !a_re || !a_im ||
+        !dy_re || !dy_im || !dx_re || !dx_im || !db_re || !db_im || !dc_re || !dc_im ||
+        !ddt || !da_re || !da_im)
+        return -1;
+    const int64_t ND = N * D;
+    /* per (b, h) partial sums of dA and dDskip, reduced in a fixed order below */
+    double *pa = (double *)calloc((size_t)(Bsz * H * 3), sizeof(double));
+    if (!pa)
+        return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t bh = 0; bh < Bsz * H; ++bh) {
+        int64_t b = bh / H, h = bh % H;
+        /* states h_{-1} .. h_{T-1}, then the running gradient */
+        double complex *hs = (double complex *)malloc(sizeof(double complex) * (size_t)((T + 1) * ND));
+        double complex *G = (double complex *)malloc(sizeof(double complex) * (size_t)ND);
+        if (!hs || !G) {
+            free(hs);
+            free(G);
+            failed |= 1;
+            continue;
+        }
+        double complex A = a_re[h] + a_im[h] * I;
+        double d = dskip ? dskip[h] : 0.0;
+        for (int64_t k = 0; k < ND; ++k)
+            hs[k] = (h0_re && h0_im) ? h0_re[bh * ND + k] + h0_im[bh * ND + k] * I : 0.0;
+        /* forward, keeping every state */
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t row = (b * T + t) * H + h;
+            double complex a = cexp(softplus(dt[row]) * A);
+            const double complex *hp = hs + t * ND;
+            double complex *hn = hs + (t + 1) * ND;
+            for (int64_t n = 0; n < N; ++n) {
+                double complex bn = b_re[row * N + n] + b_im[row * N + n] * I;
+                for (int64_t p = 0; p < D; ++p)
+                    hn[n * D + p] = a * hp[n * D + p] +
+                                    bn * (x_re[row * D + p] + x_im[row * D + p] * I);
+            }
+        }
+        /* backward */
+        for (int64_t k = 0; k < ND; ++k)
+            G[k] = (dhT_re && dhT_im) ? dhT_re[bh * ND + k] + dhT_im[bh * ND + k] * I : 0.0;
+        double complex dA = 0.0;
+        double dD = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            int64_t row = (b * T + t) * H + h;
+            double s = softplus(dt[row]);
+            double complex a = cexp(s * A);
+            const double complex *ht = hs + (t + 1) * ND, *hp = hs + t * ND;
+            for (int64_t n = 0; n < N; ++n) {
+                double complex cn = c_re[row * N + n] + c_im[row * N + n] * I;
+                for (int64_t p = 0; p < D; ++p)
+                    G[n * D + p] += conj(cn) * (dy_re[row * D + p] + dy_im[row * D + p] * I);
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                double complex acc = 0.0;
+                for (int64_t p = 0; p < D; ++p)
+                    acc += (dy_re[row * D + p] + dy_im[row * D + p] * I) * conj(ht[n * D + p]);
+                dc_re[row * N + n] = creal(acc);
+                dc_im[row * N + n] = cimag(acc);
+            }
+            for (int64_t p = 0; p < D; ++p) {
+                double complex dyp = dy_re[row * D + p] + dy_im[row * D + p] * I;
+                double complex xp = x_re[row * D + p] + x_im[row * D + p] * I;
+                double complex acc = d * dyp;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += conj(b_re[row * N + n] + b_im[row * N + n] * I) * G[n * D + p];
+                dx_re[row * D + p] = creal(acc);
+                dx_im[row * D + p] = cimag(acc);
+                dD += creal(dyp * conj(xp));
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                double complex acc = 0.0;
+                for (int64_t p = 0; p < D; ++p)
+                    acc += G[n * D + p] * conj(x_re[row * D + p] + x_im[row * D + p] * I);
+                db_re[row * N + n] = creal(acc);
+                db_im[row * N + n] = cimag(acc);
+            }
+            double complex ga = 0.0;
+            for (int64_t k = 0; k < ND; ++k)
+                ga += G[k] * conj(hp[k]);
+            double complex dz = conj(a) * ga;
+            ddt[row] = creal(dz * conj(A)) / (1.0 + exp(-dt[row]));
+            dA += s * dz;
+            for (int64_t k = 0; k < ND; ++k)
+                G[k] = conj(a) * G[k];
+        }
+        if (dh0_re && dh0_im)
+            for (int64_t k = 0; k < ND; ++k) {
+                dh0_re[bh * ND + k] = creal(G[k]);
+                dh0_im[bh * ND + k] = cimag(G[k]);
+            }
+        pa[3 * bh] = creal(dA);
+        pa[3 * bh + 1] = cimag(dA);
+        pa[3 * bh + 2] = dD;
+        free(hs);
+        free(G);
+    }
+    for (int64_t h = 0; h < H; ++h) {
+        double sr = 0.0, si = 0.0, sd = 0.0;
+        for (int64_t b = 0; b < Bsz; ++b) {
+            sr += pa[3 * (b * H + h)];
+            si += pa[3 * (b * H + h) + 1];
+            sd += pa[3 * (b * H + h) + 2];
+        }
+        da_re[h] = sr;
+        da_im[h] = si;
+        if (dd)
+            dd[h] = sd;
+    }
+    free(pa);
+    return failed ? -1 : 0;
+}
+
 /* Threads OpenMP would use for a parallel region (1 without OpenMP). */
 int oracle_max_threads(void)
 {

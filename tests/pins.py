@@ -252,6 +252,72 @@ def pin_step_infinite_against_recurrence(lib):
 
 
 # ---------------------------------------------------------------------------
+# f1: gradients -- central finite differences of the forward oracle
+# ---------------------------------------------------------------------------
+def _fd_loss(lib, args, gy, ghT):
+    """L = <dy, y> + <dhT, hT>, the real inner product of the re/im planes."""
+    y, hT = oracle.forward(*args, lib=lib)
+    return float(np.sum(gy.real * y.real + gy.imag * y.imag)
+                 + np.sum(ghT.real * hT.real + ghT.imag * hT.imag))
+
+
+def pin_backward_finite_differences(lib):
+    """Every gradient entry of a small problem against a central difference of the
+    forward oracle's loss (step 1e-6 in fp64): dt, A, Dskip and every re / im
+    element of x, B, C and h0.  Independent of the reverse-mode code: it only
+    calls the forward recurrence."""
+    rng = np.random.default_rng(909)
+    Bsz, T, H, D, N = 2, 5, 2, 3, 2
+    x, Bm, Cm, dt, A, Dk, h0 = _rand_problem(rng, Bsz, T, H, D, N)
+    gy, ghT = crandn(rng, Bsz, T, H, D), crandn(rng, Bsz, H, N, D)
+    g = oracle.backward(x, Bm, Cm, dt, A, Dk, h0, gy, ghT, lib=lib)
+    base = {"x": x, "Bm": Bm, "Cm": Cm, "dt": dt, "A": A, "Dk": Dk, "h0": h0}
+    order = ("x", "Bm", "Cm", "dt", "A", "Dk", "h0")
+    want = {"x": g["dx"], "Bm": g["dB"], "Cm": g["dC"], "dt": g["ddt"], "A": g["dA"],
+            "Dk": g["dD"], "h0": g["dh0"]}
+    eps = 1e-6
+    for name in order:
+        v = base[name]
+        parts = (1.0, 1j) if np.iscomplexobj(v) else (1.0,)
+        fd = np.zeros(v.shape, dtype=np.complex128)
+        for idx in np.ndindex(v.shape):
+            for unit in parts:
+                vals = []
+                for sign in (1.0, -1.0):
+                    w = v.copy()
+                    w[idx] += sign * eps * unit
+                    args = tuple(w if k == name else base[k] for k in order)
+                    vals.append(_fd_loss(lib, args, gy, ghT))
+                fd[idx] += (vals[0] - vals[1]) / (2 * eps) * (1.0 if unit == 1.0 else 1j)
+        got = want[name]
+        err = float(np.max(np.abs(fd - got)) / max(np.max(np.abs(fd)), 1e-30))
+        assert err < 1e-7, (name, err)
+
+
+def pin_backward_without_initial_state(lib):
+    """With no initial state and no final-state gradient, the same check on the
+    inputs that remain (the oracle's NULL paths); B = C = 0 leaves only the skip:
+    dx = D dy."""
+    rng = np.random.default_rng(910)
+    Bsz, T, H, D, N = 1, 4, 2, 2, 3
+    x, Bm, Cm, dt, A, Dk, _ = _rand_problem(rng, Bsz, T, H, D, N, with_h0=False)
+    gy = crandn(rng, Bsz, T, H, D)
+    zero_hT = np.zeros((Bsz, H, N, D), dtype=np.complex128)
+    g = oracle.backward(x, Bm, Cm, dt, A, Dk, None, gy, None, lib=lib)
+    eps = 1e-6
+    for k in np.ndindex(dt.shape):
+        w = dt.copy(); w[k] += eps
+        lp = _fd_loss(lib, (x, Bm, Cm, w, A, Dk, None), gy, zero_hT)
+        w[k] -= 2 * eps
+        lm = _fd_loss(lib, (x, Bm, Cm, w, A, Dk, None), gy, zero_hT)
+        assert abs((lp - lm) / (2 * eps) - g["ddt"][k]) < 1e-7 * max(1.0, np.max(np.abs(g["ddt"])))
+    zB = np.zeros_like(Bm)
+    g0 = oracle.backward(x, zB, zB, dt, A, Dk, None, gy, None, lib=lib)
+    assert rel_err(g0["dx"], Dk[None, None, :, None] * gy) < 1e-15
+    assert np.max(np.abs(g0["dB"])) == 0 and np.max(np.abs(g0["ddt"])) == 0
+
+
+# ---------------------------------------------------------------------------
 # p6: decay zero -- the scan reduces to per-step outer products
 # ---------------------------------------------------------------------------
 def pin_decay_zero(lib):
@@ -409,5 +475,6 @@ def pin_golden_modulus_drift(lib):
 
 ALL_PINS = [pin_bruteforce, pin_impulse, pin_constant_input, pin_fixed_point,
             pin_step_n_against_recurrence, pin_step_infinite_against_recurrence,
+            pin_backward_finite_differences, pin_backward_without_initial_state,
             pin_step_constant_input, pin_decay_zero, pin_homogeneous, pin_linearity_and_skip,
             pin_pam_dual_form, pin_pam_orthogonal_keys, pin_golden_modulus_drift]

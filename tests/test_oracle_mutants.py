@@ -60,6 +60,18 @@ MUTANTS = {
                                     "double complex yv = gain * xp;")],
     "step_infinite_gain_inverted": [("double complex gain = score / (1.0 - a);",
                                      "double complex gain = score * (1.0 - a);")],
+    "backward_readout_not_conjugated": [("G[n * D + p] += conj(cn) * (dy_re[row * D + p]",
+                                         "G[n * D + p] += cn * (dy_re[row * D + p]")],
+    "backward_decay_not_conjugated": [("G[k] = conj(a) * G[k];", "G[k] = a * G[k];")],
+    "backward_skip_dropped": [("double complex acc = d * dyp;", "double complex acc = 0.0;")],
+    "backward_softplus_slope_dropped": [
+        ("ddt[row] = creal(dz * conj(A)) / (1.0 + exp(-dt[row]));",
+         "ddt[row] = creal(dz * conj(A));")],
+    "backward_decay_grad_uses_new_state": [("ga += G[k] * conj(hp[k]);", "ga += G[k] * conj(ht[k]);")],
+    "backward_dA_without_step_size": [("dA += s * dz;", "dA += dz;")],
+    "backward_dC_uses_previous_state": [
+        ("acc += (dy_re[row * D + p] + dy_im[row * D + p] * I) * conj(ht[n * D + p]);",
+         "acc += (dy_re[row * D + p] + dy_im[row * D + p] * I) * conj(hp[n * D + p]);")],
 }
 
 
