@@ -178,6 +178,55 @@ def time_constant_input(B, H, D, N, nsteps, reps, warmup, dev, seed=4):
     return res
 
 
+def backward_dxdb_flops(B, T, H, D, N, C):
+    """Algorithmic real flops of k_bwd_dxdb: per chunk, over the causal triangle,
+    the score C B^T (tri x N), P = dY X^H (tri x D), the products giving dX (tri x D)
+    and dB (tri x N), and the two state terms conj(B) R and conj(X) R^T (C x N x D
+    each); 8 real flops per complex MAC."""
+    nC = -(-T // C)
+    tri = C * (C + 1) // 2
+    return 8 * B * H * nC * (tri * 2 * (N + D) + 2 * C * N * D)
+
+
+def time_backward(inp, steps, warmup, dev, seed=9):
+    """cssd_backward with the forward output and seeded upstream gradients resident."""
+    import torch
+    import complex_valued_state_amd as cssd
+    a = _to_dev(inp, dev)
+    d = dict(zip(("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt", "A_re", "A_im", "Dskip"), a))
+    d["h0"] = None
+    Bsz, T, H, D = inp.x_re.shape
+    N = inp.B_re.shape[-1]
+    g = torch.Generator(device=dev).manual_seed(seed)
+    r = math.sqrt(0.5)
+    dy = [torch.randn((Bsz, T, H, D), generator=g, device=dev) * r for _ in range(2)]
+    dhT = [torch.randn((Bsz, H, N, D), generator=g, device=dev) * r for _ in range(2)]
+    y = cssd.cssd_forward(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"],
+                          d["dt"], d["A_re"], d["A_im"], d["Dskip"], d["h0"], chunk=inp.chunk,
+                          return_state=False)[:2]
+    ws = torch.empty(cssd.cssd_backward_workspace_size(Bsz, T, H, D, N, inp.chunk),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        cssd.cssd_backward(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"],
+                           d["dt"], d["A_re"], d["A_im"], d["Dskip"], d["h0"], y, dy, dhT,
+                           chunk=inp.chunk, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with cssd.profile() as prof:
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+    kern = {k: v / max(prof.launches[k], 1) for k, v in prof.ms.items() if prof.launches[k]}
+    return e0.elapsed_time(e1) / steps, kern
+
+
 def time_decode(B, H, D, N, tokens, warmup, dev, seed=4):
     """cssd_step over `tokens` pre-staged tokens (seeded device-side draws)."""
     import torch
@@ -324,6 +373,19 @@ def main():
             "kernels_avg_ms": {k: round(v, 5) for k, v in kern16.items()}}
         del inp16
         d4 = wl.CONFIG_SHAPES[4]
+        progress("timing the backward pass")
+        bms, bk = time_backward(inp, max(3, args.steps // 2), 2, dev)
+        bfl = backward_dxdb_flops(B, T, H, D, N, C)
+        extra["backward_cfg1_B8_T2048_H48_D64_N64_C64_f32"] = {
+            "tokens_per_s": round(tokens / (bms * 1e-3), 1), "ms_per_step": round(bms, 4),
+            "kernels_avg_ms": {k: round(v, 5) for k, v in bk.items()},
+            "roofline": {"bound": "mfma", "kernel": "k_bwd_dxdb",
+                         "achieved": round(bfl / (bk["k_bwd_dxdb"] * 1e-3) / 1e12, 2),
+                         "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(bfl / (bk["k_bwd_dxdb"] * 1e-3) / 1e12
+                                       / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": bfl,
+                         "avg_launch_ms": round(bk["k_bwd_dxdb"], 5)}}
         progress("timing the decode step")
         dms, dkms = time_decode(d4["B"], d4["H"], d4["D"], d4["N"], d4["steps"], 8, dev)
         dbytes = decode_hbm_bytes(d4["B"], d4["H"], d4["D"], d4["N"])

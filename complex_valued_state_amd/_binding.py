@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libcssd.so")
 CSSD_OK, CSSD_ERR_INVALID_ARG, CSSD_ERR_UNSUPPORTED, CSSD_ERR_WORKSPACE, CSSD_ERR_HIP = range(5)
 CSSD_F32, CSSD_BF16 = 0, 1
 KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
-                "k_step_infinite")
+                "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz")
 
 _lock = threading.Lock()
 _lib = None
@@ -54,6 +54,11 @@ def load_library(path: Optional[str] = None):
         lib.cssd_forward.restype = ctypes.c_int
         lib.cssd_forward.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 \
             + [_vp] * 4 + [_vp, _sz, _vp]
+        lib.cssd_backward_workspace_size.restype = ctypes.c_int
+        lib.cssd_backward_workspace_size.argtypes = [_i64] * 6 + [ctypes.POINTER(_sz)]
+        lib.cssd_backward.restype = ctypes.c_int
+        lib.cssd_backward.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 \
+            + [_vp] * 2 + [_vp] * 4 + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 + [_vp, _sz, _vp]
         lib.cssd_step.restype = ctypes.c_int
         lib.cssd_step.argtypes = [_i64] * 4 + [_vp] * 10 + [_vp] * 4 + [_vp]
         lib.cssd_step_n.restype = ctypes.c_int
@@ -90,6 +95,16 @@ def cssd_forward_workspace_size(batch: int, seqlen: int, nheads: int, headdim: i
                                                     ctypes.byref(out))
     if st != CSSD_OK:
         raise CSSDError(st, "cssd_forward_workspace_size")
+    return int(out.value)
+
+
+def cssd_backward_workspace_size(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                 chunk: int) -> int:
+    out = _sz(0)
+    st = load_library().cssd_backward_workspace_size(batch, seqlen, nheads, headdim, dstate, chunk,
+                                                     ctypes.byref(out))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_backward_workspace_size")
     return int(out.value)
 
 
@@ -187,6 +202,61 @@ def cssd_forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None,
     if st != CSSD_OK:
         raise CSSDError(st, "cssd_forward")
     return y_re, y_im, hT_re, hT_im
+
+
+def cssd_backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, dy, dhT=None,
+                  *, chunk: int, want_dh0: bool = True, workspace=None, stream=None):
+    """Gradients of cssd_forward (see include/cssd.h): planar (dL/dRe, dL/dIm) pairs.
+
+    The first arguments are the forward inputs (float32); h0 as in cssd_forward;
+    y = (y_re, y_im) is the forward output for these inputs, dy = (dy_re, dy_im)
+    its upstream gradient, dhT = (dhT_re, dhT_im) that of the final state or None.
+    Returns a dict of float32 tensors: dx_re, dx_im, dB_re, dB_im, dC_re, dC_im,
+    ddt, dA_re, dA_im, dD (None without Dskip), dh0_re, dh0_im (None unless
+    want_dh0)."""
+    torch = _torch()
+    lib = load_library()
+    dev = x_re.device
+    Bsz, T, H, D = x_re.shape
+    N = B_re.shape[-1]
+    f32 = (torch.float32,)
+    p = {}
+    for name, t, shp in (("x_re", x_re, (Bsz, T, H, D)), ("x_im", x_im, (Bsz, T, H, D)),
+                         ("B_re", B_re, (Bsz, T, H, N)), ("B_im", B_im, (Bsz, T, H, N)),
+                         ("C_re", C_re, (Bsz, T, H, N)), ("C_im", C_im, (Bsz, T, H, N)),
+                         ("dt", dt, (Bsz, T, H)), ("A_re", A_re, (H,)), ("A_im", A_im, (H,)),
+                         ("y_re", y[0], (Bsz, T, H, D)), ("y_im", y[1], (Bsz, T, H, D)),
+                         ("dy_re", dy[0], (Bsz, T, H, D)), ("dy_im", dy[1], (Bsz, T, H, D))):
+        p[name] = _check(t, name, shp, f32, dev)
+    p["Dskip"] = None if Dskip is None else _check(Dskip, "Dskip", (H,), f32, dev)
+    for key, pair, shp in (("h0", h0, (Bsz, H, N, D)), ("dhT", dhT, (Bsz, H, N, D))):
+        p[key + "_re"] = None if pair is None else _check(pair[0], key + "_re", shp, f32, dev)
+        p[key + "_im"] = None if pair is None else _check(pair[1], key + "_im", shp, f32, dev)
+    e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    g = {"dx_re": e(Bsz, T, H, D), "dx_im": e(Bsz, T, H, D), "dB_re": e(Bsz, T, H, N),
+         "dB_im": e(Bsz, T, H, N), "dC_re": e(Bsz, T, H, N), "dC_im": e(Bsz, T, H, N),
+         "ddt": e(Bsz, T, H), "dA_re": e(H), "dA_im": e(H),
+         "dD": e(H) if Dskip is not None else None,
+         "dh0_re": e(Bsz, H, N, D) if want_dh0 else None,
+         "dh0_im": e(Bsz, H, N, D) if want_dh0 else None}
+    need = cssd_backward_workspace_size(Bsz, T, H, D, N, chunk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.cssd_backward(Bsz, T, H, D, N, int(chunk), CSSD_F32,
+                           p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
+                           p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"],
+                           p["y_re"], p["y_im"], p["dy_re"], p["dy_im"], p["dhT_re"],
+                           p["dhT_im"], *(ptr(g[k]) for k in ("dx_re", "dx_im", "dB_re", "dB_im",
+                                                             "dC_re", "dC_im", "ddt", "dA_re",
+                                                             "dA_im", "dD", "dh0_re", "dh0_im")),
+                           workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_backward")
+    return g
 
 
 def _step_ptrs(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h, Bsz, H, N, D, out):

@@ -105,6 +105,41 @@ Layout layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C) 
     return l;
 }
 
+// The gradient pass: the forward workspace, then its own regions.
+struct BwdLayout {
+    Layout fwd;
+    size_t r_re, r_im, q1_re, q1_im, q2_re, q2_im, ddp, hT_re, hT_im, z_re, z_im, pa, total;
+};
+
+BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C) {
+    BwdLayout l;
+    l.fwd = layout(B, T, H, D, N, C);
+    const int64_t nC = (T + C - 1) / C;
+    const size_t P = (size_t)(B * H * nC * C);
+    const size_t S = (size_t)(B * H * nC) * (size_t)(N * D);
+    const size_t HS = (size_t)(B * H) * (size_t)(N * D);
+    size_t off = l.fwd.total;
+    auto put = [&](size_t bytes) {
+        const size_t at = off;
+        off = round_up(off + bytes);
+        return at;
+    };
+    l.r_re = put(S * sizeof(float));
+    l.r_im = put(S * sizeof(float));
+    l.q1_re = put(P * sizeof(float));
+    l.q1_im = put(P * sizeof(float));
+    l.q2_re = put(P * sizeof(float));
+    l.q2_im = put(P * sizeof(float));
+    l.ddp = put(P * sizeof(float));
+    l.hT_re = put(HS * sizeof(float));
+    l.hT_im = put(HS * sizeof(float));
+    l.z_re = put((size_t)(B * H * nC) * sizeof(double));
+    l.z_im = put((size_t)(B * H * nC) * sizeof(double));
+    l.pa = put((size_t)(B * H) * 3 * sizeof(double));
+    l.total = off;
+    return l;
+}
+
 int check_shape(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C) {
     if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || N <= 0 || C <= 0) return CSSD_ERR_INVALID_ARG;
     if (!pow2_16_128(D) || !pow2_16_128(N) || !pow2_16_128(C)) return CSSD_ERR_UNSUPPORTED;
@@ -115,6 +150,40 @@ int check_shape(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C
     if (B * H > lim / (nC * C) || B * nC * C * H > lim / m) return CSSD_ERR_UNSUPPORTED;
     if (B * H * nC > lim / (N * D)) return CSSD_ERR_UNSUPPORTED;
     return CSSD_OK;
+}
+
+cssd::FwdArgs fwd_args(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int64_t chunk, int32_t in_dtype, const void* x_re,
+                       const void* x_im, const void* B_re, const void* B_im, const void* C_re,
+                       const void* C_im, const float* dt, const float* A_re, const float* A_im,
+                       const float* Dskip, const float* h0_re, const float* h0_im, float* y_re,
+                       float* y_im, float* hT_re, float* hT_im, char* ws, const Layout& L) {
+    cssd::FwdArgs a;
+    a.B = batch;
+    a.T = seqlen;
+    a.H = nheads;
+    a.D = headdim;
+    a.N = dstate;
+    a.C = chunk;
+    a.nC = (seqlen + chunk - 1) / chunk;
+    a.in_dtype = in_dtype;
+    a.x_re = x_re; a.x_im = x_im;
+    a.b_re = B_re; a.b_im = B_im;
+    a.c_re = C_re; a.c_im = C_im;
+    a.dt = dt; a.a_re = A_re; a.a_im = A_im; a.dskip = Dskip;
+    a.h0_re = h0_re; a.h0_im = h0_im;
+    a.y_re = y_re; a.y_im = y_im; a.hT_re = hT_re; a.hT_im = hT_im;
+    a.acs_re = reinterpret_cast<double*>(ws + L.acs_re);
+    a.acs_im = reinterpret_cast<double*>(ws + L.acs_im);
+    a.e_re = reinterpret_cast<float*>(ws + L.e_re);
+    a.e_im = reinterpret_cast<float*>(ws + L.e_im);
+    a.w_re = reinterpret_cast<float*>(ws + L.w_re);
+    a.w_im = reinterpret_cast<float*>(ws + L.w_im);
+    a.cd_re = reinterpret_cast<float*>(ws + L.cd_re);
+    a.cd_im = reinterpret_cast<float*>(ws + L.cd_im);
+    a.st_re = reinterpret_cast<float*>(ws + L.st_re);
+    a.st_im = reinterpret_cast<float*>(ws + L.st_im);
+    return a;
 }
 
 }  // namespace
@@ -180,33 +249,9 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
         (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return CSSD_ERR_WORKSPACE;
 
-    char* ws = static_cast<char*>(workspace);
-    cssd::FwdArgs a;
-    a.B = batch;
-    a.T = seqlen;
-    a.H = nheads;
-    a.D = headdim;
-    a.N = dstate;
-    a.C = chunk;
-    a.nC = (seqlen + chunk - 1) / chunk;
-    a.in_dtype = in_dtype;
-    a.x_re = x_re; a.x_im = x_im;
-    a.b_re = B_re; a.b_im = B_im;
-    a.c_re = C_re; a.c_im = C_im;
-    a.dt = dt; a.a_re = A_re; a.a_im = A_im; a.dskip = Dskip;
-    a.h0_re = h0_re; a.h0_im = h0_im;
-    a.y_re = y_re; a.y_im = y_im; a.hT_re = hT_re; a.hT_im = hT_im;
-    a.acs_re = reinterpret_cast<double*>(ws + L.acs_re);
-    a.acs_im = reinterpret_cast<double*>(ws + L.acs_im);
-    a.e_re = reinterpret_cast<float*>(ws + L.e_re);
-    a.e_im = reinterpret_cast<float*>(ws + L.e_im);
-    a.w_re = reinterpret_cast<float*>(ws + L.w_re);
-    a.w_im = reinterpret_cast<float*>(ws + L.w_im);
-    a.cd_re = reinterpret_cast<float*>(ws + L.cd_re);
-    a.cd_im = reinterpret_cast<float*>(ws + L.cd_im);
-    a.st_re = reinterpret_cast<float*>(ws + L.st_re);
-    a.st_im = reinterpret_cast<float*>(ws + L.st_im);
-
+    cssd::FwdArgs a = fwd_args(batch, seqlen, nheads, headdim, dstate, chunk, in_dtype, x_re, x_im,
+                               B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im, y_re,
+                               y_im, hT_re, hT_im, static_cast<char*>(workspace), L);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
@@ -215,6 +260,112 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     if (timed(cssd::K_STATE_PASS, s, [&] { return cssd::launch_state_pass(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     if (timed(cssd::K_CHUNK_SCAN, s, [&] { return cssd::launch_chunk_scan(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    return CSSD_OK;
+}
+
+int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                 int64_t dstate, int64_t chunk, size_t* bytes) {
+    if (bytes == nullptr) return CSSD_ERR_INVALID_ARG;
+    const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
+    if (st != CSSD_OK) return st;
+    *bytes = bwd_layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
+    return CSSD_OK;
+}
+
+int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                  int64_t chunk, int32_t in_dtype, const void* x_re, const void* x_im,
+                  const void* B_re, const void* B_im, const void* C_re, const void* C_im,
+                  const float* dt, const float* A_re, const float* A_im, const float* Dskip,
+                  const float* h0_re, const float* h0_im, const float* y_re, const float* y_im,
+                  const float* dy_re, const float* dy_im, const float* dhT_re,
+                  const float* dhT_im, float* dx_re, float* dx_im, float* dB_re, float* dB_im,
+                  float* dC_re, float* dC_im, float* ddt, float* dA_re, float* dA_im, float* dD,
+                  float* dh0_re, float* dh0_im, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
+    if (st != CSSD_OK) return st;
+    if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
+    if (in_dtype != CSSD_F32) return CSSD_ERR_UNSUPPORTED;
+    // row-vector reads need 16 bytes; the gradients are written element-wise
+    const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, y_re, y_im,
+                         dy_re, dy_im, dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt,
+                         dA_re, dA_im};
+    const uintptr_t req_al[] = {16, 16, 16, 16, 16, 16, 4, 4, 4, 16, 16,
+                                16, 16, 4, 4, 4, 4, 4, 4, 4, 4, 4};
+    for (int i = 0; i < 22; ++i)
+        if (req[i] == nullptr || !aligned(req[i], req_al[i])) return CSSD_ERR_INVALID_ARG;
+    if ((h0_re == nullptr) != (h0_im == nullptr) || (dhT_re == nullptr) != (dhT_im == nullptr) ||
+        (dh0_re == nullptr) != (dh0_im == nullptr))
+        return CSSD_ERR_INVALID_ARG;
+    const void* opt[] = {Dskip, h0_re, h0_im, dhT_re, dhT_im, dD, dh0_re, dh0_im};
+    const uintptr_t opt_al[] = {4, 16, 16, 16, 16, 4, 16, 16};
+    for (int i = 0; i < 8; ++i)
+        if (opt[i] != nullptr && !aligned(opt[i], opt_al[i])) return CSSD_ERR_INVALID_ARG;
+    const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re,
+                         h0_im, y_re, y_im, dy_re, dy_im, dhT_re, dhT_im};
+    const void* outs[] = {dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt, dA_re, dA_im, dD,
+                          dh0_re, dh0_im};
+    for (int i = 0; i < 12; ++i) {
+        if (outs[i] == nullptr) continue;
+        for (const void* in : ins)
+            if (outs[i] == in) return CSSD_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (outs[i] == outs[j]) return CSSD_ERR_INVALID_ARG;
+    }
+
+    const BwdLayout L = bwd_layout(batch, seqlen, nheads, headdim, dstate, chunk);
+    if (workspace == nullptr || workspace_bytes < L.total ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return CSSD_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    cssd::BwdArgs a;
+    // the recomputed forward writes its final state into the workspace, not y
+    a.f = fwd_args(batch, seqlen, nheads, headdim, dstate, chunk, in_dtype, x_re, x_im, B_re,
+                   B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im, nullptr, nullptr,
+                   reinterpret_cast<float*>(ws + L.hT_re), reinterpret_cast<float*>(ws + L.hT_im),
+                   ws, L.fwd);
+    a.y_re = y_re; a.y_im = y_im; a.dy_re = dy_re; a.dy_im = dy_im;
+    a.dhT_re = dhT_re; a.dhT_im = dhT_im;
+    a.dx_re = dx_re; a.dx_im = dx_im; a.db_re = dB_re; a.db_im = dB_im;
+    a.dc_re = dC_re; a.dc_im = dC_im; a.ddt = ddt; a.da_re = dA_re; a.da_im = dA_im; a.dd = dD;
+    a.dh0_re = dh0_re; a.dh0_im = dh0_im;
+    a.r_re = reinterpret_cast<float*>(ws + L.r_re);
+    a.r_im = reinterpret_cast<float*>(ws + L.r_im);
+    a.q1_re = reinterpret_cast<float*>(ws + L.q1_re);
+    a.q1_im = reinterpret_cast<float*>(ws + L.q1_im);
+    a.q2_re = reinterpret_cast<float*>(ws + L.q2_re);
+    a.q2_im = reinterpret_cast<float*>(ws + L.q2_im);
+    a.ddp = reinterpret_cast<float*>(ws + L.ddp);
+    a.hT_re = a.f.hT_re;
+    a.hT_im = a.f.hT_im;
+    a.z_re = reinterpret_cast<double*>(ws + L.z_re);
+    a.z_im = reinterpret_cast<double*>(ws + L.z_im);
+    a.pa = reinterpret_cast<double*>(ws + L.pa);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // forward recomputation: cumsums, chunk states, carry-in states H_c and hT
+    if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a.f, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_CHUNK_STATE, s, [&] { return cssd::launch_chunk_state(a.f, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_STATE_PASS, s, [&] { return cssd::launch_state_pass(a.f, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    // adjoint chunk states and the backward pass over chunks: R_{c+1}, dh0
+    if (timed(cssd::K_CHUNK_STATE, s, [&] {
+            return cssd::launch_chunk_state_adjoint(a.f, dy_re, dy_im, a.r_re, a.r_im, s);
+        }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_STATE_PASS, s, [&] {
+            return cssd::launch_state_pass_adjoint(a.f, a.r_re, a.r_im, dhT_re, dhT_im, dh0_re,
+                                                   dh0_im, s);
+        }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_BWD_DXDB, s, [&] { return cssd::launch_bwd_dxdb(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_BWD_DC, s, [&] { return cssd::launch_bwd_dc(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_BWD_DZ, s, [&] { return cssd::launch_bwd_dz(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     return CSSD_OK;
 }
@@ -347,8 +498,9 @@ int cssd_profile_read(double* ms, int64_t* launches, int capacity) {
 }
 
 const char* cssd_kernel_name(int kernel_id) {
-    static const char* names[cssd::K_COUNT] = {"k_cumsum",     "k_chunk_state", "k_state_pass",
-                                                "k_chunk_scan", "k_step",        "k_step_infinite"};
+    static const char* names[cssd::K_COUNT] = {
+        "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
+        "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

@@ -7,7 +7,7 @@
 namespace cssd {
 
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
-                K_STEP_INFINITE = 5, K_COUNT = 6 };
+                K_STEP_INFINITE = 5, K_BWD_DXDB = 6, K_BWD_DC = 7, K_BWD_DZ = 8, K_COUNT = 9 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -18,6 +18,24 @@ struct FwdArgs {
     // workspace regions
     double *acs_re, *acs_im;
     float *e_re, *e_im, *w_re, *w_im, *cd_re, *cd_im, *st_re, *st_im;
+};
+
+// The gradient pass: the forward problem and its workspace (f), the forward
+// output and upstream gradients, the gradients, and the extra workspace.
+struct BwdArgs {
+    FwdArgs f;
+    const float *y_re, *y_im;                // forward output
+    const float *dy_re, *dy_im;              // dL/dy
+    const float *dhT_re, *dhT_im;            // dL/dhT or NULL
+    float *dx_re, *dx_im, *db_re, *db_im, *dc_re, *dc_im, *ddt, *da_re, *da_im, *dd;
+    float *dh0_re, *dh0_im;                  // or NULL
+    // workspace
+    float *r_re, *r_im;                      // adjoint chunk states Q_c, then R_{c+1}
+    float *q1_re, *q1_im, *q2_re, *q2_im;    // per position: the dx and y halves of q
+    float *ddp;                              // per position: Re(dy . conj(x))
+    float *hT_re, *hT_im;                    // final state of the recomputed forward
+    double *z_re, *z_im;                     // per chunk: <R_{c+1}, H_{c+1}>
+    double* pa;                              // per (b, h): dA re, dA im, dDskip
 };
 
 struct StepArgs {
@@ -36,6 +54,14 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_state_pass(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+hipError_t launch_chunk_state_adjoint(const FwdArgs& a, const float* dy_re, const float* dy_im,
+                                      float* q_re, float* q_im, hipStream_t stream);
+hipError_t launch_state_pass_adjoint(const FwdArgs& a, float* q_re, float* q_im,
+                                     const float* dhT_re, const float* dhT_im, float* dh0_re,
+                                     float* dh0_im, hipStream_t stream);
+hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dz(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_step_infinite(const StepArgs& a, hipStream_t stream);
 
 }  // namespace cssd

@@ -1,0 +1,662 @@
+// Gradient kernels of the chunkwise scan (fp32 inputs).
+//
+// The gradient of a real loss with respect to a complex value u + i v is the
+// pair (dL/du, dL/dv), i.e. the complex number dL/du + i dL/dv -- the
+// convention of the complex autograd the pages train this scan with
+// (Mamba-3-Lite docs, "SSD Theory", autograd notes).  For w = c z the gradient
+// reaching z is conj(c) grad(w) and the one reaching c is grad(w) conj(z).
+//
+// Walking the recurrence h_t = a_t h_{t-1} + B_t (x) x_t, y_t = C_t . h_t + D x_t
+// backwards, G_t = dL/dh_t obeys G_t = conj(C_t) (x) dy_t + conj(a_{t+1}) G_{t+1},
+// and dx_t = conj(B_t) . G_t + D dy_t, dB_t = G_t conj(x_t), dC_t = dy_t conj(h_t).
+// Chunkwise (chunk c, rows t, l; L, e, w, cd, H_c as in the forward kernels;
+// R_{c+1} = dL/dH_{c+1}, the gradient reaching the end of the chunk):
+//   P   = dY X^H                                   (C x C)
+//   dX  = (G . L)^H dY + diag(conj w) conj(B) R_{c+1} + D dY
+//   dB  = (conj(L) . P)^T conj(C) + diag(conj w) conj(X) R_{c+1}^T
+//   dC  = (conj(L) . P) conj(B) + diag(conj e) dY H_c^H
+// with G = C B^T the forward score matrix.  R comes from the adjoint chunk
+// pass R_c = Q_c + conj(cd[c]) R_{c+1}, Q_c = C^H diag(conj e) dY (the
+// chunk-state and state-pass kernels in their adjoint modes).
+//
+// The log-decay gradient needs no per-element bookkeeping: summing the
+// recurrence for G_t . conj(h_t) telescopes to
+//   dz_t = sum_{l >= t} q_l + <dhT, hT>,
+//   q_l  = sum_p dy_l[p] conj(y_l[p] - D x_l[p]) - conj(x_l[p]) (dx_l[p] - D dy_l[p])
+// (z_t = softplus(dt_t) A, <u, v> = sum u conj(v)), and the part of that sum from
+// the start of chunk c + 1 onwards is <R_{c+1}, H_{c+1}> (the same telescoping
+// stopped at a chunk boundary).  So for t in chunk c
+//   dz_t = sum_{l >= t, l in chunk c} q_l + <R_{c+1}, H_{c+1}>,
+// a chunk-local suffix sum plus a boundary term taken from the states, which
+// keeps rounding from accumulating over the whole sequence.  Then ddt_t =
+// sigmoid(dt_t) Re(dz_t conj(A)) and dA = sum_t softplus(dt_t) dz_t.
+//
+// MFMA mapping (16x16x4 fp32, lane = i + 16 g, Gauss complex products as in the
+// forward kernels).  k_bwd_dxdb: one wave per pair of row tiles {t, NLT-1-t} of
+// the l axis (tile lt sums over the NLT - lt tiles tt >= lt).  For each (tt, lt),
+// G and P come out with register r holding [t = t0 + 4g + r][l = l0 + lane%16],
+// which is the A-operand layout for the products with dY and conj(C) rows.
+// k_bwd_dc: one wave per pair of row tiles of the t axis; P is formed as
+// conj(X) dY^T so that register r holds [t = t0 + lane%16][l = l0 + 4g + r], the
+// A-operand layout for the product with conj(B) rows.  The state terms read
+// R_{c+1} and H_c from their MFMA-fragment layout, directly for products that
+// contract over n and element-wise (four loads per fragment row) for the
+// transposed products that contract over p.
+#include "cssd_device.h"
+#include "cssd_launch.h"
+
+namespace cssd {
+
+namespace {
+
+// element (n, p) of an N x D state block in MFMA-fragment order
+template <int D>
+__device__ __forceinline__ uint32_t frag_index(int n, int p) {
+    return (uint32_t)((((n >> 4) * (D / 16) + (p >> 4)) * 4 + ((n & 15) >> 2)) * 64 +
+                      (p & 15) * 4 + (n & 3));
+}
+
+// multiply the accumulator rows by a complex factor and put them back in Gauss form
+__device__ __forceinline__ void ctile_scale(CTile& t, int r, float fr, float fi) {
+    const float re = ctile_re(t, r), im = ctile_im(t, r);
+    const float nr = fr * re - fi * im, ni = fr * im + fi * re;
+    t.t1[r] = nr;
+    t.t2[r] = 0.f;
+    t.t3[r] = nr + ni;
+}
+
+// exp(acs[t] - acs[s]) or its conjugate, from the fp64 cumsums (log2 units / turns)
+__device__ __forceinline__ void seg_exp(const double* ar, const double* ai, int t, int s, bool conj,
+                                        float& lr, float& li) {
+    const double d2 = ar[t] - ar[s];
+    double dv = ai[t] - ai[s];
+    dv -= rint(dv);
+    cexp_scaled((float)d2, (float)(conj ? -dv : dv), lr, li);
+}
+
+// sum over the 16 lanes of a lane group (lane % 16 varies, lane / 16 fixed)
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// sum over the four lane groups (lane / 16 varies, lane % 16 fixed)
+__device__ __forceinline__ float sum_groups(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+struct ChunkView {
+    int64_t row0, pbase, chunk;
+    int h, valid;
+    uint32_t sN, sD, extN, extD;
+};
+
+__device__ __forceinline__ ChunkView chunk_view(const BwdArgs& a, int64_t chunk, int C, int N,
+                                                int D) {
+    ChunkView v;
+    const FwdArgs& f = a.f;
+    v.chunk = chunk;
+    const int c = (int)(chunk % f.nC);
+    const int64_t bh = chunk / f.nC;
+    v.h = (int)(bh % f.H);
+    const int64_t b = bh / f.H;
+    const int64_t t0 = (int64_t)c * C;
+    v.valid = (int)min<int64_t>((int64_t)C, f.T - t0);
+    v.row0 = (b * f.T + t0) * f.H + v.h;
+    v.pbase = bh * f.nC * C + t0;
+    v.sN = (uint32_t)f.H * N;
+    v.sD = (uint32_t)f.H * D;
+    v.extN = (uint32_t)(v.valid - 1) * v.sN + N;
+    v.extD = (uint32_t)(v.valid - 1) * v.sD + D;
+    return v;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// dX and dB for row tile lt of one chunk
+// ----------------------------------------------------------------------------
+template <int C, int N, int D>
+__device__ __forceinline__ void dxdb_tile(const BwdArgs& a, int64_t chunk, int lt) {
+    constexpr int NK = N / 16, PT = D / 16, NLT = C / 16;
+    const FwdArgs& f = a.f;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const ChunkView v = chunk_view(a, chunk, C, N, D);
+    const int l0 = lt * 16;
+    if (l0 >= v.valid) return;
+    const BufRes rb_r = make_buf(static_cast<const float*>(f.b_re) + v.row0 * N, v.extN * 4);
+    const BufRes rb_i = make_buf(static_cast<const float*>(f.b_im) + v.row0 * N, v.extN * 4);
+    const BufRes rc_r = make_buf(static_cast<const float*>(f.c_re) + v.row0 * N, v.extN * 4);
+    const BufRes rc_i = make_buf(static_cast<const float*>(f.c_im) + v.row0 * N, v.extN * 4);
+    const BufRes rx_r = make_buf(static_cast<const float*>(f.x_re) + v.row0 * D, v.extD * 4);
+    const BufRes rx_i = make_buf(static_cast<const float*>(f.x_im) + v.row0 * D, v.extD * 4);
+    const BufRes rg_r = make_buf(a.dy_re + v.row0 * D, v.extD * 4);
+    const BufRes rg_i = make_buf(a.dy_im + v.row0 * D, v.extD * 4);
+    const BufRes rr_r = make_buf(a.r_re + chunk * (int64_t)N * D, N * D * 4);
+    const BufRes rr_i = make_buf(a.r_im + chunk * (int64_t)N * D, N * D * 4);
+    const double* __restrict__ ar = f.acs_re + v.pbase;
+    const double* __restrict__ ai = f.acs_im + v.pbase;
+    const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
+
+    // rows l0 + li of B and X (A-operands of the state terms, B-operands of G, P)
+    floatx4 bq_r[NK], bq_i[NK], xq_r[PT], xq_i[PT];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        bq_r[k] = buf_f32x4(rb_r, (uint32_t)(l0 + li) * v.sN + 16 * k + 4 * g);
+        bq_i[k] = buf_f32x4(rb_i, (uint32_t)(l0 + li) * v.sN + 16 * k + 4 * g);
+    }
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        xq_r[k] = buf_f32x4(rx_r, (uint32_t)(l0 + li) * v.sD + 16 * k + 4 * g);
+        xq_i[k] = buf_f32x4(rx_i, (uint32_t)(l0 + li) * v.sD + 16 * k + 4 * g);
+    }
+
+    // accumulators: register r <-> row l = l0 + 4g + r, column 16 tile + li
+    CTile dx[PT], db[NK];
+#pragma unroll
+    for (int k = 0; k < PT; ++k) ctile_zero(dx[k]);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) ctile_zero(db[k]);
+
+    // ---- state terms: conj(B) R and conj(X) R^T, then the row factor conj(w[l])
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        const floatx4 br = bq_r[k], bi = -bq_i[k], bs = br + bi;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            // R[16k + 4g + e][16pt + li]
+            const floatx4 rr = buf_f32x4(rr_r, (uint32_t)(k * PT + pt) * 256 + 4 * lane);
+            const floatx4 ri = buf_f32x4(rr_i, (uint32_t)(k * PT + pt) * 256 + 4 * lane);
+            const floatx4 rs = rr + ri;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ctile_mac(dx[pt], br[e], bi[e], bs[e], rr[e], ri[e], rs[e]);
+        }
+    }
+#pragma unroll
+    for (int pk = 0; pk < PT; ++pk) {
+        const floatx4 xr = xq_r[pk], xi = -xq_i[pk], xs = xr + xi;
+#pragma unroll
+        for (int nt = 0; nt < NK; ++nt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // R^T[p = 16pk + 4g + e][n = 16nt + li] = R[n][p]
+                const uint32_t fi = frag_index<D>(16 * nt + li, 16 * pk + 4 * g + e);
+                const float tr = buf_f32(rr_r, fi), ti = buf_f32(rr_i, fi);
+                ctile_mac(db[nt], xr[e], xi[e], xs[e], tr, ti, tr + ti);
+            }
+        }
+    }
+    {
+        const floatx4 wr = *reinterpret_cast<const floatx4*>(f.w_re + v.pbase + l0 + 4 * g);
+        const floatx4 wi = *reinterpret_cast<const floatx4*>(f.w_im + v.pbase + l0 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int k = 0; k < PT; ++k) ctile_scale(dx[k], r, wr[r], -wi[r]);
+#pragma unroll
+            for (int k = 0; k < NK; ++k) ctile_scale(db[k], r, wr[r], -wi[r]);
+        }
+    }
+
+    // ---- causal terms over the tiles tt >= lt
+#pragma unroll
+    for (int tt = 0; tt < NLT; ++tt) {
+        if (tt < lt) continue;  // wave-uniform
+        const int t0 = tt * 16;
+        // G[t][l] = C[t] . B[l] and P[t][l] = dY[t] . conj(X[l]); register r <->
+        // t = t0 + 4g + r, l = l0 + li
+        CTile gt, pq;
+        ctile_zero(gt);
+        ctile_zero(pq);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            const floatx4 cr = buf_f32x4(rc_r, (uint32_t)(t0 + li) * v.sN + 16 * k + 4 * g);
+            const floatx4 ci = buf_f32x4(rc_i, (uint32_t)(t0 + li) * v.sN + 16 * k + 4 * g);
+            const floatx4 cs = cr + ci, bs = bq_r[k] + bq_i[k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ctile_mac(gt, cr[e], ci[e], cs[e], bq_r[k][e], bq_i[k][e], bs[e]);
+        }
+#pragma unroll
+        for (int pk = 0; pk < PT; ++pk) {
+            const floatx4 gr = buf_f32x4(rg_r, (uint32_t)(t0 + li) * v.sD + 16 * pk + 4 * g);
+            const floatx4 gi = buf_f32x4(rg_i, (uint32_t)(t0 + li) * v.sD + 16 * pk + 4 * g);
+            const floatx4 gs = gr + gi, xs = xq_r[pk] - xq_i[pk];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ctile_mac(pq, gr[e], gi[e], gs[e], xq_r[pk][e], -xq_i[pk][e], xs[e]);
+        }
+        float cm_r[4], cm_i[4], kk_r[4], kk_i[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * g + r, l = l0 + li;
+            float lr = 0.f, lim = 0.f;
+            if (tt > lt || t >= l) seg_exp(ar, ai, t, l, false, lr, lim);
+            const float g_r = ctile_re(gt, r), g_i = ctile_im(gt, r);
+            const float p_r = ctile_re(pq, r), p_i = ctile_im(pq, r);
+            cm_r[r] = g_r * lr - g_i * lim;       // conj(G L)
+            cm_i[r] = -(g_r * lim + g_i * lr);
+            kk_r[r] = lr * p_r + lim * p_i;       // conj(L) P
+            kk_i[r] = lr * p_i - lim * p_r;
+        }
+        // dX += conj(M)^T dY[tt]; dB += K^T conj(C[tt]); k-step r <-> t = t0 + 4g + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t trow = (uint32_t)(t0 + 4 * g + r);
+            const float ms = cm_r[r] + cm_i[r], ks = kk_r[r] + kk_i[r];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const float yr = buf_f32(rg_r, trow * v.sD + 16 * pt + li);
+                const float yi = buf_f32(rg_i, trow * v.sD + 16 * pt + li);
+                ctile_mac(dx[pt], cm_r[r], cm_i[r], ms, yr, yi, yr + yi);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NK; ++nt) {
+                const float cr = buf_f32(rc_r, trow * v.sN + 16 * nt + li);
+                const float ci = -buf_f32(rc_i, trow * v.sN + 16 * nt + li);
+                ctile_mac(db[nt], kk_r[r], kk_i[r], ks, cr, ci, cr + ci);
+            }
+        }
+    }
+
+    // ---- q1[l] = -sum_p conj(x[l][p]) dx[l][p] (before the skip term), the skip
+    // term, and the stores; register r <-> row l = l0 + 4g + r
+    const BufRes rdx_r = make_buf(a.dx_re + v.row0 * D, v.extD * 4);
+    const BufRes rdx_i = make_buf(a.dx_im + v.row0 * D, v.extD * 4);
+    const BufRes rdb_r = make_buf(a.db_re + v.row0 * N, v.extN * 4);
+    const BufRes rdb_i = make_buf(a.db_im + v.row0 * N, v.extN * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lrow = (uint32_t)(l0 + 4 * g + r);
+        float qr = 0.f, qi = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const uint32_t off = lrow * v.sD + 16 * pt + li;
+            const float xr = buf_f32(rx_r, off), xi = buf_f32(rx_i, off);
+            const float gr = buf_f32(rg_r, off), gi = buf_f32(rg_i, off);
+            const float vr = ctile_re(dx[pt], r), vi = ctile_im(dx[pt], r);
+            qr += xr * vr + xi * vi;  // conj(x) dx
+            qi += xr * vi - xi * vr;
+            buf_store_f32(vr + dk * gr, rdx_r, off);
+            buf_store_f32(vi + dk * gi, rdx_i, off);
+        }
+        qr = sum16(qr);
+        qi = sum16(qi);
+        if (li == 0) {
+            a.q1_re[v.pbase + lrow] = -qr;
+            a.q1_im[v.pbase + lrow] = -qi;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NK; ++nt) {
+            const uint32_t off = lrow * v.sN + 16 * nt + li;
+            buf_store_f32(ctile_re(db[nt], r), rdb_r, off);
+            buf_store_f32(ctile_im(db[nt], r), rdb_i, off);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// dC for row tile tt of one chunk, plus the y half of q and the dD partials
+// ----------------------------------------------------------------------------
+template <int C, int N, int D>
+__device__ __forceinline__ void dc_tile(const BwdArgs& a, int64_t chunk, int tt) {
+    constexpr int NK = N / 16, PT = D / 16;
+    const FwdArgs& f = a.f;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const ChunkView v = chunk_view(a, chunk, C, N, D);
+    const int t0 = tt * 16;
+    if (t0 >= v.valid) return;
+    const BufRes rb_r = make_buf(static_cast<const float*>(f.b_re) + v.row0 * N, v.extN * 4);
+    const BufRes rb_i = make_buf(static_cast<const float*>(f.b_im) + v.row0 * N, v.extN * 4);
+    const BufRes rx_r = make_buf(static_cast<const float*>(f.x_re) + v.row0 * D, v.extD * 4);
+    const BufRes rx_i = make_buf(static_cast<const float*>(f.x_im) + v.row0 * D, v.extD * 4);
+    const BufRes ry_r = make_buf(a.y_re + v.row0 * D, v.extD * 4);
+    const BufRes ry_i = make_buf(a.y_im + v.row0 * D, v.extD * 4);
+    const BufRes rg_r = make_buf(a.dy_re + v.row0 * D, v.extD * 4);
+    const BufRes rg_i = make_buf(a.dy_im + v.row0 * D, v.extD * 4);
+    const BufRes rh_r = make_buf(f.st_re + chunk * (int64_t)N * D, N * D * 4);
+    const BufRes rh_i = make_buf(f.st_im + chunk * (int64_t)N * D, N * D * 4);
+    const double* __restrict__ ar = f.acs_re + v.pbase;
+    const double* __restrict__ ai = f.acs_im + v.pbase;
+    const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
+
+    // rows t0 + li of dY, as A-operand (over p) and as B-operand of conj(X) dY^T
+    floatx4 gq_r[PT], gq_i[PT];
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        gq_r[k] = buf_f32x4(rg_r, (uint32_t)(t0 + li) * v.sD + 16 * k + 4 * g);
+        gq_i[k] = buf_f32x4(rg_i, (uint32_t)(t0 + li) * v.sD + 16 * k + 4 * g);
+    }
+
+    // ---- the y half of q and the dD partial for rows t = t0 + li
+    {
+        float qr = 0.f, qi = 0.f, dd = 0.f;
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const uint32_t off = (uint32_t)(t0 + li) * v.sD + 16 * k + 4 * g;
+            const floatx4 yr = buf_f32x4(ry_r, off), yi = buf_f32x4(ry_i, off);
+            const floatx4 xr = buf_f32x4(rx_r, off), xi = buf_f32x4(rx_i, off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ur = yr[e] - dk * xr[e], ui = yi[e] - dk * xi[e];
+                qr += gq_r[k][e] * ur + gq_i[k][e] * ui;  // dy conj(y - D x)
+                qi += gq_i[k][e] * ur - gq_r[k][e] * ui;
+                dd += gq_r[k][e] * xr[e] + gq_i[k][e] * xi[e];
+            }
+        }
+        qr = sum_groups(qr);
+        qi = sum_groups(qi);
+        dd = sum_groups(dd);
+        if (g == 0) {
+            a.q2_re[v.pbase + t0 + li] = qr;
+            a.q2_im[v.pbase + t0 + li] = qi;
+            a.ddp[v.pbase + t0 + li] = dd;
+        }
+    }
+
+    // accumulators: register r <-> row t = t0 + 4g + r, column n = 16 nt + li
+    CTile dc[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) ctile_zero(dc[k]);
+
+    // ---- carried-state term dY H_c^H, then the row factor conj(e[t])
+#pragma unroll
+    for (int pk = 0; pk < PT; ++pk) {
+        const floatx4 gs = gq_r[pk] + gq_i[pk];
+#pragma unroll
+        for (int nt = 0; nt < NK; ++nt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // conj(H[n = 16nt + li][p = 16pk + 4g + e])
+                const uint32_t fi = frag_index<D>(16 * nt + li, 16 * pk + 4 * g + e);
+                const float hr = buf_f32(rh_r, fi), hi = -buf_f32(rh_i, fi);
+                ctile_mac(dc[nt], gq_r[pk][e], gq_i[pk][e], gs[e], hr, hi, hr + hi);
+            }
+        }
+    }
+    {
+        const floatx4 er = *reinterpret_cast<const floatx4*>(f.e_re + v.pbase + t0 + 4 * g);
+        const floatx4 ei = *reinterpret_cast<const floatx4*>(f.e_im + v.pbase + t0 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int k = 0; k < NK; ++k) ctile_scale(dc[k], r, er[r], -ei[r]);
+    }
+
+    // ---- causal terms over the tiles lt <= tt
+#pragma unroll
+    for (int lt = 0; lt < C / 16; ++lt) {
+        if (lt > tt) continue;  // wave-uniform
+        const int l0 = lt * 16;
+        // P[t][l] as conj(X[l]) . dY[t]; register r <-> t = t0 + li, l = l0 + 4g + r
+        CTile pq;
+        ctile_zero(pq);
+#pragma unroll
+        for (int pk = 0; pk < PT; ++pk) {
+            const floatx4 xr = buf_f32x4(rx_r, (uint32_t)(l0 + li) * v.sD + 16 * pk + 4 * g);
+            const floatx4 xi = -buf_f32x4(rx_i, (uint32_t)(l0 + li) * v.sD + 16 * pk + 4 * g);
+            const floatx4 xs = xr + xi, gs = gq_r[pk] + gq_i[pk];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ctile_mac(pq, xr[e], xi[e], xs[e], gq_r[pk][e], gq_i[pk][e], gs[e]);
+        }
+        float kk_r[4], kk_i[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + li, l = l0 + 4 * g + r;
+            float lr = 0.f, lim = 0.f;
+            if (lt < tt || t >= l) seg_exp(ar, ai, t, l, false, lr, lim);
+            const float p_r = ctile_re(pq, r), p_i = ctile_im(pq, r);
+            kk_r[r] = lr * p_r + lim * p_i;  // conj(L) P
+            kk_i[r] = lr * p_i - lim * p_r;
+        }
+        // dC += K conj(B[lt]); k-step r <-> l = l0 + 4g + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t lrow = (uint32_t)(l0 + 4 * g + r);
+            const float ks = kk_r[r] + kk_i[r];
+#pragma unroll
+            for (int nt = 0; nt < NK; ++nt) {
+                const float br = buf_f32(rb_r, lrow * v.sN + 16 * nt + li);
+                const float bi = -buf_f32(rb_i, lrow * v.sN + 16 * nt + li);
+                ctile_mac(dc[nt], kk_r[r], kk_i[r], ks, br, bi, br + bi);
+            }
+        }
+    }
+
+    const BufRes rdc_r = make_buf(a.dc_re + v.row0 * N, v.extN * 4);
+    const BufRes rdc_i = make_buf(a.dc_im + v.row0 * N, v.extN * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t trow = (uint32_t)(t0 + 4 * g + r);
+#pragma unroll
+        for (int nt = 0; nt < NK; ++nt) {
+            buf_store_f32(ctile_re(dc[nt], r), rdc_r, trow * v.sN + 16 * nt + li);
+            buf_store_f32(ctile_im(dc[nt], r), rdc_i, trow * v.sN + 16 * nt + li);
+        }
+    }
+}
+
+// Balanced pairs of row tiles {t, NLT-1-t} per wave, 4 / WPC chunks per block.
+template <int C, int N, int D, bool DC>
+__global__ __launch_bounds__(256) void k_bwd_tiles(BwdArgs a) {
+    constexpr int NLT = C / 16;
+    constexpr int WPC = NLT >= 2 ? NLT / 2 : 1;
+    const int wave = wave_id();
+    const int64_t chunk = (int64_t)blockIdx.x * (4 / WPC) + wave / WPC;
+    if (chunk >= a.f.B * a.f.H * a.f.nC) return;  // wave-uniform
+    const int t = wave % WPC;
+    if (DC) {
+        dc_tile<C, N, D>(a, chunk, t);
+        if (NLT - 1 - t != t) dc_tile<C, N, D>(a, chunk, NLT - 1 - t);
+    } else {
+        dxdb_tile<C, N, D>(a, chunk, t);
+        if (NLT - 1 - t != t) dxdb_tile<C, N, D>(a, chunk, NLT - 1 - t);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Z[c] = <R_{c+1}, H_{c+1}>: the tail of the log-decay gradient sum past chunk c.
+// R_{c+1} is slot c of the adjoint buffer, H_{c+1} slot c + 1 of the carry-in
+// states (both MFMA-fragment order); for the last chunk it is <dhT, hT> (both in
+// the caller's layout), or 0 without dhT.  One wave per (b, h, c), fp64 sums.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_zbound(BwdArgs a) {
+    const FwdArgs& f = a.f;
+    const int64_t chunk = (int64_t)blockIdx.x * 4 + wave_id();
+    if (chunk >= f.B * f.H * f.nC) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int c = (int)(chunk % f.nC);
+    const int64_t bh = chunk / f.nC;
+    const int64_t ND = f.N * f.D;
+    const float *ur, *ui, *vr, *vi;
+    if (c + 1 < f.nC) {
+        ur = a.r_re + chunk * ND;
+        ui = a.r_im + chunk * ND;
+        vr = f.st_re + (chunk + 1) * ND;
+        vi = f.st_im + (chunk + 1) * ND;
+    } else if (a.dhT_re != nullptr) {
+        ur = a.dhT_re + bh * ND;
+        ui = a.dhT_im + bh * ND;
+        vr = a.hT_re + bh * ND;
+        vi = a.hT_im + bh * ND;
+    } else {
+        ur = nullptr;
+    }
+    double zr = 0.0, zi = 0.0;
+    if (ur != nullptr) {
+        for (int64_t k = 4 * lane; k < ND; k += 256) {
+            const float4 a4 = *reinterpret_cast<const float4*>(ur + k);
+            const float4 b4 = *reinterpret_cast<const float4*>(ui + k);
+            const float4 c4 = *reinterpret_cast<const float4*>(vr + k);
+            const float4 d4 = *reinterpret_cast<const float4*>(vi + k);
+            const float xr[4] = {a4.x, a4.y, a4.z, a4.w}, xi[4] = {b4.x, b4.y, b4.z, b4.w};
+            const float yr[4] = {c4.x, c4.y, c4.z, c4.w}, yi[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                zr += (double)xr[q] * yr[q] + (double)xi[q] * yi[q];
+                zi += (double)xi[q] * yr[q] - (double)xr[q] * yi[q];
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            zr += __shfl_xor(zr, off, 64);
+            zi += __shfl_xor(zi, off, 64);
+        }
+    }
+    if (lane == 0) {
+        a.z_re[chunk] = zr;
+        a.z_im[chunk] = zi;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// dz_t = (suffix sum of q within chunk c) + Z[c]  ->  ddt, and per-(b, h)
+// partials of dA and dDskip.  One wave per (b, h); positions are walked from
+// the end in blocks of 64.  A chunk of 16 or 32 positions lies inside one
+// block (segmented suffix sum); a chunk of 128 spans two blocks, and its tail
+// carries from the later block to the earlier one.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a) {
+    const FwdArgs& f = a.f;
+    const int64_t bh = (int64_t)blockIdx.x * 4 + wave_id();
+    if (bh >= f.B * f.H) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int h = (int)(bh % f.H);
+    const int64_t b = bh / f.H;
+    const int64_t C = f.C;
+    const double Ar = f.a_re[h], Ai = f.a_im[h];
+    const int64_t pb = bh * f.nC * C;
+    double gar = 0.0, gai = 0.0, gd = 0.0;
+    double tail_r = 0.0, tail_i = 0.0;  // q of the current chunk in later blocks
+    for (int64_t blk = (f.T - 1) / 64; blk >= 0; --blk) {
+        const int64_t t = blk * 64 + lane;
+        double sr = 0.0, si = 0.0;
+        if (t < f.T) {
+            sr = (double)a.q1_re[pb + t] + (double)a.q2_re[pb + t];
+            si = (double)a.q1_im[pb + t] + (double)a.q2_im[pb + t];
+            gd += (double)a.ddp[pb + t];
+        }
+        // inclusive suffix sum within each chunk's part of the block
+        const int64_t ct = t / C;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double ur = __shfl_down(sr, off, 64), ui = __shfl_down(si, off, 64);
+            if (lane + off < 64 && (t + off) / C == ct) {
+                sr += ur;
+                si += ui;
+            }
+        }
+        // the chunk containing the block's last position may continue into the
+        // next block (C = 128); its later positions are in tail
+        const int64_t c_last = (blk * 64 + 63) / C;
+        const bool straddles = (c_last + 1) * C > blk * 64 + 64;
+        const double cr = (ct == c_last && straddles ? tail_r : 0.0) + a.z_re[bh * f.nC + ct];
+        const double ci = (ct == c_last && straddles ? tail_i : 0.0) + a.z_im[bh * f.nC + ct];
+        if (t < f.T) {
+            const double zr = sr + cr, zi = si + ci;
+            const int64_t row = (b * f.T + t) * f.H + h;
+            const double v = (double)f.dt[row];
+            const double s = softplus_f64(v);
+            a.ddt[row] = (float)((zr * Ar + zi * Ai) / (1.0 + exp(-v)));
+            gar += s * zr;
+            gai += s * zi;
+        }
+        // carry for the chunk that starts before this block: its part in this block
+        const int64_t c_first = (blk * 64) / C;
+        const bool starts_before = c_first * C < blk * 64;
+        if (starts_before) {
+            // lane 0 holds the suffix sum of chunk c_first over this whole block
+            const double br = __shfl(sr, 0, 64), bi = __shfl(si, 0, 64);
+            const bool same = (c_first == c_last) && straddles;
+            tail_r = br + (same ? tail_r : 0.0);
+            tail_i = bi + (same ? tail_i : 0.0);
+        } else {
+            tail_r = tail_i = 0.0;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        gar += __shfl_xor(gar, off, 64);
+        gai += __shfl_xor(gai, off, 64);
+        gd += __shfl_xor(gd, off, 64);
+    }
+    if (lane == 0) {
+        a.pa[3 * bh] = gar;
+        a.pa[3 * bh + 1] = gai;
+        a.pa[3 * bh + 2] = gd;
+    }
+}
+
+// dA[h], dDskip[h]: the per-(b, h) partials summed over b in a fixed order.
+__global__ __launch_bounds__(256) void k_bwd_reduce(BwdArgs a) {
+    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (h >= a.f.H) return;
+    double sr = 0.0, si = 0.0, sd = 0.0;
+    for (int64_t b = 0; b < a.f.B; ++b) {
+        sr += a.pa[3 * (b * a.f.H + h)];
+        si += a.pa[3 * (b * a.f.H + h) + 1];
+        sd += a.pa[3 * (b * a.f.H + h) + 2];
+    }
+    a.da_re[h] = (float)sr;
+    a.da_im[h] = (float)si;
+    if (a.dd != nullptr) a.dd[h] = (float)sd;
+}
+
+template <int C, int N, bool DC>
+static hipError_t launch_tiles_d(const BwdArgs& a, hipStream_t s) {
+    constexpr int WPC = C / 16 >= 2 ? C / 32 : 1;
+    constexpr int CPB = 4 / WPC;
+    const int64_t nchunks = a.f.B * a.f.H * a.f.nC;
+    const dim3 grid((unsigned)((nchunks + CPB - 1) / CPB)), block(256);
+    switch (a.f.D) {
+        case 16: hipLaunchKernelGGL((k_bwd_tiles<C, N, 16, DC>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((k_bwd_tiles<C, N, 32, DC>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((k_bwd_tiles<C, N, 64, DC>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_bwd_tiles<C, N, 128, DC>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+template <int C, bool DC>
+static hipError_t launch_tiles_n(const BwdArgs& a, hipStream_t s) {
+    switch (a.f.N) {
+        case 16: return launch_tiles_d<C, 16, DC>(a, s);
+        case 32: return launch_tiles_d<C, 32, DC>(a, s);
+        case 64: return launch_tiles_d<C, 64, DC>(a, s);
+        default: return launch_tiles_d<C, 128, DC>(a, s);
+    }
+}
+
+template <bool DC>
+static hipError_t launch_tiles(const BwdArgs& a, hipStream_t s) {
+    switch (a.f.C) {
+        case 16: return launch_tiles_n<16, DC>(a, s);
+        case 32: return launch_tiles_n<32, DC>(a, s);
+        case 64: return launch_tiles_n<64, DC>(a, s);
+        default: return launch_tiles_n<128, DC>(a, s);
+    }
+}
+
+hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t s) { return launch_tiles<false>(a, s); }
+hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s) { return launch_tiles<true>(a, s); }
+
+hipError_t launch_bwd_dz(const BwdArgs& a, hipStream_t s) {
+    const int64_t nchunks = a.f.B * a.f.H * a.f.nC;
+    hipLaunchKernelGGL(k_bwd_zbound, dim3((unsigned)((nchunks + 3) / 4)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t units = a.f.B * a.f.H;
+    hipLaunchKernelGGL(k_bwd_dz, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((a.f.H + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace cssd

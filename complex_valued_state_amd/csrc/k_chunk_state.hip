@@ -28,7 +28,9 @@
 
 namespace cssd {
 
-template <typename In, int C, int D>
+// CONJW: conjugate the weighted rows, S_c = (diag(w) B)^H X.  The gradient pass
+// uses it for the adjoint chunk states Q_c = C^H diag(conj(e)) dY.
+template <typename In, int C, int D, bool CONJW = false>
 __global__ __launch_bounds__(512) void k_chunk_state(
     const typename In::T* __restrict__ x_re, const typename In::T* __restrict__ x_im,
     const typename In::T* __restrict__ b_re, const typename In::T* __restrict__ b_im,
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(512) void k_chunk_state(
         Ops o = ring[j % DIST];
         if (j + DIST < KJ) load(j + DIST, ring[j % DIST]);
         __builtin_amdgcn_sched_barrier(0);
-        const float pr = wr[j] * o.br - wi[j] * o.bi;  // (w B)[l, n]
-        const float pi = wr[j] * o.bi + wi[j] * o.br;
+        const float pr = wr[j] * o.br - wi[j] * o.bi;  // (w B)[l, n], or its conjugate
+        const float pi = CONJW ? -(wr[j] * o.bi + wi[j] * o.br) : wr[j] * o.bi + wi[j] * o.br;
         const float ps = pr + pi;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
@@ -163,6 +165,41 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t stream) {
         launch_c<InBF16>(a, stream);
     else
         launch_c<InF32>(a, stream);
+    return hipGetLastError();
+}
+
+// Adjoint chunk states for the gradient pass (fp32 planes):
+//   Q_c[n, p] = sum_l conj(e[l] C[l, n]) dY[l, p]
+// the same contraction as S_c with B -> C, w -> e (conjugated) and X -> dY.
+template <int C>
+static void launch_adjoint_d(const FwdArgs& a, const float* dy_re, const float* dy_im,
+                             float* q_re, float* q_im, hipStream_t s) {
+    const float* cr = static_cast<const float*>(a.c_re);
+    const float* ci = static_cast<const float*>(a.c_im);
+#define CSSD_K3A(DD)                                                                           \
+    {                                                                                          \
+        const dim3 grid((unsigned)(a.B * a.H * a.nC)), block((unsigned)(4 * a.N));             \
+        hipLaunchKernelGGL((k_chunk_state<InF32, C, DD, true>), grid, block, 0, s, dy_re, dy_im, \
+                           cr, ci, a.e_re, a.e_im, q_re, q_im, a.T, (int)a.H, (int)a.N,        \
+                           (int)a.nC);                                                         \
+    }
+    switch (a.D) {
+        case 16: CSSD_K3A(16); break;
+        case 32: CSSD_K3A(32); break;
+        case 64: CSSD_K3A(64); break;
+        default: CSSD_K3A(128); break;
+    }
+#undef CSSD_K3A
+}
+
+hipError_t launch_chunk_state_adjoint(const FwdArgs& a, const float* dy_re, const float* dy_im,
+                                      float* q_re, float* q_im, hipStream_t stream) {
+    switch (a.C) {
+        case 16: launch_adjoint_d<16>(a, dy_re, dy_im, q_re, q_im, stream); break;
+        case 32: launch_adjoint_d<32>(a, dy_re, dy_im, q_re, q_im, stream); break;
+        case 64: launch_adjoint_d<64>(a, dy_re, dy_im, q_re, q_im, stream); break;
+        default: launch_adjoint_d<128>(a, dy_re, dy_im, q_re, q_im, stream); break;
+    }
     return hipGetLastError();
 }
 

@@ -23,6 +23,11 @@
 
 namespace cssd {
 
+// REV: the adjoint pass of the gradient computation, run from the last chunk
+// back to the first:  R_nC = dhT (or 0);  R_c = Q_c + conj(cd[c]) R_{c+1}.  The
+// buffer holds Q_c on entry and R_{c+1} (the gradient reaching the end of chunk
+// c) on exit; the init/final pointers then carry dhT in and dh0 = R_0 out.
+template <bool REV>
 __global__ __launch_bounds__(256) void k_state_pass(float4* __restrict__ st_re,
                                                     float4* __restrict__ st_im,
                                                     const float* __restrict__ cd_re,
@@ -57,17 +62,19 @@ __global__ __launch_bounds__(256) void k_state_pass(float4* __restrict__ st_re,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (c0 + u < nC) {
-                sr[u] = nt_load4(&st_re[base + (int64_t)(c0 + u) * nd4]);
-                si[u] = nt_load4(&st_im[base + (int64_t)(c0 + u) * nd4]);
+                const int c = REV ? nC - 1 - (c0 + u) : c0 + u;
+                sr[u] = nt_load4(&st_re[base + (int64_t)c * nd4]);
+                si[u] = nt_load4(&st_im[base + (int64_t)c * nd4]);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
-            if (c < nC) {
+            if (c0 + u < nC) {
+                const int c = REV ? nC - 1 - (c0 + u) : c0 + u;
                 st_re[base + (int64_t)c * nd4] = hr;
                 st_im[base + (int64_t)c * nd4] = hi;
-                const float dr = cd_re[bh * nC + c], di = cd_im[bh * nC + c];
+                const float dr = cd_re[bh * nC + c];
+                const float di = REV ? -cd_im[bh * nC + c] : cd_im[bh * nC + c];
                 float4 nr, ni;
                 nr.x = dr * hr.x - di * hi.x + sr[u].x;
                 nr.y = dr * hr.y - di * hi.y + sr[u].y;
@@ -93,9 +100,21 @@ __global__ __launch_bounds__(256) void k_state_pass(float4* __restrict__ st_re,
 hipError_t launch_state_pass(const FwdArgs& a, hipStream_t stream) {
     const int64_t total = a.B * a.H * (a.N * a.D / 4);
     const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-    hipLaunchKernelGGL(k_state_pass, grid, block, 0, stream, reinterpret_cast<float4*>(a.st_re),
-                       reinterpret_cast<float4*>(a.st_im), a.cd_re, a.cd_im, a.h0_re, a.h0_im,
-                       a.hT_re, a.hT_im, total, (int)a.N, (int)a.D, (int)a.nC);
+    hipLaunchKernelGGL(k_state_pass<false>, grid, block, 0, stream,
+                       reinterpret_cast<float4*>(a.st_re), reinterpret_cast<float4*>(a.st_im),
+                       a.cd_re, a.cd_im, a.h0_re, a.h0_im, a.hT_re, a.hT_im, total, (int)a.N,
+                       (int)a.D, (int)a.nC);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_pass_adjoint(const FwdArgs& a, float* q_re, float* q_im,
+                                     const float* dhT_re, const float* dhT_im, float* dh0_re,
+                                     float* dh0_im, hipStream_t stream) {
+    const int64_t total = a.B * a.H * (a.N * a.D / 4);
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    hipLaunchKernelGGL(k_state_pass<true>, grid, block, 0, stream, reinterpret_cast<float4*>(q_re),
+                       reinterpret_cast<float4*>(q_im), a.cd_re, a.cd_im, dhT_re, dhT_im, dh0_re,
+                       dh0_im, total, (int)a.N, (int)a.D, (int)a.nC);
     return hipGetLastError();
 }
 

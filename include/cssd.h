@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 101 /* major*100 + minor */
+#define CSSD_VERSION 102 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
@@ -172,6 +172,63 @@ int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
               float *y_re, float *y_im, void *stream);
 
 /*
+ * Workspace bytes cssd_backward needs for this shape (at least the forward's).
+ */
+int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                 int64_t headdim, int64_t dstate, int64_t chunk,
+                                 size_t *bytes);
+
+/*
+ * Gradients of cssd_forward (the pages train the scan by automatic
+ * differentiation of complex tensors: Mamba-3-Lite docs, "SSD Theory", autograd
+ * notes; "The Chunkwise Complex SSD Algorithm", the complex-dtype
+ * requirement).  For a real loss L and a complex value u + i v the gradient is
+ * the planar pair (dL/du, dL/dv), which is also the convention of complex
+ * autograd (grad = dL/du + i dL/dv).  Given the upstream gradients dy of y and,
+ * optionally, dhT of the final state, this returns dx, dB, dC (the layouts of
+ * x, B, C), ddt [B,T,H], dA [H] and dDskip [H] (summed over batch and time), and
+ * dh0 [B,H,N,D].
+ *
+ *   x_* .. h0_*      exactly the inputs of the cssd_forward call (fp32 only:
+ *                    in_dtype must be CSSD_F32, else CSSD_ERR_UNSUPPORTED)
+ *   y_re, y_im       that call's output y [B,T,H,D]; it enters the gradient of
+ *                    the log-decay (see below), so it must be the output for
+ *                    these inputs
+ *   dy_re, dy_im     [B,T,H,D] upstream gradient of y
+ *   dhT_re, dhT_im   [B,H,N,D] upstream gradient of the final state, or both
+ *                    NULL (zero)
+ *   dx_*, dB_*, dC_* gradients of x, B, C (written)
+ *   ddt              [B,T,H] gradient of the raw step dt (written)
+ *   dA_re, dA_im     [H] gradient of A (written)
+ *   dD               [H] gradient of Dskip, or NULL (not computed)
+ *   dh0_re, dh0_im   [B,H,N,D] gradient of the initial state, or both NULL
+ *   workspace        >= cssd_backward_workspace_size bytes, 256-byte aligned
+ * The forward's chunk states are recomputed inside.  The log-decay gradient
+ * dz_t (z_t = softplus(dt_t) A) uses the identity
+ *   dz_t = sum_{l>=t} [dy_l . conj(y_l - D x_l) - conj(x_l) . (dx_l - D dy_l)]
+ *          + <dhT, hT>,
+ * obtained by summing the reverse recurrence of dL/dh_t (<u, v> = sum u conj(v)).
+ * Alignment: x, B, C, y, dy (and h0, dhT, dh0) 16 bytes, the rest their
+ * element size.  Outputs may not alias inputs or each other.
+ */
+int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                  int64_t dstate, int64_t chunk, int32_t in_dtype,
+                  const void *x_re, const void *x_im,
+                  const void *B_re, const void *B_im,
+                  const void *C_re, const void *C_im,
+                  const float *dt, const float *A_re, const float *A_im,
+                  const float *Dskip,
+                  const float *h0_re, const float *h0_im,
+                  const float *y_re, const float *y_im,
+                  const float *dy_re, const float *dy_im,
+                  const float *dhT_re, const float *dhT_im,
+                  float *dx_re, float *dx_im, float *dB_re, float *dB_im,
+                  float *dC_re, float *dC_im, float *ddt,
+                  float *dA_re, float *dA_im, float *dD,
+                  float *dh0_re, float *dh0_im,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * n recurrent steps that all receive the same input, applied at once in O(1)
  * work per state element (burn-mamba docs, module step_constant: the unrolled
  * constant-input steps form a geometric series; this is its case with no
@@ -221,7 +278,9 @@ int cssd_step_infinite(int64_t batch, int64_t nheads, int64_t headdim, int64_t d
  * per kernel id into ms[k] and launches[k] for k < min(capacity, number of
  * kernels), resets the accumulators and returns the number of kernel ids (or a
  * negative status on error).  Kernel ids: 0 cumsum, 1 chunk_state,
- * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite.
+ * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite,
+ * 6 bwd_dxdb, 7 bwd_dc, 8 bwd_dz (cssd_backward also runs ids 0-2, and 1 and 2
+ * a second time in their adjoint modes).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).
  */

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("cssd_forward", "cssd_step", "cssd_step_n", "cssd_step_infinite",
+    for required in ("cssd_forward", "cssd_backward", "cssd_backward_workspace_size",
+                     "cssd_step", "cssd_step_n", "cssd_step_infinite",
                      "cssd_forward_workspace_size", "cssd_status_string", "cssd_version"):
         assert required in names
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 101
+    assert lib.cssd_version() == 102
     for st in range(5):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -152,6 +153,30 @@ def test_step_n_and_infinite_validation(lib):
     assert lib.cssd_step_infinite(1, 2, 16, 16, *ins, ins[0], y[1], None) == 1  # y aliases x
     misaligned = list(y); misaligned[0] = y[0] + 4
     assert lib.cssd_step_infinite(1, 2, 16, 16, *ins, *misaligned, None) == 1
+
+
+def test_backward_validation(lib):
+    import ctypes
+    fw, bw = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.cssd_forward_workspace_size(2, 100, 3, 32, 64, 16, ctypes.byref(fw)) == 0
+    assert lib.cssd_backward_workspace_size(2, 100, 3, 32, 64, 16, ctypes.byref(bw)) == 0
+    assert bw.value > fw.value and bw.value % 256 == 0
+    assert lib.cssd_backward_workspace_size(2, 100, 3, 32, 48, 16, ctypes.byref(bw)) == 2
+    base = 0x10000000
+    p = [base + 0x100000 * i for i in range(40)]
+    ins = p[:10] + [None, None] + p[12:16]          # x..Dskip, h0 NULL, y, dy
+    grads = p[20:30] + [p[30], None]                # dx..dD, dh0 half-NULL (bad)
+    ws = 0x20000000
+    args = lambda g, dt=0, shape=(1, 64, 2, 16, 16, 16): (
+        *shape, dt, *ins, None, None, *g, ws, 1 << 30, None)
+    assert lib.cssd_backward(*args(grads)) == 1          # dh0_re without dh0_im
+    good = p[20:30] + [None, None]
+    assert lib.cssd_backward(*args(good, dt=1)) == 2     # bf16 inputs not supported
+    assert lib.cssd_backward(*args(good, shape=(1, 64, 2, 16, 24, 16))) == 2
+    bad = list(good); bad[0] = ins[0]                     # dx aliases x
+    assert lib.cssd_backward(*args(bad)) == 1
+    bad = list(good); bad[2] = bad[0]                     # dB aliases dx
+    assert lib.cssd_backward(*args(bad)) == 1
 
 
 def test_profiler_without_launches(lib):

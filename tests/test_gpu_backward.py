@@ -1,0 +1,107 @@
+"""GPU parity of cssd_backward (the gradients of the chunkwise scan) against the
+oracle's reverse-mode recurrence, which is pinned by finite differences
+(needs an MI355X)."""
+import numpy as np
+import pytest
+
+import cssd_workloads as wl
+import oracle
+from gpu_util import dev_inputs, log, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _grads(inp: wl.ForwardInputs, with_dhT: bool, seed: int, chunk=None):
+    """(gpu gradients, oracle gradients) as complex / real numpy arrays."""
+    import torch
+    import complex_valued_state_amd as cssd
+    d = dev_inputs(inp)
+    Bsz, T, H, D = inp.x_re.shape
+    N = inp.B_re.shape[-1]
+    rng = np.random.default_rng(seed)
+    gy = (np.sqrt(0.5) * (rng.standard_normal((Bsz, T, H, D))
+                          + 1j * rng.standard_normal((Bsz, T, H, D)))).astype(np.complex64)
+    ghT = None
+    if with_dhT:
+        ghT = (np.sqrt(0.5) * (rng.standard_normal((Bsz, H, N, D))
+                               + 1j * rng.standard_normal((Bsz, H, N, D)))).astype(np.complex64)
+    c = chunk or inp.chunk
+    y = cssd.cssd_forward(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"],
+                          d["dt"], d["A_re"], d["A_im"], d["Dskip"], d["h0"], chunk=c,
+                          return_state=False)[:2]
+    g = cssd.cssd_backward(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"],
+                           d["dt"], d["A_re"], d["A_im"], d["Dskip"], d["h0"], y,
+                           (_dev(gy.real.copy()), _dev(gy.imag.copy())),
+                           None if ghT is None else (_dev(ghT.real.copy()), _dev(ghT.imag.copy())),
+                           chunk=c)
+    torch.cuda.synchronize()
+    n = lambda t: None if t is None else t.double().cpu().numpy()
+    got = {"dx": n(g["dx_re"]) + 1j * n(g["dx_im"]), "dB": n(g["dB_re"]) + 1j * n(g["dB_im"]),
+           "dC": n(g["dC_re"]) + 1j * n(g["dC_im"]), "ddt": n(g["ddt"]),
+           "dA": n(g["dA_re"]) + 1j * n(g["dA_im"]), "dD": n(g["dD"]),
+           "dh0": n(g["dh0_re"]) + 1j * n(g["dh0_im"])}
+    x, Bm, Cm, dt, A, Dk, h0 = inp.complex()
+    want = oracle.backward(x, Bm, Cm, dt, A, Dk, h0, gy.astype(np.complex128),
+                           None if ghT is None else ghT.astype(np.complex128))
+    return got, want
+
+
+def _check(got, want, skip_dD=False):
+    for k in ("dx", "dB", "dC", "ddt", "dA", "dh0") + (() if skip_dD else ("dD",)):
+        err = rel_err(got[k], want[k])
+        log(f"    {k}: rel err {err:.2e}")
+        assert err <= TOL, (k, err)
+
+
+SMALL = [
+    # (B, T, H, D, N, C, with_h0, with_dskip, with_dhT)
+    (1, 1, 1, 16, 16, 16, True, True, True),     # a single step
+    (1, 15, 2, 16, 16, 16, True, True, False),   # T < C
+    (1, 64, 2, 16, 16, 64, False, True, True),   # one chunk
+    (2, 100, 3, 32, 64, 16, True, True, True),   # ragged tail, many chunks
+    (1, 257, 2, 64, 32, 64, False, False, False),
+    (2, 130, 2, 32, 64, 64, True, True, True),
+    (1, 300, 2, 16, 128, 128, True, True, True),  # largest N and C
+    (2, 50, 2, 128, 16, 32, False, True, True),   # largest D
+    (3, 128, 2, 64, 64, 32, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}T{}H{}D{}N{}C{}{}{}{}".format(
+    *c[:6], "_h0" if c[6] else "", "_D" if c[7] else "", "_dhT" if c[8] else ""))
+def test_backward_small_shapes(case):
+    B, T, H, D, N, C, with_h0, with_d, with_dhT = case
+    inp = wl.random_forward(2000 + T, B, T, H, D, N, C, with_h0=with_h0, with_dskip=with_d,
+                            name="bwd")
+    log(f"  backward {case}")
+    got, want = _grads(inp, with_dhT, seed=T)
+    _check(got, want, skip_dD=not with_d)
+
+
+def test_backward_chunk_size_invariance():
+    """The gradients do not depend on the chunk size the scan is evaluated with."""
+    inp = wl.random_forward(31, 2, 128, 3, 32, 32, 16, with_h0=True, name="bwd_cinv")
+    ref = None
+    for C in (16, 32, 64, 128):
+        got, want = _grads(inp, True, seed=5, chunk=C)
+        _check(got, want)
+        if ref is None:
+            ref = got
+        for k in ("dx", "dB", "dC", "ddt", "dA", "dh0"):
+            assert rel_err(got[k], ref[k]) <= TOL, (C, k)
+
+
+def test_backward_mamba_layer_shape_reduced_batch():
+    """The B8 T2048 H48 D64 N64 C64 layer shape at batch 1 and 6 heads, every
+    gradient against the oracle."""
+    inp = wl.random_forward(1, 1, 2048, 6, 64, 64, 64, name="bwd_cfg1")
+    log("  backward B1 T2048 H6 D64 N64 C64")
+    got, want = _grads(inp, True, seed=11)
+    _check(got, want)
