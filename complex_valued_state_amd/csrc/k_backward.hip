@@ -443,8 +443,12 @@ __device__ __forceinline__ void dc_tile(const BwdArgs& a, int64_t chunk, int tt)
 }
 
 // Balanced pairs of row tiles {t, NLT-1-t} per wave, 4 / WPC chunks per block.
+#ifndef CSSD_BWD_WAVES
+#define CSSD_BWD_WAVES 2
+#endif
 template <int C, int N, int D, bool DC>
-__global__ __launch_bounds__(256) void k_bwd_tiles(BwdArgs a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(N * D > 64 * 64 ? 1 : CSSD_BWD_WAVES))) void k_bwd_tiles(BwdArgs a) {
     constexpr int NLT = C / 16;
     constexpr int WPC = NLT >= 2 ? NLT / 2 : 1;
     const int wave = wave_id();
