@@ -72,6 +72,8 @@ def _bind(lib):
     lib.oracle_backward_f64.restype = ctypes.c_int
     lib.oracle_backward_f64.argtypes = [_i64] * 5 + [_d] * 10 + [_d] * 2 + [_d] * 4 + [_d] * 6 \
         + [_d] * 1 + [_d] * 3 + [_d] * 2 + [ctypes.c_int]
+    lib.oracle_phase_scan_f64.restype = ctypes.c_int
+    lib.oracle_phase_scan_f64.argtypes = [_i64] * 4 + [_d] * 6 + [_d] * 4 + [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -233,6 +235,25 @@ def backward(x, Bm, Cm, dt, A, Dskip, h0, dy, dhT=None, nthreads: int = 0, lib=N
             "dC": out["dcr"] + 1j * out["dci"], "ddt": out["ddt"],
             "dA": out["dar"] + 1j * out["dai"], "dD": out["dd"],
             "dh0": out["dh0r"] + 1j * out["dh0i"]}
+
+
+def phase_scan(phi, u, b, psi0=None, nthreads: int = 0, lib=None):
+    """Per-coordinate scan psi_t = sigmoid(u_t) cayley(phi_t) psi_{t-1} + b_t.
+    phi, u: (B,T,H,N) real; b: (B,T,H,N) complex; psi0: (B,H,N) complex or None.
+    Returns (psi (B,T,H,N) complex128, psiT (B,H,N) complex128)."""
+    lib = lib or load()
+    phi = _real(phi, np.shape(phi))
+    Bsz, T, H, N = phi.shape
+    uv = _real(u, (Bsz, T, H, N))
+    br, bi = _planes(b, (Bsz, T, H, N))
+    p0r, p0i = _planes(psi0, (Bsz, H, N)) if psi0 is not None else (None, None)
+    pr = np.empty((Bsz, T, H, N)); pi = np.empty_like(pr)
+    tr = np.empty((Bsz, H, N)); ti = np.empty_like(tr)
+    rc = lib.oracle_phase_scan_f64(Bsz, T, H, N, _p(phi), _p(uv), _p(br), _p(bi), _p(p0r),
+                                   _p(p0i), _p(pr), _p(pi), _p(tr), _p(ti), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_phase_scan_f64 failed")
+    return pr + 1j * pi, tr + 1j * ti
 
 
 def max_threads(lib=None) -> int:

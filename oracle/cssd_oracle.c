@@ -466,6 +466,56 @@ int oracle_backward_f64(int64_t Bsz, int64_t T, int64_t H, int64_t D, int64_t N,
     return failed ? -1 : 0;
 }
 
+/*
+ * The per-coordinate complex scan of the phase-state paper ("Complex Phase-State
+ * Dynamics Reduce the Optimization Steps of Sequence Models", section 5.2,
+ * eq. 2-3, and Algorithm 1):
+ *   lambda_t = (1 + i phi_t) / (1 - i phi_t)    Cayley transform, |lambda| = 1
+ *   alpha_t  = 1 / (1 + e^{-u_t})               selective gate in (0, 1)
+ *   psi_t    = alpha_t lambda_t psi_{t-1} + b_t  every coordinate on its own
+ * evaluated as the plain sequential recurrence (section 5.3's chunked scan is a
+ * way of computing the same trajectory).  Layouts: phi, u [B,T,H,N] real,
+ * b [B,T,H,N] complex (planar), psi0 [B,H,N] complex or NULL (zero); outputs
+ * psi [B,T,H,N] (the state after each step) and psiT [B,H,N] (or NULL).
+ */
+int oracle_phase_scan_f64(int64_t Bsz, int64_t T, int64_t H, int64_t N,
+                          const double *phi, const double *u,
+                          const double *b_re, const double *b_im,
+                          const double *psi0_re, const double *psi0_im,
+                          double *psi_re, double *psi_im,
+                          double *psiT_re, double *psiT_im, int nthreads)
+{
+    if (Bsz <= 0 || T < 0 || H <= 0 || N <= 0)
+        return -1;
+    if (!phi || !u || !b_re || !b_im || !psi_re || !psi_im)
+        return -1;
+    const int64_t HN = H * N;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t bk = 0; bk < Bsz * HN; ++bk) {
+        int64_t b = bk / HN, k = bk % HN;
+        double complex psi = (psi0_re && psi0_im) ? psi0_re[bk] + psi0_im[bk] * I : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t at = (b * T + t) * HN + k;
+            double complex lambda = (1.0 + phi[at] * I) / (1.0 - phi[at] * I);
+            double alpha = 1.0 / (1.0 + exp(-u[at]));
+            psi = alpha * lambda * psi + (b_re[at] + b_im[at] * I);
+            psi_re[at] = creal(psi);
+            psi_im[at] = cimag(psi);
+        }
+        if (psiT_re && psiT_im) {
+            psiT_re[bk] = creal(psi);
+            psiT_im[bk] = cimag(psi);
+        }
+    }
+    return 0;
+}
+
 /* Threads OpenMP would use for a parallel region (1 without OpenMP). */
 int oracle_max_threads(void)
 {

@@ -473,7 +473,86 @@ def pin_golden_modulus_drift(lib):
         assert got < case["upper"], (case, got)
 
 
+# ---------------------------------------------------------------------------
+# f3: the per-coordinate phase-state scan (phase-state paper, section 5.2)
+# ---------------------------------------------------------------------------
+def _phase_coeff(phi, u):
+    """a = sigmoid(u) exp(2i atan(phi)): the Cayley phase through its angle (the
+    page's arg formula) and the gate through logaddexp -- a different route from
+    the oracle's complex division."""
+    return np.exp(-np.logaddexp(0.0, -np.asarray(u))) * np.exp(2j * np.arctan(phi))
+
+
+def pin_phase_unrolled(lib):
+    """psi_T = (prod_t a_t) psi_0 + sum_r (prod_{j>r} a_j) b_r for every prefix,
+    products formed explicitly (section 5.3, eq. 4 unrolled)."""
+    rng = np.random.default_rng(1111)
+    Bsz, T, H, N = 2, 7, 2, 3
+    phi = 2.0 * rng.standard_normal((Bsz, T, H, N))
+    u = 2.0 * rng.standard_normal((Bsz, T, H, N))
+    b = crandn(rng, Bsz, T, H, N)
+    psi0 = crandn(rng, Bsz, H, N)
+    psi, psiT = oracle.phase_scan(phi, u, b, psi0, lib=lib)
+    a = _phase_coeff(phi, u)
+    for t in range(T):
+        want = psi0.copy()
+        for j in range(t + 1):
+            want = want * a[:, j]
+        for r in range(t + 1):
+            term = b[:, r].copy()
+            for j in range(r + 1, t + 1):
+                term = term * a[:, j]
+            want = want + term
+        assert rel_err(psi[:, t], want) < 1e-13, (t, rel_err(psi[:, t], want))
+    assert rel_err(psiT, psi[:, -1]) == 0.0
+
+
+def pin_phase_transport(lib):
+    """Without input the phase is carried exactly (the paper's Lemma 6.2): |psi_T| =
+    |psi_0| prod alpha_t and arg psi_T = arg psi_0 + sum 2 atan(phi_t) mod 2 pi; with
+    the gate fully open the modulus stays |psi_0| over 4096 steps (exact unit
+    modulus of the Cayley transform)."""
+    rng = np.random.default_rng(1212)
+    Bsz, T, H, N = 1, 1024, 2, 4
+    phi = 3.0 * rng.standard_normal((Bsz, T, H, N))
+    u = 4.0 + rng.standard_normal((Bsz, T, H, N))
+    psi0 = crandn(rng, Bsz, H, N)
+    zero = np.zeros((Bsz, T, H, N), dtype=np.complex128)
+    _, psiT = oracle.phase_scan(phi, u, zero, psi0, lib=lib)
+    alpha = np.exp(-np.logaddexp(0.0, -u))
+    mod = np.abs(psi0) * np.prod(alpha, axis=1)
+    assert np.max(np.abs(np.abs(psiT) - mod) / mod) < 1e-12
+    ang = np.angle(psi0) + np.sum(2.0 * np.arctan(phi), axis=1)
+    dang = np.angle(psiT * np.exp(-1j * ang))
+    assert np.max(np.abs(dang)) < 1e-9
+    T2 = 4096
+    phi2 = rng.standard_normal((1, T2, 1, 2))
+    _, psiT2 = oracle.phase_scan(phi2, np.full((1, T2, 1, 2), 60.0),
+                                 np.zeros((1, T2, 1, 2), dtype=np.complex128),
+                                 np.ones((1, 1, 2), dtype=np.complex128), lib=lib)
+    assert np.max(np.abs(np.abs(psiT2) - 1.0)) < 1e-12
+
+
+def pin_phase_golden_gain(lib):
+    """The page's printed gain of a per-coordinate factor 0.99 over 1024 steps
+    (3.4e-5), reached by the scan with gate 0.99 and no rotation."""
+    g = _golden("modulus_drift.json")
+    for case in g["cases"] + g["bounds"]:
+        rho, T = case["rho"], case["steps"]
+        u = np.full((1, T, 1, 1), math.log(rho / (1.0 - rho)))
+        _, psiT = oracle.phase_scan(np.zeros((1, T, 1, 1)), u,
+                                    np.zeros((1, T, 1, 1), dtype=np.complex128),
+                                    np.ones((1, 1, 1), dtype=np.complex128), lib=lib)
+        got = abs(psiT[0, 0, 0])
+        if "printed" in case:
+            sig = case["printed_significant_digits"]
+            assert float(f"{got:.{sig}g}") == case["printed"], (case, got)
+        else:
+            assert got < case["upper"], (case, got)
+
+
 ALL_PINS = [pin_bruteforce, pin_impulse, pin_constant_input, pin_fixed_point,
+            pin_phase_unrolled, pin_phase_transport, pin_phase_golden_gain,
             pin_step_n_against_recurrence, pin_step_infinite_against_recurrence,
             pin_backward_finite_differences, pin_backward_without_initial_state,
             pin_step_constant_input, pin_decay_zero, pin_homogeneous, pin_linearity_and_skip,

@@ -72,6 +72,15 @@ MUTANTS = {
     "backward_dC_uses_previous_state": [
         ("acc += (dy_re[row * D + p] + dy_im[row * D + p] * I) * conj(ht[n * D + p]);",
          "acc += (dy_re[row * D + p] + dy_im[row * D + p] * I) * conj(hp[n * D + p]);")],
+    "phase_cayley_conjugated": [("double complex lambda = (1.0 + phi[at] * I) / (1.0 - phi[at] * I);",
+                                 "double complex lambda = (1.0 - phi[at] * I) / (1.0 + phi[at] * I);")],
+    "phase_gate_inverted": [("double alpha = 1.0 / (1.0 + exp(-u[at]));",
+                             "double alpha = 1.0 / (1.0 + exp(u[at]));")],
+    "phase_input_before_decay": [("psi = alpha * lambda * psi + (b_re[at] + b_im[at] * I);",
+                                  "psi = alpha * lambda * (psi + (b_re[at] + b_im[at] * I));")],
+    "phase_initial_state_ignored": [
+        ("double complex psi = (psi0_re && psi0_im) ? psi0_re[bk] + psi0_im[bk] * I : 0.0;",
+         "double complex psi = 0.0;")],
 }
 
 
