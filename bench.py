@@ -68,6 +68,12 @@ def decode_hbm_bytes(B, H, D, N):
     return B * H * N * D * 2 * 4 * 2 + B * H * (2 * D + 2 * N) * 2 * 4 + B * H * 4
 
 
+def phase_scan_hbm_bytes(B, T, H, N):
+    """Read phi, u, b (16 bytes) and write psi (8 bytes) per coordinate and step;
+    read psi0 and write psiT once."""
+    return B * T * H * N * 24 + B * H * N * 16
+
+
 def chunk_scan_symbol(N, D, C, dtype):
     """The kernel the library launches for the chunk-scan step at this shape (the
     rule of launch_chunk_scan_c: the LDS-staged kernel for fp32 inputs with
@@ -186,6 +192,44 @@ def backward_dxdb_flops(B, T, H, D, N, C):
     nC = -(-T // C)
     tri = C * (C + 1) // 2
     return 8 * B * H * nC * (tri * 2 * (N + D) + 2 * C * N * D)
+
+
+def time_phase_scan(B, T, H, N, steps, warmup, dev, chunk=0, seed=5):
+    """cssd_phase_scan over device-drawn inputs with the distributions of
+    cssd_workloads.phase_inputs; returns (ms per call, per-kernel ms per call)."""
+    import torch
+    import complex_valued_state_amd as cssd
+    import cssd_workloads as wl
+    g = torch.Generator(device=dev).manual_seed(seed)
+    shp = (B, T, H, N)
+    step = torch.pow(10.0, -3.0 + 2.0 * torch.rand((B, T, H, 1), generator=g, device=dev))
+    omega = torch.from_numpy(wl.phase_frequencies(H, N)).to(dev)
+    phi = (0.5 * step * (torch.randn(shp, generator=g, device=dev) + omega)).contiguous()
+    u = torch.randn(shp, generator=g, device=dev) * 2.0 + 1.5
+    b_re = torch.randn(shp, generator=g, device=dev) * math.sqrt(0.5)
+    b_im = torch.randn(shp, generator=g, device=dev) * math.sqrt(0.5)
+    psi0 = (torch.randn((B, H, N), generator=g, device=dev) * 0.25,
+            torch.randn((B, H, N), generator=g, device=dev) * 0.25)
+    outs = (torch.empty(shp, device=dev), torch.empty(shp, device=dev),
+            torch.empty((B, H, N), device=dev), torch.empty((B, H, N), device=dev))
+    ws = torch.empty(max(1, cssd.cssd_phase_scan_workspace_size(B, T, H, N, chunk)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: cssd.cssd_phase_scan(phi, u, b_re, b_im, psi0, chunk=chunk, out=outs,
+                                        workspace=ws, stream=stream)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    with cssd.profile() as prof:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    kern = {k: v / steps for k, v in prof.ms.items() if prof.launches[k]}
+    return ms, kern
 
 
 def time_backward(inp, steps, warmup, dev, seed=9):
@@ -405,6 +449,19 @@ def main():
                        "hbm_GBs": round(dbytes / (cms["step_n"] * 1e-3) / 1e9, 1),
                        "hbm_frac": round(dbytes / (cms["step_n"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "step_infinite": {"ms_per_call": round(cms["step_infinite"], 5)}}
+        progress("timing the phase-state scan")
+        pb, pt, ph, pn = 256, 1024, 16, 16
+        pms, pk = time_phase_scan(pb, pt, ph, pn, args.steps, args.warmup, dev)
+        pbytes = phase_scan_hbm_bytes(pb, pt, ph, pn)
+        pout = pk.get("k_phase_out", pms)
+        extra["phase_scan_B256_T1024_H16_N16"] = {
+            "tokens_per_s": round(pb * pt / (pms * 1e-3), 1), "ms_per_call": round(pms, 5),
+            "kernels_avg_ms": {k: round(v, 5) for k, v in pk.items()},
+            "roofline": {"bound": "hbm", "kernel": "k_phase_out",
+                         "achieved": round(pbytes / (pout * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(pbytes / (pout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": pbytes, "avg_launch_ms": round(pout, 5)}}
         if args.all:
             for name, mk in (("cfg2_long_B1_T16384_H48_N128_C128", wl.config2),
                              ("cfg3_pam_B16_T1024_H12_N128_C64", lambda: wl.config3("re"))):

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libcssd.so")
 CSSD_OK, CSSD_ERR_INVALID_ARG, CSSD_ERR_UNSUPPORTED, CSSD_ERR_WORKSPACE, CSSD_ERR_HIP = range(5)
 CSSD_F32, CSSD_BF16 = 0, 1
 KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
-                "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz")
+                "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz",
+                "k_phase_summary", "k_phase_carry", "k_phase_out")
 
 _lock = threading.Lock()
 _lib = None
@@ -65,6 +66,10 @@ def load_library(path: Optional[str] = None):
         lib.cssd_step_n.argtypes = [_i64] * 5 + [_vp] * 10 + [_vp] * 4 + [_vp]
         lib.cssd_step_infinite.restype = ctypes.c_int
         lib.cssd_step_infinite.argtypes = [_i64] * 4 + [_vp] * 10 + [_vp] * 2 + [_vp]
+        lib.cssd_phase_scan_workspace_size.restype = ctypes.c_int
+        lib.cssd_phase_scan_workspace_size.argtypes = [_i64] * 5 + [ctypes.POINTER(_sz)]
+        lib.cssd_phase_scan.restype = ctypes.c_int
+        lib.cssd_phase_scan.argtypes = [_i64] * 5 + [_vp] * 10 + [_vp, _sz, _vp]
         lib.cssd_profile_enable.restype = ctypes.c_int
         lib.cssd_profile_enable.argtypes = [ctypes.c_int]
         lib.cssd_profile_read.restype = ctypes.c_int
@@ -105,6 +110,16 @@ def cssd_backward_workspace_size(batch: int, seqlen: int, nheads: int, headdim: 
                                                      ctypes.byref(out))
     if st != CSSD_OK:
         raise CSSDError(st, "cssd_backward_workspace_size")
+    return int(out.value)
+
+
+def cssd_phase_scan_workspace_size(batch: int, seqlen: int, nheads: int, dstate: int,
+                                   chunk: int = 0) -> int:
+    out = _sz(0)
+    st = load_library().cssd_phase_scan_workspace_size(batch, seqlen, nheads, dstate, chunk,
+                                                       ctypes.byref(out))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_phase_scan_workspace_size")
     return int(out.value)
 
 
@@ -333,6 +348,57 @@ def cssd_step_infinite(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip
     if st != CSSD_OK:
         raise CSSDError(st, "cssd_step_infinite")
     return y
+
+
+def cssd_phase_scan(phi, u, b_re, b_im, psi0=None, *, chunk: int = 0, return_state: bool = True,
+                    out=None, workspace=None, stream=None):
+    """Per-coordinate scan psi_t = sigmoid(u_t) (1 + i phi_t) / (1 - i phi_t) psi_{t-1} + b_t
+    (see include/cssd.h).
+
+    phi, u, b_re, b_im: (B,T,H,N) float32; psi0: (psi0_re, psi0_im) each (B,H,N)
+    float32, or None.  out: optional (psi_re, psi_im[, psiT_re, psiT_im]).  chunk:
+    segment length, 0 = the library's choice.  Returns (psi_re, psi_im, psiT_re,
+    psiT_im) (the last two None if not return_state)."""
+    torch = _torch()
+    lib = load_library()
+    dev = phi.device
+    Bsz, T, H, N = phi.shape
+    f32 = (torch.float32,)
+    p = {}
+    for name, t in (("phi", phi), ("u", u), ("b_re", b_re), ("b_im", b_im)):
+        p[name] = _check(t, name, (Bsz, T, H, N), f32, dev)
+    if psi0 is not None:
+        p["psi0_re"] = _check(psi0[0], "psi0_re", (Bsz, H, N), f32, dev)
+        p["psi0_im"] = _check(psi0[1], "psi0_im", (Bsz, H, N), f32, dev)
+    else:
+        p["psi0_re"] = p["psi0_im"] = None
+    if out is not None:
+        psi_re, psi_im = out[0], out[1]
+        psiT_re, psiT_im = (out[2], out[3]) if (return_state and len(out) >= 4) else (None, None)
+    else:
+        psi_re = torch.empty((Bsz, T, H, N), dtype=torch.float32, device=dev)
+        psi_im = torch.empty_like(psi_re)
+        psiT_re = psiT_im = None
+    if return_state and psiT_re is None:
+        psiT_re = torch.empty((Bsz, H, N), dtype=torch.float32, device=dev)
+        psiT_im = torch.empty_like(psiT_re)
+    p["psi_re"] = _check(psi_re, "psi_re", (Bsz, T, H, N), f32, dev)
+    p["psi_im"] = _check(psi_im, "psi_im", (Bsz, T, H, N), f32, dev)
+    p["psiT_re"] = None if psiT_re is None else _check(psiT_re, "psiT_re", (Bsz, H, N), f32, dev)
+    p["psiT_im"] = None if psiT_im is None else _check(psiT_im, "psiT_im", (Bsz, H, N), f32, dev)
+    need = cssd_phase_scan_workspace_size(Bsz, T, H, N, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.cssd_phase_scan(Bsz, T, H, N, int(chunk), p["phi"], p["u"], p["b_re"], p["b_im"],
+                             p["psi0_re"], p["psi0_im"], p["psi_re"], p["psi_im"],
+                             p["psiT_re"], p["psiT_im"], workspace.data_ptr(), ws_bytes,
+                             _stream_ptr(stream, dev))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_phase_scan")
+    return psi_re, psi_im, psiT_re, psiT_im
 
 
 class profile:

@@ -462,6 +462,116 @@ int cssd_step_infinite(int64_t batch, int64_t nheads, int64_t headdim, int64_t d
     return CSSD_OK;
 }
 
+namespace {
+
+// Threads that fill the chip at one wave per SIMD (256 CUs x 4 SIMDs x 64 lanes).
+constexpr int64_t kPhaseThreads = 65536;
+
+// Segment length of the phase scan: the caller's chunk (capped at seqlen), or,
+// for chunk = 0, the whole sequence when batch x coordinates alone reach
+// kPhaseThreads, else segments (a multiple of 16 steps) short enough for about
+// four times that many threads (the segmented form reads the inputs twice, so it
+// needs more waves in flight to approach the one-pass bandwidth).
+int64_t phase_segment(int64_t B, int64_t T, int64_t HN, int64_t chunk) {
+    if (chunk > 0) return chunk < T ? chunk : T;
+    const int64_t rows = B * HN;
+    if (rows >= kPhaseThreads) return T;
+    const int64_t want = (4 * kPhaseThreads + rows - 1) / rows;
+    int64_t L = (T + want - 1) / want;
+    L = (L + 15) / 16 * 16;
+    return L < T ? L : T;
+}
+
+int check_phase_shape(int64_t B, int64_t T, int64_t H, int64_t N, int64_t chunk) {
+    if (B <= 0 || T <= 0 || H <= 0 || N <= 0 || chunk < 0) return CSSD_ERR_INVALID_ARG;
+    const int64_t lim = (int64_t)1 << 31, lim40 = (int64_t)1 << 40;
+    if (B > lim || T > lim || H > lim || N > lim) return CSSD_ERR_UNSUPPORTED;
+    const int64_t HN = H * N;
+    if (HN > lim40 || B > lim40 / HN || B * HN > lim40 / T) return CSSD_ERR_UNSUPPORTED;
+    return CSSD_OK;
+}
+
+size_t phase_workspace(int64_t B, int64_t nch, int64_t HN) {
+    if (nch == 1) return 0;
+    return 6 * round_up((size_t)(B * nch * HN) * sizeof(float));
+}
+
+}  // namespace
+
+int cssd_phase_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t dstate, int64_t chunk, size_t* bytes) {
+    if (bytes == nullptr) return CSSD_ERR_INVALID_ARG;
+    const int st = check_phase_shape(batch, seqlen, nheads, dstate, chunk);
+    if (st != CSSD_OK) return st;
+    const int64_t HN = nheads * dstate;
+    const int64_t L = phase_segment(batch, seqlen, HN, chunk);
+    *bytes = phase_workspace(batch, (seqlen + L - 1) / L, HN);
+    return CSSD_OK;
+}
+
+int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstate, int64_t chunk,
+                    const float* phi, const float* u, const float* b_re, const float* b_im,
+                    const float* psi0_re, const float* psi0_im, float* psi_re, float* psi_im,
+                    float* psiT_re, float* psiT_im, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    const int st = check_phase_shape(batch, seqlen, nheads, dstate, chunk);
+    if (st != CSSD_OK) return st;
+    const void* req[] = {phi, u, b_re, b_im, psi_re, psi_im};
+    for (const void* p : req)
+        if (p == nullptr || !aligned(p, 4)) return CSSD_ERR_INVALID_ARG;
+    if ((psi0_re == nullptr) != (psi0_im == nullptr)) return CSSD_ERR_INVALID_ARG;
+    if ((psiT_re == nullptr) != (psiT_im == nullptr)) return CSSD_ERR_INVALID_ARG;
+    if (!aligned(psi0_re, 4) || !aligned(psi0_im, 4) || !aligned(psiT_re, 4) ||
+        !aligned(psiT_im, 4))
+        return CSSD_ERR_INVALID_ARG;
+    // psiT may replace psi0 in place (same plane); nothing else may alias
+    const void* ins[] = {phi, u, b_re, b_im, psi0_re, psi0_im};
+    for (const void* i : ins)
+        if (i == psi_re || i == psi_im) return CSSD_ERR_INVALID_ARG;
+    const void* ins_t[] = {phi, u, b_re, b_im};
+    if (psiT_re != nullptr) {
+        for (const void* i : ins_t)
+            if (i == psiT_re || i == psiT_im) return CSSD_ERR_INVALID_ARG;
+        if (psiT_re == psi0_im || psiT_im == psi0_re) return CSSD_ERR_INVALID_ARG;
+        if (psiT_re == psiT_im || psiT_re == psi_re || psiT_re == psi_im ||
+            psiT_im == psi_re || psiT_im == psi_im)
+            return CSSD_ERR_INVALID_ARG;
+    }
+    if (psi_re == psi_im) return CSSD_ERR_INVALID_ARG;
+
+    cssd::PhaseArgs a;
+    a.B = batch;
+    a.T = seqlen;
+    a.HN = nheads * dstate;
+    a.L = phase_segment(batch, seqlen, a.HN, chunk);
+    a.nch = (seqlen + a.L - 1) / a.L;
+    a.phi = phi; a.u = u; a.b_re = b_re; a.b_im = b_im;
+    a.psi0_re = psi0_re; a.psi0_im = psi0_im;
+    a.psi_re = psi_re; a.psi_im = psi_im; a.psiT_re = psiT_re; a.psiT_im = psiT_im;
+    a.p_re = a.p_im = a.s_re = a.s_im = a.in_re = a.in_im = nullptr;
+    const size_t need = phase_workspace(batch, a.nch, a.HN);
+    if (need > 0) {
+        if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need)
+            return CSSD_ERR_WORKSPACE;
+        const size_t plane = need / 6;
+        char* ws = static_cast<char*>(workspace);
+        float** regions[] = {&a.p_re, &a.p_im, &a.s_re, &a.s_im, &a.in_re, &a.in_im};
+        for (int r = 0; r < 6; ++r) *regions[r] = reinterpret_cast<float*>(ws + r * plane);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.nch > 1) {
+        if (timed(cssd::K_PHASE_SUMMARY, s, [&] { return cssd::launch_phase_summary(a, s); }) !=
+            hipSuccess)
+            return CSSD_ERR_HIP;
+        if (timed(cssd::K_PHASE_CARRY, s, [&] { return cssd::launch_phase_carry(a, s); }) !=
+            hipSuccess)
+            return CSSD_ERR_HIP;
+    }
+    if (timed(cssd::K_PHASE_OUT, s, [&] { return cssd::launch_phase_out(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    return CSSD_OK;
+}
+
 int cssd_profile_enable(int on) {
     Profiler& p = prof();
     std::lock_guard<std::mutex> g(p.mu);
@@ -500,7 +610,8 @@ int cssd_profile_read(double* ms, int64_t* launches, int capacity) {
 const char* cssd_kernel_name(int kernel_id) {
     static const char* names[cssd::K_COUNT] = {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
-        "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz"};
+        "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz",
+        "k_phase_summary", "k_phase_carry", "k_phase_out"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

@@ -7,7 +7,8 @@
 namespace cssd {
 
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
-                K_STEP_INFINITE = 5, K_BWD_DXDB = 6, K_BWD_DC = 7, K_BWD_DZ = 8, K_COUNT = 9 };
+                K_STEP_INFINITE = 5, K_BWD_DXDB = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
+                K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_COUNT = 12 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -45,6 +46,16 @@ struct StepArgs {
     float *h_re, *h_im, *y_re, *y_im;
 };
 
+// The per-coordinate phase scan: HN = nheads * dstate coordinates per batch row,
+// time cut into nch segments of L steps (the last one ragged).
+struct PhaseArgs {
+    int64_t B, T, HN, L, nch;
+    const float *phi, *u, *b_re, *b_im, *psi0_re, *psi0_im;  // psi0 may be NULL
+    float *psi_re, *psi_im, *psiT_re, *psiT_im;               // psiT may be NULL
+    // workspace, [B, nch, HN] each (unused when nch == 1)
+    float *p_re, *p_im, *s_re, *s_im, *in_re, *in_im;
+};
+
 // Number of compute units of the current device (queried once per device).
 hipError_t device_cu_count(int* cus);
 
@@ -63,5 +74,8 @@ hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dz(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_step_infinite(const StepArgs& a, hipStream_t stream);
+hipError_t launch_phase_summary(const PhaseArgs& a, hipStream_t stream);
+hipError_t launch_phase_carry(const PhaseArgs& a, hipStream_t stream);
+hipError_t launch_phase_out(const PhaseArgs& a, hipStream_t stream);
 
 }  // namespace cssd

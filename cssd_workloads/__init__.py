@@ -310,3 +310,71 @@ def decode_steps(seed: int, steps: int, B: int, H: int, D: int, N: int):
         toks = list(ex.map(lambda s: decode_step(seed, s, B, H, D, N), range(steps)))
     return StepInputs(*[np.stack([getattr(t, f.name) for t in toks])
                         for f in dataclasses.fields(StepInputs)])
+
+
+# ---------------------------------------------------------------------------
+# The per-coordinate phase scan (the phase-state paper's H-Mamba layer)
+# ---------------------------------------------------------------------------
+PHASE_TENSORS = ("phi", "u", "b_re", "b_im", "psi0_re", "psi0_im", "dt", "delta")
+_KP = {name: 100 + i for i, name in enumerate(PHASE_TENSORS)}
+
+
+@dataclasses.dataclass
+class PhaseInputs:
+    """phi, u, b (B,T,H,N) float32 planes; psi0 (B,H,N) float32 planes."""
+    phi: np.ndarray
+    u: np.ndarray
+    b_re: np.ndarray
+    b_im: np.ndarray
+    psi0_re: np.ndarray
+    psi0_im: np.ndarray
+
+    @property
+    def shape(self):
+        return self.phi.shape
+
+    def b(self):
+        return self.b_re.astype(np.float64) + 1j * self.b_im.astype(np.float64)
+
+    def psi0(self):
+        return self.psi0_re.astype(np.float64) + 1j * self.psi0_im.astype(np.float64)
+
+
+def phase_frequencies(H: int, N: int) -> np.ndarray:
+    """Per-coordinate base frequencies (H, N): magnitudes on a geometric grid from
+    0.1 to 10 over the N coordinates of a head, signs alternating."""
+    n = np.arange(N, dtype=np.float64)
+    mag = 0.1 * 100.0 ** (n / max(N - 1, 1))
+    sign = np.where(n % 2 == 0, 1.0, -1.0)
+    return np.broadcast_to((sign * mag).astype(np.float32), (H, N)).copy()
+
+
+def phase_inputs(seed: int, B: int, T: int, H: int, N: int) -> PhaseInputs:
+    """Seeded inputs shaped like the phase-state paper's H-Mamba layer (sections
+    5.2, 5.6, 5.7): the phase parameter is half a step size times a shift plus a
+    base frequency, with the step size per (b, t, h) log-uniform on [1e-3, 1e-1]
+    (the page caps it at 0.1), the shift N(0, 1) per coordinate and the base
+    frequencies of ``phase_frequencies``; gate logits u ~ N(1.5, 2^2) (gates from
+    about 0.1 to 0.99); b ~ N(0, 1/2) per plane; psi0 a complex normal draw per
+    (h, n), scaled to unit norm per head and shared by every batch row."""
+    shp = (B, T, H, N)
+    with ThreadPoolExecutor(_WORKERS) as ex:
+        fut = {
+            "delta": ex.submit(_normal, seed, _KP["delta"], shp),
+            "u": ex.submit(_normal, seed, _KP["u"], shp, 2.0),
+            "b_re": ex.submit(_normal, seed, _KP["b_re"], shp, _HALF_STD),
+            "b_im": ex.submit(_normal, seed, _KP["b_im"], shp, _HALF_STD),
+        }
+        r = {k: f.result() for k, f in fut.items()}
+    lg = _rng(seed, _KP["dt"]).random((B, T, H, 1), dtype=np.float32)
+    step = np.power(np.float32(10.0), np.float32(-3.0) + np.float32(2.0) * lg)
+    phi = np.float32(0.5) * step * (r["delta"] + phase_frequencies(H, N)[None, None])
+    u = r["u"] + np.float32(1.5)
+    z_re = _normal(seed, _KP["psi0_re"], (H, N))
+    z_im = _normal(seed, _KP["psi0_im"], (H, N))
+    nrm = np.sqrt(np.sum(z_re.astype(np.float64) ** 2 + z_im.astype(np.float64) ** 2, axis=1,
+                         keepdims=True))
+    p_re = np.broadcast_to((z_re / nrm).astype(np.float32), (B, H, N)).copy()
+    p_im = np.broadcast_to((z_im / nrm).astype(np.float32), (B, H, N)).copy()
+    return PhaseInputs(phi.astype(np.float32), u.astype(np.float32), r["b_re"], r["b_im"],
+                       p_re, p_im)

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 102 /* major*100 + minor */
+#define CSSD_VERSION 103 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
@@ -271,8 +271,48 @@ int cssd_step_infinite(int64_t batch, int64_t nheads, int64_t headdim, int64_t d
                        float *y_re, float *y_im, void *stream);
 
 /*
+ * The per-coordinate complex recurrence of the phase-state paper ("Complex
+ * Phase-State Dynamics Reduce the Optimization Steps of Sequence Models",
+ * section 5.2, eq. 2 and 3): every coordinate k of every (batch, head) row
+ * evolves on its own,
+ *     lambda = (1 + i phi) / (1 - i phi)    (Cayley transform, |lambda| = 1)
+ *     alpha  = 1 / (1 + exp(-u))            (gate in (0, 1))
+ *     psi_t  = alpha_t lambda_t psi_{t-1} + b_t
+ * and every state psi_1..psi_T is returned.  The evaluation follows section
+ * 5.3: time is cut into segments, each segment's end state seeds the next.
+ * Arguments (device pointers, fp32, planar complex, row-major):
+ *   phi, u          [B,T,H,N] phase parameter and gate logit (any finite values)
+ *   b_re, b_im      [B,T,H,N] input term b_t
+ *   psi0_re/_im     [B,H,N] initial state, or both NULL (zero)
+ *   psi_re, psi_im  [B,T,H,N] the state after each step (written)
+ *   psiT_re/_im     [B,H,N] the final state, or both NULL (not written); may be
+ *                   the same arrays as psi0_re/_im (the state advances in place)
+ *   chunk           segment length in steps; 0 lets the library choose (the
+ *                   whole sequence in one pass when batch*H*N >= 65536, else
+ *                   shorter segments for parallelism); chunk >= seqlen is one
+ *                   pass.  The result is the same up to rounding.
+ *   workspace       >= cssd_phase_scan_workspace_size bytes (0 for one pass,
+ *                   then workspace may be NULL), 256-byte aligned
+ * Within a segment the recurrence is stepped forward in fp32; no reciprocal of a
+ * cumulative product is formed, so the page's floor on the log-magnitude of
+ * that product is not needed and the trajectory is exact up to rounding, also
+ * where the product underflows.  Limits: batch*seqlen*H*N < 2^40.  Alignment:
+ * element size.  Outputs may not alias inputs except psiT on psi0.
+ */
+int cssd_phase_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t dstate, int64_t chunk, size_t *bytes);
+int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstate,
+                    int64_t chunk,
+                    const float *phi, const float *u,
+                    const float *b_re, const float *b_im,
+                    const float *psi0_re, const float *psi0_im,
+                    float *psi_re, float *psi_im,
+                    float *psiT_re, float *psiT_im,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Optional per-kernel timing (a measurement aid, not part of the operation).
- * While enabled, every kernel launch of cssd_forward/cssd_step is bracketed by
+ * While enabled, every kernel launch of every entry point is bracketed by
  * two hipEvents recorded on the caller's stream.  cssd_profile_read waits for
  * the recorded events, writes the accumulated milliseconds and launch counts
  * per kernel id into ms[k] and launches[k] for k < min(capacity, number of
@@ -280,7 +320,8 @@ int cssd_step_infinite(int64_t batch, int64_t nheads, int64_t headdim, int64_t d
  * negative status on error).  Kernel ids: 0 cumsum, 1 chunk_state,
  * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite,
  * 6 bwd_dxdb, 7 bwd_dc, 8 bwd_dz (cssd_backward also runs ids 0-2, and 1 and 2
- * a second time in their adjoint modes).
+ * a second time in their adjoint modes), 9 phase_summary, 10 phase_carry,
+ * 11 phase_out (cssd_phase_scan).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).
  */

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("cssd_forward", "cssd_backward", "cssd_backward_workspace_size",
-                     "cssd_step", "cssd_step_n", "cssd_step_infinite",
+                     "cssd_step", "cssd_step_n", "cssd_step_infinite", "cssd_phase_scan",
+                     "cssd_phase_scan_workspace_size",
                      "cssd_forward_workspace_size", "cssd_status_string", "cssd_version"):
         assert required in names
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 102
+    assert lib.cssd_version() == 103
     for st in range(5):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -179,11 +180,59 @@ def test_backward_validation(lib):
     assert lib.cssd_backward(*args(bad)) == 1
 
 
+def _phase_ws(lib, *shape):
+    n = ctypes.c_size_t(0)
+    st = lib.cssd_phase_scan_workspace_size(*shape, ctypes.byref(n))
+    return st, n.value
+
+
+def test_phase_scan_workspace_size(lib):
+    # one pass over the sequence needs no workspace: batch x coordinates fill the chip
+    assert _phase_ws(lib, 256, 1024, 16, 16, 0) == (0, 0)
+    assert _phase_ws(lib, 4, 100, 3, 16, 200) == (0, 0)          # chunk >= seqlen
+    # explicit segments of 16 steps: 7 segments, six fp32 planes of (B, 7, H*N)
+    assert _phase_ws(lib, 2, 100, 4, 16, 16) == (0, 6 * _align(2 * 7 * 64 * 4))
+    # automatic segments for a small batch are a multiple of 16 steps
+    st, n = _phase_ws(lib, 1, 4096, 2, 8, 0)
+    assert st == 0 and n > 0 and n % (6 * 256) == 0
+    assert _phase_ws(lib, 0, 10, 1, 1, 0)[0] == 1
+    assert _phase_ws(lib, 1, 10, 1, 1, -1)[0] == 1
+    assert _phase_ws(lib, 1 << 20, 1 << 20, 1, 2, 0)[0] == 2     # 2^41 elements per plane
+    assert lib.cssd_phase_scan_workspace_size(1, 10, 1, 1, 0, None) == 1
+
+
+def test_phase_scan_validation(lib):
+    base = 0x10000000
+    p = [base + 0x100000 * i for i in range(12)]
+    ins, psi0, psi, psiT = p[:4], p[4:6], p[6:8], p[8:10]
+    ws = 0x20000000
+    call = lambda ins=ins, psi0=psi0, psi=psi, psiT=psiT, shape=(2, 64, 2, 16, 16), wsb=1 << 30, w=ws: \
+        lib.cssd_phase_scan(*shape, *ins, *psi0, *psi, *psiT, w, wsb, None)
+    assert call(shape=(0, 64, 2, 16, 16)) == 1
+    assert call(shape=(2, 64, 2, 16, -1)) == 1
+    bad = list(ins); bad[1] = None                                  # u missing
+    assert call(ins=bad) == 1
+    bad = list(ins); bad[0] += 2                                    # phi misaligned
+    assert call(ins=bad) == 1
+    assert call(psi0=[psi0[0], None]) == 1                          # half a state
+    assert call(psiT=[None, psiT[1]]) == 1
+    assert call(psi=[ins[2], psi[1]]) == 1                          # psi aliases b
+    assert call(psi=[psi[0], psi[0]]) == 1
+    assert call(psi=[psi0[1], psi[1]]) == 1                         # psi aliases psi0
+    assert call(psiT=[ins[0], psiT[1]]) == 1                        # psiT aliases phi
+    assert call(psiT=[psi0[1], psi0[0]]) == 1                       # planes swapped
+    assert call(psiT=[psi[0], psiT[1]]) == 1
+    assert call(w=None) == 3                                        # segments need workspace
+    assert call(wsb=16) == 3
+    assert call(w=ws + 64) == 3
+
+
 def test_profiler_without_launches(lib):
     import complex_valued_state_amd as cssd
     with cssd.profile() as prof:
         pass
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
-    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(9) is None
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(12) is None
     assert lib.cssd_kernel_name(5) == b"k_step_infinite"
+    assert lib.cssd_kernel_name(11) == b"k_phase_out"
