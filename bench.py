@@ -10,9 +10,13 @@ Inputs are seeded synthetic data already resident in HBM when timing starts.
 Prints ONE JSON line.  Per-kernel durations come from HIP events the library
 records around each launch on the launch stream during the timed region.
 
-Extra figures in the same line: the bf16-input variant of the same workload,
-the decode step at batch 256 x 48 heads x N128 x D64 over 512 pre-staged tokens,
-and (with --all) the long-sequence and phase-associative-memory workloads.
+Extra figures in the same line: the bf16-input variant of the same workload, the
+backward pass of the same workload, the decode step at batch 256 x 48 heads x
+N128 x D64 over 512 pre-staged tokens, the constant-input calls at that shape,
+the per-coordinate phase-state scan at 256 x 1024 x 16 x 16, and (with --all)
+the long-sequence and phase-associative-memory workloads.  "traffic" figures are
+HBM bytes per launch from committed rocprofv3 counter runs (profiles/traffic.json),
+null once the kernel's sources have changed since.
 """
 from __future__ import annotations
 
@@ -30,13 +34,18 @@ sys.path.insert(0, ROOT)
 METRIC = "complex SSD fwd tokens/s at B8 T2048 H48; % of MFMA/HBM roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
-# source files that make up each kernel (besides the shared device/launch headers)
-KERNEL_SRC = {"k_chunk_scan": ("k_chunk_scan.h", "k_chunk_scan_lds.h", "k_chunk_scan.hip",
-                               "k_chunk_scan_c16.hip",
-                               "k_chunk_scan_c32.hip", "k_chunk_scan_c64.hip",
-                               "k_chunk_scan_c128.hip"),
+# source files that make up each kernel (besides the shared device/launch headers),
+# by the kernel's name stem as rocprofv3 reports it
+_SCAN_SRC = ("k_chunk_scan.h", "k_chunk_scan_lds.h", "k_chunk_scan.hip", "k_chunk_scan_c16.hip",
+             "k_chunk_scan_c32.hip", "k_chunk_scan_c64.hip", "k_chunk_scan_c128.hip")
+KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_chunk_state": ("k_chunk_state.hip",), "k_state_pass": ("k_state_pass.hip",),
-              "k_cumsum": ("k_cumsum.hip",), "k_step": ("k_step.hip",)}
+              "k_cumsum": ("k_cumsum.hip",), "k_step": ("k_step.hip",),
+              "k_step_infinite": ("k_step.hip",),
+              "k_bwd_tiles": ("k_backward.hip",), "k_bwd_zbound": ("k_backward.hip",),
+              "k_bwd_dz": ("k_backward.hip",), "k_bwd_reduce": ("k_backward.hip",),
+              "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
+              "k_phase_out": ("k_phase_scan.hip",)}
 
 
 # ---------------------------------------------------------------------------
@@ -83,25 +92,27 @@ def chunk_scan_symbol(N, D, C, dtype):
     return f"k_chunk_scan<cssd::In{'F32' if dtype == 'f32' else 'BF16'}, {C}, {N}, {D}>"
 
 
-def src_hash(name):
+def src_hash(symbol):
+    """Hash of the sources of the kernel named `symbol` (its stem before any '<')."""
     d = os.path.join(ROOT, "complex_valued_state_amd", "csrc")
     h = hashlib.sha256()
-    for f in KERNEL_SRC[name] + ("cssd_device.h", "cssd_launch.h"):
+    for f in KERNEL_SRC[symbol.split("<")[0]] + ("cssd_device.h", "cssd_launch.h"):
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(name, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    none exist or the kernel source changed since they were taken."""
+def load_traffic(symbol):
+    """HBM bytes per launch of the kernel `symbol` (as rocprofv3 names it) from the
+    committed counter runs over this benchmark, or None when there are none or the
+    kernel's sources changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(f"{name}/{workload}")
+        rec = json.load(open(path)).get(symbol)
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("src_sha256_16") != src_hash(name):
+    if not rec or rec.get("src_sha256_16") != src_hash(symbol):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -381,8 +392,7 @@ def main():
     k2_ms = kern.get("k_chunk_scan")
     k2_flops = chunk_scan_flops(B, T, H, D, N, C)
     achieved = k2_flops / (k2_ms * 1e-3) / 1e12
-    workload = "cfg1_mamba_B8_T2048_H48_D64_N64_C64_f32"
-    traffic = load_traffic("k_chunk_scan", workload)
+    traffic = load_traffic(chunk_scan_symbol(N, D, C, "f32"))
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -428,6 +438,8 @@ def main():
                          "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(bfl / (bk["k_bwd_dxdb"] * 1e-3) / 1e12
                                        / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "symbol": f"k_bwd_tiles<{C}, {N}, {D}, false>",
+                         "traffic": load_traffic(f"k_bwd_tiles<{C}, {N}, {D}, false>"),
                          "algorithmic_flops_per_launch": bfl,
                          "avg_launch_ms": round(bk["k_bwd_dxdb"], 5)}}
         progress("timing the decode step")
@@ -436,6 +448,8 @@ def main():
         extra["decode_B256_H48_N128_D64"] = {
             "tokens_per_s": round(d4["B"] / (dms * 1e-3), 1), "ms_per_token_step": round(dms, 5),
             "roofline": {"bound": "hbm", "kernel": "k_step",
+                         "symbol": f"k_step<{d4['N']}, {d4['D']}>",
+                         "traffic": load_traffic(f"k_step<{d4['N']}, {d4['D']}>"),
                          "achieved": round(dbytes / (dkms * 1e-3) / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(dbytes / (dkms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -457,7 +471,8 @@ def main():
         extra["phase_scan_B256_T1024_H16_N16"] = {
             "tokens_per_s": round(pb * pt / (pms * 1e-3), 1), "ms_per_call": round(pms, 5),
             "kernels_avg_ms": {k: round(v, 5) for k, v in pk.items()},
-            "roofline": {"bound": "hbm", "kernel": "k_phase_out",
+            "roofline": {"bound": "hbm", "kernel": "k_phase_out", "symbol": "k_phase_out",
+                         "traffic": load_traffic("k_phase_out"),
                          "achieved": round(pbytes / (pout * 1e-3) / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(pbytes / (pout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
