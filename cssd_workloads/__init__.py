@@ -378,3 +378,40 @@ def phase_inputs(seed: int, B: int, T: int, H: int, N: int) -> PhaseInputs:
     p_im = np.broadcast_to((z_im / nrm).astype(np.float32), (B, H, N)).copy()
     return PhaseInputs(phi.astype(np.float32), u.astype(np.float32), r["b_re"], r["b_im"],
                        p_re, p_im)
+
+
+# ---------------------------------------------------------------------------
+# Causal Born attention (the phase-state paper's H-Transformer layer)
+# ---------------------------------------------------------------------------
+BORN_TENSORS = ("q_re", "q_im", "k_re", "k_im", "v_re", "v_im", "tau")
+_KB = {name: 200 + i for i, name in enumerate(BORN_TENSORS)}
+
+
+@dataclasses.dataclass
+class BornInputs:
+    """q, k, v (B,T,H,D) float32 planes; tau (B,T,H) float32."""
+    q_re: np.ndarray
+    q_im: np.ndarray
+    k_re: np.ndarray
+    k_im: np.ndarray
+    v_re: np.ndarray
+    v_im: np.ndarray
+    tau: np.ndarray
+
+    def complex(self):
+        c = lambda r, i: r.astype(np.float64) + 1j * i.astype(np.float64)
+        return (c(self.q_re, self.q_im), c(self.k_re, self.k_im), c(self.v_re, self.v_im),
+                self.tau.astype(np.float64))
+
+
+def born_inputs(seed: int, B: int, T: int, H: int, D: int) -> BornInputs:
+    """Seeded inputs shaped like the phase-state paper's H-Transformer layer
+    (sections 5.5, 5.7): complex queries, keys and values N(0, 1/2) per plane,
+    and a temperature per (b, t, h) uniform on [0.5, 2)."""
+    shp = (B, T, H, D)
+    with ThreadPoolExecutor(_WORKERS) as ex:
+        fut = {n: ex.submit(_normal, seed, _KB[n], shp, _HALF_STD) for n in BORN_TENSORS[:6]}
+        r = {k: f.result() for k, f in fut.items()}
+    tau = np.float32(0.5) + np.float32(1.5) * _rng(seed, _KB["tau"]).random((B, T, H),
+                                                                          dtype=np.float32)
+    return BornInputs(r["q_re"], r["q_im"], r["k_re"], r["k_im"], r["v_re"], r["v_im"], tau)

@@ -17,6 +17,10 @@ at the top of ``cssd_oracle.c``:
     h_t = a_t h_{t-1} + B_t (x) x_t          (Mamba-3-Lite docs, "SSD Theory",
     y_t = sum_n C_t[n] h_t[n,:] + D x_t       section 2; skip term from the
                                               burn-mamba step_constant module)
+
+with its constant-input forms, its gradients, the phase-state paper's
+per-coordinate Cayley-phase scan (section 5.2) and its causal Born attention
+(section 5.5, eq. 5).
 """
 from __future__ import annotations
 
@@ -74,6 +78,9 @@ def _bind(lib):
         + [_d] * 1 + [_d] * 3 + [_d] * 2 + [ctypes.c_int]
     lib.oracle_phase_scan_f64.restype = ctypes.c_int
     lib.oracle_phase_scan_f64.argtypes = [_i64] * 4 + [_d] * 6 + [_d] * 4 + [ctypes.c_int]
+    lib.oracle_born_attention_f64.argtypes = [_i64] * 4 + [_d] * 7 + [_d] * 2 + [ctypes.c_int]
+    lib.oracle_born_attention_rows_f64.argtypes = [_i64] * 4 + [_d] * 7 + [_i64,
+                                                  ctypes.POINTER(_i64)] + [_d] * 2 + [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -254,6 +261,52 @@ def phase_scan(phi, u, b, psi0=None, nthreads: int = 0, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_phase_scan_f64 failed")
     return pr + 1j * pi, tr + 1j * ti
+
+
+def born_attention(q, k, v, tau=None, nthreads: int = 0, lib=None):
+    """Causal Born attention psi_i = sum_{j<=i} s_ij v_j / sum_{j<=i} s_ij with
+    s_ij = |<q_i|k_j>|^2 / (D tau_i).  q, k, v: (B,T,H,D) complex; tau: (B,T,H)
+    real or None.  Returns psi (B,T,H,D) complex128."""
+    lib = lib or load()
+    q = np.asarray(q)
+    Bsz, T, H, D = q.shape
+    qr, qi = _planes(q)
+    kr, ki = _planes(k, (Bsz, T, H, D))
+    vr, vi = _planes(v, (Bsz, T, H, D))
+    tv = _real(tau, (Bsz, T, H)) if tau is not None else None
+    outr = np.empty((Bsz, T, H, D)); outi = np.empty_like(outr)
+    rc = lib.oracle_born_attention_f64(Bsz, T, H, D, _p(qr), _p(qi), _p(kr), _p(ki), _p(vr), _p(vi),
+                                       _p(tv), _p(outr), _p(outi), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_born_attention_f64 failed")
+    return outr + 1j * outi
+
+
+def born_attention_rows(q, k, v, tau, rows, nthreads: int = 0, lib=None):
+    """born_attention for the listed rows only: rows is an (M, 3) integer array
+    of (b, t, h); returns (M, D) complex128.  The planes may be given as
+    (re, im) pairs of float arrays to avoid forming complex copies."""
+    lib = lib or load()
+    pl = lambda z: tuple(np.ascontiguousarray(a, dtype=np.float64) for a in z) \
+        if isinstance(z, tuple) else _planes(z)
+    qr, qi = pl(q)
+    Bsz, T, H, D = qr.shape
+    kr, ki = pl(k)
+    vr, vi = pl(v)
+    for a in (qi, kr, ki, vr, vi):
+        if a.shape != (Bsz, T, H, D):
+            raise ValueError("q, k, v planes must share one (B,T,H,D) shape")
+    tv = _real(tau, (Bsz, T, H)) if tau is not None else None
+    rw = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    M = rw.shape[0]
+    outr = np.empty((M, D)); outi = np.empty_like(outr)
+    rc = lib.oracle_born_attention_rows_f64(Bsz, T, H, D, _p(qr), _p(qi), _p(kr), _p(ki), _p(vr),
+                                            _p(vi), _p(tv), M,
+                                            rw.ctypes.data_as(ctypes.POINTER(_i64)), _p(outr),
+                                            _p(outi), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_born_attention_rows_f64 failed")
+    return outr + 1j * outi
 
 
 def max_threads(lib=None) -> int:

@@ -34,6 +34,10 @@
  *
  * Parallelism: OpenMP over the independent (batch, head) sequences only; the
  * loop over time inside one sequence is the plain serial recurrence.
+ *
+ * Later in this file, each with its own sources: the constant-input closed forms,
+ * the reverse-mode gradients of the recurrence, the phase-state paper's
+ * per-coordinate scan and its causal Born attention.
  */
 #include <math.h>
 #include <stddef.h>
@@ -514,6 +518,104 @@ int oracle_phase_scan_f64(int64_t Bsz, int64_t T, int64_t H, int64_t N,
         }
     }
     return 0;
+}
+
+/*
+ * Causal Born attention of the phase-state paper ("Complex Phase-State Dynamics
+ * Reduce the Optimization Steps of Sequence Models", section 5.5, eq. 5, and
+ * Appendix A, Algorithm 3), per (batch, head):
+ *   s_ij  = |<q_i|k_j>|^2 / (D tau_i)  for j <= i,   <q|k> = sum_d conj(q_d) k_d
+ *   psi_i = (sum_{j<=i} s_ij v_j) / (sum_{j<=i} s_ij)
+ * computed row by row exactly as written: every overlap, its squared modulus,
+ * the weighted sum and the normalising sum, in fp64.  A row whose scores are
+ * all zero (0/0) is returned as zero.  Layouts: q, k, v [B,T,H,D] complex
+ * (planar); tau [B,T,H] or NULL (1); out [B,T,H,D].
+ */
+static void born_row(int64_t T, int64_t H, int64_t D, int64_t b, int64_t h, int64_t i,
+                     const double *q_re, const double *q_im, const double *k_re,
+                     const double *k_im, const double *v_re, const double *v_im,
+                     const double *tau, double *o_re, double *o_im)
+{
+    const int64_t qi = ((b * T + i) * H + h) * D;
+    const double t = tau ? tau[(b * T + i) * H + h] : 1.0;
+    double complex *num = calloc((size_t)D, sizeof(double complex));
+    double den = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+        const int64_t kj = ((b * T + j) * H + h) * D;
+        double complex overlap = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            overlap += conj(q_re[qi + d] + q_im[qi + d] * I) * (k_re[kj + d] + k_im[kj + d] * I);
+        const double mod = cabs(overlap);
+        const double sij = mod * mod / ((double)D * t);
+        for (int64_t d = 0; d < D; ++d)
+            num[d] += sij * (v_re[kj + d] + v_im[kj + d] * I);
+        den += sij;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        const double complex o = den != 0.0 ? num[d] / den : 0.0;
+        o_re[d] = creal(o);
+        o_im[d] = cimag(o);
+    }
+    free(num);
+}
+
+int oracle_born_attention_f64(int64_t Bsz, int64_t T, int64_t H, int64_t D,
+                              const double *q_re, const double *q_im,
+                              const double *k_re, const double *k_im,
+                              const double *v_re, const double *v_im,
+                              const double *tau, double *out_re, double *out_im, int nthreads)
+{
+    if (Bsz <= 0 || T <= 0 || H <= 0 || D <= 0)
+        return -1;
+    if (!q_re || !q_im || !k_re || !k_im || !v_re || !v_im || !out_re || !out_im)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < Bsz * T * H; ++r) {
+        const int64_t b = r / (T * H), i = (r / H) % T, h = r % H;
+        const int64_t at = r * D;  /* (b, i, h) row of [B,T,H,D] */
+        born_row(T, H, D, b, h, i, q_re, q_im, k_re, k_im, v_re, v_im, tau, out_re + at, out_im + at);
+    }
+    return 0;
+}
+
+/*
+ * The same output for a list of rows only: rows[3m..3m+2] = (b, i, h); the row's
+ * D outputs go to out_re/out_im[m * D ...].  For checking sampled rows of large
+ * problems.
+ */
+int oracle_born_attention_rows_f64(int64_t Bsz, int64_t T, int64_t H, int64_t D,
+                                   const double *q_re, const double *q_im,
+                                   const double *k_re, const double *k_im,
+                                   const double *v_re, const double *v_im,
+                                   const double *tau, int64_t nrows, const int64_t *rows,
+                                   double *out_re, double *out_im, int nthreads)
+{
+    if (Bsz <= 0 || T <= 0 || H <= 0 || D <= 0 || nrows < 0 || !rows)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|| : failed)
+    for (int64_t m = 0; m < nrows; ++m) {
+        const int64_t b = rows[3 * m], i = rows[3 * m + 1], h = rows[3 * m + 2];
+        if (b < 0 || b >= Bsz || i < 0 || i >= T || h < 0 || h >= H) {
+            failed = 1;
+            continue;
+        }
+        born_row(T, H, D, b, h, i, q_re, q_im, k_re, k_im, v_re, v_im, tau, out_re + m * D,
+                 out_im + m * D);
+    }
+    return failed ? -1 : 0;
 }
 
 /* Threads OpenMP would use for a parallel region (1 without OpenMP). */

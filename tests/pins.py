@@ -551,8 +551,119 @@ def pin_phase_golden_gain(lib):
             assert got < case["upper"], (case, got)
 
 
+# ---------------------------------------------------------------------------
+# f4: causal Born attention (phase-state paper, section 5.5 eq. 5, Algorithm 3)
+# ---------------------------------------------------------------------------
+def _dft_keys(D):
+    """Orthonormal keys with unit-modulus phases: row j of the D-point DFT / sqrt(D)."""
+    n = np.arange(D)
+    return np.exp(2j * np.pi * np.outer(n, n) / D) / math.sqrt(D)
+
+
+def pin_born_orthogonal_keys(lib):
+    """With orthonormal keys and each query a multiple of one earlier key, the
+    Born score is nonzero only for that key, so the output is exactly that key's
+    value (lossless retrieval).  Keys are DFT rows, whose complex phases differ
+    coordinate by coordinate, so an overlap taken without the conjugate fails."""
+    rng = np.random.default_rng(2121)
+    for D in (8, 16):
+        T, H, Bsz = D, 2, 2
+        K = _dft_keys(D)
+        k = np.broadcast_to(K[None, :, None, :], (Bsz, T, H, D)).copy()
+        v = crandn(rng, Bsz, T, H, D)
+        pick = np.array([[[rng.integers(0, i + 1) for _ in range(H)] for i in range(T)]
+                         for _ in range(Bsz)])
+        c = crandn(rng, Bsz, T, H) * 3.0
+        q = c[..., None] * K[pick]
+        tau = 0.5 + rng.random((Bsz, T, H))
+        out = oracle.born_attention(q, k, v, tau, lib=lib)
+        want = np.take_along_axis(v, pick[..., None], axis=1)
+        assert np.max(np.abs(out - want)) < 1e-12, np.max(np.abs(out - want))
+
+
+def pin_born_two_state_interference(lib):
+    """The page's two-state computation (section 5.5): for a key
+    (phi_1 + e^{i theta} phi_2)/sqrt 2 and the query (phi_1 + phi_2)/sqrt 2 the Born
+    weight is (1 + cos theta)/2, falling to 0 at theta = pi; a second key phi_1 has
+    weight 1/2.  So psi_1 = (p(theta) v_0 + v_1 / 2) / (p(theta) + 1/2), and the
+    first key is extinguished by phase opposition at theta = pi."""
+    D = 4
+    phi1, phi2 = np.eye(D)[0].astype(complex), np.eye(D)[1].astype(complex)
+    v = np.zeros((1, 2, 1, D), dtype=complex)
+    v[0, 0, 0] = [1.0, 2.0j, -1.0, 0.5]
+    v[0, 1, 0] = [0.0, 1.0, 1.0j, -2.0]
+    for theta in np.linspace(0.0, math.pi, 9):
+        k = np.zeros((1, 2, 1, D), dtype=complex)
+        k[0, 0, 0] = (phi1 + np.exp(1j * theta) * phi2) / math.sqrt(2)
+        k[0, 1, 0] = phi1
+        q = np.zeros_like(k)
+        q[0, 0, 0] = phi1
+        q[0, 1, 0] = (phi1 + phi2) / math.sqrt(2)
+        out = oracle.born_attention(q, k, v, None, lib=lib)
+        p = 0.5 * (1.0 + math.cos(theta))
+        want = (p * v[0, 0, 0] + 0.5 * v[0, 1, 0]) / (p + 0.5)
+        assert np.max(np.abs(out[0, 1, 0] - want)) < 1e-14, (theta, out[0, 1, 0], want)
+    assert np.max(np.abs(out[0, 1, 0] - v[0, 1, 0])) < 1e-14   # theta = pi
+    assert np.max(np.abs(out[0, 0, 0] - v[0, 0, 0])) < 1e-14   # the first row sees only itself
+
+
+def pin_born_density_matrix_form(lib):
+    """Brute force through the density-matrix form the page gives for the Born
+    score (section 5.5: the score is tr(M rho), linear in rho = |q><q|, here with
+    M = |k><k|): tiny problems with the score formed as a trace of a matrix
+    product and the causal normalisation written as explicit loops."""
+    rng = np.random.default_rng(2222)
+    Bsz, T, H, D = 2, 6, 2, 3
+    q, k, v = crandn(rng, Bsz, T, H, D), crandn(rng, Bsz, T, H, D), crandn(rng, Bsz, T, H, D)
+    tau = 0.3 + rng.random((Bsz, T, H))
+    out = oracle.born_attention(q, k, v, tau, lib=lib)
+    for b in range(Bsz):
+        for h in range(H):
+            for i in range(T):
+                rho = np.outer(q[b, i, h], np.conj(q[b, i, h]))
+                num = np.zeros(D, dtype=complex)
+                den = 0.0
+                for j in range(i + 1):
+                    M = np.outer(k[b, j, h], np.conj(k[b, j, h]))
+                    sij = np.trace(M @ rho).real / (D * tau[b, i, h])
+                    num += sij * v[b, j, h]
+                    den += sij
+                assert np.max(np.abs(out[b, i, h] - num / den)) < 1e-13
+
+
+def pin_born_invariances(lib):
+    """Properties of eq. 5 at a random size: the temperature and the factor D cancel
+    in the normalisation (rescaling tau per row changes nothing); a global phase on
+    any query or key changes no squared modulus; row i ignores keys and values after
+    i; equal values are returned unchanged; the first row returns its own value."""
+    rng = np.random.default_rng(2323)
+    Bsz, T, H, D = 2, 40, 3, 8
+    q, k, v = crandn(rng, Bsz, T, H, D), crandn(rng, Bsz, T, H, D), crandn(rng, Bsz, T, H, D)
+    tau = 0.5 + rng.random((Bsz, T, H))
+    base = oracle.born_attention(q, k, v, tau, lib=lib)
+    scaled = oracle.born_attention(q, k, v, tau * np.exp(3.0 * rng.standard_normal(tau.shape)),
+                                   lib=lib)
+    assert np.max(np.abs(scaled - base)) < 1e-12
+    ph = lambda *s: np.exp(1j * rng.uniform(-math.pi, math.pi, s))
+    rot = oracle.born_attention(q * ph(Bsz, T, H, 1), k * ph(Bsz, T, H, 1), v, tau, lib=lib)
+    assert np.max(np.abs(rot - base)) < 1e-12
+    i0 = 17
+    k2, v2 = k.copy(), v.copy()
+    k2[:, i0 + 1:] = crandn(rng, Bsz, T - i0 - 1, H, D)
+    v2[:, i0 + 1:] = crandn(rng, Bsz, T - i0 - 1, H, D)
+    causal = oracle.born_attention(q, k2, v2, tau, lib=lib)
+    assert np.array_equal(causal[:, :i0 + 1], base[:, :i0 + 1])
+    assert np.max(np.abs(causal[:, i0 + 1:] - base[:, i0 + 1:])) > 1e-3
+    same = np.broadcast_to(crandn(rng, Bsz, 1, H, D), (Bsz, T, H, D))
+    const = oracle.born_attention(q, k, same, tau, lib=lib)
+    assert np.max(np.abs(const - same)) < 1e-13
+    assert np.max(np.abs(base[:, 0] - v[:, 0])) < 1e-14
+
+
 ALL_PINS = [pin_bruteforce, pin_impulse, pin_constant_input, pin_fixed_point,
             pin_phase_unrolled, pin_phase_transport, pin_phase_golden_gain,
+            pin_born_orthogonal_keys, pin_born_two_state_interference,
+            pin_born_density_matrix_form, pin_born_invariances,
             pin_step_n_against_recurrence, pin_step_infinite_against_recurrence,
             pin_backward_finite_differences, pin_backward_without_initial_state,
             pin_step_constant_input, pin_decay_zero, pin_homogeneous, pin_linearity_and_skip,

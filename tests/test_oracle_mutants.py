@@ -81,6 +81,25 @@ MUTANTS = {
     "phase_initial_state_ignored": [
         ("double complex psi = (psi0_re && psi0_im) ? psi0_re[bk] + psi0_im[bk] * I : 0.0;",
          "double complex psi = 0.0;")],
+    "born_overlap_not_conjugated": [
+        ("overlap += conj(q_re[qi + d] + q_im[qi + d] * I) * (k_re[kj + d] + k_im[kj + d] * I);",
+         "overlap += (q_re[qi + d] + q_im[qi + d] * I) * (k_re[kj + d] + k_im[kj + d] * I);")],
+    "born_not_causal": [("for (int64_t j = 0; j <= i; ++j) {\n        const int64_t kj",
+                         "for (int64_t j = 0; j < T; ++j) {\n        const int64_t kj")],
+    "born_diagonal_excluded": [("for (int64_t j = 0; j <= i; ++j) {\n        const int64_t kj",
+                                "for (int64_t j = 0; j < i; ++j) {\n        const int64_t kj")],
+    "born_modulus_not_squared": [("const double sij = mod * mod / ((double)D * t);",
+                                  "const double sij = mod / ((double)D * t);")],
+    "born_real_part_score": [("const double sij = mod * mod / ((double)D * t);",
+                              "const double sij = creal(overlap) * creal(overlap) / ((double)D * t);")],
+    "born_unnormalised": [("const double complex o = den != 0.0 ? num[d] / den : 0.0;",
+                           "const double complex o = num[d];")],
+    "born_value_of_query_row": [("num[d] += sij * (v_re[kj + d] + v_im[kj + d] * I);",
+                                 "num[d] += sij * (v_re[qi + d] + v_im[qi + d] * I);")],
+    "born_value_conjugated": [("num[d] += sij * (v_re[kj + d] + v_im[kj + d] * I);",
+                               "num[d] += sij * (v_re[kj + d] - v_im[kj + d] * I);")],
+    "born_temperature_of_key": [("const double sij = mod * mod / ((double)D * t);",
+                                 "const double sij = mod * mod / ((double)D * (tau ? tau[(b * T + j) * H + h] : 1.0));")],
 }
 
 
