@@ -13,7 +13,8 @@ records around each launch on the launch stream during the timed region.
 Extra figures in the same line: the bf16-input variant of the same workload, the
 backward pass of the same workload, the decode step at batch 256 x 48 heads x
 N128 x D64 over 512 pre-staged tokens, the constant-input calls at that shape,
-the per-coordinate phase-state scan at 256 x 1024 x 16 x 16, and (with --all)
+the per-coordinate phase-state scan at 256 x 1024 x 16 x 16, causal Born
+attention at 256 x 1024 x 16 heads x width 16, and (with --all)
 the long-sequence and phase-associative-memory workloads.  "traffic" figures are
 HBM bytes per launch from committed rocprofv3 counter runs (profiles/traffic.json),
 null once the kernel's sources have changed since.
@@ -45,7 +46,7 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_bwd_tiles": ("k_backward.hip",), "k_bwd_zbound": ("k_backward.hip",),
               "k_bwd_dz": ("k_backward.hip",), "k_bwd_reduce": ("k_backward.hip",),
               "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
-              "k_phase_out": ("k_phase_scan.hip",)}
+              "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",)}
 
 
 # ---------------------------------------------------------------------------
@@ -81,6 +82,13 @@ def phase_scan_hbm_bytes(B, T, H, N):
     """Read phi, u, b (16 bytes) and write psi (8 bytes) per coordinate and step;
     read psi0 and write psiT once."""
     return B * T * H * N * 24 + B * H * N * 16
+
+
+def born_flops(B, T, H, D):
+    """Real flops of causal Born attention: per (query, key <= query) pair the
+    complex overlap (D complex MACs, 8 flops each), its squared modulus (3), the
+    weighted value sum (D real-by-complex MACs, 4 flops each) and the normaliser (1)."""
+    return B * H * (T * (T + 1) // 2) * (12 * D + 4)
 
 
 def chunk_scan_symbol(N, D, C, dtype):
@@ -241,6 +249,32 @@ def time_phase_scan(B, T, H, N, steps, warmup, dev, chunk=0, seed=5):
     ms = e0.elapsed_time(e1) / steps
     kern = {k: v / steps for k, v in prof.ms.items() if prof.launches[k]}
     return ms, kern
+
+
+def time_born(B, T, H, D, steps, warmup, dev, seed=6):
+    """cssd_born_attention over device-drawn inputs with the distributions of
+    cssd_workloads.born_inputs; returns (ms per call, kernel ms per call)."""
+    import torch
+    import complex_valued_state_amd as cssd
+    g = torch.Generator(device=dev).manual_seed(seed)
+    shp = (B, T, H, D)
+    r = math.sqrt(0.5)
+    planes = [torch.randn(shp, generator=g, device=dev) * r for _ in range(6)]
+    tau = 0.5 + 1.5 * torch.rand((B, T, H), generator=g, device=dev)
+    out = (torch.empty(shp, device=dev), torch.empty(shp, device=dev))
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: cssd.cssd_born_attention(*planes, tau, out=out, stream=stream)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    with cssd.profile() as prof:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+    return e0.elapsed_time(e1) / steps, prof.ms["k_born"] / max(1, prof.launches["k_born"])
 
 
 def time_backward(inp, steps, warmup, dev, seed=9):
@@ -477,6 +511,18 @@ def main():
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(pbytes / (pout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes_per_launch": pbytes, "avg_launch_ms": round(pout, 5)}}
+        progress("timing causal Born attention")
+        bb, bt, bhd, bd = 256, 1024, 16, 16
+        bms, bkms = time_born(bb, bt, bhd, bd, max(3, args.steps // 2), 2, dev)
+        bfl = born_flops(bb, bt, bhd, bd)
+        extra["born_attention_B256_T1024_H16_D16_f32"] = {
+            "tokens_per_s": round(bb * bt / (bms * 1e-3), 1), "ms_per_call": round(bms, 5),
+            "roofline": {"bound": "mfma", "kernel": "k_born", "symbol": f"k_born<{bd}>",
+                         "traffic": load_traffic(f"k_born<{bd}>"),
+                         "achieved": round(bfl / (bkms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(bfl / (bkms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": bfl, "avg_launch_ms": round(bkms, 5)}}
         if args.all:
             for name, mk in (("cfg2_long_B1_T16384_H48_N128_C128", wl.config2),
                              ("cfg3_pam_B16_T1024_H12_N128_C64", lambda: wl.config3("re"))):

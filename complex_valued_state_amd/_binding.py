@@ -21,7 +21,7 @@ CSSD_OK, CSSD_ERR_INVALID_ARG, CSSD_ERR_UNSUPPORTED, CSSD_ERR_WORKSPACE, CSSD_ER
 CSSD_F32, CSSD_BF16 = 0, 1
 KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
                 "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz",
-                "k_phase_summary", "k_phase_carry", "k_phase_out")
+                "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born")
 
 _lock = threading.Lock()
 _lib = None
@@ -70,6 +70,8 @@ def load_library(path: Optional[str] = None):
         lib.cssd_phase_scan_workspace_size.argtypes = [_i64] * 5 + [ctypes.POINTER(_sz)]
         lib.cssd_phase_scan.restype = ctypes.c_int
         lib.cssd_phase_scan.argtypes = [_i64] * 5 + [_vp] * 10 + [_vp, _sz, _vp]
+        lib.cssd_born_attention.restype = ctypes.c_int
+        lib.cssd_born_attention.argtypes = [_i64] * 4 + [_i32] + [_vp] * 7 + [_vp] * 2 + [_vp]
         lib.cssd_profile_enable.restype = ctypes.c_int
         lib.cssd_profile_enable.argtypes = [ctypes.c_int]
         lib.cssd_profile_read.restype = ctypes.c_int
@@ -399,6 +401,35 @@ def cssd_phase_scan(phi, u, b_re, b_im, psi0=None, *, chunk: int = 0, return_sta
     if st != CSSD_OK:
         raise CSSDError(st, "cssd_phase_scan")
     return psi_re, psi_im, psiT_re, psiT_im
+
+
+def cssd_born_attention(q_re, q_im, k_re, k_im, v_re, v_im, tau=None, *, out=None, stream=None):
+    """Causal Born attention (see include/cssd.h): psi_i = sum_{j<=i} s_ij v_j /
+    sum_{j<=i} s_ij with s_ij = |<q_i|k_j>|^2 / (D tau_i).
+
+    q_*, k_*, v_*: (B,T,H,D) float32; tau: (B,T,H) float32 or None.
+    out: optional (out_re, out_im).  Returns (out_re, out_im), each (B,T,H,D)."""
+    torch = _torch()
+    lib = load_library()
+    dev = q_re.device
+    Bsz, T, H, D = q_re.shape
+    f32 = (torch.float32,)
+    p = {}
+    for name, t in (("q_re", q_re), ("q_im", q_im), ("k_re", k_re), ("k_im", k_im),
+                    ("v_re", v_re), ("v_im", v_im)):
+        p[name] = _check(t, name, (Bsz, T, H, D), f32, dev)
+    p["tau"] = None if tau is None else _check(tau, "tau", (Bsz, T, H), f32, dev)
+    if out is None:
+        out = (torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev),
+               torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev))
+    p["out_re"] = _check(out[0], "out_re", (Bsz, T, H, D), f32, dev)
+    p["out_im"] = _check(out[1], "out_im", (Bsz, T, H, D), f32, dev)
+    st = lib.cssd_born_attention(Bsz, T, H, D, CSSD_F32, p["q_re"], p["q_im"], p["k_re"],
+                                 p["k_im"], p["v_re"], p["v_im"], p["tau"], p["out_re"],
+                                 p["out_im"], _stream_ptr(stream, dev))
+    if st != CSSD_OK:
+        raise CSSDError(st, "cssd_born_attention")
+    return out[0], out[1]
 
 
 class profile:

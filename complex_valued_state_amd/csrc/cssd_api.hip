@@ -572,6 +572,49 @@ int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstat
     return CSSD_OK;
 }
 
+int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int32_t in_dtype, const void* q_re, const void* q_im, const void* k_re,
+                        const void* k_im, const void* v_re, const void* v_im, const float* tau,
+                        float* out_re, float* out_im, void* stream) {
+    if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0) return CSSD_ERR_INVALID_ARG;
+    if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
+    if (in_dtype != CSSD_F32) return CSSD_ERR_UNSUPPORTED;
+    if (headdim != 16 && headdim != 32 && headdim != 64) return CSSD_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 31, lim40 = (int64_t)1 << 40;
+    if (batch > lim || seqlen > lim || nheads > lim || batch * nheads > lim / 64 ||
+        batch * nheads * seqlen > lim40 / headdim)
+        return CSSD_ERR_UNSUPPORTED;
+    const void* req[] = {q_re, q_im, k_re, k_im, v_re, v_im, out_re, out_im};
+    for (const void* p : req)
+        if (p == nullptr || !aligned(p, 16)) return CSSD_ERR_INVALID_ARG;
+    if (!aligned(tau, 4)) return CSSD_ERR_INVALID_ARG;
+    const void* ins[] = {q_re, q_im, k_re, k_im, v_re, v_im, tau};
+    for (const void* i : ins)
+        if (i == out_re || i == out_im) return CSSD_ERR_INVALID_ARG;
+    if (out_re == out_im) return CSSD_ERR_INVALID_ARG;
+    cssd::BornArgs a;
+    a.B = batch;
+    a.T = seqlen;
+    a.H = nheads;
+    a.D = headdim;
+    a.nqb = (seqlen + 63) / 64;
+    a.npair = (a.nqb + 1) / 2;
+    a.hpl = headdim >= 32 ? 1 : 32 / headdim;
+    a.q_re = static_cast<const float*>(q_re);
+    a.q_im = static_cast<const float*>(q_im);
+    a.k_re = static_cast<const float*>(k_re);
+    a.k_im = static_cast<const float*>(k_im);
+    a.v_re = static_cast<const float*>(v_re);
+    a.v_im = static_cast<const float*>(v_im);
+    a.tau = tau;
+    a.out_re = out_re;
+    a.out_im = out_im;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (timed(cssd::K_BORN, s, [&] { return cssd::launch_born(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    return CSSD_OK;
+}
+
 int cssd_profile_enable(int on) {
     Profiler& p = prof();
     std::lock_guard<std::mutex> g(p.mu);
@@ -611,7 +654,7 @@ const char* cssd_kernel_name(int kernel_id) {
     static const char* names[cssd::K_COUNT] = {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
         "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz",
-        "k_phase_summary", "k_phase_carry", "k_phase_out"};
+        "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

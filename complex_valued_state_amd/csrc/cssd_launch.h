@@ -8,7 +8,8 @@ namespace cssd {
 
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
                 K_STEP_INFINITE = 5, K_BWD_DXDB = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
-                K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_COUNT = 12 };
+                K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_BORN = 12,
+                K_COUNT = 13 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -56,6 +57,15 @@ struct PhaseArgs {
     float *p_re, *p_im, *s_re, *s_im, *in_re, *in_im;
 };
 
+// Causal Born attention over (B, T, H, D) planar q, k, v.  nqb query blocks of
+// 64 rows per (b, h), taken in npair workgroups (blocks p and nqb - 1 - p);
+// hpl heads share one 128-byte line of a time step and go to the same XCD.
+struct BornArgs {
+    int64_t B, T, H, D, nqb, npair, hpl;
+    const float *q_re, *q_im, *k_re, *k_im, *v_re, *v_im, *tau;  // tau may be NULL
+    float *out_re, *out_im;
+};
+
 // Number of compute units of the current device (queried once per device).
 hipError_t device_cu_count(int* cus);
 
@@ -77,5 +87,6 @@ hipError_t launch_step_infinite(const StepArgs& a, hipStream_t stream);
 hipError_t launch_phase_summary(const PhaseArgs& a, hipStream_t stream);
 hipError_t launch_phase_carry(const PhaseArgs& a, hipStream_t stream);
 hipError_t launch_phase_out(const PhaseArgs& a, hipStream_t stream);
+hipError_t launch_born(const BornArgs& a, hipStream_t stream);
 
 }  // namespace cssd

@@ -32,11 +32,13 @@
  *    status before anything is enqueued, and the library never reads device
  *    memory from the host.  Launch failures return CSSD_ERR_HIP.  No C++
  *    exception crosses this boundary.
- *  - Supported sizes: headdim D and dstate N in {16, 32, 64, 128}; chunk in
+ *  - Supported sizes of the scan entry points (cssd_forward, cssd_backward,
+ *    cssd_step*): headdim D and dstate N in {16, 32, 64, 128}; chunk in
  *    {16, 32, 64, 128}; any seqlen >= 1 (a partial last chunk is masked inside
  *    the kernels, nothing is padded in memory); batch, nheads >= 1, with
- *    batch*seqlen*nheads*max(D,N) < 2^31 elements per plane.  Other sizes
- *    return CSSD_ERR_UNSUPPORTED.  There is one kernel path and no fallback.
+ *    batch*seqlen*nheads*max(D,N) < 2^31 elements per plane.  The phase scan
+ *    and Born attention state their own limits.  Other sizes return
+ *    CSSD_ERR_UNSUPPORTED.  There is one kernel path and no fallback.
  *  - Outputs must not alias inputs (except the decode state, updated in place).
  *  - The library keeps no per-call state and is safe to call from several host
  *    threads on different streams.  The optional profiler (cssd_profile_*)
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 103 /* major*100 + minor */
+#define CSSD_VERSION 104 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
@@ -311,6 +313,34 @@ int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstat
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Causal Born attention of the phase-state paper ("Complex Phase-State Dynamics
+ * Reduce the Optimization Steps of Sequence Models", section 5.5, eq. 5, and
+ * Appendix A, Algorithm 3), for every (batch, head):
+ *     s_ij  = |<q_i|k_j>|^2 / (D tau_i)   for j <= i,  <q|k> = sum_d conj(q_d) k_d
+ *     psi_i = (sum_{j<=i} s_ij v_j) / (sum_{j<=i} s_ij)
+ * a causal average of the values weighted by the squared modulus of the complex
+ * overlap (no softmax).  Accumulation is fp32 throughout.
+ * Arguments (device pointers, planar complex, row-major):
+ *   q_*, k_*, v_*   [B,T,H,D] queries, keys, values (float32; in_dtype must be
+ *                   CSSD_F32, CSSD_BF16 returns CSSD_ERR_UNSUPPORTED)
+ *   tau             [B,T,H] float32 temperatures, or NULL (all 1).  tau_i and D
+ *                   scale every score of row i alike and so cancel in the
+ *                   normalisation; they change only rounding.
+ *   out_re, out_im  [B,T,H,D] float32 psi (written)
+ * Supported: headdim D in {16, 32, 64}; any seqlen >= 1; batch*nheads*seqlen*D
+ * < 2^40.  A row whose scores are all zero (its query orthogonal to every key
+ * up to it, e.g. a zero query) is returned as zero.  Alignment: q, k, v, out
+ * 16 bytes, tau 4.  Outputs may not alias inputs or each other.
+ */
+int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int32_t in_dtype,
+                        const void *q_re, const void *q_im,
+                        const void *k_re, const void *k_im,
+                        const void *v_re, const void *v_im,
+                        const float *tau,
+                        float *out_re, float *out_im, void *stream);
+
+/*
  * Optional per-kernel timing (a measurement aid, not part of the operation).
  * While enabled, every kernel launch of every entry point is bracketed by
  * two hipEvents recorded on the caller's stream.  cssd_profile_read waits for
@@ -321,7 +351,7 @@ int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstat
  * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite,
  * 6 bwd_dxdb, 7 bwd_dc, 8 bwd_dz (cssd_backward also runs ids 0-2, and 1 and 2
  * a second time in their adjoint modes), 9 phase_summary, 10 phase_carry,
- * 11 phase_out (cssd_phase_scan).
+ * 11 phase_out (cssd_phase_scan), 12 born (cssd_born_attention).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).
  */

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("cssd_forward", "cssd_backward", "cssd_backward_workspace_size",
                      "cssd_step", "cssd_step_n", "cssd_step_infinite", "cssd_phase_scan",
-                     "cssd_phase_scan_workspace_size",
+                     "cssd_phase_scan_workspace_size", "cssd_born_attention",
                      "cssd_forward_workspace_size", "cssd_status_string", "cssd_version"):
         assert required in names
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 103
+    assert lib.cssd_version() == 104
     for st in range(5):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -227,12 +227,36 @@ def test_phase_scan_validation(lib):
     assert call(w=ws + 64) == 3
 
 
+def test_born_attention_validation(lib):
+    base = 0x10000000
+    p = [base + 0x100000 * i for i in range(10)]
+    ins, tau, out = p[:6], p[6], p[7:9]
+    call = lambda shape=(2, 100, 3, 16), dt=0, ins=ins, tau=tau, out=out: \
+        lib.cssd_born_attention(*shape, dt, *ins, tau, *out, None)
+    assert call(shape=(0, 100, 3, 16)) == 1
+    assert call(shape=(2, 0, 3, 16)) == 1
+    assert call(shape=(2, 100, 3, 24)) == 2                  # D not supported
+    assert call(shape=(2, 100, 3, 128)) == 2
+    assert call(dt=1) == 2                                   # bf16 inputs not yet
+    assert call(dt=7) == 1
+    bad = list(ins); bad[3] = None                           # k_im missing
+    assert call(ins=bad) == 1
+    bad = list(ins); bad[0] += 4                             # q_re misaligned
+    assert call(ins=bad) == 1
+    assert call(tau=tau + 2) == 1                            # tau misaligned
+    assert call(out=[ins[4], out[1]]) == 1                   # out aliases v
+    assert call(out=[out[0], tau]) == 1                      # out aliases tau
+    assert call(out=[out[0], out[0]]) == 1
+    assert call(out=[None, out[1]]) == 1
+
+
 def test_profiler_without_launches(lib):
     import complex_valued_state_amd as cssd
     with cssd.profile() as prof:
         pass
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
-    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(12) is None
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(13) is None
+    assert lib.cssd_kernel_name(12) == b"k_born"
     assert lib.cssd_kernel_name(5) == b"k_step_infinite"
     assert lib.cssd_kernel_name(11) == b"k_phase_out"

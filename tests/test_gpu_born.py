@@ -1,0 +1,118 @@
+"""GPU parity of cssd_born_attention, the causal Born attention, against the
+oracle's row-by-row fp64 evaluation of eq. 5 (needs an MI355X)."""
+import math
+
+import numpy as np
+import pytest
+
+import cssd_workloads as wl
+import oracle
+from gpu_util import log, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+
+
+def _c(r, i):
+    return r.double().cpu().numpy() + 1j * i.double().cpu().numpy()
+
+
+def _run(p, with_tau=True):
+    import torch
+    import complex_valued_state_amd as cssd
+    o = cssd.cssd_born_attention(_dev(p.q_re), _dev(p.q_im), _dev(p.k_re), _dev(p.k_im),
+                                 _dev(p.v_re), _dev(p.v_im), _dev(p.tau) if with_tau else None)
+    torch.cuda.synchronize()
+    return _c(*o)
+
+
+@pytest.mark.parametrize("B,T,H,D", [
+    (1, 1, 1, 16),        # one row: psi_0 = v_0
+    (2, 64, 3, 16),       # exactly one block
+    (2, 100, 3, 16),      # ragged second block
+    (3, 257, 5, 16),      # five query blocks: pairs (0,4), (1,3) and the middle block alone
+    (1, 200, 2, 32),
+    (1, 130, 2, 64),
+    (2, 513, 1, 32),      # odd head count: lines shared across a batch boundary
+])
+def test_born_vs_oracle(B, T, H, D):
+    log(f"  born B{B} T{T} H{H} D{D}")
+    p = wl.born_inputs(90 + T, B, T, H, D)
+    got = _run(p)
+    q, k, v, tau = p.complex()
+    want = oracle.born_attention(q, k, v, tau)
+    assert rel_err(got, want) <= TOL, rel_err(got, want)
+
+
+def test_born_without_temperature():
+    p = wl.born_inputs(91, 2, 150, 2, 16)
+    got = _run(p, with_tau=False)
+    q, k, v, _ = p.complex()
+    want = oracle.born_attention(q, k, v, None)
+    assert rel_err(got, want) <= TOL
+    # the temperature cancels: with and without it agree to rounding
+    assert rel_err(_run(p), got) <= TOL
+
+
+def test_born_orthogonal_keys_retrieve_values():
+    """Orthonormal DFT keys, each query a multiple of one earlier key: the output
+    is that key's value (lossless retrieval), to fp32 rounding."""
+    B, H, D = 2, 3, 16
+    T = 3 * D
+    rng = np.random.default_rng(92)
+    n = np.arange(D)
+    K = np.exp(2j * np.pi * np.outer(n, n) / D) / math.sqrt(D)
+    keys = np.tile(K, (T // D, 1))                         # key t is DFT row t mod D
+    pick = np.array([[[rng.integers(max(0, i - D + 1), i + 1) for _ in range(H)]
+                      for i in range(T)] for _ in range(B)])
+    q = keys[pick] * (1.0 + rng.random((B, T, H, 1)))
+    k = np.broadcast_to(keys[None, :, None, :], (B, T, H, D))
+    v = rng.standard_normal((B, T, H, D)) + 1j * rng.standard_normal((B, T, H, D))
+    p = wl.BornInputs(q.real.astype(np.float32), q.imag.astype(np.float32),
+                      k.real.astype(np.float32), k.imag.astype(np.float32),
+                      v.real.astype(np.float32), v.imag.astype(np.float32),
+                      np.ones((B, T, H), dtype=np.float32))
+    got = _run(p)
+    want = np.take_along_axis(v, pick[..., None], axis=1)
+    # within the last D keys only the picked one overlaps; earlier copies of the
+    # same DFT row also overlap, so compare with the oracle and check retrieval
+    # on the first D rows where every key is distinct
+    qo, ko, vo, to = p.complex()
+    assert rel_err(got, oracle.born_attention(qo, ko, vo, to)) <= TOL
+    assert np.max(np.abs(got[:, :D] - want[:, :D])) <= 1e-4
+
+
+def test_born_zero_query_rows_are_zero():
+    """A zero query scores 0 against every key; the row is returned as zero."""
+    p = wl.born_inputs(93, 1, 80, 2, 16)
+    p.q_re[:, 5::7] = 0.0
+    p.q_im[:, 5::7] = 0.0
+    got = _run(p)
+    q, k, v, tau = p.complex()
+    want = oracle.born_attention(q, k, v, tau)
+    assert np.all(got[:, 5::7] == 0)
+    assert rel_err(got, want) <= TOL
+
+
+def test_born_layer_shape_sampled_rows():
+    """The H-Transformer layer shape of the phase-state paper per GPU (256
+    sequences of 1024 steps, 16 heads of width 16): the whole output against the
+    oracle on sampled rows (first and last rows, block edges, random rows)."""
+    B, T, H, D = 256, 1024, 16, 16
+    log(f"  born layer shape B{B} T{T} H{H} D{D}")
+    p = wl.born_inputs(1, B, T, H, D)
+    got = _run(p)
+    rng = np.random.default_rng(94)
+    ts = np.concatenate([[0, 1, 63, 64, 65, 511, 512, 1022, 1023], rng.integers(0, T, 400)])
+    rows = np.stack([rng.integers(0, B, ts.size), ts, rng.integers(0, H, ts.size)], axis=1)
+    want = oracle.born_attention_rows((p.q_re, p.q_im), (p.k_re, p.k_im), (p.v_re, p.v_im),
+                                      p.tau, rows)
+    sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert rel_err(sel, want) <= TOL, rel_err(sel, want)
+    assert np.all(np.isfinite(got))
