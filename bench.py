@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "complex SSD fwd tokens/s at B8 T2048 H48; % of MFMA/HBM roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 # source files that make up each kernel (besides the shared device/launch headers),
 # by the kernel's name stem as rocprofv3 reports it
 _SCAN_SRC = ("k_chunk_scan.h", "k_chunk_scan_lds.h", "k_chunk_scan.hip", "k_chunk_scan_c16.hip",
@@ -46,7 +47,8 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_bwd_tiles": ("k_backward.hip",), "k_bwd_zbound": ("k_backward.hip",),
               "k_bwd_dz": ("k_backward.hip",), "k_bwd_reduce": ("k_backward.hip",),
               "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
-              "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",)}
+              "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",),
+              "k_born_bf16": ("k_born.hip",)}
 
 
 # ---------------------------------------------------------------------------
@@ -251,15 +253,18 @@ def time_phase_scan(B, T, H, N, steps, warmup, dev, chunk=0, seed=5):
     return ms, kern
 
 
-def time_born(B, T, H, D, steps, warmup, dev, seed=6):
+def time_born(B, T, H, D, steps, warmup, dev, seed=6, bf16=False):
     """cssd_born_attention over device-drawn inputs with the distributions of
-    cssd_workloads.born_inputs; returns (ms per call, kernel ms per call)."""
+    cssd_workloads.born_inputs (q, k, v in bf16 when `bf16`); returns (ms per
+    call, kernel ms per call)."""
     import torch
     import complex_valued_state_amd as cssd
     g = torch.Generator(device=dev).manual_seed(seed)
     shp = (B, T, H, D)
     r = math.sqrt(0.5)
     planes = [torch.randn(shp, generator=g, device=dev) * r for _ in range(6)]
+    if bf16:
+        planes = [t.to(torch.bfloat16) for t in planes]
     tau = 0.5 + 1.5 * torch.rand((B, T, H), generator=g, device=dev)
     out = (torch.empty(shp, device=dev), torch.empty(shp, device=dev))
     stream = torch.cuda.current_stream(dev)
@@ -523,6 +528,16 @@ def main():
                          "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(bfl / (bkms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
                          "algorithmic_flops_per_launch": bfl, "avg_launch_ms": round(bkms, 5)}}
+        progress("timing causal Born attention with bf16 inputs")
+        b16ms, b16kms = time_born(bb, bt, bhd, bd, max(3, args.steps // 2), 2, dev, bf16=True)
+        extra["born_attention_B256_T1024_H16_D16_bf16_inputs"] = {
+            "tokens_per_s": round(bb * bt / (b16ms * 1e-3), 1), "ms_per_call": round(b16ms, 5),
+            "roofline": {"bound": "mfma", "kernel": "k_born_bf16", "symbol": f"k_born_bf16<{bd}>",
+                         "traffic": load_traffic(f"k_born_bf16<{bd}>"),
+                         "achieved": round(bfl / (b16kms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(bfl / (b16kms * 1e-3) / 1e12 / PEAK_BF16_MFMA_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": bfl, "avg_launch_ms": round(b16kms, 5)}}
         if args.all:
             for name, mk in (("cfg2_long_B1_T16384_H48_N128_C128", wl.config2),
                              ("cfg3_pam_B16_T1024_H12_N128_C64", lambda: wl.config3("re"))):

@@ -407,24 +407,31 @@ def cssd_born_attention(q_re, q_im, k_re, k_im, v_re, v_im, tau=None, *, out=Non
     """Causal Born attention (see include/cssd.h): psi_i = sum_{j<=i} s_ij v_j /
     sum_{j<=i} s_ij with s_ij = |<q_i|k_j>|^2 / (D tau_i).
 
-    q_*, k_*, v_*: (B,T,H,D) float32; tau: (B,T,H) float32 or None.
-    out: optional (out_re, out_im).  Returns (out_re, out_im), each (B,T,H,D)."""
+    q_*, k_*, v_*: (B,T,H,D), all float32 or all bfloat16 (the bf16-input kernel);
+    tau: (B,T,H) float32 or None.  out: optional (out_re, out_im) float32.
+    Returns (out_re, out_im), each (B,T,H,D) float32."""
     torch = _torch()
     lib = load_library()
     dev = q_re.device
     Bsz, T, H, D = q_re.shape
+    if q_re.dtype == torch.float32:
+        code, okd = CSSD_F32, (torch.float32,)
+    elif q_re.dtype == torch.bfloat16:
+        code, okd = CSSD_BF16, (torch.bfloat16,)
+    else:
+        raise TypeError("q/k/v planes must be float32 or bfloat16")
     f32 = (torch.float32,)
     p = {}
     for name, t in (("q_re", q_re), ("q_im", q_im), ("k_re", k_re), ("k_im", k_im),
                     ("v_re", v_re), ("v_im", v_im)):
-        p[name] = _check(t, name, (Bsz, T, H, D), f32, dev)
+        p[name] = _check(t, name, (Bsz, T, H, D), okd, dev)
     p["tau"] = None if tau is None else _check(tau, "tau", (Bsz, T, H), f32, dev)
     if out is None:
         out = (torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev),
                torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev))
     p["out_re"] = _check(out[0], "out_re", (Bsz, T, H, D), f32, dev)
     p["out_im"] = _check(out[1], "out_im", (Bsz, T, H, D), f32, dev)
-    st = lib.cssd_born_attention(Bsz, T, H, D, CSSD_F32, p["q_re"], p["q_im"], p["k_re"],
+    st = lib.cssd_born_attention(Bsz, T, H, D, code, p["q_re"], p["q_im"], p["k_re"],
                                  p["k_im"], p["v_re"], p["v_im"], p["tau"], p["out_re"],
                                  p["out_im"], _stream_ptr(stream, dev))
     if st != CSSD_OK:

@@ -28,9 +28,16 @@ CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Extra flags per source.  The attention kernels keep their matrix-core
+# accumulators in ordinary VGPRs (measured faster: no copies between the
+# accumulation and vector registers); the same option crashes the compiler on
+# the gradient kernels, so it is not global.
+FILE_FLAGS = {"k_born.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -578,7 +578,6 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
                         float* out_re, float* out_im, void* stream) {
     if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0) return CSSD_ERR_INVALID_ARG;
     if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
-    if (in_dtype != CSSD_F32) return CSSD_ERR_UNSUPPORTED;
     if (headdim != 16 && headdim != 32 && headdim != 64) return CSSD_ERR_UNSUPPORTED;
     const int64_t lim = (int64_t)1 << 31, lim40 = (int64_t)1 << 40;
     if (batch > lim || seqlen > lim || nheads > lim || batch * nheads > lim / 64 ||
@@ -599,7 +598,10 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
     a.D = headdim;
     a.nqb = (seqlen + 63) / 64;
     a.npair = (a.nqb + 1) / 2;
-    a.hpl = headdim >= 32 ? 1 : 32 / headdim;
+    // heads sharing one 128-byte line of a time step go to the same XCD
+    const int64_t row_bytes = headdim * (in_dtype == CSSD_F32 ? 4 : 2);
+    a.hpl = row_bytes >= 128 ? 1 : 128 / row_bytes;
+    a.in_dtype = in_dtype;
     a.q_re = static_cast<const float*>(q_re);
     a.q_im = static_cast<const float*>(q_im);
     a.k_re = static_cast<const float*>(k_re);

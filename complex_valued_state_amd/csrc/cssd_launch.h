@@ -62,6 +62,7 @@ struct PhaseArgs {
 // hpl heads share one 128-byte line of a time step and go to the same XCD.
 struct BornArgs {
     int64_t B, T, H, D, nqb, npair, hpl;
+    int in_dtype;  // 0: q, k, v float32; 1: bfloat16 bit patterns (read through the float pointers)
     const float *q_re, *q_im, *k_re, *k_im, *v_re, *v_im, *tau;  // tau may be NULL
     float *out_re, *out_im;
 };

@@ -204,10 +204,245 @@ __global__ __launch_bounds__(256) void k_born(BornArgs a) {
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 inputs (the page trains this attention in half precision with fp32
+// accumulation): the same decomposition on v_mfma_f32_16x16x32_bf16, which
+// takes A[i][k] from lane i + 16 (k / 8), slot k % 8, B[k][j] from lane
+// j + 16 (k / 8), slot k % 8, and leaves D[4g + r][j] in register r of lane
+// j + 16g.
+//  * Overlap: MFMA step m covers features d in [16m, 16m + 16); lane group g
+//    holds d in [16m + 4g, 16m + 4g + 4) of the real plane in slots 0-3 and of
+//    the imaginary plane in slots 4-7.  Key rows sit in LDS in exactly that
+//    order (real quad, imaginary quad, next quad ...), and a second time with
+//    each pair of quads swapped, so one 16-byte read is the A operand of the
+//    real part and one more that of the imaginary part.
+//  * Weighted sum: the 32-key step s pairs key tiles 2s and 2s + 1: slot j < 4
+//    is key 32s + 4g + j, slot j >= 4 is key 32s + 16 + 4g + j - 4, which is
+//    where the score tiles leave them, so the scores are packed to bf16 in
+//    place.  Values sit in LDS transposed ([column][key]), so the B operand is
+//    two 8-byte reads.  The normaliser sums the rounded weights (one more
+//    product, against a column of ones), so the output is an exact convex
+//    combination of the values with those weights.
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ bf16x4 bf4_of_bits(uint2 v) { return __builtin_bit_cast(bf16x4, v); }
+__device__ __forceinline__ float bf_to_f(__bf16 v) {
+    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, v) << 16);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
+    constexpr int NM = D / 16;          // MFMA steps over the features (per part)
+    constexpr int KS = 4 * D + 16;      // LDS key row stride (bytes): D/4 quads of 16 B, padded
+    constexpr int VS = 2 * kBornBlock + 16;  // LDS value column stride (bytes): 64 keys, padded
+    constexpr int NCT = 2 * D / 16;     // 16-column tiles of [vr | vi]
+    constexpr int KQ = kBornBlock * D / 4 / 256;   // key quads staged per thread
+    constexpr int VQ = kBornBlock * 2 * D / 8 / 256;  // 8-value chunks of V staged per thread
+    // key rows twice: quads [re, im] (A of the real part) and [im, re] (A of the imaginary part)
+    __shared__ __align__(16) unsigned char lds_k[2][2][kBornBlock * KS];
+    __shared__ __align__(16) unsigned char lds_v[2][2 * D * VS];
+
+    int64_t bh, pair;
+    if (!born_item(a, blockIdx.x, bh, pair)) return;  // workgroup-uniform
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int64_t rs = a.H * D;
+    const int64_t base = (b * a.T * a.H + h) * D;
+    const uint16_t* qr_p = reinterpret_cast<const uint16_t*>(a.q_re);
+    const uint16_t* qi_p = reinterpret_cast<const uint16_t*>(a.q_im);
+    const uint16_t* kr_p = reinterpret_cast<const uint16_t*>(a.k_re);
+    const uint16_t* ki_p = reinterpret_cast<const uint16_t*>(a.k_im);
+    const uint16_t* vr_p = reinterpret_cast<const uint16_t*>(a.v_re);
+    const uint16_t* vi_p = reinterpret_cast<const uint16_t*>(a.v_im);
+
+    const int nblk = pair == a.nqb - 1 - pair ? 1 : 2;
+    for (int which = 0; which < nblk; ++which) {
+        const int64_t qb = which == 0 ? pair : a.nqb - 1 - pair;
+        const int64_t qrow = qb * kBornBlock + 16 * w + lr;
+        // B operands: [qr quad, qi quad] and [-qr quad, qi quad], scaled by 1/sqrt(D tau)
+        bf16x8 bre[NM], bim[NM];
+        {
+            float scale = 0.f;
+            int64_t o = 0;
+            if (qrow < a.T) {
+                o = base + qrow * rs;
+                const float tq = a.tau != nullptr ? a.tau[(b * a.T + qrow) * a.H + h] : 1.f;
+                scale = rsqrtf((float)D * tq);
+            }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                bf16x4 r4 = {}, i4 = {};
+                if (qrow < a.T) {
+                    r4 = bf4_of_bits(*reinterpret_cast<const uint2*>(qr_p + o + 16 * m + 4 * lg));
+                    i4 = bf4_of_bits(*reinterpret_cast<const uint2*>(qi_p + o + 16 * m + 4 * lg));
+                }
+                bf16x4 sr, si, nr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float fr = bf_to_f(r4[j]) * scale, fi = bf_to_f(i4[j]) * scale;
+                    sr[j] = (__bf16)fr;
+                    si[j] = (__bf16)fi;
+                    nr[j] = (__bf16)(-fr);
+                }
+                bre[m] = cat8(sr, si);
+                bim[m] = cat8(nr, si);
+            }
+        }
+        floatx4 o[NCT];
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) o[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // row sums of the rounded weights, as one more product with a column of ones:
+        // register r of lane j + 16g ends up with the sum for query 4g + r
+        floatx4 den4 = {0.f, 0.f, 0.f, 0.f};
+        const __bf16 one = (__bf16)1.0f;
+        const bf16x8 ones = {one, one, one, one, one, one, one, one};
+
+        // staging registers: KQ key quads (real 8 B + imaginary 8 B) and VQ value chunks (16 B)
+        uint2 skr[KQ], ski[KQ];
+        uint4 sv[VQ];
+        auto fetch = [&](int64_t kb) {
+#pragma unroll
+            for (int i = 0; i < KQ; ++i) {
+                const int idx = i * 256 + tid, row = idx / (D / 4), q = idx % (D / 4);
+                const int64_t key = kb * kBornBlock + row;
+                if (key < a.T) {
+                    skr[i] = *reinterpret_cast<const uint2*>(kr_p + base + key * rs + 4 * q);
+                    ski[i] = *reinterpret_cast<const uint2*>(ki_p + base + key * rs + 4 * q);
+                } else {
+                    skr[i] = make_uint2(0u, 0u);
+                    ski[i] = make_uint2(0u, 0u);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < VQ; ++i) {
+                // chunk idx: plane (re, im), key row, 8 consecutive columns
+                const int idx = i * 256 + tid;
+                const int pl = idx / (kBornBlock * D / 8), rem = idx % (kBornBlock * D / 8);
+                const int row = rem / (D / 8), c8 = rem % (D / 8);
+                const int64_t key = kb * kBornBlock + row;
+                const uint16_t* src = pl == 0 ? vr_p : vi_p;
+                sv[i] = key < a.T ? *reinterpret_cast<const uint4*>(src + base + key * rs + 8 * c8)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+            }
+        };
+        auto commit = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < KQ; ++i) {
+                const int idx = i * 256 + tid, row = idx / (D / 4), q = idx % (D / 4);
+                *reinterpret_cast<uint4*>(&lds_k[buf][0][row * KS + 16 * q]) =
+                    make_uint4(skr[i].x, skr[i].y, ski[i].x, ski[i].y);
+                *reinterpret_cast<uint4*>(&lds_k[buf][1][row * KS + 16 * q]) =
+                    make_uint4(ski[i].x, ski[i].y, skr[i].x, skr[i].y);
+            }
+#pragma unroll
+            for (int i = 0; i < VQ; ++i) {
+                const int idx = i * 256 + tid;
+                const int pl = idx / (kBornBlock * D / 8), rem = idx % (kBornBlock * D / 8);
+                const int row = rem / (D / 8), c8 = rem % (D / 8);
+                const uint32_t wv[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int col = pl * D + 8 * c8 + j;
+                    *reinterpret_cast<uint16_t*>(&lds_v[buf][col * VS + 2 * row]) =
+                        (uint16_t)(j % 2 == 0 ? wv[j / 2] & 0xffffu : wv[j / 2] >> 16);
+                }
+            }
+        };
+
+        fetch(0);
+        __syncthreads();
+        commit(0);
+        __syncthreads();
+        for (int64_t kb = 0; kb <= qb; ++kb) {
+            const int buf = kb & 1;
+            if (kb < qb) fetch(kb + 1);
+            const bool diag = kb == qb;
+            const int ntile = diag ? w + 1 : 4;
+            // score tiles: key 16t + 4g + r of query lr in register r
+            floatx4 sc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                sc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (t >= ntile) continue;  // wave-uniform
+                floatx4 sre = {0.f, 0.f, 0.f, 0.f}, sim = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    const int ko = (16 * t + lr) * KS + 16 * (4 * m + lg);
+                    const bf16x8 are = *reinterpret_cast<const bf16x8*>(&lds_k[buf][0][ko]);
+                    const bf16x8 aim = *reinterpret_cast<const bf16x8*>(&lds_k[buf][1][ko]);
+                    sre = __builtin_amdgcn_mfma_f32_16x16x32_bf16(are, bre[m], sre, 0, 0, 0);
+                    sim = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aim, bim[m], sim, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = sre[r] * sre[r] + sim[r] * sim[r];
+                    if (diag && 16 * t + 4 * lg + r > 16 * w + lr) v = 0.f;
+                    sc[t][r] = v;
+                }
+            }
+            // O += P . [vr | vi] over the 32-key steps (tiles 2s, 2s + 1)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (2 * s2 >= ntile) continue;  // wave-uniform
+                bf16x8 pa;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pa[j] = (__bf16)sc[2 * s2][j];
+                    pa[j + 4] = (__bf16)sc[2 * s2 + 1][j];
+                }
+                den4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, den4, 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    const int col = 16 * c + lr;
+                    const unsigned char* vrow = &lds_v[buf][col * VS];
+                    const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * s2 + 4 * lg));
+                    const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * s2 + 16 + 4 * lg));
+                    const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
+                }
+            }
+            if (kb < qb) commit(buf ^ 1);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int qloc = 4 * lg + r;
+            const float den = den4[r];
+            const int64_t row = qb * kBornBlock + 16 * w + qloc;
+            if (row >= a.T) continue;
+            const float inv = den != 0.f ? 1.f / den : 0.f;
+            const int64_t at = base + row * rs;
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) {
+                float* dst = (16 * c) < D ? a.out_re : a.out_im;
+                dst[at + (16 * c) % D + lr] = o[c][r] * inv;
+            }
+        }
+    }
+}
+
 hipError_t launch_born(const BornArgs& a, hipStream_t s) {
     const int64_t groups = (a.B * a.H + a.hpl - 1) / a.hpl;
     const int64_t per_xcd = (groups + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(kXcds * per_xcd * a.hpl * a.npair)), block(256);
+    if (a.in_dtype == 1) {
+        switch (a.D) {
+            case 16: hipLaunchKernelGGL(k_born_bf16<16>, grid, block, 0, s, a); break;
+            case 32: hipLaunchKernelGGL(k_born_bf16<32>, grid, block, 0, s, a); break;
+            case 64: hipLaunchKernelGGL(k_born_bf16<64>, grid, block, 0, s, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (a.D) {
         case 16: hipLaunchKernelGGL(k_born<16>, grid, block, 0, s, a); break;
         case 32: hipLaunchKernelGGL(k_born<32>, grid, block, 0, s, a); break;

@@ -321,8 +321,11 @@ int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstat
  * a causal average of the values weighted by the squared modulus of the complex
  * overlap (no softmax).  Accumulation is fp32 throughout.
  * Arguments (device pointers, planar complex, row-major):
- *   q_*, k_*, v_*   [B,T,H,D] queries, keys, values (float32; in_dtype must be
- *                   CSSD_F32, CSSD_BF16 returns CSSD_ERR_UNSUPPORTED)
+ *   q_*, k_*, v_*   [B,T,H,D] queries, keys, values: float32 (CSSD_F32) or
+ *                   bfloat16 bit patterns (CSSD_BF16; the page's half-precision
+ *                   setting: products on the bf16 matrix cores, accumulation in
+ *                   fp32, the weights rounded to bf16 before they multiply the
+ *                   values and the normaliser summing those rounded weights)
  *   tau             [B,T,H] float32 temperatures, or NULL (all 1).  tau_i and D
  *                   scale every score of row i alike and so cancel in the
  *                   normalisation; they change only rounding.
@@ -330,7 +333,9 @@ int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstat
  * Supported: headdim D in {16, 32, 64}; any seqlen >= 1; batch*nheads*seqlen*D
  * < 2^40.  A row whose scores are all zero (its query orthogonal to every key
  * up to it, e.g. a zero query) is returned as zero.  Alignment: q, k, v, out
- * 16 bytes, tau 4.  Outputs may not alias inputs or each other.
+ * 16 bytes, tau 4.  Accuracy: fp32 inputs agree with the exact result to about
+ * 1e-6 relative; bf16 inputs to about 1e-2 (bf16 rounding of the scaled queries
+ * and of the weights).  Outputs may not alias inputs or each other.
  */
 int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                         int32_t in_dtype,

@@ -237,7 +237,6 @@ def test_born_attention_validation(lib):
     assert call(shape=(2, 0, 3, 16)) == 1
     assert call(shape=(2, 100, 3, 24)) == 2                  # D not supported
     assert call(shape=(2, 100, 3, 128)) == 2
-    assert call(dt=1) == 2                                   # bf16 inputs not yet
     assert call(dt=7) == 1
     bad = list(ins); bad[3] = None                           # k_im missing
     assert call(ins=bad) == 1

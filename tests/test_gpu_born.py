@@ -116,3 +116,63 @@ def test_born_layer_shape_sampled_rows():
     sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
     assert rel_err(sel, want) <= TOL, rel_err(sel, want)
     assert np.all(np.isfinite(got))
+
+
+# ---------------------------------------------------------------------------
+# bf16 inputs: the oracle runs on the bf16-rounded values, tolerance 2e-2
+# ---------------------------------------------------------------------------
+TOL16 = 2e-2
+
+
+def _bf16(p):
+    """The inputs rounded to bf16 (as float32 arrays holding bf16 values)."""
+    r = wl.round_bf16
+    return wl.BornInputs(r(p.q_re), r(p.q_im), r(p.k_re), r(p.k_im), r(p.v_re), r(p.v_im), p.tau)
+
+
+def _run16(p, with_tau=True):
+    import torch
+    import complex_valued_state_amd as cssd
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0").to(torch.bfloat16)
+    o = cssd.cssd_born_attention(t(p.q_re), t(p.q_im), t(p.k_re), t(p.k_im), t(p.v_re),
+                                 t(p.v_im), _dev(p.tau) if with_tau else None)
+    torch.cuda.synchronize()
+    return _c(*o)
+
+
+@pytest.mark.parametrize("B,T,H,D", [
+    (1, 1, 1, 16), (2, 64, 3, 16), (2, 100, 3, 16), (3, 257, 5, 16), (1, 200, 2, 32),
+    (1, 130, 2, 64), (2, 513, 1, 32),
+])
+def test_born_bf16_vs_oracle(B, T, H, D):
+    log(f"  born bf16 B{B} T{T} H{H} D{D}")
+    p = _bf16(wl.born_inputs(95 + T, B, T, H, D))
+    got = _run16(p)
+    want = oracle.born_attention(*p.complex())
+    assert rel_err(got, want) <= TOL16, rel_err(got, want)
+
+
+def test_born_bf16_without_temperature_and_zero_rows():
+    p = _bf16(wl.born_inputs(96, 2, 150, 2, 16))
+    p.q_re[:, 3::11] = 0.0
+    p.q_im[:, 3::11] = 0.0
+    got = _run16(p, with_tau=False)
+    q, k, v, _ = p.complex()
+    want = oracle.born_attention(q, k, v, None)
+    assert rel_err(got, want) <= TOL16
+    assert np.all(got[:, 3::11] == 0)
+
+
+def test_born_bf16_layer_shape_sampled_rows():
+    B, T, H, D = 256, 1024, 16, 16
+    log(f"  born bf16 layer shape B{B} T{T} H{H} D{D}")
+    p = _bf16(wl.born_inputs(1, B, T, H, D))
+    got = _run16(p)
+    rng = np.random.default_rng(97)
+    ts = np.concatenate([[0, 1, 63, 64, 65, 511, 512, 1022, 1023], rng.integers(0, T, 400)])
+    rows = np.stack([rng.integers(0, B, ts.size), ts, rng.integers(0, H, ts.size)], axis=1)
+    want = oracle.born_attention_rows((p.q_re, p.q_im), (p.k_re, p.k_im), (p.v_re, p.v_im),
+                                      p.tau, rows)
+    sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert rel_err(sel, want) <= TOL16, rel_err(sel, want)
+    assert np.all(np.isfinite(got))
