@@ -205,14 +205,14 @@ def time_constant_input(B, H, D, N, nsteps, reps, warmup, dev, seed=4):
     return res
 
 
-def backward_dxdb_flops(B, T, H, D, N, C):
-    """Algorithmic real flops of k_bwd_dxdb: per chunk, over the causal triangle,
-    the score C B^T (tri x N), P = dY X^H (tri x D), the products giving dX (tri x D)
-    and dB (tri x N), and the two state terms conj(B) R and conj(X) R^T (C x N x D
-    each); 8 real flops per complex MAC."""
+def backward_dx_flops(B, T, H, D, N, C):
+    """Algorithmic real flops of k_bwd_dx: per chunk, over the causal triangle, the
+    score C B^T (tri x N) and the product giving dX (tri x D), and the state term
+    conj(B) R (C x N x D); 8 real flops per complex MAC.  k_bwd_db does the same
+    amount with N and D exchanged in the triangle terms."""
     nC = -(-T // C)
     tri = C * (C + 1) // 2
-    return 8 * B * H * nC * (tri * 2 * (N + D) + 2 * C * N * D)
+    return 8 * B * H * nC * (tri * (N + D) + C * N * D)
 
 
 def time_phase_scan(B, T, H, N, steps, warmup, dev, chunk=0, seed=5):
@@ -468,19 +468,19 @@ def main():
         d4 = wl.CONFIG_SHAPES[4]
         progress("timing the backward pass")
         bms, bk = time_backward(inp, max(3, args.steps // 2), 2, dev)
-        bfl = backward_dxdb_flops(B, T, H, D, N, C)
+        bfl = backward_dx_flops(B, T, H, D, N, C)
+        bsym = f"k_bwd_tiles<{C}, {N}, {D}, 0>"
         extra["backward_cfg1_B8_T2048_H48_D64_N64_C64_f32"] = {
             "tokens_per_s": round(tokens / (bms * 1e-3), 1), "ms_per_step": round(bms, 4),
             "kernels_avg_ms": {k: round(v, 5) for k, v in bk.items()},
-            "roofline": {"bound": "mfma", "kernel": "k_bwd_dxdb",
-                         "achieved": round(bfl / (bk["k_bwd_dxdb"] * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "kernel": "k_bwd_dx", "symbol": bsym,
+                         "traffic": load_traffic(bsym),
+                         "achieved": round(bfl / (bk["k_bwd_dx"] * 1e-3) / 1e12, 2),
                          "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(bfl / (bk["k_bwd_dxdb"] * 1e-3) / 1e12
+                         "frac": round(bfl / (bk["k_bwd_dx"] * 1e-3) / 1e12
                                        / PEAK_FP32_MFMA_TFLOPS, 4),
-                         "symbol": f"k_bwd_tiles<{C}, {N}, {D}, false>",
-                         "traffic": load_traffic(f"k_bwd_tiles<{C}, {N}, {D}, false>"),
                          "algorithmic_flops_per_launch": bfl,
-                         "avg_launch_ms": round(bk["k_bwd_dxdb"], 5)}}
+                         "avg_launch_ms": round(bk["k_bwd_dx"], 5)}}
         progress("timing the decode step")
         dms, dkms = time_decode(d4["B"], d4["H"], d4["D"], d4["N"], d4["steps"], 8, dev)
         dbytes = decode_hbm_bytes(d4["B"], d4["H"], d4["D"], d4["N"])

@@ -361,7 +361,9 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
                                                    dh0_im, s);
         }) != hipSuccess)
         return CSSD_ERR_HIP;
-    if (timed(cssd::K_BWD_DXDB, s, [&] { return cssd::launch_bwd_dxdb(a, s); }) != hipSuccess)
+    if (timed(cssd::K_BWD_DX, s, [&] { return cssd::launch_bwd_dx(a, s); }) != hipSuccess)
+        return CSSD_ERR_HIP;
+    if (timed(cssd::K_BWD_DB, s, [&] { return cssd::launch_bwd_db(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     if (timed(cssd::K_BWD_DC, s, [&] { return cssd::launch_bwd_dc(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
@@ -655,8 +657,8 @@ int cssd_profile_read(double* ms, int64_t* launches, int capacity) {
 const char* cssd_kernel_name(int kernel_id) {
     static const char* names[cssd::K_COUNT] = {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
-        "k_step_infinite", "k_bwd_dxdb", "k_bwd_dc", "k_bwd_dz",
-        "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born"};
+        "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
+        "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

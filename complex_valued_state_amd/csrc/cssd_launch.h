@@ -7,9 +7,9 @@
 namespace cssd {
 
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
-                K_STEP_INFINITE = 5, K_BWD_DXDB = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
+                K_STEP_INFINITE = 5, K_BWD_DX = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
                 K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_BORN = 12,
-                K_COUNT = 13 };
+                K_BWD_DB = 13, K_COUNT = 14 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -81,7 +81,8 @@ hipError_t launch_chunk_state_adjoint(const FwdArgs& a, const float* dy_re, cons
 hipError_t launch_state_pass_adjoint(const FwdArgs& a, float* q_re, float* q_im,
                                      const float* dhT_re, const float* dhT_im, float* dh0_re,
                                      float* dh0_im, hipStream_t stream);
-hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dx(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_db(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dz(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_step_infinite(const StepArgs& a, hipStream_t stream);

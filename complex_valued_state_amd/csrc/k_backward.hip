@@ -32,10 +32,11 @@
 // sigmoid(dt_t) Re(dz_t conj(A)) and dA = sum_t softplus(dt_t) dz_t.
 //
 // MFMA mapping (16x16x4 fp32, lane = i + 16 g, Gauss complex products as in the
-// forward kernels).  k_bwd_dxdb: one wave per pair of row tiles {t, NLT-1-t} of
-// the l axis (tile lt sums over the NLT - lt tiles tt >= lt).  For each (tt, lt),
-// G and P come out with register r holding [t = t0 + 4g + r][l = l0 + lane%16],
-// which is the A-operand layout for the products with dY and conj(C) rows.
+// forward kernels).  dX and dB (two kernels, PART 0 and 1): one wave per pair of
+// row tiles {t, NLT-1-t} of the l axis (tile lt sums over the NLT - lt tiles
+// tt >= lt).  For each (tt, lt), G (for dX) or P (for dB) comes out with
+// register r holding [t = t0 + 4g + r][l = l0 + lane%16], which is the A-operand
+// layout for the product with dY rows (dX) or conj(C) rows (dB).
 // k_bwd_dc: one wave per pair of row tiles of the t axis; P is formed as
 // conj(X) dY^T so that register r holds [t = t0 + lane%16][l = l0 + 4g + r], the
 // A-operand layout for the product with conj(B) rows.  The state terms read
@@ -117,11 +118,14 @@ __device__ __forceinline__ ChunkView chunk_view(const BwdArgs& a, int64_t chunk,
 }  // namespace
 
 // ----------------------------------------------------------------------------
-// dX and dB for row tile lt of one chunk
+// dX (DX = true) or dB (DX = false) for row tile lt of one chunk.  The two are
+// separate kernels: dX needs only the forward scores G and dB only P, so the
+// split does no extra matrix work and halves the live accumulators.
 // ----------------------------------------------------------------------------
-template <int C, int N, int D>
+template <int C, int N, int D, bool DX>
 __device__ __forceinline__ void dxdb_tile(const BwdArgs& a, int64_t chunk, int lt) {
     constexpr int NK = N / 16, PT = D / 16, NLT = C / 16;
+    constexpr int NO = DX ? PT : NK;  // output column tiles
     const FwdArgs& f = a.f;
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
@@ -140,53 +144,56 @@ __device__ __forceinline__ void dxdb_tile(const BwdArgs& a, int64_t chunk, int l
     const BufRes rr_i = make_buf(a.r_im + chunk * (int64_t)N * D, N * D * 4);
     const double* __restrict__ ar = f.acs_re + v.pbase;
     const double* __restrict__ ai = f.acs_im + v.pbase;
-    const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
 
-    // rows l0 + li of B and X (A-operands of the state terms, B-operands of G, P)
-    floatx4 bq_r[NK], bq_i[NK], xq_r[PT], xq_i[PT];
+    // rows l0 + li of B (dX) or X (dB): the A operand of the state term and the
+    // B operand of the scores G (or P)
+    constexpr int NQ = DX ? NK : PT;
+    floatx4 oq_r[NQ], oq_i[NQ];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-        bq_r[k] = buf_f32x4(rb_r, (uint32_t)(l0 + li) * v.sN + 16 * k + 4 * g);
-        bq_i[k] = buf_f32x4(rb_i, (uint32_t)(l0 + li) * v.sN + 16 * k + 4 * g);
-    }
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-        xq_r[k] = buf_f32x4(rx_r, (uint32_t)(l0 + li) * v.sD + 16 * k + 4 * g);
-        xq_i[k] = buf_f32x4(rx_i, (uint32_t)(l0 + li) * v.sD + 16 * k + 4 * g);
+    for (int k = 0; k < NQ; ++k) {
+        if constexpr (DX) {
+            oq_r[k] = buf_f32x4(rb_r, (uint32_t)(l0 + li) * v.sN + 16 * k + 4 * g);
+            oq_i[k] = buf_f32x4(rb_i, (uint32_t)(l0 + li) * v.sN + 16 * k + 4 * g);
+        } else {
+            oq_r[k] = buf_f32x4(rx_r, (uint32_t)(l0 + li) * v.sD + 16 * k + 4 * g);
+            oq_i[k] = buf_f32x4(rx_i, (uint32_t)(l0 + li) * v.sD + 16 * k + 4 * g);
+        }
     }
 
     // accumulators: register r <-> row l = l0 + 4g + r, column 16 tile + li
-    CTile dx[PT], db[NK];
+    CTile acc[NO];
 #pragma unroll
-    for (int k = 0; k < PT; ++k) ctile_zero(dx[k]);
-#pragma unroll
-    for (int k = 0; k < NK; ++k) ctile_zero(db[k]);
+    for (int k = 0; k < NO; ++k) ctile_zero(acc[k]);
 
-    // ---- state terms: conj(B) R and conj(X) R^T, then the row factor conj(w[l])
+    // ---- state term: conj(B) R (dX) or conj(X) R^T (dB), then the row factor conj(w[l])
+    if constexpr (DX) {
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-        const floatx4 br = bq_r[k], bi = -bq_i[k], bs = br + bi;
+        for (int k = 0; k < NK; ++k) {
+            const floatx4 br = oq_r[k], bi = -oq_i[k], bs = br + bi;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            // R[16k + 4g + e][16pt + li]
-            const floatx4 rr = buf_f32x4(rr_r, (uint32_t)(k * PT + pt) * 256 + 4 * lane);
-            const floatx4 ri = buf_f32x4(rr_i, (uint32_t)(k * PT + pt) * 256 + 4 * lane);
-            const floatx4 rs = rr + ri;
+            for (int pt = 0; pt < PT; ++pt) {
+                // R[16k + 4g + e][16pt + li]
+                const floatx4 rr = buf_f32x4(rr_r, (uint32_t)(k * PT + pt) * 256 + 4 * lane);
+                const floatx4 ri = buf_f32x4(rr_i, (uint32_t)(k * PT + pt) * 256 + 4 * lane);
+                const floatx4 rs = rr + ri;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ctile_mac(dx[pt], br[e], bi[e], bs[e], rr[e], ri[e], rs[e]);
+                for (int e = 0; e < 4; ++e)
+                    ctile_mac(acc[pt], br[e], bi[e], bs[e], rr[e], ri[e], rs[e]);
+            }
         }
-    }
+    } else {
 #pragma unroll
-    for (int pk = 0; pk < PT; ++pk) {
-        const floatx4 xr = xq_r[pk], xi = -xq_i[pk], xs = xr + xi;
+        for (int pk = 0; pk < PT; ++pk) {
+            const floatx4 xr = oq_r[pk], xi = -oq_i[pk], xs = xr + xi;
 #pragma unroll
-        for (int nt = 0; nt < NK; ++nt) {
+            for (int nt = 0; nt < NK; ++nt) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // R^T[p = 16pk + 4g + e][n = 16nt + li] = R[n][p]
-                const uint32_t fi = frag_index<D>(16 * nt + li, 16 * pk + 4 * g + e);
-                const float tr = buf_f32(rr_r, fi), ti = buf_f32(rr_i, fi);
-                ctile_mac(db[nt], xr[e], xi[e], xs[e], tr, ti, tr + ti);
+                for (int e = 0; e < 4; ++e) {
+                    // R^T[p = 16pk + 4g + e][n = 16nt + li] = R[n][p]
+                    const uint32_t fi = frag_index<D>(16 * nt + li, 16 * pk + 4 * g + e);
+                    const float tr = buf_f32(rr_r, fi), ti = buf_f32(rr_i, fi);
+                    ctile_mac(acc[nt], xr[e], xi[e], xs[e], tr, ti, tr + ti);
+                }
             }
         }
     }
@@ -194,12 +201,9 @@ __device__ __forceinline__ void dxdb_tile(const BwdArgs& a, int64_t chunk, int l
         const floatx4 wr = *reinterpret_cast<const floatx4*>(f.w_re + v.pbase + l0 + 4 * g);
         const floatx4 wi = *reinterpret_cast<const floatx4*>(f.w_im + v.pbase + l0 + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int k = 0; k < PT; ++k) ctile_scale(dx[k], r, wr[r], -wi[r]);
-#pragma unroll
-            for (int k = 0; k < NK; ++k) ctile_scale(db[k], r, wr[r], -wi[r]);
-        }
+            for (int k = 0; k < NO; ++k) ctile_scale(acc[k], r, wr[r], -wi[r]);
     }
 
     // ---- causal terms over the tiles tt >= lt
@@ -207,94 +211,104 @@ __device__ __forceinline__ void dxdb_tile(const BwdArgs& a, int64_t chunk, int l
     for (int tt = 0; tt < NLT; ++tt) {
         if (tt < lt) continue;  // wave-uniform
         const int t0 = tt * 16;
-        // G[t][l] = C[t] . B[l] and P[t][l] = dY[t] . conj(X[l]); register r <->
-        // t = t0 + 4g + r, l = l0 + li
-        CTile gt, pq;
-        ctile_zero(gt);
-        ctile_zero(pq);
+        // dX: G[t][l] = C[t] . B[l];  dB: P[t][l] = dY[t] . conj(X[l]);
+        // register r <-> t = t0 + 4g + r, l = l0 + li
+        CTile sq;
+        ctile_zero(sq);
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            const floatx4 cr = buf_f32x4(rc_r, (uint32_t)(t0 + li) * v.sN + 16 * k + 4 * g);
-            const floatx4 ci = buf_f32x4(rc_i, (uint32_t)(t0 + li) * v.sN + 16 * k + 4 * g);
-            const floatx4 cs = cr + ci, bs = bq_r[k] + bq_i[k];
+        for (int k = 0; k < NQ; ++k) {
+            if constexpr (DX) {
+                const floatx4 cr = buf_f32x4(rc_r, (uint32_t)(t0 + li) * v.sN + 16 * k + 4 * g);
+                const floatx4 ci = buf_f32x4(rc_i, (uint32_t)(t0 + li) * v.sN + 16 * k + 4 * g);
+                const floatx4 cs = cr + ci, bs = oq_r[k] + oq_i[k];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ctile_mac(gt, cr[e], ci[e], cs[e], bq_r[k][e], bq_i[k][e], bs[e]);
+                for (int e = 0; e < 4; ++e)
+                    ctile_mac(sq, cr[e], ci[e], cs[e], oq_r[k][e], oq_i[k][e], bs[e]);
+            } else {
+                const floatx4 gr = buf_f32x4(rg_r, (uint32_t)(t0 + li) * v.sD + 16 * k + 4 * g);
+                const floatx4 gi = buf_f32x4(rg_i, (uint32_t)(t0 + li) * v.sD + 16 * k + 4 * g);
+                const floatx4 gs = gr + gi, xs = oq_r[k] - oq_i[k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ctile_mac(sq, gr[e], gi[e], gs[e], oq_r[k][e], -oq_i[k][e], xs[e]);
+            }
         }
-#pragma unroll
-        for (int pk = 0; pk < PT; ++pk) {
-            const floatx4 gr = buf_f32x4(rg_r, (uint32_t)(t0 + li) * v.sD + 16 * pk + 4 * g);
-            const floatx4 gi = buf_f32x4(rg_i, (uint32_t)(t0 + li) * v.sD + 16 * pk + 4 * g);
-            const floatx4 gs = gr + gi, xs = xq_r[pk] - xq_i[pk];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ctile_mac(pq, gr[e], gi[e], gs[e], xq_r[pk][e], -xq_i[pk][e], xs[e]);
-        }
-        float cm_r[4], cm_i[4], kk_r[4], kk_i[4];
+        float m_r[4], m_i[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = t0 + 4 * g + r, l = l0 + li;
             float lr = 0.f, lim = 0.f;
             if (tt > lt || t >= l) seg_exp(ar, ai, t, l, false, lr, lim);
-            const float g_r = ctile_re(gt, r), g_i = ctile_im(gt, r);
-            const float p_r = ctile_re(pq, r), p_i = ctile_im(pq, r);
-            cm_r[r] = g_r * lr - g_i * lim;       // conj(G L)
-            cm_i[r] = -(g_r * lim + g_i * lr);
-            kk_r[r] = lr * p_r + lim * p_i;       // conj(L) P
-            kk_i[r] = lr * p_i - lim * p_r;
+            const float s_r = ctile_re(sq, r), s_i = ctile_im(sq, r);
+            if constexpr (DX) {
+                m_r[r] = s_r * lr - s_i * lim;  // conj(G L)
+                m_i[r] = -(s_r * lim + s_i * lr);
+            } else {
+                m_r[r] = lr * s_r + lim * s_i;  // conj(L) P
+                m_i[r] = lr * s_i - lim * s_r;
+            }
         }
-        // dX += conj(M)^T dY[tt]; dB += K^T conj(C[tt]); k-step r <-> t = t0 + 4g + r
+        // dX += conj(G L)^T dY[tt];  dB += (conj(L) P)^T conj(C[tt]);
+        // k-step r <-> t = t0 + 4g + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t trow = (uint32_t)(t0 + 4 * g + r);
-            const float ms = cm_r[r] + cm_i[r], ks = kk_r[r] + kk_i[r];
+            const float ms = m_r[r] + m_i[r];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const float yr = buf_f32(rg_r, trow * v.sD + 16 * pt + li);
-                const float yi = buf_f32(rg_i, trow * v.sD + 16 * pt + li);
-                ctile_mac(dx[pt], cm_r[r], cm_i[r], ms, yr, yi, yr + yi);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NK; ++nt) {
-                const float cr = buf_f32(rc_r, trow * v.sN + 16 * nt + li);
-                const float ci = -buf_f32(rc_i, trow * v.sN + 16 * nt + li);
-                ctile_mac(db[nt], kk_r[r], kk_i[r], ks, cr, ci, cr + ci);
+            for (int k = 0; k < NO; ++k) {
+                float yr, yi;
+                if constexpr (DX) {
+                    yr = buf_f32(rg_r, trow * v.sD + 16 * k + li);
+                    yi = buf_f32(rg_i, trow * v.sD + 16 * k + li);
+                } else {
+                    yr = buf_f32(rc_r, trow * v.sN + 16 * k + li);
+                    yi = -buf_f32(rc_i, trow * v.sN + 16 * k + li);
+                }
+                ctile_mac(acc[k], m_r[r], m_i[r], ms, yr, yi, yr + yi);
             }
         }
     }
 
-    // ---- q1[l] = -sum_p conj(x[l][p]) dx[l][p] (before the skip term), the skip
-    // term, and the stores; register r <-> row l = l0 + 4g + r
-    const BufRes rdx_r = make_buf(a.dx_re + v.row0 * D, v.extD * 4);
-    const BufRes rdx_i = make_buf(a.dx_im + v.row0 * D, v.extD * 4);
-    const BufRes rdb_r = make_buf(a.db_re + v.row0 * N, v.extN * 4);
-    const BufRes rdb_i = make_buf(a.db_im + v.row0 * N, v.extN * 4);
+    // ---- stores; for dX also the skip term and q1[l] = -sum_p conj(x[l][p]) dx[l][p]
+    // (before the skip term); register r <-> row l = l0 + 4g + r
+    if constexpr (DX) {
+        const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
+        const BufRes rdx_r = make_buf(a.dx_re + v.row0 * D, v.extD * 4);
+        const BufRes rdx_i = make_buf(a.dx_im + v.row0 * D, v.extD * 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t lrow = (uint32_t)(l0 + 4 * g + r);
-        float qr = 0.f, qi = 0.f;
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t lrow = (uint32_t)(l0 + 4 * g + r);
+            float qr = 0.f, qi = 0.f;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const uint32_t off = lrow * v.sD + 16 * pt + li;
-            const float xr = buf_f32(rx_r, off), xi = buf_f32(rx_i, off);
-            const float gr = buf_f32(rg_r, off), gi = buf_f32(rg_i, off);
-            const float vr = ctile_re(dx[pt], r), vi = ctile_im(dx[pt], r);
-            qr += xr * vr + xi * vi;  // conj(x) dx
-            qi += xr * vi - xi * vr;
-            buf_store_f32(vr + dk * gr, rdx_r, off);
-            buf_store_f32(vi + dk * gi, rdx_i, off);
+            for (int pt = 0; pt < PT; ++pt) {
+                const uint32_t off = lrow * v.sD + 16 * pt + li;
+                const float xr = buf_f32(rx_r, off), xi = buf_f32(rx_i, off);
+                const float gr = buf_f32(rg_r, off), gi = buf_f32(rg_i, off);
+                const float vr = ctile_re(acc[pt], r), vi = ctile_im(acc[pt], r);
+                qr += xr * vr + xi * vi;  // conj(x) dx
+                qi += xr * vi - xi * vr;
+                buf_store_f32(vr + dk * gr, rdx_r, off);
+                buf_store_f32(vi + dk * gi, rdx_i, off);
+            }
+            qr = sum16(qr);
+            qi = sum16(qi);
+            if (li == 0) {
+                a.q1_re[v.pbase + lrow] = -qr;
+                a.q1_im[v.pbase + lrow] = -qi;
+            }
         }
-        qr = sum16(qr);
-        qi = sum16(qi);
-        if (li == 0) {
-            a.q1_re[v.pbase + lrow] = -qr;
-            a.q1_im[v.pbase + lrow] = -qi;
-        }
+    } else {
+        const BufRes rdb_r = make_buf(a.db_re + v.row0 * N, v.extN * 4);
+        const BufRes rdb_i = make_buf(a.db_im + v.row0 * N, v.extN * 4);
 #pragma unroll
-        for (int nt = 0; nt < NK; ++nt) {
-            const uint32_t off = lrow * v.sN + 16 * nt + li;
-            buf_store_f32(ctile_re(db[nt], r), rdb_r, off);
-            buf_store_f32(ctile_im(db[nt], r), rdb_i, off);
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t lrow = (uint32_t)(l0 + 4 * g + r);
+#pragma unroll
+            for (int nt = 0; nt < NK; ++nt) {
+                const uint32_t off = lrow * v.sN + 16 * nt + li;
+                buf_store_f32(ctile_re(acc[nt], r), rdb_r, off);
+                buf_store_f32(ctile_im(acc[nt], r), rdb_i, off);
+            }
         }
     }
 }
@@ -443,24 +457,30 @@ __device__ __forceinline__ void dc_tile(const BwdArgs& a, int64_t chunk, int tt)
 }
 
 // Balanced pairs of row tiles {t, NLT-1-t} per wave, 4 / WPC chunks per block.
-#ifndef CSSD_BWD_WAVES
-#define CSSD_BWD_WAVES 2
-#endif
-template <int C, int N, int D, bool DC>
+// PART: 0 dX, 1 dB, 2 dC.  Waves per SIMD: 1 for the large states; otherwise 3
+// where the live tiles (complex accumulators, 12 registers each, and resident
+// operand fragments, 8 each) fit, else 2 (more waves spill there).
+constexpr int bwd_waves(int C, int N, int D, int PART) {
+    const int no = PART == 0 ? D / 16 : N / 16;  // accumulator tiles
+    const int nq = PART == 0 ? N / 16 : D / 16;  // resident operand fragments
+    return N * D > 64 * 64 ? 1 : (12 * no + 8 * nq <= 80 && C <= 64 ? 3 : 2);
+}
+
+template <int C, int N, int D, int PART>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(N * D > 64 * 64 ? 1 : CSSD_BWD_WAVES))) void k_bwd_tiles(BwdArgs a) {
+__attribute__((amdgpu_waves_per_eu(bwd_waves(C, N, D, PART)))) void k_bwd_tiles(BwdArgs a) {
     constexpr int NLT = C / 16;
     constexpr int WPC = NLT >= 2 ? NLT / 2 : 1;
     const int wave = wave_id();
     const int64_t chunk = (int64_t)blockIdx.x * (4 / WPC) + wave / WPC;
     if (chunk >= a.f.B * a.f.H * a.f.nC) return;  // wave-uniform
     const int t = wave % WPC;
-    if (DC) {
+    if constexpr (PART == 2) {
         dc_tile<C, N, D>(a, chunk, t);
         if (NLT - 1 - t != t) dc_tile<C, N, D>(a, chunk, NLT - 1 - t);
     } else {
-        dxdb_tile<C, N, D>(a, chunk, t);
-        if (NLT - 1 - t != t) dxdb_tile<C, N, D>(a, chunk, NLT - 1 - t);
+        dxdb_tile<C, N, D, PART == 0>(a, chunk, t);
+        if (NLT - 1 - t != t) dxdb_tile<C, N, D, PART == 0>(a, chunk, NLT - 1 - t);
     }
 }
 
@@ -612,43 +632,44 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(BwdArgs a) {
     if (a.dd != nullptr) a.dd[h] = (float)sd;
 }
 
-template <int C, int N, bool DC>
+template <int C, int N, int PART>
 static hipError_t launch_tiles_d(const BwdArgs& a, hipStream_t s) {
     constexpr int WPC = C / 16 >= 2 ? C / 32 : 1;
     constexpr int CPB = 4 / WPC;
     const int64_t nchunks = a.f.B * a.f.H * a.f.nC;
     const dim3 grid((unsigned)((nchunks + CPB - 1) / CPB)), block(256);
     switch (a.f.D) {
-        case 16: hipLaunchKernelGGL((k_bwd_tiles<C, N, 16, DC>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((k_bwd_tiles<C, N, 32, DC>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((k_bwd_tiles<C, N, 64, DC>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_bwd_tiles<C, N, 128, DC>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((k_bwd_tiles<C, N, 16, PART>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((k_bwd_tiles<C, N, 32, PART>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((k_bwd_tiles<C, N, 64, PART>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_bwd_tiles<C, N, 128, PART>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
 
-template <int C, bool DC>
+template <int C, int PART>
 static hipError_t launch_tiles_n(const BwdArgs& a, hipStream_t s) {
     switch (a.f.N) {
-        case 16: return launch_tiles_d<C, 16, DC>(a, s);
-        case 32: return launch_tiles_d<C, 32, DC>(a, s);
-        case 64: return launch_tiles_d<C, 64, DC>(a, s);
-        default: return launch_tiles_d<C, 128, DC>(a, s);
+        case 16: return launch_tiles_d<C, 16, PART>(a, s);
+        case 32: return launch_tiles_d<C, 32, PART>(a, s);
+        case 64: return launch_tiles_d<C, 64, PART>(a, s);
+        default: return launch_tiles_d<C, 128, PART>(a, s);
     }
 }
 
-template <bool DC>
+template <int PART>
 static hipError_t launch_tiles(const BwdArgs& a, hipStream_t s) {
     switch (a.f.C) {
-        case 16: return launch_tiles_n<16, DC>(a, s);
-        case 32: return launch_tiles_n<32, DC>(a, s);
-        case 64: return launch_tiles_n<64, DC>(a, s);
-        default: return launch_tiles_n<128, DC>(a, s);
+        case 16: return launch_tiles_n<16, PART>(a, s);
+        case 32: return launch_tiles_n<32, PART>(a, s);
+        case 64: return launch_tiles_n<64, PART>(a, s);
+        default: return launch_tiles_n<128, PART>(a, s);
     }
 }
 
-hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t s) { return launch_tiles<false>(a, s); }
-hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s) { return launch_tiles<true>(a, s); }
+hipError_t launch_bwd_dx(const BwdArgs& a, hipStream_t s) { return launch_tiles<0>(a, s); }
+hipError_t launch_bwd_db(const BwdArgs& a, hipStream_t s) { return launch_tiles<1>(a, s); }
+hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s) { return launch_tiles<2>(a, s); }
 
 hipError_t launch_bwd_dz(const BwdArgs& a, hipStream_t s) {
     const int64_t nchunks = a.f.B * a.f.H * a.f.nC;
