@@ -4,8 +4,9 @@
 
 One step = one cssd_forward over the Mamba-style layer workload (batch 8,
 T = 2048, 48 heads, head dim 64, state 64, chunk 64, fp32 complex planes): the
-discretise + chunk-local cumsum, the chunk states, the inter-chunk state pass
-and the intra-chunk output with the combine, all in the library's HIP kernels.
+discretise + chunk-local cumsum, the chunk states with the inter-chunk state
+pass (one fused kernel) and the intra-chunk output with the combine, all in the
+library's HIP kernels.
 Inputs are seeded synthetic data already resident in HBM when timing starts.
 Prints ONE JSON line.  Per-kernel durations come from HIP events the library
 records around each launch on the launch stream during the timed region.
@@ -48,7 +49,7 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_bwd_dz": ("k_backward.hip",), "k_bwd_reduce": ("k_backward.hip",),
               "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
               "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",),
-              "k_born_bf16": ("k_born.hip",)}
+              "k_born_bf16": ("k_born.hip",), "k_state_scan": ("k_state_scan.hip",)}
 
 
 # ---------------------------------------------------------------------------

@@ -255,9 +255,7 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
-    if (timed(cssd::K_CHUNK_STATE, s, [&] { return cssd::launch_chunk_state(a, s); }) != hipSuccess)
-        return CSSD_ERR_HIP;
-    if (timed(cssd::K_STATE_PASS, s, [&] { return cssd::launch_state_pass(a, s); }) != hipSuccess)
+    if (timed(cssd::K_STATE_SCAN, s, [&] { return cssd::launch_state_scan(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     if (timed(cssd::K_CHUNK_SCAN, s, [&] { return cssd::launch_chunk_scan(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
@@ -347,9 +345,7 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
     // forward recomputation: cumsums, chunk states, carry-in states H_c and hT
     if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a.f, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
-    if (timed(cssd::K_CHUNK_STATE, s, [&] { return cssd::launch_chunk_state(a.f, s); }) != hipSuccess)
-        return CSSD_ERR_HIP;
-    if (timed(cssd::K_STATE_PASS, s, [&] { return cssd::launch_state_pass(a.f, s); }) != hipSuccess)
+    if (timed(cssd::K_STATE_SCAN, s, [&] { return cssd::launch_state_scan(a.f, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     // adjoint chunk states and the backward pass over chunks: R_{c+1}, dh0
     if (timed(cssd::K_CHUNK_STATE, s, [&] {
@@ -658,7 +654,8 @@ const char* cssd_kernel_name(int kernel_id) {
     static const char* names[cssd::K_COUNT] = {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
         "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
-        "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db"};
+        "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db",
+        "k_state_scan"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

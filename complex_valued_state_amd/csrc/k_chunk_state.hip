@@ -1,4 +1,6 @@
-// K3: per-chunk end states, as a complex GEMM on the fp32 matrix cores.
+// K3: per-chunk end states, as a complex GEMM on the fp32 matrix cores.  The
+// forward computes them fused with the chunk-to-chunk pass (k_state_scan.hip);
+// this kernel serves the gradient pass, in its conjugate-weight mode.
 //
 //   S_c[n, p] = sum_l  w[l] B[l, n] X[l, p],   w[l] = exp(acs[C-1] - acs[l])
 //
@@ -129,43 +131,6 @@ __global__ __launch_bounds__(512) void k_chunk_state(
         *reinterpret_cast<floatx4*>(st_re + off) = vr;
         *reinterpret_cast<floatx4*>(st_im + off) = vi;
     }
-}
-
-template <typename In, int C>
-static void launch_d(const FwdArgs& a, hipStream_t s) {
-    const auto* xr = static_cast<const typename In::T*>(a.x_re);
-    const auto* xi = static_cast<const typename In::T*>(a.x_im);
-    const auto* br = static_cast<const typename In::T*>(a.b_re);
-    const auto* bi = static_cast<const typename In::T*>(a.b_im);
-    const dim3 grid((unsigned)(a.B * a.H * a.nC)), block((unsigned)(4 * a.N));
-#define CSSD_K3(DD)                                                                            \
-    hipLaunchKernelGGL((k_chunk_state<In, C, DD>), grid, block, 0, s, xr, xi, br, bi, a.w_re,  \
-                       a.w_im, a.st_re, a.st_im, a.T, (int)a.H, (int)a.N, (int)a.nC)
-    switch (a.D) {
-        case 16: CSSD_K3(16); break;
-        case 32: CSSD_K3(32); break;
-        case 64: CSSD_K3(64); break;
-        default: CSSD_K3(128); break;
-    }
-#undef CSSD_K3
-}
-
-template <typename In>
-static void launch_c(const FwdArgs& a, hipStream_t s) {
-    switch (a.C) {
-        case 16: launch_d<In, 16>(a, s); break;
-        case 32: launch_d<In, 32>(a, s); break;
-        case 64: launch_d<In, 64>(a, s); break;
-        default: launch_d<In, 128>(a, s); break;
-    }
-}
-
-hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t stream) {
-    if (a.in_dtype == 1)
-        launch_c<InBF16>(a, stream);
-    else
-        launch_c<InF32>(a, stream);
-    return hipGetLastError();
 }
 
 // Adjoint chunk states for the gradient pass (fp32 planes):

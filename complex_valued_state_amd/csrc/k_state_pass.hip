@@ -1,4 +1,6 @@
-// K4: the chunk-level scan that carries the state from chunk to chunk.
+// K4: the chunk-level scan that carries the state from chunk to chunk.  The
+// forward computes it fused with the chunk states (k_state_scan.hip); this
+// kernel serves the gradient pass in its reverse (adjoint) mode.
 //
 //   H_0 = h0 (or 0);   H_{c+1} = cd[c] * H_c + S_c;   hT = H_{nC}
 //
@@ -95,16 +97,6 @@ __global__ __launch_bounds__(256) void k_state_pass(float4* __restrict__ st_re,
         hT_im[sbase] = hi.x; hT_im[sbase + D] = hi.y;
         hT_im[sbase + 2 * D] = hi.z; hT_im[sbase + 3 * D] = hi.w;
     }
-}
-
-hipError_t launch_state_pass(const FwdArgs& a, hipStream_t stream) {
-    const int64_t total = a.B * a.H * (a.N * a.D / 4);
-    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-    hipLaunchKernelGGL(k_state_pass<false>, grid, block, 0, stream,
-                       reinterpret_cast<float4*>(a.st_re), reinterpret_cast<float4*>(a.st_im),
-                       a.cd_re, a.cd_im, a.h0_re, a.h0_im, a.hT_re, a.hT_im, total, (int)a.N,
-                       (int)a.D, (int)a.nC);
-    return hipGetLastError();
 }
 
 hipError_t launch_state_pass_adjoint(const FwdArgs& a, float* q_re, float* q_im,

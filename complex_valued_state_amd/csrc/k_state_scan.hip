@@ -1,0 +1,236 @@
+// The chunk end states and the chunk-to-chunk pass of the forward, fused:
+//
+//   S_c = (diag(w) B)^T X   over the rows of chunk c   (the chunk-state kernel)
+//   H_0 = h0 (or 0);  H_{c+1} = cd[c] H_c + S_c;  hT = H_{nC}
+//
+// (Mamba-3-Lite docs, "SSD Theory" 4.5, and "The Chunkwise Complex SSD
+// Algorithm" 4.5: the per-chunk states einsum, then the recurrence over the
+// T/C chunk boundaries, evaluated in that sequential form).  The separate
+// kernels write every S_c to memory and read it back to form H_c; here one wave
+// owns one 16 x 16 tile (n, p) of the state of one (b, h) and walks the chunks
+// in order, so S_c lives only in the wave's accumulator and H in its
+// registers (a wave owns up to two tiles p of one n).  What is written is
+// exactly what the output kernel reads: the
+// carry-in state H_c of every chunk (MFMA-fragment order, the accumulator
+// layout itself, one contiguous 1 KB float4 store per tile), and hT.
+//
+// Mapping as in the chunk-state kernel: step j of the 16x16x4 MFMA contracts
+// time l = (C/4) g + j (g = lane/16); B and X are read with lane%16 along their
+// contiguous axis through per-chunk buffer views whose extent ends at the
+// chunk's last real row (padded rows read as zero).  The operands (B and X) of
+// the next DIST k-steps are kept in flight in a register ring that runs on
+// across chunk boundaries.  All workgroups of one (b, h) go to
+// the same XCD (dispatch is round-robin over the 8 XCDs), so the B and X rows
+// that several waves of that (b, h) read are fetched into one L2.
+#include "cssd_device.h"
+#include "cssd_launch.h"
+
+namespace cssd {
+
+namespace {
+
+constexpr int kScanXcds = 8;
+
+}  // namespace
+
+// A wave owns PW consecutive 16-column tiles p of one 16-row tile n (operand
+// reuse: the B row segment serves all PW tiles).  The weights w of the current
+// chunk sit in a wave-private LDS slot (16 lanes read the same weight: a
+// broadcast), refilled once per chunk from registers loaded a chunk ahead.
+template <typename In, int C, int PW>
+__global__ __launch_bounds__(256) void k_state_scan(
+    const typename In::T* __restrict__ x_re, const typename In::T* __restrict__ x_im,
+    const typename In::T* __restrict__ b_re, const typename In::T* __restrict__ b_im,
+    const float* __restrict__ w_re, const float* __restrict__ w_im,
+    const float* __restrict__ cd_re, const float* __restrict__ cd_im,
+    const float* __restrict__ h0_re, const float* __restrict__ h0_im, float* __restrict__ st_re,
+    float* __restrict__ st_im, float* __restrict__ hT_re, float* __restrict__ hT_im, int64_t T,
+    int H, int N, int D, int nC, int64_t nbh) {
+    constexpr int KJ = C / 4;  // MFMA k-steps per chunk
+    constexpr int DIST = 4;    // k-steps in flight (8 measured no faster, at more registers)
+    constexpr int RING = DIST < KJ ? DIST : KJ;
+    constexpr int WPL = (C + 63) / 64;  // weights per lane and plane when loading a chunk's w
+    __shared__ float lds_w[4][2 * C];  // per wave: w re, w im of the current chunk
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int wv = wave_id();
+    const int NK = N / 16, PT = D / 16, units = NK * (PT / PW);
+    // work item: (b, h, unit).  With at least 4 units per (b, h) a workgroup
+    // takes 4 units of one (b, h), and the workgroups of one (b, h) share an XCD.
+    int64_t bh;
+    int unit;
+    if (units >= 4) {
+        const int per = units / 4;  // workgroups per (b, h)
+        const int64_t x = blockIdx.x % kScanXcds, y = blockIdx.x / kScanXcds;
+        bh = (y / per) * kScanXcds + x;
+        unit = (int)(y % per) * 4 + wv;
+    } else {
+        const int64_t u = (int64_t)blockIdx.x * 4 + wv;
+        bh = u / units;
+        unit = (int)(u % units);
+    }
+    if (bh >= nbh) return;  // wave-uniform; the kernel has no barriers
+    const int nt = unit / (PT / PW), pt0 = (unit % (PT / PW)) * PW;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
+    float* const lw = lds_w[wv];
+
+    // carried state, tile q register r <-> (n = 16 nt + 4g + r, p = 16 (pt0 + q) + li)
+    const int64_t sbase = (bh * N + nt * 16 + 4 * g) * (int64_t)D + pt0 * 16 + li;
+    float hr[PW][4], hi[PW][4];
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hr[q][r] = h0_re != nullptr ? h0_re[sbase + r * D + 16 * q] : 0.f;
+            hi[q][r] = h0_im != nullptr ? h0_im[sbase + r * D + 16 * q] : 0.f;
+        }
+
+    struct Ops {
+        float br, bi, xr[PW], xi[PW];
+    };
+    // operands of k-step j of chunk c (c < nC)
+    auto load = [&](int c, int j, Ops& o) {
+        const int64_t t0 = (int64_t)c * C;
+        const int valid = (int)min<int64_t>((int64_t)C, T - t0);
+        const int64_t row0 = (b * T + t0) * H + h;
+        const uint32_t extN = (uint32_t)(valid - 1) * sN + N, extD = (uint32_t)(valid - 1) * sD + D;
+        const BufRes rb_r = make_buf(b_re + row0 * N, extN * sizeof(typename In::T));
+        const BufRes rb_i = make_buf(b_im + row0 * N, extN * sizeof(typename In::T));
+        const BufRes rx_r = make_buf(x_re + row0 * D, extD * sizeof(typename In::T));
+        const BufRes rx_i = make_buf(x_im + row0 * D, extD * sizeof(typename In::T));
+        const uint32_t l = (uint32_t)(KJ * g + j);
+        o.br = In::bload1(rb_r, l * sN + nt * 16 + li);
+        o.bi = In::bload1(rb_i, l * sN + nt * 16 + li);
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            o.xr[q] = In::bload1(rx_r, l * sD + (pt0 + q) * 16 + li);
+            o.xi[q] = In::bload1(rx_i, l * sD + (pt0 + q) * 16 + li);
+        }
+    };
+    // the weights of chunk c: lane takes positions lane + 64 k
+    float wn_r[WPL], wn_i[WPL];
+    auto load_w = [&](int c) {
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            const int pos = lane + 64 * k;
+            const int64_t at = bh * (int64_t)nC * C + (int64_t)c * C + pos;
+            wn_r[k] = pos < C ? w_re[at] : 0.f;
+            wn_i[k] = pos < C ? w_im[at] : 0.f;
+        }
+    };
+
+    Ops ring[RING];
+#pragma unroll
+    for (int j = 0; j < RING; ++j) load(0, j, ring[j]);
+    load_w(0);
+
+    const int64_t slot = ((int64_t)nt * PT + pt0) * 256 + 4 * lane;  // within one chunk's N x D block
+    for (int c = 0; c < nC; ++c) {
+        // carry-in state of chunk c
+        {
+            const int64_t off = (bh * nC + c) * (int64_t)N * D + slot;
+#pragma unroll
+            for (int q = 0; q < PW; ++q) {
+                *reinterpret_cast<floatx4*>(st_re + off + 256 * q) =
+                    floatx4{hr[q][0], hr[q][1], hr[q][2], hr[q][3]};
+                *reinterpret_cast<floatx4*>(st_im + off + 256 * q) =
+                    floatx4{hi[q][0], hi[q][1], hi[q][2], hi[q][3]};
+            }
+        }
+        // this chunk's weights into the wave's LDS slot, the next chunk's into registers
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            const int pos = lane + 64 * k;
+            if (pos < C) {
+                lw[pos] = wn_r[k];
+                lw[C + pos] = wn_i[k];
+            }
+        }
+        if (c + 1 < nC) load_w(c + 1);
+        const float dr = cd_re[bh * nC + c], di = cd_im[bh * nC + c];
+        CTile acc[PW];
+#pragma unroll
+        for (int q = 0; q < PW; ++q) ctile_zero(acc[q]);
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const Ops o = ring[j % RING];
+            // refill this slot with the operands RING steps ahead
+            const int jn = j + RING;
+            if (jn < KJ)
+                load(c, jn, ring[j % RING]);
+            else if (c + 1 < nC)  // wave-uniform
+                load(c + 1, jn - KJ, ring[j % RING]);
+            __builtin_amdgcn_sched_barrier(0);
+            const float wr = lw[KJ * g + j], wi = lw[C + KJ * g + j];
+            const float pr = wr * o.br - wi * o.bi;  // (w B)[l, n]
+            const float pi = wr * o.bi + wi * o.br;
+            const float ps = pr + pi;
+#pragma unroll
+            for (int q = 0; q < PW; ++q) ctile_mac(acc[q], pr, pi, ps, o.xr[q], o.xi[q], o.xr[q] + o.xi[q]);
+        }
+        // H_{c+1} = cd[c] H_c + S_c
+#pragma unroll
+        for (int q = 0; q < PW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float nr = dr * hr[q][r] - di * hi[q][r] + ctile_re(acc[q], r);
+                const float ni = dr * hi[q][r] + di * hr[q][r] + ctile_im(acc[q], r);
+                hr[q][r] = nr;
+                hi[q][r] = ni;
+            }
+    }
+    if (hT_re != nullptr) {
+#pragma unroll
+        for (int q = 0; q < PW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hT_re[sbase + r * D + 16 * q] = hr[q][r];
+                hT_im[sbase + r * D + 16 * q] = hi[q][r];
+            }
+    }
+}
+
+template <typename In, int C, int PW>
+static hipError_t launch_scan_pw(const FwdArgs& a, hipStream_t s) {
+    const int units = (int)((a.N / 16) * (a.D / 16 / PW));
+    const int64_t nbh = a.B * a.H;
+    int64_t blocks;
+    if (units >= 4)
+        blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * (units / 4);
+    else
+        blocks = (nbh * units + 3) / 4;
+    hipLaunchKernelGGL((k_state_scan<In, C, PW>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const typename In::T*>(a.x_re),
+                       static_cast<const typename In::T*>(a.x_im),
+                       static_cast<const typename In::T*>(a.b_re),
+                       static_cast<const typename In::T*>(a.b_im), a.w_re, a.w_im, a.cd_re,
+                       a.cd_im, a.h0_re, a.h0_im, a.st_re, a.st_im, a.hT_re, a.hT_im, a.T,
+                       (int)a.H, (int)a.N, (int)a.D, (int)a.nC, nbh);
+    return hipGetLastError();
+}
+
+// Two tiles per wave where D allows (measured at B8 T2048 H48 N64 D64 C64: one
+// tile per wave 0.52 ms, two 0.38 ms, against 0.41 ms for the separate
+// chunk-state and state-pass kernels).
+template <typename In, int C>
+static hipError_t launch_scan_c(const FwdArgs& a, hipStream_t s) {
+    return a.D >= 32 ? launch_scan_pw<In, C, 2>(a, s) : launch_scan_pw<In, C, 1>(a, s);
+}
+
+template <typename In>
+static hipError_t launch_scan_in(const FwdArgs& a, hipStream_t s) {
+    switch (a.C) {
+        case 16: return launch_scan_c<In, 16>(a, s);
+        case 32: return launch_scan_c<In, 32>(a, s);
+        case 64: return launch_scan_c<In, 64>(a, s);
+        default: return launch_scan_c<In, 128>(a, s);
+    }
+}
+
+hipError_t launch_state_scan(const FwdArgs& a, hipStream_t s) {
+    return a.in_dtype == 1 ? launch_scan_in<InBF16>(a, s) : launch_scan_in<InF32>(a, s);
+}
+
+}  // namespace cssd

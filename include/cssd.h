@@ -354,8 +354,9 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
  * kernels), resets the accumulators and returns the number of kernel ids (or a
  * negative status on error).  Kernel ids: 0 cumsum, 1 chunk_state,
  * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite,
- * 6 bwd_dx, 7 bwd_dc, 8 bwd_dz, 13 bwd_db (cssd_backward also runs ids 0-2, and
- * 1 and 2 a second time in their adjoint modes), 9 phase_summary,
+ * 14 state_scan (cssd_forward: the chunk states fused with the state pass),
+ * 6 bwd_dx, 7 bwd_dc, 8 bwd_dz, 13 bwd_db (cssd_backward also runs ids 0 and 14,
+ * and 1 and 2 in their adjoint modes), 9 phase_summary,
  * 10 phase_carry, 11 phase_out (cssd_phase_scan), 12 born (cssd_born_attention).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).

@@ -255,7 +255,8 @@ def test_profiler_without_launches(lib):
         pass
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
-    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(14) is None
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(15) is None
+    assert lib.cssd_kernel_name(14) == b"k_state_scan"
     assert lib.cssd_kernel_name(13) == b"k_bwd_db" and lib.cssd_kernel_name(6) == b"k_bwd_dx"
     assert lib.cssd_kernel_name(12) == b"k_born"
     assert lib.cssd_kernel_name(5) == b"k_step_infinite"
