@@ -1,5 +1,5 @@
-// Instantiation of the chunk-scan kernel for chunk size 128 (kernels in k_chunk_scan.h and k_chunk_scan_lds.h).
-#include "k_chunk_scan_lds.h"
+// Instantiation of the chunk-scan kernel for chunk size 128 (kernels in k_chunk_scan.h, k_chunk_scan_lds.h and k_chunk_scan_bf16.h).
+#include "k_chunk_scan_bf16.h"
 
 namespace cssd {
 template hipError_t launch_chunk_scan_c<128>(const FwdArgs& f, hipStream_t s);

@@ -322,15 +322,5 @@ hipError_t launch_staged_d(const FwdArgs& f, hipStream_t s) {
 
 // The LDS-staged kernel where its shape allows, the register-operand kernel
 // otherwise (and for bf16 inputs).
-template <int C>
-hipError_t launch_chunk_scan_c(const FwdArgs& f, hipStream_t s) {
-    if (f.in_dtype != 0) return launch_chunk_scan_regs<C>(f, s);
-    switch (f.N) {
-        case 16: return launch_staged_d<C, 16>(f, s);
-        case 32: return launch_staged_d<C, 32>(f, s);
-        case 64: return launch_staged_d<C, 64>(f, s);
-        default: return launch_staged_d<C, 128>(f, s);
-    }
-}
 
 }  // namespace cssd
