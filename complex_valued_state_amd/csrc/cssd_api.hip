@@ -594,7 +594,9 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
     a.T = seqlen;
     a.H = nheads;
     a.D = headdim;
-    a.nqb = (seqlen + 63) / 64;
+    // query blocks of 64 rows (fp32 kernel) or 128 rows (bf16 kernel)
+    const int64_t qrows = in_dtype == CSSD_F32 ? 64 : 128;
+    a.nqb = (seqlen + qrows - 1) / qrows;
     a.npair = (a.nqb + 1) / 2;
     // heads sharing one 128-byte line of a time step go to the same XCD
     const int64_t row_bytes = headdim * (in_dtype == CSSD_F32 ? 4 : 2);

@@ -58,7 +58,8 @@ struct PhaseArgs {
 };
 
 // Causal Born attention over (B, T, H, D) planar q, k, v.  nqb query blocks of
-// 64 rows per (b, h), taken in npair workgroups (blocks p and nqb - 1 - p);
+// 64 rows (fp32) or 128 rows (bf16) per (b, h), taken in npair workgroups
+// (blocks p and nqb - 1 - p);
 // hpl heads share one 128-byte line of a time step and go to the same XCD.
 struct BornArgs {
     int64_t B, T, H, D, nqb, npair, hpl;

@@ -264,13 +264,17 @@ __global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
     const uint16_t* vr_p = reinterpret_cast<const uint16_t*>(a.v_re);
     const uint16_t* vi_p = reinterpret_cast<const uint16_t*>(a.v_im);
 
+    // query blocks of 128 rows: wave w owns query tiles u = 0, 1 (rows 32w + 16u of
+    // the block), so every key and value operand read from LDS serves two score tiles
+    constexpr int QBR = 2 * kBornBlock;
     const int nblk = pair == a.nqb - 1 - pair ? 1 : 2;
     for (int which = 0; which < nblk; ++which) {
         const int64_t qb = which == 0 ? pair : a.nqb - 1 - pair;
-        const int64_t qrow = qb * kBornBlock + 16 * w + lr;
         // B operands: [qr quad, qi quad] and [-qr quad, qi quad], scaled by 1/sqrt(D tau)
-        bf16x8 bre[NM], bim[NM];
-        {
+        bf16x8 bre[2][NM], bim[2][NM];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t qrow = qb * QBR + 32 * w + 16 * u + lr;
             float scale = 0.f;
             int64_t o = 0;
             if (qrow < a.T) {
@@ -293,16 +297,20 @@ __global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
                     si[j] = (__bf16)fi;
                     nr[j] = (__bf16)(-fr);
                 }
-                bre[m] = cat8(sr, si);
-                bim[m] = cat8(nr, si);
+                bre[u][m] = cat8(sr, si);
+                bim[u][m] = cat8(nr, si);
             }
         }
-        floatx4 o[NCT];
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) o[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 o[2][NCT];
         // row sums of the rounded weights, as one more product with a column of ones:
-        // register r of lane j + 16g ends up with the sum for query 4g + r
-        floatx4 den4 = {0.f, 0.f, 0.f, 0.f};
+        // register r of lane j + 16g ends up with the sum for query 4g + r of the tile
+        floatx4 den4[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            den4[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) o[u][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
         const __bf16 one = (__bf16)1.0f;
         const bf16x8 ones = {one, one, one, one, one, one, one, one};
 
@@ -358,48 +366,66 @@ __global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
             }
         };
 
+        // key blocks of 64 up to the end of this query block
+        const int64_t nkb = 2 * qb + 2;
         fetch(0);
         __syncthreads();
         commit(0);
         __syncthreads();
-        for (int64_t kb = 0; kb <= qb; ++kb) {
+        for (int64_t kb = 0; kb < nkb; ++kb) {
             const int buf = kb & 1;
-            if (kb < qb) fetch(kb + 1);
-            const bool diag = kb == qb;
-            const int ntile = diag ? w + 1 : 4;
-            // score tiles: key 16t + 4g + r of query lr in register r
-            floatx4 sc[4];
+            if (kb + 1 < nkb) fetch(kb + 1);
+            // key tile t of this block starts kd = 64 kb + 16 t - (128 qb + 32 w + 16 u)
+            // rows after query tile u: kd < 0 unmasked, kd = 0 the diagonal tile, kd > 0 empty
+            const int64_t kd0 = 64 * kb - QBR * qb - 32 * w;
+            floatx4 sc[2][4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                sc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-                if (t >= ntile) continue;  // wave-uniform
-                floatx4 sre = {0.f, 0.f, 0.f, 0.f}, sim = {0.f, 0.f, 0.f, 0.f};
+                sc[0][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                sc[1][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (kd0 + 16 * t - 16 > 0) continue;  // empty for both query tiles (wave-uniform)
+                bf16x8 are[NM], aim[NM];
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
                     const int ko = (16 * t + lr) * KS + 16 * (4 * m + lg);
-                    const bf16x8 are = *reinterpret_cast<const bf16x8*>(&lds_k[buf][0][ko]);
-                    const bf16x8 aim = *reinterpret_cast<const bf16x8*>(&lds_k[buf][1][ko]);
-                    sre = __builtin_amdgcn_mfma_f32_16x16x32_bf16(are, bre[m], sre, 0, 0, 0);
-                    sim = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aim, bim[m], sim, 0, 0, 0);
+                    are[m] = *reinterpret_cast<const bf16x8*>(&lds_k[buf][0][ko]);
+                    aim[m] = *reinterpret_cast<const bf16x8*>(&lds_k[buf][1][ko]);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = sre[r] * sre[r] + sim[r] * sim[r];
-                    if (diag && 16 * t + 4 * lg + r > 16 * w + lr) v = 0.f;
-                    sc[t][r] = v;
+                for (int u = 0; u < 2; ++u) {
+                    const int64_t kd = kd0 + 16 * t - 16 * u;
+                    if (kd > 0) continue;  // wave-uniform
+                    floatx4 sre = {0.f, 0.f, 0.f, 0.f}, sim = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        sre = __builtin_amdgcn_mfma_f32_16x16x32_bf16(are[m], bre[u][m], sre, 0, 0, 0);
+                        sim = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aim[m], bim[u][m], sim, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float v = sre[r] * sre[r] + sim[r] * sim[r];
+                        if (kd == 0 && 4 * lg + r > lr) v = 0.f;
+                        sc[u][t][r] = v;
+                    }
                 }
             }
             // O += P . [vr | vi] over the 32-key steps (tiles 2s, 2s + 1)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                if (2 * s2 >= ntile) continue;  // wave-uniform
-                bf16x8 pa;
+                if (kd0 + 32 * s2 - 16 > 0) continue;  // both query tiles empty (wave-uniform)
+                bf16x8 pa[2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pa[j] = (__bf16)sc[2 * s2][j];
-                    pa[j + 4] = (__bf16)sc[2 * s2 + 1][j];
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pa[u][j] = (__bf16)sc[u][2 * s2][j];
+                        pa[u][j + 4] = (__bf16)sc[u][2 * s2 + 1][j];
+                    }
                 }
-                den4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, den4, 0, 0, 0);
+                const bool act1 = kd0 + 32 * s2 - 16 <= 0;  // query tile 1 sees this step
+                const bool act0 = kd0 + 32 * s2 <= 0;
+                if (act0) den4[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], ones, den4[0], 0, 0, 0);
+                if (act1) den4[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], ones, den4[1], 0, 0, 0);
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
                     const int col = 16 * c + lr;
@@ -407,24 +433,28 @@ __global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
                     const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * s2 + 4 * lg));
                     const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * s2 + 16 + 4 * lg));
                     const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-                    o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
+                    if (act0) o[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, o[0][c], 0, 0, 0);
+                    if (act1) o[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, o[1][c], 0, 0, 0);
                 }
             }
-            if (kb < qb) commit(buf ^ 1);
+            if (kb + 1 < nkb) commit(buf ^ 1);
             __syncthreads();
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int qloc = 4 * lg + r;
-            const float den = den4[r];
-            const int64_t row = qb * kBornBlock + 16 * w + qloc;
-            if (row >= a.T) continue;
-            const float inv = den != 0.f ? 1.f / den : 0.f;
-            const int64_t at = base + row * rs;
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-            for (int c = 0; c < NCT; ++c) {
-                float* dst = (16 * c) < D ? a.out_re : a.out_im;
-                dst[at + (16 * c) % D + lr] = o[c][r] * inv;
+            for (int r = 0; r < 4; ++r) {
+                const int qloc = 4 * lg + r;
+                const float den = den4[u][r];
+                const int64_t row = qb * QBR + 32 * w + 16 * u + qloc;
+                if (row >= a.T) continue;
+                const float inv = den != 0.f ? 1.f / den : 0.f;
+                const int64_t at = base + row * rs;
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    float* dst = (16 * c) < D ? a.out_re : a.out_im;
+                    dst[at + (16 * c) % D + lr] = o[u][c][r] * inv;
+                }
             }
         }
     }
