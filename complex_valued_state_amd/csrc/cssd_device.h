@@ -93,6 +93,10 @@ struct InF32 {
     __device__ __forceinline__ static floatx4 bload4(BufRes r, uint32_t e) {
         return buf_f32x4(r, e);
     }
+    // elements e, e + 1 (e even)
+    __device__ __forceinline__ static float2 bload2(BufRes r, uint32_t e) {
+        return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, e * 4u, 0, 0));
+    }
 };
 
 struct InBF16 {
@@ -114,6 +118,11 @@ struct InBF16 {
         const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, e * 2u, 0, 0));
         return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
                        __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+    }
+    // elements e, e + 1 (e even)
+    __device__ __forceinline__ static float2 bload2(BufRes r, uint32_t e) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, e * 2u, 0, 0);
+        return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
     }
 };
 

@@ -17,9 +17,15 @@
 // Mapping as in the chunk-state kernel: step j of the 16x16x4 MFMA contracts
 // time l = (C/4) g + j (g = lane/16); B and X are read with lane%16 along their
 // contiguous axis through per-chunk buffer views whose extent ends at the
-// chunk's last real row (padded rows read as zero).  The operands (B and X) of
-// the next DIST k-steps are kept in flight in a register ring that runs on
-// across chunk boundaries.  All workgroups of one (b, h) go to
+// chunk's last real row (padded rows read as zero).  For bf16 inputs with two
+// p tiles per wave a lane reads two adjacent X columns in one 4-byte load, so
+// a wave's X row segment is one 64-byte piece instead of two 32-byte ones;
+// tile q then holds the columns p = 16 pt0 + 2 (lane%16) + q, and each store
+// puts the values back in their fragment slots (measured at B8 T2048 H48 N64
+// D64 C64: 0.45 -> 0.42 ms, with 8 k-steps in flight).  For fp32 inputs the
+// paired 8-byte load measured slower (0.38 -> 0.41 ms) and is off.  The
+// operands (B and X) of the next DIST k-steps are kept in flight in a register
+// ring that runs on across chunk boundaries.  All workgroups of one (b, h) go to
 // the same XCD (dispatch is round-robin over the 8 XCDs), so the B and X rows
 // that several waves of that (b, h) read are fetched into one L2.
 #include "cssd_device.h"
@@ -30,6 +36,31 @@ namespace cssd {
 namespace {
 
 constexpr int kScanXcds = 8;
+
+// k-steps whose operands are in flight (a divisor of C/4), and whether a lane
+// reads two adjacent X columns in one load, per input type
+#ifndef CSSD_SCAN_DIST_F32
+#define CSSD_SCAN_DIST_F32 4
+#endif
+#ifndef CSSD_SCAN_DIST_BF16
+#define CSSD_SCAN_DIST_BF16 8
+#endif
+#ifndef CSSD_SCAN_PAIR_F32
+#define CSSD_SCAN_PAIR_F32 0
+#endif
+#ifndef CSSD_SCAN_PAIR_BF16
+#define CSSD_SCAN_PAIR_BF16 1
+#endif
+template <typename In>
+struct ScanTune {
+    static constexpr int dist = CSSD_SCAN_DIST_F32;
+    static constexpr bool pair = CSSD_SCAN_PAIR_F32;
+};
+template <>
+struct ScanTune<InBF16> {
+    static constexpr int dist = CSSD_SCAN_DIST_BF16;
+    static constexpr bool pair = CSSD_SCAN_PAIR_BF16;
+};
 
 }  // namespace
 
@@ -47,7 +78,8 @@ __global__ __launch_bounds__(256) void k_state_scan(
     float* __restrict__ st_im, float* __restrict__ hT_re, float* __restrict__ hT_im, int64_t T,
     int H, int N, int D, int nC, int64_t nbh) {
     constexpr int KJ = C / 4;  // MFMA k-steps per chunk
-    constexpr int DIST = 4;    // k-steps in flight (8 measured no faster, at more registers)
+    constexpr int DIST = ScanTune<In>::dist;
+    constexpr bool PAIR = PW == 2 && ScanTune<In>::pair;
     constexpr int RING = DIST < KJ ? DIST : KJ;
     constexpr int WPL = (C + 63) / 64;  // weights per lane and plane when loading a chunk's w
     __shared__ float lds_w[4][2 * C];  // per wave: w re, w im of the current chunk
@@ -76,15 +108,16 @@ __global__ __launch_bounds__(256) void k_state_scan(
     const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
     float* const lw = lds_w[wv];
 
-    // carried state, tile q register r <-> (n = 16 nt + 4g + r, p = 16 (pt0 + q) + li)
-    const int64_t sbase = (bh * N + nt * 16 + 4 * g) * (int64_t)D + pt0 * 16 + li;
+    // carried state, tile q register r <-> (n = 16 nt + 4g + r, p = pcol(q))
+    auto pcol = [&](int q) { return PAIR ? 16 * pt0 + 2 * li + q : 16 * (pt0 + q) + li; };
+    const int64_t sbase = (bh * N + nt * 16 + 4 * g) * (int64_t)D;
     float hr[PW][4], hi[PW][4];
 #pragma unroll
     for (int q = 0; q < PW; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            hr[q][r] = h0_re != nullptr ? h0_re[sbase + r * D + 16 * q] : 0.f;
-            hi[q][r] = h0_im != nullptr ? h0_im[sbase + r * D + 16 * q] : 0.f;
+            hr[q][r] = h0_re != nullptr ? h0_re[sbase + r * D + pcol(q)] : 0.f;
+            hi[q][r] = h0_im != nullptr ? h0_im[sbase + r * D + pcol(q)] : 0.f;
         }
 
     struct Ops {
@@ -103,10 +136,19 @@ __global__ __launch_bounds__(256) void k_state_scan(
         const uint32_t l = (uint32_t)(KJ * g + j);
         o.br = In::bload1(rb_r, l * sN + nt * 16 + li);
         o.bi = In::bload1(rb_i, l * sN + nt * 16 + li);
+        if constexpr (PAIR) {
+            const float2 vr = In::bload2(rx_r, l * sD + pt0 * 16 + 2 * li);
+            const float2 vi = In::bload2(rx_i, l * sD + pt0 * 16 + 2 * li);
+            o.xr[0] = vr.x;
+            o.xr[1] = vr.y;
+            o.xi[0] = vi.x;
+            o.xi[1] = vi.y;
+        } else {
 #pragma unroll
-        for (int q = 0; q < PW; ++q) {
-            o.xr[q] = In::bload1(rx_r, l * sD + (pt0 + q) * 16 + li);
-            o.xi[q] = In::bload1(rx_i, l * sD + (pt0 + q) * 16 + li);
+            for (int q = 0; q < PW; ++q) {
+                o.xr[q] = In::bload1(rx_r, l * sD + (pt0 + q) * 16 + li);
+                o.xi[q] = In::bload1(rx_i, l * sD + (pt0 + q) * 16 + li);
+            }
         }
     };
     // the weights of chunk c: lane takes positions lane + 64 k
@@ -126,16 +168,21 @@ __global__ __launch_bounds__(256) void k_state_scan(
     for (int j = 0; j < RING; ++j) load(0, j, ring[j]);
     load_w(0);
 
-    const int64_t slot = ((int64_t)nt * PT + pt0) * 256 + 4 * lane;  // within one chunk's N x D block
+    // tile q's place within one chunk's N x D block: fragment (nt, p/16), lane p%16 + 16g
+    // (with paired columns a tile's store covers every other 16-byte slot of two fragments)
+    int64_t slot[PW];
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+        slot[q] = ((int64_t)nt * PT + pcol(q) / 16) * 256 + 4 * (pcol(q) % 16 + 16 * g);
     for (int c = 0; c < nC; ++c) {
         // carry-in state of chunk c
         {
-            const int64_t off = (bh * nC + c) * (int64_t)N * D + slot;
+            const int64_t off = (bh * nC + c) * (int64_t)N * D;
 #pragma unroll
             for (int q = 0; q < PW; ++q) {
-                *reinterpret_cast<floatx4*>(st_re + off + 256 * q) =
+                *reinterpret_cast<floatx4*>(st_re + off + slot[q]) =
                     floatx4{hr[q][0], hr[q][1], hr[q][2], hr[q][3]};
-                *reinterpret_cast<floatx4*>(st_im + off + 256 * q) =
+                *reinterpret_cast<floatx4*>(st_im + off + slot[q]) =
                     floatx4{hi[q][0], hi[q][1], hi[q][2], hi[q][3]};
             }
         }
@@ -186,8 +233,8 @@ __global__ __launch_bounds__(256) void k_state_scan(
         for (int q = 0; q < PW; ++q)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                hT_re[sbase + r * D + 16 * q] = hr[q][r];
-                hT_im[sbase + r * D + 16 * q] = hi[q][r];
+                hT_re[sbase + r * D + pcol(q)] = hr[q][r];
+                hT_im[sbase + r * D + pcol(q)] = hi[q][r];
             }
     }
 }
