@@ -71,6 +71,7 @@ SMALL = [
     (1, 300, 2, 16, 128, 128, True, True, True),  # largest N and C
     (2, 50, 2, 128, 16, 32, False, True, True),   # largest D
     (3, 128, 2, 64, 64, 32, True, True, True),
+    (2, 200, 3, 64, 64, 64, True, True, True),    # N = D = C = 64, ragged tail
 ]
 
 

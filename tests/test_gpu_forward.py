@@ -47,6 +47,10 @@ SMALL = [
     (1, 190, 1, 128, 128, 128, True, True),  # largest everything, partial chunk
     (3, 128, 2, 64, 64, 32, True, True),
     (2, 130, 2, 32, 64, 64, True, True),     # two waves, five score tiles each, ragged tail
+    # N = D = 64, C = 64: the state scan staged through LDS
+    (1, 30, 1, 64, 64, 64, False, True),     # one chunk, shorter than a stage
+    (2, 200, 3, 64, 64, 64, True, True),     # ragged tail; fewer (b, h) than XCDs
+    (3, 320, 5, 64, 64, 64, True, False),    # whole chunks, 15 (b, h) over 8 XCDs
 ]
 
 
@@ -160,6 +164,7 @@ BF16_CASES = [
     (1, 130, 2, 64, 32, 64, False, True),
     (2, 70, 2, 32, 32, 64, True, True),
     (1, 33, 1, 64, 64, 64, False, True),     # one partial chunk
+    (3, 130, 5, 64, 64, 64, True, True),     # 15 (b, h) over the 8 XCDs, ragged tail
     (2, 100, 2, 32, 64, 32, True, True),     # register-operand kernel
 ]
 
