@@ -39,9 +39,11 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 # source files that make up each kernel (besides the shared device/launch headers),
 # by the kernel's name stem as rocprofv3 reports it
-_SCAN_SRC = ("k_chunk_scan.h", "k_chunk_scan_lds.h", "k_chunk_scan.hip", "k_chunk_scan_c16.hip",
-             "k_chunk_scan_c32.hip", "k_chunk_scan_c64.hip", "k_chunk_scan_c128.hip")
+_SCAN_SRC = ("k_chunk_scan.h", "k_chunk_scan_lds.h", "k_chunk_scan_bf16.h", "k_chunk_scan.hip",
+             "k_chunk_scan_c16.hip", "k_chunk_scan_c32.hip", "k_chunk_scan_c64.hip",
+             "k_chunk_scan_c128.hip")
 KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
+              "k_chunk_scan_bf16": _SCAN_SRC,
               "k_chunk_state": ("k_chunk_state.hip",), "k_state_pass": ("k_state_pass.hip",),
               "k_cumsum": ("k_cumsum.hip",), "k_step": ("k_step.hip",),
               "k_step_infinite": ("k_step.hip",),
@@ -49,7 +51,8 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_bwd_dz": ("k_backward.hip",), "k_bwd_reduce": ("k_backward.hip",),
               "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
               "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",),
-              "k_born_bf16": ("k_born.hip",), "k_state_scan": ("k_state_scan.hip",)}
+              "k_born_bf16": ("k_born.hip",), "k_state_scan": ("k_state_scan.hip",),
+              "k_state_scan_lds": ("k_state_scan.hip",)}
 
 
 # ---------------------------------------------------------------------------
