@@ -133,9 +133,12 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int6
     l.ddp = put(P * sizeof(float));
     l.hT_re = put(HS * sizeof(float));
     l.hT_im = put(HS * sizeof(float));
-    l.z_re = put((size_t)(B * H * nC) * sizeof(double));
-    l.z_im = put((size_t)(B * H * nC) * sizeof(double));
-    l.pa = put((size_t)(B * H) * 3 * sizeof(double));
+    // boundary terms of the log-decay gradient, two partials per chunk
+    l.z_re = put((size_t)(B * H * nC) * 2 * sizeof(double));
+    l.z_im = put((size_t)(B * H * nC) * 2 * sizeof(double));
+    // dA / dDskip partials: one per span of max(C, 64) positions of each (b, h)
+    const int64_t span = C > 64 ? C : 64;
+    l.pa = put((size_t)(B * H * ((nC * C + span - 1) / span)) * 3 * sizeof(double));
     l.total = off;
     return l;
 }
@@ -347,23 +350,35 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
         return CSSD_ERR_HIP;
     if (timed(cssd::K_STATE_SCAN, s, [&] { return cssd::launch_state_scan(a.f, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
-    // adjoint chunk states and the backward pass over chunks: R_{c+1}, dh0
-    if (timed(cssd::K_CHUNK_STATE, s, [&] {
-            return cssd::launch_chunk_state_adjoint(a.f, dy_re, dy_im, a.r_re, a.r_im, s);
-        }) != hipSuccess)
-        return CSSD_ERR_HIP;
-    if (timed(cssd::K_STATE_PASS, s, [&] {
-            return cssd::launch_state_pass_adjoint(a.f, a.r_re, a.r_im, dhT_re, dhT_im, dh0_re,
-                                                   dh0_im, s);
-        }) != hipSuccess)
-        return CSSD_ERR_HIP;
+    // adjoint chunk states and the backward pass over chunks: R_{c+1}, dh0 (and,
+    // where the two are fused, the boundary terms of the log-decay gradient)
+    const bool fused_adj = cssd::state_scan_adjoint_fused(a.f);
+    if (fused_adj) {
+        if (timed(cssd::K_STATE_SCAN_ADJ, s, [&] {
+                return cssd::launch_state_scan_adjoint(a.f, dy_re, dy_im, dhT_re, dhT_im, a.r_re,
+                                                       a.r_im, dh0_re, dh0_im, a.hT_re, a.hT_im,
+                                                       a.z_re, a.z_im, s);
+            }) != hipSuccess)
+            return CSSD_ERR_HIP;
+    } else {
+        if (timed(cssd::K_CHUNK_STATE, s, [&] {
+                return cssd::launch_chunk_state_adjoint(a.f, dy_re, dy_im, a.r_re, a.r_im, s);
+            }) != hipSuccess)
+            return CSSD_ERR_HIP;
+        if (timed(cssd::K_STATE_PASS, s, [&] {
+                return cssd::launch_state_pass_adjoint(a.f, a.r_re, a.r_im, dhT_re, dhT_im,
+                                                       dh0_re, dh0_im, s);
+            }) != hipSuccess)
+            return CSSD_ERR_HIP;
+    }
     if (timed(cssd::K_BWD_DX, s, [&] { return cssd::launch_bwd_dx(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     if (timed(cssd::K_BWD_DB, s, [&] { return cssd::launch_bwd_db(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     if (timed(cssd::K_BWD_DC, s, [&] { return cssd::launch_bwd_dc(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
-    if (timed(cssd::K_BWD_DZ, s, [&] { return cssd::launch_bwd_dz(a, s); }) != hipSuccess)
+    if (timed(cssd::K_BWD_DZ, s, [&] { return cssd::launch_bwd_dz(a, !fused_adj, s); }) !=
+        hipSuccess)
         return CSSD_ERR_HIP;
     return CSSD_OK;
 }
@@ -657,7 +672,7 @@ const char* cssd_kernel_name(int kernel_id) {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
         "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
         "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db",
-        "k_state_scan"};
+        "k_state_scan", "k_state_scan_adj"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

@@ -9,7 +9,7 @@ namespace cssd {
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
                 K_STEP_INFINITE = 5, K_BWD_DX = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
                 K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_BORN = 12,
-                K_BWD_DB = 13, K_STATE_SCAN = 14, K_COUNT = 15 };
+                K_BWD_DB = 13, K_STATE_SCAN = 14, K_STATE_SCAN_ADJ = 15, K_COUNT = 16 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -36,8 +36,8 @@ struct BwdArgs {
     float *q1_re, *q1_im, *q2_re, *q2_im;    // per position: the dx and y halves of q
     float *ddp;                              // per position: Re(dy . conj(x))
     float *hT_re, *hT_im;                    // final state of the recomputed forward
-    double *z_re, *z_im;                     // per chunk: <R_{c+1}, H_{c+1}>
-    double* pa;                              // per (b, h): dA re, dA im, dDskip
+    double *z_re, *z_im;                     // per chunk, two partials: <R_{c+1}, H_{c+1}>
+    double* pa;                              // per span of each (b, h): dA re, dA im, dDskip
 };
 
 struct StepArgs {
@@ -85,7 +85,16 @@ hipError_t launch_state_pass_adjoint(const FwdArgs& a, float* q_re, float* q_im,
 hipError_t launch_bwd_dx(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_db(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_dz(const BwdArgs& a, hipStream_t stream);
+// the adjoint chunk states and pass fused, with the log-decay boundary terms
+// (shapes for which state_scan_adjoint_fused holds; hipErrorNotSupported else)
+bool state_scan_adjoint_fused(const FwdArgs& a);
+hipError_t launch_state_scan_adjoint(const FwdArgs& a, const float* dy_re, const float* dy_im,
+                                     const float* dhT_re, const float* dhT_im, float* r_re,
+                                     float* r_im, float* dh0_re, float* dh0_im,
+                                     const float* hT_re, const float* hT_im, double* z_re,
+                                     double* z_im, hipStream_t stream);
+// with_zbound: compute the boundary terms <R_{c+1}, H_{c+1}> here (not yet done)
+hipError_t launch_bwd_dz(const BwdArgs& a, bool with_zbound, hipStream_t stream);
 hipError_t launch_step_infinite(const StepArgs& a, hipStream_t stream);
 hipError_t launch_phase_summary(const PhaseArgs& a, hipStream_t stream);
 hipError_t launch_phase_carry(const PhaseArgs& a, hipStream_t stream);

@@ -485,7 +485,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves(C, N, D, PART)))) void k_bwd_tiles(
 }
 
 // ----------------------------------------------------------------------------
-// Z[c] = <R_{c+1}, H_{c+1}>: the tail of the log-decay gradient sum past chunk c.
+// Z[c] = <R_{c+1}, H_{c+1}>: the tail of the log-decay gradient sum past chunk c,
+// stored as two partials per chunk (the fused adjoint scan writes one per half
+// of the n rows; this kernel writes the whole term and a zero).
 // R_{c+1} is slot c of the adjoint buffer, H_{c+1} slot c + 1 of the carry-in
 // states (both MFMA-fragment order); for the last chunk it is <dhT, hT> (both in
 // the caller's layout), or 0 without dhT.  One wave per (b, h, c), fp64 sums.
@@ -533,32 +535,46 @@ __global__ __launch_bounds__(256) void k_bwd_zbound(BwdArgs a) {
             zi += __shfl_xor(zi, off, 64);
         }
     }
-    if (lane == 0) {
-        a.z_re[chunk] = zr;
-        a.z_im[chunk] = zi;
+    if (lane == 0) {  // the whole term in the first of the chunk's two partials
+        a.z_re[2 * chunk] = zr;
+        a.z_im[2 * chunk] = zi;
+        a.z_re[2 * chunk + 1] = 0.0;
+        a.z_im[2 * chunk + 1] = 0.0;
     }
 }
 
 // ----------------------------------------------------------------------------
-// dz_t = (suffix sum of q within chunk c) + Z[c]  ->  ddt, and per-(b, h)
-// partials of dA and dDskip.  One wave per (b, h); positions are walked from
-// the end in blocks of 64.  A chunk of 16 or 32 positions lies inside one
-// block (segmented suffix sum); a chunk of 128 spans two blocks, and its tail
-// carries from the later block to the earlier one.
+// dz_t = (suffix sum of q within chunk c) + Z[c]  ->  ddt, and partials of dA
+// and dDskip.  The sum never crosses a chunk boundary, so the positions of one
+// (b, h) are cut into spans of max(C, 64) whole chunks, one wave each (the
+// partials of every span are kept apart and summed later in a fixed order).
+// A wave walks its span from the end in blocks of 64: a chunk of 16 or 32
+// positions lies inside one block (segmented suffix sum); a chunk of 128 spans
+// two blocks, and its tail carries from the later block to the earlier one.
 // ----------------------------------------------------------------------------
+__host__ __device__ inline int64_t dz_span(int64_t C) { return C > 64 ? C : 64; }
+__host__ __device__ inline int64_t dz_spans(int64_t nC, int64_t C) {
+    return (nC * C + dz_span(C) - 1) / dz_span(C);
+}
+
 __global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a) {
     const FwdArgs& f = a.f;
-    const int64_t bh = (int64_t)blockIdx.x * 4 + wave_id();
-    if (bh >= f.B * f.H) return;  // wave-uniform
+    const int64_t C = f.C, S = dz_span(C), nsp = dz_spans(f.nC, C);
+    const int64_t unit = (int64_t)blockIdx.x * 4 + wave_id();
+    if (unit >= f.B * f.H * nsp) return;  // wave-uniform
+    const int64_t bh = unit / nsp, sp = unit % nsp;
     const int lane = threadIdx.x & 63;
     const int h = (int)(bh % f.H);
     const int64_t b = bh / f.H;
-    const int64_t C = f.C;
     const double Ar = f.a_re[h], Ai = f.a_im[h];
     const int64_t pb = bh * f.nC * C;
     double gar = 0.0, gai = 0.0, gd = 0.0;
     double tail_r = 0.0, tail_i = 0.0;  // q of the current chunk in later blocks
-    for (int64_t blk = (f.T - 1) / 64; blk >= 0; --blk) {
+    // the span starts and ends on chunk boundaries, and it holds at least one
+    // position t < T (its first position is a chunk start before nC C)
+    const int64_t blk_first = sp * S / 64;
+    const int64_t blk_last = min((sp * S + S) / 64 - 1, (f.T - 1) / 64);
+    for (int64_t blk = blk_last; blk >= blk_first; --blk) {
         const int64_t t = blk * 64 + lane;
         double sr = 0.0, si = 0.0;
         if (t < f.T) {
@@ -580,8 +596,11 @@ __global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a) {
         // next block (C = 128); its later positions are in tail
         const int64_t c_last = (blk * 64 + 63) / C;
         const bool straddles = (c_last + 1) * C > blk * 64 + 64;
-        const double cr = (ct == c_last && straddles ? tail_r : 0.0) + a.z_re[bh * f.nC + ct];
-        const double ci = (ct == c_last && straddles ? tail_i : 0.0) + a.z_im[bh * f.nC + ct];
+        // (lanes past T may sit in a chunk past the last one: clamp their read)
+        const int64_t cz = min(ct, (int64_t)f.nC - 1);
+        const int64_t zk = 2 * (bh * f.nC + cz);
+        const double cr = (ct == c_last && straddles ? tail_r : 0.0) + (a.z_re[zk] + a.z_re[zk + 1]);
+        const double ci = (ct == c_last && straddles ? tail_i : 0.0) + (a.z_im[zk] + a.z_im[zk + 1]);
         if (t < f.T) {
             const double zr = sr + cr, zi = si + ci;
             const int64_t row = (b * f.T + t) * f.H + h;
@@ -611,22 +630,25 @@ __global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a) {
         gd += __shfl_xor(gd, off, 64);
     }
     if (lane == 0) {
-        a.pa[3 * bh] = gar;
-        a.pa[3 * bh + 1] = gai;
-        a.pa[3 * bh + 2] = gd;
+        a.pa[3 * unit] = gar;
+        a.pa[3 * unit + 1] = gai;
+        a.pa[3 * unit + 2] = gd;
     }
 }
 
-// dA[h], dDskip[h]: the per-(b, h) partials summed over b in a fixed order.
+// dA[h], dDskip[h]: the per-span partials summed over b and the spans in a fixed order.
 __global__ __launch_bounds__(256) void k_bwd_reduce(BwdArgs a) {
     const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (h >= a.f.H) return;
+    const int64_t nsp = dz_spans(a.f.nC, a.f.C);
     double sr = 0.0, si = 0.0, sd = 0.0;
-    for (int64_t b = 0; b < a.f.B; ++b) {
-        sr += a.pa[3 * (b * a.f.H + h)];
-        si += a.pa[3 * (b * a.f.H + h) + 1];
-        sd += a.pa[3 * (b * a.f.H + h) + 2];
-    }
+    for (int64_t b = 0; b < a.f.B; ++b)
+        for (int64_t sp = 0; sp < nsp; ++sp) {
+            const int64_t u = (b * a.f.H + h) * nsp + sp;
+            sr += a.pa[3 * u];
+            si += a.pa[3 * u + 1];
+            sd += a.pa[3 * u + 2];
+        }
     a.da_re[h] = (float)sr;
     a.da_im[h] = (float)si;
     if (a.dd != nullptr) a.dd[h] = (float)sd;
@@ -671,12 +693,15 @@ hipError_t launch_bwd_dx(const BwdArgs& a, hipStream_t s) { return launch_tiles<
 hipError_t launch_bwd_db(const BwdArgs& a, hipStream_t s) { return launch_tiles<1>(a, s); }
 hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s) { return launch_tiles<2>(a, s); }
 
-hipError_t launch_bwd_dz(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_dz(const BwdArgs& a, bool with_zbound, hipStream_t s) {
     const int64_t nchunks = a.f.B * a.f.H * a.f.nC;
-    hipLaunchKernelGGL(k_bwd_zbound, dim3((unsigned)((nchunks + 3) / 4)), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t units = a.f.B * a.f.H;
+    hipError_t e;
+    if (with_zbound) {
+        hipLaunchKernelGGL(k_bwd_zbound, dim3((unsigned)((nchunks + 3) / 4)), dim3(256), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t units = a.f.B * a.f.H * dz_spans(a.f.nC, a.f.C);
     hipLaunchKernelGGL(k_bwd_dz, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

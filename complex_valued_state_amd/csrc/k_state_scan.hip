@@ -261,7 +261,20 @@ __device__ __forceinline__ int swz_b(int r) { return 4 * (((r >> 1) ^ r) & 1); }
 __device__ __forceinline__ int swz_x(int r) { return 4 * (r & 3); }               // X rows: 16 units
 }  // namespace
 
-template <typename In>
+// The adjoint mode (ADJ) serves the gradient pass: with B -> C, X -> dY and
+// w -> e it walks the chunks from the last to the first,
+//   R_nC = dhT (or 0);  Q_c = C^H diag(conj e) dY;  R_c = Q_c + conj(cd[c]) R_{c+1},
+// stores R_{c+1} in slot c and R_0 = dh0, and with R_{c+1} in registers also
+// forms the log-decay gradient's boundary term <R_{c+1}, H_{c+1}> (the forward
+// state entering chunk c + 1, or hT after the last chunk), one fp64 partial per
+// workgroup (half of the n rows) and chunk.
+struct AdjExtra {
+    const float *hs_re, *hs_im;  // forward carry-in states H_c, fragment order
+    const float *hT_re, *hT_im;  // forward final state (caller's layout), or NULL
+    double *z_re, *z_im;         // [(b, h, c) * 2 + half]
+};
+
+template <typename In, bool ADJ>
 __global__ __launch_bounds__(256) void k_state_scan_lds(
     const typename In::T* __restrict__ x_re, const typename In::T* __restrict__ x_im,
     const typename In::T* __restrict__ b_re, const typename In::T* __restrict__ b_im,
@@ -269,13 +282,14 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
     const float* __restrict__ cd_re, const float* __restrict__ cd_im,
     const float* __restrict__ h0_re, const float* __restrict__ h0_im, float* __restrict__ st_re,
     float* __restrict__ st_im, float* __restrict__ hT_re, float* __restrict__ hT_im, int64_t T,
-    int H, int nC, int64_t nbh) {
+    int H, int nC, int64_t nbh, AdjExtra adj) {
     constexpr int C = 64, N = 64, D = 64, PT = D / 16;
     constexpr int NS = C / kSR;  // stages per chunk
     constexpr int KS = kSR / 4;  // k-steps per stage
     __shared__ floatx4 sb[2][2][kSR * 8];   // [buffer][plane][row * 8 + unit]: 32 B columns per row
     __shared__ floatx4 sx[2][2][kSR * 16];  // [buffer][plane][row * 16 + unit]: all 64 X columns
     __shared__ float lds_w[4][2 * C];
+    __shared__ double lds_z[4][2];  // ADJ: per-wave partials of the boundary term
     const int tid = threadIdx.x, lane = tid & 63;
     const int li = lane & 15, g = lane >> 4;
     const int wv = wave_id();
@@ -315,8 +329,10 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
     // bf16: B plane wv / 2, row (tid / 4) % 32, 8-value unit tid % 4; X row tid / 8, unit tid % 8
     const int rb = kBF16 ? (tid >> 2) & 31 : tid >> 3, ub = kBF16 ? tid & 3 : tid & 7;
     const int pb = wv >> 1;  // bf16: the B plane this wave fetches (wave-uniform)
+    // the chunk of stage qs (the adjoint walks the chunks backwards)
+    auto chunk_of = [&](int qs) { return ADJ ? nC - 1 - qs / NS : qs / NS; };
     auto gload = [&](int qs, StageIn& R) {
-        const int c = qs / NS, s = qs % NS;
+        const int c = chunk_of(qs), s = qs % NS;
         const int64_t t0 = (int64_t)c * C;
         const int valid = (int)min<int64_t>((int64_t)C, T - t0);
         const int64_t row0 = (b * T + t0) * H + h;
@@ -396,10 +412,18 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
     // stage qs: Rx holds stage qs + 1, and its registers are then refilled with
     // stage qs + 3 (two stages are in flight in registers, one in each set)
     auto body = [&](int qs, StageIn& Rx) {
-        const int c = qs / NS, s = qs % NS, buf = qs & 1;
+        const int c = chunk_of(qs), s = qs % NS, buf = qs & 1;
         __syncthreads();  // stage qs is in LDS; nobody reads the other buffer any more
         if (qs + 1 < total) lstore(buf ^ 1, Rx);
         if (qs + 3 < total) gload(qs + 3, Rx);
+        if constexpr (ADJ) {
+            // the partials written at this chunk's first stage are visible now
+            if (s == 1 && tid == 0) {
+                const int64_t zi = (bh * nC + c) * 2 + h2;
+                adj.z_re[zi] = (lds_z[0][0] + lds_z[1][0]) + (lds_z[2][0] + lds_z[3][0]);
+                adj.z_im[zi] = (lds_z[0][1] + lds_z[1][1]) + (lds_z[2][1] + lds_z[3][1]);
+            }
+        }
         if (s == 0) {
             const int64_t off = (bh * nC + c) * (int64_t)N * D + slot;
 #pragma unroll
@@ -409,9 +433,52 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
                 *reinterpret_cast<floatx4*>(st_im + off + 256 * q) =
                     floatx4{hi[q][0], hi[q][1], hi[q][2], hi[q][3]};
             }
+            if constexpr (ADJ) {
+                // <R_{c+1}, H_{c+1}> over this wave's two tiles, in fp64
+                float vr[2][4], vi[2][4];
+                if (c + 1 < nC) {
+                    const int64_t hoff = (bh * nC + c + 1) * (int64_t)N * D + slot;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const floatx4 ur = *reinterpret_cast<const floatx4*>(adj.hs_re + hoff + 256 * q);
+                        const floatx4 ui = *reinterpret_cast<const floatx4*>(adj.hs_im + hoff + 256 * q);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            vr[q][r] = ur[r];
+                            vi[q][r] = ui[r];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool has = adj.hT_re != nullptr && h0_re != nullptr;
+                            vr[q][r] = has ? adj.hT_re[sbase + r * D + 16 * q] : 0.f;
+                            vi[q][r] = has ? adj.hT_im[sbase + r * D + 16 * q] : 0.f;
+                        }
+                }
+                double zr = 0.0, zi = 0.0;
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        zr += (double)hr[q][r] * vr[q][r] + (double)hi[q][r] * vi[q][r];
+                        zi += (double)hi[q][r] * vr[q][r] - (double)hr[q][r] * vi[q][r];
+                    }
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) {
+                    zr += __shfl_xor(zr, off, 64);
+                    zi += __shfl_xor(zi, off, 64);
+                }
+                if (lane == 0) {
+                    lds_z[wv][0] = zr;
+                    lds_z[wv][1] = zi;
+                }
+            }
             lw[lane] = wn_r;
             lw[C + lane] = wn_i;
-            if (c + 1 < nC) load_w(c + 1);
+            if (ADJ ? c > 0 : c + 1 < nC) load_w(ADJ ? c - 1 : c + 1);
 #pragma unroll
             for (int q = 0; q < 2; ++q) ctile_zero(acc[q]);
         }
@@ -424,8 +491,8 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
             const int l = s * kSR + 4 * j + g;
             const float wr = lw[l], wi = lw[C + l];
             const float br = pb_r[128 * j], bi = pb_i[128 * j];
-            const float pr = wr * br - wi * bi;  // (w B)[l, n]
-            const float pi = wr * bi + wi * br;
+            const float pr = wr * br - wi * bi;  // (w B)[l, n], conjugated in the adjoint
+            const float pi = ADJ ? -(wr * bi + wi * br) : wr * bi + wi * br;
             const float ps = pr + pi;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -434,7 +501,7 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
             }
         }
         if (s == NS - 1) {
-            const float dr = cd_re[bh * nC + c], di = cd_im[bh * nC + c];
+            const float dr = cd_re[bh * nC + c], di = ADJ ? -cd_im[bh * nC + c] : cd_im[bh * nC + c];
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -446,7 +513,7 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
                 }
         }
     };
-    load_w(0);
+    load_w(ADJ ? nC - 1 : 0);
     StageIn R0, R1;
     gload(0, R0);
     lstore(0, R0);
@@ -472,11 +539,33 @@ static hipError_t launch_scan_lds(const FwdArgs& a, hipStream_t s) {
     const int64_t nbh = a.B * a.H;
     const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * 2;
     typedef const typename In::T* P;
-    hipLaunchKernelGGL(k_state_scan_lds<In>, dim3((unsigned)blocks), dim3(256), 0, s,
+    const AdjExtra none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    hipLaunchKernelGGL((k_state_scan_lds<In, false>), dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<P>(a.x_re), static_cast<P>(a.x_im), static_cast<P>(a.b_re),
                        static_cast<P>(a.b_im),
                        a.w_re, a.w_im, a.cd_re, a.cd_im, a.h0_re, a.h0_im, a.st_re, a.st_im,
-                       a.hT_re, a.hT_im, a.T, (int)a.H, (int)a.nC, nbh);
+                       a.hT_re, a.hT_im, a.T, (int)a.H, (int)a.nC, nbh, none);
+    return hipGetLastError();
+}
+
+bool state_scan_adjoint_fused(const FwdArgs& a) {
+    return a.in_dtype == 0 && a.C == 64 && a.N == 64 && a.D == 64;
+}
+
+hipError_t launch_state_scan_adjoint(const FwdArgs& a, const float* dy_re, const float* dy_im,
+                                     const float* dhT_re, const float* dhT_im, float* r_re,
+                                     float* r_im, float* dh0_re, float* dh0_im,
+                                     const float* hT_re, const float* hT_im, double* z_re,
+                                     double* z_im, hipStream_t s) {
+    if (!state_scan_adjoint_fused(a)) return hipErrorNotSupported;
+    const int64_t nbh = a.B * a.H;
+    const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * 2;
+    const AdjExtra adj = {a.st_re, a.st_im, hT_re, hT_im, z_re, z_im};
+    hipLaunchKernelGGL((k_state_scan_lds<InF32, true>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       dy_re, dy_im, static_cast<const float*>(a.c_re),
+                       static_cast<const float*>(a.c_im), a.e_re, a.e_im, a.cd_re, a.cd_im,
+                       dhT_re, dhT_im, r_re, r_im, dh0_re, dh0_im, a.T, (int)a.H, (int)a.nC, nbh,
+                       adj);
     return hipGetLastError();
 }
 

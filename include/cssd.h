@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 104 /* major*100 + minor */
+#define CSSD_VERSION 105 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
@@ -356,7 +356,8 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
  * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite,
  * 14 state_scan (cssd_forward: the chunk states fused with the state pass),
  * 6 bwd_dx, 7 bwd_dc, 8 bwd_dz, 13 bwd_db (cssd_backward also runs ids 0 and 14,
- * and 1 and 2 in their adjoint modes), 9 phase_summary,
+ * then 15 state_scan_adj, the adjoint chunk states and pass fused, where
+ * dstate = headdim = chunk = 64, else 1 and 2 in their adjoint modes), 9 phase_summary,
  * 10 phase_carry, 11 phase_out (cssd_phase_scan), 12 born (cssd_born_attention).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).

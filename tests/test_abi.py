@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 104
+    assert lib.cssd_version() == 105
     for st in range(5):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -255,8 +255,9 @@ def test_profiler_without_launches(lib):
         pass
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
-    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(15) is None
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(16) is None
     assert lib.cssd_kernel_name(14) == b"k_state_scan"
+    assert lib.cssd_kernel_name(15) == b"k_state_scan_adj"
     assert lib.cssd_kernel_name(13) == b"k_bwd_db" and lib.cssd_kernel_name(6) == b"k_bwd_dx"
     assert lib.cssd_kernel_name(12) == b"k_born"
     assert lib.cssd_kernel_name(5) == b"k_step_infinite"

@@ -71,7 +71,9 @@ SMALL = [
     (1, 300, 2, 16, 128, 128, True, True, True),  # largest N and C
     (2, 50, 2, 128, 16, 32, False, True, True),   # largest D
     (3, 128, 2, 64, 64, 32, True, True, True),
-    (2, 200, 3, 64, 64, 64, True, True, True),    # N = D = C = 64, ragged tail
+    (2, 200, 3, 64, 64, 64, True, True, True),    # N = D = C = 64 (fused adjoint pass), ragged tail
+    (1, 64, 2, 64, 64, 64, False, True, False),   # the same, one chunk, no dhT
+    (3, 190, 3, 64, 64, 64, True, False, False),  # the same, no dhT, 9 (b, h) over 8 XCDs
 ]
 
 
