@@ -45,6 +45,7 @@
 // transposed products that contract over p.
 #include "cssd_device.h"
 #include "cssd_launch.h"
+#include "k_chunk_scan_lds.h"
 
 namespace cssd {
 
@@ -313,6 +314,298 @@ __device__ __forceinline__ void dxdb_tile(const BwdArgs& a, int64_t chunk, int l
     }
 }
 
+// ----------------------------------------------------------------------------
+// dX for N = D = C = 64 with the chunk's rows staged through LDS (the forward
+// chunk-scan kernel's organisation): one workgroup of four waves per chunk, wave
+// w owning the output columns p in [16 w, 16 w + 16) of every row l.
+//  0. the chunk's C and B rows (both planes) go to LDS by direct-to-LDS loads
+//     (16-byte pieces, XOR-swizzled by row as in the forward kernel), with the
+//     fp64 cumsums and w; each wave loads its column block of R_{c+1}
+//     (fragment order) and of dY into registers.
+//  1. state term: conj(B) R_{c+1} on the wave's columns, rows scaled by conj(w[l]).
+//  2. the ten causal 16 x 16 tiles (t tile >= l tile) of G = C B^T are split over
+//     the waves; M' = conj(G . L) comes out with register r holding
+//     [l = l0 + lane%16][t = t0 + 4 (lane/16) + r], the A-operand layout of the
+//     product with dY rows; the tiles are exchanged through LDS (over the C rows).
+//  3. dX[l, p] += sum_t M'[l, t] dY[t, p] on the wave's columns, then the skip
+//     term D dY, and q1[l] = -sum_p conj(x[l, p]) dx[l, p] (before the skip),
+//     summed over the four waves' columns through LDS.
+// Each operand row is fetched from memory once per chunk (the tile kernel read
+// C and dY rows once per row tile it served, and R twice per wave).
+// ----------------------------------------------------------------------------
+template <bool DX>
+__global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
+    constexpr int C = 64, N = 64, D = 64, NK = N / 16, W = D / 16, NLT = C / 16;
+    static_assert(N == D, "the two staged row sets share one row width");
+    constexpr int NP = NLT * (NLT + 1) / 2;  // causal tiles (tt >= lt), tt-major
+    constexpr int MQ = (NP + W - 1) / W;
+    constexpr int PLANE = C * N, IPP = PLANE / 256;
+    static_assert(NP * 512 <= 2 * PLANE, "the M tiles must fit over the first row set");
+    // dX: C rows (scores' A operand), later the M tiles; B rows
+    // dB: dY rows (scores' A operand), later the M tiles; X rows
+    __shared__ floatx4 lds_s4[2 * PLANE / 4];
+    __shared__ floatx4 lds_o4[2 * PLANE / 4];  // later the q1 partials (dX)
+    __shared__ floatx4 lds_a4[1024 / 4];       // acs re, acs im (fp64), w re, w im
+    float* const lds_s = reinterpret_cast<float*>(lds_s4);
+    float* const lds_o = reinterpret_cast<float*>(lds_o4);
+    float* const lda = reinterpret_cast<float*>(lds_a4);
+    const double* const lacs_r = reinterpret_cast<const double*>(lda);
+    const double* const lacs_i = reinterpret_cast<const double*>(lda + 256);
+    const float* const lw_r = lda + 512;
+    const float* const lw_i = lda + 768;
+
+    const FwdArgs& f = a.f;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int w = wave_id();
+    const int64_t chunk = blockIdx.x;
+    const ChunkView v = chunk_view(a, chunk, C, N, D);
+
+    // ---- 0. staging
+    auto stage_plane = [&](const void* src, float* dst_plane, int first) {
+        const BufRes r = make_buf(static_cast<const float*>(src) + v.row0 * N, v.extN * 4);
+        for (int blk = (w - first + W) % W; blk < IPP; blk += W) {  // wave-uniform
+            const int u = blk * 64 + lane;  // physical 16-byte piece within the plane
+            const int row = u / (N / 4), pc = u % (N / 4);
+            const uint32_t voff = ((uint32_t)row * v.sN + 4 * lds_swz<N>(row, pc)) * 4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(dst_plane + blk * 256), 16, voff,
+                                                     0, 0, 0);
+        }
+    };
+    stage_plane(DX ? f.c_re : a.dy_re, lds_s, 0);
+    stage_plane(DX ? f.c_im : a.dy_im, lds_s + PLANE, IPP % W);
+    stage_plane(DX ? f.b_re : f.x_re, lds_o, (2 * IPP) % W);
+    stage_plane(DX ? f.b_im : f.x_im, lds_o + PLANE, (3 * IPP) % W);
+    if (w == W - 1) {
+        const void* const aux[4] = {f.acs_re + v.pbase, f.acs_im + v.pbase, f.w_re + v.pbase,
+                                    f.w_im + v.pbase};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_buf(aux[j], (j < 2 ? 8 : 4) * C),
+                                                     (LdsPtr)(lda + 256 * j), 16, 16 * lane,
+                                                     0, 0, 0);
+    }
+    const BufRes rr_r = make_buf(a.r_re + chunk * (int64_t)N * D, N * D * 4);
+    const BufRes rr_i = make_buf(a.r_im + chunk * (int64_t)N * D, N * D * 4);
+    // the state term's B operand: R_{c+1}[16k + 4g + e][16w + li] (dX, over n) or
+    // R_{c+1}[16w + li][16k + 4g + e] (dB, over p, element-wise from the fragments)
+    floatx4 rreg_r[NK], rreg_i[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        if constexpr (DX) {
+            rreg_r[k] = buf_f32x4(rr_r, (uint32_t)(k * W + w) * 256 + 4 * lane);
+            rreg_i[k] = buf_f32x4(rr_i, (uint32_t)(k * W + w) * 256 + 4 * lane);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t fi = frag_index<D>(16 * w + li, 16 * k + 4 * g + e);
+                rreg_r[k][e] = buf_f32(rr_r, fi);
+                rreg_i[k][e] = buf_f32(rr_i, fi);
+            }
+        }
+    }
+    // the causal product's B operand, rows 16 tt + 4g + r, column 16w + li:
+    // dY (dX; also the skip term) or conj(C) (dB)
+    const BufRes rg_r = DX ? make_buf(a.dy_re + v.row0 * D, v.extD * 4)
+                           : make_buf(static_cast<const float*>(f.c_re) + v.row0 * N, v.extN * 4);
+    const BufRes rg_i = DX ? make_buf(a.dy_im + v.row0 * D, v.extD * 4)
+                           : make_buf(static_cast<const float*>(f.c_im) + v.row0 * N, v.extN * 4);
+    float gy_r[NLT][4], gy_i[NLT][4];
+#pragma unroll
+    for (int tt = 0; tt < NLT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (uint32_t)(tt * 16 + 4 * g + r) * (DX ? v.sD : v.sN) + 16 * w + li;
+            gy_r[tt][r] = buf_f32(rg_r, off);
+            gy_i[tt][r] = DX ? buf_f32(rg_i, off) : -buf_f32(rg_i, off);
+        }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+
+    auto row4 = [&](const float* plane, int row, int ch) -> floatx4 {
+        return *reinterpret_cast<const floatx4*>(plane + row * N + 4 * lds_swz<N>(row, ch));
+    };
+
+    // ---- 1. state term conj(B[l]) R (dX) or conj(X[l]) R^T (dB), then the row
+    // factor conj(w[l])
+    CTile acc[NLT];
+#pragma unroll
+    for (int lt = 0; lt < NLT; ++lt) ctile_zero(acc[lt]);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        const floatx4 rr = rreg_r[k], ri = rreg_i[k], rs = rr + ri;
+#pragma unroll
+        for (int lt = 0; lt < NLT; ++lt) {
+            const floatx4 br = row4(lds_o, lt * 16 + li, 4 * k + g);
+            const floatx4 bi = -row4(lds_o + PLANE, lt * 16 + li, 4 * k + g);
+            const floatx4 bs = br + bi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ctile_mac(acc[lt], br[e], bi[e], bs[e], rr[e], ri[e], rs[e]);
+        }
+    }
+#pragma unroll
+    for (int lt = 0; lt < NLT; ++lt) {
+        const floatx4 wr = *reinterpret_cast<const floatx4*>(lw_r + lt * 16 + 4 * g);
+        const floatx4 wi = *reinterpret_cast<const floatx4*>(lw_i + lt * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ctile_scale(acc[lt], r, wr[r], -wi[r]);
+    }
+
+    // ---- 2. score tiles q in [q0, q1) -> M in registers:
+    // dX: G = C B^T, M = conj(G L);  dB: P = dY X^H, M = conj(L) P
+    const int q0 = (w * NP) / W, q1 = ((w + 1) * NP) / W;
+    floatx4 m_r[MQ], m_i[MQ];
+    {
+        int tt = 0, lt = q0;  // tt-major decode of q0
+        while (lt > tt) {
+            lt -= tt + 1;
+            ++tt;
+        }
+#pragma unroll
+        for (int j = 0; j < MQ; ++j) {
+            if (q0 + j < q1) {  // wave-uniform
+                const int t0 = tt * 16, l0 = lt * 16;
+                CTile sq;
+                ctile_zero(sq);
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
+                    const floatx4 cr = row4(lds_s, t0 + li, 4 * k + g);
+                    const floatx4 ci = row4(lds_s + PLANE, t0 + li, 4 * k + g);
+                    const floatx4 br = row4(lds_o, l0 + li, 4 * k + g);
+                    const floatx4 bi0 = row4(lds_o + PLANE, l0 + li, 4 * k + g);
+                    const floatx4 bi = DX ? bi0 : -bi0;
+                    const floatx4 cs = cr + ci, bs = br + bi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ctile_mac(sq, cr[e], ci[e], cs[e], br[e], bi[e], bs[e]);
+                }
+                // register r <-> (t = t0 + 4g + r, l = l0 + li)
+                const int l = l0 + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = t0 + 4 * g + r;
+                    float lr = 0.f, lim = 0.f;
+                    if (tt > lt || t >= l) seg_exp(lacs_r, lacs_i, t, l, false, lr, lim);
+                    const float s_r = ctile_re(sq, r), s_i = ctile_im(sq, r);
+                    if constexpr (DX) {
+                        m_r[j][r] = s_r * lr - s_i * lim;  // conj(G L)
+                        m_i[j][r] = -(s_r * lim + s_i * lr);
+                    } else {
+                        m_r[j][r] = lr * s_r + lim * s_i;  // conj(L) P
+                        m_i[j][r] = lr * s_i - lim * s_r;
+                    }
+                }
+                if (++lt > tt) {
+                    lt = 0;
+                    ++tt;
+                }
+            }
+        }
+    }
+
+    // ---- the M tiles replace the first row set
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < MQ; ++j) {
+        if (q0 + j < q1) {
+            const int q = q0 + j;
+            *reinterpret_cast<floatx4*>(lds_s + (2 * q) * 256 + 4 * lane) = m_r[j];
+            *reinterpret_cast<floatx4*>(lds_s + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
+        }
+    }
+    __syncthreads();
+
+    // dX: x[16 lt + 4g + r][16w + li] for q1, in flight during the products below
+    // (loaded only at the stores, its latency was not hidden: 0.79 -> 0.62 ms)
+    const BufRes rx_r = make_buf(static_cast<const float*>(f.x_re) + v.row0 * D, v.extD * 4);
+    const BufRes rx_i = make_buf(static_cast<const float*>(f.x_im) + v.row0 * D, v.extD * 4);
+    float xb_r[NLT][4], xb_i[NLT][4];
+    if constexpr (DX) {
+#pragma unroll
+        for (int lt = 0; lt < NLT; ++lt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t off = (uint32_t)(lt * 16 + 4 * g + r) * v.sD + 16 * w + li;
+                xb_r[lt][r] = buf_f32(rx_r, off);
+                xb_i[lt][r] = buf_f32(rx_i, off);
+            }
+    }
+
+    // ---- 3. out[lt] += M(lt, tt) . (dY or conj C)[tt rows, this wave's columns], tt >= lt
+#pragma unroll
+    for (int tt = 0; tt < NLT; ++tt) {
+        float ys[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ys[r] = gy_r[tt][r] + gy_i[tt][r];
+#pragma unroll
+        for (int lt = 0; lt <= tt; ++lt) {
+            const int q = tt * (tt + 1) / 2 + lt;
+            const floatx4 mr = *reinterpret_cast<const floatx4*>(lds_s + (2 * q) * 256 + 4 * lane);
+            const floatx4 mi = *reinterpret_cast<const floatx4*>(lds_s + (2 * q + 1) * 256 + 4 * lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ctile_mac(acc[lt], mr[r], mi[r], mr[r] + mi[r], gy_r[tt][r], gy_i[tt][r], ys[r]);
+        }
+    }
+
+    if constexpr (!DX) {
+        // ---- dB stores; register r <-> row l = 16 lt + 4g + r, column n = 16w + li
+        const BufRes rdb_r = make_buf(a.db_re + v.row0 * N, v.extN * 4);
+        const BufRes rdb_i = make_buf(a.db_im + v.row0 * N, v.extN * 4);
+#pragma unroll
+        for (int lt = 0; lt < NLT; ++lt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t off = (uint32_t)(lt * 16 + 4 * g + r) * v.sN + 16 * w + li;
+                buf_store_f32(ctile_re(acc[lt], r), rdb_r, off);
+                buf_store_f32(ctile_im(acc[lt], r), rdb_i, off);
+            }
+        return;
+    } else {
+        // ---- dX stores: dx = acc + D dY; q1 partials of this wave's 16 columns
+        const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
+        const BufRes rdx_r = make_buf(a.dx_re + v.row0 * D, v.extD * 4);
+        const BufRes rdx_i = make_buf(a.dx_im + v.row0 * D, v.extD * 4);
+        float* const qpart = lds_o;  // [wave][row][re, im]; the B rows are no longer read
+        // conj(x) dx for the 16 rows m = 4 lt + r of this lane's column
+        float pr[16], pi[16];
+#pragma unroll
+        for (int lt = 0; lt < NLT; ++lt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lrow = lt * 16 + 4 * g + r;
+                const uint32_t off = (uint32_t)lrow * v.sD + 16 * w + li;
+                const float xr = xb_r[lt][r], xi = xb_i[lt][r];
+                const float vr = ctile_re(acc[lt], r), vi = ctile_im(acc[lt], r);
+                pr[4 * lt + r] = xr * vr + xi * vi;
+                pi[4 * lt + r] = xr * vi - xi * vr;
+                buf_store_f32(vr + dk * gy_r[lt][r], rdx_r, off);
+                buf_store_f32(vi + dk * gy_i[lt][r], rdx_i, off);
+            }
+        // sum each row over the wave's 16 columns (a butterfly that leaves lane li
+        // with row li measured slower than these per-row sums)
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            pr[m] = sum16(pr[m]);
+            pi[m] = sum16(pi[m]);
+        }
+        if (li == 0)
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int lrow = (m >> 2) * 16 + 4 * g + (m & 3);
+                qpart[(w * C + lrow) * 2] = pr[m];
+                qpart[(w * C + lrow) * 2 + 1] = pi[m];
+            }
+        __syncthreads();
+        if (threadIdx.x < 2 * C) {
+            const int lrow = threadIdx.x >> 1, part = threadIdx.x & 1;
+            float sum = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < W; ++ww) sum += qpart[(ww * C + lrow) * 2 + part];
+            (part ? a.q1_im : a.q1_re)[v.pbase + lrow] = -sum;
+        }
+    }
+}
 // ----------------------------------------------------------------------------
 // dC for row tile tt of one chunk, plus the y half of q and the dD partials
 // ----------------------------------------------------------------------------
@@ -689,8 +982,21 @@ static hipError_t launch_tiles(const BwdArgs& a, hipStream_t s) {
     }
 }
 
-hipError_t launch_bwd_dx(const BwdArgs& a, hipStream_t s) { return launch_tiles<0>(a, s); }
-hipError_t launch_bwd_db(const BwdArgs& a, hipStream_t s) { return launch_tiles<1>(a, s); }
+// N = D = C = 64: the chunk-staged kernels; other shapes: the tile kernels
+static bool bwd_staged(const BwdArgs& a) { return a.f.C == 64 && a.f.N == 64 && a.f.D == 64; }
+
+hipError_t launch_bwd_dx(const BwdArgs& a, hipStream_t s) {
+    if (!bwd_staged(a)) return launch_tiles<0>(a, s);
+    hipLaunchKernelGGL(k_bwd_lds<true>, dim3((unsigned)(a.f.B * a.f.H * a.f.nC)), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+}
+hipError_t launch_bwd_db(const BwdArgs& a, hipStream_t s) {
+    if (!bwd_staged(a)) return launch_tiles<1>(a, s);
+    hipLaunchKernelGGL(k_bwd_lds<false>, dim3((unsigned)(a.f.B * a.f.H * a.f.nC)), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+}
 hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s) { return launch_tiles<2>(a, s); }
 
 hipError_t launch_bwd_dz(const BwdArgs& a, bool with_zbound, hipStream_t s) {
