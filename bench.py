@@ -48,6 +48,8 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_cumsum": ("k_cumsum.hip",), "k_step": ("k_step.hip",),
               "k_step_infinite": ("k_step.hip",),
               "k_bwd_tiles": ("k_backward.hip",), "k_bwd_zbound": ("k_backward.hip",),
+              "k_bwd_lds": ("k_backward.hip", "k_chunk_scan_lds.h"),
+              "k_bwd_dc_lds": ("k_backward.hip", "k_chunk_scan_lds.h"),
               "k_bwd_dz": ("k_backward.hip",), "k_bwd_reduce": ("k_backward.hip",),
               "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
               "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",),
@@ -473,7 +475,7 @@ def main():
         progress("timing the backward pass")
         bms, bk = time_backward(inp, max(3, args.steps // 2), 2, dev)
         bfl = backward_dx_flops(B, T, H, D, N, C)
-        bsym = f"k_bwd_tiles<{C}, {N}, {D}, 0>"
+        bsym = "k_bwd_lds<true>" if C == N == D == 64 else f"k_bwd_tiles<{C}, {N}, {D}, 0>"
         extra["backward_cfg1_B8_T2048_H48_D64_N64_C64_f32"] = {
             "tokens_per_s": round(tokens / (bms * 1e-3), 1), "ms_per_step": round(bms, 4),
             "kernels_avg_ms": {k: round(v, 5) for k, v in bk.items()},

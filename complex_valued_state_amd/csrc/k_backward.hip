@@ -607,6 +607,245 @@ __global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
     }
 }
 // ----------------------------------------------------------------------------
+// dC for N = D = C = 64, staged per chunk like k_bwd_lds: one workgroup per
+// chunk, wave w owning the output columns n in [16 w, 16 w + 16) of every row t.
+// The chunk's dY and X rows go to LDS; each wave loads its column blocks of
+// conj(H_c) (element-wise from the fragments) and conj(B) into registers.
+//  1. state term dY H_c^H on the wave's columns, rows scaled by conj(e[t]);
+//     wave w also forms q2 and the dD partial of rows [16 w, 16 w + 16).
+//  2. the causal tiles of P^T = conj(X) dY^T (t tile >= l tile) split over the
+//     waves; K = conj(L) P comes out with register r holding
+//     [t = t0 + lane%16][l = l0 + 4 (lane/16) + r], the A-operand layout of
+//     the product with conj(B) rows; exchanged through LDS (over the X rows).
+//  3. dC[t, n] += sum_l K[t, l] conj(B[l, n]).
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
+    constexpr int C = 64, N = 64, D = 64, NK = N / 16, PT = D / 16, W = N / 16, NLT = C / 16;
+    static_assert(N == D, "the two staged row sets share one row width");
+    constexpr int NP = NLT * (NLT + 1) / 2;  // causal tiles (tt >= lt), tt-major
+    constexpr int MQ = (NP + W - 1) / W;
+    constexpr int PLANE = C * D, IPP = PLANE / 256;
+    __shared__ floatx4 lds_g4[2 * PLANE / 4];  // dY rows
+    __shared__ floatx4 lds_x4[2 * PLANE / 4];  // X rows, later the K tiles
+    __shared__ floatx4 lds_a4[1024 / 4];       // acs re, acs im (fp64), e re, e im
+    float* const ldg = reinterpret_cast<float*>(lds_g4);
+    float* const ldx = reinterpret_cast<float*>(lds_x4);
+    float* const lda = reinterpret_cast<float*>(lds_a4);
+    const double* const lacs_r = reinterpret_cast<const double*>(lda);
+    const double* const lacs_i = reinterpret_cast<const double*>(lda + 256);
+    const float* const le_r = lda + 512;
+    const float* const le_i = lda + 768;
+
+    const FwdArgs& f = a.f;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int w = wave_id();
+    const int64_t chunk = blockIdx.x;
+    const ChunkView v = chunk_view(a, chunk, C, N, D);
+
+    // ---- 0. staging
+    auto stage_plane = [&](const void* src, float* dst_plane, int first) {
+        const BufRes r = make_buf(static_cast<const float*>(src) + v.row0 * D, v.extD * 4);
+        for (int blk = (w - first + W) % W; blk < IPP; blk += W) {  // wave-uniform
+            const int u = blk * 64 + lane;  // physical 16-byte piece within the plane
+            const int row = u / (D / 4), pc = u % (D / 4);
+            const uint32_t voff = ((uint32_t)row * v.sD + 4 * lds_swz<D>(row, pc)) * 4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(dst_plane + blk * 256), 16, voff,
+                                                     0, 0, 0);
+        }
+    };
+    stage_plane(a.dy_re, ldg, 0);
+    stage_plane(a.dy_im, ldg + PLANE, IPP % W);
+    stage_plane(f.x_re, ldx, (2 * IPP) % W);
+    stage_plane(f.x_im, ldx + PLANE, (3 * IPP) % W);
+    if (w == W - 1) {
+        const void* const aux[4] = {f.acs_re + v.pbase, f.acs_im + v.pbase, f.e_re + v.pbase,
+                                    f.e_im + v.pbase};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_buf(aux[j], (j < 2 ? 8 : 4) * C),
+                                                     (LdsPtr)(lda + 256 * j), 16, 16 * lane,
+                                                     0, 0, 0);
+    }
+    // conj(H_c[16w + li][16k + 4g + e]), the B operand of the state term
+    const BufRes rh_r = make_buf(f.st_re + chunk * (int64_t)N * D, N * D * 4);
+    const BufRes rh_i = make_buf(f.st_im + chunk * (int64_t)N * D, N * D * 4);
+    floatx4 hreg_r[PT], hreg_i[PT];
+#pragma unroll
+    for (int k = 0; k < PT; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t fi = frag_index<D>(16 * w + li, 16 * k + 4 * g + e);
+            hreg_r[k][e] = buf_f32(rh_r, fi);
+            hreg_i[k][e] = -buf_f32(rh_i, fi);
+        }
+    // conj(B[16 lt + 4g + r][16w + li]), the B operand of step 3
+    const BufRes rb_r = make_buf(static_cast<const float*>(f.b_re) + v.row0 * N, v.extN * 4);
+    const BufRes rb_i = make_buf(static_cast<const float*>(f.b_im) + v.row0 * N, v.extN * 4);
+    float cb_r[NLT][4], cb_i[NLT][4];
+#pragma unroll
+    for (int lt = 0; lt < NLT; ++lt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (uint32_t)(lt * 16 + 4 * g + r) * v.sN + 16 * w + li;
+            cb_r[lt][r] = buf_f32(rb_r, off);
+            cb_i[lt][r] = -buf_f32(rb_i, off);
+        }
+    // y rows 16 w + li for q2
+    const BufRes ry_r = make_buf(a.y_re + v.row0 * D, v.extD * 4);
+    const BufRes ry_i = make_buf(a.y_im + v.row0 * D, v.extD * 4);
+    floatx4 yq_r[PT], yq_i[PT];
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        yq_r[k] = buf_f32x4(ry_r, (uint32_t)(16 * w + li) * v.sD + 16 * k + 4 * g);
+        yq_i[k] = buf_f32x4(ry_i, (uint32_t)(16 * w + li) * v.sD + 16 * k + 4 * g);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+
+    auto row4 = [&](const float* plane, int row, int ch) -> floatx4 {
+        return *reinterpret_cast<const floatx4*>(plane + row * D + 4 * lds_swz<D>(row, ch));
+    };
+    const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
+
+    // ---- the y half of q and the dD partial for row t = 16 w + li
+    {
+        const int t = 16 * w + li;
+        float qr = 0.f, qi = 0.f, dd = 0.f;
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const floatx4 gr = row4(ldg, t, 4 * k + g), gi = row4(ldg + PLANE, t, 4 * k + g);
+            const floatx4 xr = row4(ldx, t, 4 * k + g), xi = row4(ldx + PLANE, t, 4 * k + g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ur = yq_r[k][e] - dk * xr[e], ui = yq_i[k][e] - dk * xi[e];
+                qr += gr[e] * ur + gi[e] * ui;  // dy conj(y - D x)
+                qi += gi[e] * ur - gr[e] * ui;
+                dd += gr[e] * xr[e] + gi[e] * xi[e];
+            }
+        }
+        qr = sum_groups(qr);
+        qi = sum_groups(qi);
+        dd = sum_groups(dd);
+        if (g == 0) {
+            a.q2_re[v.pbase + t] = qr;
+            a.q2_im[v.pbase + t] = qi;
+            a.ddp[v.pbase + t] = dd;
+        }
+    }
+
+    // ---- 1. state term dY H_c^H, then the row factor conj(e[t])
+    CTile acc[NLT];
+#pragma unroll
+    for (int tt = 0; tt < NLT; ++tt) ctile_zero(acc[tt]);
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        const floatx4 hr = hreg_r[k], hi = hreg_i[k], hs = hr + hi;
+#pragma unroll
+        for (int tt = 0; tt < NLT; ++tt) {
+            const floatx4 gr = row4(ldg, tt * 16 + li, 4 * k + g);
+            const floatx4 gi = row4(ldg + PLANE, tt * 16 + li, 4 * k + g);
+            const floatx4 gs = gr + gi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ctile_mac(acc[tt], gr[e], gi[e], gs[e], hr[e], hi[e], hs[e]);
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NLT; ++tt) {
+        const floatx4 er = *reinterpret_cast<const floatx4*>(le_r + tt * 16 + 4 * g);
+        const floatx4 ei = *reinterpret_cast<const floatx4*>(le_i + tt * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ctile_scale(acc[tt], r, er[r], -ei[r]);
+    }
+
+    // ---- 2. tiles (tt, lt), lt <= tt: P^T = conj(X) dY^T, K = conj(L) P
+    const int q0 = (w * NP) / W, q1 = ((w + 1) * NP) / W;
+    floatx4 m_r[MQ], m_i[MQ];
+    {
+        int tt = 0, lt = q0;  // tt-major decode of q0
+        while (lt > tt) {
+            lt -= tt + 1;
+            ++tt;
+        }
+#pragma unroll
+        for (int j = 0; j < MQ; ++j) {
+            if (q0 + j < q1) {  // wave-uniform
+                const int t0 = tt * 16, l0 = lt * 16;
+                CTile pq;
+                ctile_zero(pq);
+#pragma unroll
+                for (int k = 0; k < PT; ++k) {
+                    const floatx4 xr = row4(ldx, l0 + li, 4 * k + g);
+                    const floatx4 xi = -row4(ldx + PLANE, l0 + li, 4 * k + g);
+                    const floatx4 gr = row4(ldg, t0 + li, 4 * k + g);
+                    const floatx4 gi = row4(ldg + PLANE, t0 + li, 4 * k + g);
+                    const floatx4 xs = xr + xi, gs = gr + gi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ctile_mac(pq, xr[e], xi[e], xs[e], gr[e], gi[e], gs[e]);
+                }
+                // register r <-> (t = t0 + li, l = l0 + 4g + r)
+                const int t = t0 + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int l = l0 + 4 * g + r;
+                    float lr = 0.f, lim = 0.f;
+                    if (lt < tt || t >= l) seg_exp(lacs_r, lacs_i, t, l, false, lr, lim);
+                    const float p_r = ctile_re(pq, r), p_i = ctile_im(pq, r);
+                    m_r[j][r] = lr * p_r + lim * p_i;  // conj(L) P
+                    m_i[j][r] = lr * p_i - lim * p_r;
+                }
+                if (++lt > tt) {
+                    lt = 0;
+                    ++tt;
+                }
+            }
+        }
+    }
+
+    // ---- the K tiles replace the X rows
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < MQ; ++j) {
+        if (q0 + j < q1) {
+            const int q = q0 + j;
+            *reinterpret_cast<floatx4*>(ldx + (2 * q) * 256 + 4 * lane) = m_r[j];
+            *reinterpret_cast<floatx4*>(ldx + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. dC[tt] += K(tt, lt) conj(B)[lt rows, this wave's columns], lt <= tt
+#pragma unroll
+    for (int lt = 0; lt < NLT; ++lt) {
+        float bs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bs[r] = cb_r[lt][r] + cb_i[lt][r];
+#pragma unroll
+        for (int tt = lt; tt < NLT; ++tt) {
+            const int q = tt * (tt + 1) / 2 + lt;
+            const floatx4 mr = *reinterpret_cast<const floatx4*>(ldx + (2 * q) * 256 + 4 * lane);
+            const floatx4 mi = *reinterpret_cast<const floatx4*>(ldx + (2 * q + 1) * 256 + 4 * lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ctile_mac(acc[tt], mr[r], mi[r], mr[r] + mi[r], cb_r[lt][r], cb_i[lt][r], bs[r]);
+        }
+    }
+
+    // ---- stores; register r <-> row t = 16 tt + 4g + r, column n = 16w + li
+    const BufRes rdc_r = make_buf(a.dc_re + v.row0 * N, v.extN * 4);
+    const BufRes rdc_i = make_buf(a.dc_im + v.row0 * N, v.extN * 4);
+#pragma unroll
+    for (int tt = 0; tt < NLT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (uint32_t)(tt * 16 + 4 * g + r) * v.sN + 16 * w + li;
+            buf_store_f32(ctile_re(acc[tt], r), rdc_r, off);
+            buf_store_f32(ctile_im(acc[tt], r), rdc_i, off);
+        }
+}
+
+// ----------------------------------------------------------------------------
 // dC for row tile tt of one chunk, plus the y half of q and the dD partials
 // ----------------------------------------------------------------------------
 template <int C, int N, int D>
@@ -997,7 +1236,12 @@ hipError_t launch_bwd_db(const BwdArgs& a, hipStream_t s) {
                        s, a);
     return hipGetLastError();
 }
-hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s) { return launch_tiles<2>(a, s); }
+hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s) {
+    if (!bwd_staged(a)) return launch_tiles<2>(a, s);
+    hipLaunchKernelGGL(k_bwd_dc_lds, dim3((unsigned)(a.f.B * a.f.H * a.f.nC)), dim3(256), 0, s,
+                       a);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_dz(const BwdArgs& a, bool with_zbound, hipStream_t s) {
     const int64_t nchunks = a.f.B * a.f.H * a.f.nC;
