@@ -44,8 +44,22 @@ __device__ __forceinline__ int lds_swz(int row, int c) {
 // left at their maxima, i.e. not waited on).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// At N = D = C = 64 the B rows are staged in two halves (rows 0-31 for the score
+// tiles of the first two column tiles, then rows 32-63 for the other three), so
+// that a workgroup takes 52 KB of LDS instead of 68 and three fit on a CU, with
+// the registers held to three waves per SIMD.
+#ifndef CSSD_K2_HALFB
+#define CSSD_K2_HALFB 1
+#endif
 template <int C, int N, int D>
-__global__ __launch_bounds__(64 * (D / 16)) void k_chunk_scan_lds(ScanArgs a) {
+constexpr bool k2_half_b() {
+    return CSSD_K2_HALFB && C == 64 && N == 64 && D == 64;
+}
+
+template <int C, int N, int D>
+__global__ __launch_bounds__(64 * (D / 16))
+__attribute__((amdgpu_waves_per_eu(k2_half_b<C, N, D>() ? 3 : 1))) void k_chunk_scan_lds(
+    ScanArgs a) {
     constexpr int NK = N / 16;                // 16-wide tiles of the n axis
     constexpr int W = D / 16;                 // waves = 16-wide column tiles of p
     constexpr int NLT = C / 16;               // row tiles per chunk
@@ -54,11 +68,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_chunk_scan_lds(ScanArgs a) {
     constexpr int PLANE = C * N;              // floats of one staged plane
     constexpr int IPP = PLANE / 256;          // 64-lane x 16-byte loads per plane
     constexpr int MFL = NP * 512;             // floats of the M tiles
-    constexpr int BREG = 2 * PLANE > MFL ? 2 * PLANE : MFL;  // B planes, later M
+    constexpr bool HB = k2_half_b<C, N, D>();
+    constexpr int BPLANE = HB ? PLANE / 2 : PLANE;  // floats of one staged B plane
+    constexpr int BIPP = BPLANE / 256;
+    // B planes; later the M tiles (which go over the C rows when B is staged in halves)
+    constexpr int BREG = HB ? 2 * BPLANE : (2 * PLANE > MFL ? 2 * PLANE : MFL);
+    static_assert(!HB || MFL <= 2 * PLANE, "the M tiles must fit over the C rows");
     // vector-memory operations every wave issues after the first staging group
     // (a lower bound: each B plane gives a wave at least IPP / W blocks; then
     // its X loads), so waiting down to LATE outstanding completes the first group
-    constexpr int LATE = 2 * (IPP / W) + 2 * 4 * NLT;
+    constexpr int LATE = 2 * (BIPP / W) + (HB ? 0 : 2 * 4 * NLT);
     static_assert(PLANE % 256 == 0, "staged plane must be whole 1 KB blocks");
     static_assert(LATE < 64, "vmcnt holds at most 63");
     static_assert(8 * C <= 1024, "a chunk's cumsums must fit one 1 KB slot");
@@ -70,6 +89,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_chunk_scan_lds(ScanArgs a) {
     float* const lds = reinterpret_cast<float*>(lds_b4);
     float* const ldc = reinterpret_cast<float*>(lds_c4);
     float* const lda = reinterpret_cast<float*>(lds_a4);
+    float* const ldm = HB ? ldc : lds;  // the M tiles
     const double* const lacs_r = reinterpret_cast<const double*>(lda);
     const double* const lacs_i = reinterpret_cast<const double*>(lda + 256);
     const float* const le_r = lda + 512;
@@ -98,21 +118,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_chunk_scan_lds(ScanArgs a) {
     const int64_t pbase = bh * (int64_t)a.nC * C + t0;  // per-position workspace base
     const float dk = a.dskip != nullptr ? a.dskip[h] : 0.f;
 
-    // one staged plane: its IPP 1 KB blocks, dealt round-robin to the waves
-    auto stage_plane = [&](const void* src, float* dst_plane, int first) {
+    // one staged plane (rows r0 .. r0 + nblk * 256 / N - 1): its nblk 1 KB blocks,
+    // dealt round-robin to the waves; rows are swizzled by their staged index
+    auto stage_plane = [&](const void* src, float* dst_plane, int first, int r0, int nblk) {
         const BufRes r = make_buf(static_cast<const float*>(src) + row0 * N, extN * 4);
-        for (int blk = (w - first + W) % W; blk < IPP; blk += W) {  // wave-uniform
+        for (int blk = (w - first + W) % W; blk < nblk; blk += W) {  // wave-uniform
             const int u = blk * 64 + lane;  // physical 16-byte chunk within the plane
             const int row = u / (N / 4), pc = u % (N / 4);
-            const uint32_t voff = ((uint32_t)row * sN + 4 * lds_swz<N>(row, pc)) * 4;
+            const uint32_t voff = ((uint32_t)(r0 + row) * sN + 4 * lds_swz<N>(row, pc)) * 4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(dst_plane + blk * 256), 16, voff,
                                                      0, 0, 0);
         }
     };
 
     // ---- 0a. first group: C rows, cumsums, exp(acs), H_c block
-    stage_plane(a.c_re, ldc, 0);
-    stage_plane(a.c_im, ldc + PLANE, IPP % W);
+    stage_plane(a.c_re, ldc, 0, 0, IPP);
+    stage_plane(a.c_im, ldc + PLANE, IPP % W, 0, IPP);
     if (w == W - 1) {
         // cumsums (fp64, 8C bytes each) and exp(acs) (fp32, 4C bytes each), one
         // 1 KB slot each; lanes past the end read zero into the rest of the slot
@@ -133,17 +154,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_chunk_scan_lds(ScanArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the two groups in issue order
     // ---- 0b. second group: B rows, X block X[16 st + 4g + r][16w + li]
-    stage_plane(a.b_re, lds, (2 * IPP) % W);
-    stage_plane(a.b_im, lds + PLANE, (3 * IPP) % W);
+    stage_plane(a.b_re, lds, (2 * IPP) % W, 0, BIPP);
+    stage_plane(a.b_im, lds + BPLANE, (3 * IPP) % W, 0, BIPP);
     float xreg_r[NLT][4], xreg_i[NLT][4];
+    if constexpr (!HB) {
 #pragma unroll
-    for (int st = 0; st < NLT; ++st)
+        for (int st = 0; st < NLT; ++st)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t off = (uint32_t)(st * 16 + 4 * g + r) * sD + 16 * w + li;
-            xreg_r[st][r] = buf_f32(rx_r, off);
-            xreg_i[st][r] = buf_f32(rx_i, off);
-        }
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t off = (uint32_t)(st * 16 + 4 * g + r) * sD + 16 * w + li;
+                xreg_r[st][r] = buf_f32(rx_r, off);
+                xreg_i[st][r] = buf_f32(rx_i, off);
+            }
+    }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(LATE));  // the first group is in
     __syncthreads();
@@ -190,66 +213,154 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_chunk_scan_lds(ScanArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the second group is in
     __syncthreads();
 
-    // ---- 2. score tiles q in [q0, q1) -> M in registers
-    const int q0 = (w * NP) / W, q1 = ((w + 1) * NP) / W;
+    // ---- 2. score tiles -> M in registers
     floatx4 m_r[MQ], m_i[MQ];
-    {
-        int lt = 0, st = q0;  // lt-major decode of q0
-        while (st > lt) {
-            st -= lt + 1;
-            ++lt;
+    const int q0 = (w * NP) / W, q1 = ((w + 1) * NP) / W;  // without the half split
+    int qidx[MQ], nq;  // the tile index of each kept M and their number
+    // tile (lt, st) from the B rows staged from row b0 on
+    auto score_tile = [&](int lt, int st, int b0, floatx4& mr, floatx4& mi) {
+        const int l0 = lt * 16, s0 = st * 16;
+        CTile gt;
+        ctile_zero(gt);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            const floatx4 br = row4(lds, s0 - b0 + li, 4 * k + g);
+            const floatx4 bi = row4(lds + BPLANE, s0 - b0 + li, 4 * k + g);
+            const floatx4 cr = row4(ldc, l0 + li, 4 * k + g);
+            const floatx4 ci = row4(ldc + PLANE, l0 + li, 4 * k + g);
+            const floatx4 bs = br + bi, cs = cr + ci;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ctile_mac(gt, br[e], bi[e], bs[e], cr[e], ci[e], cs[e]);
         }
+        // register r <-> (l = l0 + li, s = s0 + 4g + r)
+        const int lrow = l0 + li;
+        const bool diag = (lt == st);
+        const double alr = lacs_r[lrow], ali = lacs_i[lrow];
 #pragma unroll
-        for (int j = 0; j < MQ; ++j) {
-            if (q0 + j < q1) {  // wave-uniform
-                const int l0 = lt * 16, s0 = st * 16;
-                CTile gt;
-                ctile_zero(gt);
+        for (int r = 0; r < 4; ++r) {
+            const int s = s0 + 4 * g + r;
+            const float gr = ctile_re(gt, r), gi = ctile_im(gt, r);
+            float lr = 0.f, lim = 0.f;
+            if (!diag || s <= lrow) {
+                const double d2 = alr - lacs_r[s];
+                double dv = ali - lacs_i[s];
+                dv -= rint(dv);
+                cexp_scaled((float)d2, (float)dv, lr, lim);
+            }
+            mr[r] = gr * lr - gi * lim + ((diag && s == lrow) ? dk : 0.f);
+            mi[r] = gr * lim + gi * lr;
+        }
+    };
+    // the tiles this wave owns, as (lt, st) in fixed slots (wave-uniform values):
+    // with B in halves, the seven tiles with st < 2 (lt-major, idx -> ((idx + 1) / 2,
+    // (idx + 1) % 2) for idx >= 1) two per wave and one for wave 3, then (2,2) to
+    // wave 1, (3,2) to wave 2 and (3,3) to wave 3; else the NP tiles in lt-major
+    // order, split evenly
+    if constexpr (HB) {
+        int own_lt[MQ], own_st[MQ], nown;
+        static_assert(MQ == 3 && W == 4 && NLT == 4, "the split is for C = D = 64");
+        auto a_tile = [](int idx, int& lt, int& st) {
+            lt = idx == 0 ? 0 : (idx + 1) / 2;
+            st = idx == 0 ? 0 : (idx + 1) % 2;
+        };
+        a_tile(2 * w, own_lt[0], own_st[0]);
+        if (w < 3) {
+            a_tile(2 * w + 1, own_lt[1], own_st[1]);
+        } else {
+            own_lt[1] = 3;
+            own_st[1] = 3;
+        }
+        own_lt[2] = w == 1 ? 2 : 3;
+        own_st[2] = 2;
+        nown = (w == 1 || w == 2) ? 3 : 2;
+        nq = nown;
 #pragma unroll
-                for (int k = 0; k < NK; ++k) {
-                    const floatx4 br = row4(lds, s0 + li, 4 * k + g);
-                    const floatx4 bi = row4(lds + PLANE, s0 + li, 4 * k + g);
-                    const floatx4 cr = row4(ldc, l0 + li, 4 * k + g);
-                    const floatx4 ci = row4(ldc + PLANE, l0 + li, 4 * k + g);
-                    const floatx4 bs = br + bi, cs = cr + ci;
+        for (int j = 0; j < MQ; ++j) qidx[j] = own_lt[j] * (own_lt[j] + 1) / 2 + own_st[j];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        ctile_mac(gt, br[e], bi[e], bs[e], cr[e], ci[e], cs[e]);
-                }
-                // register r <-> (l = l0 + li, s = s0 + 4g + r)
-                const int lrow = l0 + li;
-                const bool diag = (lt == st);
-                const double alr = lacs_r[lrow], ali = lacs_i[lrow];
+        for (int j = 0; j < MQ; ++j)
+            if (j < nown && own_st[j] < 2) score_tile(own_lt[j], own_st[j], 0, m_r[j], m_i[j]);
+        __syncthreads();  // every wave is done with B rows 0-31
+        stage_plane(a.b_re, lds, 0, C / 2, BIPP);
+        stage_plane(a.b_im, lds + BPLANE, BIPP % W, C / 2, BIPP);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = s0 + 4 * g + r;
-                    const float gr = ctile_re(gt, r), gi = ctile_im(gt, r);
-                    float lr = 0.f, lim = 0.f;
-                    if (!diag || s <= lrow) {
-                        const double d2 = alr - lacs_r[s];
-                        double dv = ali - lacs_i[s];
-                        dv -= rint(dv);
-                        cexp_scaled((float)d2, (float)dv, lr, lim);
+        for (int j = 0; j < MQ; ++j)
+            if (j < nown && own_st[j] >= 2) score_tile(own_lt[j], own_st[j], C / 2, m_r[j], m_i[j]);
+    } else {
+        nq = q1 - q0;
+#pragma unroll
+        for (int j = 0; j < MQ; ++j) qidx[j] = q0 + j;
+        {
+            int lt = 0, st = q0;  // lt-major decode of q0
+            while (st > lt) {
+                st -= lt + 1;
+                ++lt;
+            }
+#pragma unroll
+            for (int j = 0; j < MQ; ++j) {
+                if (q0 + j < q1) {  // wave-uniform
+                    const int l0 = lt * 16, s0 = st * 16;
+                    CTile gt;
+                    ctile_zero(gt);
+#pragma unroll
+                    for (int k = 0; k < NK; ++k) {
+                        const floatx4 br = row4(lds, s0 + li, 4 * k + g);
+                        const floatx4 bi = row4(lds + PLANE, s0 + li, 4 * k + g);
+                        const floatx4 cr = row4(ldc, l0 + li, 4 * k + g);
+                        const floatx4 ci = row4(ldc + PLANE, l0 + li, 4 * k + g);
+                        const floatx4 bs = br + bi, cs = cr + ci;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            ctile_mac(gt, br[e], bi[e], bs[e], cr[e], ci[e], cs[e]);
                     }
-                    m_r[j][r] = gr * lr - gi * lim + ((diag && s == lrow) ? dk : 0.f);
-                    m_i[j][r] = gr * lim + gi * lr;
-                }
-                if (++st > lt) {
-                    st = 0;
-                    ++lt;
+                    // register r <-> (l = l0 + li, s = s0 + 4g + r)
+                    const int lrow = l0 + li;
+                    const bool diag = (lt == st);
+                    const double alr = lacs_r[lrow], ali = lacs_i[lrow];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int s = s0 + 4 * g + r;
+                        const float gr = ctile_re(gt, r), gi = ctile_im(gt, r);
+                        float lr = 0.f, lim = 0.f;
+                        if (!diag || s <= lrow) {
+                            const double d2 = alr - lacs_r[s];
+                            double dv = ali - lacs_i[s];
+                            dv -= rint(dv);
+                            cexp_scaled((float)d2, (float)dv, lr, lim);
+                        }
+                        m_r[j][r] = gr * lr - gi * lim + ((diag && s == lrow) ? dk : 0.f);
+                        m_i[j][r] = gr * lim + gi * lr;
+                    }
+                    if (++st > lt) {
+                        st = 0;
+                        ++lt;
+                    }
                 }
             }
         }
     }
+    if constexpr (HB) {
+        // the X block, late: its registers would not fit during the scores
+#pragma unroll
+        for (int st = 0; st < NLT; ++st)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t off = (uint32_t)(st * 16 + 4 * g + r) * sD + 16 * w + li;
+                xreg_r[st][r] = buf_f32(rx_r, off);
+                xreg_i[st][r] = buf_f32(rx_i, off);
+            }
+    }
 
-    // ---- 3. the M tiles replace the B rows
+    // ---- 3. the M tiles replace the B rows (or, with B in halves, the C rows)
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < MQ; ++j) {
-        if (q0 + j < q1) {
-            const int q = q0 + j;
-            *reinterpret_cast<floatx4*>(lds + (2 * q) * 256 + 4 * lane) = m_r[j];
-            *reinterpret_cast<floatx4*>(lds + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
+        if (j < nq) {
+            const int q = qidx[j];
+            *reinterpret_cast<floatx4*>(ldm + (2 * q) * 256 + 4 * lane) = m_r[j];
+            *reinterpret_cast<floatx4*>(ldm + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
         }
     }
     __syncthreads();
@@ -263,8 +374,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_chunk_scan_lds(ScanArgs a) {
 #pragma unroll
         for (int lt = st; lt < NLT; ++lt) {
             const int q = lt * (lt + 1) / 2 + st;
-            const floatx4 mr = *reinterpret_cast<const floatx4*>(lds + (2 * q) * 256 + 4 * lane);
-            const floatx4 mi = *reinterpret_cast<const floatx4*>(lds + (2 * q + 1) * 256 + 4 * lane);
+            const floatx4 mr = *reinterpret_cast<const floatx4*>(ldm + (2 * q) * 256 + 4 * lane);
+            const floatx4 mi = *reinterpret_cast<const floatx4*>(ldm + (2 * q + 1) * 256 + 4 * lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 ctile_mac(acc[lt], mr[r], mi[r], mr[r] + mi[r], xreg_r[st][r], xreg_i[st][r],
