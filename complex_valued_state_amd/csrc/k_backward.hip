@@ -334,17 +334,21 @@ __device__ __forceinline__ void dxdb_tile(const BwdArgs& a, int64_t chunk, int l
 // C and dY rows once per row tile it served, and R twice per wave).
 // ----------------------------------------------------------------------------
 template <bool DX>
-__global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_lds(
+    BwdArgs a) {
     constexpr int C = 64, N = 64, D = 64, NK = N / 16, W = D / 16, NLT = C / 16;
     static_assert(N == D, "the two staged row sets share one row width");
     constexpr int NP = NLT * (NLT + 1) / 2;  // causal tiles (tt >= lt), tt-major
     constexpr int MQ = (NP + W - 1) / W;
     constexpr int PLANE = C * N, IPP = PLANE / 256;
-    static_assert(NP * 512 <= 2 * PLANE, "the M tiles must fit over the first row set");
-    // dX: C rows (scores' A operand), later the M tiles; B rows
-    // dB: dY rows (scores' A operand), later the M tiles; X rows
-    __shared__ floatx4 lds_s4[2 * PLANE / 4];
-    __shared__ floatx4 lds_o4[2 * PLANE / 4];  // later the q1 partials (dX)
+    constexpr int SPLANE = PLANE / 2, SIPP = SPLANE / 256;  // half of the first row set
+    static_assert(NP * 512 <= 2 * PLANE, "the M tiles must fit over the second row set");
+    // The first row set (the scores' A operand: C rows for dX, dY rows for dB) is
+    // staged in halves, rows 32-63 for the seven tiles with tt >= 2, then rows
+    // 0-31 for the other three; the second (B rows for dX, X rows for dB) whole.
+    // That is 52 KB of LDS, three workgroups per CU.
+    __shared__ floatx4 lds_s4[2 * SPLANE / 4];  // later the q1 partials (dX)
+    __shared__ floatx4 lds_o4[2 * PLANE / 4];   // later the M tiles
     __shared__ floatx4 lds_a4[1024 / 4];       // acs re, acs im (fp64), w re, w im
     float* const lds_s = reinterpret_cast<float*>(lds_s4);
     float* const lds_o = reinterpret_cast<float*>(lds_o4);
@@ -362,20 +366,23 @@ __global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
     const ChunkView v = chunk_view(a, chunk, C, N, D);
 
     // ---- 0. staging
-    auto stage_plane = [&](const void* src, float* dst_plane, int first) {
+    // rows r0 .. r0 + nblk * 256 / N - 1 of one plane, swizzled by staged row index
+    auto stage_plane = [&](const void* src, float* dst_plane, int first, int r0, int nblk) {
         const BufRes r = make_buf(static_cast<const float*>(src) + v.row0 * N, v.extN * 4);
-        for (int blk = (w - first + W) % W; blk < IPP; blk += W) {  // wave-uniform
+        for (int blk = (w - first + W) % W; blk < nblk; blk += W) {  // wave-uniform
             const int u = blk * 64 + lane;  // physical 16-byte piece within the plane
             const int row = u / (N / 4), pc = u % (N / 4);
-            const uint32_t voff = ((uint32_t)row * v.sN + 4 * lds_swz<N>(row, pc)) * 4;
+            const uint32_t voff = ((uint32_t)(r0 + row) * v.sN + 4 * lds_swz<N>(row, pc)) * 4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(dst_plane + blk * 256), 16, voff,
                                                      0, 0, 0);
         }
     };
-    stage_plane(DX ? f.c_re : a.dy_re, lds_s, 0);
-    stage_plane(DX ? f.c_im : a.dy_im, lds_s + PLANE, IPP % W);
-    stage_plane(DX ? f.b_re : f.x_re, lds_o, (2 * IPP) % W);
-    stage_plane(DX ? f.b_im : f.x_im, lds_o + PLANE, (3 * IPP) % W);
+    const void* const s_re = DX ? f.c_re : a.dy_re;
+    const void* const s_im = DX ? f.c_im : a.dy_im;
+    stage_plane(s_re, lds_s, 0, C / 2, SIPP);
+    stage_plane(s_im, lds_s + SPLANE, SIPP % W, C / 2, SIPP);
+    stage_plane(DX ? f.b_re : f.x_re, lds_o, 0, 0, IPP);
+    stage_plane(DX ? f.b_im : f.x_im, lds_o + PLANE, IPP % W, 0, IPP);
     if (w == W - 1) {
         const void* const aux[4] = {f.acs_re + v.pbase, f.acs_im + v.pbase, f.w_re + v.pbase,
                                     f.w_im + v.pbase};
@@ -410,15 +417,7 @@ __global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
                            : make_buf(static_cast<const float*>(f.c_re) + v.row0 * N, v.extN * 4);
     const BufRes rg_i = DX ? make_buf(a.dy_im + v.row0 * D, v.extD * 4)
                            : make_buf(static_cast<const float*>(f.c_im) + v.row0 * N, v.extN * 4);
-    float gy_r[NLT][4], gy_i[NLT][4];
-#pragma unroll
-    for (int tt = 0; tt < NLT; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t off = (uint32_t)(tt * 16 + 4 * g + r) * (DX ? v.sD : v.sN) + 16 * w + li;
-            gy_r[tt][r] = buf_f32(rg_r, off);
-            gy_i[tt][r] = DX ? buf_f32(rg_i, off) : -buf_f32(rg_i, off);
-        }
+    float gy_r[NLT][4], gy_i[NLT][4];  // loaded after the scores (registers)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
 
@@ -451,66 +450,84 @@ __global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
         for (int r = 0; r < 4; ++r) ctile_scale(acc[lt], r, wr[r], -wi[r]);
     }
 
-    // ---- 2. score tiles q in [q0, q1) -> M in registers:
+    // ---- 2. score tiles -> M in registers:
     // dX: G = C B^T, M = conj(G L);  dB: P = dY X^H, M = conj(L) P
-    const int q0 = (w * NP) / W, q1 = ((w + 1) * NP) / W;
     floatx4 m_r[MQ], m_i[MQ];
-    {
-        int tt = 0, lt = q0;  // tt-major decode of q0
+    // tile q (tt-major) with the first row set staged from row s0 on
+    auto score_tile = [&](int q, int s0, floatx4& mr, floatx4& mi) {
+        int tt = 0, lt = q;  // tt-major decode
         while (lt > tt) {
             lt -= tt + 1;
             ++tt;
         }
+        const int t0 = tt * 16, l0 = lt * 16;
+        CTile sq;
+        ctile_zero(sq);
 #pragma unroll
-        for (int j = 0; j < MQ; ++j) {
-            if (q0 + j < q1) {  // wave-uniform
-                const int t0 = tt * 16, l0 = lt * 16;
-                CTile sq;
-                ctile_zero(sq);
+        for (int k = 0; k < NK; ++k) {
+            const floatx4 cr = row4(lds_s, t0 - s0 + li, 4 * k + g);
+            const floatx4 ci = row4(lds_s + SPLANE, t0 - s0 + li, 4 * k + g);
+            const floatx4 br = row4(lds_o, l0 + li, 4 * k + g);
+            const floatx4 bi0 = row4(lds_o + PLANE, l0 + li, 4 * k + g);
+            const floatx4 bi = DX ? bi0 : -bi0;
+            const floatx4 cs = cr + ci, bs = br + bi;
 #pragma unroll
-                for (int k = 0; k < NK; ++k) {
-                    const floatx4 cr = row4(lds_s, t0 + li, 4 * k + g);
-                    const floatx4 ci = row4(lds_s + PLANE, t0 + li, 4 * k + g);
-                    const floatx4 br = row4(lds_o, l0 + li, 4 * k + g);
-                    const floatx4 bi0 = row4(lds_o + PLANE, l0 + li, 4 * k + g);
-                    const floatx4 bi = DX ? bi0 : -bi0;
-                    const floatx4 cs = cr + ci, bs = br + bi;
+            for (int e = 0; e < 4; ++e) ctile_mac(sq, cr[e], ci[e], cs[e], br[e], bi[e], bs[e]);
+        }
+        // register r <-> (t = t0 + 4g + r, l = l0 + li)
+        const int l = l0 + li;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        ctile_mac(sq, cr[e], ci[e], cs[e], br[e], bi[e], bs[e]);
-                }
-                // register r <-> (t = t0 + 4g + r, l = l0 + li)
-                const int l = l0 + li;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = t0 + 4 * g + r;
-                    float lr = 0.f, lim = 0.f;
-                    if (tt > lt || t >= l) seg_exp(lacs_r, lacs_i, t, l, false, lr, lim);
-                    const float s_r = ctile_re(sq, r), s_i = ctile_im(sq, r);
-                    if constexpr (DX) {
-                        m_r[j][r] = s_r * lr - s_i * lim;  // conj(G L)
-                        m_i[j][r] = -(s_r * lim + s_i * lr);
-                    } else {
-                        m_r[j][r] = lr * s_r + lim * s_i;  // conj(L) P
-                        m_i[j][r] = lr * s_i - lim * s_r;
-                    }
-                }
-                if (++lt > tt) {
-                    lt = 0;
-                    ++tt;
-                }
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * g + r;
+            float lr = 0.f, lim = 0.f;
+            if (tt > lt || t >= l) seg_exp(lacs_r, lacs_i, t, l, false, lr, lim);
+            const float s_r = ctile_re(sq, r), s_i = ctile_im(sq, r);
+            if constexpr (DX) {
+                mr[r] = s_r * lr - s_i * lim;  // conj(G L)
+                mi[r] = -(s_r * lim + s_i * lr);
+            } else {
+                mr[r] = lr * s_r + lim * s_i;  // conj(L) P
+                mi[r] = lr * s_i - lim * s_r;
             }
         }
-    }
+    };
+    // tiles per wave, in fixed slots: the seven with tt >= 2 (q = 3 .. 9) as
+    // q = 3 + 2w and 4 + 2w (wave 3: 9 only), then q = 0, 1, 2 to waves 1, 2, 3
+    int qs[MQ];
+    qs[0] = 3 + 2 * w;
+    qs[1] = w < 3 ? 4 + 2 * w : 2;
+    qs[2] = w == 1 ? 0 : 1;
+    const int nq = (w == 1 || w == 2) ? 3 : 2;
+    static_assert(MQ == 3 && W == 4 && NLT == 4, "the split is for C = 64");
+#pragma unroll
+    for (int j = 0; j < MQ; ++j)
+        if (j < nq && qs[j] >= 3) score_tile(qs[j], C / 2, m_r[j], m_i[j]);
+    __syncthreads();  // every wave is done with rows 32-63 of the first set
+    stage_plane(s_re, lds_s, 0, 0, SIPP);
+    stage_plane(s_im, lds_s + SPLANE, SIPP % W, 0, SIPP);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < MQ; ++j)
+        if (j < nq && qs[j] < 3) score_tile(qs[j], 0, m_r[j], m_i[j]);
+    // the causal product's B operand, rows 16 tt + 4g + r, column 16w + li
+#pragma unroll
+    for (int tt = 0; tt < NLT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (uint32_t)(tt * 16 + 4 * g + r) * (DX ? v.sD : v.sN) + 16 * w + li;
+            gy_r[tt][r] = buf_f32(rg_r, off);
+            gy_i[tt][r] = DX ? buf_f32(rg_i, off) : -buf_f32(rg_i, off);
+        }
 
-    // ---- the M tiles replace the first row set
+    // ---- the M tiles replace the second row set
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < MQ; ++j) {
-        if (q0 + j < q1) {
-            const int q = q0 + j;
-            *reinterpret_cast<floatx4*>(lds_s + (2 * q) * 256 + 4 * lane) = m_r[j];
-            *reinterpret_cast<floatx4*>(lds_s + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
+        if (j < nq) {
+            const int q = qs[j];
+            *reinterpret_cast<floatx4*>(lds_o + (2 * q) * 256 + 4 * lane) = m_r[j];
+            *reinterpret_cast<floatx4*>(lds_o + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
         }
     }
     __syncthreads();
@@ -540,8 +557,8 @@ __global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
 #pragma unroll
         for (int lt = 0; lt <= tt; ++lt) {
             const int q = tt * (tt + 1) / 2 + lt;
-            const floatx4 mr = *reinterpret_cast<const floatx4*>(lds_s + (2 * q) * 256 + 4 * lane);
-            const floatx4 mi = *reinterpret_cast<const floatx4*>(lds_s + (2 * q + 1) * 256 + 4 * lane);
+            const floatx4 mr = *reinterpret_cast<const floatx4*>(lds_o + (2 * q) * 256 + 4 * lane);
+            const floatx4 mi = *reinterpret_cast<const floatx4*>(lds_o + (2 * q + 1) * 256 + 4 * lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 ctile_mac(acc[lt], mr[r], mi[r], mr[r] + mi[r], gy_r[tt][r], gy_i[tt][r], ys[r]);
@@ -566,7 +583,7 @@ __global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
         const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
         const BufRes rdx_r = make_buf(a.dx_re + v.row0 * D, v.extD * 4);
         const BufRes rdx_i = make_buf(a.dx_im + v.row0 * D, v.extD * 4);
-        float* const qpart = lds_o;  // [wave][row][re, im]; the B rows are no longer read
+        float* const qpart = lds_s;  // [wave][row][re, im]; the first row set is no longer read
         // conj(x) dx for the 16 rows m = 4 lt + r of this lane's column
         float pr[16], pi[16];
 #pragma unroll
@@ -619,14 +636,19 @@ __global__ __launch_bounds__(256) void k_bwd_lds(BwdArgs a) {
 //     the product with conj(B) rows; exchanged through LDS (over the X rows).
 //  3. dC[t, n] += sum_l K[t, l] conj(B[l, n]).
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dc_lds(
+    BwdArgs a) {
     constexpr int C = 64, N = 64, D = 64, NK = N / 16, PT = D / 16, W = N / 16, NLT = C / 16;
     static_assert(N == D, "the two staged row sets share one row width");
     constexpr int NP = NLT * (NLT + 1) / 2;  // causal tiles (tt >= lt), tt-major
     constexpr int MQ = (NP + W - 1) / W;
     constexpr int PLANE = C * D, IPP = PLANE / 256;
-    __shared__ floatx4 lds_g4[2 * PLANE / 4];  // dY rows
-    __shared__ floatx4 lds_x4[2 * PLANE / 4];  // X rows, later the K tiles
+    constexpr int XPLANE = PLANE / 2, XIPP = XPLANE / 256;  // half of the X rows
+    // The X rows are staged in halves: rows 0-31 for the seven tiles with lt < 2
+    // (and the q2 rows of waves 0 and 1), then rows 32-63 for the other three
+    // (and waves 2 and 3): 52 KB of LDS, three workgroups per CU.
+    __shared__ floatx4 lds_g4[2 * PLANE / 4];   // dY rows, later the K tiles
+    __shared__ floatx4 lds_x4[2 * XPLANE / 4];  // X rows, half at a time
     __shared__ floatx4 lds_a4[1024 / 4];       // acs re, acs im (fp64), e re, e im
     float* const ldg = reinterpret_cast<float*>(lds_g4);
     float* const ldx = reinterpret_cast<float*>(lds_x4);
@@ -644,20 +666,21 @@ __global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
     const ChunkView v = chunk_view(a, chunk, C, N, D);
 
     // ---- 0. staging
-    auto stage_plane = [&](const void* src, float* dst_plane, int first) {
+    // rows r0 .. r0 + nblk * 256 / D - 1 of one plane, swizzled by staged row index
+    auto stage_plane = [&](const void* src, float* dst_plane, int first, int r0, int nblk) {
         const BufRes r = make_buf(static_cast<const float*>(src) + v.row0 * D, v.extD * 4);
-        for (int blk = (w - first + W) % W; blk < IPP; blk += W) {  // wave-uniform
+        for (int blk = (w - first + W) % W; blk < nblk; blk += W) {  // wave-uniform
             const int u = blk * 64 + lane;  // physical 16-byte piece within the plane
             const int row = u / (D / 4), pc = u % (D / 4);
-            const uint32_t voff = ((uint32_t)row * v.sD + 4 * lds_swz<D>(row, pc)) * 4;
+            const uint32_t voff = ((uint32_t)(r0 + row) * v.sD + 4 * lds_swz<D>(row, pc)) * 4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(dst_plane + blk * 256), 16, voff,
                                                      0, 0, 0);
         }
     };
-    stage_plane(a.dy_re, ldg, 0);
-    stage_plane(a.dy_im, ldg + PLANE, IPP % W);
-    stage_plane(f.x_re, ldx, (2 * IPP) % W);
-    stage_plane(f.x_im, ldx + PLANE, (3 * IPP) % W);
+    stage_plane(a.dy_re, ldg, 0, 0, IPP);
+    stage_plane(a.dy_im, ldg + PLANE, IPP % W, 0, IPP);
+    stage_plane(f.x_re, ldx, 0, 0, XIPP);
+    stage_plane(f.x_im, ldx + XPLANE, XIPP % W, 0, XIPP);
     if (w == W - 1) {
         const void* const aux[4] = {f.acs_re + v.pbase, f.acs_im + v.pbase, f.e_re + v.pbase,
                                     f.e_im + v.pbase};
@@ -679,18 +702,10 @@ __global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
             hreg_r[k][e] = buf_f32(rh_r, fi);
             hreg_i[k][e] = -buf_f32(rh_i, fi);
         }
-    // conj(B[16 lt + 4g + r][16w + li]), the B operand of step 3
+    // conj(B[16 lt + 4g + r][16w + li]), the B operand of step 3 (loaded after the scores)
     const BufRes rb_r = make_buf(static_cast<const float*>(f.b_re) + v.row0 * N, v.extN * 4);
     const BufRes rb_i = make_buf(static_cast<const float*>(f.b_im) + v.row0 * N, v.extN * 4);
     float cb_r[NLT][4], cb_i[NLT][4];
-#pragma unroll
-    for (int lt = 0; lt < NLT; ++lt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t off = (uint32_t)(lt * 16 + 4 * g + r) * v.sN + 16 * w + li;
-            cb_r[lt][r] = buf_f32(rb_r, off);
-            cb_i[lt][r] = -buf_f32(rb_i, off);
-        }
     // y rows 16 w + li for q2
     const BufRes ry_r = make_buf(a.y_re + v.row0 * D, v.extD * 4);
     const BufRes ry_i = make_buf(a.y_im + v.row0 * D, v.extD * 4);
@@ -708,14 +723,16 @@ __global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
     };
     const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
 
-    // ---- the y half of q and the dD partial for row t = 16 w + li
-    {
+    // ---- the y half of q and the dD partial for row t = 16 w + li, with the X
+    // rows staged from row x0 on (called in the phase that holds row t)
+    auto q2_row = [&](int x0) {
         const int t = 16 * w + li;
         float qr = 0.f, qi = 0.f, dd = 0.f;
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
             const floatx4 gr = row4(ldg, t, 4 * k + g), gi = row4(ldg + PLANE, t, 4 * k + g);
-            const floatx4 xr = row4(ldx, t, 4 * k + g), xi = row4(ldx + PLANE, t, 4 * k + g);
+            const floatx4 xr = row4(ldx, t - x0, 4 * k + g);
+            const floatx4 xi = row4(ldx + XPLANE, t - x0, 4 * k + g);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float ur = yq_r[k][e] - dk * xr[e], ui = yq_i[k][e] - dk * xi[e];
@@ -732,7 +749,8 @@ __global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
             a.q2_im[v.pbase + t] = qi;
             a.ddp[v.pbase + t] = dd;
         }
-    }
+    };
+    if (w < 2) q2_row(0);
 
     // ---- 1. state term dY H_c^H, then the row factor conj(e[t])
     CTile acc[NLT];
@@ -759,58 +777,78 @@ __global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
     }
 
     // ---- 2. tiles (tt, lt), lt <= tt: P^T = conj(X) dY^T, K = conj(L) P
-    const int q0 = (w * NP) / W, q1 = ((w + 1) * NP) / W;
     floatx4 m_r[MQ], m_i[MQ];
-    {
-        int tt = 0, lt = q0;  // tt-major decode of q0
+    // tile q (tt-major) with the X rows staged from row x0 on
+    auto score_tile = [&](int q, int x0, floatx4& mr, floatx4& mi) {
+        int tt = 0, lt = q;  // tt-major decode
         while (lt > tt) {
             lt -= tt + 1;
             ++tt;
         }
+        const int t0 = tt * 16, l0 = lt * 16;
+        CTile pq;
+        ctile_zero(pq);
 #pragma unroll
-        for (int j = 0; j < MQ; ++j) {
-            if (q0 + j < q1) {  // wave-uniform
-                const int t0 = tt * 16, l0 = lt * 16;
-                CTile pq;
-                ctile_zero(pq);
+        for (int k = 0; k < PT; ++k) {
+            const floatx4 xr = row4(ldx, l0 - x0 + li, 4 * k + g);
+            const floatx4 xi = -row4(ldx + XPLANE, l0 - x0 + li, 4 * k + g);
+            const floatx4 gr = row4(ldg, t0 + li, 4 * k + g);
+            const floatx4 gi = row4(ldg + PLANE, t0 + li, 4 * k + g);
+            const floatx4 xs = xr + xi, gs = gr + gi;
 #pragma unroll
-                for (int k = 0; k < PT; ++k) {
-                    const floatx4 xr = row4(ldx, l0 + li, 4 * k + g);
-                    const floatx4 xi = -row4(ldx + PLANE, l0 + li, 4 * k + g);
-                    const floatx4 gr = row4(ldg, t0 + li, 4 * k + g);
-                    const floatx4 gi = row4(ldg + PLANE, t0 + li, 4 * k + g);
-                    const floatx4 xs = xr + xi, gs = gr + gi;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        ctile_mac(pq, xr[e], xi[e], xs[e], gr[e], gi[e], gs[e]);
-                }
-                // register r <-> (t = t0 + li, l = l0 + 4g + r)
-                const int t = t0 + li;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int l = l0 + 4 * g + r;
-                    float lr = 0.f, lim = 0.f;
-                    if (lt < tt || t >= l) seg_exp(lacs_r, lacs_i, t, l, false, lr, lim);
-                    const float p_r = ctile_re(pq, r), p_i = ctile_im(pq, r);
-                    m_r[j][r] = lr * p_r + lim * p_i;  // conj(L) P
-                    m_i[j][r] = lr * p_i - lim * p_r;
-                }
-                if (++lt > tt) {
-                    lt = 0;
-                    ++tt;
-                }
-            }
+            for (int e = 0; e < 4; ++e) ctile_mac(pq, xr[e], xi[e], xs[e], gr[e], gi[e], gs[e]);
         }
-    }
+        // register r <-> (t = t0 + li, l = l0 + 4g + r)
+        const int t = t0 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int l = l0 + 4 * g + r;
+            float lr = 0.f, lim = 0.f;
+            if (lt < tt || t >= l) seg_exp(lacs_r, lacs_i, t, l, false, lr, lim);
+            const float p_r = ctile_re(pq, r), p_i = ctile_im(pq, r);
+            mr[r] = lr * p_r + lim * p_i;  // conj(L) P
+            mi[r] = lr * p_i - lim * p_r;
+        }
+    };
+    // tiles per wave, in fixed slots: the seven with lt < 2 (q = 0 1 2 3 4 6 7)
+    // two per wave (wave 3 one), then q = 5, 8, 9 to waves 1, 2, 3
+    auto a_tile = [](int i) { return i < 5 ? i : i + 1; };
+    int qs[MQ];
+    qs[0] = a_tile(2 * w);
+    qs[1] = w < 3 ? a_tile(2 * w + 1) : 9;
+    qs[2] = w == 1 ? 5 : 8;
+    const int nq = (w == 1 || w == 2) ? 3 : 2;
+    static_assert(MQ == 3 && W == 4 && NLT == 4, "the split is for C = 64");
+    auto second_half = [](int q) { return q == 5 || q >= 8; };
+#pragma unroll
+    for (int j = 0; j < MQ; ++j)
+        if (j < nq && !second_half(qs[j])) score_tile(qs[j], 0, m_r[j], m_i[j]);
+    __syncthreads();  // every wave is done with X rows 0-31
+    stage_plane(f.x_re, ldx, 0, C / 2, XIPP);
+    stage_plane(f.x_im, ldx + XPLANE, XIPP % W, C / 2, XIPP);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (w >= 2) q2_row(C / 2);
+#pragma unroll
+    for (int j = 0; j < MQ; ++j)
+        if (j < nq && second_half(qs[j])) score_tile(qs[j], C / 2, m_r[j], m_i[j]);
+#pragma unroll
+    for (int lt = 0; lt < NLT; ++lt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (uint32_t)(lt * 16 + 4 * g + r) * v.sN + 16 * w + li;
+            cb_r[lt][r] = buf_f32(rb_r, off);
+            cb_i[lt][r] = -buf_f32(rb_i, off);
+        }
 
-    // ---- the K tiles replace the X rows
+    // ---- the K tiles replace the dY rows
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < MQ; ++j) {
-        if (q0 + j < q1) {
-            const int q = q0 + j;
-            *reinterpret_cast<floatx4*>(ldx + (2 * q) * 256 + 4 * lane) = m_r[j];
-            *reinterpret_cast<floatx4*>(ldx + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
+        if (j < nq) {
+            const int q = qs[j];
+            *reinterpret_cast<floatx4*>(ldg + (2 * q) * 256 + 4 * lane) = m_r[j];
+            *reinterpret_cast<floatx4*>(ldg + (2 * q + 1) * 256 + 4 * lane) = m_i[j];
         }
     }
     __syncthreads();
@@ -824,8 +862,8 @@ __global__ __launch_bounds__(256) void k_bwd_dc_lds(BwdArgs a) {
 #pragma unroll
         for (int tt = lt; tt < NLT; ++tt) {
             const int q = tt * (tt + 1) / 2 + lt;
-            const floatx4 mr = *reinterpret_cast<const floatx4*>(ldx + (2 * q) * 256 + 4 * lane);
-            const floatx4 mi = *reinterpret_cast<const floatx4*>(ldx + (2 * q + 1) * 256 + 4 * lane);
+            const floatx4 mr = *reinterpret_cast<const floatx4*>(ldg + (2 * q) * 256 + 4 * lane);
+            const floatx4 mi = *reinterpret_cast<const floatx4*>(ldg + (2 * q + 1) * 256 + 4 * lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 ctile_mac(acc[tt], mr[r], mi[r], mr[r] + mi[r], cb_r[lt][r], cb_i[lt][r], bs[r]);
