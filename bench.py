@@ -75,6 +75,20 @@ def chunk_state_flops(B, T, H, D, N, C):
     return 8 * B * H * nC * C * N * D
 
 
+def state_scan_hbm_bytes(B, T, H, D, N, C, in_bytes=4):
+    """The fused chunk-state scan: read the B and X rows once, write every carry-in
+    state H_c and the final state (fp32)."""
+    nC = math.ceil(T / C)
+    return B * T * H * (N + D) * 2 * in_bytes + B * H * (nC + 1) * N * D * 2 * 4
+
+
+def cumsum_hbm_bytes(B, T, H, C):
+    """Read dt (4 bytes) and write the fp64 cumsum, exp(acs) and w (32 bytes) per
+    position, plus the chunk decay (8 bytes) per chunk."""
+    nC = math.ceil(T / C)
+    return B * T * H * 4 + B * H * nC * C * 32 + B * H * nC * 8
+
+
 def forward_hbm_bytes(B, T, H, D, N, in_bytes=4):
     """Read x, B, C, dt once; write y and the final state once."""
     return (B * T * H * (D + 2 * N) * 2 * in_bytes + B * T * H * 4
@@ -389,10 +403,33 @@ def cpu_baseline(inp, budget_s=15.0):
     while bs == s["B"] and sum(times) < budget_s * 0.6 and len(times) < 10:
         times.append(run(bs))
     t = float(np.median(times))
+    # one thread on one (b, h) sequence, scaled to the H sequences a token spans
+    one = _one_sequence(inp).complex()
+    t_one = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.forward(*one, nthreads=1, lib=lib)
+        t_one.append(time.perf_counter() - t0)
+    t1s = float(np.median(t_one))
     return {"value": bs * s["T"] / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{bs} of {s['B']} batch rows (all {s['H']} heads, full T={s['T']}) of the "
                       f"same workload, median of {len(times)} run(s); fp64 sequential recurrence, "
-                      f"OpenMP over (batch, head); {t:.2f} s wall per run"}
+                      f"OpenMP over (batch, head); {t:.2f} s wall per run",
+            "single_thread": {"value": s["T"] / (s["H"] * t1s), "unit": "tokens/s", "cores": 1,
+                              "sample": f"one (b, h) sequence of T={s['T']} on one thread, median "
+                                        f"of 3 runs ({t1s:.3f} s), scaled by the {s['H']} heads "
+                                        f"a token spans"}}
+
+
+def _one_sequence(inp):
+    """Batch row 0, head 0 of the workload (H = 1)."""
+    import cssd_workloads as wl
+    import numpy as np
+    c = lambda a: None if a is None else np.ascontiguousarray(a[:1, :, :1])
+    h = lambda a: None if a is None else np.ascontiguousarray(a[:1])
+    return wl.ForwardInputs(c(inp.x_re), c(inp.x_im), c(inp.B_re), c(inp.B_im), c(inp.C_re),
+                            c(inp.C_im), c(inp.dt), h(inp.A_re), h(inp.A_im), h(inp.Dskip),
+                            inp.chunk, c(inp.h0_re), c(inp.h0_im), inp.in_dtype, inp.name)
 
 
 def _rows(inp, bs):
@@ -454,6 +491,17 @@ def main():
                      "traffic": traffic, "algorithmic_flops_per_launch": k2_flops,
                      "avg_launch_ms": round(k2_ms, 5)},
         "kernels_avg_ms": {k: round(v, 5) for k, v in kern.items()},
+    }
+    # the other two forward kernels, by their algorithmic work
+    ss_ms, cs_ms = kern.get("k_state_scan"), kern.get("k_cumsum")
+    ss_flops = chunk_state_flops(B, T, H, D, N, C)
+    out["kernels_achieved"] = {
+        "k_state_scan": {"TFLOP/s": round(ss_flops / (ss_ms * 1e-3) / 1e12, 2),
+                         "frac_fp32_mfma": round(ss_flops / (ss_ms * 1e-3) / 1e12
+                                                 / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "GB/s": round(state_scan_hbm_bytes(B, T, H, D, N, C) / (ss_ms * 1e-3)
+                                       / 1e9, 1)},
+        "k_cumsum": {"GB/s": round(cumsum_hbm_bytes(B, T, H, C) / (cs_ms * 1e-3) / 1e9, 1)},
     }
     fwd_flops = k2_flops + chunk_state_flops(B, T, H, D, N, C)
     out["forward_mfma_frac"] = round(fwd_flops / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)
