@@ -43,6 +43,10 @@
 // R_{c+1} and H_c from their MFMA-fragment layout, directly for products that
 // contract over n and element-wise (four loads per fragment row) for the
 // transposed products that contract over p.
+// At N = D = C = 64 the same three products run in the chunk-staged kernels
+// k_bwd_lds<true> (dX), k_bwd_lds<false> (dB) and k_bwd_dc_lds (dC): one
+// workgroup per chunk with its rows in LDS, the organisation of the forward
+// chunk-scan kernel (the comments at those kernels give the details).
 #include "cssd_device.h"
 #include "cssd_launch.h"
 #include "k_chunk_scan_lds.h"

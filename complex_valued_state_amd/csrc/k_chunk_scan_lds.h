@@ -21,7 +21,8 @@
 //  3. barrier; the M tiles overwrite the B rows in LDS; barrier.
 //  4. Y_diag: every causal tile's M from LDS times the wave's columns of X.
 // Two workgroups share a CU (the LDS bounds it), so one's staging overlaps the
-// other's matrix work.
+// other's matrix work; three at N = D = C = 64, where the B rows are staged in
+// halves (below).
 #pragma once
 
 #include "k_chunk_scan.h"
