@@ -411,7 +411,17 @@ def cpu_baseline(inp, budget_s=15.0):
         oracle.forward(*one, nthreads=1, lib=lib)
         t_one.append(time.perf_counter() - t0)
     t1s = float(np.median(t_one))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": bs * s["T"] / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{bs} of {s['B']} batch rows (all {s['H']} heads, full T={s['T']}) of the "
                       f"same workload, median of {len(times)} run(s); fp64 sequential recurrence, "
                       f"OpenMP over (batch, head); {t:.2f} s wall per run",

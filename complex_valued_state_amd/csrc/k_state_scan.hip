@@ -607,10 +607,8 @@ static hipError_t launch_scan_in(const FwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_state_scan(const FwdArgs& a, hipStream_t s) {
-#ifndef CSSD_SCAN_NO_LDS
     if (a.C == 64 && a.N == 64 && a.D == 64)
         return a.in_dtype == 1 ? launch_scan_lds<InBF16>(a, s) : launch_scan_lds<InF32>(a, s);
-#endif
     return a.in_dtype == 1 ? launch_scan_in<InBF16>(a, s) : launch_scan_in<InF32>(a, s);
 }
 
