@@ -54,7 +54,7 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
               "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",),
               "k_born_bf16": ("k_born.hip",), "k_state_scan": ("k_state_scan.hip",),
-              "k_state_scan_lds": ("k_state_scan.hip",)}
+              "k_state_scan_lds": ("k_state_scan.hip",), "k_state_scan_mm": ("k_state_scan.hip",)}
 
 
 # ---------------------------------------------------------------------------

@@ -22,14 +22,13 @@
 // a wave's X row segment is one 64-byte piece instead of two 32-byte ones;
 // tile q then holds the columns p = 16 pt0 + 2 (lane%16) + q, and each store
 // puts the values back in their fragment slots (measured at B8 T2048 H48 N64
-// D64 C64: 0.45 -> 0.42 ms, with 8 k-steps in flight).  For fp32 inputs the
+// D64 C64, before that shape moved to k_state_scan_mm: 0.45 -> 0.42 ms, with 8
+// k-steps in flight).  For fp32 inputs the
 // paired 8-byte load measured slower (0.38 -> 0.41 ms) and is off.  The
 // operands (B and X) of the next DIST k-steps are kept in flight in a register
 // ring that runs on across chunk boundaries.  All workgroups of one (b, h) go to
 // the same XCD (dispatch is round-robin over the 8 XCDs), so the B and X rows
 // that several waves of that (b, h) read are fetched into one L2.
-#include <type_traits>
-
 #include "cssd_device.h"
 #include "cssd_launch.h"
 
@@ -274,10 +273,10 @@ struct AdjExtra {
     double *z_re, *z_im;         // [(b, h, c) * 2 + half]
 };
 
-template <typename In, bool ADJ>
+template <bool ADJ>
 __global__ __launch_bounds__(256) void k_state_scan_lds(
-    const typename In::T* __restrict__ x_re, const typename In::T* __restrict__ x_im,
-    const typename In::T* __restrict__ b_re, const typename In::T* __restrict__ b_im,
+    const float* __restrict__ x_re, const float* __restrict__ x_im,
+    const float* __restrict__ b_re, const float* __restrict__ b_im,
     const float* __restrict__ w_re, const float* __restrict__ w_im,
     const float* __restrict__ cd_re, const float* __restrict__ cd_im,
     const float* __restrict__ h0_re, const float* __restrict__ h0_im, float* __restrict__ st_re,
@@ -315,20 +314,12 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
             hi[q][r] = h0_im != nullptr ? h0_im[sbase + r * D + 16 * q] : 0.f;
         }
 
-    // one stage in registers: B (this half's 32 columns) and X (64 columns),
-    // both planes, as fetched (fp32: 4 values, bf16: 8 values per 16 bytes)
-    constexpr bool kBF16 = sizeof(typename In::T) == 2;
-    struct StageF32 {
+    // one stage in registers: B (this half's 32 columns) and X (64 columns), both planes
+    struct StageIn {
         floatx4 b[2], x[2][2];
     };
-    struct StageBF16 {
-        u32x4 b, x[2];
-    };
-    using StageIn = std::conditional_t<kBF16, StageBF16, StageF32>;
-    // fp32: B row rb, 16-byte unit ub of each plane; X rows idx / 16, units idx % 16
-    // bf16: B plane wv / 2, row (tid / 4) % 32, 8-value unit tid % 4; X row tid / 8, unit tid % 8
-    const int rb = kBF16 ? (tid >> 2) & 31 : tid >> 3, ub = kBF16 ? tid & 3 : tid & 7;
-    const int pb = wv >> 1;  // bf16: the B plane this wave fetches (wave-uniform)
+    // B row rb, 16-byte unit ub of each plane; X rows idx / 16, units idx % 16
+    const int rb = tid >> 3, ub = tid & 7;
     // the chunk of stage qs (the adjoint walks the chunks backwards)
     auto chunk_of = [&](int qs) { return ADJ ? nC - 1 - qs / NS : qs / NS; };
     auto gload = [&](int qs, StageIn& R) {
@@ -337,61 +328,27 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
         const int valid = (int)min<int64_t>((int64_t)C, T - t0);
         const int64_t row0 = (b * T + t0) * H + h;
         const uint32_t extN = (uint32_t)(valid - 1) * sN + N, extD = (uint32_t)(valid - 1) * sD + D;
-        constexpr uint32_t es = sizeof(typename In::T);
-        if constexpr (kBF16) {
-            const BufRes vb = make_buf((pb ? b_im : b_re) + row0 * N, extN * es);
-            const BufRes vx_r = make_buf(x_re + row0 * D, extD * es), vx_i = make_buf(x_im + row0 * D, extD * es);
-            const uint32_t eb = (uint32_t)(s * kSR + rb) * sN + 32 * h2 + 8 * ub;
-            R.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vb, eb * es, 0, 0));
-            const uint32_t ex = (uint32_t)(s * kSR + (tid >> 3)) * sD + 8 * (tid & 7);
-            R.x[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vx_r, ex * es, 0, 0));
-            R.x[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vx_i, ex * es, 0, 0));
-        } else {
-            const BufRes vb_r = make_buf(b_re + row0 * N, extN * es), vb_i = make_buf(b_im + row0 * N, extN * es);
-            const BufRes vx_r = make_buf(x_re + row0 * D, extD * es), vx_i = make_buf(x_im + row0 * D, extD * es);
-            const uint32_t eb = (uint32_t)(s * kSR + rb) * sN + 32 * h2 + 4 * ub;
-            R.b[0] = buf_f32x4(vb_r, eb);
-            R.b[1] = buf_f32x4(vb_i, eb);
+        const BufRes vb_r = make_buf(b_re + row0 * N, extN * 4u), vb_i = make_buf(b_im + row0 * N, extN * 4u);
+        const BufRes vx_r = make_buf(x_re + row0 * D, extD * 4u), vx_i = make_buf(x_im + row0 * D, extD * 4u);
+        const uint32_t eb = (uint32_t)(s * kSR + rb) * sN + 32 * h2 + 4 * ub;
+        R.b[0] = buf_f32x4(vb_r, eb);
+        R.b[1] = buf_f32x4(vb_i, eb);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int idx = tid + 256 * k, rx = idx >> 4, ux = idx & 15;
-                const uint32_t ex = (uint32_t)(s * kSR + rx) * sD + 4 * ux;
-                R.x[0][k] = buf_f32x4(vx_r, ex);
-                R.x[1][k] = buf_f32x4(vx_i, ex);
-            }
+        for (int k = 0; k < 2; ++k) {
+            const int idx = tid + 256 * k, rx = idx >> 4, ux = idx & 15;
+            const uint32_t ex = (uint32_t)(s * kSR + rx) * sD + 4 * ux;
+            R.x[0][k] = buf_f32x4(vx_r, ex);
+            R.x[1][k] = buf_f32x4(vx_i, ex);
         }
     };
-    // 8 bf16 values -> two groups of 4 floats
-    auto widen = [](const u32x4& v, floatx4& lo, floatx4& hi) {
-        lo = floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
-                     __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
-        hi = floatx4{__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xffff0000u),
-                     __uint_as_float(v[3] << 16), __uint_as_float(v[3] & 0xffff0000u)};
-    };
     auto lstore = [&](int buf, const StageIn& R) {
-        if constexpr (kBF16) {
-            floatx4 lo, hi;
-            widen(R.b, lo, hi);
-            const int u = rb * 8 + ((2 * ub) ^ swz_b(rb));  // units 2 ub, 2 ub + 1 stay adjacent
-            sb[buf][pb][u] = lo;
-            sb[buf][pb][u + 1] = hi;
-            const int rx = tid >> 3, ux = 2 * (tid & 7);
+        sb[buf][0][rb * 8 + (ub ^ swz_b(rb))] = R.b[0];
+        sb[buf][1][rb * 8 + (ub ^ swz_b(rb))] = R.b[1];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                widen(R.x[k], lo, hi);
-                const int v = rx * 16 + (ux ^ swz_x(rx));
-                sx[buf][k][v] = lo;
-                sx[buf][k][v + 1] = hi;
-            }
-        } else {
-            sb[buf][0][rb * 8 + (ub ^ swz_b(rb))] = R.b[0];
-            sb[buf][1][rb * 8 + (ub ^ swz_b(rb))] = R.b[1];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int idx = tid + 256 * k, rx = idx >> 4, ux = idx & 15;
-                sx[buf][0][rx * 16 + (ux ^ swz_x(rx))] = R.x[0][k];
-                sx[buf][1][rx * 16 + (ux ^ swz_x(rx))] = R.x[1][k];
-            }
+        for (int k = 0; k < 2; ++k) {
+            const int idx = tid + 256 * k, rx = idx >> 4, ux = idx & 15;
+            sx[buf][0][rx * 16 + (ux ^ swz_x(rx))] = R.x[0][k];
+            sx[buf][1][rx * 16 + (ux ^ swz_x(rx))] = R.x[1][k];
         }
     };
     float wn_r, wn_i;  // the next chunk's weights, position lane
@@ -534,13 +491,12 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
     }
 }
 
-template <typename In>
 static hipError_t launch_scan_lds(const FwdArgs& a, hipStream_t s) {
     const int64_t nbh = a.B * a.H;
     const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * 2;
-    typedef const typename In::T* P;
+    typedef const float* P;
     const AdjExtra none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-    hipLaunchKernelGGL((k_state_scan_lds<In, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_state_scan_lds<false>), dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<P>(a.x_re), static_cast<P>(a.x_im), static_cast<P>(a.b_re),
                        static_cast<P>(a.b_im),
                        a.w_re, a.w_im, a.cd_re, a.cd_im, a.h0_re, a.h0_im, a.st_re, a.st_im,
@@ -561,11 +517,225 @@ hipError_t launch_state_scan_adjoint(const FwdArgs& a, const float* dy_re, const
     const int64_t nbh = a.B * a.H;
     const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * 2;
     const AdjExtra adj = {a.st_re, a.st_im, hT_re, hT_im, z_re, z_im};
-    hipLaunchKernelGGL((k_state_scan_lds<InF32, true>), dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_state_scan_lds<true>), dim3((unsigned)blocks), dim3(256), 0, s,
                        dy_re, dy_im, static_cast<const float*>(a.c_re),
                        static_cast<const float*>(a.c_im), a.e_re, a.e_im, a.cd_re, a.cd_im,
                        dhT_re, dhT_im, r_re, r_im, dh0_re, dh0_im, a.T, (int)a.H, (int)a.nC, nbh,
                        adj);
+    return hipGetLastError();
+}
+
+// bf16 inputs at N = D = C = 64: the same scan with the chunk-state contraction
+// on the bf16 matrix cores.  v_mfma_f32_16x16x32_bf16 contracts 32 time steps in
+// one instruction, with lane i + 16 g holding the 8 consecutive steps 8g .. 8g+7
+// of row i of each operand, so both operands are staged transposed: a row per
+// feature (n of w B, p of X) over the 32 steps of a half chunk.  The weights w
+// are applied while staging, in fp32, and w B is then rounded to bf16 as an
+// operand (B and X are bf16 already); the products accumulate in fp32 and the
+// carried state stays fp32.  A complex product is four real products with the
+// imaginary A operand negated for the real part (a sum of bf16 operands would
+// round).  Workgroup and wave mapping, carry-in stores and the chunk-to-chunk
+// update are those of k_state_scan_lds.
+namespace {
+typedef __bf16 bf16x8_s __attribute__((ext_vector_type(8)));
+constexpr int kRowB = 80;  // bytes per staged feature row: 32 bf16 + 16 B (distinct banks)
+__device__ __forceinline__ bf16x8_s neg8(bf16x8_s v) {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+    u ^= 0x80008000u;
+    return __builtin_bit_cast(bf16x8_s, u);
+}
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_state_scan_mm(
+    const uint16_t* __restrict__ x_re, const uint16_t* __restrict__ x_im,
+    const uint16_t* __restrict__ b_re, const uint16_t* __restrict__ b_im,
+    const float* __restrict__ w_re, const float* __restrict__ w_im,
+    const float* __restrict__ cd_re, const float* __restrict__ cd_im,
+    const float* __restrict__ h0_re, const float* __restrict__ h0_im, float* __restrict__ st_re,
+    float* __restrict__ st_im, float* __restrict__ hT_re, float* __restrict__ hT_im, int64_t T,
+    int H, int nC, int64_t nbh) {
+    constexpr int C = 64, N = 64, D = 64, PT = D / 16;
+    constexpr int NS = C / kSR;  // stages (of 32 steps) per chunk
+    // [buffer][plane][feature row]: w B for this half's 32 n, X for all 64 p
+    __shared__ __align__(16) unsigned char lds_wb[2][2][32 * kRowB];
+    __shared__ __align__(16) unsigned char lds_xt[2][2][64 * kRowB];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int wv = wave_id();
+    const int64_t xcd = blockIdx.x % kScanXcds, y = blockIdx.x / kScanXcds;
+    const int64_t bh = xcd * (int64_t)(gridDim.x / (2 * kScanXcds)) + y / 2;
+    const int h2 = (int)(y % 2);
+    if (bh >= nbh) return;  // uniform over the workgroup
+    const int ntl = wv >> 1, pt0 = (wv & 1) * 2, nt = 2 * h2 + ntl;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
+
+    const int64_t sbase = (bh * N + nt * 16 + 4 * g) * (int64_t)D + pt0 * 16 + li;
+    float hr[2][4], hi[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hr[q][r] = h0_re != nullptr ? h0_re[sbase + r * D + 16 * q] : 0.f;
+            hi[q][r] = h0_im != nullptr ? h0_im[sbase + r * D + 16 * q] : 0.f;
+        }
+
+    // staging items: threads 0-127 take X features 2 pp, 2 pp + 1 over the 8
+    // steps 8 rg .. 8 rg + 7 (pp = tid % 32, rg = tid / 32); threads 128-191
+    // take B features 32 h2 + 2 np, + 1 (np = tid % 16, rg = (tid - 128) / 16)
+    const bool is_x = tid < 128, is_b = tid >= 128 && tid < 192;
+    const int pp = tid & 31, np = (tid - 128) & 15;
+    const int rg = is_x ? tid >> 5 : ((tid - 128) >> 4) & 3;
+    struct Raw {
+        uint32_t re[8], im[8];  // two features (low, high half) at 8 steps
+        float wr[8], wi[8];     // B items: the weights of those steps
+    };
+    auto gload = [&](int qs, Raw& R) {
+        const int c = qs / NS, s = qs % NS;
+        const int64_t t0 = (int64_t)c * C;
+        const int valid = (int)min<int64_t>((int64_t)C, T - t0);
+        const int64_t row0 = (b * T + t0) * H + h;
+        if (is_x) {
+            const uint32_t ext = ((uint32_t)(valid - 1) * sD + D) * 2u;
+            const BufRes vr = make_buf(x_re + row0 * D, ext), vi = make_buf(x_im + row0 * D, ext);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t e = (uint32_t)(s * kSR + 8 * rg + r) * sD + 2 * pp;
+                R.re[r] = __builtin_amdgcn_raw_buffer_load_b32(vr, e * 2u, 0, 0);
+                R.im[r] = __builtin_amdgcn_raw_buffer_load_b32(vi, e * 2u, 0, 0);
+            }
+        } else if (is_b) {
+            const uint32_t ext = ((uint32_t)(valid - 1) * sN + N) * 2u;
+            const BufRes vr = make_buf(b_re + row0 * N, ext), vi = make_buf(b_im + row0 * N, ext);
+            const int64_t wbase = (bh * nC + c) * (int64_t)C + s * kSR + 8 * rg;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t e = (uint32_t)(s * kSR + 8 * rg + r) * sN + 32 * h2 + 2 * np;
+                R.re[r] = __builtin_amdgcn_raw_buffer_load_b32(vr, e * 2u, 0, 0);
+                R.im[r] = __builtin_amdgcn_raw_buffer_load_b32(vi, e * 2u, 0, 0);
+                R.wr[r] = w_re[wbase + r];
+                R.wi[r] = w_im[wbase + r];
+            }
+        }
+    };
+    auto lstore = [&](int buf, const Raw& R) {
+        if (is_x) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                uint32_t pr[4], pi[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t a0 = (R.re[2 * k] >> (16 * f)) & 0xffffu;
+                    const uint32_t a1 = (R.re[2 * k + 1] >> (16 * f)) & 0xffffu;
+                    const uint32_t b0 = (R.im[2 * k] >> (16 * f)) & 0xffffu;
+                    const uint32_t b1 = (R.im[2 * k + 1] >> (16 * f)) & 0xffffu;
+                    pr[k] = a0 | (a1 << 16);
+                    pi[k] = b0 | (b1 << 16);
+                }
+                const int off = (2 * pp + f) * kRowB + 16 * rg;
+                *reinterpret_cast<uint4*>(&lds_xt[buf][0][off]) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+                *reinterpret_cast<uint4*>(&lds_xt[buf][1][off]) = make_uint4(pi[0], pi[1], pi[2], pi[3]);
+            }
+        } else if (is_b) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                uint32_t pr[4], pi[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t ur[2], ui[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int r = 2 * k + e;
+                        const float br = __uint_as_float(((R.re[r] >> (16 * f)) & 0xffffu) << 16);
+                        const float bi = __uint_as_float(((R.im[r] >> (16 * f)) & 0xffffu) << 16);
+                        ur[e] = bf16_bits(R.wr[r] * br - R.wi[r] * bi);  // (w B)[l, n]
+                        ui[e] = bf16_bits(R.wr[r] * bi + R.wi[r] * br);
+                    }
+                    pr[k] = ur[0] | (ur[1] << 16);
+                    pi[k] = ui[0] | (ui[1] << 16);
+                }
+                const int off = (2 * np + f) * kRowB + 16 * rg;
+                *reinterpret_cast<uint4*>(&lds_wb[buf][0][off]) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+                *reinterpret_cast<uint4*>(&lds_wb[buf][1][off]) = make_uint4(pi[0], pi[1], pi[2], pi[3]);
+            }
+        }
+    };
+
+    const int total = nC * NS;
+    const int64_t slot = ((int64_t)nt * PT + pt0) * 256 + 4 * lane;
+    floatx4 sre[2], sim[2];
+    Raw R;
+    gload(0, R);
+    lstore(0, R);
+    if (total > 1) gload(1, R);
+    for (int qs = 0; qs < total; ++qs) {
+        const int c = qs / NS, s = qs % NS, buf = qs & 1;
+        __syncthreads();  // stage qs is in LDS; nobody reads the other buffer any more
+        if (qs + 1 < total) lstore(buf ^ 1, R);
+        if (qs + 2 < total) gload(qs + 2, R);
+        if (s == 0) {
+            const int64_t off = (bh * nC + c) * (int64_t)N * D + slot;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                *reinterpret_cast<floatx4*>(st_re + off + 256 * q) =
+                    floatx4{hr[q][0], hr[q][1], hr[q][2], hr[q][3]};
+                *reinterpret_cast<floatx4*>(st_im + off + 256 * q) =
+                    floatx4{hi[q][0], hi[q][1], hi[q][2], hi[q][3]};
+                sre[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+                sim[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        // A: (w B)^T rows n = 16 ntl + li, steps 8g .. 8g + 7; B: X^T rows p
+        const int ao = (16 * ntl + li) * kRowB + 16 * g;
+        const bf16x8_s ar = *reinterpret_cast<const bf16x8_s*>(&lds_wb[buf][0][ao]);
+        const bf16x8_s ai = *reinterpret_cast<const bf16x8_s*>(&lds_wb[buf][1][ao]);
+        const bf16x8_s nai = neg8(ai);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int xo = (16 * (pt0 + q) + li) * kRowB + 16 * g;
+            const bf16x8_s xr = *reinterpret_cast<const bf16x8_s*>(&lds_xt[buf][0][xo]);
+            const bf16x8_s xi = *reinterpret_cast<const bf16x8_s*>(&lds_xt[buf][1][xo]);
+            sre[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, xr, sre[q], 0, 0, 0);
+            sre[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nai, xi, sre[q], 0, 0, 0);
+            sim[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, xi, sim[q], 0, 0, 0);
+            sim[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, xr, sim[q], 0, 0, 0);
+        }
+        if (s == NS - 1) {
+            const float dr = cd_re[bh * nC + c], di = cd_im[bh * nC + c];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float nr = dr * hr[q][r] - di * hi[q][r] + sre[q][r];
+                    const float ni = dr * hi[q][r] + di * hr[q][r] + sim[q][r];
+                    hr[q][r] = nr;
+                    hi[q][r] = ni;
+                }
+        }
+    }
+    if (hT_re != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hT_re[sbase + r * D + 16 * q] = hr[q][r];
+                hT_im[sbase + r * D + 16 * q] = hi[q][r];
+            }
+    }
+}
+
+static hipError_t launch_scan_mm(const FwdArgs& a, hipStream_t s) {
+    const int64_t nbh = a.B * a.H;
+    const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * 2;
+    typedef const uint16_t* P;
+    hipLaunchKernelGGL(k_state_scan_mm, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<P>(a.x_re), static_cast<P>(a.x_im), static_cast<P>(a.b_re),
+                       static_cast<P>(a.b_im), a.w_re, a.w_im, a.cd_re, a.cd_im, a.h0_re, a.h0_im,
+                       a.st_re, a.st_im, a.hT_re, a.hT_im, a.T, (int)a.H, (int)a.nC, nbh);
     return hipGetLastError();
 }
 
@@ -608,7 +778,7 @@ static hipError_t launch_scan_in(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_state_scan(const FwdArgs& a, hipStream_t s) {
     if (a.C == 64 && a.N == 64 && a.D == 64)
-        return a.in_dtype == 1 ? launch_scan_lds<InBF16>(a, s) : launch_scan_lds<InF32>(a, s);
+        return a.in_dtype == 1 ? launch_scan_mm(a, s) : launch_scan_lds(a, s);
     return a.in_dtype == 1 ? launch_scan_in<InBF16>(a, s) : launch_scan_in<InF32>(a, s);
 }
 
