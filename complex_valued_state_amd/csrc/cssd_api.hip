@@ -152,6 +152,9 @@ int check_shape(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C
     if (B > lim || T > lim || H > lim) return CSSD_ERR_UNSUPPORTED;
     if (B * H > lim / (nC * C) || B * nC * C * H > lim / m) return CSSD_ERR_UNSUPPORTED;
     if (B * H * nC > lim / (N * D)) return CSSD_ERR_UNSUPPORTED;
+    // the kernels address one chunk's rows of a plane through a buffer view whose
+    // extent, (C - 1) H m + m elements of up to 4 bytes, must fit 32 bits
+    if (C * H * m > lim / 2) return CSSD_ERR_UNSUPPORTED;
     return CSSD_OK;
 }
 

@@ -36,7 +36,8 @@
  *    cssd_step*): headdim D and dstate N in {16, 32, 64, 128}; chunk in
  *    {16, 32, 64, 128}; any seqlen >= 1 (a partial last chunk is masked inside
  *    the kernels, nothing is padded in memory); batch, nheads >= 1, with
- *    batch*seqlen*nheads*max(D,N) < 2^31 elements per plane.  The phase scan
+ *    batch*seqlen*nheads*max(D,N) < 2^31 elements per plane and, for
+ *    cssd_forward and cssd_backward, chunk*nheads*max(D,N) <= 2^30.  The phase scan
  *    and Born attention state their own limits.  Other sizes return
  *    CSSD_ERR_UNSUPPORTED.  There is one kernel path and no fallback.
  *  - Outputs must not alias inputs (except the decode state, updated in place).

@@ -88,6 +88,8 @@ def test_workspace_never_holds_the_segment_matrix(lib):
     ((0, 64, 2, 16, 16, 16), 1), ((1, 0, 2, 16, 16, 16), 1), ((1, 64, -1, 16, 16, 16), 1),
     ((1, 64, 2, 24, 16, 16), 2), ((1, 64, 2, 16, 256, 16), 2), ((1, 64, 2, 16, 16, 48), 2),
     ((1, 64, 2, 16, 16, 8), 2), ((1 << 20, 1 << 20, 64, 128, 128, 64), 2),
+    # under 2^31 elements in all, but one chunk's rows of a plane span more than 4 GB
+    ((1, 64, 300000, 64, 64, 64), 2),
 ])
 def test_workspace_size_rejects(lib, shape, status):
     assert _ws(lib, *shape)[0] == status
