@@ -523,7 +523,7 @@ def main():
         inp16 = wl.config1("bf16")
         ms16, kern16 = time_forward(inp16, args.steps, args.warmup, dev)
         hbm16 = forward_hbm_bytes(B, T, H, D, N, in_bytes=2)
-        extra["cfg1_bf16_inputs"] = {
+        extra["forward_B8_T2048_H48_D64_N64_C64_bf16_inputs"] = {
             "tokens_per_s": round(tokens / (ms16 * 1e-3), 1), "ms_per_step": round(ms16, 4),
             "hbm_roofline_frac": round(hbm16 / (ms16 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             # the products run on the bf16 matrix cores (the bound that binds is HBM)
@@ -535,7 +535,7 @@ def main():
         bms, bk = time_backward(inp, max(3, args.steps // 2), 2, dev)
         bfl = backward_dx_flops(B, T, H, D, N, C)
         bsym = "k_bwd_lds<true>" if C == N == D == 64 else f"k_bwd_tiles<{C}, {N}, {D}, 0>"
-        extra["backward_cfg1_B8_T2048_H48_D64_N64_C64_f32"] = {
+        extra["backward_B8_T2048_H48_D64_N64_C64_f32"] = {
             "tokens_per_s": round(tokens / (bms * 1e-3), 1), "ms_per_step": round(bms, 4),
             "kernels_avg_ms": {k: round(v, 5) for k, v in bk.items()},
             "roofline": {"bound": "mfma", "kernel": "k_bwd_dx", "symbol": bsym,
@@ -604,8 +604,8 @@ def main():
                          "frac": round(bfl / (b16kms * 1e-3) / 1e12 / PEAK_BF16_MFMA_TFLOPS, 4),
                          "algorithmic_flops_per_launch": bfl, "avg_launch_ms": round(b16kms, 5)}}
         if args.all:
-            for name, mk in (("cfg2_long_B1_T16384_H48_N128_C128", wl.config2),
-                             ("cfg3_pam_B16_T1024_H12_N128_C64", lambda: wl.config3("re"))):
+            for name, mk in (("forward_long_B1_T16384_H48_D64_N128_C128", wl.config2),
+                             ("forward_pam_B16_T1024_H12_D64_N128_C64", lambda: wl.config3("re"))):
                 progress(f"timing {name}")
                 i2 = mk()
                 sh = i2.shape
