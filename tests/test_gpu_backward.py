@@ -74,6 +74,7 @@ SMALL = [
     (2, 200, 3, 64, 64, 64, True, True, True),    # N = D = C = 64 (fused adjoint pass), ragged tail
     (1, 64, 2, 64, 64, 64, False, True, False),   # the same, one chunk, no dhT
     (3, 190, 3, 64, 64, 64, True, False, False),  # the same, no dhT, 9 (b, h) over 8 XCDs
+    (1, 512, 2, 32, 32, 16, True, True, True),    # 32 chunks per (b, h) in the recompute
 ]
 
 

@@ -51,6 +51,9 @@ SMALL = [
     (1, 30, 1, 64, 64, 64, False, True),     # one chunk, shorter than a stage
     (2, 200, 3, 64, 64, 64, True, True),     # ragged tail; fewer (b, h) than XCDs
     (3, 320, 5, 64, 64, 64, True, False),    # whole chunks, 15 (b, h) over 8 XCDs
+    # few (b, h), many chunks: each state-scan wave walks a long chunk chain
+    (1, 1024, 1, 16, 16, 16, True, True),    # 64 chunks
+    (2, 1000, 2, 32, 64, 32, True, True),    # 32 chunks, ragged tail
 ]
 
 
@@ -165,6 +168,7 @@ BF16_CASES = [
     (2, 70, 2, 32, 32, 64, True, True),
     (1, 33, 1, 64, 64, 64, False, True),     # one partial chunk
     (3, 130, 5, 64, 64, 64, True, True),     # 15 (b, h) over the 8 XCDs, ragged tail
+    (1, 640, 2, 32, 64, 32, True, True),     # 20 chunks per (b, h), bf16 inputs
     (2, 100, 2, 32, 64, 32, True, True),     # register-operand kernel
 ]
 
