@@ -329,7 +329,8 @@ int oracle_step_infinite_f64(int64_t Bsz, int64_t H, int64_t D, int64_t N,
  *   ddt_t   = sigmoid(dt_t) Re(dz_t conj(A)),  dA += s_t dz_t,
  *   dDskip += Re(sum_p dy_t[p] conj(x_t[p]))
  *   G       = conj(a_t) G                              back to h_{t-1}
- * starting from G = dL/dh_T (dhT, or zero) and ending with dh0 = G.
+ * starting from G = dL/dh_T (dhT, or zero) and ending with dh0 = G.  With
+ * T = 0 no step is walked: dh0 = dhT, and dA, dDskip are empty sums (zero).
  * Inputs as oracle_forward_f64 plus dy [B,T,H,D] and dhT [B,H,N,D] (or NULL);
  * outputs dx, dB, dC (input layouts), ddt [B,T,H], dA [H] and dDskip [H]
  * (summed over batch and time; dDskip may be NULL), dh0 [B,H,N,D] (or NULL).
@@ -348,7 +349,7 @@ int oracle_backward_f64(int64_t Bsz, int64_t T, int64_t H, int64_t D, int64_t N,
                         double *da_re, double *da_im, double *dd,
                         double *dh0_re, double *dh0_im, int nthreads)
 {
-    if (Bsz <= 0 || T < 1 || H <= 0 || D <= 0 || N <= 0)
+    if (Bsz <= 0 || T < 0 || H <= 0 || D <= 0 || N <= 0)
         return -1;
     if (!x_re || !x_im || !b_re || !b_im || !c_re || !c_im || !dt || !a_re || !a_im ||
         !dy_re || !dy_im || !dx_re || !dx_im || !db_re || !db_im || !dc_re || !dc_im ||
@@ -565,7 +566,7 @@ int oracle_born_attention_f64(int64_t Bsz, int64_t T, int64_t H, int64_t D,
                               const double *v_re, const double *v_im,
                               const double *tau, double *out_re, double *out_im, int nthreads)
 {
-    if (Bsz <= 0 || T <= 0 || H <= 0 || D <= 0)
+    if (Bsz <= 0 || T < 0 || H <= 0 || D <= 0)
         return -1;
     if (!q_re || !q_im || !k_re || !k_im || !v_re || !v_im || !out_re || !out_im)
         return -1;

@@ -660,7 +660,36 @@ def pin_born_invariances(lib):
     assert np.max(np.abs(base[:, 0] - v[:, 0])) < 1e-14
 
 
-ALL_PINS = [pin_bruteforce, pin_impulse, pin_constant_input, pin_fixed_point,
+# ---------------------------------------------------------------------------
+# empty sequences: a scan of no time steps
+# ---------------------------------------------------------------------------
+def pin_empty_sequence(lib):
+    """With T = 0 the recurrence is never applied (Mamba-3-Lite docs, "Complex-Valued
+    State Spaces", the naive scan): the final state is the initial one (zero
+    without one), the gradient reaching h0 is the one given for hT, and the sums
+    over time, dA and dDskip, are empty.  The phase scan keeps psi0 and Born
+    attention has no rows."""
+    rng = np.random.default_rng(77)
+    Bsz, H, D, N = 2, 3, 4, 5
+    x, Bm, Cm, dt, A, Dk, h0 = _rand_problem(rng, Bsz, 0, H, D, N)
+    y, hT = oracle.forward(x, Bm, Cm, dt, A, Dk, h0, lib=lib)
+    assert y.shape == (Bsz, 0, H, D) and np.array_equal(hT, h0)
+    _, hz = oracle.forward(x, Bm, Cm, dt, A, Dk, None, lib=lib)
+    assert hz.shape == (Bsz, H, N, D) and not np.any(hz)
+    dhT = crandn(rng, Bsz, H, N, D)
+    g = oracle.backward(x, Bm, Cm, dt, A, Dk, h0, np.zeros((Bsz, 0, H, D), complex), dhT, lib=lib)
+    assert np.array_equal(g["dh0"], dhT)
+    assert not np.any(g["dA"]) and not np.any(g["dD"])
+    assert g["dx"].shape == (Bsz, 0, H, D) and g["ddt"].shape == (Bsz, 0, H)
+    psi0 = crandn(rng, Bsz, H, N)
+    z = np.zeros((Bsz, 0, H, N))
+    psi, psiT = oracle.phase_scan(z, z, z.astype(complex), psi0, lib=lib)
+    assert psi.shape == (Bsz, 0, H, N) and np.array_equal(psiT, psi0)
+    e = np.zeros((Bsz, 0, H, D), complex)
+    assert oracle.born_attention(e, e, e, lib=lib).shape == (Bsz, 0, H, D)
+
+
+ALL_PINS = [pin_bruteforce, pin_empty_sequence, pin_impulse, pin_constant_input, pin_fixed_point,
             pin_phase_unrolled, pin_phase_transport, pin_phase_golden_gain,
             pin_born_orthogonal_keys, pin_born_two_state_interference,
             pin_born_density_matrix_form, pin_born_invariances,
