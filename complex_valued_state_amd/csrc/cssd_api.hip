@@ -143,13 +143,17 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int6
     return l;
 }
 
+bool empty_problem(int64_t B, int64_t T, int64_t H) { return B == 0 || T == 0 || H == 0; }
+
 int check_shape(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C) {
-    if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || N <= 0 || C <= 0) return CSSD_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || D <= 0 || N <= 0 || C <= 0) return CSSD_ERR_INVALID_ARG;
     if (!pow2_16_128(D) || !pow2_16_128(N) || !pow2_16_128(C)) return CSSD_ERR_UNSUPPORTED;
-    const int64_t nC = (T + C - 1) / C;
     const int64_t lim = (int64_t)1 << 31;
     const int64_t m = D > N ? D : N;
     if (B > lim || T > lim || H > lim) return CSSD_ERR_UNSUPPORTED;
+    if (B * H > lim / (N * D)) return CSSD_ERR_UNSUPPORTED;  // one [B,H,N,D] state plane
+    if (empty_problem(B, T, H)) return CSSD_OK;
+    const int64_t nC = (T + C - 1) / C;
     if (B * H > lim / (nC * C) || B * nC * C * H > lim / m) return CSSD_ERR_UNSUPPORTED;
     if (B * H * nC > lim / (N * D)) return CSSD_ERR_UNSUPPORTED;
     // the kernels address one chunk's rows of a plane through a buffer view whose
@@ -192,6 +196,60 @@ cssd::FwdArgs fwd_args(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
     return a;
 }
 
+// Both planes of one output: dst = src, or zeros when src is NULL.
+hipError_t fill_planes(float* dst_re, float* dst_im, const float* src_re, const float* src_im,
+                       int64_t n, hipStream_t s) {
+    hipError_t e = timed(cssd::K_FILL, s, [&] { return cssd::launch_fill(dst_re, src_re, n, s); });
+    if (e != hipSuccess) return e;
+    return timed(cssd::K_FILL, s, [&] { return cssd::launch_fill(dst_im, src_im, n, s); });
+}
+
+// cssd_forward over zero time steps (or no batch rows or heads): nothing but
+// hT is written, and hT = h0 (zero without h0).  n = elements of one state plane.
+int empty_forward(int64_t n, const float* h0_re, const float* h0_im, float* hT_re, float* hT_im,
+                  void* stream) {
+    if ((h0_re == nullptr) != (h0_im == nullptr) || (hT_re == nullptr) != (hT_im == nullptr))
+        return CSSD_ERR_INVALID_ARG;
+    const void* st[] = {h0_re, h0_im, hT_re, hT_im};
+    for (const void* p : st)
+        if (!aligned(p, 16)) return CSSD_ERR_INVALID_ARG;
+    if (hT_re == nullptr) return CSSD_OK;
+    if (hT_re == hT_im || hT_re == h0_re || hT_re == h0_im || hT_im == h0_re || hT_im == h0_im)
+        return CSSD_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return fill_planes(hT_re, hT_im, h0_re, h0_im, n, s) == hipSuccess ? CSSD_OK : CSSD_ERR_HIP;
+}
+
+// cssd_backward of an empty problem: dA and dDskip are empty sums (zero) and
+// dh0 = dhT (zero without dhT).  H = heads, n = elements of one state plane.
+int empty_backward(int64_t H, int64_t n, const float* dhT_re, const float* dhT_im, float* dA_re,
+                   float* dA_im, float* dD, float* dh0_re, float* dh0_im, void* stream) {
+    if (H > 0 && (dA_re == nullptr || dA_im == nullptr)) return CSSD_ERR_INVALID_ARG;
+    if ((dhT_re == nullptr) != (dhT_im == nullptr) || (dh0_re == nullptr) != (dh0_im == nullptr))
+        return CSSD_ERR_INVALID_ARG;
+    if (!aligned(dA_re, 4) || !aligned(dA_im, 4) || !aligned(dD, 4) || !aligned(dhT_re, 16) ||
+        !aligned(dhT_im, 16) || !aligned(dh0_re, 16) || !aligned(dh0_im, 16))
+        return CSSD_ERR_INVALID_ARG;
+    float* outs[] = {dA_re, dA_im, dD, dh0_re, dh0_im};
+    for (int i = 0; i < 5; ++i) {
+        if (outs[i] == nullptr) continue;
+        if (outs[i] == dhT_re || outs[i] == dhT_im) return CSSD_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (outs[i] == outs[j]) return CSSD_ERR_INVALID_ARG;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (H > 0) {
+        if (fill_planes(dA_re, dA_im, nullptr, nullptr, H, s) != hipSuccess) return CSSD_ERR_HIP;
+        if (dD != nullptr &&
+            timed(cssd::K_FILL, s, [&] { return cssd::launch_fill(dD, nullptr, H, s); }) !=
+                hipSuccess)
+            return CSSD_ERR_HIP;
+    }
+    if (dh0_re != nullptr && fill_planes(dh0_re, dh0_im, dhT_re, dhT_im, n, s) != hipSuccess)
+        return CSSD_ERR_HIP;
+    return CSSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,7 +272,9 @@ int cssd_forward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, i
     if (bytes == nullptr) return CSSD_ERR_INVALID_ARG;
     const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
     if (st != CSSD_OK) return st;
-    *bytes = layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
+    *bytes = empty_problem(batch, seqlen, nheads)
+                 ? 0
+                 : layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
     return CSSD_OK;
 }
 
@@ -227,6 +287,8 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
     if (st != CSSD_OK) return st;
     if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
+    if (empty_problem(batch, seqlen, nheads))
+        return empty_forward(batch * nheads * dstate * headdim, h0_re, h0_im, hT_re, hT_im, stream);
     // B and C rows are read as 16-byte (f32) / 8-byte (bf16) vectors, states as
     // float4; everything else only needs its element alignment.
     const uintptr_t in_el = in_dtype == CSSD_BF16 ? 2 : 4, in_vec = 4 * in_el;
@@ -273,7 +335,9 @@ int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, 
     if (bytes == nullptr) return CSSD_ERR_INVALID_ARG;
     const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
     if (st != CSSD_OK) return st;
-    *bytes = bwd_layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
+    *bytes = empty_problem(batch, seqlen, nheads)
+                 ? 0
+                 : bwd_layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
     return CSSD_OK;
 }
 
@@ -291,6 +355,9 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
     if (st != CSSD_OK) return st;
     if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
     if (in_dtype != CSSD_F32) return CSSD_ERR_UNSUPPORTED;
+    if (empty_problem(batch, seqlen, nheads))
+        return empty_backward(nheads, batch * nheads * dstate * headdim, dhT_re, dhT_im, dA_re,
+                              dA_im, dD, dh0_re, dh0_im, stream);
     // row-vector reads need 16 bytes; the gradients are written element-wise
     const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, y_re, y_im,
                          dy_re, dy_im, dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt,
@@ -388,6 +455,16 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
 
 namespace {
 
+// Sizes of the decode entry points (batch or nheads 0: nothing to do).
+int step_sizes(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate) {
+    if (batch < 0 || nheads < 0 || headdim <= 0 || dstate <= 0) return CSSD_ERR_INVALID_ARG;
+    if (!pow2_16_128(headdim) || !pow2_16_128(dstate)) return CSSD_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 31;
+    if (batch > lim || nheads > lim || batch * nheads > lim / (headdim * dstate))
+        return CSSD_ERR_UNSUPPORTED;
+    return CSSD_OK;
+}
+
 // Host-side checks shared by the decode entry points.  h_re/h_im may be NULL
 // (the stationary-output entry point has no state).
 int check_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, const float* x_re,
@@ -395,11 +472,8 @@ int check_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, c
                const float* C_im, const float* dt, const float* A_re, const float* A_im,
                const float* Dskip, const float* h_re, const float* h_im, const float* y_re,
                const float* y_im, bool with_state) {
-    if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0) return CSSD_ERR_INVALID_ARG;
-    if (!pow2_16_128(headdim) || !pow2_16_128(dstate)) return CSSD_ERR_UNSUPPORTED;
-    const int64_t lim = (int64_t)1 << 31;
-    if (batch > lim || nheads > lim || batch * nheads > lim / (headdim * dstate))
-        return CSSD_ERR_UNSUPPORTED;
+    const int sz = step_sizes(batch, nheads, headdim, dstate);
+    if (sz != CSSD_OK) return sz;
     // x, the state and y are accessed as float4; B, C, dt, A, Dskip as scalars
     const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, y_re, y_im};
     const uintptr_t req_al[] = {16, 16, 4, 4, 4, 4, 4, 4, 4, 16, 16};
@@ -449,6 +523,8 @@ int cssd_step_n(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, 
                 const float* A_im, const float* Dskip, float* h_re, float* h_im, float* y_re,
                 float* y_im, void* stream) {
     if (nsteps < 1) return CSSD_ERR_INVALID_ARG;
+    const int sz = step_sizes(batch, nheads, headdim, dstate);
+    if (sz != CSSD_OK || batch == 0 || nheads == 0) return sz;
     const int st = check_step(batch, nheads, headdim, dstate, x_re, x_im, B_re, B_im, C_re, C_im,
                               dt, A_re, A_im, Dskip, h_re, h_im, y_re, y_im, true);
     if (st != CSSD_OK) return st;
@@ -466,6 +542,8 @@ int cssd_step_infinite(int64_t batch, int64_t nheads, int64_t headdim, int64_t d
                        const float* C_re, const float* C_im, const float* dt, const float* A_re,
                        const float* A_im, const float* Dskip, float* y_re, float* y_im,
                        void* stream) {
+    const int sz = step_sizes(batch, nheads, headdim, dstate);
+    if (sz != CSSD_OK || batch == 0 || nheads == 0) return sz;
     const int st = check_step(batch, nheads, headdim, dstate, x_re, x_im, B_re, B_im, C_re, C_im,
                               dt, A_re, A_im, Dskip, nullptr, nullptr, y_re, y_im, false);
     if (st != CSSD_OK) return st;
@@ -499,11 +577,13 @@ int64_t phase_segment(int64_t B, int64_t T, int64_t HN, int64_t chunk) {
 }
 
 int check_phase_shape(int64_t B, int64_t T, int64_t H, int64_t N, int64_t chunk) {
-    if (B <= 0 || T <= 0 || H <= 0 || N <= 0 || chunk < 0) return CSSD_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || N <= 0 || chunk < 0) return CSSD_ERR_INVALID_ARG;
     const int64_t lim = (int64_t)1 << 31, lim40 = (int64_t)1 << 40;
     if (B > lim || T > lim || H > lim || N > lim) return CSSD_ERR_UNSUPPORTED;
     const int64_t HN = H * N;
-    if (HN > lim40 || B > lim40 / HN || B * HN > lim40 / T) return CSSD_ERR_UNSUPPORTED;
+    if (HN > lim40 || (HN > 0 && B > lim40 / HN)) return CSSD_ERR_UNSUPPORTED;
+    if (empty_problem(B, T, H)) return CSSD_OK;
+    if (B * HN > lim40 / T) return CSSD_ERR_UNSUPPORTED;
     return CSSD_OK;
 }
 
@@ -519,6 +599,10 @@ int cssd_phase_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
     if (bytes == nullptr) return CSSD_ERR_INVALID_ARG;
     const int st = check_phase_shape(batch, seqlen, nheads, dstate, chunk);
     if (st != CSSD_OK) return st;
+    if (empty_problem(batch, seqlen, nheads)) {
+        *bytes = 0;
+        return CSSD_OK;
+    }
     const int64_t HN = nheads * dstate;
     const int64_t L = phase_segment(batch, seqlen, HN, chunk);
     *bytes = phase_workspace(batch, (seqlen + L - 1) / L, HN);
@@ -532,6 +616,23 @@ int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstat
                     void* stream) {
     const int st = check_phase_shape(batch, seqlen, nheads, dstate, chunk);
     if (st != CSSD_OK) return st;
+    if (empty_problem(batch, seqlen, nheads)) {
+        // no step is taken: psiT = psi0 (zero without psi0), also in place
+        if ((psi0_re == nullptr) != (psi0_im == nullptr) ||
+            (psiT_re == nullptr) != (psiT_im == nullptr))
+            return CSSD_ERR_INVALID_ARG;
+        if (!aligned(psi0_re, 4) || !aligned(psi0_im, 4) || !aligned(psiT_re, 4) ||
+            !aligned(psiT_im, 4))
+            return CSSD_ERR_INVALID_ARG;
+        if (psiT_re == nullptr) return CSSD_OK;
+        if (psiT_re == psiT_im || psiT_re == psi0_im || psiT_im == psi0_re)
+            return CSSD_ERR_INVALID_ARG;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        return fill_planes(psiT_re, psiT_im, psi0_re, psi0_im, batch * nheads * dstate, s) ==
+                       hipSuccess
+                   ? CSSD_OK
+                   : CSSD_ERR_HIP;
+    }
     const void* req[] = {phi, u, b_re, b_im, psi_re, psi_im};
     for (const void* p : req)
         if (p == nullptr || !aligned(p, 4)) return CSSD_ERR_INVALID_ARG;
@@ -592,13 +693,14 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
                         int32_t in_dtype, const void* q_re, const void* q_im, const void* k_re,
                         const void* k_im, const void* v_re, const void* v_im, const float* tau,
                         float* out_re, float* out_im, void* stream) {
-    if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0) return CSSD_ERR_INVALID_ARG;
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim <= 0) return CSSD_ERR_INVALID_ARG;
     if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
     if (headdim != 16 && headdim != 32 && headdim != 64) return CSSD_ERR_UNSUPPORTED;
     const int64_t lim = (int64_t)1 << 31, lim40 = (int64_t)1 << 40;
     if (batch > lim || seqlen > lim || nheads > lim || batch * nheads > lim / 64 ||
         batch * nheads * seqlen > lim40 / headdim)
         return CSSD_ERR_UNSUPPORTED;
+    if (empty_problem(batch, seqlen, nheads)) return CSSD_OK;  // no rows to write
     const void* req[] = {q_re, q_im, k_re, k_im, v_re, v_im, out_re, out_im};
     for (const void* p : req)
         if (p == nullptr || !aligned(p, 16)) return CSSD_ERR_INVALID_ARG;
@@ -675,7 +777,7 @@ const char* cssd_kernel_name(int kernel_id) {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
         "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
         "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db",
-        "k_state_scan", "k_state_scan_adj"};
+        "k_state_scan", "k_state_scan_adj", "k_fill"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

@@ -9,7 +9,7 @@ namespace cssd {
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
                 K_STEP_INFINITE = 5, K_BWD_DX = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
                 K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_BORN = 12,
-                K_BWD_DB = 13, K_STATE_SCAN = 14, K_STATE_SCAN_ADJ = 15, K_COUNT = 16 };
+                K_BWD_DB = 13, K_STATE_SCAN = 14, K_STATE_SCAN_ADJ = 15, K_FILL = 16, K_COUNT = 17 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -100,5 +100,8 @@ hipError_t launch_phase_summary(const PhaseArgs& a, hipStream_t stream);
 hipError_t launch_phase_carry(const PhaseArgs& a, hipStream_t stream);
 hipError_t launch_phase_out(const PhaseArgs& a, hipStream_t stream);
 hipError_t launch_born(const BornArgs& a, hipStream_t stream);
+// dst[0, n) = src[0, n), or zeros when src is NULL (the state and sums of an
+// empty problem); nothing is launched for n <= 0 or dst == src
+hipError_t launch_fill(float* dst, const float* src, int64_t n, hipStream_t stream);
 
 }  // namespace cssd

@@ -34,12 +34,19 @@
  *    exception crosses this boundary.
  *  - Supported sizes of the scan entry points (cssd_forward, cssd_backward,
  *    cssd_step*): headdim D and dstate N in {16, 32, 64, 128}; chunk in
- *    {16, 32, 64, 128}; any seqlen >= 1 (a partial last chunk is masked inside
- *    the kernels, nothing is padded in memory); batch, nheads >= 1, with
+ *    {16, 32, 64, 128}; any seqlen >= 0 (a partial last chunk is masked inside
+ *    the kernels, nothing is padded in memory); batch, nheads >= 0, with
  *    batch*seqlen*nheads*max(D,N) < 2^31 elements per plane and, for
  *    cssd_forward and cssd_backward, chunk*nheads*max(D,N) <= 2^30.  The phase scan
  *    and Born attention state their own limits.  Other sizes return
  *    CSSD_ERR_UNSUPPORTED.  There is one kernel path and no fallback.
+ *  - Empty problems: batch, seqlen or nheads may be 0 in every entry point
+ *    (seqlen where it has one).  Arrays with a zero extent are never accessed
+ *    and may be NULL, and so may the workspace (its size is then 0).  What is
+ *    left is what a scan of no time steps gives: the final state equals the
+ *    initial one (cssd_forward's hT = h0, cssd_phase_scan's psiT = psi0; zero
+ *    when the initial state is NULL), cssd_backward's dh0 = dhT (or zero) and
+ *    its sums over batch and time, dA and dDskip, are zero.
  *  - Outputs must not alias inputs (except the decode state, updated in place).
  *  - The library keeps no per-call state and is safe to call from several host
  *    threads on different streams.  The optional profiler (cssd_profile_*)
@@ -55,11 +62,11 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 105 /* major*100 + minor */
+#define CSSD_VERSION 106 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
-    CSSD_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, misalignment, aliasing */
+    CSSD_ERR_INVALID_ARG = 1, /* null required pointer, negative size, misalignment, aliasing */
     CSSD_ERR_UNSUPPORTED = 2, /* sizes outside the supported set */
     CSSD_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned */
     CSSD_ERR_HIP = 4          /* a HIP launch or runtime call failed */
@@ -100,7 +107,7 @@ const char *cssd_status_string(int status);
  *                                         element (n, p) at
  *                                         (((n/16)(D/16) + p/16)*4 + (n%16)/4)*64
  *                                         + (p%16)*4 + n%4
- * Returns CSSD_OK, CSSD_ERR_INVALID_ARG (null bytes / non-positive size) or
+ * Returns CSSD_OK, CSSD_ERR_INVALID_ARG (null bytes / negative size) or
  * CSSD_ERR_UNSUPPORTED.
  */
 int cssd_forward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
@@ -331,7 +338,7 @@ int cssd_phase_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t dstat
  *                   scale every score of row i alike and so cancel in the
  *                   normalisation; they change only rounding.
  *   out_re, out_im  [B,T,H,D] float32 psi (written)
- * Supported: headdim D in {16, 32, 64}; any seqlen >= 1; batch*nheads*seqlen*D
+ * Supported: headdim D in {16, 32, 64}; any seqlen >= 0; batch*nheads*seqlen*D
  * < 2^40.  A row whose scores are all zero (its query orthogonal to every key
  * up to it, e.g. a zero query) is returned as zero.  Alignment: q, k, v, out
  * 16 bytes, tau 4.  Accuracy: fp32 inputs agree with the exact result to about
@@ -359,7 +366,8 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
  * 6 bwd_dx, 7 bwd_dc, 8 bwd_dz, 13 bwd_db (cssd_backward also runs ids 0 and 14,
  * then 15 state_scan_adj, the adjoint chunk states and pass fused, where
  * dstate = headdim = chunk = 64, else 1 and 2 in their adjoint modes), 9 phase_summary,
- * 10 phase_carry, 11 phase_out (cssd_phase_scan), 12 born (cssd_born_attention).
+ * 10 phase_carry, 11 phase_out (cssd_phase_scan), 12 born (cssd_born_attention),
+ * 16 fill (the states and zeroed sums of an empty problem, one launch per plane).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).
  */

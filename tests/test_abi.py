@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 105
+    assert lib.cssd_version() == 106
     for st in range(5):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -85,7 +85,8 @@ def test_workspace_never_holds_the_segment_matrix(lib):
 
 
 @pytest.mark.parametrize("shape,status", [
-    ((0, 64, 2, 16, 16, 16), 1), ((1, 0, 2, 16, 16, 16), 1), ((1, 64, -1, 16, 16, 16), 1),
+    ((-1, 64, 2, 16, 16, 16), 1), ((1, -1, 2, 16, 16, 16), 1), ((1, 64, -1, 16, 16, 16), 1),
+    ((0, 64, 2, 24, 16, 16), 2), ((1, 0, 2, 16, 16, 0), 1),
     ((1, 64, 2, 24, 16, 16), 2), ((1, 64, 2, 16, 256, 16), 2), ((1, 64, 2, 16, 16, 48), 2),
     ((1, 64, 2, 16, 16, 8), 2), ((1 << 20, 1 << 20, 64, 128, 128, 64), 2),
     # under 2^31 elements in all, but one chunk's rows of a plane span more than 4 GB
@@ -93,6 +94,14 @@ def test_workspace_never_holds_the_segment_matrix(lib):
 ])
 def test_workspace_size_rejects(lib, shape, status):
     assert _ws(lib, *shape)[0] == status
+
+
+@pytest.mark.parametrize("shape", [(0, 64, 2, 16, 16, 16), (2, 0, 3, 32, 64, 16),
+                                   (2, 100, 0, 32, 64, 16), (0, 0, 0, 128, 128, 128)])
+def test_empty_problems_need_no_workspace(lib, shape):
+    assert _ws(lib, *shape) == (0, 0)
+    n = ctypes.c_size_t(7)
+    assert lib.cssd_backward_workspace_size(*shape, ctypes.byref(n)) == 0 and n.value == 0
 
 
 def _fwd(lib, shape=(1, 64, 2, 16, 16, 16), dtype=0, ptrs=None, ws=None, ws_bytes=1 << 30):
@@ -130,7 +139,7 @@ def test_step_validation(lib):
     base = 0x10000000
     ptrs = [base + 0x100000 * i for i in range(14)]
     args = ptrs[:10] + ptrs[10:14]
-    assert lib.cssd_step(0, 2, 16, 16, *args, None) == 1
+    assert lib.cssd_step(-1, 2, 16, 16, *args, None) == 1
     assert lib.cssd_step(1, 2, 20, 16, *args, None) == 2
     bad = list(args); bad[0] = None
     assert lib.cssd_step(1, 2, 16, 16, *bad, None) == 1
@@ -148,7 +157,7 @@ def test_step_n_and_infinite_validation(lib):
     assert lib.cssd_step_n(1, 2, 16, 16, -5, *ins, *h, *y, None) == 1
     assert lib.cssd_step_n(1, 2, 16, 24, 3, *ins, *h, *y, None) == 2      # N not supported
     assert lib.cssd_step_n(1, 2, 16, 16, 3, *ins, None, h[1], *y, None) == 1
-    assert lib.cssd_step_infinite(0, 2, 16, 16, *ins, *y, None) == 1
+    assert lib.cssd_step_infinite(-1, 2, 16, 16, *ins, *y, None) == 1
     assert lib.cssd_step_infinite(1, 2, 16, 48, *ins, *y, None) == 2
     bad = list(ins); bad[6] = None                                         # dt missing
     assert lib.cssd_step_infinite(1, 2, 16, 16, *bad, *y, None) == 1
@@ -197,7 +206,10 @@ def test_phase_scan_workspace_size(lib):
     # automatic segments for a small batch are a multiple of 16 steps
     st, n = _phase_ws(lib, 1, 4096, 2, 8, 0)
     assert st == 0 and n > 0 and n % (6 * 256) == 0
-    assert _phase_ws(lib, 0, 10, 1, 1, 0)[0] == 1
+    assert _phase_ws(lib, -1, 10, 1, 1, 0)[0] == 1
+    assert _phase_ws(lib, 1, 10, 1, 0, 0)[0] == 1                # dstate 0
+    assert _phase_ws(lib, 0, 10, 1, 1, 0) == (0, 0)              # empty problems
+    assert _phase_ws(lib, 3, 0, 2, 4, 16) == (0, 0)
     assert _phase_ws(lib, 1, 10, 1, 1, -1)[0] == 1
     assert _phase_ws(lib, 1 << 20, 1 << 20, 1, 2, 0)[0] == 2     # 2^41 elements per plane
     assert lib.cssd_phase_scan_workspace_size(1, 10, 1, 1, 0, None) == 1
@@ -210,7 +222,7 @@ def test_phase_scan_validation(lib):
     ws = 0x20000000
     call = lambda ins=ins, psi0=psi0, psi=psi, psiT=psiT, shape=(2, 64, 2, 16, 16), wsb=1 << 30, w=ws: \
         lib.cssd_phase_scan(*shape, *ins, *psi0, *psi, *psiT, w, wsb, None)
-    assert call(shape=(0, 64, 2, 16, 16)) == 1
+    assert call(shape=(-1, 64, 2, 16, 16)) == 1
     assert call(shape=(2, 64, 2, 16, -1)) == 1
     bad = list(ins); bad[1] = None                                  # u missing
     assert call(ins=bad) == 1
@@ -235,8 +247,8 @@ def test_born_attention_validation(lib):
     ins, tau, out = p[:6], p[6], p[7:9]
     call = lambda shape=(2, 100, 3, 16), dt=0, ins=ins, tau=tau, out=out: \
         lib.cssd_born_attention(*shape, dt, *ins, tau, *out, None)
-    assert call(shape=(0, 100, 3, 16)) == 1
-    assert call(shape=(2, 0, 3, 16)) == 1
+    assert call(shape=(-1, 100, 3, 16)) == 1
+    assert call(shape=(2, -1, 3, 16)) == 1
     assert call(shape=(2, 100, 3, 24)) == 2                  # D not supported
     assert call(shape=(2, 100, 3, 128)) == 2
     assert call(dt=7) == 1
@@ -257,10 +269,50 @@ def test_profiler_without_launches(lib):
         pass
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
-    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(16) is None
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(17) is None
+    assert lib.cssd_kernel_name(16) == b"k_fill"
     assert lib.cssd_kernel_name(14) == b"k_state_scan"
     assert lib.cssd_kernel_name(15) == b"k_state_scan_adj"
     assert lib.cssd_kernel_name(13) == b"k_bwd_db" and lib.cssd_kernel_name(6) == b"k_bwd_dx"
     assert lib.cssd_kernel_name(12) == b"k_born"
     assert lib.cssd_kernel_name(5) == b"k_step_infinite"
     assert lib.cssd_kernel_name(11) == b"k_phase_out"
+
+
+def test_empty_problems_validate_and_enqueue_nothing(lib):
+    """Empty problems (batch, seqlen or nheads 0): arrays with a zero extent may be
+    NULL.  The calls below have nothing non-empty to write, so they return CSSD_OK
+    without a launch (which is why they run without a GPU); bad pairs of the
+    state pointers are still rejected."""
+    n = None
+    # forward: all 16 arrays NULL, no workspace
+    for shape in [(0, 64, 2, 16, 16, 16), (2, 0, 3, 32, 64, 16), (2, 64, 0, 16, 16, 16)]:
+        assert lib.cssd_forward(*shape, 0, *[n] * 16, n, 0, n) == 0
+        assert lib.cssd_forward(*shape, 1, *[n] * 16, n, 0, n) == 0
+        assert lib.cssd_forward(*shape, 5, *[n] * 16, n, 0, n) == 1      # bad dtype
+    base = 0x10000000
+    h0, hT = [base, base + 0x100000], [base + 0x200000, base + 0x300000]
+    # T = 0 with hT requested launches the copy; here only the validation is run
+    shape = (2, 0, 3, 32, 64, 16)
+    assert lib.cssd_forward(*shape, 0, *[n] * 10, h0[0], n, *[n] * 2, *hT, n, 0, n) == 1
+    assert lib.cssd_forward(*shape, 0, *[n] * 10, *h0, *[n] * 2, hT[0], n, n, 0, n) == 1
+    assert lib.cssd_forward(*shape, 0, *[n] * 10, *h0, *[n] * 2, h0[0], hT[1], n, 0, n) == 1
+    assert lib.cssd_forward(*shape, 0, *[n] * 10, *h0, *[n] * 2, hT[0] + 8, hT[1], n, 0, n) == 1
+    # with batch 0 the state planes are empty too: nothing to launch
+    assert lib.cssd_forward(0, 64, 2, 16, 16, 16, 0, *[n] * 10, *h0, *[n] * 2, *hT, n, 0, n) == 0
+    # backward: no heads -> nothing at all; heads but no dA -> invalid
+    assert lib.cssd_backward(2, 64, 0, 16, 16, 16, 0, *[n] * 18, *[n] * 12, n, 0, n) == 0
+    assert lib.cssd_backward(2, 0, 3, 16, 16, 16, 0, *[n] * 18, *[n] * 12, n, 0, n) == 1
+    assert lib.cssd_backward(2, 0, 3, 16, 16, 16, 1, *[n] * 18, *[n] * 12, n, 0, n) == 2
+    # decode with no rows or heads; nsteps is still checked
+    assert lib.cssd_step(0, 2, 16, 16, *[n] * 14, n) == 0
+    assert lib.cssd_step_n(3, 0, 16, 16, 4, *[n] * 14, n) == 0
+    assert lib.cssd_step_n(0, 2, 16, 16, 0, *[n] * 14, n) == 1
+    assert lib.cssd_step_infinite(0, 2, 16, 16, *[n] * 12, n) == 0
+    assert lib.cssd_step(0, 2, 16, 24, *[n] * 14, n) == 2
+    # phase scan with batch 0 (empty psiT), Born attention of nothing
+    assert lib.cssd_phase_scan(0, 64, 2, 16, 0, *[n] * 10, n, 0, n) == 0
+    assert lib.cssd_phase_scan(0, 64, 2, 16, 0, *[n] * 4, base, n, *[n] * 4, n, 0, n) == 1
+    for shape in [(0, 100, 3, 16), (2, 0, 3, 32), (2, 100, 0, 64)]:
+        assert lib.cssd_born_attention(*shape, 0, *[n] * 7, n, n, n) == 0
+    assert lib.cssd_born_attention(2, 0, 3, 24, 0, *[n] * 7, n, n, n) == 2
