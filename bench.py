@@ -302,8 +302,9 @@ def time_born(B, T, H, D, steps, warmup, dev, seed=6, bf16=False):
     return e0.elapsed_time(e1) / steps, prof.ms["k_born"] / max(1, prof.launches["k_born"])
 
 
-def time_backward(inp, steps, warmup, dev, seed=9):
-    """cssd_backward with the forward output and seeded upstream gradients resident."""
+def time_backward(inp, steps, warmup, dev, seed=9, saved=False):
+    """cssd_backward with the forward output and seeded upstream gradients resident
+    (saved: cssd_backward_saved on the states the forward left in the workspace)."""
     import torch
     import complex_valued_state_amd as cssd
     a = _to_dev(inp, dev)
@@ -315,17 +316,20 @@ def time_backward(inp, steps, warmup, dev, seed=9):
     r = math.sqrt(0.5)
     dy = [torch.randn((Bsz, T, H, D), generator=g, device=dev) * r for _ in range(2)]
     dhT = [torch.randn((Bsz, H, N, D), generator=g, device=dev) * r for _ in range(2)]
-    y = cssd.cssd_forward(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"],
-                          d["dt"], d["A_re"], d["A_im"], d["Dskip"], d["h0"], chunk=inp.chunk,
-                          return_state=False)[:2]
     ws = torch.empty(cssd.cssd_backward_workspace_size(Bsz, T, H, D, N, inp.chunk),
                      dtype=torch.uint8, device=dev)
+    ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
+           d["A_im"], d["Dskip"], d["h0"])
+    out = cssd.cssd_forward(*ins, chunk=inp.chunk, workspace=ws)
+    y, hT = out[:2], out[2:]
     stream = torch.cuda.current_stream(dev)
 
     def run():
-        cssd.cssd_backward(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"],
-                           d["dt"], d["A_re"], d["A_im"], d["Dskip"], d["h0"], y, dy, dhT,
-                           chunk=inp.chunk, workspace=ws, stream=stream)
+        if saved:
+            cssd.cssd_backward_saved(*ins, y, hT, dy, dhT, chunk=inp.chunk, workspace=ws,
+                                     stream=stream)
+        else:
+            cssd.cssd_backward(*ins, y, dy, dhT, chunk=inp.chunk, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         run()
@@ -546,6 +550,11 @@ def main():
                                        / PEAK_FP32_MFMA_TFLOPS, 4),
                          "algorithmic_flops_per_launch": bfl,
                          "avg_launch_ms": round(bk["k_bwd_dx"], 5)}}
+        progress("timing the backward pass on the forward's saved states")
+        sms, sk = time_backward(inp, max(3, args.steps // 2), 2, dev, saved=True)
+        extra["backward_saved_states_B8_T2048_H48_D64_N64_C64_f32"] = {
+            "tokens_per_s": round(tokens / (sms * 1e-3), 1), "ms_per_step": round(sms, 4),
+            "kernels_avg_ms": {k: round(v, 5) for k, v in sk.items()}}
         progress("timing the decode step")
         dms, dkms = time_decode(d4["B"], d4["H"], d4["D"], d4["N"], d4["steps"], 8, dev)
         dbytes = decode_hbm_bytes(d4["B"], d4["H"], d4["D"], d4["N"])

@@ -61,6 +61,10 @@ def load_library(path: Optional[str] = None):
         lib.cssd_backward.restype = ctypes.c_int
         lib.cssd_backward.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 \
             + [_vp] * 2 + [_vp] * 4 + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 + [_vp, _sz, _vp]
+        lib.cssd_backward_saved.restype = ctypes.c_int
+        lib.cssd_backward_saved.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 \
+            + [_vp] * 2 + [_vp] * 2 + [_vp] * 2 + [_vp] * 4 + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 \
+            + [_vp, _sz, _vp]
         lib.cssd_step.restype = ctypes.c_int
         lib.cssd_step.argtypes = [_i64] * 4 + [_vp] * 10 + [_vp] * 4 + [_vp]
         lib.cssd_step_n.restype = ctypes.c_int
@@ -232,6 +236,25 @@ def cssd_backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0,
     Returns a dict of float32 tensors: dx_re, dx_im, dB_re, dB_im, dC_re, dC_im,
     ddt, dA_re, dA_im, dD (None without Dskip), dh0_re, dh0_im (None unless
     want_dh0)."""
+    return _backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, dy, dhT,
+                     chunk, want_dh0, workspace, stream, None)
+
+
+def cssd_backward_saved(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, hT, dy,
+                        dhT=None, *, chunk: int, workspace, want_dh0: bool = True, stream=None):
+    """cssd_backward on the states a cssd_forward call left in `workspace` (a uint8
+    tensor of at least cssd_backward_workspace_size bytes that was that call's
+    workspace, untouched since); hT = (hT_re, hT_im) is that call's final state,
+    needed when dhT is given, else may be None.  Same result as cssd_backward,
+    without the forward recomputation."""
+    if workspace is None:
+        raise ValueError("cssd_backward_saved needs the forward call's workspace")
+    return _backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, dy, dhT,
+                     chunk, want_dh0, workspace, stream, (hT,))
+
+
+def _backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, dy, dhT, chunk,
+              want_dh0, workspace, stream, saved):
     torch = _torch()
     lib = load_library()
     dev = x_re.device
@@ -247,7 +270,9 @@ def cssd_backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0,
                          ("dy_re", dy[0], (Bsz, T, H, D)), ("dy_im", dy[1], (Bsz, T, H, D))):
         p[name] = _check(t, name, shp, f32, dev)
     p["Dskip"] = None if Dskip is None else _check(Dskip, "Dskip", (H,), f32, dev)
-    for key, pair, shp in (("h0", h0, (Bsz, H, N, D)), ("dhT", dhT, (Bsz, H, N, D))):
+    hT = None if saved is None else saved[0]
+    for key, pair, shp in (("h0", h0, (Bsz, H, N, D)), ("dhT", dhT, (Bsz, H, N, D)),
+                           ("hT", hT, (Bsz, H, N, D))):
         p[key + "_re"] = None if pair is None else _check(pair[0], key + "_re", shp, f32, dev)
         p[key + "_im"] = None if pair is None else _check(pair[1], key + "_im", shp, f32, dev)
     e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
@@ -264,16 +289,19 @@ def cssd_backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0,
         raise ValueError("workspace must be a contiguous tensor on the same device")
     ws_bytes = workspace.numel() * workspace.element_size()
     ptr = lambda t: None if t is None else t.data_ptr()
-    st = lib.cssd_backward(Bsz, T, H, D, N, int(chunk), CSSD_F32,
-                           p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
-                           p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"],
-                           p["y_re"], p["y_im"], p["dy_re"], p["dy_im"], p["dhT_re"],
-                           p["dhT_im"], *(ptr(g[k]) for k in ("dx_re", "dx_im", "dB_re", "dB_im",
-                                                             "dC_re", "dC_im", "ddt", "dA_re",
-                                                             "dA_im", "dD", "dh0_re", "dh0_im")),
-                           workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
+    head = (Bsz, T, H, D, N, int(chunk), CSSD_F32,
+            p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
+            p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"], p["y_re"], p["y_im"])
+    tail = (p["dy_re"], p["dy_im"], p["dhT_re"], p["dhT_im"],
+            *(ptr(g[k]) for k in ("dx_re", "dx_im", "dB_re", "dB_im", "dC_re", "dC_im", "ddt",
+                                  "dA_re", "dA_im", "dD", "dh0_re", "dh0_im")),
+            workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
+    if saved is None:
+        st, name = lib.cssd_backward(*head, *tail), "cssd_backward"
+    else:
+        st, name = lib.cssd_backward_saved(*head, p["hT_re"], p["hT_im"], *tail), "cssd_backward_saved"
     if st != CSSD_OK:
-        raise CSSDError(st, "cssd_backward")
+        raise CSSDError(st, name)
     return g
 
 

@@ -341,16 +341,23 @@ int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, 
     return CSSD_OK;
 }
 
-int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
-                  int64_t chunk, int32_t in_dtype, const void* x_re, const void* x_im,
-                  const void* B_re, const void* B_im, const void* C_re, const void* C_im,
-                  const float* dt, const float* A_re, const float* A_im, const float* Dskip,
-                  const float* h0_re, const float* h0_im, const float* y_re, const float* y_im,
-                  const float* dy_re, const float* dy_im, const float* dhT_re,
-                  const float* dhT_im, float* dx_re, float* dx_im, float* dB_re, float* dB_im,
-                  float* dC_re, float* dC_im, float* ddt, float* dA_re, float* dA_im, float* dD,
-                  float* dh0_re, float* dh0_im, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// cssd_backward and cssd_backward_saved.  saved: the workspace already holds the
+// forward's cumsums and chunk states and fhT_* is the forward's final state (read
+// only with dhT); else both are recomputed here.
+int backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+             int64_t chunk, int32_t in_dtype, const void* x_re, const void* x_im,
+             const void* B_re, const void* B_im, const void* C_re, const void* C_im,
+             const float* dt, const float* A_re, const float* A_im, const float* Dskip,
+             const float* h0_re, const float* h0_im, const float* y_re, const float* y_im,
+             const float* dy_re, const float* dy_im, const float* dhT_re, const float* dhT_im,
+             float* dx_re, float* dx_im, float* dB_re, float* dB_im, float* dC_re, float* dC_im,
+             float* ddt, float* dA_re, float* dA_im, float* dD, float* dh0_re, float* dh0_im,
+             void* workspace, size_t workspace_bytes, void* stream, bool saved,
+             const float* fhT_re, const float* fhT_im) {
     const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
     if (st != CSSD_OK) return st;
     if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
@@ -373,8 +380,16 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
     const uintptr_t opt_al[] = {4, 16, 16, 16, 16, 4, 16, 16};
     for (int i = 0; i < 8; ++i)
         if (opt[i] != nullptr && !aligned(opt[i], opt_al[i])) return CSSD_ERR_INVALID_ARG;
+    if (saved) {
+        // the forward's final state enters only the term <dhT, hT>
+        if ((fhT_re == nullptr) != (fhT_im == nullptr) || !aligned(fhT_re, 16) ||
+            !aligned(fhT_im, 16) || (dhT_re != nullptr && fhT_re == nullptr))
+            return CSSD_ERR_INVALID_ARG;
+    } else {
+        fhT_re = fhT_im = nullptr;
+    }
     const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re,
-                         h0_im, y_re, y_im, dy_re, dy_im, dhT_re, dhT_im};
+                         h0_im, y_re, y_im, dy_re, dy_im, dhT_re, dhT_im, fhT_re, fhT_im};
     const void* outs[] = {dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt, dA_re, dA_im, dD,
                           dh0_re, dh0_im};
     for (int i = 0; i < 12; ++i) {
@@ -408,18 +423,21 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
     a.q2_re = reinterpret_cast<float*>(ws + L.q2_re);
     a.q2_im = reinterpret_cast<float*>(ws + L.q2_im);
     a.ddp = reinterpret_cast<float*>(ws + L.ddp);
-    a.hT_re = a.f.hT_re;
-    a.hT_im = a.f.hT_im;
+    a.hT_re = saved ? fhT_re : a.f.hT_re;
+    a.hT_im = saved ? fhT_im : a.f.hT_im;
     a.z_re = reinterpret_cast<double*>(ws + L.z_re);
     a.z_im = reinterpret_cast<double*>(ws + L.z_im);
     a.pa = reinterpret_cast<double*>(ws + L.pa);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     // forward recomputation: cumsums, chunk states, carry-in states H_c and hT
-    if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a.f, s); }) != hipSuccess)
-        return CSSD_ERR_HIP;
-    if (timed(cssd::K_STATE_SCAN, s, [&] { return cssd::launch_state_scan(a.f, s); }) != hipSuccess)
-        return CSSD_ERR_HIP;
+    if (!saved) {
+        if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a.f, s); }) != hipSuccess)
+            return CSSD_ERR_HIP;
+        if (timed(cssd::K_STATE_SCAN, s, [&] { return cssd::launch_state_scan(a.f, s); }) !=
+            hipSuccess)
+            return CSSD_ERR_HIP;
+    }
     // adjoint chunk states and the backward pass over chunks: R_{c+1}, dh0 (and,
     // where the two are fused, the boundary terms of the log-decay gradient)
     const bool fused_adj = cssd::state_scan_adjoint_fused(a.f);
@@ -451,6 +469,45 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
         hipSuccess)
         return CSSD_ERR_HIP;
     return CSSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                  int64_t chunk, int32_t in_dtype, const void* x_re, const void* x_im,
+                  const void* B_re, const void* B_im, const void* C_re, const void* C_im,
+                  const float* dt, const float* A_re, const float* A_im, const float* Dskip,
+                  const float* h0_re, const float* h0_im, const float* y_re, const float* y_im,
+                  const float* dy_re, const float* dy_im, const float* dhT_re,
+                  const float* dhT_im, float* dx_re, float* dx_im, float* dB_re, float* dB_im,
+                  float* dC_re, float* dC_im, float* ddt, float* dA_re, float* dA_im, float* dD,
+                  float* dh0_re, float* dh0_im, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    return backward(batch, seqlen, nheads, headdim, dstate, chunk, in_dtype, x_re, x_im, B_re,
+                    B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im, y_re, y_im, dy_re,
+                    dy_im, dhT_re, dhT_im, dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt, dA_re,
+                    dA_im, dD, dh0_re, dh0_im, workspace, workspace_bytes, stream, false, nullptr,
+                    nullptr);
+}
+
+int cssd_backward_saved(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t chunk, int32_t in_dtype, const void* x_re,
+                        const void* x_im, const void* B_re, const void* B_im, const void* C_re,
+                        const void* C_im, const float* dt, const float* A_re, const float* A_im,
+                        const float* Dskip, const float* h0_re, const float* h0_im,
+                        const float* y_re, const float* y_im, const float* hT_re,
+                        const float* hT_im, const float* dy_re, const float* dy_im,
+                        const float* dhT_re, const float* dhT_im, float* dx_re, float* dx_im,
+                        float* dB_re, float* dB_im, float* dC_re, float* dC_im, float* ddt,
+                        float* dA_re, float* dA_im, float* dD, float* dh0_re, float* dh0_im,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return backward(batch, seqlen, nheads, headdim, dstate, chunk, in_dtype, x_re, x_im, B_re,
+                    B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im, y_re, y_im, dy_re,
+                    dy_im, dhT_re, dhT_im, dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt, dA_re,
+                    dA_im, dD, dh0_re, dh0_im, workspace, workspace_bytes, stream, true, hT_re,
+                    hT_im);
 }
 
 namespace {

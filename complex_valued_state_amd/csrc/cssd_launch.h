@@ -35,7 +35,7 @@ struct BwdArgs {
     float *r_re, *r_im;                      // adjoint chunk states Q_c, then R_{c+1}
     float *q1_re, *q1_im, *q2_re, *q2_im;    // per position: the dx and y halves of q
     float *ddp;                              // per position: Re(dy . conj(x))
-    float *hT_re, *hT_im;                    // final state of the recomputed forward
+    const float *hT_re, *hT_im;              // the forward's final state (read only)
     double *z_re, *z_im;                     // per chunk, two partials: <R_{c+1}, H_{c+1}>
     double* pa;                              // per span of each (b, h): dA re, dA im, dDskip
 };

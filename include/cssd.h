@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 106 /* major*100 + minor */
+#define CSSD_VERSION 107 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
@@ -239,6 +239,39 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * cssd_backward without the forward recomputation: the caller ran cssd_forward
+ * for these same inputs and chunk on `workspace` (a buffer of at least
+ * cssd_backward_workspace_size bytes; the backward's layout begins with the
+ * forward's), left it untouched since, and passes that call's final state.  The
+ * cumsums and chunk states the forward stored there are used as they are (the
+ * autograd of the pages keeps forward tensors for the gradient in the same
+ * way: Mamba-3-Lite docs, "SSD Theory", autograd notes), which saves the
+ * recomputation's launches (ids 0 and 14).  The gradients are bit-identical to
+ * cssd_backward's for the same inputs.
+ *   hT_re, hT_im   [B,H,N,D] the forward's final state; required when dhT is
+ *                  given (it enters <dhT, hT>), else may be NULL
+ * Every other argument as cssd_backward.  A workspace that does not hold that
+ * forward's results gives undefined gradients (this is not detected).
+ */
+int cssd_backward_saved(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t chunk, int32_t in_dtype,
+                        const void *x_re, const void *x_im,
+                        const void *B_re, const void *B_im,
+                        const void *C_re, const void *C_im,
+                        const float *dt, const float *A_re, const float *A_im,
+                        const float *Dskip,
+                        const float *h0_re, const float *h0_im,
+                        const float *y_re, const float *y_im,
+                        const float *hT_re, const float *hT_im,
+                        const float *dy_re, const float *dy_im,
+                        const float *dhT_re, const float *dhT_im,
+                        float *dx_re, float *dx_im, float *dB_re, float *dB_im,
+                        float *dC_re, float *dC_im, float *ddt,
+                        float *dA_re, float *dA_im, float *dD,
+                        float *dh0_re, float *dh0_im,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * n recurrent steps that all receive the same input, applied at once in O(1)
  * work per state element (burn-mamba docs, module step_constant: the unrolled
  * constant-input steps form a geometric series; this is its case with no
@@ -364,7 +397,7 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
  * 2 state_pass, 3 chunk_scan, 4 step (also cssd_step_n), 5 step_infinite,
  * 14 state_scan (cssd_forward: the chunk states fused with the state pass),
  * 6 bwd_dx, 7 bwd_dc, 8 bwd_dz, 13 bwd_db (cssd_backward also runs ids 0 and 14,
- * then 15 state_scan_adj, the adjoint chunk states and pass fused, where
+ * cssd_backward_saved does not; both then run 15 state_scan_adj, the adjoint chunk states and pass fused, where
  * dstate = headdim = chunk = 64, else 1 and 2 in their adjoint modes), 9 phase_summary,
  * 10 phase_carry, 11 phase_out (cssd_phase_scan), 12 born (cssd_born_attention),
  * 16 fill (the states and zeroed sums of an empty problem, one launch per plane).

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("cssd_forward", "cssd_backward", "cssd_backward_workspace_size",
+    for required in ("cssd_forward", "cssd_backward", "cssd_backward_saved",
+                     "cssd_backward_workspace_size",
                      "cssd_step", "cssd_step_n", "cssd_step_infinite", "cssd_phase_scan",
                      "cssd_phase_scan_workspace_size", "cssd_born_attention",
                      "cssd_forward_workspace_size", "cssd_status_string", "cssd_version"):
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 106
+    assert lib.cssd_version() == 107
     for st in range(5):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -189,6 +190,17 @@ def test_backward_validation(lib):
     assert lib.cssd_backward(*args(bad)) == 1
     bad = list(good); bad[2] = bad[0]                     # dB aliases dx
     assert lib.cssd_backward(*args(bad)) == 1
+    # the saved-state form: the forward's hT is needed with dhT, and may alias no output
+    hT = [p[32], p[33]]
+    sargs = lambda g, hT=hT, dhT=(None, None), shape=(1, 64, 2, 16, 16, 16): (
+        *shape, 0, *ins[:14], *hT, *ins[14:], *dhT, *g, ws, 1 << 30, None)
+    assert lib.cssd_backward_saved(*sargs(grads)) == 1
+    assert lib.cssd_backward_saved(*sargs(good, hT=(None, None), dhT=(p[34], p[35]))) == 1
+    assert lib.cssd_backward_saved(*sargs(good, hT=(p[32], None))) == 1
+    assert lib.cssd_backward_saved(*sargs(good, hT=(p[32] + 4, p[33]))) == 1
+    bad = list(good); bad[0] = hT[0]                      # dx aliases hT
+    assert lib.cssd_backward_saved(*sargs(bad)) == 1
+    assert lib.cssd_backward_saved(*sargs(good, shape=(1, 64, 2, 16, 24, 16))) == 2
 
 
 def _phase_ws(lib, *shape):

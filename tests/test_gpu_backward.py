@@ -109,3 +109,56 @@ def test_backward_mamba_layer_shape_reduced_batch():
     log("  backward B1 T2048 H6 D64 N64 C64")
     got, want = _grads(inp, True, seed=11)
     _check(got, want)
+
+
+SAVED = [
+    # (B, T, H, D, N, C, with_h0, with_dskip, with_dhT)
+    (2, 200, 3, 64, 64, 64, True, True, True),     # staged kernels and fused adjoint pass
+    (3, 190, 3, 64, 64, 64, False, True, False),
+    (2, 100, 3, 32, 64, 16, True, True, True),     # tile kernels, adjoint pass in two launches
+    (1, 300, 2, 16, 128, 128, True, False, False),
+]
+
+
+@pytest.mark.parametrize("case", SAVED, ids=lambda c: "B{}T{}H{}D{}N{}C{}{}{}{}".format(
+    *c[:6], "_h0" if c[6] else "", "_D" if c[7] else "", "_dhT" if c[8] else ""))
+def test_backward_saved_states(case):
+    """cssd_backward_saved on the workspace and final state a cssd_forward call
+    left gives cssd_backward's gradients bit for bit (same kernels on the same
+    states), and both meet the oracle."""
+    import torch
+    import complex_valued_state_amd as cssd
+    Bsz, T, H, D, N, C, with_h0, with_d, with_dhT = case
+    log(f"backward saved {case}")
+    inp = wl.random_forward(61, Bsz, T, H, D, N, C, with_h0=with_h0, with_dskip=with_d)
+    d = dev_inputs(inp)
+    rng = np.random.default_rng(62)
+    cz = lambda *s: (np.sqrt(0.5) * (rng.standard_normal(s) + 1j * rng.standard_normal(s))
+                     ).astype(np.complex64)
+    gy = cz(Bsz, T, H, D)
+    ghT = cz(Bsz, H, N, D) if with_dhT else None
+    pl = lambda a: (_dev(a.real.copy()), _dev(a.imag.copy()))
+    ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
+           d["A_im"], d["Dskip"], d["h0"])
+    ws = torch.empty(cssd.cssd_backward_workspace_size(Bsz, T, H, D, N, C), dtype=torch.uint8,
+                     device="cuda:0")
+    y_re, y_im, hT_re, hT_im = cssd.cssd_forward(*ins, chunk=C, workspace=ws)
+    with cssd.profile() as prof:
+        gs = cssd.cssd_backward_saved(*ins, (y_re, y_im), (hT_re, hT_im), pl(gy),
+                                      None if ghT is None else pl(ghT), chunk=C, workspace=ws)
+        torch.cuda.synchronize()
+    assert prof.launches["k_cumsum"] == 0 and prof.launches["k_state_scan"] == 0
+    g = cssd.cssd_backward(*ins, (y_re, y_im), pl(gy), None if ghT is None else pl(ghT), chunk=C)
+    torch.cuda.synchronize()
+    for k, v in g.items():
+        if v is not None:
+            assert torch.equal(v, gs[k]), k
+    n = lambda t: None if t is None else t.double().cpu().numpy()
+    got = {"dx": n(gs["dx_re"]) + 1j * n(gs["dx_im"]), "dB": n(gs["dB_re"]) + 1j * n(gs["dB_im"]),
+           "dC": n(gs["dC_re"]) + 1j * n(gs["dC_im"]), "ddt": n(gs["ddt"]),
+           "dA": n(gs["dA_re"]) + 1j * n(gs["dA_im"]), "dD": n(gs["dD"]),
+           "dh0": n(gs["dh0_re"]) + 1j * n(gs["dh0_im"])}
+    x, Bm, Cm, dt, A, Dk, h0 = inp.complex()
+    want = oracle.backward(x, Bm, Cm, dt, A, Dk, h0, gy.astype(np.complex128),
+                           None if ghT is None else ghT.astype(np.complex128))
+    _check(got, want, skip_dD=not with_d)
