@@ -269,3 +269,62 @@ def test_config2_homogeneous_phase_transport():
     # relative to each head's own scale: heads decay by very different amounts
     for h in range(s["H"]):
         assert rel_err(hT[0, h], want[0, h]) <= TOL_F32, h
+
+
+NONFINITE = [
+    # (input, value, B, T, H, D, N, C)
+    ("x_re", np.nan, 2, 200, 3, 64, 64, 64),
+    ("B_im", np.inf, 2, 200, 3, 64, 64, 64),
+    ("C_re", np.nan, 2, 200, 3, 64, 64, 64),
+    ("dt", np.nan, 2, 200, 3, 64, 64, 64),
+    ("x_im", np.inf, 2, 150, 3, 32, 64, 16),
+    ("B_re", np.nan, 2, 150, 3, 32, 64, 16),
+    ("dt", np.nan, 2, 150, 3, 32, 64, 16),
+    ("C_im", np.inf, 2, 150, 3, 32, 64, 16),
+]
+
+
+@pytest.mark.parametrize("case", NONFINITE, ids=lambda c: f"{c[0]}_{c[1]}_D{c[5]}N{c[6]}C{c[7]}")
+def test_nonfinite_input_propagates(case):
+    """A NaN or Inf placed in one input element at (b, t0, h) is not clamped away:
+    every output the recurrence makes non-finite (the oracle on the same inputs)
+    is non-finite here too.  Other (b, h) and the positions before t0's 16-step
+    tile are bit-identical to the clean run; inside that tile earlier positions may
+    turn NaN as well (a masked product 0 x NaN in the tile's matrix product is
+    NaN).  Outputs that stay finite on both sides meet the oracle.  (dt = +inf is
+    left out: its limit a = 0 is finite, and the pages give it no value.)"""
+    import dataclasses
+    name, val, Bsz, T, H, D, N, C = case
+    b0, t0, h0 = 1, 77, 2
+    log(f"non-finite {case}")
+    inp = wl.random_forward(71, Bsz, T, H, D, N, C, with_h0=True)
+    arr = getattr(inp, name).copy()
+    if arr.ndim == 3:
+        arr[b0, t0, h0] = val
+    else:
+        arr[b0, t0, h0, 5] = val
+    bad = dataclasses.replace(inp, **{name: arr})
+    y_c, hT_c = gpu_forward(inp)
+    y_b, hT_b = gpu_forward(bad)
+    y_r, hT_r = oracle_forward(bad)
+    assert not np.all(np.isfinite(y_r))
+    assert np.all(np.isfinite(hT_r)) == name.startswith("C")  # C never enters the state
+    # no clamping
+    assert np.all(~np.isfinite(y_b)[~np.isfinite(y_r)])
+    assert np.all(~np.isfinite(hT_b)[~np.isfinite(hT_r)])
+    # untouched rows and earlier tiles are unchanged bit for bit
+    other = np.ones((Bsz, H), bool)
+    other[b0, h0] = False
+    assert np.array_equal(y_b.transpose(0, 2, 1, 3)[other], y_c.transpose(0, 2, 1, 3)[other])
+    assert np.array_equal(hT_b[other], hT_c[other])
+    tile0 = t0 // 16 * 16
+    assert np.array_equal(y_b[b0, :tile0, h0], y_c[b0, :tile0, h0])
+    # past t0, what the oracle keeps finite is finite here and matches it
+    y_after, r_after = y_b[b0, t0:, h0], y_r[b0, t0:, h0]
+    fin = np.isfinite(r_after)
+    assert np.all(np.isfinite(y_after[fin]))
+    scale = float(np.max(np.abs(y_c[b0, :, h0])))
+    if fin.any():
+        assert float(np.max(np.abs(y_after[fin] - r_after[fin]))) / scale <= TOL_F32
+    finT = np.isfinite(hT_r[b0, h0])
+    assert np.all(np.isfinite(hT_b[b0, h0][finT]))
