@@ -162,6 +162,23 @@ def _to_dev(inp, dev):
             None if inp.Dskip is None else t(inp.Dskip)]
 
 
+SETTLE_S = 0.2
+
+
+def settle(call, dev, seconds=SETTLE_S):
+    """Run `call` untimed for `seconds` of wall time before the warm-up steps.  An
+    idle GPU (it waits while the host draws the inputs) takes tens of milliseconds
+    of work to reach its steady clocks, longer than a few warm-up calls: measured
+    on the forward workload, 0.87 ms per step in the first 20 steps after five
+    warm-up calls and 0.78 ms once settled."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize(dev)
+
+
 def time_forward(inp, steps, warmup, dev):
     import torch
     import complex_valued_state_amd as cssd
@@ -176,6 +193,7 @@ def time_forward(inp, steps, warmup, dev):
     stream = torch.cuda.current_stream(dev)
     run = lambda: cssd.cssd_forward(*args, None, chunk=s["C"], out=(y_re, y_im, h_re, h_im),
                                     workspace=ws, stream=stream)
+    settle(run, dev)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize(dev)
@@ -212,6 +230,7 @@ def time_constant_input(B, H, D, N, nsteps, reps, warmup, dev, seed=4):
     res = {}
     for name, call in (("step_n", lambda: cssd.cssd_step_n(*args, h_re, h_im, nsteps, stream=stream)),
                        ("step_infinite", lambda: cssd.cssd_step_infinite(*args, stream=stream))):
+        settle(call, dev)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize(dev)
@@ -258,6 +277,7 @@ def time_phase_scan(B, T, H, N, steps, warmup, dev, chunk=0, seed=5):
     stream = torch.cuda.current_stream(dev)
     call = lambda: cssd.cssd_phase_scan(phi, u, b_re, b_im, psi0, chunk=chunk, out=outs,
                                         workspace=ws, stream=stream)
+    settle(call, dev)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize(dev)
@@ -289,6 +309,7 @@ def time_born(B, T, H, D, steps, warmup, dev, seed=6, bf16=False):
     out = (torch.empty(shp, device=dev), torch.empty(shp, device=dev))
     stream = torch.cuda.current_stream(dev)
     call = lambda: cssd.cssd_born_attention(*planes, tau, out=out, stream=stream)
+    settle(call, dev)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize(dev)
@@ -331,6 +352,7 @@ def time_backward(inp, steps, warmup, dev, seed=9, saved=False):
         else:
             cssd.cssd_backward(*ins, y, dy, dhT, chunk=inp.chunk, workspace=ws, stream=stream)
 
+    settle(run, dev)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize(dev)
@@ -367,6 +389,7 @@ def time_decode(B, H, D, N, tokens, warmup, dev, seed=4):
         cssd.cssd_step(xs[0][t], xs[1][t], bs[0][t], bs[1][t], cs[0][t], cs[1][t], dts[t], a_re,
                        a_im, dk, h_re, h_im, out=(y_re[t], y_im[t]), stream=stream)
 
+    settle(lambda: step(0), dev)
     for t in range(warmup):
         step(t % tokens)
     h_re.zero_(); h_im.zero_()
