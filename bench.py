@@ -8,11 +8,13 @@ discretise + chunk-local cumsum, the chunk states with the inter-chunk state
 pass (one fused kernel) and the intra-chunk output with the combine, all in the
 library's HIP kernels.
 Inputs are seeded synthetic data already resident in HBM when timing starts.
-Prints ONE JSON line.  Per-kernel durations come from HIP events the library
+Each timed call first runs untimed for 200 ms (the GPU clocks settle), then W
+warm-up calls, then exactly K timed calls.  Prints ONE JSON line.  Per-kernel durations come from HIP events the library
 records around each launch on the launch stream during the timed region.
 
 Extra figures in the same line: the bf16-input variant of the same workload, the
-backward pass of the same workload, the decode step at batch 256 x 48 heads x
+backward pass of the same workload (recomputing the forward's states, and on the
+states a forward call saved), the decode step at batch 256 x 48 heads x
 N128 x D64 over 512 pre-staged tokens, the constant-input calls at that shape,
 the per-coordinate phase-state scan at 256 x 1024 x 16 x 16, causal Born
 attention at 256 x 1024 x 16 heads x width 16, and (with --all)
