@@ -1,0 +1,114 @@
+"""HIP graph capture of the library's calls (needs an MI355X).
+
+The entry points never allocate, copy, clear or synchronise: each enqueues its
+kernels on the caller's stream.  So a caller may capture them in a graph and
+replay it.  Each test captures once, replays several times with the program's
+own eager work (overwriting the outputs, resetting the state) and a
+synchronisation between replays, and checks every replay bit for bit against
+the eager result.
+"""
+import numpy as np
+import pytest
+
+import cssd_workloads as wl
+from gpu_util import dev_inputs, log
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def test_training_step_graph_replays():
+    """Forward on a backward-sized workspace, then the backward on the states it
+    saved: one captured graph, replayed."""
+    import torch
+    import complex_valued_state_amd as cssd
+    Bsz, T, H, D, N, C = 2, 300, 3, 64, 64, 64
+    log("graph: forward + backward_saved")
+    inp = wl.random_forward(81, Bsz, T, H, D, N, C, with_h0=True)
+    d = dev_inputs(inp)
+    ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
+           d["A_im"], d["Dskip"], d["h0"])
+    g = torch.Generator(device="cuda:0").manual_seed(82)
+    dy = [torch.randn((Bsz, T, H, D), generator=g, device="cuda:0") for _ in range(2)]
+    dhT = [torch.randn((Bsz, H, N, D), generator=g, device="cuda:0") for _ in range(2)]
+    ws = torch.empty(cssd.cssd_backward_workspace_size(Bsz, T, H, D, N, C), dtype=torch.uint8,
+                     device="cuda:0")
+    y = [torch.empty((Bsz, T, H, D), device="cuda:0") for _ in range(2)]
+    hT = [torch.empty((Bsz, H, N, D), device="cuda:0") for _ in range(2)]
+
+    def step():
+        cssd.cssd_forward(*ins, chunk=C, out=(*y, *hT), workspace=ws)
+        return cssd.cssd_backward_saved(*ins, tuple(y), tuple(hT), dy, dhT, chunk=C,
+                                        workspace=ws)
+
+    ref_g = step()
+    torch.cuda.synchronize()
+    ref = {"y_re": y[0].clone(), "y_im": y[1].clone(), "hT_re": hT[0].clone(),
+           "hT_im": hT[1].clone(), **{k: v.clone() for k, v in ref_g.items() if v is not None}}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gg = step()
+    for rep in range(REPLAYS):
+        for t in (*y, *hT, *(v for v in gg.values() if v is not None)):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {"y_re": y[0], "y_im": y[1], "hT_re": hT[0], "hT_im": hT[1],
+               **{k: v for k, v in gg.items() if v is not None}}
+        for k, v in ref.items():
+            assert torch.equal(got[k], v), (rep, k)
+
+
+def test_decode_step_graph_replays():
+    """cssd_step updates its state in place: the state is reset eagerly before
+    each replay, and the replay must give the eager step's state and output."""
+    import torch
+    import complex_valued_state_amd as cssd
+    B, H, D, N = 8, 6, 64, 128
+    log("graph: decode step")
+    st = wl.decode_step(83, 0, B, H, D, N)
+    a_re, a_im, dk = (_dev(v) for v in wl.decode_params(83, H))
+    args = [_dev(getattr(st, f)) for f in ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt")]
+    rng = np.random.default_rng(84)
+    h0 = [_dev(rng.standard_normal((B, H, N, D)).astype(np.float32)) for _ in range(2)]
+    h = [t.clone() for t in h0]
+    y = [torch.empty((B, H, D), device="cuda:0") for _ in range(2)]
+
+    def step():
+        cssd.cssd_step(*args, a_re, a_im, dk, h[0], h[1], out=tuple(y))
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (*h, *y)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(REPLAYS):
+        h[0].copy_(h0[0])
+        h[1].copy_(h0[1])
+        y[0].fill_(float("nan"))
+        y[1].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (got, want) in enumerate(zip((*h, *y), ref)):
+            assert torch.equal(got, want), (rep, k)
