@@ -328,3 +328,51 @@ def test_nonfinite_input_propagates(case):
         assert float(np.max(np.abs(y_after[fin] - r_after[fin]))) / scale <= TOL_F32
     finT = np.isfinite(hT_r[b0, h0])
     assert np.all(np.isfinite(hT_b[b0, h0][finT]))
+
+
+def test_maximum_size_sampled():
+    """The largest problem the forward accepts at D = N = C = 64 with 64 heads:
+    B1 T524287 H64 (2^31 - 4096 elements per plane, a ragged last chunk, every
+    size limit of the entry point met with equality, about 80 GB of HBM).  Inputs
+    are drawn on the device (torch's seeded generator, the config-0
+    distributions).  The oracle runs the last head's whole sequence (the highest
+    addresses, the ragged tail, hT) and the first 4096 steps of head 0."""
+    import torch
+    import complex_valued_state_amd as cssd
+    import oracle
+    Bsz, T, H, D, N, C = 1, (1 << 19) - 1, 64, 64, 64, 64
+    assert Bsz * T * H * max(D, N) == (1 << 31) - 4096
+    log("max size: drawing inputs on the device")
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(91)
+    r = math.sqrt(0.5)
+    pl = lambda n: [torch.randn((Bsz, T, H, n), generator=g, device=dev).mul_(r) for _ in range(2)]
+    x, Bm, Cm = pl(D), pl(N), pl(N)
+    dt = torch.randn((Bsz, T, H), generator=g, device=dev)
+    a_re = -(0.1 + 0.9 * torch.rand(H, generator=g, device=dev))
+    a_im = (2 * torch.rand(H, generator=g, device=dev) - 1) * math.pi
+    dk = torch.randn(H, generator=g, device=dev)
+    log("max size: forward")
+    y_re, y_im, h_re, h_im = cssd.cssd_forward(*x, *Bm, *Cm, dt, a_re, a_im, dk, None, chunk=C)
+    torch.cuda.synchronize()
+    log("max size: oracle")
+    f64 = lambda t: t.double().cpu().numpy()
+    for h, steps in ((H - 1, T), (0, 4096)):
+        sl = lambda p: p[:, :steps, h:h + 1]
+        xs = f64(sl(x[0])) + 1j * f64(sl(x[1]))
+        bs = f64(sl(Bm[0])) + 1j * f64(sl(Bm[1]))
+        cs = f64(sl(Cm[0])) + 1j * f64(sl(Cm[1]))
+        A = np.array([float(a_re[h]) + 1j * float(a_im[h])])
+        yr, hTr = oracle.forward(xs, bs, cs, f64(dt[:, :steps, h:h + 1]), A,
+                                 np.array([float(dk[h])]), None)
+        yg = f64(sl(y_re)) + 1j * f64(sl(y_im))
+        err = rel_err(yg, yr)
+        log(f"  head {h}, {steps} steps: y rel err {err:.2e}")
+        assert err <= TOL_F32, (h, err)
+        if steps == T:
+            hg = f64(h_re[:, h:h + 1]) + 1j * f64(h_im[:, h:h + 1])
+            errh = rel_err(hg, hTr)
+            log(f"  head {h}: hT rel err {errh:.2e}")
+            assert errh <= TOL_F32, (h, errh)
+    del x, Bm, Cm, dt, y_re, y_im, h_re, h_im
+    torch.cuda.empty_cache()
