@@ -162,3 +162,56 @@ def test_backward_saved_states(case):
     want = oracle.backward(x, Bm, Cm, dt, A, Dk, h0, gy.astype(np.complex128),
                            None if ghT is None else ghT.astype(np.complex128))
     _check(got, want, skip_dD=not with_d)
+
+
+def test_backward_maximum_size_sampled():
+    """The gradient pass at the largest size the entry points accept at
+    D = N = C = 64 with 64 heads, taken as B64 T8191 H64 (2^31 - 2^18 elements
+    per plane, a ragged last chunk, the size checks met with equality; about 180
+    GB of HBM with inputs, outputs and workspaces).  Inputs are drawn on the
+    device (torch's seeded generator, the config-0 distributions).  The oracle
+    runs three whole (b, h) sequences, among them the last one (the highest
+    addresses); dA and dDskip sum over every batch row and are checked at the
+    smaller sizes above."""
+    import math
+    import torch
+    import complex_valued_state_amd as cssd
+    Bsz, T, H, D, N, C = 64, 8191, 64, 64, 64, 64
+    assert Bsz * T * H * max(D, N) == (1 << 31) - (1 << 18)
+    log("backward max size: drawing inputs on the device")
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(92)
+    r = math.sqrt(0.5)
+    pl = lambda *s: [torch.randn(s, generator=g, device=dev).mul_(r) for _ in range(2)]
+    x, Bm, Cm, dy = pl(Bsz, T, H, D), pl(Bsz, T, H, N), pl(Bsz, T, H, N), pl(Bsz, T, H, D)
+    dhT = pl(Bsz, H, N, D)
+    dt = torch.randn((Bsz, T, H), generator=g, device=dev)
+    a_re = -(0.1 + 0.9 * torch.rand(H, generator=g, device=dev))
+    a_im = (2 * torch.rand(H, generator=g, device=dev) - 1) * math.pi
+    dk = torch.randn(H, generator=g, device=dev)
+    ins = (*x, *Bm, *Cm, dt, a_re, a_im, dk, None)
+    log("backward max size: forward, backward")
+    y = cssd.cssd_forward(*ins, chunk=C, return_state=False)[:2]
+    torch.cuda.synchronize()
+    gr = cssd.cssd_backward(*ins, y, dy, dhT, chunk=C)
+    torch.cuda.synchronize()
+    log("backward max size: oracle")
+    f64 = lambda t: t.double().cpu().numpy()
+    cplx = lambda p, sl: f64(sl(p[0])) + 1j * f64(sl(p[1]))
+    for b, h in ((Bsz - 1, H - 1), (0, 0), (37, 21)):
+        sl = lambda t: t[b:b + 1, :, h:h + 1]
+        slh = lambda t: t[b:b + 1, h:h + 1]
+        A = np.array([float(a_re[h]) + 1j * float(a_im[h])])
+        want = oracle.backward(cplx(x, sl), cplx(Bm, sl), cplx(Cm, sl), f64(sl(dt)), A,
+                               np.array([float(dk[h])]), None, cplx(dy, sl), cplx(dhT, slh))
+        got = {"dx": f64(sl(gr["dx_re"])) + 1j * f64(sl(gr["dx_im"])),
+               "dB": f64(sl(gr["dB_re"])) + 1j * f64(sl(gr["dB_im"])),
+               "dC": f64(sl(gr["dC_re"])) + 1j * f64(sl(gr["dC_im"])),
+               "ddt": f64(sl(gr["ddt"])),
+               "dh0": f64(slh(gr["dh0_re"])) + 1j * f64(slh(gr["dh0_im"]))}
+        for k, v in got.items():
+            err = rel_err(v, want[k])
+            log(f"  (b, h) = ({b}, {h}) {k}: rel err {err:.2e}")
+            assert err <= TOL, (b, h, k, err)
+    del x, Bm, Cm, dy, dhT, dt, y, gr
+    torch.cuda.empty_cache()
