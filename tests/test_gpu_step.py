@@ -176,3 +176,42 @@ def test_prefill_then_decode():
     yr, hr = oracle_forward(inp)
     assert rel_err(y_dec, yr[:, T1:]) <= TOL and rel_err(h_dec, hr) <= TOL
     assert rel_err(y_dec, y_all[:, T1:]) <= TOL and rel_err(h_dec, h_all) <= TOL
+
+
+def test_step_maximum_size_sampled():
+    """The largest decode step accepted at D = 64, N = 128: batch 4096 x 64 heads,
+    2^31 elements per state plane (16 GB of state, updated in place).  Inputs are
+    drawn on the device (torch's seeded generator); the oracle steps sampled
+    (b, h) rows, the last one included."""
+    import torch
+    import complex_valued_state_amd as cssd
+    import oracle
+    B, H, D, N = 4096, 64, 64, 128
+    assert B * H * D * N == 1 << 31
+    log("step max size: drawing inputs on the device")
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(93)
+    r = math.sqrt(0.5)
+    pl = lambda *s: [torch.randn(s, generator=g, device=dev).mul_(r) for _ in range(2)]
+    x, Bm, Cm, h = pl(B, H, D), pl(B, H, N), pl(B, H, N), pl(B, H, N, D)
+    dt = torch.randn((B, H), generator=g, device=dev)
+    a_re = -(0.1 + 0.9 * torch.rand(H, generator=g, device=dev))
+    a_im = (2 * torch.rand(H, generator=g, device=dev) - 1) * math.pi
+    dk = torch.randn(H, generator=g, device=dev)
+    rows = ((B - 1, H - 1), (0, 0), (2049, 33))
+    f64 = lambda t: t.double().cpu().numpy()
+    h_before = {bh: (f64(h[0][bh[0], bh[1]]), f64(h[1][bh[0], bh[1]])) for bh in rows}
+    log("step max size: step")
+    y = cssd.cssd_step(*x, *Bm, *Cm, dt, a_re, a_im, dk, h[0], h[1])
+    torch.cuda.synchronize()
+    for b, hh in rows:
+        one = lambda p: f64(p[0][b:b + 1, hh:hh + 1]) + 1j * f64(p[1][b:b + 1, hh:hh + 1])
+        h0 = (h_before[(b, hh)][0] + 1j * h_before[(b, hh)][1])[None, None]
+        yr, hr = oracle.step(one(x), one(Bm), one(Cm), f64(dt[b:b + 1, hh:hh + 1]),
+                             np.array([float(a_re[hh]) + 1j * float(a_im[hh])]),
+                             np.array([float(dk[hh])]), h0)
+        ey, eh = rel_err(one(y), yr), rel_err(one(h), hr)
+        log(f"  (b, h) = ({b}, {hh}): y {ey:.2e}, state {eh:.2e}")
+        assert ey <= TOL and eh <= TOL, (b, hh, ey, eh)
+    del x, Bm, Cm, h, dt, y
+    torch.cuda.empty_cache()
