@@ -328,3 +328,30 @@ def test_empty_problems_validate_and_enqueue_nothing(lib):
     for shape in [(0, 100, 3, 16), (2, 0, 3, 32), (2, 100, 0, 64)]:
         assert lib.cssd_born_attention(*shape, 0, *[n] * 7, n, n, n) == 0
     assert lib.cssd_born_attention(2, 0, 3, 24, 0, *[n] * 7, n, n, n) == 2
+
+
+def test_missing_library_raises(tmp_path, monkeypatch):
+    """No fallback: without the built library every call fails loudly."""
+    import complex_valued_state_amd._binding as bd
+    monkeypatch.setattr(bd, "_lib", None)
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "libcssd.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        bd.cssd_forward_workspace_size(1, 64, 2, 16, 16, 16)
+
+
+def test_product_never_reaches_the_oracle():
+    """The package (binding and HIP sources) neither imports, includes nor names the
+    CPU oracle: it is test infrastructure only."""
+    import ast
+    import glob
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "complex_valued_state_amd")
+    for f in glob.glob(os.path.join(pkg, "*.py")):
+        tree = ast.parse(open(f).read())
+        for node in ast.walk(tree):
+            if isinstance(node, ast.Import):
+                assert not any(a.name.split(".")[0] == "oracle" for a in node.names), f
+            if isinstance(node, ast.ImportFrom):
+                assert (node.module or "").split(".")[0] != "oracle", f
+    for f in glob.glob(os.path.join(pkg, "csrc", "*")):
+        assert "oracle" not in open(f).read().lower(), f
