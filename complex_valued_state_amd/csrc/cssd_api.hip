@@ -65,11 +65,24 @@ hipError_t timed(int kernel, hipStream_t stream, F&& launch) {
             e1 = take_event(p);
         }
     }
-    if (e0 && e1 && hipEventRecord(e0, stream) != hipSuccess) return hipGetLastError();
+    // on every early return the events go back to the pool, so none is leaked
+    auto give_back = [&](hipError_t err) {
+        if (e0 || e1) {
+            std::lock_guard<std::mutex> g(p.mu);
+            if (e0) p.pool.push_back(e0);
+            if (e1) p.pool.push_back(e1);
+        }
+        return err;
+    };
+    if (!(e0 && e1)) {
+        give_back(hipSuccess);
+        e0 = e1 = nullptr;
+    }
+    if (e0 && hipEventRecord(e0, stream) != hipSuccess) return give_back(hipGetLastError());
     hipError_t err = launch();
-    if (err != hipSuccess) return err;
-    if (e0 && e1) {
-        if (hipEventRecord(e1, stream) != hipSuccess) return hipGetLastError();
+    if (err != hipSuccess) return give_back(err);
+    if (e0) {
+        if (hipEventRecord(e1, stream) != hipSuccess) return give_back(hipGetLastError());
         std::lock_guard<std::mutex> g(p.mu);
         p.pending.push_back(Pending{kernel, e0, e1});
     }
