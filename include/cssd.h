@@ -403,6 +403,9 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
  * 16 fill (the states and zeroed sums of an empty problem, one launch per plane).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).
+ * Keep the profiler off while a stream is being captured into a HIP graph: the
+ * event records would be captured along with the kernels, and the timings read
+ * for them would not describe any replay.
  */
 int cssd_profile_enable(int on);
 int cssd_profile_read(double *ms, int64_t *launches, int capacity);
