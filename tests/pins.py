@@ -660,6 +660,38 @@ def pin_born_invariances(lib):
     assert np.max(np.abs(base[:, 0] - v[:, 0])) < 1e-14
 
 
+
+def pin_born_rows_match_full(lib):
+    """The sampled-row form of Born attention returns, for each listed (b, i, h),
+    exactly the row the full evaluation of eq. 5 gives there (the phase-state
+    paper, section 5.5): each row's output depends only on that query and the
+    keys and values up to it, so selecting rows after or before the evaluation
+    must agree bit for bit.  Rows are random (b, i, h) triples with b, i and h
+    drawn from ranges of different lengths, so that a decode that swaps any two
+    of them reads the wrong row or leaves the problem; the first and last rows
+    and repeated rows are included, in an order unrelated to memory order.  Both
+    the complex and the (re, im) plane forms of the inputs are checked."""
+    rng = np.random.default_rng(2424)
+    Bsz, T, H, D = 3, 29, 5, 4
+    q, k, v = crandn(rng, Bsz, T, H, D), crandn(rng, Bsz, T, H, D), crandn(rng, Bsz, T, H, D)
+    tau = 0.5 + rng.random((Bsz, T, H))
+    full = oracle.born_attention(q, k, v, tau, lib=lib)
+    rows = np.stack([rng.integers(0, Bsz, 40), rng.integers(0, T, 40), rng.integers(0, H, 40)], 1)
+    rows = np.concatenate([[[0, 0, 0], [Bsz - 1, T - 1, H - 1], [Bsz - 1, 0, H - 1],
+                            [0, T - 1, 0]], rows, rows[:3]])
+    want = full[rows[:, 0], rows[:, 1], rows[:, 2]]
+    pl = lambda z: (z.real.copy(), z.imag.copy())
+    for args in ((q, k, v), (pl(q), pl(k), pl(v))):
+        try:
+            got = oracle.born_attention_rows(*args, tau, rows, lib=lib)
+        except RuntimeError as e:  # a decode that leaves the problem is a failure of the pin
+            raise AssertionError(f"born_attention_rows rejected valid rows: {e}")
+        assert got.shape == want.shape and np.array_equal(got, want), rel_err(got, want)
+    # without a temperature: tau = 1 on every row
+    full1 = oracle.born_attention(q, k, v, None, lib=lib)
+    got1 = oracle.born_attention_rows(q, k, v, None, rows, lib=lib)
+    assert np.array_equal(got1, full1[rows[:, 0], rows[:, 1], rows[:, 2]])
+
 # ---------------------------------------------------------------------------
 # empty sequences: a scan of no time steps
 # ---------------------------------------------------------------------------
@@ -692,7 +724,7 @@ def pin_empty_sequence(lib):
 ALL_PINS = [pin_bruteforce, pin_empty_sequence, pin_impulse, pin_constant_input, pin_fixed_point,
             pin_phase_unrolled, pin_phase_transport, pin_phase_golden_gain,
             pin_born_orthogonal_keys, pin_born_two_state_interference,
-            pin_born_density_matrix_form, pin_born_invariances,
+            pin_born_density_matrix_form, pin_born_invariances, pin_born_rows_match_full,
             pin_step_n_against_recurrence, pin_step_infinite_against_recurrence,
             pin_backward_finite_differences, pin_backward_without_initial_state,
             pin_step_constant_input, pin_decay_zero, pin_homogeneous, pin_linearity_and_skip,

@@ -98,6 +98,11 @@ MUTANTS = {
                                  "num[d] += sij * (v_re[qi + d] + v_im[qi + d] * I);")],
     "born_value_conjugated": [("num[d] += sij * (v_re[kj + d] + v_im[kj + d] * I);",
                                "num[d] += sij * (v_re[kj + d] - v_im[kj + d] * I);")],
+    "born_rows_time_and_head_swapped": [
+        ("const int64_t b = rows[3 * m], i = rows[3 * m + 1], h = rows[3 * m + 2];",
+         "const int64_t b = rows[3 * m], i = rows[3 * m + 2], h = rows[3 * m + 1];")],
+    "born_rows_output_not_strided": [("out_re + m * D,\n                 out_im + m * D);",
+                                      "out_re + m,\n                 out_im + m);")],
     "born_temperature_of_key": [("const double sij = mod * mod / ((double)D * t);",
                                  "const double sij = mod * mod / ((double)D * (tau ? tau[(b * T + j) * H + h] : 1.0));")],
 }
