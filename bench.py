@@ -1,6 +1,6 @@
 """Throughput of the complex chunkwise scan on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 
 One step = one cssd_forward over the Mamba-style layer workload (batch 8,
 T = 2048, 48 heads, head dim 64, state 64, chunk 64, fp32 complex planes): the
@@ -9,16 +9,20 @@ pass (one fused kernel) and the intra-chunk output with the combine, all in the
 library's HIP kernels.
 Inputs are seeded synthetic data already resident in HBM when timing starts.
 Each timed call first runs untimed for 200 ms (the GPU clocks settle), then W
-warm-up calls, then exactly K timed calls.  Prints ONE JSON line.  Per-kernel durations come from HIP events the library
-records around each launch on the launch stream during the timed region.
+warm-up calls, then exactly K timed calls.  Prints ONE JSON line.  Per-kernel
+durations come from HIP events the library records around each launch on the
+launch stream, during a second timed pass of the same K calls.
 
 Extra figures in the same line: the bf16-input variant of the same workload, the
 backward pass of the same workload (recomputing the forward's states, and on the
 states a forward call saved), the decode step at batch 256 x 48 heads x
 N128 x D64 over 512 pre-staged tokens, the constant-input calls at that shape,
 the per-coordinate phase-state scan at 256 x 1024 x 16 x 16, causal Born
-attention at 256 x 1024 x 16 heads x width 16, and (with --all)
-the long-sequence and phase-associative-memory workloads.  "traffic" figures are
+attention at 256 x 1024 x 16 heads x width 16, and the other forward
+workloads (the tiny 64-step one, the long sequence and the phase-associative
+memory), each with the oracle timed beside it on a bounded sample.  Step
+times are taken with the per-kernel profiler off; the per-kernel averages come
+from a second, profiled pass of the same K calls.  "traffic" figures are
 HBM bytes per launch from committed rocprofv3 counter runs (profiles/traffic.json),
 null once the kernel's sources have changed since.
 """
@@ -182,6 +186,10 @@ def settle(call, dev, seconds=SETTLE_S):
 
 
 def time_forward(inp, steps, warmup, dev):
+    """Times K forward calls twice after the settle and warm-up calls: first with
+    the per-kernel profiler off (the step time reported), then with it on (each
+    launch bracketed by two HIP events on its stream: the per-kernel averages).
+    Returns (ms per step, {kernel: avg ms per launch}, ms per step profiled)."""
     import torch
     import complex_valued_state_amd as cssd
     s = inp.shape
@@ -200,16 +208,92 @@ def time_forward(inp, steps, warmup, dev):
         run()
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    total_ms = e0.elapsed_time(e1)
     with cssd.profile() as prof:
         e0.record(stream)
         for _ in range(steps):
             run()
         e1.record(stream)
         torch.cuda.synchronize(dev)
-    total_ms = e0.elapsed_time(e1)
+    prof_ms = e0.elapsed_time(e1)
     kern = {k: prof.ms[k] / prof.launches[k] for k in prof.ms if prof.launches[k]}
     del args, ws
-    return total_ms / steps, kern
+    return total_ms / steps, kern, prof_ms / steps
+
+
+def forward_entry(inp, steps, warmup, dev, cpu_budget_s=None):
+    """One forward workload: tokens/s, ms per step (profiler off), the per-kernel
+    averages (profiled pass), the chunk-scan kernel's roofline object, the whole
+    forward's fractions and, with a budget, the oracle on the host beside it."""
+    sh = inp.shape
+    B, T, H, D, N, C = sh["B"], sh["T"], sh["H"], sh["D"], sh["N"], sh["C"]
+    dtype = "bf16" if inp.in_dtype == "bf16" else "f32"
+    ms, kern, ms_prof = time_forward(inp, steps, warmup, dev)
+    k2_ms = kern.get("k_chunk_scan")
+    k2_flops = chunk_scan_flops(B, T, H, D, N, C)
+    fwd_flops = k2_flops + chunk_state_flops(B, T, H, D, N, C)
+    sym = chunk_scan_symbol(N, D, C, dtype)
+    hbm = forward_hbm_bytes(B, T, H, D, N, in_bytes=2 if dtype == "bf16" else 4)
+    peak = PEAK_BF16_MFMA_TFLOPS if dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    k2_achieved = k2_flops / (k2_ms * 1e-3) / 1e12
+    e = {"tokens_per_s": round(B * T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+         "ms_per_step_profiled": round(ms_prof, 4),
+         "kernels_avg_ms": {k: round(v, 5) for k, v in kern.items()},
+         "roofline": {"bound": "mfma", "kernel": "k_chunk_scan", "symbol": sym,
+                      "achieved": round(k2_achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                      "frac": round(k2_achieved / peak, 4), "traffic": load_traffic(sym),
+                      "algorithmic_flops_per_launch": k2_flops, "avg_launch_ms": round(k2_ms, 5)},
+         "forward_mfma_frac": round(fwd_flops / (ms * 1e-3) / 1e12 / peak, 4),
+         "forward_hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+         "algorithmic_bytes": hbm}
+    ss_ms = kern.get("k_state_scan")
+    if ss_ms:
+        ss_flops = chunk_state_flops(B, T, H, D, N, C)
+        e["kernels_achieved"] = {"k_state_scan": {
+            "TFLOP/s": round(ss_flops / (ss_ms * 1e-3) / 1e12, 2),
+            "frac_peak": round(ss_flops / (ss_ms * 1e-3) / 1e12 / peak, 4),
+            "GB/s": round(state_scan_hbm_bytes(B, T, H, D, N, C,
+                                               in_bytes=2 if dtype == "bf16" else 4)
+                          / (ss_ms * 1e-3) / 1e9, 1)}}
+    cs_ms = kern.get("k_cumsum")
+    if cs_ms:
+        e.setdefault("kernels_achieved", {})["k_cumsum"] = {
+            "GB/s": round(cumsum_hbm_bytes(B, T, H, C) / (cs_ms * 1e-3) / 1e9, 1)}
+    if cpu_budget_s:
+        e["cpu_baseline"] = cpu_baseline(inp, budget_s=cpu_budget_s)
+    return e
+
+
+def timed_pair(call, steps, stream, dev, reset=None):
+    """`steps` calls timed with HIP events on `stream`, the library's per-kernel
+    profiler off; then the same number of calls again with it on (`reset`, if
+    given, runs untimed before each pass).  Returns (ms per call of the first
+    pass, the profile of the second)."""
+    import torch
+    import complex_valued_state_amd as cssd
+    if reset is not None:
+        reset()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    if reset is not None:
+        reset()
+        torch.cuda.synchronize(dev)
+    with cssd.profile() as prof:
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize(dev)
+    return ms, prof
 
 
 def time_constant_input(B, H, D, N, nsteps, reps, warmup, dev, seed=4):
@@ -282,15 +366,7 @@ def time_phase_scan(B, T, H, N, steps, warmup, dev, chunk=0, seed=5):
     settle(call, dev)
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize(dev)
-    with cssd.profile() as prof:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-    ms = e0.elapsed_time(e1) / steps
+    ms, prof = timed_pair(call, steps, stream, dev)
     kern = {k: v / steps for k, v in prof.ms.items() if prof.launches[k]}
     return ms, kern
 
@@ -314,15 +390,8 @@ def time_born(B, T, H, D, steps, warmup, dev, seed=6, bf16=False):
     settle(call, dev)
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize(dev)
-    with cssd.profile() as prof:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-    return e0.elapsed_time(e1) / steps, prof.ms["k_born"] / max(1, prof.launches["k_born"])
+    ms, prof = timed_pair(call, steps, stream, dev)
+    return ms, prof.ms["k_born"] / max(1, prof.launches["k_born"])
 
 
 def time_backward(inp, steps, warmup, dev, seed=9, saved=False):
@@ -357,16 +426,9 @@ def time_backward(inp, steps, warmup, dev, seed=9, saved=False):
     settle(run, dev)
     for _ in range(warmup):
         run()
-    torch.cuda.synchronize(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with cssd.profile() as prof:
-        e0.record(stream)
-        for _ in range(steps):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
+    ms, prof = timed_pair(run, steps, stream, dev)
     kern = {k: v / max(prof.launches[k], 1) for k, v in prof.ms.items() if prof.launches[k]}
-    return e0.elapsed_time(e1) / steps, kern
+    return ms, kern
 
 
 def time_decode(B, H, D, N, tokens, warmup, dev, seed=4):
@@ -394,31 +456,53 @@ def time_decode(B, H, D, N, tokens, warmup, dev, seed=4):
     settle(lambda: step(0), dev)
     for t in range(warmup):
         step(t % tokens)
-    h_re.zero_(); h_im.zero_()
     torch.cuda.synchronize(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with cssd.profile() as prof:
-        e0.record(stream)
-        for t in range(tokens):
-            step(t)
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-    ms = e0.elapsed_time(e1) / tokens
+    pos = [0]
+
+    def reset():  # each pass over the tokens starts from a zero state
+        h_re.zero_()
+        h_im.zero_()
+        pos[0] = 0
+
+    def next_token():
+        step(pos[0])
+        pos[0] += 1
+
+    ms, prof = timed_pair(next_token, tokens, stream, dev, reset=reset)
     kms = prof.ms["k_step"] / max(1, prof.launches["k_step"])
     return ms, kms
+
+
+def host_threads():
+    """Host threads the oracle may use: every core this process may run on,
+    capped by OMP_NUM_THREADS where the job sets it (the share of the machine's
+    cores the job is given)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return min(n, cap) if cap > 0 else n
 
 
 def cpu_baseline(inp, budget_s=15.0):
     """The fp64 oracle, untuned, on a bounded sample of the same workload: the
     first b_s batch rows (all heads, full length), b_s calibrated so the run
-    takes roughly `budget_s` seconds.  Returns tokens/s scaled to the sample."""
+    takes roughly `budget_s` seconds; the whole workload, repeated up to ten
+    times (median taken), when it fits the budget.  Returns tokens/s scaled to
+    the sample."""
     import numpy as np
     import oracle
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = host_threads()
     lib = oracle.load()
 
+    cache = {}
+
     def run(bs):
-        x, Bm, Cm, dt, A, Dk, h0 = inp.complex() if bs is None else _rows(inp, bs).complex()
+        if bs not in cache:  # the complex fp64 copies are made once per sample size
+            cache.clear()
+            cache[bs] = _rows(inp, bs).complex()
+        x, Bm, Cm, dt, A, Dk, h0 = cache[bs]
         t0 = time.perf_counter()
         oracle.forward(x, Bm, Cm, dt, A, Dk, h0, nthreads=threads, lib=lib)
         return time.perf_counter() - t0
@@ -432,6 +516,7 @@ def cpu_baseline(inp, budget_s=15.0):
     while bs == s["B"] and sum(times) < budget_s * 0.6 and len(times) < 10:
         times.append(run(bs))
     t = float(np.median(times))
+    cache.clear()
     # one thread on one (b, h) sequence, scaled to the H sequences a token spans
     one = _one_sequence(inp).complex()
     t_one = []
@@ -449,14 +534,15 @@ def cpu_baseline(inp, budget_s=15.0):
                     break
     except OSError:
         pass
-    return {"value": bs * s["T"] / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model,
+    return {"value": round(bs * s["T"] / t, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"{bs} of {s['B']} batch rows (all {s['H']} heads, full T={s['T']}) of the "
                       f"same workload, median of {len(times)} run(s); fp64 sequential recurrence, "
-                      f"OpenMP over (batch, head); {t:.2f} s wall per run",
-            "single_thread": {"value": s["T"] / (s["H"] * t1s), "unit": "tokens/s", "cores": 1,
+                      f"OpenMP over (batch, head) on {threads} threads; {t:.3f} s wall per run",
+            "single_thread": {"value": round(s["T"] / (s["H"] * t1s), 1), "unit": "tokens/s",
+                              "cores": 1,
                               "sample": f"one (b, h) sequence of T={s['T']} on one thread, median "
-                                        f"of 3 runs ({t1s:.3f} s), scaled by the {s['H']} heads "
+                                        f"of 3 runs ({t1s:.4f} s), scaled by the {s['H']} heads "
                                         f"a token spans"}}
 
 
@@ -485,7 +571,6 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--all", action="store_true", help="also time the long and PAM workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
     args = ap.parse_args()
@@ -506,59 +591,46 @@ def main():
     progress("generating the B8 T2048 H48 D64 N64 C64 inputs")
     inp = wl.config1("f32")
     progress("timing the fp32 forward")
-    ms, kern = time_forward(inp, args.steps, args.warmup, dev)
+    head = forward_entry(inp, args.steps, args.warmup, dev)
+    ms = head["ms_per_step"]
     progress(f"fp32 forward {ms:.4f} ms/step")
     tokens = B * T
-    value = tokens / (ms * 1e-3)
-    k2_ms = kern.get("k_chunk_scan")
-    k2_flops = chunk_scan_flops(B, T, H, D, N, C)
-    achieved = k2_flops / (k2_ms * 1e-3) / 1e12
-    traffic = load_traffic(chunk_scan_symbol(N, D, C, "f32"))
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "complex chunkwise scan forward, Mamba-style layer: batch 8, T 2048, "
                                "48 heads, head dim 64, state 64, chunk 64, fp32 complex planes",
                    "batch": B, "seqlen": T, "heads": H, "headdim": D, "dstate": N, "chunk": C,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "k_chunk_scan",
-                     "symbol": chunk_scan_symbol(N, D, C, "f32"), "achieved": round(achieved, 2),
-                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
-                     "traffic": traffic, "algorithmic_flops_per_launch": k2_flops,
-                     "avg_launch_ms": round(k2_ms, 5)},
-        "kernels_avg_ms": {k: round(v, 5) for k, v in kern.items()},
+        "roofline": head["roofline"],
+        "ms_per_step_profiled": head["ms_per_step_profiled"],
+        "kernels_avg_ms": head["kernels_avg_ms"],
+        "kernels_achieved": head["kernels_achieved"],
+        "forward_mfma_frac": head["forward_mfma_frac"],
+        "forward_hbm_frac": head["forward_hbm_frac"],
     }
-    # the other two forward kernels, by their algorithmic work
-    ss_ms, cs_ms = kern.get("k_state_scan"), kern.get("k_cumsum")
-    ss_flops = chunk_state_flops(B, T, H, D, N, C)
-    out["kernels_achieved"] = {
-        "k_state_scan": {"TFLOP/s": round(ss_flops / (ss_ms * 1e-3) / 1e12, 2),
-                         "frac_fp32_mfma": round(ss_flops / (ss_ms * 1e-3) / 1e12
-                                                 / PEAK_FP32_MFMA_TFLOPS, 4),
-                         "GB/s": round(state_scan_hbm_bytes(B, T, H, D, N, C) / (ss_ms * 1e-3)
-                                       / 1e9, 1)},
-        "k_cumsum": {"GB/s": round(cumsum_hbm_bytes(B, T, H, C) / (cs_ms * 1e-3) / 1e9, 1)},
-    }
-    fwd_flops = k2_flops + chunk_state_flops(B, T, H, D, N, C)
-    out["forward_mfma_frac"] = round(fwd_flops / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)
-    out["forward_hbm_frac"] = round(forward_hbm_bytes(B, T, H, D, N) / (ms * 1e-3) / 1e9
-                                    / PEAK_HBM_GBS, 4)
     extra = {}
     if not args.no_extras:
         progress("timing the bf16-input forward")
         inp16 = wl.config1("bf16")
-        ms16, kern16 = time_forward(inp16, args.steps, args.warmup, dev)
-        hbm16 = forward_hbm_bytes(B, T, H, D, N, in_bytes=2)
-        extra["forward_B8_T2048_H48_D64_N64_C64_bf16_inputs"] = {
-            "tokens_per_s": round(tokens / (ms16 * 1e-3), 1), "ms_per_step": round(ms16, 4),
-            "hbm_roofline_frac": round(hbm16 / (ms16 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            # the products run on the bf16 matrix cores (the bound that binds is HBM)
-            "bf16_mfma_frac": round(fwd_flops / (ms16 * 1e-3) / 1e12 / PEAK_BF16_MFMA_TFLOPS, 4),
-            "kernels_avg_ms": {k: round(v, 5) for k, v in kern16.items()}}
+        e16 = forward_entry(inp16, args.steps, args.warmup, dev)
+        # HBM binds this variant: its fraction of the HBM roofline is the headline one
+        e16["hbm_roofline_frac"] = e16.pop("forward_hbm_frac")
+        e16["bf16_mfma_frac"] = e16.pop("forward_mfma_frac")
+        extra["forward_B8_T2048_H48_D64_N64_C64_bf16_inputs"] = e16
         del inp16
+        # the other forward workloads, each with the oracle timed beside it
+        for name, mk, budget in (
+                ("forward_tiny_B1_T64_H2_D16_N16_C16", wl.config0, 2.0),
+                ("forward_long_B1_T16384_H48_D64_N128_C128", wl.config2, 6.0),
+                ("forward_pam_B16_T1024_H12_D64_N128_C64", lambda: wl.config3("re"), 4.0)):
+            progress(f"timing {name}")
+            i2 = mk()
+            extra[name] = forward_entry(i2, args.steps, args.warmup, dev,
+                                        cpu_budget_s=None if args.no_cpu_baseline else budget)
+            del i2
         d4 = wl.CONFIG_SHAPES[4]
         progress("timing the backward pass")
         bms, bk = time_backward(inp, max(3, args.steps // 2), 2, dev)
@@ -637,20 +709,6 @@ def main():
                          "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(bfl / (b16kms * 1e-3) / 1e12 / PEAK_BF16_MFMA_TFLOPS, 4),
                          "algorithmic_flops_per_launch": bfl, "avg_launch_ms": round(b16kms, 5)}}
-        if args.all:
-            for name, mk in (("forward_long_B1_T16384_H48_D64_N128_C128", wl.config2),
-                             ("forward_pam_B16_T1024_H12_D64_N128_C64", lambda: wl.config3("re"))):
-                progress(f"timing {name}")
-                i2 = mk()
-                sh = i2.shape
-                m2, k2 = time_forward(i2, args.steps, args.warmup, dev)
-                fl = (chunk_scan_flops(sh["B"], sh["T"], sh["H"], sh["D"], sh["N"], sh["C"])
-                      + chunk_state_flops(sh["B"], sh["T"], sh["H"], sh["D"], sh["N"], sh["C"]))
-                extra[name] = {"tokens_per_s": round(sh["B"] * sh["T"] / (m2 * 1e-3), 1),
-                               "ms_per_step": round(m2, 4),
-                               "mfma_frac": round(fl / (m2 * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
-                               "kernels_avg_ms": {k: round(v, 5) for k, v in k2.items()}}
-                del i2
     out["extra"] = extra
     if not args.no_cpu_baseline:
         progress("timing the fp64 oracle on the host cores")

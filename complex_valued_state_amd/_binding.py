@@ -9,7 +9,9 @@ built, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 import threading
 from typing import Optional, Sequence
@@ -153,6 +155,21 @@ def _check(t, name, shape: Sequence[int], dtypes, device):
     return t.data_ptr()
 
 
+def _on_stream(fn):
+    """Run a binding call with `stream` (when given) as torch's current stream, so
+    that the outputs and workspace the binding allocates come from that stream's
+    pool of the caching allocator.  A block freed after the call is then reused
+    only by later work on the same stream, which the kernels already enqueued
+    there precede; allocated on another stream, it could be handed to new work
+    there while the kernels still use it."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kwargs):
+        ctx = contextlib.nullcontext() if stream is None else _torch().cuda.stream(stream)
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return call
+
+
 def _stream_ptr(stream, device):
     torch = _torch()
     if stream is None:
@@ -160,6 +177,7 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(int(stream.cuda_stream))
 
 
+@_on_stream
 def cssd_forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None, h0=None, *,
                  chunk: int, return_state: bool = True, out=None, workspace=None, stream=None):
     """Chunkwise complex scan over a whole sequence (see include/cssd.h).
@@ -170,6 +188,12 @@ def cssd_forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None,
     out: optional (y_re, y_im[, hT_re, hT_im]) preallocated outputs.
     Returns (y_re, y_im, hT_re, hT_im) (the last two None if not return_state).
     """
+    return _forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, chunk,
+                    return_state, out, workspace, stream)
+
+
+def _forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, chunk, return_state,
+             out, workspace, stream):
     torch = _torch()
     lib = load_library()
     dev = x_re.device
@@ -210,22 +234,23 @@ def cssd_forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None,
     p["y_im"] = _check(y_im, "y_im", (Bsz, T, H, D), f32, dev)
     p["hT_re"] = None if hT_re is None else _check(hT_re, "hT_re", (Bsz, H, N, D), f32, dev)
     p["hT_im"] = None if hT_im is None else _check(hT_im, "hT_im", (Bsz, H, N, D), f32, dev)
+    args = (Bsz, T, H, D, N, int(chunk), code,
+            p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
+            p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"],
+            p["y_re"], p["y_im"], p["hT_re"], p["hT_im"])
     need = cssd_forward_workspace_size(Bsz, T, H, D, N, chunk)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the same device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.cssd_forward(Bsz, T, H, D, N, int(chunk), code,
-                          p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
-                          p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"],
-                          p["y_re"], p["y_im"], p["hT_re"], p["hT_im"],
-                          workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
+    st = lib.cssd_forward(*args, workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
     if st != CSSD_OK:
         raise CSSDError(st, "cssd_forward")
     return y_re, y_im, hT_re, hT_im
 
 
+@_on_stream
 def cssd_backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, dy, dhT=None,
                   *, chunk: int, want_dh0: bool = True, workspace=None, stream=None):
     """Gradients of cssd_forward (see include/cssd.h): planar (dL/dRe, dL/dIm) pairs.
@@ -240,6 +265,7 @@ def cssd_backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0,
                      chunk, want_dh0, workspace, stream, None)
 
 
+@_on_stream
 def cssd_backward_saved(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, hT, dy,
                         dhT=None, *, chunk: int, workspace, want_dh0: bool = True, stream=None):
     """cssd_backward on the states a cssd_forward call left in `workspace` (a uint8
@@ -330,6 +356,7 @@ def _step_ptrs(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h, Bsz
     return p, (y_re, y_im), dev
 
 
+@_on_stream
 def cssd_step(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h_im, *,
               out=None, stream=None):
     """One decode token for all (batch, head); the state (h_re, h_im) is updated
@@ -347,6 +374,7 @@ def cssd_step(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h
     return y
 
 
+@_on_stream
 def cssd_step_n(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re, h_im, nsteps,
                 *, out=None, stream=None):
     """nsteps decode steps that all receive the same input, applied at once; the
@@ -364,6 +392,7 @@ def cssd_step_n(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h_re,
     return y
 
 
+@_on_stream
 def cssd_step_infinite(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, *,
                        out=None, stream=None):
     """The stationary output of an endless constant input (no state).  Arguments
@@ -381,6 +410,7 @@ def cssd_step_infinite(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip
     return y
 
 
+@_on_stream
 def cssd_phase_scan(phi, u, b_re, b_im, psi0=None, *, chunk: int = 0, return_state: bool = True,
                     out=None, workspace=None, stream=None):
     """Per-coordinate scan psi_t = sigmoid(u_t) (1 + i phi_t) / (1 - i phi_t) psi_{t-1} + b_t
@@ -432,6 +462,7 @@ def cssd_phase_scan(phi, u, b_re, b_im, psi0=None, *, chunk: int = 0, return_sta
     return psi_re, psi_im, psiT_re, psiT_im
 
 
+@_on_stream
 def cssd_born_attention(q_re, q_im, k_re, k_im, v_re, v_im, tau=None, *, out=None, stream=None):
     """Causal Born attention (see include/cssd.h): psi_i = sum_{j<=i} s_ij v_j /
     sum_{j<=i} s_ij with s_ij = |<q_i|k_j>|^2 / (D tau_i).

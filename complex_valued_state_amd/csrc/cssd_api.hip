@@ -58,12 +58,19 @@ template <typename F>
 hipError_t timed(int kernel, hipStream_t stream, F&& launch) {
     Profiler& p = prof();
     hipEvent_t e0 = nullptr, e1 = nullptr;
+    bool on;
     {
         std::lock_guard<std::mutex> g(p.mu);
-        if (p.on) {
-            e0 = take_event(p);
-            e1 = take_event(p);
-        }
+        on = p.on;
+    }
+    // a stream being captured into a graph gets no event brackets: they would
+    // be captured with the kernels and never complete outside a replay
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (on && hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+        cap == hipStreamCaptureStatusNone) {
+        std::lock_guard<std::mutex> g(p.mu);
+        e0 = take_event(p);
+        e1 = take_event(p);
     }
     // on every early return the events go back to the pool, so none is leaked
     auto give_back = [&](hipError_t err) {
@@ -816,21 +823,32 @@ int cssd_profile_enable(int on) {
 
 int cssd_profile_read(double* ms, int64_t* launches, int capacity) {
     Profiler& p = prof();
-    std::lock_guard<std::mutex> g(p.mu);
-    int status = CSSD_OK;
-    for (const Pending& q : p.pending) {
-        float t = 0.f;
-        if (hipEventSynchronize(q.stop) != hipSuccess ||
-            hipEventElapsedTime(&t, q.start, q.stop) != hipSuccess) {
-            status = CSSD_ERR_HIP;
-        } else {
-            p.ms[q.kernel] += t;
-            p.launches[q.kernel] += 1;
-        }
-        p.pool.push_back(q.start);
-        p.pool.push_back(q.stop);
+    // take the pending brackets out under the lock, then wait for them without
+    // it, so that other threads' launches are not held up meanwhile
+    std::vector<Pending> mine;
+    {
+        std::lock_guard<std::mutex> g(p.mu);
+        mine.swap(p.pending);
     }
-    p.pending.clear();
+    int status = CSSD_OK;
+    std::vector<float> took(mine.size(), -1.f);
+    for (size_t j = 0; j < mine.size(); ++j) {
+        float t = 0.f;
+        if (hipEventSynchronize(mine[j].stop) != hipSuccess ||
+            hipEventElapsedTime(&t, mine[j].start, mine[j].stop) != hipSuccess)
+            status = CSSD_ERR_HIP;
+        else
+            took[j] = t;
+    }
+    std::lock_guard<std::mutex> g(p.mu);
+    for (size_t j = 0; j < mine.size(); ++j) {
+        if (took[j] >= 0.f) {
+            p.ms[mine[j].kernel] += took[j];
+            p.launches[mine[j].kernel] += 1;
+        }
+        p.pool.push_back(mine[j].start);
+        p.pool.push_back(mine[j].stop);
+    }
     for (int k = 0; k < cssd::K_COUNT && k < capacity; ++k) {
         if (ms) ms[k] = p.ms[k];
         if (launches) launches[k] = p.launches[k];

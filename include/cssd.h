@@ -403,9 +403,12 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
  * 16 fill (the states and zeroed sums of an empty problem, one launch per plane).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).
- * Keep the profiler off while a stream is being captured into a HIP graph: the
- * event records would be captured along with the kernels, and the timings read
- * for them would not describe any replay.
+ * Launches on a stream that is being captured into a HIP graph are not
+ * bracketed (the events would be captured with the kernels and would time no
+ * replay): they are neither timed nor counted.  cssd_profile_read waits for the
+ * events without holding the library's lock, so other threads keep launching
+ * meanwhile; launches bracketed after it took the pending list are left for
+ * the next read.
  */
 int cssd_profile_enable(int on);
 int cssd_profile_read(double *ms, int64_t *launches, int capacity);

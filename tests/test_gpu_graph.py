@@ -112,3 +112,52 @@ def test_decode_step_graph_replays():
         torch.cuda.synchronize()
         for k, (got, want) in enumerate(zip((*h, *y), ref)):
             assert torch.equal(got, want), (rep, k)
+
+
+def test_profiler_on_during_capture_counts_eager_launches_only():
+    """With the per-kernel profiler on, a forward captured into a graph gets no
+    event brackets: the replays are neither timed nor counted, the captured graph
+    replays bit-identically to an eager call, and the read afterwards succeeds
+    and counts exactly the eager calls made while profiling."""
+    import torch
+    import complex_valued_state_amd as cssd
+    Bsz, T, H, D, N, C = 2, 200, 3, 64, 64, 64
+    log("graph: forward captured with the profiler on")
+    inp = wl.random_forward(85, Bsz, T, H, D, N, C, with_h0=True)
+    d = dev_inputs(inp)
+    ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
+           d["A_im"], d["Dskip"], d["h0"])
+    ws = torch.empty(cssd.cssd_forward_workspace_size(Bsz, T, H, D, N, C), dtype=torch.uint8,
+                     device="cuda:0")
+    out = [torch.empty((Bsz, T, H, D), device="cuda:0") for _ in range(2)] + \
+          [torch.empty((Bsz, H, N, D), device="cuda:0") for _ in range(2)]
+    call = lambda: cssd.cssd_forward(*ins, chunk=C, out=tuple(out), workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with cssd.profile() as prof:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        for rep in range(REPLAYS):
+            for t in out:
+                t.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for k, (got, want) in enumerate(zip(out, ref)):
+                assert torch.equal(got, want), (rep, k)
+        call()
+        call()
+        torch.cuda.synchronize()
+    log(f"  launches counted: {prof.launches['k_cumsum']}, {prof.launches['k_state_scan']}, "
+        f"{prof.launches['k_chunk_scan']}")
+    for k in ("k_cumsum", "k_state_scan", "k_chunk_scan"):
+        assert prof.launches[k] == 2, (k, prof.launches[k])
+        assert prof.ms[k] > 0.0

@@ -108,6 +108,61 @@ def test_step_full_decode_shape_sampled():
         assert rel_err(h[b, hh], hr[0, 0]) <= TOL, (b, hh)
 
 
+def test_step_decode_workload_as_written():
+    """The decode workload exactly as specified: batch 256 x 48 heads, N128 D64,
+    512 consecutive tokens from a zero state, token s drawn from the streams
+    SeedSequence([4, s, k]) (generated on the host in batches while the GPU
+    steps).  Every step's y and the final state of six sampled (b, h), the last
+    one (255, 47) included, are compared with the oracle run over the same 512
+    tokens ("Complex-Valued State Spaces", the naive scan, one token at a time)."""
+    import torch
+    import complex_valued_state_amd as cssd
+    from concurrent.futures import ThreadPoolExecutor
+    s4 = wl.CONFIG_SHAPES[4]
+    B, H, D, N, S = s4["B"], s4["H"], s4["D"], s4["N"], s4["steps"]
+    A_re, A_im, Dk = wl.decode_params(4, H)
+    a_re, a_im, dk = _dev(A_re), _dev(A_im), _dev(Dk)
+    pairs = [(0, 0), (17, 5), (130, 47), (64, 33), (200, 11), (255, 47)]
+    h_re = torch.zeros((B, H, N, D), dtype=torch.float32, device="cuda:0")
+    h_im = torch.zeros_like(h_re)
+    y_re = torch.empty((S, B, H, D), dtype=torch.float32, device="cuda:0")
+    y_im = torch.empty_like(y_re)
+    fields = ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im", "dt")
+    kept = {f: [] for f in fields}  # the sampled sequences' inputs, token by token
+    batch = 32
+    log(f"  decode workload B{B} H{H} N{N} D{D}, {S} tokens")
+    with ThreadPoolExecutor(16) as ex:
+        nxt = ex.map(lambda t: wl.decode_step(4, t, B, H, D, N), range(0, min(batch, S)))
+        for t0 in range(0, S, batch):
+            toks = list(nxt)
+            if t0 + batch < S:
+                nxt = ex.map(lambda t: wl.decode_step(4, t, B, H, D, N),
+                             range(t0 + batch, min(t0 + 2 * batch, S)))
+            for j, tok in enumerate(toks):
+                d = {f: _dev(getattr(tok, f)) for f in fields}
+                cssd.cssd_step(d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"],
+                               d["dt"], a_re, a_im, dk, h_re, h_im,
+                               out=(y_re[t0 + j], y_im[t0 + j]))
+                for f in fields:
+                    a = getattr(tok, f)
+                    kept[f].append(np.stack([a[b, hh] for b, hh in pairs]))
+            torch.cuda.synchronize()
+    import oracle
+    c = lambda r, i: r.double().cpu().numpy() + 1j * i.double().cpu().numpy()
+    worst_y = worst_h = 0.0
+    for m, (b, hh) in enumerate(pairs):
+        sub = wl.StepInputs(*[np.ascontiguousarray(np.stack(kept[f])[:, m][:, None, None])
+                              for f in fields])
+        seq = _as_sequence(sub, A_re[hh:hh + 1], A_im[hh:hh + 1], Dk[hh:hh + 1])
+        x, Bm, Cm, dt, A, Dd, _ = seq.complex()
+        yr, hr = oracle.forward(x, Bm, Cm, dt, A, Dd, None)
+        ey = rel_err(c(y_re[:, b, hh], y_im[:, b, hh]), yr[0, :, 0])
+        eh = rel_err(c(h_re[b, hh], h_im[b, hh]), hr[0, 0])
+        worst_y, worst_h = max(worst_y, ey), max(worst_h, eh)
+        assert ey <= TOL and eh <= TOL, (b, hh, ey, eh)
+    log(f"    rel err over {S} steps: y={worst_y:.3e} h={worst_h:.3e}")
+
+
 def test_step_constant_input_closed_form():
     """One draw of (x, B, C, dt) held for n = 4096 tokens at the full decode
     shape, from a zero state: y_n = (1 - a^n)/(1 - a) (C . B) x + D x, and at

@@ -91,3 +91,40 @@ def test_threads_on_separate_streams_match_serial_calls():
     assert prof.launches["k_chunk_scan"] == calls
     assert prof.launches["k_state_scan"] == calls
     assert all(prof.ms[k] > 0.0 for k in ("k_cumsum", "k_chunk_scan", "k_state_scan"))
+
+
+def test_side_stream_call_without_workspace():
+    """A call given a stream other than torch's current one, with no workspace or
+    outputs passed: the binding allocates them from that stream's pool, so the
+    blocks it frees on return are not handed to new work on the current stream
+    while the kernels still run.  The current stream then allocates and fills
+    tensors of the same sizes at once; the results must equal those of the same
+    call made alone on the current stream, bit for bit, and the oracle within
+    2e-4."""
+    import torch
+    import complex_valued_state_amd as cssd
+    inp = wl.random_forward(305, 4, 1024, 8, 64, 64, 64, with_h0=True, name="side_stream")
+    d = dev_inputs(inp)
+    ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
+           d["A_im"], d["Dskip"], d["h0"])
+    ref = cssd.cssd_forward(*ins, chunk=inp.chunk)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in ref]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ws_bytes = cssd.cssd_forward_workspace_size(4, 1024, 8, 64, 64, 64)
+    log("  forward on a side stream, binding-owned workspace and outputs")
+    for rep in range(4):
+        got = cssd.cssd_forward(*ins, chunk=inp.chunk, stream=side)
+        # new work on the current stream, sized like the blocks the call just freed
+        junk = [torch.full((ws_bytes // 4,), float("nan"), device="cuda:0") for _ in range(2)]
+        junk += [torch.full(tuple(t.shape), float("nan"), device="cuda:0") for t in ref]
+        side.synchronize()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), (rep, k)
+        del junk, got
+    to = lambda r, im: r.double().cpu().numpy() + 1j * im.double().cpu().numpy()
+    yr, hr = oracle_forward(inp)
+    assert rel_err(to(ref[0], ref[1]), yr) <= TOL_F32
+    assert rel_err(to(ref[2], ref[3]), hr) <= TOL_F32
