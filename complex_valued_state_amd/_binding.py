@@ -58,6 +58,9 @@ def load_library(path: Optional[str] = None):
         lib.cssd_forward.restype = ctypes.c_int
         lib.cssd_forward.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 \
             + [_vp] * 4 + [_vp, _sz, _vp]
+        lib.cssd_forward_noalloc.restype = ctypes.c_int
+        lib.cssd_forward_noalloc.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 \
+            + [_vp] * 2 + [_vp] * 4 + [_vp]
         lib.cssd_backward_workspace_size.restype = ctypes.c_int
         lib.cssd_backward_workspace_size.argtypes = [_i64] * 6 + [ctypes.POINTER(_sz)]
         lib.cssd_backward.restype = ctypes.c_int
@@ -189,11 +192,28 @@ def cssd_forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None,
     Returns (y_re, y_im, hT_re, hT_im) (the last two None if not return_state).
     """
     return _forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, chunk,
-                    return_state, out, workspace, stream)
+                    return_state, out, workspace, stream, noalloc=False)
+
+
+@_on_stream
+def cssd_forward_noalloc(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip=None,
+                         h0=None, *, chunk: int, return_state: bool = True, out=None,
+                         stream=None):
+    """cssd_forward with its workspace in the library's fixed device array (see
+    include/cssd.h): the library allocates nothing.  Arguments and result as
+    cssd_forward, without a workspace; pass `out` as well for a call in which
+    nothing at all is allocated.  Problems whose workspace exceeds
+    CSSD_NOALLOC_SCRATCH_BYTES raise CSSDError (CSSD_ERR_TOO_LARGE)."""
+    return _forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, chunk,
+                    return_state, out, None, stream, noalloc=True)
+
+
+CSSD_NOALLOC_SCRATCH_BYTES = 64 << 20
+CSSD_ERR_TOO_LARGE = 5
 
 
 def _forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, chunk, return_state,
-             out, workspace, stream):
+             out, workspace, stream, noalloc):
     torch = _torch()
     lib = load_library()
     dev = x_re.device
@@ -238,6 +258,11 @@ def _forward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, chun
             p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
             p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"],
             p["y_re"], p["y_im"], p["hT_re"], p["hT_im"])
+    if noalloc:
+        st = lib.cssd_forward_noalloc(*args, _stream_ptr(stream, dev))
+        if st != CSSD_OK:
+            raise CSSDError(st, "cssd_forward_noalloc")
+        return y_re, y_im, hT_re, hT_im
     need = cssd_forward_workspace_size(Bsz, T, H, D, N, chunk)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

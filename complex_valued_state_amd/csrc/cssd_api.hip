@@ -283,6 +283,9 @@ const char* cssd_status_string(int status) {
         case CSSD_ERR_UNSUPPORTED: return "CSSD_ERR_UNSUPPORTED: sizes outside the supported set";
         case CSSD_ERR_WORKSPACE: return "CSSD_ERR_WORKSPACE: workspace missing, too small or misaligned";
         case CSSD_ERR_HIP: return "CSSD_ERR_HIP: a HIP launch or runtime call failed";
+        case CSSD_ERR_TOO_LARGE:
+            return "CSSD_ERR_TOO_LARGE: the problem's workspace exceeds the fixed device array "
+                   "of cssd_forward_noalloc";
         default: return "unknown cssd status";
     }
 }

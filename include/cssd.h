@@ -69,7 +69,8 @@ typedef enum cssd_status {
     CSSD_ERR_INVALID_ARG = 1, /* null required pointer, negative size, misalignment, aliasing */
     CSSD_ERR_UNSUPPORTED = 2, /* sizes outside the supported set */
     CSSD_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned */
-    CSSD_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+    CSSD_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
+    CSSD_ERR_TOO_LARGE = 5    /* cssd_forward_noalloc: the workspace would exceed its fixed array */
 } cssd_status;
 
 typedef enum cssd_dtype {
@@ -154,6 +155,35 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                  float *y_re, float *y_im,
                  float *hT_re, float *hT_im,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * cssd_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result and errors as cssd_forward, minus the workspace: it runs in
+ * a fixed device array of CSSD_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library, one per GPU, held from the first call on that GPU until the process
+ * ends.  The call allocates nothing itself (its first call on a GPU looks the
+ * array's address up once); the caller still owns every input and output.
+ * A problem whose cssd_forward_workspace_size exceeds the array returns
+ * CSSD_ERR_TOO_LARGE before anything is enqueued (at D = N = chunk = 64 the
+ * array holds about 1,900 chunks, batch * nheads * ceil(seqlen / chunk)).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from several host threads) race on it and
+ * must be ordered by the caller; calls on one stream are ordered already.  The
+ * array needs no clearing between calls (every region is written before it is
+ * read); it holds the last call's workspace contents afterwards.
+ */
+#define CSSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+int cssd_forward_noalloc(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                         int64_t dstate, int64_t chunk, int32_t in_dtype,
+                         const void *x_re, const void *x_im,
+                         const void *B_re, const void *B_im,
+                         const void *C_re, const void *C_im,
+                         const float *dt, const float *A_re, const float *A_im,
+                         const float *Dskip,
+                         const float *h0_re, const float *h0_im,
+                         float *y_re, float *y_im,
+                         float *hT_re, float *hT_im, void *stream);
 
 /*
  * One recurrent decode step for every (batch, head), state updated in place
