@@ -60,7 +60,8 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC,
               "k_phase_summary": ("k_phase_scan.hip",), "k_phase_carry": ("k_phase_scan.hip",),
               "k_phase_out": ("k_phase_scan.hip",), "k_born": ("k_born.hip",),
               "k_born_bf16": ("k_born.hip",), "k_state_scan": ("k_state_scan.hip",),
-              "k_state_scan_lds": ("k_state_scan.hip",), "k_state_scan_mm": ("k_state_scan.hip",)}
+              "k_state_scan_lds": ("k_state_scan.hip",), "k_state_scan_mm": ("k_state_scan.hip",),
+              "k_scan_fused_bf16": ("k_scan_fused_bf16.hip",)}
 
 
 # ---------------------------------------------------------------------------
@@ -99,6 +100,13 @@ def forward_hbm_bytes(B, T, H, D, N, in_bytes=4):
     """Read x, B, C, dt once; write y and the final state once."""
     return (B * T * H * (D + 2 * N) * 2 * in_bytes + B * T * H * 4
             + B * T * H * D * 2 * 4 + B * H * N * D * 2 * 4)
+
+
+def scan_fused_hbm_bytes(B, T, H, D, N, in_bytes=2):
+    """The one-kernel forward after the cumsum: read x, B, C once, write y and the
+    final state once (dt is read by the cumsum kernel)."""
+    return (B * T * H * (D + 2 * N) * 2 * in_bytes + B * T * H * D * 2 * 4
+            + B * H * N * D * 2 * 4)
 
 
 def decode_hbm_bytes(B, H, D, N):
@@ -234,20 +242,35 @@ def forward_entry(inp, steps, warmup, dev, cpu_budget_s=None):
     B, T, H, D, N, C = sh["B"], sh["T"], sh["H"], sh["D"], sh["N"], sh["C"]
     dtype = "bf16" if inp.in_dtype == "bf16" else "f32"
     ms, kern, ms_prof = time_forward(inp, steps, warmup, dev)
-    k2_ms = kern.get("k_chunk_scan")
     k2_flops = chunk_scan_flops(B, T, H, D, N, C)
     fwd_flops = k2_flops + chunk_state_flops(B, T, H, D, N, C)
-    sym = chunk_scan_symbol(N, D, C, dtype)
-    hbm = forward_hbm_bytes(B, T, H, D, N, in_bytes=2 if dtype == "bf16" else 4)
+    in_bytes = 2 if dtype == "bf16" else 4
+    hbm = forward_hbm_bytes(B, T, H, D, N, in_bytes=in_bytes)
     peak = PEAK_BF16_MFMA_TFLOPS if dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    k2_achieved = k2_flops / (k2_ms * 1e-3) / 1e12
+    if "k_scan_fused" in kern:
+        # one kernel does the chunk states, the chunk-to-chunk pass and the output:
+        # HBM binds it; its algorithmic bytes are the forward's without dt
+        f_ms = kern["k_scan_fused"]
+        f_bytes = scan_fused_hbm_bytes(B, T, H, D, N, in_bytes)
+        f_gbs = f_bytes / (f_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_scan_fused", "symbol": "k_scan_fused_bf16",
+                "achieved": round(f_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(f_gbs / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic("k_scan_fused_bf16"),
+                "algorithmic_bytes_per_launch": f_bytes, "avg_launch_ms": round(f_ms, 5),
+                "mfma_frac": round(fwd_flops / (f_ms * 1e-3) / 1e12 / peak, 4)}
+    else:
+        k2_ms = kern.get("k_chunk_scan")
+        sym = chunk_scan_symbol(N, D, C, dtype)
+        k2_achieved = k2_flops / (k2_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "k_chunk_scan", "symbol": sym,
+                "achieved": round(k2_achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(k2_achieved / peak, 4), "traffic": load_traffic(sym),
+                "algorithmic_flops_per_launch": k2_flops, "avg_launch_ms": round(k2_ms, 5)}
     e = {"tokens_per_s": round(B * T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
          "ms_per_step_profiled": round(ms_prof, 4),
          "kernels_avg_ms": {k: round(v, 5) for k, v in kern.items()},
-         "roofline": {"bound": "mfma", "kernel": "k_chunk_scan", "symbol": sym,
-                      "achieved": round(k2_achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                      "frac": round(k2_achieved / peak, 4), "traffic": load_traffic(sym),
-                      "algorithmic_flops_per_launch": k2_flops, "avg_launch_ms": round(k2_ms, 5)},
+         "roofline": roof,
          "forward_mfma_frac": round(fwd_flops / (ms * 1e-3) / 1e12 / peak, 4),
          "forward_hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
          "algorithmic_bytes": hbm}
@@ -566,6 +589,34 @@ def _rows(inp, bs):
                             c(inp.h0_re), c(inp.h0_im), inp.in_dtype, inp.name)
 
 
+# the forward workloads --only can time alone: name -> (generator function, argument)
+ONLY = {"forward_f32": ("config1", "f32"), "forward_bf16": ("config1", "bf16"),
+        "forward_tiny": ("config0", None), "forward_long": ("config2", None),
+        "forward_pam": ("config3", "re")}
+
+
+def only_inputs(name):
+    import cssd_workloads as wl
+    fn, arg = ONLY[name]
+    return getattr(wl, fn)() if arg is None else getattr(wl, fn)(arg)
+
+
+def copy_calibration(dev, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, for scaling HBM byte counters:
+    each copy reads exactly `nbytes` and writes exactly `nbytes` (the buffers are
+    four times larger than the on-package caches), so what FETCH_SIZE and
+    WRITE_SIZE report for it gives the factor between the counters' units and
+    bytes on this machine."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copied_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -573,6 +624,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
+    ap.add_argument("--only", choices=sorted(ONLY), default=None,
+                    help="time one forward workload alone and print its figures (for "
+                         "profiler runs); not the benchmark line")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy a 1 GiB buffer three times (the reference kernel that scales "
+                         "the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -583,8 +640,16 @@ def main():
     import complex_valued_state_amd as cssd
     import cssd_workloads as wl
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cssd.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+    cssd.load_library()
+    if args.only:
+        progress(f"timing {args.only} alone")
+        e = forward_entry(only_inputs(args.only), args.steps, args.warmup, dev)
+        print(json.dumps({"workload": args.only, **e}), flush=True)
+        return
 
     s = wl.CONFIG_SHAPES[1]
     B, T, H, D, N, C = s["B"], s["T"], s["H"], s["D"], s["N"], s["C"]

@@ -24,7 +24,7 @@ CSSD_F32, CSSD_BF16 = 0, 1
 KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
                 "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
                 "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db",
-                "k_state_scan", "k_state_scan_adj", "k_fill")
+                "k_state_scan", "k_state_scan_adj", "k_fill", "k_scan_fused")
 
 _lock = threading.Lock()
 _lib = None

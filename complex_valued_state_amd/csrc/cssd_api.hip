@@ -344,6 +344,12 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                                B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im, y_re,
                                y_im, hT_re, hT_im, static_cast<char*>(workspace), L);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cssd::scan_fused(a)) {  // one kernel, the cumsum included
+        if (timed(cssd::K_SCAN_FUSED, s, [&] { return cssd::launch_scan_fused(a, s); }) !=
+            hipSuccess)
+            return CSSD_ERR_HIP;
+        return CSSD_OK;
+    }
     if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a, s); }) != hipSuccess)
         return CSSD_ERR_HIP;
     if (timed(cssd::K_STATE_SCAN, s, [&] { return cssd::launch_state_scan(a, s); }) != hipSuccess)
@@ -868,7 +874,7 @@ const char* cssd_kernel_name(int kernel_id) {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
         "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
         "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db",
-        "k_state_scan", "k_state_scan_adj", "k_fill"};
+        "k_state_scan", "k_state_scan_adj", "k_fill", "k_scan_fused"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

@@ -9,7 +9,8 @@ namespace cssd {
 enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN = 3, K_STEP = 4,
                 K_STEP_INFINITE = 5, K_BWD_DX = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
                 K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_BORN = 12,
-                K_BWD_DB = 13, K_STATE_SCAN = 14, K_STATE_SCAN_ADJ = 15, K_FILL = 16, K_COUNT = 17 };
+                K_BWD_DB = 13, K_STATE_SCAN = 14, K_STATE_SCAN_ADJ = 15, K_FILL = 16,
+                K_SCAN_FUSED = 17, K_COUNT = 18 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -76,6 +77,10 @@ hipError_t launch_cumsum(const FwdArgs& a, hipStream_t stream);
 // chunk states and the chunk-to-chunk pass fused (forward): writes H_c and hT
 hipError_t launch_state_scan(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t stream);
+// the chunk states, the chunk-to-chunk pass and the output in one kernel that
+// walks each (b, h)'s chunks (bf16 inputs at N = D = C = 64, where scan_fused holds)
+bool scan_fused(const FwdArgs& a);
+hipError_t launch_scan_fused(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 hipError_t launch_chunk_state_adjoint(const FwdArgs& a, const float* dy_re, const float* dy_im,
                                       float* q_re, float* q_im, hipStream_t stream);

@@ -1,0 +1,542 @@
+// The whole chunkwise forward for bf16 inputs in one kernel: one workgroup per
+// (b, h) walks that sequence's chunks in order and keeps the carried state in
+// registers, so the carry-in states never reach memory and every input row is
+// read once.  Chunk size, head dim and state dim are 64.
+//
+// For chunk c of sequence (b, h), rows l and columns s of the chunk:
+//   y[l, :]  = sum_{s<=l} (G . L)[l, s] X[s, :] + exp(acs[l]) C[l, :] H_c + Dskip X[l, :]
+//   G        = C B^T,  L[l, s] = exp(acs[l] - acs[s]) 1[l >= s]
+//   H_{c+1}  = cd[c] H_c + (diag(w) B)^T X,  H_0 = h0,  hT = H_nC
+// (Mamba-3-Lite docs, "SSD Theory" 4.3-4.5 and "The Chunkwise Complex SSD
+// Algorithm" 4.2-4.5: the segment matrix, the intra-chunk term, the chunk
+// states and the chunk-to-chunk recurrence taken in its sequential form; the
+// skip term follows the burn-mamba step_constant readout).  The discretisation
+// and the chunk-local cumsum (acs, e = exp(acs), w = exp(acs[C-1] - acs),
+// cd = exp(acs[C-1])) are done here too, one chunk ahead, by the wave with the
+// fewest score tiles.
+//
+// Every product runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  That
+// instruction takes A[i][k] from lane i + 16 (k / 8), slot k % 8, B[k][j] from
+// lane j + 16 (k / 8), slot k % 8, and leaves D[4g + r][j] in register r of lane
+// j + 16 g.  Wave w of the four owns the 16 columns p = 16 w + (lane % 16) of y
+// and of the state; its part of H sits in the accumulator layout of the
+// chunk-state product: tile nt, register r of lane p + 16 g <-> n = 16 nt + 4 g + r.
+//  * C H_c: A = C rows, B = H.  The 32-wide contraction over n takes state tiles
+//    2 ks and 2 ks + 1: slot j < 4 is n = 32 ks + 4 g + j and slot j >= 4 is
+//    n = 32 ks + 16 + 4 g + j - 4, which is where the accumulators hold them, so
+//    H enters the product straight from its registers (rounded to bf16 as an
+//    operand only); the C row is read as the two matching 8-byte pieces.
+//  * G^T = B C^T: A = B rows, B = C rows, both 16-byte reads of staged rows;
+//    register r of lane l + 16 g then holds G[l][s0 + 4 g + r], where
+//    M = G . L (+ Dskip on the diagonal) is formed in fp32, rounded to bf16 and
+//    written row-major into LDS for every wave to read.
+//  * M X and (w B)^T X contract over time with 8 consecutive steps per lane
+//    group, so X and w B are staged transposed (one LDS row per feature over the
+//    chunk's 64 steps); the X^T operand of the wave's columns serves both.
+// Complex products are four real products (a sum of bf16 operands would round),
+// the imaginary operand negated where the real part needs it.
+//
+// Staging: the next chunk's C, B and X rows are loaded into registers while
+// the current chunk is computed, then written to LDS (C and B
+// rows with 16-byte pieces XOR-swizzled by the row; X transposed).  w B is then
+// formed from the staged B rows in fp32 and rounded to bf16 into its transposed
+// rows; the M tiles overwrite the B rows once the scores are done.  70 KB of
+// LDS: two workgroups per CU.  Rows of a partial last chunk past the sequence
+// read as zero through the buffer extents and their stores are dropped.
+#include "cssd_device.h"
+#include "cssd_launch.h"
+
+namespace cssd {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRow = 128;   // bytes of a staged bf16 row of 64 values (C, B, M)
+constexpr int kTRow = 144;  // bytes of a transposed row: 64 steps + 16 B (X^T, (w B)^T)
+
+// physical 16-byte piece of logical piece `ch` of staged row `row`: two rows per
+// 256-byte window, so 16 consecutive rows reading one logical piece hit 8
+// distinct windows at 8 distinct offsets
+__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ floatx4 mfma_bf(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 bneg(bf16x8 v) {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+    u ^= 0x80008000u;
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+__device__ __forceinline__ float lo_f(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float hi_f(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+struct FusedArgs {
+    const uint16_t *x_re, *x_im, *b_re, *b_im, *c_re, *c_im;
+    const float *dt, *a_re, *a_im, *dskip;
+    const float *h0_re, *h0_im;
+    float *y_re, *y_im, *hT_re, *hT_im;
+    int64_t T;
+    int H, nC;
+};
+
+// one chunk's inputs in flight in registers
+struct Pre {
+    u32x4 c[2][2], b[2][2];  // [plane][piece]: 16-byte pieces of the C and B rows
+    uint32_t x[2][8];        // [plane][step]: two adjacent X columns at 8 steps
+};
+
+}  // namespace
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_fused_bf16(
+    FusedArgs a) {
+    constexpr int C = 64, N = 64, D = 64;
+    __shared__ __align__(16) unsigned char l_c[2][C * kRow];    // C rows (re, im)
+    __shared__ __align__(16) unsigned char l_b[2][C * kRow];    // B rows, then the M rows
+    __shared__ __align__(16) unsigned char l_xt[2][D * kTRow];  // X^T: [p][s]
+    __shared__ __align__(16) unsigned char l_wb[2][N * kTRow];  // (w B)^T: [n][s]
+    // per chunk, in two slots (chunk parity): the cumsums (real part in log2
+    // units; imaginary part in turns, reduced to its fractional part in fp64
+    // before it is rounded to fp32), exp(acs), exp(acs[C-1] - acs) and the
+    // chunk decay exp(acs[C-1])
+    __shared__ __align__(16) float l_acs[2][2][C];
+    __shared__ __align__(16) float l_e[2][2][C];
+    __shared__ __align__(16) float l_w[2][2][C];
+    __shared__ float l_cd[2][2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int w = wave_id();
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % a.H);
+    const int64_t b = bh / a.H;
+    const uint32_t sN = (uint32_t)a.H * N, sD = (uint32_t)a.H * D;
+    const float dk = a.dskip != nullptr ? a.dskip[h] : 0.f;
+    const int pcol = 16 * w + li;  // this lane's column of y and of the state
+
+    // the carried state, tile nt register r <-> (n = 16 nt + 4 g + r, p = pcol);
+    // the state planes are addressed through buffer views of this (b, h)'s N x D
+    // block, so one lane offset serves all 16 elements (the rest is immediate)
+    float hr[4][4], hi[4][4];
+    const uint32_t soff = (uint32_t)(4 * g) * D + pcol;
+    if (a.h0_re != nullptr) {
+        const BufRes r0 = make_buf(a.h0_re + bh * (int64_t)N * D, N * D * 4);
+        const BufRes i0 = make_buf(a.h0_im + bh * (int64_t)N * D, N * D * 4);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hr[nt][r] = buf_f32(r0, soff + (16 * nt + r) * D);
+                hi[nt][r] = buf_f32(i0, soff + (16 * nt + r) * D);
+            }
+    } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hr[nt][r] = hi[nt][r] = 0.f;
+    }
+
+    // staging roles: C and B pieces u = tid + 256 k (row u / 8, piece u % 8); X
+    // columns 2 xp, 2 xp + 1 at steps 8 xg .. 8 xg + 7; threads 0-127 one piece
+    // of the cumsums (0-63), exp(acs) (64-95) or the weights (96-127)
+    const int xp = tid & 31, xg = tid >> 5;
+    auto load = [&](int c, Pre& P) {
+        const int64_t t0 = (int64_t)c * C;
+        const int valid = (int)min<int64_t>((int64_t)C, a.T - t0);
+        const int64_t row0 = (b * a.T + t0) * a.H + h;
+        const uint32_t extN = ((uint32_t)(valid - 1) * sN + N) * 2u;
+        const uint32_t extD = ((uint32_t)(valid - 1) * sD + D) * 2u;
+        const BufRes rc[2] = {make_buf(a.c_re + row0 * N, extN), make_buf(a.c_im + row0 * N, extN)};
+        const BufRes rb[2] = {make_buf(a.b_re + row0 * N, extN), make_buf(a.b_im + row0 * N, extN)};
+        const BufRes rx[2] = {make_buf(a.x_re + row0 * D, extD), make_buf(a.x_im + row0 * D, extD)};
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int u = tid + 256 * k;
+                const uint32_t off = ((uint32_t)(u >> 3) * sN + 8 * (u & 7)) * 2u;
+                P.c[pl][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc[pl], off, 0, 0));
+                P.b[pl][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb[pl], off, 0, 0));
+            }
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t off = ((uint32_t)(8 * xg + r) * sD + 2 * xp) * 2u;
+                P.x[pl][r] = __builtin_amdgcn_raw_buffer_load_b32(rx[pl], off, 0, 0);
+            }
+    };
+    auto stage = [&](const Pre& P) {
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int u = tid + 256 * k, row = u >> 3;
+                const int at = row * kRow + 16 * swz(row, u & 7);
+                *reinterpret_cast<u32x4*>(&l_c[pl][at]) = P.c[pl][k];
+                *reinterpret_cast<u32x4*>(&l_b[pl][at]) = P.b[pl][k];
+            }
+        // X^T rows 2 xp + f, steps 8 xg .. 8 xg + 7
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                u32x4 v;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t a0 = (P.x[pl][2 * k] >> (16 * f)) & 0xffffu;
+                    const uint32_t a1 = (P.x[pl][2 * k + 1] >> (16 * f)) & 0xffffu;
+                    v[k] = a0 | (a1 << 16);
+                }
+                *reinterpret_cast<u32x4*>(&l_xt[pl][(2 * xp + f) * kTRow + 16 * xg]) = v;
+            }
+    };
+    // the discretisation and chunk-local cumsum of chunk c (wave 0, lane l holds
+    // position l), from its raw steps dtv, into slot c & 1:
+    //   A_log[l] = softplus(dt) A (0 past the sequence), acs = inclusive cumsum,
+    //   e = exp(acs), w = exp(acs[C-1] - acs), cd = exp(acs[C-1])
+    // ("The Chunkwise Complex SSD Algorithm" 4.2, "SSD Theory" 4.3 and 4.5).  The
+    // sums stay fp64; the exponentials take the fp64 arguments reduced to log2
+    // units and to half a turn, then the fp32 hardware exp2 / sin / cos, as the
+    // segment matrix does.
+    const float are_f = a.a_re[h], aim_f = a.a_im[h];
+    auto cumsum = [&](int c, float dtv) {
+        float fr = are_f, fi = aim_f;
+        asm volatile("" : "+s"(fr), "+s"(fi));  // widened here, not kept live as fp64
+        const double are = fr, aim = fi;
+        // an opaque copy of the lane index: the addresses below are recomputed
+        // here rather than kept live across the loop
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const int slot = c & 1;
+        const int64_t t = (int64_t)c * C + lane;
+        double vr = 0.0, vi = 0.0;
+        if (t < a.T) {
+            // softplus in fp32 (log1pf / expf of the device library, about one ulp):
+            // this path's operands are bf16, whose rounding is 2^15 times coarser
+            const double sp = (double)(fmaxf(dtv, 0.f) + log1pf(expf(-fabsf(dtv))));
+            vr = sp * are;
+            vi = sp * aim;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double ur = __shfl_up(vr, off, 64), ui = __shfl_up(vi, off, 64);
+            if (lane >= off) {
+                vr += ur;
+                vi += ui;
+            }
+        }
+        const double tr = __shfl(vr, 63, 64), ti = __shfl(vi, 63, 64);
+        const double ar2 = vr * kLog2e, at2 = vi * kInvTwoPi;  // log2 units, turns
+        l_acs[slot][0][lane] = (float)ar2;
+        l_acs[slot][1][lane] = (float)(at2 - rint(at2));
+        float er, ei, wr, wi;
+        cexp_scaled((float)ar2, (float)(at2 - rint(at2)), er, ei);
+        const double wr2 = (tr - vr) * kLog2e, wt2 = (ti - vi) * kInvTwoPi;
+        cexp_scaled((float)wr2, (float)(wt2 - rint(wt2)), wr, wi);
+        l_e[slot][0][lane] = er;
+        l_e[slot][1][lane] = ei;
+        l_w[slot][0][lane] = wr;
+        l_w[slot][1][lane] = wi;
+        if (lane == 63) {  // acs[C-1] is the chunk total
+            l_cd[slot][0] = er;
+            l_cd[slot][1] = ei;
+        }
+    };
+    auto load_dt = [&](int c) {
+        const int64_t t = (int64_t)c * C + lane;
+        return t < a.T ? a.dt[(b * a.T + t) * a.H + h] : 0.f;
+    };
+
+    Pre P;
+    load(0, P);
+    float dtn = 0.f;  // wave 0: the raw steps of the chunk after next
+    if (w == 0) {
+        cumsum(0, load_dt(0));
+        if (a.nC > 1) dtn = load_dt(1);
+    }
+    for (int c = 0; c < a.nC; ++c) {
+        const int64_t t0 = (int64_t)c * C;
+        const int valid = (int)min<int64_t>((int64_t)C, a.T - t0);
+        const int64_t row0 = (b * a.T + t0) * a.H + h;
+        const int slot = c & 1;
+        const float* const acs_r = l_acs[slot][0];
+        const float* const acs_i = l_acs[slot][1];
+        const float* const lw_r = l_w[slot][0];
+        const float* const lw_i = l_w[slot][1];
+        const float* const le_r = l_e[slot][0];
+        const float* const le_i = l_e[slot][1];
+
+        __syncthreads();  // every wave is done with the previous chunk's LDS
+        stage(P);
+        if (c + 1 < a.nC) load(c + 1, P);
+        __syncthreads();
+
+        // ---- (w B)^T rows 2 xp + f over steps 8 xg .. 8 xg + 7, from the staged B rows
+        {
+            u32x4 pr[2], pi[2];  // [feature]: 8 steps of (w B)[s][2 xp + f], re and im
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t ur[2][2], ui[2][2];  // [feature][step of the pair]
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    const int s = 8 * xg + 2 * k + e2;
+                    const int at = s * kRow + 16 * swz(s, xp >> 2) + 4 * (xp & 3);
+                    const uint32_t vr = *reinterpret_cast<const uint32_t*>(&l_b[0][at]);
+                    const uint32_t vi = *reinterpret_cast<const uint32_t*>(&l_b[1][at]);
+                    const float wr = lw_r[s], wi = lw_i[s];
+                    const float br[2] = {lo_f(vr), hi_f(vr)}, bi[2] = {lo_f(vi), hi_f(vi)};
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        ur[f][e2] = bf16_bits(wr * br[f] - wi * bi[f]);
+                        ui[f][e2] = bf16_bits(wr * bi[f] + wi * br[f]);
+                    }
+                }
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    pr[f][k] = ur[f][0] | (ur[f][1] << 16);
+                    pi[f][k] = ui[f][0] | (ui[f][1] << 16);
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                *reinterpret_cast<u32x4*>(&l_wb[0][(2 * xp + f) * kTRow + 16 * xg]) = pr[f];
+                *reinterpret_cast<u32x4*>(&l_wb[1][(2 * xp + f) * kTRow + 16 * xg]) = pi[f];
+            }
+        }
+
+        // ---- wave 0 has the fewest score tiles: it discretises the next chunk first
+        // (into the other slot, last read in the previous chunk)
+        if (w == 0 && c + 1 < a.nC) {
+            cumsum(c + 1, dtn);
+            if (c + 2 < a.nC) dtn = load_dt(c + 2);
+        }
+
+        // ---- score tiles q in [q0, q1) (lt-major causal tiles): M = G . L (+ Dskip)
+        constexpr int NP = 10, MQ = 3;
+        const int q0 = (w * NP) / 4, q1 = ((w + 1) * NP) / 4;
+        bf16x4 m_r[MQ], m_i[MQ];
+        int m_lt[MQ], m_st[MQ];
+        {
+            int lt = 0, st = q0;
+            while (st > lt) {
+                st -= lt + 1;
+                ++lt;
+            }
+#pragma unroll
+            for (int jq = 0; jq < MQ; ++jq) {
+                m_lt[jq] = lt;
+                m_st[jq] = st;
+                if (q0 + jq < q1) {  // wave-uniform
+                    floatx4 gr = {0.f, 0.f, 0.f, 0.f}, gi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const int ch = 4 * ks + g;
+                        const int sb = 16 * st + li, lb = 16 * lt + li;
+                        const bf16x8 br = *reinterpret_cast<const bf16x8*>(&l_b[0][sb * kRow + 16 * swz(sb, ch)]);
+                        const bf16x8 bi = *reinterpret_cast<const bf16x8*>(&l_b[1][sb * kRow + 16 * swz(sb, ch)]);
+                        const bf16x8 cr = *reinterpret_cast<const bf16x8*>(&l_c[0][lb * kRow + 16 * swz(lb, ch)]);
+                        const bf16x8 ci = *reinterpret_cast<const bf16x8*>(&l_c[1][lb * kRow + 16 * swz(lb, ch)]);
+                        gr = mfma_bf(br, cr, gr);
+                        gr = mfma_bf(bneg(bi), ci, gr);
+                        gi = mfma_bf(br, ci, gi);
+                        gi = mfma_bf(bi, cr, gi);
+                    }
+                    // register r <-> (l = 16 lt + li, s = 16 st + 4 g + r)
+                    const int lrow = 16 * lt + li;
+                    const bool diag = (lt == st);
+                    // L from fp32 differences: the real parts differ by a chunk's
+                    // log-decay at most, the turns are fractional parts, and their
+                    // difference is reduced to half a turn again
+                    const float alr = acs_r[lrow], ali = acs_i[lrow];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int s = 16 * st + 4 * g + r;
+                        float lr = 0.f, lim = 0.f;
+                        if (!diag || s <= lrow) {
+                            float dv = ali - acs_i[s];
+                            dv -= rintf(dv);
+                            cexp_scaled(alr - acs_r[s], dv, lr, lim);
+                        }
+                        m_r[jq][r] = (__bf16)(gr[r] * lr - gi[r] * lim + ((diag && s == lrow) ? dk : 0.f));
+                        m_i[jq][r] = (__bf16)(gr[r] * lim + gi[r] * lr);
+                    }
+                    if (++st > lt) {
+                        st = 0;
+                        ++lt;
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the B rows are free: every wave's scores and (w B)^T are done
+
+        // ---- the M rows [l][s] over the B rows; the two non-causal tiles that a
+        // 32-step product reads, (0, 1) and (2, 3), are zero
+#pragma unroll
+        for (int jq = 0; jq < MQ; ++jq) {
+            if (q0 + jq < q1) {
+                const int l = 16 * m_lt[jq] + li, s0 = 16 * m_st[jq] + 4 * g;
+                const int at = l * kRow + 16 * swz(l, s0 >> 3) + 2 * (s0 & 7);
+                *reinterpret_cast<bf16x4*>(&l_b[0][at]) = m_r[jq];
+                *reinterpret_cast<bf16x4*>(&l_b[1][at]) = m_i[jq];
+            }
+        }
+        if (w == 0) {
+            int zl = threadIdx.x & 63;  // opaque copy of the lane index (see cumsum)
+            asm volatile("" : "+v"(zl));
+#pragma unroll
+            for (int zt = 0; zt < 2; ++zt) {
+                const int l = 32 * zt + (zl & 15), s0 = 32 * zt + 16 + 4 * (zl >> 4);
+                const int at = l * kRow + 16 * swz(l, s0 >> 3) + 2 * (s0 & 7);
+                *reinterpret_cast<u32x2*>(&l_b[0][at]) = u32x2{0u, 0u};
+                *reinterpret_cast<u32x2*>(&l_b[1][at]) = u32x2{0u, 0u};
+            }
+        }
+        __syncthreads();
+
+        // ---- X^T operand of this wave's columns: slot j <-> s = 32 k2 + 8 g + j
+        bf16x8 xr[2], xi[2], xni[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int at = pcol * kTRow + 64 * k2 + 16 * g;
+            xr[k2] = *reinterpret_cast<const bf16x8*>(&l_xt[0][at]);
+            xi[k2] = *reinterpret_cast<const bf16x8*>(&l_xt[1][at]);
+            xni[k2] = bneg(xi[k2]);
+        }
+        // ---- per row tile lt: y = diag(exp(acs)) C H_c + M X, then stored (register
+        // r <-> row 16 lt + 4 g + r; rows past the sequence are dropped)
+        {
+            // H_c as the B operand of C H_c: slot j <-> n = 32 ks + 4 g + j (j < 4),
+            // 32 ks + 16 + 4 g + j - 4 (j >= 4), the accumulator registers themselves
+            bf16x8 hb_r[2], hb_i[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    hb_r[ks][j] = (__bf16)hr[2 * ks][j];
+                    hb_r[ks][j + 4] = (__bf16)hr[2 * ks + 1][j];
+                    hb_i[ks][j] = (__bf16)hi[2 * ks][j];
+                    hb_i[ks][j + 4] = (__bf16)hi[2 * ks + 1][j];
+                }
+            const uint32_t extD = (uint32_t)(valid - 1) * sD + D;
+            const BufRes ry_r = make_buf(a.y_re + row0 * D, extD * 4);
+            const BufRes ry_i = make_buf(a.y_im + row0 * D, extD * 4);
+#pragma unroll
+            for (int lt = 0; lt < 4; ++lt) {
+                floatx4 yr = {0.f, 0.f, 0.f, 0.f}, yi = {0.f, 0.f, 0.f, 0.f};
+                const int l = 16 * lt + li;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    // C[l][32 ks + 4 g + 0..3] and C[l][32 ks + 16 + 4 g + 0..3]
+                    const int ch = 4 * ks + (g >> 1), o8 = 8 * (g & 1);
+                    const int a0 = l * kRow + 16 * swz(l, ch) + o8;
+                    const int a1 = l * kRow + 16 * swz(l, ch + 2) + o8;
+                    const u32x2 r0 = *reinterpret_cast<const u32x2*>(&l_c[0][a0]);
+                    const u32x2 r1 = *reinterpret_cast<const u32x2*>(&l_c[0][a1]);
+                    const u32x2 i0 = *reinterpret_cast<const u32x2*>(&l_c[1][a0]);
+                    const u32x2 i1 = *reinterpret_cast<const u32x2*>(&l_c[1][a1]);
+                    const bf16x8 cr = __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
+                    const bf16x8 ci = __builtin_bit_cast(bf16x8, u32x4{i0[0], i0[1], i1[0], i1[1]});
+                    yr = mfma_bf(cr, hb_r[ks], yr);
+                    yr = mfma_bf(ci, bneg(hb_i[ks]), yr);
+                    yi = mfma_bf(cr, hb_i[ks], yi);
+                    yi = mfma_bf(ci, hb_r[ks], yi);
+                }
+                {
+                    const floatx4 er = *reinterpret_cast<const floatx4*>(&le_r[16 * lt + 4 * g]);
+                    const floatx4 ei = *reinterpret_cast<const floatx4*>(&le_i[16 * lt + 4 * g]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float re = yr[r], im = yi[r];
+                        yr[r] = er[r] * re - ei[r] * im;
+                        yi[r] = er[r] * im + ei[r] * re;
+                    }
+                }
+                // M X over s in 32-steps (the second only for rows 32 and up)
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    if (k2 == 1 && lt < 2) continue;
+                    const int ch = 4 * k2 + g;
+                    const bf16x8 mr = *reinterpret_cast<const bf16x8*>(&l_b[0][l * kRow + 16 * swz(l, ch)]);
+                    const bf16x8 mi = *reinterpret_cast<const bf16x8*>(&l_b[1][l * kRow + 16 * swz(l, ch)]);
+                    yr = mfma_bf(mr, xr[k2], yr);
+                    yr = mfma_bf(mi, xni[k2], yr);
+                    yi = mfma_bf(mr, xi[k2], yi);
+                    yi = mfma_bf(mi, xr[k2], yi);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t off = (uint32_t)(16 * lt + 4 * g + r) * sD + pcol;
+                    buf_store_f32(yr[r], ry_r, off);
+                    buf_store_f32(yi[r], ry_i, off);
+                }
+            }
+        }
+        // ---- S_c = (w B)^T X on this wave's columns, then H_{c+1} = cd H_c + S_c
+        const float dr = l_cd[slot][0], di = l_cd[slot][1];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            floatx4 sr = {0.f, 0.f, 0.f, 0.f}, si = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int at = (16 * nt + li) * kTRow + 64 * k2 + 16 * g;
+                const bf16x8 ar = *reinterpret_cast<const bf16x8*>(&l_wb[0][at]);
+                const bf16x8 ai = *reinterpret_cast<const bf16x8*>(&l_wb[1][at]);
+                sr = mfma_bf(ar, xr[k2], sr);
+                sr = mfma_bf(ai, xni[k2], sr);
+                si = mfma_bf(ar, xi[k2], si);
+                si = mfma_bf(ai, xr[k2], si);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float nr = dr * hr[nt][r] - di * hi[nt][r] + sr[r];
+                const float ni = dr * hi[nt][r] + di * hr[nt][r] + si[r];
+                hr[nt][r] = nr;
+                hi[nt][r] = ni;
+            }
+        }
+    }
+    if (a.hT_re != nullptr) {
+        const BufRes r1 = make_buf(a.hT_re + bh * (int64_t)N * D, N * D * 4);
+        const BufRes i1 = make_buf(a.hT_im + bh * (int64_t)N * D, N * D * 4);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                buf_store_f32(hr[nt][r], r1, soff + (16 * nt + r) * D);
+                buf_store_f32(hi[nt][r], i1, soff + (16 * nt + r) * D);
+            }
+    }
+}
+
+bool scan_fused(const FwdArgs& f) {
+    return f.in_dtype == 1 && f.C == 64 && f.N == 64 && f.D == 64;
+}
+
+hipError_t launch_scan_fused(const FwdArgs& f, hipStream_t s) {
+    if (!scan_fused(f)) return hipErrorNotSupported;
+    FusedArgs a;
+    a.x_re = static_cast<const uint16_t*>(f.x_re);
+    a.x_im = static_cast<const uint16_t*>(f.x_im);
+    a.b_re = static_cast<const uint16_t*>(f.b_re);
+    a.b_im = static_cast<const uint16_t*>(f.b_im);
+    a.c_re = static_cast<const uint16_t*>(f.c_re);
+    a.c_im = static_cast<const uint16_t*>(f.c_im);
+    a.dt = f.dt; a.a_re = f.a_re; a.a_im = f.a_im; a.dskip = f.dskip;
+    a.h0_re = f.h0_re; a.h0_im = f.h0_im;
+    a.y_re = f.y_re; a.y_im = f.y_im; a.hT_re = f.hT_re; a.hT_im = f.hT_im;
+    a.T = f.T; a.H = (int)f.H; a.nC = (int)f.nC;
+    hipLaunchKernelGGL(k_scan_fused_bf16, dim3((unsigned)(f.B * f.H)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace cssd

@@ -281,7 +281,7 @@ def test_profiler_without_launches(lib):
         pass
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
-    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(17) is None
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(18) is None
     assert lib.cssd_kernel_name(16) == b"k_fill"
     assert lib.cssd_kernel_name(14) == b"k_state_scan"
     assert lib.cssd_kernel_name(15) == b"k_state_scan_adj"
