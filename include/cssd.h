@@ -93,7 +93,9 @@ const char *cssd_status_string(int status);
  * term grows like 8*B*T*H*C bytes ("SSD Theory" section 5).
  *
  * Layout (nC = ceil(T/C), P = nC*C padded positions, every region 256-byte
- * aligned, in this order; a caller may read it after the stream completes):
+ * aligned, in this order; a caller may read it after the stream completes,
+ * except after a bf16-input call with headdim = dstate = chunk = 64, which runs
+ * as one kernel that keeps these quantities on chip and writes nothing here):
  *   acs_re, acs_im : double [B][H][P]     inclusive chunk-local cumsum of
  *                                         softplus(dt)*A (0 increments on
  *                                         padded positions), real part in log2
