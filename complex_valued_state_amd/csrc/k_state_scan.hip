@@ -273,7 +273,7 @@ struct AdjExtra {
     double *z_re, *z_im;         // [(b, h, c) * 2 + half]
 };
 
-template <bool ADJ>
+template <bool ADJ, int C, int N>
 __global__ __launch_bounds__(256) void k_state_scan_lds(
     const float* __restrict__ x_re, const float* __restrict__ x_im,
     const float* __restrict__ b_re, const float* __restrict__ b_im,
@@ -282,9 +282,12 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
     const float* __restrict__ h0_re, const float* __restrict__ h0_im, float* __restrict__ st_re,
     float* __restrict__ st_im, float* __restrict__ hT_re, float* __restrict__ hT_im, int64_t T,
     int H, int nC, int64_t nbh, AdjExtra adj) {
-    constexpr int C = 64, N = 64, D = 64, PT = D / 16;
+    constexpr int D = 64, PT = D / 16;
+    constexpr int NQ = N / 32;   // workgroups per (b, h): 32 rows n each
     constexpr int NS = C / kSR;  // stages per chunk
     constexpr int KS = kSR / 4;  // k-steps per stage
+    constexpr int WPL = C / 64;  // weights per lane when a chunk's w is loaded
+    static_assert(!ADJ || (C == 64 && N == 64), "the adjoint mode is built for N = C = 64");
     __shared__ floatx4 sb[2][2][kSR * 8];   // [buffer][plane][row * 8 + unit]: 32 B columns per row
     __shared__ floatx4 sx[2][2][kSR * 16];  // [buffer][plane][row * 16 + unit]: all 64 X columns
     __shared__ float lds_w[4][2 * C];
@@ -295,8 +298,8 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
     const int64_t xcd = blockIdx.x % kScanXcds, y = blockIdx.x / kScanXcds;
     // each XCD takes a run of consecutive (b, h): the rows of neighbouring heads
     // are adjacent in memory (measured slightly faster than interleaving them)
-    const int64_t bh = xcd * (int64_t)(gridDim.x / (2 * kScanXcds)) + y / 2;
-    const int h2 = (int)(y % 2);
+    const int64_t bh = xcd * (int64_t)(gridDim.x / (NQ * kScanXcds)) + y / NQ;
+    const int h2 = (int)(y % NQ);
     if (bh >= nbh) return;  // uniform over the workgroup
     const int ntl = wv >> 1, pt0 = (wv & 1) * 2, nt = 2 * h2 + ntl;
     const int h = (int)(bh % H);
@@ -351,11 +354,14 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
             sx[buf][1][rx * 16 + (ux ^ swz_x(rx))] = R.x[1][k];
         }
     };
-    float wn_r, wn_i;  // the next chunk's weights, position lane
+    float wn_r[WPL], wn_i[WPL];  // the next chunk's weights, positions lane + 64 k
     auto load_w = [&](int c) {
-        const int64_t at = (bh * nC + c) * (int64_t)C + lane;
-        wn_r = w_re[at];
-        wn_i = w_im[at];
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            const int64_t at = (bh * nC + c) * (int64_t)C + lane + 64 * k;
+            wn_r[k] = w_re[at];
+            wn_i[k] = w_im[at];
+        }
     };
     // per-lane operand offsets (floats) within a stage buffer; row 4 j + g adds 4 j rows
     const int offb = g * 32 + (((4 * ntl + (li >> 2)) ^ swz_b(g)) << 2) + (li & 3);
@@ -433,8 +439,11 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
                     lds_z[wv][1] = zi;
                 }
             }
-            lw[lane] = wn_r;
-            lw[C + lane] = wn_i;
+#pragma unroll
+            for (int k = 0; k < WPL; ++k) {
+                lw[lane + 64 * k] = wn_r[k];
+                lw[C + lane + 64 * k] = wn_i[k];
+            }
             if (ADJ ? c > 0 : c + 1 < nC) load_w(ADJ ? c - 1 : c + 1);
 #pragma unroll
             for (int q = 0; q < 2; ++q) ctile_zero(acc[q]);
@@ -491,12 +500,13 @@ __global__ __launch_bounds__(256) void k_state_scan_lds(
     }
 }
 
+template <int C, int N>
 static hipError_t launch_scan_lds(const FwdArgs& a, hipStream_t s) {
     const int64_t nbh = a.B * a.H;
-    const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * 2;
+    const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * (N / 32);
     typedef const float* P;
     const AdjExtra none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-    hipLaunchKernelGGL((k_state_scan_lds<false>), dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_state_scan_lds<false, C, N>), dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<P>(a.x_re), static_cast<P>(a.x_im), static_cast<P>(a.b_re),
                        static_cast<P>(a.b_im),
                        a.w_re, a.w_im, a.cd_re, a.cd_im, a.h0_re, a.h0_im, a.st_re, a.st_im,
@@ -517,7 +527,7 @@ hipError_t launch_state_scan_adjoint(const FwdArgs& a, const float* dy_re, const
     const int64_t nbh = a.B * a.H;
     const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * 2;
     const AdjExtra adj = {a.st_re, a.st_im, hT_re, hT_im, z_re, z_im};
-    hipLaunchKernelGGL((k_state_scan_lds<true>), dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_state_scan_lds<true, 64, 64>), dim3((unsigned)blocks), dim3(256), 0, s,
                        dy_re, dy_im, static_cast<const float*>(a.c_re),
                        static_cast<const float*>(a.c_im), a.e_re, a.e_im, a.cd_re, a.cd_im,
                        dhT_re, dhT_im, r_re, r_im, dh0_re, dh0_im, a.T, (int)a.H, (int)a.nC, nbh,
@@ -778,7 +788,13 @@ static hipError_t launch_scan_in(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_state_scan(const FwdArgs& a, hipStream_t s) {
     if (a.C == 64 && a.N == 64 && a.D == 64)
-        return a.in_dtype == 1 ? launch_scan_mm(a, s) : launch_scan_lds(a, s);
+        return a.in_dtype == 1 ? launch_scan_mm(a, s) : launch_scan_lds<64, 64>(a, s);
+    // staged through LDS at N = 128, C = 64 (four workgroups per (b, h)) where the
+    // problem has a workgroup for every CU: with fewer the one wave per SIMD of the
+    // staged form loses to the plain scan's (measured at B1 T16384 H48 C128:
+    // 0.82 ms staged against 0.71 ms)
+    if (a.in_dtype == 0 && a.D == 64 && a.N == 128 && a.C == 64 && a.B * a.H * 4 >= 256)
+        return launch_scan_lds<64, 128>(a, s);
     return a.in_dtype == 1 ? launch_scan_in<InBF16>(a, s) : launch_scan_in<InF32>(a, s);
 }
 

@@ -54,6 +54,16 @@ SMALL = [
     # few (b, h), many chunks: each state-scan wave walks a long chunk chain
     (1, 1024, 1, 16, 16, 16, True, True),    # 64 chunks
     (2, 1000, 2, 32, 64, 32, True, True),    # 32 chunks, ragged tail
+    # D = 64, N = 128 (the long-sequence and PAM shapes' state): four staged
+    # state-scan workgroups per (b, h), chunks of 64 and 128 (four stages each)
+    (2, 300, 3, 64, 128, 64, True, True),    # ragged tail, 6 (b, h)
+    (1, 1000, 2, 64, 128, 128, True, True),  # 8 chunks of 128, ragged tail
+    (3, 128, 5, 64, 128, 128, False, True),  # exactly one chunk, 15 (b, h) over 8 XCDs
+    (1, 70, 9, 64, 128, 64, True, False),    # T just past one chunk, 9 heads
+    (4, 130, 16, 64, 128, 64, True, True),   # 64 (b, h): the staged state scan at N = 128
+    (8, 64, 9, 64, 128, 64, False, True),    # 72 (b, h), exactly one chunk
+    (1, 777, 3, 64, 64, 128, True, True),    # 7 chunks of 128, ragged tail
+    (2, 500, 1, 32, 64, 64, True, True),     # D = 32: one p pair per n tile
 ]
 
 
