@@ -26,6 +26,7 @@
 #pragma once
 
 #include "k_chunk_scan_lds.h"
+#include "k_chunk_scan_nb.h"
 
 namespace cssd {
 
@@ -299,6 +300,9 @@ hipError_t launch_chunk_scan_c(const FwdArgs& f, hipStream_t s) {
             if (f.N == 32 && f.D == 32) return launch_chunk_scan_bf16<32, 32>(f, s);
         }
         return launch_chunk_scan_regs<C>(f, s);
+    }
+    if constexpr (C == 64) {
+        if (f.N == 128 && f.D == 64) return launch_chunk_scan_nb<64, 128, 64>(f, s);
     }
     switch (f.N) {
         case 16: return launch_staged_d<C, 16>(f, s);
