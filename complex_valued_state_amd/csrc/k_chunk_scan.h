@@ -45,13 +45,6 @@
 
 namespace cssd {
 
-#ifndef CSSD_K2_GAUSS
-#define CSSD_K2_GAUSS 1
-#endif
-#ifndef CSSD_K2_PREFETCH
-#define CSSD_K2_PREFETCH 1
-#endif
-
 struct ScanArgs {
     const void *x_re, *x_im, *b_re, *b_im, *c_re, *c_im;
     const float* dskip;
@@ -70,7 +63,7 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
     constexpr int NK = N / 16;   // 16-wide tiles of the n axis
     constexpr int PT = D / 16;   // 16-wide tiles of the p axis
     constexpr int NLT = C / 16;  // row tiles per chunk
-    constexpr bool PF = CSSD_K2_PREFETCH && NK <= 4 && PT <= 4;  // prefetch one tile ahead
+    constexpr bool PF = NK <= 4 && PT <= 4;  // prefetch one tile ahead
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
     const int c = (int)(chunk % a.nC);
@@ -150,7 +143,6 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
     const float er = a.e_re[pbase + lrow], ei = a.e_im[pbase + lrow];
     const float dk = a.dskip != nullptr ? a.dskip[h] : 0.f;
 
-#if CSSD_K2_GAUSS
     CTile y[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) ctile_zero(y[pt]);
@@ -158,14 +150,6 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
     floatx4 csum[NK];
 #pragma unroll
     for (int k = 0; k < NK; ++k) csum[k] = cre[k] + cim[k];
-#else
-    floatx4 yr[PT], yi[PT];
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-        yr[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        yi[pt] = yr[pt];
-    }
-#endif
 
     // ---- Y_off = diag(exp(acs)) C H_c : contraction over n
     STile s_tiles[NLT];
@@ -184,22 +168,11 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
             const float cr = cre[k][q], ci = cim[k][q];
             const float ar = er * cr - ei * ci;
             const float ai = er * ci + ei * cr;
-#if CSSD_K2_GAUSS
             const float as = ar + ai;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
                 ctile_mac(y[pt], ar, ai, as, hcur.r[pt][q], hcur.i[pt][q],
                           hcur.r[pt][q] + hcur.i[pt][q]);
-#else
-            const float nai = -ai;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                yr[pt] = mfma4(ar, hcur.r[pt][q], yr[pt]);
-                yr[pt] = mfma4(nai, hcur.i[pt][q], yr[pt]);
-                yi[pt] = mfma4(ar, hcur.i[pt][q], yi[pt]);
-                yi[pt] = mfma4(ai, hcur.r[pt][q], yi[pt]);
-            }
-#endif
         }
         if (k + 1 < NK) {
             if (PF)
@@ -223,7 +196,6 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
             }
             const STile& o = s_tiles[st];
             // G^T block: A = B[s0 + li, n], B-operand = C[l0 + li, n]
-#if CSSD_K2_GAUSS
             CTile gt;
             ctile_zero(gt);
 #pragma unroll
@@ -240,21 +212,6 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
                 gr[r] = ctile_re(gt, r);
                 gi[r] = ctile_im(gt, r);
             }
-#else
-            floatx4 gr = floatx4{0.f, 0.f, 0.f, 0.f}, gi = gr;
-#pragma unroll
-            for (int k = 0; k < NK; ++k) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float br = o.br[k][q], bi = o.bi[k][q];
-                    const float cr = cre[k][q], ci = cim[k][q];
-                    gr = mfma4(br, cr, gr);
-                    gr = mfma4(-bi, ci, gr);
-                    gi = mfma4(br, ci, gi);
-                    gi = mfma4(bi, cr, gi);
-                }
-            }
-#endif
             // M = G . L + Dskip on the diagonal; register r <-> s = s0 + 4g + r
             float mr[4], mi[4];
 #pragma unroll
@@ -273,22 +230,11 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
             // Y += M X
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-#if CSSD_K2_GAUSS
                 const float ms = mr[r] + mi[r];
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt)
                     ctile_mac(y[pt], mr[r], mi[r], ms, o.xr[r][pt], o.xi[r][pt],
                               o.xr[r][pt] + o.xi[r][pt]);
-#else
-                const float nmi = -mi[r];
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    yr[pt] = mfma4(mr[r], o.xr[r][pt], yr[pt]);
-                    yr[pt] = mfma4(nmi, o.xi[r][pt], yr[pt]);
-                    yi[pt] = mfma4(mr[r], o.xi[r][pt], yi[pt]);
-                    yi[pt] = mfma4(mi[r], o.xr[r][pt], yi[pt]);
-                }
-#endif
             }
         }
     }
@@ -299,13 +245,8 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
         const uint32_t off = (uint32_t)(l0 + 4 * g + r) * sD + li;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-#if CSSD_K2_GAUSS
             buf_store_f32(ctile_re(y[pt], r), ry_r, off + pt * 16);
             buf_store_f32(ctile_im(y[pt], r), ry_i, off + pt * 16);
-#else
-            buf_store_f32(yr[pt][r], ry_r, off + pt * 16);
-            buf_store_f32(yi[pt][r], ry_i, off + pt * 16);
-#endif
         }
     }
 }
@@ -314,10 +255,7 @@ __device__ __forceinline__ void chunk_scan_tile(const ScanArgs& a, int64_t chunk
 // a chunk share a CU; each wave runs the balanced pair of row tiles.
 template <typename In, int C, int N, int D>
 __global__ __launch_bounds__(256)
-#ifndef CSSD_K2_WAVES
-#define CSSD_K2_WAVES 2
-#endif
-__attribute__((amdgpu_waves_per_eu(N * D > 64 * 128 ? 1 : CSSD_K2_WAVES))) void k_chunk_scan(ScanArgs a) {
+__attribute__((amdgpu_waves_per_eu(N * D > 64 * 128 ? 1 : 2))) void k_chunk_scan(ScanArgs a) {
     constexpr int NLT = C / 16;
     constexpr int WPC = NLT >= 2 ? NLT / 2 : 1;  // waves per chunk
     const int wave = wave_id();

@@ -49,12 +49,9 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // tiles of the first two column tiles, then rows 32-63 for the other three), so
 // that a workgroup takes 52 KB of LDS instead of 68 and three fit on a CU, with
 // the registers held to three waves per SIMD.
-#ifndef CSSD_K2_HALFB
-#define CSSD_K2_HALFB 1
-#endif
 template <int C, int N, int D>
 constexpr bool k2_half_b() {
-    return CSSD_K2_HALFB && C == 64 && N == 64 && D == 64;
+    return C == 64 && N == 64 && D == 64;
 }
 
 template <int C, int N, int D>

@@ -42,10 +42,7 @@ __global__ __launch_bounds__(512) void k_chunk_state(
     constexpr int KJ = C / 4;   // MFMA k-steps per chunk
     constexpr int PT = D / 16;  // column tiles (p)
     // operands of DIST future k-steps are kept in flight (register ring)
-#ifndef CSSD_K3_DIST
-#define CSSD_K3_DIST 4
-#endif
-    constexpr int DW = PT <= 4 ? CSSD_K3_DIST : CSSD_K3_DIST / 2;
+    constexpr int DW = PT <= 4 ? 4 : 2;
     constexpr int DIST = DW < KJ ? DW : KJ;
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;

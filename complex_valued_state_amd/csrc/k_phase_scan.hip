@@ -36,10 +36,7 @@ namespace cssd {
 
 namespace {
 
-#ifndef CSSD_PHASE_U
-#define CSSD_PHASE_U 8
-#endif
-constexpr int kPhaseU = CSSD_PHASE_U;  // steps per prefetch block
+constexpr int kPhaseU = 8;  // steps per prefetch block
 
 // Every input is read once and every state written once per launch: streaming
 // (non-temporal) loads and stores keep them from displacing other lines in the

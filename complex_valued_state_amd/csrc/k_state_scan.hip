@@ -40,27 +40,15 @@ constexpr int kScanXcds = 8;
 
 // k-steps whose operands are in flight (a divisor of C/4), and whether a lane
 // reads two adjacent X columns in one load, per input type
-#ifndef CSSD_SCAN_DIST_F32
-#define CSSD_SCAN_DIST_F32 4
-#endif
-#ifndef CSSD_SCAN_DIST_BF16
-#define CSSD_SCAN_DIST_BF16 8
-#endif
-#ifndef CSSD_SCAN_PAIR_F32
-#define CSSD_SCAN_PAIR_F32 0
-#endif
-#ifndef CSSD_SCAN_PAIR_BF16
-#define CSSD_SCAN_PAIR_BF16 1
-#endif
 template <typename In>
 struct ScanTune {
-    static constexpr int dist = CSSD_SCAN_DIST_F32;
-    static constexpr bool pair = CSSD_SCAN_PAIR_F32;
+    static constexpr int dist = 4;
+    static constexpr bool pair = false;
 };
 template <>
 struct ScanTune<InBF16> {
-    static constexpr int dist = CSSD_SCAN_DIST_BF16;
-    static constexpr bool pair = CSSD_SCAN_PAIR_BF16;
+    static constexpr int dist = 8;
+    static constexpr bool pair = true;
 };
 
 }  // namespace

@@ -76,6 +76,23 @@ def test_small_shapes(case):
     _check_full(inp)
 
 
+@pytest.mark.parametrize("C", [16, 32, 64, 128])
+def test_every_short_length_every_chunk(C):
+    """Every T = 1..8 with chunk C (one partial chunk each): the GPU forward
+    against the oracle and against the unrolled double sum of "The Chunkwise
+    Complex SSD Algorithm" section 3 (tests/pins.py bruteforce: every (t, s) pair
+    with explicit decay products), with an initial state and the skip term."""
+    import pins
+    for T in range(1, 9):
+        inp = wl.random_forward(500 + 10 * T + C // 16, 2, T, 2, 16, 16, C, with_h0=True,
+                                name="short")
+        y, hT = gpu_forward(inp)
+        yr, hr = oracle_forward(inp)
+        yb, hb = pins.bruteforce(*inp.complex())
+        e = (rel_err(y, yr), rel_err(hT, hr), rel_err(y, yb), rel_err(hT, hb))
+        assert max(e) <= TOL_F32, (T, C, e)
+
+
 def test_chunk_size_invariance():
     """The chunk size is an implementation knob: C = 16..128 on the same inputs
     give the same result (SSD theorem; C = T is the single-chunk case)."""
@@ -183,11 +200,26 @@ BF16_CASES = [
 ]
 
 
+def bf16_diagnostic_bounds(N, D, C):
+    """Bounds on the error against the oracle run on the bf16-rounded inputs
+    themselves, per kernel path, set from the measured errors (about 3x the worst
+    seen).  Paths on the bf16 matrix cores round intermediates to bf16 as operands:
+    at C = 64 with N, D in {32, 64} the score-times-segment product M = G . L and
+    the copy of the carried state that enters C H_c (y: measured up to 3.4e-3);
+    at N = D = C = 64 also w B, the operand of the chunk-state product (hT:
+    measured up to 1.7e-3).  Every other path computes in fp32 on the rounded
+    inputs and is held to the fp32 bar."""
+    mm = C == 64 and N in (32, 64) and D in (32, 64)
+    y_bound = 1e-2 if mm else TOL_F32
+    h_bound = 5e-3 if (N == 64 and D == 64 and C == 64) else TOL_F32
+    return y_bound, h_bound
+
+
 @pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "B{}T{}H{}D{}N{}C{}".format(*c[:6]))
 def test_bf16_inputs_small(case):
     """bf16 x, B, C: within 2e-2 of the oracle on the pre-rounding inputs (the
-    bf16-input tolerance), and on the rounded inputs themselves (the products
-    round their operands, M = G . L and the carried state's copy, to bf16)."""
+    bf16-input tolerance); and, as a diagnostic of the intermediate roundings,
+    within the path's bound of the oracle on the rounded inputs themselves."""
     B, T, H, D, N, C, with_h0, with_d = case
     inp32 = wl.random_forward(99 + T, B, T, H, D, N, C, with_h0=with_h0, with_dskip=with_d,
                               name="bf16small")
@@ -197,9 +229,11 @@ def test_bf16_inputs_small(case):
     yr32, hr32 = oracle_forward(inp32)   # pre-rounding inputs: the bf16 tolerance
     yr16, hr16 = oracle_forward(inp16)   # the rounded inputs themselves
     e = (rel_err(y, yr32), rel_err(hT, hr32), rel_err(y, yr16), rel_err(hT, hr16))
+    yb, hb = bf16_diagnostic_bounds(N, D, C)
     log(f"    bf16 rel err vs pre-rounding y={e[0]:.2e} hT={e[1]:.2e}; "
-        f"vs rounded y={e[2]:.2e} hT={e[3]:.2e}")
-    assert max(e) <= TOL_BF16, e
+        f"vs rounded y={e[2]:.2e} (bound {yb:.0e}) hT={e[3]:.2e} (bound {hb:.0e})")
+    assert max(e[:2]) <= TOL_BF16, e
+    assert e[2] <= yb and e[3] <= hb, e
 
 
 def test_pam_orthogonal_keys_gpu():
@@ -243,8 +277,22 @@ def test_config1_fp32_sampled():
 
 
 def test_config1_bf16_sampled():
+    """The bf16-input variant of the Mamba-style layer: sampled sequences within
+    2e-2 of the oracle on the pre-rounding (fp32) draws, and within the
+    diagnostic bounds of the oracle on the rounded inputs."""
+    pairs = [(0, 1), (4, 23), (7, 46), (7, 47)]
     inp = wl.config1("bf16")
-    _check_sampled(inp, [(0, 1), (4, 23), (7, 46)], TOL_BF16)
+    y, hT = _check_sampled(inp, pairs, TOL_BF16)
+    yb, hb = bf16_diagnostic_bounds(64, 64, 64)
+    ref16 = sampled_oracle(inp, pairs)
+    del inp
+    ref32 = sampled_oracle(wl.config1("f32"), pairs)
+    for (b, h) in pairs:
+        e32 = (rel_err(y[b, :, h, :], ref32[(b, h)][0]), rel_err(hT[b, h], ref32[(b, h)][1]))
+        e16 = (rel_err(y[b, :, h, :], ref16[(b, h)][0]), rel_err(hT[b, h], ref16[(b, h)][1]))
+        log(f"    ({b}, {h}) vs pre-rounding {e32[0]:.2e} {e32[1]:.2e}; "
+            f"vs rounded {e16[0]:.2e} {e16[1]:.2e}")
+        assert max(e32) <= TOL_BF16 and e16[0] <= yb and e16[1] <= hb, ((b, h), e32, e16)
 
 
 def test_config2_long_sampled():
