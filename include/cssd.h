@@ -33,7 +33,10 @@
  *    memory from the host.  Launch failures return CSSD_ERR_HIP.  No C++
  *    exception crosses this boundary.
  *  - Supported sizes of the scan entry points (cssd_forward, cssd_backward,
- *    cssd_step*): headdim D and dstate N in {16, 32, 64, 128}; chunk in
+ *    cssd_step*): headdim D and dstate N in {16, 32, 64, 128} (each kernel is
+ *    compiled per width; other multiples of 16 are not built: zero-padding x, B
+ *    and C to the next supported width gives the same y and, in the leading
+ *    block, the same state); chunk in
  *    {16, 32, 64, 128}; any seqlen >= 0 (a partial last chunk is masked inside
  *    the kernels, nothing is padded in memory); batch, nheads >= 0, with
  *    batch*seqlen*nheads*max(D,N) < 2^31 elements per plane and, for
