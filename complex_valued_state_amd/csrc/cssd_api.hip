@@ -4,6 +4,7 @@
 // memory; every kernel is enqueued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -53,9 +54,32 @@ hipEvent_t take_event(Profiler& p) {
     return e;
 }
 
+// CSSD_DEBUG_SYNC=1 in the environment (read once): after every launch the
+// stream is synchronised and an asynchronous error of the kernel is returned as
+// the launch's error, so a failing call names its kernel.  Off by default: the
+// library otherwise never synchronises.  Streams being captured are left alone.
+bool debug_sync() {
+    static const bool on = [] {
+        const char* v = std::getenv("CSSD_DEBUG_SYNC");
+        return v != nullptr && v[0] != '\0' && v[0] != '0';
+    }();
+    return on;
+}
+
+hipError_t after_launch(hipStream_t stream, hipError_t err) {
+    if (err != hipSuccess || !debug_sync()) return err;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return err;
+    const hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
 // Runs one launcher, bracketed by events while profiling is on.
 template <typename F>
-hipError_t timed(int kernel, hipStream_t stream, F&& launch) {
+hipError_t timed(int kernel, hipStream_t stream, F&& launch_fn) {
+    auto launch = [&] { return after_launch(stream, launch_fn()); };
     Profiler& p = prof();
     hipEvent_t e0 = nullptr, e1 = nullptr;
     bool on;

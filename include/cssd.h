@@ -54,6 +54,11 @@
  *  - The library keeps no per-call state and is safe to call from several host
  *    threads on different streams.  The optional profiler (cssd_profile_*)
  *    is process-wide and guarded by a lock.
+ *  - Debugging: with CSSD_DEBUG_SYNC=1 in the environment when the library is
+ *    first called, every entry point synchronises its stream after each kernel
+ *    it launches and returns CSSD_ERR_HIP as soon as one reports an error (a
+ *    stream being captured into a graph is not synchronised).  This is the one
+ *    exception to "never synchronises" and is off by default.
  */
 #ifndef CSSD_H
 #define CSSD_H

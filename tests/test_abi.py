@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.cssd_version() == 107
-    for st in range(5):
+    for st in range(6):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
 
