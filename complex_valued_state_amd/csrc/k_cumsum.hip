@@ -18,7 +18,8 @@
 // C = 128).  The scan runs in fp64 with wave shuffles: the imaginary part of a
 // 128-step chunk reaches thousands of radians, and every consumer later takes
 // differences of these sums, so they are kept exact to fp64 and stored as
-// fp64.  Exponentials are evaluated in fp64 and rounded once to fp32.
+// fp64.  The exponentials take the fp64 arguments to log2 units and to half a
+// turn, then the fp32 hardware exp2 / sin / cos.
 // Padded positions get a zero increment, so a partial last chunk's total equals
 // the sum over its valid positions and the final state never decays through
 // padding.
@@ -93,6 +94,14 @@ __global__ __launch_bounds__(256) void k_cumsum(const float* __restrict__ dt,
     tot_r = __shfl(tot_r, last_lane, 64);
     tot_i = __shfl(tot_i, last_lane, 64);
 
+    // exp of a complex fp64 log-decay, rounded to fp32: the argument is taken to
+    // log2 units and to a fraction of a turn in fp64, then the fp32 hardware
+    // exp2 / sin / cos (about one ulp each) finish it
+    auto cexp_f = [](double re, double im, float& out_re, float& out_im) {
+        double t = im * kInvTwoPi;
+        t -= rint(t);
+        cexp_scaled((float)(re * kLog2e), (float)t, out_re, out_im);
+    };
     const int64_t base = bh * (int64_t)nC * C + t0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -100,23 +109,20 @@ __global__ __launch_bounds__(256) void k_cumsum(const float* __restrict__ dt,
         if (l < C) {
             acs_re[base + l] = vr[j] * kLog2e;
             acs_im[base + l] = vi[j] * kInvTwoPi;
-            double sn, cs;
-            sincos(vi[j], &sn, &cs);
-            const double m = exp(vr[j]);
-            e_re[base + l] = (float)(m * cs);
-            e_im[base + l] = (float)(m * sn);
-            sincos(tot_i - vi[j], &sn, &cs);
-            const double mw = exp(tot_r - vr[j]);
-            w_re[base + l] = (float)(mw * cs);
-            w_im[base + l] = (float)(mw * sn);
+            float er, ei, wr, wi;
+            cexp_f(vr[j], vi[j], er, ei);
+            cexp_f(tot_r - vr[j], tot_i - vi[j], wr, wi);
+            e_re[base + l] = er;
+            e_im[base + l] = ei;
+            w_re[base + l] = wr;
+            w_im[base + l] = wi;
         }
     }
     if (lane == 0) {
-        double sn, cs;
-        sincos(tot_i, &sn, &cs);
-        const double m = exp(tot_r);
-        cd_re[bh * nC + c] = (float)(m * cs);
-        cd_im[bh * nC + c] = (float)(m * sn);
+        float dr, di;
+        cexp_f(tot_r, tot_i, dr, di);
+        cd_re[bh * nC + c] = dr;
+        cd_im[bh * nC + c] = di;
     }
 }
 
