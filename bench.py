@@ -46,10 +46,11 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 # source files that make up each kernel (besides the shared device/launch headers),
 # by the kernel's name stem as rocprofv3 reports it
 _SCAN_SRC = ("k_chunk_scan.h", "k_chunk_scan_lds.h", "k_chunk_scan_bf16.h", "k_chunk_scan_nb.h",
-             "k_chunk_scan.hip",
+             "k_chunk_scan_wide.h", "k_chunk_scan.hip",
              "k_chunk_scan_c16.hip", "k_chunk_scan_c32.hip", "k_chunk_scan_c64.hip",
              "k_chunk_scan_c128.hip")
 KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC, "k_chunk_scan_nb": _SCAN_SRC,
+              "k_chunk_scan_wide": _SCAN_SRC,
               "k_chunk_scan_bf16": _SCAN_SRC,
               "k_chunk_state": ("k_chunk_state.hip",), "k_state_pass": ("k_state_pass.hip",),
               "k_cumsum": ("k_cumsum.hip",), "k_step": ("k_step.hip",),
@@ -130,11 +131,13 @@ def born_flops(B, T, H, D):
 
 def chunk_scan_symbol(N, D, C, dtype):
     """The kernel the library launches for the chunk-scan step at this shape (the
-    rule of launch_chunk_scan_c: the n-blocked staged kernel for fp32 inputs at
-    C = 64, N = 128, D = 64; the LDS-staged kernel for fp32 inputs with C <= 64,
-    C*N <= 4096, D <= 64 and not (C = 64, D = 16)), as rocprofv3 names it."""
+    rule of launch_chunk_scan_c: the n-blocked staged kernels for fp32 inputs at
+    C = 64 or 128, N = 128, D = 64; the LDS-staged kernel for fp32 inputs with
+    C <= 64, C*N <= 4096, D <= 64 and not (C = 64, D = 16)), as rocprofv3 names it."""
     if dtype == "f32" and C == 64 and N == 128 and D == 64:
         return "k_chunk_scan_nb<64, 128, 64>"
+    if dtype == "f32" and C == 128 and N == 128 and D == 64:
+        return "k_chunk_scan_wide<128, 128, 64>"
     if dtype == "f32" and C <= 64 and C * N <= 4096 and D <= 64 and not (C == 64 and D == 16):
         return f"k_chunk_scan_lds<{C}, {N}, {D}>"
     return f"k_chunk_scan<cssd::In{'F32' if dtype == 'f32' else 'BF16'}, {C}, {N}, {D}>"

@@ -27,6 +27,7 @@
 
 #include "k_chunk_scan_lds.h"
 #include "k_chunk_scan_nb.h"
+#include "k_chunk_scan_wide.h"
 
 namespace cssd {
 
@@ -303,6 +304,9 @@ hipError_t launch_chunk_scan_c(const FwdArgs& f, hipStream_t s) {
     }
     if constexpr (C == 64) {
         if (f.N == 128 && f.D == 64) return launch_chunk_scan_nb<64, 128, 64>(f, s);
+    }
+    if constexpr (C == 128) {
+        if (f.N == 128 && f.D == 64) return launch_chunk_scan_wide<128, 128, 64>(f, s);
     }
     switch (f.N) {
         case 16: return launch_staged_d<C, 16>(f, s);

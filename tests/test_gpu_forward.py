@@ -63,6 +63,9 @@ SMALL = [
     (4, 130, 16, 64, 128, 64, True, True),   # 64 (b, h): the staged state scan at N = 128
     (8, 64, 9, 64, 128, 64, False, True),    # 72 (b, h), exactly one chunk
     (1, 777, 3, 64, 64, 128, True, True),    # 7 chunks of 128, ragged tail
+    # C = N = 128, D = 64 on the persistent kernel: 1,360 chunks, so every
+    # workgroup walks five or six chunks, ragged tail
+    (2, 2100, 40, 64, 128, 128, True, True),
     (2, 500, 1, 32, 64, 64, True, True),     # D = 32: one p pair per n tile
 ]
 
