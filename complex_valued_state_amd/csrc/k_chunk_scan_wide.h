@@ -8,11 +8,10 @@
 // [16 (w % 4), 16 (w % 4) + 16) of the four row tiles {h, 2 + h, 5 - h, 7 - h},
 // h = w / 4: both halves carry 18 causal tile products.  The state dimension n
 // is taken in eight blocks of 16.  For each block the chunk's C and B rows
-// restricted to it (32 KB) are staged in LDS by direct-to-LDS buffer loads
-// (16-byte pieces XOR-swizzled by the row) into three buffers, block k + 2
-// issued while block k is used (the third buffer is the start of the M region,
-// free until the last block); each wave loads its 16 x 16 tile of H_c for the
-// next block into registers.  Per block:
+// restricted to it (32 KB) and the block's rows of H_c (8 KB) are staged in LDS
+// by direct-to-LDS buffer loads (row pieces XOR-swizzled) into three buffers,
+// block k + 2 issued while block k is used (the third buffer is the start of the
+// M region, free until the last block).  Per block:
 //   Y_off += C[:, blk] H_c[blk, cols]            (the wave's four row tiles)
 //   G^T   += B[s tile, blk] C[l tile, blk]^T     (the wave's score tiles: 36
 //                                                 causal tiles, five for waves
@@ -20,17 +19,18 @@
 //                                                 two waves of a SIMD hold nine)
 // After the last block: Y_off times exp(acs[l]) per row, M = G . L (+ Dskip on
 // the diagonal) in registers and into a 72 KB LDS region, the wave's columns of
-// X into registers (half of them issued with the last block), Y_diag = M X, and
-// the stores.  The next chunk's first two blocks are staged while the M X
-// products run.  140 KB of LDS: one workgroup per CU.
+// X into registers (half of them issued with the last block), Y_diag = M X.  The
+// next chunk's first two blocks are staged while the M X products run, and this
+// chunk's outputs are stored during the next chunk's first block.  156 KB of
+// LDS: one workgroup per CU.
 #pragma once
 
 #include "k_chunk_scan_lds.h"
 
 namespace cssd {
 
-// s_waitcnt immediate for at most `vm` vector-memory and `lgkm` LDS operations
-// outstanding (gfx9 encoding; expcnt not waited on)
+// s_waitcnt immediate for at most `vm` vector-memory and `lgkm` LDS/scalar
+// operations outstanding (gfx9 encoding; expcnt not waited on)
 constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
     return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
 }
@@ -45,20 +45,25 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 
 template <int C, int N, int D>
 __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
-    constexpr int NB = 16;                  // n per staged block
-    constexpr int NBLK = N / NB;            // blocks per chunk
-    constexpr int NLT = C / 16;             // row tiles per chunk
+    constexpr int NB = 16;                   // n per staged block
+    constexpr int NBLK = N / NB;             // blocks per chunk
+    constexpr int NLT = C / 16;              // row tiles per chunk
     constexpr int NP = NLT * (NLT + 1) / 2;  // causal tiles, lt-major
-    constexpr int MQ = 5;                   // most score tiles one wave owns
-    constexpr int PL = C * NB;              // floats of one staged block plane
+    constexpr int MQ = 5;                    // most score tiles one wave owns
+    constexpr int PL = C * NB;               // floats of one staged C or B plane
+    constexpr int HP = NB * D;               // floats of one staged H plane
+    constexpr int BUF = 4 * PL + 2 * HP;     // floats of one block buffer
+    // direct-to-LDS loads per wave for one block: four C/B pieces and one H piece
+    constexpr int LPB = 5;
     static_assert(C == 128 && N == 128 && D == 64, "built for C = N = 128, D = 64");
-    static_assert(PL == 8 * 256, "a block plane is one 1 KB load per wave");
+    static_assert(PL == 8 * 256 && HP == 4 * 256, "one 1 KB load per wave and plane");
     static_assert(NP == 36 && 4 * 5 + 4 * 4 == NP, "score tiles: five for waves 0-3, four for 4-7");
+    static_assert(BUF <= NP * 512, "the third block buffer must fit in the M region");
     // separate LDS objects, so that the compiler's wait for pending direct-to-LDS
     // writes before an LDS read covers only the object read
-    __shared__ floatx4 lds_s0[4 * PL / 4];  // block buffer 0: C re, C im, B re, B im
-    __shared__ floatx4 lds_s1[4 * PL / 4];  // block buffer 1
-    __shared__ floatx4 lds_m4[NP * 512 / 4];  // the M tiles (re, im planes of 1 KB)
+    __shared__ floatx4 lds_s0[BUF / 4];       // block buffer 0: C re, C im, B re, B im, H re, H im
+    __shared__ floatx4 lds_s1[BUF / 4];       // block buffer 1
+    __shared__ floatx4 lds_m4[NP * 512 / 4];  // the M tiles (re, im planes of 1 KB); buffer 2
     __shared__ floatx4 lds_a4[4 * 256 / 4];   // acs re, acs im (fp64), e re, e im
     float* const ls0 = reinterpret_cast<float*>(lds_s0);
     float* const ls1 = reinterpret_cast<float*>(lds_s1);
@@ -68,6 +73,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
     const double* const lacs_i = reinterpret_cast<const double*>(lda + 256);
     const float* const le_r = lda + 512;
     const float* const le_i = lda + 768;
+    // block k of a chunk lives in buffer k % 3
+    auto buf_of = [&](int k) -> float* { return k % 3 == 0 ? ls0 : (k % 3 == 1 ? ls1 : ldm); };
 
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
@@ -130,10 +137,13 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
     // 256 distinct bytes modulo 256, so the reads are free of bank conflicts
     // whether a pass serves 8 or 16 lanes.
     auto swz = [](int row, int c) { return c ^ ((((row & 15) >> 2) ^ ((row & 15) >> 1)) & 3); };
-    // block blk of a chunk's C and B rows: wave w loads 1 KB piece-block w of each
-    // of the four planes; lane i's 16 bytes land at base + 16 i
-    // (the per-lane byte offset is one VGPR; the block part, which never moves a
-    // read past the row it starts in, goes in the instruction's scalar offset)
+    // block blk of a chunk: wave w loads 1 KB piece-block w of each of the four C/B
+    // planes, and piece w % 4 of H plane w / 4 (H_c is stored in MFMA-fragment
+    // order, tile (n tile, column tile) at (n tile * D/16 + column tile) * 1 KB, so
+    // block blk's 16 rows of H_c are 4 KB per plane).  Lane i's 16 bytes land at
+    // the instruction's base + 16 i.  The per-lane byte offsets are one VGPR each;
+    // the block and piece parts, which never move a read past the row or tile it
+    // starts in, go in the instructions' scalar offsets.
     const uint32_t stage_voff = [&] {
         const int u = w * 64 + lane;  // physical 16-byte piece within a plane
         const int row = u >> 2, pc = u & 3;
@@ -147,6 +157,11 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(dst + p * PL + w * 256), 16,
                                                      stage_voff, NB * blk * 4, 0, 0);
         }
+        const float* const hsrc = (w >> 2) ? a.hc_im : a.hc_re;
+        const BufRes rh = make_buf(hsrc + x.chunk * (int64_t)N * D, N * D * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rh, (LdsPtr)(dst + 4 * PL + (w >> 2) * HP + (w & 3) * 256), 16, 16 * lane,
+            (blk * HP + (w & 3) * 256) * 4, 0, 0);
     };
     // the chunk's fp64 cumsums and exp(acs): waves 0-3 one 1 KB slot each
     auto stage_aux = [&](const Ctx& x) {
@@ -159,16 +174,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
                                                      (LdsPtr)(lda + 256 * w), 16, 16 * lane, 0, 0, 0);
         }
     };
-    // H_c[n = 16 blk + 4 g + e][16 ct + li] (fragment order)
-    auto load_h = [&](const Ctx& x, int blk, floatx4& hr, floatx4& hi) {
-        const BufRes rh_r = make_buf(a.hc_re + x.chunk * (int64_t)N * D, N * D * 4);
-        const BufRes rh_i = make_buf(a.hc_im + x.chunk * (int64_t)N * D, N * D * 4);
-        const int tile = blk * (D / 16) + ct;
-        hr = __builtin_bit_cast(floatx4,
-                                __builtin_amdgcn_raw_buffer_load_b128(rh_r, 16 * lane, tile * 1024, 0));
-        hi = __builtin_bit_cast(floatx4,
-                                __builtin_amdgcn_raw_buffer_load_b128(rh_i, 16 * lane, tile * 1024, 0));
-    };
     // operand rows 16 t + li of a staged plane, this lane's 16-byte piece g; the
     // swizzle depends on the row only through li, so one lane offset serves every
     // tile (kept opaque per block, so that the compiler forms the few addresses
@@ -177,19 +182,48 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
     auto row4 = [&](const float* plane, int t, int lo) -> floatx4 {
         return *reinterpret_cast<const floatx4*>(plane + t * 16 * NB + lo);
     };
-
-    // block k of a chunk lives in buffer k % 3; the third buffer is the first
-    // 32 KB of the M region, which the M tiles need only after the last block
-    auto buf_of = [&](int k) -> float* { return k % 3 == 0 ? ls0 : (k % 3 == 1 ? ls1 : ldm); };
+    // the skip weight through the scalar cache (uniform, read-only)
+    auto skip_of = [&](int h) -> float {
+        typedef const __attribute__((address_space(4))) float* ConstF;
+        return a.dskip != nullptr ? ((ConstF)a.dskip)[h] : 0.f;
+    };
+    // per-lane byte offset of (row 4 g, column 16 ct + li) in a [row][D] plane
+    const uint32_t dvo = ((uint32_t)(4 * g) * sD + 16 * ct + li) * 4;
 
     int64_t chunk = blockIdx.x;
     if (chunk >= a.nchunks) return;  // workgroup-uniform
     Ctx cur = ctx_of(chunk);
-    floatx4 hcur_r, hcur_i;
-    load_h(cur, 0, hcur_r, hcur_i);
     stage(cur, 0, ls0);
     stage(cur, 1, ls1);
+    // the previous chunk's outputs, stored during the next chunk's first block:
+    // register r <-> row 16 rows[i] + 4 g + r, column 16 ct + li
+    float yp_r[4][4], yp_i[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yp_r[i][r] = yp_i[i][r] = 0.f;
+    Ctx prev = cur;
     bool first = true;
+    // the stores of the previous chunk's outputs (before the first chunk, the same
+    // 32 stores per wave go through views of extent 0 and are dropped, so that the
+    // count of memory operations in flight is the same on every pass; padded rows
+    // of a partial chunk are dropped likewise)
+    auto store_prev = [&]() {
+        const uint32_t ext = first ? 0u : prev.extD * 4;
+        const BufRes ry_r = make_buf(a.y_re + prev.row0 * D, ext);
+        const BufRes ry_i = make_buf(a.y_im + prev.row0 * D, ext);
+        uint32_t vo0 = dvo;
+        asm volatile("" : "+v"(vo0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t vo = vo0 + (uint32_t)(rows[i] * 16 + r) * sD * 4;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yp_r[i][r]), ry_r, vo, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yp_i[i][r]), ry_i, vo, 0, 0);
+            }
+        }
+    };
 
     for (;;) {
         CTile acc[4];  // Y_off, then y
@@ -199,57 +233,61 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
 #pragma unroll
         for (int j = 0; j < MQ; ++j) ctile_zero(gt[j]);
         float xr[NLT][4], xi[NLT][4];  // the wave's columns of X (loaded from block 7 on)
-        const BufRes rx_r = make_buf(static_cast<const float*>(a.x_re) + cur.row0 * D, cur.extD * 4);
-        const BufRes rx_i = make_buf(static_cast<const float*>(a.x_im) + cur.row0 * D, cur.extD * 4);
-        uint32_t xvo = 0;
         // X[16 st + 4 g + r][16 ct + li] for st in [st0, st1)
         auto load_x = [&](int st0, int st1) {
+            const BufRes rx_r = make_buf(static_cast<const float*>(a.x_re) + cur.row0 * D, cur.extD * 4);
+            const BufRes rx_i = make_buf(static_cast<const float*>(a.x_im) + cur.row0 * D, cur.extD * 4);
+            uint32_t vo0 = dvo;
+            asm volatile("" : "+v"(vo0));
 #pragma unroll
             for (int st = st0; st < st1; ++st)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const uint32_t vo = xvo + (uint32_t)(st * 16 + r) * sD * 4;
+                    const uint32_t vo = vo0 + (uint32_t)(st * 16 + r) * sD * 4;
                     xr[st][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx_r, vo, 0, 0));
                     xi[st][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx_i, vo, 0, 0));
                 }
         };
 
-        // Loads in flight at the top of block k, in issue order: H tile k, then the
-        // C/B rows of block k + 1 (4 per wave) -- and before the first block of a
-        // chunk other than the first, the previous chunk's 32 stores after those.
-        // Block k's rows were issued before H tile k, so waiting down to that many
-        // outstanding completes both.
+        // Vector-memory operations of this wave in flight at the top of block k, in
+        // issue order, after block k's staged loads:
+        //   k = 0: block 1 (LPB)
+        //   k = 1: the cumsum tables (waves 0-3, one), block 2 (LPB), the previous
+        //          chunk's 32 stores
+        //   k = 2: the stores, block 3 (LPB)
+        //   k = 3..6: block k + 1 (LPB)
+        //   k = 7: nothing
+        // Waiting down to that count completes block k (every wave's part of it,
+        // after the barrier).
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk) {
-            if (blk == 0 && !first)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(4 + 32, 0));
+            if (blk == 1 || blk == 2)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(LPB + 32, 0));
             else if (blk + 1 < NBLK)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(4, 0));
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(LPB, 0));
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 0));
             barrier_no_fence();  // block blk is in; every wave is done with block blk - 1
             const float* const bc = buf_of(blk);
             int lo = lane_off;
             asm volatile("" : "+v"(lo));
-            floatx4 hnxt_r, hnxt_i;
             if (blk == 0) stage_aux(cur);
-            if (blk + 1 < NBLK) load_h(cur, blk + 1, hnxt_r, hnxt_i);
             if (blk + 2 < NBLK) stage(cur, blk + 2, buf_of(blk + 2));
-            if (blk == NBLK - 1) {
-                xvo = ((uint32_t)(4 * g) * sD + 16 * ct + li) * 4;
-                asm volatile("" : "+v"(xvo));
-                load_x(0, NLT / 2);
-            }
+            if (blk == 0) store_prev();
+            if (blk == NBLK - 1) load_x(0, NLT / 2);
             // Y_off += C[:, blk] H_c[blk, cols]
             {
-                const floatx4 hs = hcur_r + hcur_i;
+                const floatx4 hr = *reinterpret_cast<const floatx4*>(bc + 4 * PL + ct * 256 + 4 * lane);
+                const floatx4 hi =
+                    *reinterpret_cast<const floatx4*>(bc + 4 * PL + HP + ct * 256 + 4 * lane);
+                const floatx4 hs = hr + hi;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const floatx4 cr = row4(bc, rows[i], lo), ci = row4(bc + PL, rows[i], lo);
                     const floatx4 cs = cr + ci;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        ctile_mac(acc[i], cr[e], ci[e], cs[e], hcur_r[e], hcur_i[e], hs[e]);
+                        ctile_mac(acc[i], cr[e], ci[e], cs[e], hr[e], hi[e], hs[e]);
                 }
             }
             // G^T += B[s tile, blk] C[l tile, blk]^T
@@ -264,10 +302,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
                     for (int e = 0; e < 4; ++e)
                         ctile_mac(gt[j], br[e], bi[e], bs[e], cr[e], ci[e], cs[e]);
                 }
-            }
-            if (blk + 1 < NBLK) {
-                hcur_r = hnxt_r;
-                hcur_i = hnxt_i;
             }
         }
 
@@ -289,9 +323,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
             }
         }
         // M = G . L (+ Dskip on the diagonal) into LDS; register r <-> (l = l0 + li,
-        // s = s0 + 4 g + r).  The M region was last read by the previous chunk's
-        // products, before eight barriers.
-        const float dk = a.dskip != nullptr ? a.dskip[cur.h] : 0.f;
+        // s = s0 + 4 g + r).  The M region was last read as block 5's buffer.
+        const float dk = skip_of(cur.h);
 #pragma unroll
         for (int j = 0; j < MQ; ++j) {
             if (j < nq) {
@@ -320,18 +353,18 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
             }
         }
         load_x(NLT / 2, NLT);
-        // the next chunk's first two blocks and H tile, while the products below run
-        // (every wave is done with buffer 0, block 6's; buffer 1 is block 7's)
+        // the next chunk's first two blocks, while the products below run (block 0
+        // goes to buffer 0, block 6's; block 1 to buffer 1 once every wave is done
+        // with block 7)
         const int64_t next = chunk + gridDim.x;
         const bool more = next < a.nchunks;  // workgroup-uniform
         Ctx nx = cur;
         if (more) {
             nx = ctx_of(next);
-            load_h(nx, 0, hcur_r, hcur_i);
             stage(nx, 0, ls0);
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(63, 0));
-        barrier_no_fence();  // the M tiles are in; every wave is done with block 7's buffer
+        barrier_no_fence();  // the M tiles are in
         if (more) stage(nx, 1, ls1);
         // Y_diag: y[lt] += M(lt, st) X[st rows, this wave's columns]
 #pragma unroll
@@ -353,28 +386,20 @@ __global__ __launch_bounds__(512) void k_chunk_scan_wide(ScanArgs a) {
                 }
             }
         }
-        // stores (32 per wave); register r <-> row l = 16 lt + 4 g + r (padded rows
-        // are dropped)
-        {
-            const BufRes ry_r = make_buf(a.y_re + cur.row0 * D, cur.extD * 4);
-            const BufRes ry_i = make_buf(a.y_im + cur.row0 * D, cur.extD * 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t vo = xvo + (uint32_t)(rows[i] * 16 + r) * sD * 4;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ctile_re(acc[i], r)), ry_r,
-                                                          vo, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ctile_im(acc[i], r)), ry_i,
-                                                          vo, 0, 0);
-                }
+            for (int r = 0; r < 4; ++r) {
+                yp_r[i][r] = ctile_re(acc[i], r);
+                yp_i[i][r] = ctile_im(acc[i], r);
             }
-        }
+        prev = cur;
+        first = false;
         if (!more) break;
         chunk = next;
         cur = nx;
-        first = false;
     }
+    store_prev();  // the last chunk's outputs
 }
 
 template <int C, int N, int D>
