@@ -228,6 +228,193 @@ __global__ __launch_bounds__(256) void k_state_scan(
     }
 }
 
+// The same scan with the chunks dealt to four waves, for problems whose (b, h)
+// count leaves the plain form with about one wave per SIMD or fewer (each wave
+// there waits on its own operand stream with nothing to overlap).  A workgroup
+// of four waves owns one unit (PW tiles) of one (b, h).  In round r wave k
+// forms S_c of chunk c = 4 r + k with the plain form's k-step loop (operands in
+// a register ring that runs on to chunk c + 4); the four S_c meet in LDS, and
+// every wave then runs the round's four steps H_{c+1} = cd[c] H_c + S_c on its
+// copy of the carried state, storing the carry-in of its own chunk.  The state
+// stays in registers and the four copies stay identical (the same operations
+// in the same order).  The workgroups of one (b, h) share an XCD as above.
+template <typename In, int C, int PW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_state_scan_cp(
+    const typename In::T* __restrict__ x_re, const typename In::T* __restrict__ x_im,
+    const typename In::T* __restrict__ b_re, const typename In::T* __restrict__ b_im,
+    const float* __restrict__ w_re, const float* __restrict__ w_im,
+    const float* __restrict__ cd_re, const float* __restrict__ cd_im,
+    const float* __restrict__ h0_re, const float* __restrict__ h0_im, float* __restrict__ st_re,
+    float* __restrict__ st_im, float* __restrict__ hT_re, float* __restrict__ hT_im, int64_t T,
+    int H, int N, int D, int nC, int64_t nbh) {
+    constexpr int KJ = C / 4;  // MFMA k-steps per chunk
+    constexpr int DIST = ScanTune<In>::dist;
+    constexpr int RING = DIST < KJ ? DIST : KJ;
+    constexpr int WPL = (C + 63) / 64;
+    constexpr int SPLIT = 4;  // chunks per round = waves per workgroup
+    static_assert(!(PW == 2 && ScanTune<In>::pair), "paired X columns are not used here");
+    __shared__ float lds_w[SPLIT][2 * C];                // per wave: w of its current chunk
+    __shared__ floatx4 lds_s[2][SPLIT][2 * PW][64];      // [round parity][wave][tile re/im][lane]
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int wv = wave_id();
+    const int NK = N / 16, PT = D / 16, units = NK * (PT / PW);
+    const int64_t xcd = blockIdx.x % kScanXcds, y = blockIdx.x / kScanXcds;
+    const int64_t bh = (y / units) * kScanXcds + xcd;
+    const int unit = (int)(y % units);
+    if (bh >= nbh) return;  // workgroup-uniform
+    const int nt = unit / (PT / PW), pt0 = (unit % (PT / PW)) * PW;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const uint32_t sN = (uint32_t)H * N, sD = (uint32_t)H * D;
+    float* const lw = lds_w[wv];
+
+    // carried state, tile q register r <-> (n = 16 nt + 4g + r, p = 16 (pt0 + q) + li)
+    const int64_t sbase = (bh * N + nt * 16 + 4 * g) * (int64_t)D;
+    float hr[PW][4], hi[PW][4];
+#pragma unroll
+    for (int q = 0; q < PW; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hr[q][r] = h0_re != nullptr ? h0_re[sbase + r * D + 16 * (pt0 + q) + li] : 0.f;
+            hi[q][r] = h0_im != nullptr ? h0_im[sbase + r * D + 16 * (pt0 + q) + li] : 0.f;
+        }
+
+    struct Ops {
+        float br, bi, xr[PW], xi[PW];
+    };
+    const uint32_t lane_b = (uint32_t)(KJ * g) * sN + nt * 16 + li;
+    const uint32_t lane_x = (uint32_t)(KJ * g) * sD + pt0 * 16 + li;
+    auto load = [&](int c, int j, Ops& o) {
+        const int64_t t0 = (int64_t)c * C;
+        const int valid = (int)min<int64_t>((int64_t)C, T - t0);
+        const int64_t row0 = (b * T + t0) * H + h;
+        const uint32_t extN = (uint32_t)(valid - 1) * sN + N, extD = (uint32_t)(valid - 1) * sD + D;
+        const BufRes rb_r = make_buf(b_re + row0 * N, extN * sizeof(typename In::T));
+        const BufRes rb_i = make_buf(b_im + row0 * N, extN * sizeof(typename In::T));
+        const BufRes rx_r = make_buf(x_re + row0 * D, extD * sizeof(typename In::T));
+        const BufRes rx_i = make_buf(x_im + row0 * D, extD * sizeof(typename In::T));
+        // time l = KJ g + j: the lane parts of the offsets are opaque per call, so
+        // that the compiler adds the step's row offset here instead of holding
+        // every step's offsets in registers across the unrolled loop
+        uint32_t eb = lane_b, ex = lane_x;
+        asm volatile("" : "+v"(eb), "+v"(ex));
+        const uint32_t db = (uint32_t)j * sN, dx = (uint32_t)j * sD;
+        o.br = In::bload1(rb_r, eb + db);
+        o.bi = In::bload1(rb_i, eb + db);
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            o.xr[q] = In::bload1(rx_r, ex + dx + q * 16);
+            o.xi[q] = In::bload1(rx_i, ex + dx + q * 16);
+        }
+    };
+    float wn_r[WPL], wn_i[WPL];
+    auto load_w = [&](int c) {
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            const int pos = lane + 64 * k;
+            const int64_t at = bh * (int64_t)nC * C + (int64_t)c * C + pos;
+            wn_r[k] = pos < C ? w_re[at] : 0.f;
+            wn_i[k] = pos < C ? w_im[at] : 0.f;
+        }
+    };
+
+    Ops ring[RING];
+    if (wv < nC) {
+#pragma unroll
+        for (int j = 0; j < RING; ++j) load(wv, j, ring[j]);
+        load_w(wv);
+    }
+    int64_t slot[PW];
+#pragma unroll
+    for (int q = 0; q < PW; ++q) slot[q] = ((int64_t)nt * PT + pt0 + q) * 256 + 4 * lane;
+
+    for (int r0 = 0; r0 < nC; r0 += SPLIT) {
+        const int par = (r0 / SPLIT) & 1;
+        const int c = r0 + wv;  // this wave's chunk
+        CTile acc[PW];
+#pragma unroll
+        for (int q = 0; q < PW; ++q) ctile_zero(acc[q]);
+        if (c < nC) {  // wave-uniform
+#pragma unroll
+            for (int k = 0; k < WPL; ++k) {
+                const int pos = lane + 64 * k;
+                if (pos < C) {
+                    lw[pos] = wn_r[k];
+                    lw[C + pos] = wn_i[k];
+                }
+            }
+            const int cn = c + SPLIT;  // this wave's next chunk
+            if (cn < nC) load_w(cn);
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const Ops o = ring[j % RING];
+                const int jn = j + RING;
+                if (jn < KJ)
+                    load(c, jn, ring[j % RING]);
+                else if (cn < nC)  // wave-uniform
+                    load(cn, jn - KJ, ring[j % RING]);
+                __builtin_amdgcn_sched_barrier(0);
+                const float wr = lw[KJ * g + j], wi = lw[C + KJ * g + j];
+                const float pr = wr * o.br - wi * o.bi;  // (w B)[l, n]
+                const float pi = wr * o.bi + wi * o.br;
+                const float ps = pr + pi;
+#pragma unroll
+                for (int q = 0; q < PW; ++q)
+                    ctile_mac(acc[q], pr, pi, ps, o.xr[q], o.xi[q], o.xr[q] + o.xi[q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            floatx4 sr, si;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sr[r] = ctile_re(acc[q], r);
+                si[r] = ctile_im(acc[q], r);
+            }
+            lds_s[par][wv][2 * q][lane] = sr;
+            lds_s[par][wv][2 * q + 1][lane] = si;
+        }
+        __syncthreads();  // the round's S_c are in (and the other parity's are read)
+        // the round's chunk-to-chunk steps, the same on every wave
+        for (int k = 0; k < SPLIT; ++k) {
+            const int ck = r0 + k;
+            if (ck >= nC) break;  // workgroup-uniform
+            if (k == wv) {  // carry-in state of this wave's chunk
+                const int64_t off = (bh * nC + ck) * (int64_t)N * D;
+#pragma unroll
+                for (int q = 0; q < PW; ++q) {
+                    *reinterpret_cast<floatx4*>(st_re + off + slot[q]) =
+                        floatx4{hr[q][0], hr[q][1], hr[q][2], hr[q][3]};
+                    *reinterpret_cast<floatx4*>(st_im + off + slot[q]) =
+                        floatx4{hi[q][0], hi[q][1], hi[q][2], hi[q][3]};
+                }
+            }
+            const float dr = cd_re[bh * nC + ck], di = cd_im[bh * nC + ck];
+#pragma unroll
+            for (int q = 0; q < PW; ++q) {
+                const floatx4 sr = lds_s[par][k][2 * q][lane], si = lds_s[par][k][2 * q + 1][lane];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float nr = dr * hr[q][r] - di * hi[q][r] + sr[r];
+                    const float ni = dr * hi[q][r] + di * hr[q][r] + si[r];
+                    hr[q][r] = nr;
+                    hi[q][r] = ni;
+                }
+            }
+        }
+    }
+    if (hT_re != nullptr && wv == 0) {
+#pragma unroll
+        for (int q = 0; q < PW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hT_re[sbase + r * D + 16 * (pt0 + q) + li] = hr[q][r];
+                hT_im[sbase + r * D + 16 * (pt0 + q) + li] = hi[q][r];
+            }
+    }
+}
+
 // The same scan for fp32 inputs at N = D = 64, C = 64, with the B and X rows
 // staged through LDS.  A workgroup (4 waves) owns half of one (b, h)'s state:
 // rows n in [32 h2, 32 h2 + 32) and every column p; wave w owns the tiles
@@ -756,6 +943,19 @@ static hipError_t launch_scan_pw(const FwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int C>
+static hipError_t launch_scan_cp(const FwdArgs& a, hipStream_t s) {
+    const int units = (int)((a.N / 16) * (a.D / 16 / 2));
+    const int64_t nbh = a.B * a.H;
+    const int64_t blocks = kScanXcds * ((nbh + kScanXcds - 1) / kScanXcds) * units;
+    hipLaunchKernelGGL((k_state_scan_cp<InF32, C, 2>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const float*>(a.x_re), static_cast<const float*>(a.x_im),
+                       static_cast<const float*>(a.b_re), static_cast<const float*>(a.b_im),
+                       a.w_re, a.w_im, a.cd_re, a.cd_im, a.h0_re, a.h0_im, a.st_re, a.st_im,
+                       a.hT_re, a.hT_im, a.T, (int)a.H, (int)a.N, (int)a.D, (int)a.nC, nbh);
+    return hipGetLastError();
+}
+
 // Two tiles per wave where D allows (measured at B8 T2048 H48 N64 D64 C64: one
 // tile per wave 0.52 ms, two 0.38 ms, against 0.41 ms for the separate
 // chunk-state and state-pass kernels).
@@ -783,6 +983,11 @@ hipError_t launch_state_scan(const FwdArgs& a, hipStream_t s) {
     // 0.82 ms staged against 0.71 ms)
     if (a.in_dtype == 0 && a.D == 64 && a.N == 128 && a.C == 64 && a.B * a.H * 4 >= 256)
         return launch_scan_lds<64, 128>(a, s);
+    // the chunks dealt to four waves where the plain form would have fewer waves
+    // than the chip has SIMDs and each sequence has several rounds of chunks
+    if (a.in_dtype == 0 && a.D >= 32 && a.C == 128 && a.nC >= 8 &&
+        a.B * a.H * (a.N / 16) * (a.D / 32) < 1024)
+        return launch_scan_cp<128>(a, s);
     return a.in_dtype == 1 ? launch_scan_in<InBF16>(a, s) : launch_scan_in<InF32>(a, s);
 }
 

@@ -66,6 +66,12 @@ SMALL = [
     # C = N = 128, D = 64 on the persistent kernel: 1,360 chunks, so every
     # workgroup walks five or six chunks, ragged tail
     (2, 2100, 40, 64, 128, 128, True, True),
+    # few sequences of many 128-chunks: the state scan deals each sequence's
+    # chunks to four waves in rounds of four (17, 11 and 10 chunks: partial
+    # last rounds of one, three and two chunks)
+    (1, 2100, 3, 64, 128, 128, True, True),
+    (2, 1400, 2, 64, 64, 128, True, False),
+    (1, 1200, 2, 32, 128, 128, False, True),
     (2, 500, 1, 32, 64, 64, True, True),     # D = 32: one p pair per n tile
 ]
 
