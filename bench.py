@@ -597,10 +597,29 @@ def _rows(inp, bs):
                             c(inp.h0_re), c(inp.h0_im), inp.in_dtype, inp.name)
 
 
-# the forward workloads --only can time alone: name -> (generator function, argument)
+def born_entry(steps, dev, bf16):
+    """Causal Born attention at B256 T1024 H16 D16 (fp32 or bf16 inputs): tokens/s and
+    the matrix-core roofline of the attention kernel."""
+    bb, bt, bhd, bd = 256, 1024, 16, 16
+    ms, kms = time_born(bb, bt, bhd, bd, max(3, steps // 2), 2, dev, bf16=bf16)
+    fl = born_flops(bb, bt, bhd, bd)
+    kern = "k_born_bf16" if bf16 else "k_born"
+    peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    return {
+        "tokens_per_s": round(bb * bt / (ms * 1e-3), 1), "ms_per_call": round(ms, 5),
+        "roofline": {"bound": "mfma", "kernel": kern, "symbol": f"{kern}<{bd}>",
+                     "traffic": load_traffic(f"{kern}<{bd}>"),
+                     "achieved": round(fl / (kms * 1e-3) / 1e12, 2),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(fl / (kms * 1e-3) / 1e12 / peak, 4),
+                     "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(kms, 5)}}
+
+
+# the workloads --only can time alone: name -> (generator function, argument) for the
+# forward ones; the Born attention ones take no inputs from here
 ONLY = {"forward_f32": ("config1", "f32"), "forward_bf16": ("config1", "bf16"),
         "forward_tiny": ("config0", None), "forward_long": ("config2", None),
-        "forward_pam": ("config3", "re")}
+        "forward_pam": ("config3", "re"), "born_f32": None, "born_bf16": None}
 
 
 def only_inputs(name):
@@ -655,7 +674,10 @@ def main():
     cssd.load_library()
     if args.only:
         progress(f"timing {args.only} alone")
-        e = forward_entry(only_inputs(args.only), args.steps, args.warmup, dev)
+        if args.only.startswith("born_"):
+            e = born_entry(args.steps, dev, bf16=args.only == "born_bf16")
+        else:
+            e = forward_entry(only_inputs(args.only), args.steps, args.warmup, dev)
         print(json.dumps({"workload": args.only, **e}), flush=True)
         return
 
@@ -761,27 +783,9 @@ def main():
                          "frac": round(pbytes / (pout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes_per_launch": pbytes, "avg_launch_ms": round(pout, 5)}}
         progress("timing causal Born attention")
-        bb, bt, bhd, bd = 256, 1024, 16, 16
-        bms, bkms = time_born(bb, bt, bhd, bd, max(3, args.steps // 2), 2, dev)
-        bfl = born_flops(bb, bt, bhd, bd)
-        extra["born_attention_B256_T1024_H16_D16_f32"] = {
-            "tokens_per_s": round(bb * bt / (bms * 1e-3), 1), "ms_per_call": round(bms, 5),
-            "roofline": {"bound": "mfma", "kernel": "k_born", "symbol": f"k_born<{bd}>",
-                         "traffic": load_traffic(f"k_born<{bd}>"),
-                         "achieved": round(bfl / (bkms * 1e-3) / 1e12, 2),
-                         "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(bfl / (bkms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
-                         "algorithmic_flops_per_launch": bfl, "avg_launch_ms": round(bkms, 5)}}
+        extra["born_attention_B256_T1024_H16_D16_f32"] = born_entry(args.steps, dev, bf16=False)
         progress("timing causal Born attention with bf16 inputs")
-        b16ms, b16kms = time_born(bb, bt, bhd, bd, max(3, args.steps // 2), 2, dev, bf16=True)
-        extra["born_attention_B256_T1024_H16_D16_bf16_inputs"] = {
-            "tokens_per_s": round(bb * bt / (b16ms * 1e-3), 1), "ms_per_call": round(b16ms, 5),
-            "roofline": {"bound": "mfma", "kernel": "k_born_bf16", "symbol": f"k_born_bf16<{bd}>",
-                         "traffic": load_traffic(f"k_born_bf16<{bd}>"),
-                         "achieved": round(bfl / (b16kms * 1e-3) / 1e12, 2),
-                         "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(bfl / (b16kms * 1e-3) / 1e12 / PEAK_BF16_MFMA_TFLOPS, 4),
-                         "algorithmic_flops_per_launch": bfl, "avg_launch_ms": round(b16kms, 5)}}
+        extra["born_attention_B256_T1024_H16_D16_bf16_inputs"] = born_entry(args.steps, dev, bf16=True)
     out["extra"] = extra
     if not args.no_cpu_baseline:
         progress("timing the fp64 oracle on the host cores")

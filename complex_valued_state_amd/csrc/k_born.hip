@@ -219,13 +219,16 @@ __global__ __launch_bounds__(256) void k_born(BornArgs a) {
 //  * Weighted sum: the 32-key step s pairs key tiles 2s and 2s + 1: slot j < 4
 //    is key 32s + 4g + j, slot j >= 4 is key 32s + 16 + 4g + j - 4, which is
 //    where the score tiles leave them, so the scores are packed to bf16 in
-//    place.  Values sit in LDS transposed ([column][key]), so the B operand is
-//    two 8-byte reads.  The normaliser sums the rounded weights (one more
+//    place.  Values sit in LDS as rows ([key][vr | vi]) and reach the B operand
+//    through two transposing LDS reads (ds_read_b64_tr_b16: within each group of
+//    16 lanes, lane 4q + x receives element x of the 8-byte pieces that lanes q,
+//    4 + q, 8 + q and 12 + q point at).  The normaliser sums the rounded weights (one more
 //    product, against a column of ones), so the output is an exact convex
 //    combination of the values with those weights.
 // ----------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -239,22 +242,31 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 
 }  // namespace
 
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3 : 1))) void k_born_bf16(
+    BornArgs a) {
     constexpr int NM = D / 16;          // MFMA steps over the features (per part)
     constexpr int KS = 4 * D + 16;      // LDS key row stride (bytes): D/4 quads of 16 B, padded
-    constexpr int VS = 2 * kBornBlock + 16;  // LDS value column stride (bytes): 64 keys, padded
+    constexpr int VS = 4 * D + 16;      // LDS value row stride (bytes): [vr | vi] of one key, padded
     constexpr int NCT = 2 * D / 16;     // 16-column tiles of [vr | vi]
     constexpr int KQ = kBornBlock * D / 4 / 256;   // key quads staged per thread
     constexpr int VQ = kBornBlock * 2 * D / 8 / 256;  // 8-value chunks of V staged per thread
+    // key blocks in flight in registers: a block's work shrinks with D, so small D
+    // needs more of them to cover the global-load latency
+    constexpr int RD = D == 16 ? 2 : 1;
     // key rows twice: quads [re, im] (A of the real part) and [im, re] (A of the imaginary part)
     __shared__ __align__(16) unsigned char lds_k[2][2][kBornBlock * KS];
-    __shared__ __align__(16) unsigned char lds_v[2][2 * D * VS];
+    __shared__ __align__(16) unsigned char lds_v[2][kBornBlock * VS];
 
     int64_t bh, pair;
     if (!born_item(a, blockIdx.x, bh, pair)) return;  // workgroup-uniform
     const int64_t b = bh / a.H, h = bh % a.H;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int64_t rs = a.H * D;
     const int64_t base = (b * a.T * a.H + h) * D;
     const uint16_t* qr_p = reinterpret_cast<const uint16_t*>(a.q_re);
@@ -314,20 +326,21 @@ __global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
         const __bf16 one = (__bf16)1.0f;
         const bf16x8 ones = {one, one, one, one, one, one, one, one};
 
-        // staging registers: KQ key quads (real 8 B + imaginary 8 B) and VQ value chunks (16 B)
-        uint2 skr[KQ], ski[KQ];
-        uint4 sv[VQ];
-        auto fetch = [&](int64_t kb) {
+        // staging registers, RD sets (blocks kb + 1 .. kb + RD in flight while block kb
+        // is used): KQ key quads (real 8 B + imaginary 8 B) and VQ value chunks (16 B)
+        uint2 skr[RD][KQ], ski[RD][KQ];
+        uint4 sv[RD][VQ];
+        auto fetch = [&](int64_t kb, int set) {
 #pragma unroll
             for (int i = 0; i < KQ; ++i) {
                 const int idx = i * 256 + tid, row = idx / (D / 4), q = idx % (D / 4);
                 const int64_t key = kb * kBornBlock + row;
                 if (key < a.T) {
-                    skr[i] = *reinterpret_cast<const uint2*>(kr_p + base + key * rs + 4 * q);
-                    ski[i] = *reinterpret_cast<const uint2*>(ki_p + base + key * rs + 4 * q);
+                    skr[set][i] = *reinterpret_cast<const uint2*>(kr_p + base + key * rs + 4 * q);
+                    ski[set][i] = *reinterpret_cast<const uint2*>(ki_p + base + key * rs + 4 * q);
                 } else {
-                    skr[i] = make_uint2(0u, 0u);
-                    ski[i] = make_uint2(0u, 0u);
+                    skr[set][i] = make_uint2(0u, 0u);
+                    ski[set][i] = make_uint2(0u, 0u);
                 }
             }
 #pragma unroll
@@ -338,108 +351,118 @@ __global__ __launch_bounds__(256) void k_born_bf16(BornArgs a) {
                 const int row = rem / (D / 8), c8 = rem % (D / 8);
                 const int64_t key = kb * kBornBlock + row;
                 const uint16_t* src = pl == 0 ? vr_p : vi_p;
-                sv[i] = key < a.T ? *reinterpret_cast<const uint4*>(src + base + key * rs + 8 * c8)
-                                  : make_uint4(0u, 0u, 0u, 0u);
+                sv[set][i] = key < a.T ? *reinterpret_cast<const uint4*>(src + base + key * rs + 8 * c8)
+                                       : make_uint4(0u, 0u, 0u, 0u);
             }
         };
-        auto commit = [&](int buf) {
+        auto commit = [&](int buf, int set) {
 #pragma unroll
             for (int i = 0; i < KQ; ++i) {
                 const int idx = i * 256 + tid, row = idx / (D / 4), q = idx % (D / 4);
                 *reinterpret_cast<uint4*>(&lds_k[buf][0][row * KS + 16 * q]) =
-                    make_uint4(skr[i].x, skr[i].y, ski[i].x, ski[i].y);
+                    make_uint4(skr[set][i].x, skr[set][i].y, ski[set][i].x, ski[set][i].y);
                 *reinterpret_cast<uint4*>(&lds_k[buf][1][row * KS + 16 * q]) =
-                    make_uint4(ski[i].x, ski[i].y, skr[i].x, skr[i].y);
+                    make_uint4(ski[set][i].x, ski[set][i].y, skr[set][i].x, skr[set][i].y);
             }
 #pragma unroll
             for (int i = 0; i < VQ; ++i) {
                 const int idx = i * 256 + tid;
                 const int pl = idx / (kBornBlock * D / 8), rem = idx % (kBornBlock * D / 8);
                 const int row = rem / (D / 8), c8 = rem % (D / 8);
-                const uint32_t wv[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int col = pl * D + 8 * c8 + j;
-                    *reinterpret_cast<uint16_t*>(&lds_v[buf][col * VS + 2 * row]) =
-                        (uint16_t)(j % 2 == 0 ? wv[j / 2] & 0xffffu : wv[j / 2] >> 16);
-                }
+                *reinterpret_cast<uint4*>(&lds_v[buf][row * VS + 2 * (pl * D + 8 * c8)]) = sv[set][i];
             }
         };
 
-        // key blocks of 64 up to the end of this query block
+        // key blocks of 64 up to the end of this query block; block b's loads go to
+        // register set b % RD and are written to LDS buffer b % 2 at the end of block
+        // b - 1, after which the set takes block b + RD
         const int64_t nkb = 2 * qb + 2;
-        fetch(0);
+        fetch(0, 0);
+        __syncthreads();  // the previous query block is done with the LDS buffers
+        commit(0, 0);
+#pragma unroll
+        for (int j = 1; j <= RD; ++j)
+            if (j < nkb) fetch(j, j % RD);
         __syncthreads();
-        commit(0);
-        __syncthreads();
-        for (int64_t kb = 0; kb < nkb; ++kb) {
+        // a block wholly before the query block (kb < 2 qb) has no masked or empty
+        // score tile for any wave; only the two blocks on the diagonal need the checks
+        auto step = [&](int64_t kb, int set_next, auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
             const int buf = kb & 1;
-            if (kb + 1 < nkb) fetch(kb + 1);
             // key tile t of this block starts kd = 64 kb + 16 t - (128 qb + 32 w + 16 u)
             // rows after query tile u: kd < 0 unmasked, kd = 0 the diagonal tile, kd > 0 empty
-            const int64_t kd0 = 64 * kb - QBR * qb - 32 * w;
-            floatx4 sc[2][4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                sc[0][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-                sc[1][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-                if (kd0 + 16 * t - 16 > 0) continue;  // empty for both query tiles (wave-uniform)
-                bf16x8 are[NM], aim[NM];
-#pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    const int ko = (16 * t + lr) * KS + 16 * (4 * m + lg);
-                    are[m] = *reinterpret_cast<const bf16x8*>(&lds_k[buf][0][ko]);
-                    aim[m] = *reinterpret_cast<const bf16x8*>(&lds_k[buf][1][ko]);
-                }
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int64_t kd = kd0 + 16 * t - 16 * u;
-                    if (kd > 0) continue;  // wave-uniform
-                    floatx4 sre = {0.f, 0.f, 0.f, 0.f}, sim = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int m = 0; m < NM; ++m) {
-                        sre = __builtin_amdgcn_mfma_f32_16x16x32_bf16(are[m], bre[u][m], sre, 0, 0, 0);
-                        sim = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aim[m], bim[u][m], sim, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float v = sre[r] * sre[r] + sim[r] * sim[r];
-                        if (kd == 0 && 4 * lg + r > lr) v = 0.f;
-                        sc[u][t][r] = v;
-                    }
-                }
-            }
-            // O += P . [vr | vi] over the 32-key steps (tiles 2s, 2s + 1)
+            const int kd0 = (int)(64 * kb - QBR * qb) - 32 * w;
+            // per 32-key step s2 (key tiles 2 s2, 2 s2 + 1): the scores of both query
+            // tiles, packed to bf16 where the matrix core leaves them, then
+            // O += P . [vr | vi] and the row sums
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                if (kd0 + 32 * s2 - 16 > 0) continue;  // both query tiles empty (wave-uniform)
+                if (!FULL && kd0 + 32 * s2 - 16 > 0) continue;  // both query tiles empty (wave-uniform)
+                bf16x8 are[2][NM], aim[2][NM];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        const int ko = (16 * (2 * s2 + tt) + lr) * KS + 16 * (4 * m + lg);
+                        are[tt][m] = *reinterpret_cast<const bf16x8*>(&lds_k[buf][0][ko]);
+                        aim[tt][m] = *reinterpret_cast<const bf16x8*>(&lds_k[buf][1][ko]);
+                    }
                 bf16x8 pa[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pa[u][j] = (__bf16)sc[u][2 * s2][j];
-                        pa[u][j + 4] = (__bf16)sc[u][2 * s2 + 1][j];
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const int kd = kd0 + 16 * (2 * s2 + tt) - 16 * u;
+                        float v[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (FULL || kd <= 0) {  // wave-uniform
+                            floatx4 sre = {0.f, 0.f, 0.f, 0.f}, sim = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int m = 0; m < NM; ++m) {
+                                sre = __builtin_amdgcn_mfma_f32_16x16x32_bf16(are[tt][m], bre[u][m], sre, 0, 0, 0);
+                                sim = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aim[tt][m], bim[u][m], sim, 0, 0, 0);
+                            }
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) v[r] = sre[r] * sre[r] + sim[r] * sim[r];
+                            if (!FULL && kd == 0) {  // the diagonal tile: keys after the query drop
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (4 * lg + r > lr) v[r] = 0.f;
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) pa[u][4 * tt + r] = (__bf16)v[r];
                     }
                 }
-                const bool act1 = kd0 + 32 * s2 - 16 <= 0;  // query tile 1 sees this step
-                const bool act0 = kd0 + 32 * s2 <= 0;
+                const bool act1 = FULL || kd0 + 32 * s2 - 16 <= 0;  // query tile 1 sees this step
+                const bool act0 = FULL || kd0 + 32 * s2 <= 0;
                 if (act0) den4[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], ones, den4[0], 0, 0, 0);
                 if (act1) den4[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], ones, den4[1], 0, 0, 0);
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
-                    const int col = 16 * c + lr;
-                    const unsigned char* vrow = &lds_v[buf][col * VS];
-                    const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * s2 + 4 * lg));
-                    const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 2 * (32 * s2 + 16 + 4 * lg));
-                    const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    // lane 4 r + q of group lg points at key 32 s2 + 4 lg + r (and + 16),
+                    // columns 16 c + 4 q .. + 3; the transpose read hands lane 4 q + x
+                    // column 16 c + 4 q + x of those four keys
+                    const int vo = (32 * s2 + 4 * lg + (lr >> 2)) * VS + 2 * (16 * c + 4 * (lr & 3));
+                    const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16*)(&lds_v[buf][vo]));
+                    const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16*)(&lds_v[buf][vo + 16 * VS]));
+                    const bf16x8 vb = cat8(__builtin_bit_cast(bf16x4, v0), __builtin_bit_cast(bf16x4, v1));
                     if (act0) o[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vb, o[0][c], 0, 0, 0);
                     if (act1) o[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vb, o[1][c], 0, 0, 0);
                 }
             }
-            if (kb + 1 < nkb) commit(buf ^ 1);
+            if (kb + 1 < nkb) commit(buf ^ 1, set_next);
+            if (kb + 1 + RD < nkb) fetch(kb + 1 + RD, set_next);
             __syncthreads();
+        };
+        static_assert(RD == 1 || RD == 2, "2 qb must be a multiple of RD");
+        for (int64_t kb0 = 0; kb0 < 2 * qb; kb0 += RD) {
+#pragma unroll
+            for (int j = 0; j < RD; ++j) step(kb0 + j, (j + 1) % RD, BoolTag<true>());
         }
+        step(2 * qb, 1 % RD, BoolTag<false>());
+        step(2 * qb + 1, 0, BoolTag<false>());
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
