@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
                 const float den = den4[u][r];
                 const int64_t row = qb * QBR + 32 * w + 16 * u + qloc;
                 if (row >= a.T) continue;
-                const float inv = den != 0.f ? 1.f / den : 0.f;
+                const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;  // about 1 ulp
                 const int64_t at = base + row * rs;
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
