@@ -58,10 +58,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRow = 128;   // bytes of a staged bf16 row of 64 values (C, B, M)
 constexpr int kTRow = 144;  // bytes of a transposed row: 64 steps + 16 B (X^T, (w B)^T)
 
-// physical 16-byte piece of logical piece `ch` of staged row `row`: two rows per
-// 256-byte window, so 16 consecutive rows reading one logical piece hit 8
-// distinct windows at 8 distinct offsets
-__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
+// physical 16-byte piece of logical piece `ch` of staged row `row`:
+// ch ^ f(row & 15), f(i) = (i & 7) ^ (i >> 3).  16 consecutive rows reading one
+// logical piece (16-byte operand reads) then hit 8 distinct offsets within any 8
+// consecutive rows, and 16 distinct 16-byte slots modulo 256 over all 16, so
+// the reads are free of bank conflicts whether a pass serves 8 or 16 lanes
+// (with f(i) = i >> 1, two rows of every 8 shared an offset)
+__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row & 7) ^ ((row >> 3) & 1)); }
 
 __device__ __forceinline__ floatx4 mfma_bf(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -75,6 +78,39 @@ __device__ __forceinline__ bf16x8 bneg(bf16x8 v) {
 
 __device__ __forceinline__ uint32_t bf16_bits(float v) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// x moved across lanes by a DPP pattern (both 32-bit halves); lanes the pattern
+// or the row mask leaves without a source read 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// inclusive prefix sum over the 64 lanes in fp64: shifts right by 1, 2, 4, 8
+// within each row of 16 lanes, then row 0's total into rows 1 and 3
+// (row_bcast:15) and rows 0-1's total into rows 2 and 3 (row_bcast:31).  The
+// moves stay in the vector unit (a shuffle-based scan goes through LDS with
+// ds_bpermute); the association of the sums differs from a lane-by-lane scan's
+// only by fp64 rounding
+__device__ __forceinline__ void wave_inclusive_scan(double& v) {
+    v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_f64<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15
+    v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31
+}
+
+// the value of lane `l` (wave-uniform l), through the scalar unit
+__device__ __forceinline__ double lane_value(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ float lo_f(uint32_t v) { return __uint_as_float(v << 16); }
@@ -227,15 +263,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             vr = sp * are;
             vi = sp * aim;
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double ur = __shfl_up(vr, off, 64), ui = __shfl_up(vi, off, 64);
-            if (lane >= off) {
-                vr += ur;
-                vi += ui;
-            }
-        }
-        const double tr = __shfl(vr, 63, 64), ti = __shfl(vi, 63, 64);
+        wave_inclusive_scan(vr);
+        wave_inclusive_scan(vi);
+        const double tr = lane_value(vr, 63), ti = lane_value(vi, 63);
         const double ar2 = vr * kLog2e, at2 = vi * kInvTwoPi;  // log2 units, turns
         l_acs[slot][0][lane] = (float)ar2;
         l_acs[slot][1][lane] = (float)(at2 - rint(at2));
