@@ -252,7 +252,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
     BornArgs a) {
     constexpr int NM = D / 16;          // MFMA steps over the features (per part)
     constexpr int KS = 4 * D + 16;      // LDS key row stride (bytes): D/4 quads of 16 B, padded
-    constexpr int VS = 4 * D + 16;      // LDS value row stride (bytes): [vr | vi] of one key, padded
+    // LDS value row stride (bytes): [vr | vi] of one key, padded by 32 B so that the
+    // four rows one transposing read takes (32 B each) fall in distinct banks
+    constexpr int VS = 4 * D + 32;
     constexpr int NCT = 2 * D / 16;     // 16-column tiles of [vr | vi]
     constexpr int KQ = kBornBlock * D / 4 / 256;   // key quads staged per thread
     constexpr int VQ = kBornBlock * 2 * D / 8 / 256;  // 8-value chunks of V staged per thread
@@ -269,6 +271,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int64_t rs = a.H * D;
     const int64_t base = (b * a.T * a.H + h) * D;
+    // every row a workgroup addresses (up to the end of the last 128-row query
+    // block, past T) lies within 2 GB of this (b, h)'s first row: stores through
+    // 32-bit buffer offsets
+    const bool small = ((a.T + 2 * kBornBlock) * rs + D) * 4 < ((int64_t)1 << 31);
     const uint16_t* qr_p = reinterpret_cast<const uint16_t*>(a.q_re);
     const uint16_t* qi_p = reinterpret_cast<const uint16_t*>(a.q_im);
     const uint16_t* kr_p = reinterpret_cast<const uint16_t*>(a.k_re);
@@ -463,20 +469,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
         }
         step(2 * qb, 1 % RD, BoolTag<false>());
         step(2 * qb + 1, 0, BoolTag<false>());
+        if (small) {
+            // through views of this (b, h)'s rows: 32-bit offsets, rows past the
+            // sequence dropped by the extent
+            const uint32_t ext = (uint32_t)(((a.T - 1) * rs + D) * 4);
+            const BufRes vre = make_buf(a.out_re + base, ext), vim = make_buf(a.out_im + base, ext);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < 2; ++u) {
+                uint32_t vo = (uint32_t)(((qb * QBR + 32 * w + 16 * u + 4 * lg) * rs + lr) * 4);
+                asm volatile("" : "+v"(vo));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int qloc = 4 * lg + r;
-                const float den = den4[u][r];
-                const int64_t row = qb * QBR + 32 * w + 16 * u + qloc;
-                if (row >= a.T) continue;
-                const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;  // about 1 ulp
-                const int64_t at = base + row * rs;
+                for (int r = 0; r < 4; ++r) {
+                    const float den = den4[u][r];
+                    const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;  // about 1 ulp
 #pragma unroll
-                for (int c = 0; c < NCT; ++c) {
-                    float* dst = (16 * c) < D ? a.out_re : a.out_im;
-                    dst[at + (16 * c) % D + lr] = o[u][c][r] * inv;
+                    for (int c = 0; c < NCT; ++c)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __float_as_uint(o[u][c][r] * inv), (16 * c) < D ? vre : vim,
+                            vo + (uint32_t)(r * rs + (16 * c) % D) * 4, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qloc = 4 * lg + r;
+                    const float den = den4[u][r];
+                    const int64_t row = qb * QBR + 32 * w + 16 * u + qloc;
+                    if (row >= a.T) continue;
+                    const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;  // about 1 ulp
+                    const int64_t at = base + row * rs;
+#pragma unroll
+                    for (int c = 0; c < NCT; ++c) {
+                        float* dst = (16 * c) < D ? a.out_re : a.out_im;
+                        dst[at + (16 * c) % D + lr] = o[u][c][r] * inv;
+                    }
                 }
             }
         }
