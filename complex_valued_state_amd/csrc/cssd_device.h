@@ -55,6 +55,39 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// x moved across lanes by a DPP pattern (both 32-bit halves); lanes the pattern
+// or the row mask leaves without a source read 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// inclusive prefix sum over the 64 lanes in fp64: shifts right by 1, 2, 4, 8
+// within each row of 16 lanes, then row 0's total into rows 1 and 3
+// (row_bcast:15) and rows 0-1's total into rows 2 and 3 (row_bcast:31).  The
+// moves stay in the vector unit (a shuffle-based scan goes through LDS with
+// ds_bpermute); the association of the sums differs from a lane-by-lane scan's
+// only by fp64 rounding
+__device__ __forceinline__ void wave_inclusive_scan(double& v) {
+    v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_f64<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15
+    v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31
+}
+
+// the value of lane `l` (wave-uniform l), through the scalar unit
+__device__ __forceinline__ double lane_value(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ double softplus_f64(double v) {
     return fmax(v, 0.0) + log1p(exp(-fabs(v)));
 }

@@ -15,7 +15,8 @@
 // (log-decay A_log = softplus(dt) A and its cumsum over the chunk axis).
 //
 // One wave per (b, h, c); lane l holds position l (two positions per lane for
-// C = 128).  The scan runs in fp64 with wave shuffles: the imaginary part of a
+// C = 128).  The scan runs in fp64 across the lanes (DPP row shifts and row
+// broadcasts, no LDS round trips): the imaginary part of a
 // 128-step chunk reaches thousands of radians, and every consumer later takes
 // differences of these sums, so they are kept exact to fp64 and stored as
 // fp64.  The exponentials take the fp64 arguments to log2 units and to half a
@@ -69,15 +70,8 @@ __global__ __launch_bounds__(256) void k_cumsum(const float* __restrict__ dt,
         vi[j] += vi[j - 1];
     }
     double sr = vr[PER - 1], si = vi[PER - 1];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double ur = __shfl_up(sr, off, 64);
-        const double ui = __shfl_up(si, off, 64);
-        if (lane >= off) {
-            sr += ur;
-            si += ui;
-        }
-    }
+    wave_inclusive_scan(sr);
+    wave_inclusive_scan(si);
     const double exr = sr - vr[PER - 1], exi = si - vi[PER - 1];  // exclusive prefix of the lane
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -91,8 +85,8 @@ __global__ __launch_bounds__(256) void k_cumsum(const float* __restrict__ dt,
         tot_r = vr[0];
         tot_i = vi[0];
     }
-    tot_r = __shfl(tot_r, last_lane, 64);
-    tot_i = __shfl(tot_i, last_lane, 64);
+    tot_r = lane_value(tot_r, last_lane);
+    tot_i = lane_value(tot_i, last_lane);
 
     // exp of a complex fp64 log-decay, rounded to fp32: the argument is taken to
     // log2 units and to a fraction of a turn in fp64, then the fp32 hardware
