@@ -31,18 +31,22 @@
 //    M = G . L (+ Dskip on the diagonal) is formed in fp32, rounded to bf16 and
 //    written row-major into LDS for every wave to read.
 //  * M X and (w B)^T X contract over time with 8 consecutive steps per lane
-//    group, so X and w B are staged transposed (one LDS row per feature over the
-//    chunk's 64 steps); the X^T operand of the wave's columns serves both.
+//    group: X and w B are staged row-major like C and B and their operands come
+//    from transposing LDS reads (ds_read_b64_tr_b16: lane 4 q + x of a 16-lane
+//    group receives element x of the 8-byte pieces that lanes q, 4 + q, 8 + q and
+//    12 + q point at, so lanes 4 t + q pointing at step t, columns 4 q .. 4 q + 3,
+//    hand lane 4 q + x column 4 q + x of four consecutive steps).  The X operand
+//    of the wave's columns serves both products.
 // Complex products are four real products (a sum of bf16 operands would round),
 // the imaginary operand negated where the real part needs it.
 //
-// Staging: the next chunk's C, B and X rows are loaded into registers while
-// the current chunk is computed, then written to LDS (C and B
-// rows with 16-byte pieces XOR-swizzled by the row; X transposed).  w B is then
-// formed from the staged B rows in fp32 and rounded to bf16 into its transposed
-// rows; the M tiles overwrite the B rows once the scores are done.  70 KB of
-// LDS: two workgroups per CU.  Rows of a partial last chunk past the sequence
-// read as zero through the buffer extents and their stores are dropped.
+// Staging: the next chunk's C, B and X rows are loaded into registers (16-byte
+// pieces) while the current chunk is computed, then written to LDS with the
+// pieces XOR-swizzled by the row; w B is formed from the same B pieces in fp32
+// and rounded to bf16 on the way.  The M tiles overwrite the B rows once the
+// scores are done.  65 KB of LDS: two workgroups per CU.  Rows of a partial last
+// chunk past the sequence read as zero through the buffer extents and their
+// stores are dropped.
 #include "cssd_device.h"
 #include "cssd_launch.h"
 
@@ -55,8 +59,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRow = 128;   // bytes of a staged bf16 row of 64 values (C, B, M)
-constexpr int kTRow = 144;  // bytes of a transposed row: 64 steps + 16 B (X^T, (w B)^T)
+constexpr int kRow = 128;  // bytes of a staged bf16 row of 64 values (C, B, M, X, w B)
 
 // physical 16-byte piece of logical piece `ch` of staged row `row`:
 // ch ^ f(row & 15), f(i) = (i & 7) ^ (i >> 3).  16 consecutive rows reading one
@@ -65,6 +68,25 @@ constexpr int kTRow = 144;  // bytes of a transposed row: 64 steps + 16 B (X^T, 
 // the reads are free of bank conflicts whether a pass serves 8 or 16 lanes
 // (with f(i) = i >> 1, two rows of every 8 shared an offset)
 __device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row & 7) ^ ((row >> 3) & 1)); }
+
+// the same for the rows read by transposing reads (X, w B): ch ^ f(row),
+// f(i) = 2 bit1(i) + 4 bit3(i).  Such a read covers rows r0 + {0..3} (r0 a
+// multiple of 4) per 16-lane group and r0 + {0..3, 8..11} per 32 lanes, 32
+// bytes (pieces ch, ch + 1 of an even ch) of each; rows of one parity then take
+// disjoint piece pairs, so the 16 pieces are distinct modulo 256 bytes
+__device__ __forceinline__ int swt(int row, int ch) { return ch ^ ((row & 2) | ((row >> 1) & 4)); }
+
+// four bf16 at 8-byte LDS piece `at`, transposed across each 16-lane group
+__device__ __forceinline__ bf16x4 ld_tr(const unsigned char* base, int at) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(base + at));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 __device__ __forceinline__ floatx4 mfma_bf(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -94,8 +116,7 @@ struct FusedArgs {
 
 // one chunk's inputs in flight in registers
 struct Pre {
-    u32x4 c[2][2], b[2][2];  // [plane][piece]: 16-byte pieces of the C and B rows
-    uint32_t x[2][8];        // [plane][step]: two adjacent X columns at 8 steps
+    u32x4 c[2][2], b[2][2], x[2][2];  // [plane][piece]: 16-byte pieces of the C, B, X rows
 };
 
 }  // namespace
@@ -105,8 +126,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     constexpr int C = 64, N = 64, D = 64;
     __shared__ __align__(16) unsigned char l_c[2][C * kRow];    // C rows (re, im)
     __shared__ __align__(16) unsigned char l_b[2][C * kRow];    // B rows, then the M rows
-    __shared__ __align__(16) unsigned char l_xt[2][D * kTRow];  // X^T: [p][s]
-    __shared__ __align__(16) unsigned char l_wb[2][N * kTRow];  // (w B)^T: [n][s]
+    __shared__ __align__(16) unsigned char l_x[2][C * kRow];    // X rows [s][p]
+    __shared__ __align__(16) unsigned char l_wb[2][C * kRow];   // w B rows [s][n]
     // per chunk, in two slots (chunk parity): the cumsums (real part in log2
     // units; imaginary part in turns, reduced to its fractional part in fp64
     // before it is rounded to fp32), exp(acs), exp(acs[C-1] - acs) and the
@@ -148,10 +169,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int r = 0; r < 4; ++r) hr[nt][r] = hi[nt][r] = 0.f;
     }
 
-    // staging roles: C and B pieces u = tid + 256 k (row u / 8, piece u % 8); X
-    // columns 2 xp, 2 xp + 1 at steps 8 xg .. 8 xg + 7; threads 0-127 one piece
-    // of the cumsums (0-63), exp(acs) (64-95) or the weights (96-127)
-    const int xp = tid & 31, xg = tid >> 5;
+    // staging roles: C, B and X pieces u = tid + 256 k (row u / 8, piece u % 8);
+    // N = D, so one offset serves the three
     auto load = [&](int c, Pre& P) {
         const int64_t t0 = (int64_t)c * C;
         const int valid = (int)min<int64_t>((int64_t)C, a.T - t0);
@@ -169,39 +188,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 const uint32_t off = ((uint32_t)(u >> 3) * sN + 8 * (u & 7)) * 2u;
                 P.c[pl][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc[pl], off, 0, 0));
                 P.b[pl][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb[pl], off, 0, 0));
-            }
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const uint32_t off = ((uint32_t)(8 * xg + r) * sD + 2 * xp) * 2u;
-                P.x[pl][r] = __builtin_amdgcn_raw_buffer_load_b32(rx[pl], off, 0, 0);
+                P.x[pl][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx[pl], off, 0, 0));
             }
     };
-    auto stage = [&](const Pre& P) {
+    // the staged rows of chunk slot `slot`, and w B from the B pieces and w of
+    // that chunk (formed in fp32, rounded to bf16)
+    auto stage = [&](const Pre& P, int slot) {
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
+        for (int k = 0; k < 2; ++k) {
+            const int u = tid + 256 * k, row = u >> 3;
+            const int at = row * kRow + 16 * swz(row, u & 7);
+            const int atx = row * kRow + 16 * swt(row, u & 7);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int u = tid + 256 * k, row = u >> 3;
-                const int at = row * kRow + 16 * swz(row, u & 7);
+            for (int pl = 0; pl < 2; ++pl) {
                 *reinterpret_cast<u32x4*>(&l_c[pl][at]) = P.c[pl][k];
                 *reinterpret_cast<u32x4*>(&l_b[pl][at]) = P.b[pl][k];
+                *reinterpret_cast<u32x4*>(&l_x[pl][atx]) = P.x[pl][k];
             }
-        // X^T rows 2 xp + f, steps 8 xg .. 8 xg + 7
+            const float wr = l_w[slot][0][row], wi = l_w[slot][1][row];
+            u32x4 pr, pi;
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t vr = P.b[0][k][j], vi = P.b[1][k][j];
+                const float br[2] = {lo_f(vr), hi_f(vr)}, bi[2] = {lo_f(vi), hi_f(vi)};
+                uint32_t ur[2], ui[2];
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                u32x4 v;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t a0 = (P.x[pl][2 * k] >> (16 * f)) & 0xffffu;
-                    const uint32_t a1 = (P.x[pl][2 * k + 1] >> (16 * f)) & 0xffffu;
-                    v[k] = a0 | (a1 << 16);
+                for (int f = 0; f < 2; ++f) {
+                    ur[f] = bf16_bits(wr * br[f] - wi * bi[f]);
+                    ui[f] = bf16_bits(wr * bi[f] + wi * br[f]);
                 }
-                *reinterpret_cast<u32x4*>(&l_xt[pl][(2 * xp + f) * kTRow + 16 * xg]) = v;
+                pr[j] = ur[0] | (ur[1] << 16);
+                pi[j] = ui[0] | (ui[1] << 16);
             }
+            *reinterpret_cast<u32x4*>(&l_wb[0][atx]) = pr;
+            *reinterpret_cast<u32x4*>(&l_wb[1][atx]) = pi;
+        }
     };
     // the discretisation and chunk-local cumsum of chunk c (wave 0, lane l holds
     // position l), from its raw steps dtv, into slot c & 1:
@@ -254,13 +275,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         return t < a.T ? a.dt[(b * a.T + t) * a.H + h] : 0.f;
     };
 
+    // Memory operations are issued in the same order and number on every wave and
+    // every pass: per chunk c, the next chunk's rows (load), the raw steps of chunk
+    // c + 2 (every wave loads them; wave 0 uses them), then the 32 output stores.
+    // The prologue mirrors that with 32 stores through a view of extent 0 (all
+    // dropped).  The compiler's waits for a prefetch then count the operations
+    // issued after it exactly, also across the loop's back edge, instead of
+    // waiting for the output stores or for the loads just issued.
     Pre P;
     load(0, P);
-    float dtn = 0.f;  // wave 0: the raw steps of the chunk after next
-    if (w == 0) {
-        cumsum(0, load_dt(0));
-        if (a.nC > 1) dtn = load_dt(1);
+    const float dt0 = load_dt(0);
+    float dtn = a.nC > 1 ? load_dt(1) : 0.f;  // the raw steps of the chunk after next
+    {
+        const BufRes none = make_buf(a.y_re, 0);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) buf_store_f32(0.f, none, (uint32_t)i);
     }
+    if (w == 0) cumsum(0, dt0);
     for (int c = 0; c < a.nC; ++c) {
         const int64_t t0 = (int64_t)c * C;
         const int valid = (int)min<int64_t>((int64_t)C, a.T - t0);
@@ -268,55 +299,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int slot = c & 1;
         const float* const acs_r = l_acs[slot][0];
         const float* const acs_i = l_acs[slot][1];
-        const float* const lw_r = l_w[slot][0];
-        const float* const lw_i = l_w[slot][1];
         const float* const le_r = l_e[slot][0];
         const float* const le_i = l_e[slot][1];
 
         __syncthreads();  // every wave is done with the previous chunk's LDS
-        stage(P);
+        stage(P, slot);
         if (c + 1 < a.nC) load(c + 1, P);
         __syncthreads();
 
-        // ---- (w B)^T rows 2 xp + f over steps 8 xg .. 8 xg + 7, from the staged B rows
-        {
-            u32x4 pr[2], pi[2];  // [feature]: 8 steps of (w B)[s][2 xp + f], re and im
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                uint32_t ur[2][2], ui[2][2];  // [feature][step of the pair]
-#pragma unroll
-                for (int e2 = 0; e2 < 2; ++e2) {
-                    const int s = 8 * xg + 2 * k + e2;
-                    const int at = s * kRow + 16 * swz(s, xp >> 2) + 4 * (xp & 3);
-                    const uint32_t vr = *reinterpret_cast<const uint32_t*>(&l_b[0][at]);
-                    const uint32_t vi = *reinterpret_cast<const uint32_t*>(&l_b[1][at]);
-                    const float wr = lw_r[s], wi = lw_i[s];
-                    const float br[2] = {lo_f(vr), hi_f(vr)}, bi[2] = {lo_f(vi), hi_f(vi)};
-#pragma unroll
-                    for (int f = 0; f < 2; ++f) {
-                        ur[f][e2] = bf16_bits(wr * br[f] - wi * bi[f]);
-                        ui[f][e2] = bf16_bits(wr * bi[f] + wi * br[f]);
-                    }
-                }
-#pragma unroll
-                for (int f = 0; f < 2; ++f) {
-                    pr[f][k] = ur[f][0] | (ur[f][1] << 16);
-                    pi[f][k] = ui[f][0] | (ui[f][1] << 16);
-                }
-            }
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                *reinterpret_cast<u32x4*>(&l_wb[0][(2 * xp + f) * kTRow + 16 * xg]) = pr[f];
-                *reinterpret_cast<u32x4*>(&l_wb[1][(2 * xp + f) * kTRow + 16 * xg]) = pi[f];
-            }
-        }
-
         // ---- wave 0 has the fewest score tiles: it discretises the next chunk first
         // (into the other slot, last read in the previous chunk)
-        if (w == 0 && c + 1 < a.nC) {
-            cumsum(c + 1, dtn);
-            if (c + 2 < a.nC) dtn = load_dt(c + 2);
-        }
+        if (w == 0 && c + 1 < a.nC) cumsum(c + 1, dtn);
+        if (c + 2 < a.nC) dtn = load_dt(c + 2);
 
         // ---- score tiles q in [q0, q1) (lt-major causal tiles): M = G . L (+ Dskip)
         constexpr int NP = 10, MQ = 3;
@@ -374,7 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 }
             }
         }
-        __syncthreads();  // the B rows are free: every wave's scores and (w B)^T are done
+        __syncthreads();  // the B rows are free: every wave's scores are done
 
         // ---- the M rows [l][s] over the B rows; the two non-causal tiles that a
         // 32-step product reads, (0, 1) and (2, 3), are zero
@@ -400,14 +394,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
         __syncthreads();
 
-        // ---- X^T operand of this wave's columns: slot j <-> s = 32 k2 + 8 g + j
+        // ---- the X operand of this wave's columns: slot j <-> s = 32 k2 + 8 g + j.
+        // Lane 4 t + q (of li) points at step 8 g + t (+ 4 for slots 4-7, + 32 k2),
+        // columns 16 c16 + 4 q .. + 3; the read hands lane li column 16 c16 + li.
+        // The swizzle depends on bits 1 and 3 of the step only, so the + 4 and
+        // + 32 k2 steps are immediate offsets (512 and 4096 k2 bytes), and column
+        // group c16 sits at tr_base(c16) = tr_base(0) ^ 32 c16.
+        auto tr_base = [&](int c16) {
+            int s = 8 * g + (li >> 2);
+            asm volatile("" : "+v"(s));  // recomputed where used, not kept live
+            return (s * kRow + 16 * swt(s, (li & 3) >> 1) + 8 * (li & 1)) ^ (32 * c16);
+        };
         bf16x8 xr[2], xi[2], xni[2];
+        {
+            const int ax = tr_base(w);
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int at = pcol * kTRow + 64 * k2 + 16 * g;
-            xr[k2] = *reinterpret_cast<const bf16x8*>(&l_xt[0][at]);
-            xi[k2] = *reinterpret_cast<const bf16x8*>(&l_xt[1][at]);
-            xni[k2] = bneg(xi[k2]);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int a0 = ax + 4096 * k2, a1 = a0 + 512;
+                xr[k2] = cat8(ld_tr(l_x[0], a0), ld_tr(l_x[0], a1));
+                xi[k2] = cat8(ld_tr(l_x[1], a0), ld_tr(l_x[1], a1));
+                xni[k2] = bneg(xi[k2]);
+            }
         }
         // ---- per row tile lt: y = diag(exp(acs)) C H_c + M X, then stored (register
         // r <-> row 16 lt + 4 g + r; rows past the sequence are dropped)
@@ -483,11 +490,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             floatx4 sr = {0.f, 0.f, 0.f, 0.f}, si = {0.f, 0.f, 0.f, 0.f};
+            const int an = tr_base(nt);
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                const int at = (16 * nt + li) * kTRow + 64 * k2 + 16 * g;
-                const bf16x8 ar = *reinterpret_cast<const bf16x8*>(&l_wb[0][at]);
-                const bf16x8 ai = *reinterpret_cast<const bf16x8*>(&l_wb[1][at]);
+                // (w B)^T[16 nt + li][32 k2 + 8 g + j] in slot j
+                const int a0 = an + 4096 * k2, a1 = a0 + 512;
+                const bf16x8 ar = cat8(ld_tr(l_wb[0], a0), ld_tr(l_wb[0], a1));
+                const bf16x8 ai = cat8(ld_tr(l_wb[1], a0), ld_tr(l_wb[1], a1));
                 sr = mfma_bf(ar, xr[k2], sr);
                 sr = mfma_bf(ai, xni[k2], sr);
                 si = mfma_bf(ar, xi[k2], si);
