@@ -21,16 +21,19 @@
 // j + 16 g.  Wave w of the four owns the 16 columns p = 16 w + (lane % 16) of y
 // and of the state; its part of H sits in the accumulator layout of the
 // chunk-state product: tile nt, register r of lane p + 16 g <-> n = 16 nt + 4 g + r.
-//  * C H_c: A = C rows, B = H.  The 32-wide contraction over n takes state tiles
-//    2 ks and 2 ks + 1: slot j < 4 is n = 32 ks + 4 g + j and slot j >= 4 is
-//    n = 32 ks + 16 + 4 g + j - 4, which is where the accumulators hold them, so
-//    H enters the product straight from its registers (rounded to bf16 as an
+//  * y is formed transposed, y^T = H_c^T C^T (scaled by exp(acs)) + X^T M^T, so
+//    that register r of lane l + 16 g holds y[l][16 w + 4 g + r]: four adjacent
+//    columns of one row, stored with one 16-byte store per plane.
+//  * H_c^T C^T: A = H^T, B = C rows.  The 32-wide contraction over n takes state
+//    tiles 2 ks and 2 ks + 1: slot j < 4 is n = 32 ks + 4 g + j and slot j >= 4
+//    is n = 32 ks + 16 + 4 g + j - 4, which is where the accumulators hold them,
+//    so H enters the product straight from its registers (rounded to bf16 as an
 //    operand only); the C row is read as the two matching 8-byte pieces.
 //  * G^T = B C^T: A = B rows, B = C rows, both 16-byte reads of staged rows;
 //    register r of lane l + 16 g then holds G[l][s0 + 4 g + r], where
 //    M = G . L (+ Dskip on the diagonal) is formed in fp32, rounded to bf16 and
 //    written row-major into LDS for every wave to read.
-//  * M X and (w B)^T X contract over time with 8 consecutive steps per lane
+//  * X^T M^T and (w B)^T X contract over time with 8 consecutive steps per lane
 //    group: X and w B are staged row-major like C and B and their operands come
 //    from transposing LDS reads (ds_read_b64_tr_b16: lane 4 q + x of a 16-lane
 //    group receives element x of the 8-byte pieces that lanes q, 4 + q, 8 + q and
@@ -277,8 +280,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     // Memory operations are issued in the same order and number on every wave and
     // every pass: per chunk c, the next chunk's rows (load), the raw steps of chunk
-    // c + 2 (every wave loads them; wave 0 uses them), then the 32 output stores.
-    // The prologue mirrors that with 32 stores through a view of extent 0 (all
+    // c + 2 (every wave loads them; wave 0 uses them), then the 8 output stores.
+    // The prologue mirrors that with 8 stores through a view of extent 0 (all
     // dropped).  The compiler's waits for a prefetch then count the operations
     // issued after it exactly, also across the loop's back edge, instead of
     // waiting for the output stores or for the loads just issued.
@@ -289,7 +292,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     {
         const BufRes none = make_buf(a.y_re, 0);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) buf_store_f32(0.f, none, (uint32_t)i);
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, none, 16u * i, 0, 0);
     }
     if (w == 0) cumsum(0, dt0);
     for (int c = 0; c < a.nC; ++c) {
@@ -314,6 +318,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
         // ---- score tiles q in [q0, q1) (lt-major causal tiles): M = G . L (+ Dskip)
         constexpr int NP = 10, MQ = 3;
+        static_assert(NP / 4 == 2 && (NP + 3) / 4 == MQ, "two or three tiles a wave");
         const int q0 = (w * NP) / 4, q1 = ((w + 1) * NP) / 4;
         bf16x4 m_r[MQ], m_i[MQ];
         int m_lt[MQ], m_st[MQ];
@@ -327,38 +332,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int jq = 0; jq < MQ; ++jq) {
                 m_lt[jq] = lt;
                 m_st[jq] = st;
-                if (q0 + jq < q1) {  // wave-uniform
+                // every wave has two tiles or three: the first two are unconditional,
+                // so the compiler can overlap them
+                if (jq < 2 || q0 + jq < q1) {  // wave-uniform
+                    // register r <-> (l = 16 lt + li, s = 16 st + 4 g + r)
+                    const int lrow = 16 * lt + li, s0 = 16 * st + 4 * g;
+                    const float alr = acs_r[lrow], ali = acs_i[lrow];
+                    const floatx4 asr = *reinterpret_cast<const floatx4*>(&acs_r[s0]);
+                    const floatx4 asi = *reinterpret_cast<const floatx4*>(&acs_i[s0]);
                     floatx4 gr = {0.f, 0.f, 0.f, 0.f}, gi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         const int ch = 4 * ks + g;
-                        const int sb = 16 * st + li, lb = 16 * lt + li;
+                        const int sb = 16 * st + li;
                         const bf16x8 br = *reinterpret_cast<const bf16x8*>(&l_b[0][sb * kRow + 16 * swz(sb, ch)]);
                         const bf16x8 bi = *reinterpret_cast<const bf16x8*>(&l_b[1][sb * kRow + 16 * swz(sb, ch)]);
-                        const bf16x8 cr = *reinterpret_cast<const bf16x8*>(&l_c[0][lb * kRow + 16 * swz(lb, ch)]);
-                        const bf16x8 ci = *reinterpret_cast<const bf16x8*>(&l_c[1][lb * kRow + 16 * swz(lb, ch)]);
+                        const bf16x8 cr = *reinterpret_cast<const bf16x8*>(&l_c[0][lrow * kRow + 16 * swz(lrow, ch)]);
+                        const bf16x8 ci = *reinterpret_cast<const bf16x8*>(&l_c[1][lrow * kRow + 16 * swz(lrow, ch)]);
                         gr = mfma_bf(br, cr, gr);
                         gr = mfma_bf(bneg(bi), ci, gr);
                         gi = mfma_bf(br, ci, gi);
                         gi = mfma_bf(bi, cr, gi);
                     }
-                    // register r <-> (l = 16 lt + li, s = 16 st + 4 g + r)
-                    const int lrow = 16 * lt + li;
-                    const bool diag = (lt == st);
                     // L from fp32 differences: the real parts differ by a chunk's
                     // log-decay at most, the turns are fractional parts, and their
-                    // difference is reduced to half a turn again
-                    const float alr = acs_r[lrow], ali = acs_i[lrow];
+                    // difference is reduced to half a turn again.  Computed for every
+                    // element and selected (not branched on), so the four overlap;
+                    // above the diagonal the exponential may overflow and is dropped.
+                    const bool diag = (lt == st);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int s = 16 * st + 4 * g + r;
-                        float lr = 0.f, lim = 0.f;
-                        if (!diag || s <= lrow) {
-                            float dv = ali - acs_i[s];
-                            dv -= rintf(dv);
-                            cexp_scaled(alr - acs_r[s], dv, lr, lim);
-                        }
-                        m_r[jq][r] = (__bf16)(gr[r] * lr - gi[r] * lim + ((diag && s == lrow) ? dk : 0.f));
+                        float dv = ali - asi[r];
+                        dv -= rintf(dv);
+                        float lr, lim;
+                        cexp_scaled(alr - asr[r], dv, lr, lim);
+                        const bool keep = !diag || s0 + r <= lrow;
+                        lr = keep ? lr : 0.f;
+                        lim = keep ? lim : 0.f;
+                        m_r[jq][r] = (__bf16)(gr[r] * lr - gi[r] * lim + ((diag && s0 + r == lrow) ? dk : 0.f));
                         m_i[jq][r] = (__bf16)(gr[r] * lim + gi[r] * lr);
                     }
                     if (++st > lt) {
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // 32-step product reads, (0, 1) and (2, 3), are zero
 #pragma unroll
         for (int jq = 0; jq < MQ; ++jq) {
-            if (q0 + jq < q1) {
+            if (jq < 2 || q0 + jq < q1) {
                 const int l = 16 * m_lt[jq] + li, s0 = 16 * m_st[jq] + 4 * g;
                 const int at = l * kRow + 16 * swz(l, s0 >> 3) + 2 * (s0 & 7);
                 *reinterpret_cast<bf16x4*>(&l_b[0][at]) = m_r[jq];
@@ -416,10 +427,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 xni[k2] = bneg(xi[k2]);
             }
         }
-        // ---- per row tile lt: y = diag(exp(acs)) C H_c + M X, then stored (register
-        // r <-> row 16 lt + 4 g + r; rows past the sequence are dropped)
+        // ---- per row tile lt: y^T = (C H_c)^T diag(exp(acs)) + X^T M^T, then stored
+        // (register r of lane li + 16 g <-> row 16 lt + li, column 16 w + 4 g + r;
+        // rows past the sequence are dropped by the extent)
         {
-            // H_c as the B operand of C H_c: slot j <-> n = 32 ks + 4 g + j (j < 4),
+            // H_c^T as the A operand: slot j <-> n = 32 ks + 4 g + j (j < 4),
             // 32 ks + 16 + 4 g + j - 4 (j >= 4), the accumulator registers themselves
             bf16x8 hb_r[2], hb_i[2];
 #pragma unroll
@@ -450,39 +462,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     const u32x2 i1 = *reinterpret_cast<const u32x2*>(&l_c[1][a1]);
                     const bf16x8 cr = __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
                     const bf16x8 ci = __builtin_bit_cast(bf16x8, u32x4{i0[0], i0[1], i1[0], i1[1]});
-                    yr = mfma_bf(cr, hb_r[ks], yr);
-                    yr = mfma_bf(ci, bneg(hb_i[ks]), yr);
-                    yi = mfma_bf(cr, hb_i[ks], yi);
-                    yi = mfma_bf(ci, hb_r[ks], yi);
+                    yr = mfma_bf(hb_r[ks], cr, yr);
+                    yr = mfma_bf(bneg(hb_i[ks]), ci, yr);
+                    yi = mfma_bf(hb_i[ks], cr, yi);
+                    yi = mfma_bf(hb_r[ks], ci, yi);
                 }
                 {
-                    const floatx4 er = *reinterpret_cast<const floatx4*>(&le_r[16 * lt + 4 * g]);
-                    const floatx4 ei = *reinterpret_cast<const floatx4*>(&le_i[16 * lt + 4 * g]);
+                    const float er = le_r[l], ei = le_i[l];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float re = yr[r], im = yi[r];
-                        yr[r] = er[r] * re - ei[r] * im;
-                        yi[r] = er[r] * im + ei[r] * re;
+                        yr[r] = er * re - ei * im;
+                        yi[r] = er * im + ei * re;
                     }
                 }
-                // M X over s in 32-steps (the second only for rows 32 and up)
+                // X^T M^T over s in 32-steps (the second only for rows 32 and up)
 #pragma unroll
                 for (int k2 = 0; k2 < 2; ++k2) {
                     if (k2 == 1 && lt < 2) continue;
                     const int ch = 4 * k2 + g;
                     const bf16x8 mr = *reinterpret_cast<const bf16x8*>(&l_b[0][l * kRow + 16 * swz(l, ch)]);
                     const bf16x8 mi = *reinterpret_cast<const bf16x8*>(&l_b[1][l * kRow + 16 * swz(l, ch)]);
-                    yr = mfma_bf(mr, xr[k2], yr);
-                    yr = mfma_bf(mi, xni[k2], yr);
-                    yi = mfma_bf(mr, xi[k2], yi);
-                    yi = mfma_bf(mi, xr[k2], yi);
+                    yr = mfma_bf(xr[k2], mr, yr);
+                    yr = mfma_bf(xni[k2], mi, yr);
+                    yi = mfma_bf(xi[k2], mr, yi);
+                    yi = mfma_bf(xr[k2], mi, yi);
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t off = (uint32_t)(16 * lt + 4 * g + r) * sD + pcol;
-                    buf_store_f32(yr[r], ry_r, off);
-                    buf_store_f32(yi[r], ry_i, off);
-                }
+                const uint32_t off = ((uint32_t)l * sD + 16 * w + 4 * g) * 4u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yr), ry_r, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yi), ry_i, off, 0, 0);
             }
         }
         // ---- S_c = (w B)^T X on this wave's columns, then H_{c+1} = cd H_c + S_c
