@@ -65,18 +65,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRow = 128;  // bytes of a staged bf16 row of 64 values (C, B, M, X, w B)
 
 // physical 16-byte piece of logical piece `ch` of staged row `row`:
-// ch ^ f(row & 15), f(i) = (i & 7) ^ (i >> 3).  16 consecutive rows reading one
-// logical piece (16-byte operand reads) then hit 8 distinct offsets within any 8
-// consecutive rows, and 16 distinct 16-byte slots modulo 256 over all 16, so
-// the reads are free of bank conflicts whether a pass serves 8 or 16 lanes
-// (with f(i) = i >> 1, two rows of every 8 shared an offset)
-__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row & 7) ^ ((row >> 3) & 1)); }
+// ch ^ ((row >> 1) & 7).  Measured with the LDS bank-conflict counter on this chip,
+// in isolation: the 16-byte operand reads (rows r0 + li, pieces 4 k + g) and the
+// 8-byte C reads (two half pieces per row) are both free of conflicts with it; with
+// row & 7 the 8-byte reads take 2 conflict cycles an instruction, and with a row
+// bit 3 term XOR-ed in as well the 16-byte reads take 4.  The 8-byte M tile writes
+// take 4 with every row swizzle tried.
+__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
 
 // the same for the rows read by transposing reads (X, w B): ch ^ f(row),
 // f(i) = 2 bit1(i) + 4 bit3(i).  Such a read covers rows r0 + {0..3} (r0 a
 // multiple of 4) per 16-lane group and r0 + {0..3, 8..11} per 32 lanes, 32
 // bytes (pieces ch, ch + 1 of an even ch) of each; rows of one parity then take
-// disjoint piece pairs, so the 16 pieces are distinct modulo 256 bytes
+// disjoint piece pairs, so the 16 pieces are distinct modulo 256 bytes (the LDS
+// bank-conflict counter reads none for these reads)
 __device__ __forceinline__ int swt(int row, int ch) { return ch ^ ((row & 2) | ((row >> 1) & 4)); }
 
 // four bf16 at 8-byte LDS piece `at`, transposed across each 16-lane group
@@ -127,7 +129,11 @@ struct Pre {
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_fused_bf16(
     FusedArgs a) {
     constexpr int C = 64, N = 64, D = 64;
-    __shared__ __align__(16) unsigned char l_c[2][C * kRow];    // C rows (re, im)
+    // C rows (re, im).  The planes are 16 bytes more than a multiple of the bank
+    // window apart: 8-byte reads of the two planes at one offset, which the compiler
+    // merges into one two-address read, then fall in different banks (0 instead of 8
+    // conflict cycles an instruction, measured).
+    __shared__ __align__(16) unsigned char l_c[2][C * kRow + 16];
     __shared__ __align__(16) unsigned char l_b[2][C * kRow];    // B rows, then the M rows
     __shared__ __align__(16) unsigned char l_x[2][C * kRow];    // X rows [s][p]
     __shared__ __align__(16) unsigned char l_wb[2][C * kRow];   // w B rows [s][n]
