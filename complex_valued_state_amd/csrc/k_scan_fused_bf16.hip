@@ -322,10 +322,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (w == 0 && c + 1 < a.nC) cumsum(c + 1, dtn);
         if (c + 2 < a.nC) dtn = load_dt(c + 2);
 
-        // ---- score tiles q in [q0, q1) (lt-major causal tiles): M = G . L (+ Dskip)
-        constexpr int NP = 10, MQ = 3;
-        static_assert(NP / 4 == 2 && (NP + 3) / 4 == MQ, "two or three tiles a wave");
-        const int q0 = (w * NP) / 4, q1 = ((w + 1) * NP) / 4;
+        // ---- score tiles q in [q0, q0 + nq) of the 10 lt-major causal tiles:
+        // M = G . L (+ Dskip).  Wave 0, which also discretises the next chunk, takes
+        // the first diagonal tile alone; waves 1-3 take three tiles each, one of
+        // them diagonal.
+        constexpr int MQ = 3;
+        const int q0 = w == 0 ? 0 : 3 * w - 2;
+        const bool full = w != 0;  // wave-uniform: three tiles
         bf16x4 m_r[MQ], m_i[MQ];
         int m_lt[MQ], m_st[MQ];
         {
@@ -338,9 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int jq = 0; jq < MQ; ++jq) {
                 m_lt[jq] = lt;
                 m_st[jq] = st;
-                // every wave has two tiles or three: the first two are unconditional,
-                // so the compiler can overlap them
-                if (jq < 2 || q0 + jq < q1) {  // wave-uniform
+                if (jq == 0 || full) {  // wave-uniform
                     // register r <-> (l = 16 lt + li, s = 16 st + 4 g + r)
                     const int lrow = 16 * lt + li, s0 = 16 * st + 4 * g;
                     const float alr = acs_r[lrow], ali = acs_i[lrow];
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // 32-step product reads, (0, 1) and (2, 3), are zero
 #pragma unroll
         for (int jq = 0; jq < MQ; ++jq) {
-            if (jq < 2 || q0 + jq < q1) {
+            if (jq == 0 || full) {
                 const int l = 16 * m_lt[jq] + li, s0 = 16 * m_st[jq] + 4 * g;
                 const int at = l * kRow + 16 * swz(l, s0 >> 3) + 2 * (s0 & 7);
                 *reinterpret_cast<bf16x4*>(&l_b[0][at]) = m_r[jq];
