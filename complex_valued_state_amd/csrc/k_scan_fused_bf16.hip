@@ -117,6 +117,10 @@ struct FusedArgs {
     float *y_re, *y_im, *hT_re, *hT_im;
     int64_t T;
     int H, nC;
+    // workgroups from `late` on are dispatched onto CUs that already hold one
+    // (late = CU count when there are more sequences than CUs, but no more than
+    // twice as many; otherwise no workgroup is late and priorities stay default)
+    int late;
 };
 
 // one chunk's inputs in flight in registers
@@ -302,7 +306,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, none, 16u * i, 0, 0);
     }
     if (w == 0) cumsum(0, dt0);
+    // Wave priority.  Of two workgroups on one CU, the one dispatched first wins
+    // instruction arbitration and the other falls behind (measured: 14.1K against
+    // 17.2K clocks a chunk), and the kernel waits for the one behind.  So the late
+    // workgroup takes priority for the first half of its chunks and the early one
+    // for the second half; both then finish at about the same time.
+    const bool late = (int)blockIdx.x >= a.late;  // wave-uniform
+    if (late) __builtin_amdgcn_s_setprio(1);
     for (int c = 0; c < a.nC; ++c) {
+        if (c == a.nC / 2 && a.late < (1 << 30)) {
+            if (late) __builtin_amdgcn_s_setprio(0);
+            else __builtin_amdgcn_s_setprio(1);
+        }
         const int64_t t0 = (int64_t)c * C;
         const int valid = (int)min<int64_t>((int64_t)C, a.T - t0);
         const int64_t row0 = (b * a.T + t0) * a.H + h;
@@ -556,6 +571,10 @@ hipError_t launch_scan_fused(const FwdArgs& f, hipStream_t s) {
     a.h0_re = f.h0_re; a.h0_im = f.h0_im;
     a.y_re = f.y_re; a.y_im = f.y_im; a.hT_re = f.hT_re; a.hT_im = f.hT_im;
     a.T = f.T; a.H = (int)f.H; a.nC = (int)f.nC;
+    const int64_t nseq = f.B * f.H;
+    int cus = 0;
+    if (device_cu_count(&cus) != hipSuccess) cus = 0;
+    a.late = (cus > 0 && nseq > cus && nseq <= 2 * (int64_t)cus) ? cus : (1 << 30);
     hipLaunchKernelGGL(k_scan_fused_bf16, dim3((unsigned)(f.B * f.H)), dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -304,6 +304,22 @@ def test_config1_bf16_sampled():
         assert max(e32) <= TOL_BF16 and e16[0] <= yb and e16[1] <= hb, ((b, h), e32, e16)
 
 
+def test_bf16_more_sequences_than_cus():
+    """bf16 inputs at N = D = C = 64 with more sequences than CUs (at most twice as
+    many): the workgroups dispatched onto occupied CUs change wave priority
+    halfway, which must leave the results alone.  257 sequences with a ragged
+    tail: sampled early and late workgroups, and the last sequence, within the
+    path's bounds of the oracle on the rounded inputs."""
+    inp = wl.random_forward(11, 1, 130, 257, 64, 64, 64, with_h0=True, with_dskip=True,
+                            in_dtype="bf16", name="manyseq")
+    pairs = [(0, 0), (0, 1), (0, 128), (0, 254), (0, 255), (0, 256)]
+    y, hT = _check_sampled(inp, pairs, TOL_BF16)
+    yb, hb = bf16_diagnostic_bounds(64, 64, 64)
+    ref = sampled_oracle(inp, pairs)
+    for (b, h), (yr, hr) in ref.items():
+        assert rel_err(y[b, :, h, :], yr) <= yb and rel_err(hT[b, h], hr) <= hb, (b, h)
+
+
 def test_config2_long_sampled():
     inp = wl.config2()
     _check_sampled(inp, [(0, 0), (0, 13), (0, 29), (0, 47)], TOL_F32)
