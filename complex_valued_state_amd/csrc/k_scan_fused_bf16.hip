@@ -141,11 +141,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ __align__(16) unsigned char l_b[2][C * kRow];    // B rows, then the M rows
     __shared__ __align__(16) unsigned char l_x[2][C * kRow];    // X rows [s][p]
     __shared__ __align__(16) unsigned char l_wb[2][C * kRow];   // w B rows [s][n]
-    // per chunk, in two slots (chunk parity): the cumsums (real part in log2
-    // units; imaginary part in turns, reduced to its fractional part in fp64
-    // before it is rounded to fp32), exp(acs), exp(acs[C-1] - acs) and the
-    // chunk decay exp(acs[C-1])
-    __shared__ __align__(16) float l_acs[2][2][C];
+    // per chunk, in two slots (chunk parity): the real part of the cumsums in log2
+    // units, the unit phasors u = exp(i Im acs) (cos and sin of the imaginary part,
+    // taken in turns and reduced to its fractional part in fp64 first), exp(acs),
+    // exp(acs[C-1] - acs) and the chunk decay exp(acs[C-1])
+    __shared__ __align__(16) float l_acs[2][C];
+    __shared__ __align__(16) float l_u[2][2][C];
     __shared__ __align__(16) float l_e[2][2][C];
     __shared__ __align__(16) float l_w[2][2][C];
     __shared__ float l_cd[2][2];
@@ -268,10 +269,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         wave_inclusive_scan(vi);
         const double tr = lane_value(vr, 63), ti = lane_value(vi, 63);
         const double ar2 = vr * kLog2e, at2 = vi * kInvTwoPi;  // log2 units, turns
-        l_acs[slot][0][lane] = (float)ar2;
-        l_acs[slot][1][lane] = (float)(at2 - rint(at2));
-        float er, ei, wr, wi;
-        cexp_scaled((float)ar2, (float)(at2 - rint(at2)), er, ei);
+        l_acs[slot][lane] = (float)ar2;
+        const float turn = (float)(at2 - rint(at2));
+        const float ur = __builtin_amdgcn_cosf(turn), ui = __builtin_amdgcn_sinf(turn);
+        l_u[slot][0][lane] = ur;
+        l_u[slot][1][lane] = ui;
+        const float mag = __builtin_amdgcn_exp2f((float)ar2);
+        const float er = mag * ur, ei = mag * ui;
+        float wr, wi;
         const double wr2 = (tr - vr) * kLog2e, wt2 = (ti - vi) * kInvTwoPi;
         cexp_scaled((float)wr2, (float)(wt2 - rint(wt2)), wr, wi);
         l_e[slot][0][lane] = er;
@@ -324,8 +329,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int valid = (int)min<int64_t>((int64_t)C, a.T - t0);
         const int64_t row0 = (b * a.T + t0) * a.H + h;
         const int slot = c & 1;
-        const float* const acs_r = l_acs[slot][0];
-        const float* const acs_i = l_acs[slot][1];
+        const float* const acs_r = l_acs[slot];
+        const float* const u_r = l_u[slot][0];
+        const float* const u_i = l_u[slot][1];
         const float* const le_r = l_e[slot][0];
         const float* const le_i = l_e[slot][1];
 
@@ -361,9 +367,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 if (jq == 0 || full) {  // wave-uniform
                     // register r <-> (l = 16 lt + li, s = 16 st + 4 g + r)
                     const int lrow = 16 * lt + li, s0 = 16 * st + 4 * g;
-                    const float alr = acs_r[lrow], ali = acs_i[lrow];
+                    const float alr = acs_r[lrow], ulr = u_r[lrow], uli = u_i[lrow];
                     const floatx4 asr = *reinterpret_cast<const floatx4*>(&acs_r[s0]);
-                    const floatx4 asi = *reinterpret_cast<const floatx4*>(&acs_i[s0]);
+                    const floatx4 usr = *reinterpret_cast<const floatx4*>(&u_r[s0]);
+                    const floatx4 usi = *reinterpret_cast<const floatx4*>(&u_i[s0]);
                     floatx4 gr = {0.f, 0.f, 0.f, 0.f}, gi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
@@ -378,21 +385,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                         gi = mfma_bf(br, ci, gi);
                         gi = mfma_bf(bi, cr, gi);
                     }
-                    // L from fp32 differences: the real parts differ by a chunk's
-                    // log-decay at most, the turns are fractional parts, and their
-                    // difference is reduced to half a turn again.  Computed for every
-                    // element and selected (not branched on), so the four overlap;
-                    // above the diagonal the exponential may overflow and is dropped.
+                    // L = exp2(Re acs[l] - Re acs[s]) u[l] conj(u[s]): the magnitude
+                    // from an fp32 difference of log2 cumsums (they differ by a chunk's
+                    // log-decay at most), the phase as a product of unit phasors.
+                    // Computed for every element and selected (not branched on), so
+                    // the four overlap; above the diagonal the magnitude may overflow
+                    // and is dropped.
                     const bool diag = (lt == st);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float dv = ali - asi[r];
-                        dv -= rintf(dv);
-                        float lr, lim;
-                        cexp_scaled(alr - asr[r], dv, lr, lim);
+                        const float mag = __builtin_amdgcn_exp2f(alr - asr[r]);
+                        const float pr = ulr * usr[r] + uli * usi[r];
+                        const float pim = uli * usr[r] - ulr * usi[r];
                         const bool keep = !diag || s0 + r <= lrow;
-                        lr = keep ? lr : 0.f;
-                        lim = keep ? lim : 0.f;
+                        const float lr = keep ? mag * pr : 0.f;
+                        const float lim = keep ? mag * pim : 0.f;
                         m_r[jq][r] = (__bf16)(gr[r] * lr - gi[r] * lim + ((diag && s0 + r == lrow) ? dk : 0.f));
                         m_i[jq][r] = (__bf16)(gr[r] * lim + gi[r] * lr);
                     }
