@@ -50,6 +50,8 @@
 // scores are done.  65 KB of LDS: two workgroups per CU.  Rows of a partial last
 // chunk past the sequence read as zero through the buffer extents and their
 // stores are dropped.
+#include <type_traits>
+
 #include "cssd_device.h"
 #include "cssd_launch.h"
 
@@ -123,16 +125,31 @@ struct FusedArgs {
     int late;
 };
 
-// one chunk's inputs in flight in registers
+// one chunk's inputs in flight in registers: KP 16-byte pieces a thread of each
+// plane of the C, B and X rows
+template <int KP>
 struct Pre {
-    u32x4 c[2][2], b[2][2], x[2][2];  // [plane][piece]: 16-byte pieces of the C, B, X rows
+    u32x4 c[2][KP], b[2][KP], x[2][KP];  // [plane][piece]
 };
 
 }  // namespace
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_fused_bf16(
+// WAVES = 4: wave w owns the 16 columns 16 w .. of y and of the state and does all
+// of that column block's work.  WAVES = 8: waves w and w + 4 share the column block;
+// half hv = wave / 4 computes the row tiles {0, 3} (hv = 0) or {1, 2} of y (equal
+// shares of the causal product) and the state tiles {2 hv, 2 hv + 1} of S_c and of
+// the update, and both keep the whole carried state of their columns: each half's
+// updated tiles pass to the other through LDS, read after the next chunk's first
+// barrier.  One eight-wave workgroup per CU (101 KB of LDS); its per-chunk time is
+// about half that of a four-wave workgroup alone.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_fused_bf16(
     FusedArgs a) {
+    static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
     constexpr int C = 64, N = 64, D = 64;
+    constexpr int NT = 64 * WAVES;       // threads
+    constexpr int KP = 512 / NT;         // 16-byte pieces a thread of each staged plane
+    constexpr bool W8 = WAVES == 8;
     // C rows (re, im).  The planes are 16 bytes more than a multiple of the bank
     // window apart: 8-byte reads of the two planes at one offset, which the compiler
     // merges into one two-address read, then fall in different banks (0 instead of 8
@@ -150,10 +167,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ __align__(16) float l_e[2][2][C];
     __shared__ __align__(16) float l_w[2][2][C];
     __shared__ float l_cd[2][2];
+    // WAVES = 8: each wave's two updated state tiles, [wave][4 floats][lane] x 4
+    __shared__ __align__(16) float l_hx[W8 ? 8 : 1][4][64][4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int li = lane & 15, g = lane >> 4;
-    const int w = wave_id();
+    const int wv = wave_id();
+    const int w = wv & 3, hv = wv >> 2;  // column block, half (WAVES = 8)
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % a.H);
     const int64_t b = bh / a.H;
@@ -183,9 +203,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int r = 0; r < 4; ++r) hr[nt][r] = hi[nt][r] = 0.f;
     }
 
-    // staging roles: C, B and X pieces u = tid + 256 k (row u / 8, piece u % 8);
+    // staging roles: C, B and X pieces u = tid + NT k (row u / 8, piece u % 8);
     // N = D, so one offset serves the three
-    auto load = [&](int c, Pre& P) {
+    auto load = [&](int c, Pre<KP>& P) {
         const int64_t t0 = (int64_t)c * C;
         const int valid = (int)min<int64_t>((int64_t)C, a.T - t0);
         const int64_t row0 = (b * a.T + t0) * a.H + h;
@@ -197,8 +217,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int u = tid + 256 * k;
+            for (int k = 0; k < KP; ++k) {
+                const int u = tid + NT * k;
                 const uint32_t off = ((uint32_t)(u >> 3) * sN + 8 * (u & 7)) * 2u;
                 P.c[pl][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc[pl], off, 0, 0));
                 P.b[pl][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb[pl], off, 0, 0));
@@ -207,10 +227,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     // the staged rows of chunk slot `slot`, and w B from the B pieces and w of
     // that chunk (formed in fp32, rounded to bf16)
-    auto stage = [&](const Pre& P, int slot) {
+    auto stage = [&](const Pre<KP>& P, int slot) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int u = tid + 256 * k, row = u >> 3;
+        for (int k = 0; k < KP; ++k) {
+            const int u = tid + NT * k, row = u >> 3;
             const int at = row * kRow + 16 * swz(row, u & 7);
             const int atx = row * kRow + 16 * swt(row, u & 7);
 #pragma unroll
@@ -295,22 +315,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     // Memory operations are issued in the same order and number on every wave and
     // every pass: per chunk c, the next chunk's rows (load), the raw steps of chunk
-    // c + 2 (every wave loads them; wave 0 uses them), then the 8 output stores.
-    // The prologue mirrors that with 8 stores through a view of extent 0 (all
-    // dropped).  The compiler's waits for a prefetch then count the operations
+    // c + 2 (every wave loads them; wave 0 uses them), then the output stores (two
+    // a row tile).  The prologue mirrors that with as many stores through a view of
+    // extent 0 (all dropped).  The compiler's waits for a prefetch then count the operations
     // issued after it exactly, also across the loop's back edge, instead of
     // waiting for the output stores or for the loads just issued.
-    Pre P;
+    constexpr int NLT = W8 ? 2 : 4;  // row tiles of y a wave
+    Pre<KP> P;
     load(0, P);
     const float dt0 = load_dt(0);
     float dtn = a.nC > 1 ? load_dt(1) : 0.f;  // the raw steps of the chunk after next
     {
         const BufRes none = make_buf(a.y_re, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 2 * NLT; ++i)
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, none, 16u * i, 0, 0);
     }
-    if (w == 0) cumsum(0, dt0);
+    if (wv == 0) cumsum(0, dt0);
     // Wave priority.  Of two workgroups on one CU, the one dispatched first wins
     // instruction arbitration and the other falls behind (measured: 14.1K against
     // 17.2K clocks a chunk), and the kernel waits for the one behind.  So the late
@@ -336,26 +357,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const float* const le_i = l_e[slot][1];
 
         __syncthreads();  // every wave is done with the previous chunk's LDS
+        if (W8 && c > 0) {
+            // the other half's two updated state tiles (2 (1 - hv), 2 (1 - hv) + 1)
+            const float4* src = reinterpret_cast<const float4*>(&l_hx[W8 ? (wv ^ 4) : 0][0][lane][0]);
+            auto take = [&](auto nt0) {
+                constexpr int T0 = decltype(nt0)::value;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float4 vr = src[(2 * j) * 64], vi = src[(2 * j + 1) * 64];
+                    hr[T0 + j][0] = vr.x; hr[T0 + j][1] = vr.y; hr[T0 + j][2] = vr.z; hr[T0 + j][3] = vr.w;
+                    hi[T0 + j][0] = vi.x; hi[T0 + j][1] = vi.y; hi[T0 + j][2] = vi.z; hi[T0 + j][3] = vi.w;
+                }
+            };
+            if (hv == 0) take(std::integral_constant<int, 2>());
+            else take(std::integral_constant<int, 0>());
+        }
         stage(P, slot);
         if (c + 1 < a.nC) load(c + 1, P);
         __syncthreads();
 
         // ---- wave 0 has the fewest score tiles: it discretises the next chunk first
         // (into the other slot, last read in the previous chunk)
-        if (w == 0 && c + 1 < a.nC) cumsum(c + 1, dtn);
+        if (wv == 0 && c + 1 < a.nC) cumsum(c + 1, dtn);
         if (c + 2 < a.nC) dtn = load_dt(c + 2);
 
         // ---- score tiles q in [q0, q0 + nq) of the 10 lt-major causal tiles:
         // M = G . L (+ Dskip).  Wave 0, which also discretises the next chunk, takes
         // the first diagonal tile alone; waves 1-3 take three tiles each, one of
         // them diagonal.
-        constexpr int MQ = 3;
-        const int q0 = w == 0 ? 0 : 3 * w - 2;
-        const bool full = w != 0;  // wave-uniform: three tiles
+        // WAVES = 8: wave 0 only discretises; waves 1-3 take two tiles (q 0-5),
+        // waves 4-7 one (q 6-9)
+        constexpr int MQ = W8 ? 2 : 3;
+        const int q0 = W8 ? (wv <= 3 ? 2 * (wv - 1) : wv + 2) : (wv == 0 ? 0 : 3 * wv - 2);
+        const int nq = W8 ? (wv == 0 ? 0 : (wv <= 3 ? 2 : 1)) : (wv == 0 ? 1 : 3);  // wave-uniform
+        const bool full = W8 ? false : wv != 0;  // four waves: three tiles, unconditional
         bf16x4 m_r[MQ], m_i[MQ];
         int m_lt[MQ], m_st[MQ];
         {
-            int lt = 0, st = q0;
+            int lt = 0, st = W8 && wv == 0 ? 0 : q0;
             while (st > lt) {
                 st -= lt + 1;
                 ++lt;
@@ -364,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int jq = 0; jq < MQ; ++jq) {
                 m_lt[jq] = lt;
                 m_st[jq] = st;
-                if (jq == 0 || full) {  // wave-uniform
+                if ((!W8 && (jq == 0 || full)) || (W8 && jq < nq)) {  // wave-uniform
                     // register r <-> (l = 16 lt + li, s = 16 st + 4 g + r)
                     const int lrow = 16 * lt + li, s0 = 16 * st + 4 * g;
                     const float alr = acs_r[lrow], ulr = u_r[lrow], uli = u_i[lrow];
@@ -416,14 +455,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // 32-step product reads, (0, 1) and (2, 3), are zero
 #pragma unroll
         for (int jq = 0; jq < MQ; ++jq) {
-            if (jq == 0 || full) {
+            if ((!W8 && (jq == 0 || full)) || (W8 && jq < nq)) {
                 const int l = 16 * m_lt[jq] + li, s0 = 16 * m_st[jq] + 4 * g;
                 const int at = l * kRow + 16 * swz(l, s0 >> 3) + 2 * (s0 & 7);
                 *reinterpret_cast<bf16x4*>(&l_b[0][at]) = m_r[jq];
                 *reinterpret_cast<bf16x4*>(&l_b[1][at]) = m_i[jq];
             }
         }
-        if (w == 0) {
+        if (wv == 0) {
             int zl = threadIdx.x & 63;  // opaque copy of the lane index (see cumsum)
             asm volatile("" : "+v"(zl));
 #pragma unroll
@@ -478,7 +517,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             const BufRes ry_r = make_buf(a.y_re + row0 * D, extD * 4);
             const BufRes ry_i = make_buf(a.y_im + row0 * D, extD * 4);
 #pragma unroll
-            for (int lt = 0; lt < 4; ++lt) {
+            for (int jt = 0; jt < NLT; ++jt) {
+                const int lt = W8 ? (hv == 0 ? 3 * jt : 1 + jt) : jt;  // wave-uniform
                 floatx4 yr = {0.f, 0.f, 0.f, 0.f}, yi = {0.f, 0.f, 0.f, 0.f};
                 const int l = 16 * lt + li;
 #pragma unroll
@@ -526,8 +566,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
         // ---- S_c = (w B)^T X on this wave's columns, then H_{c+1} = cd H_c + S_c
         const float dr = l_cd[slot][0], di = l_cd[slot][1];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        auto update = [&](auto nt_c) {
+            constexpr int nt = decltype(nt_c)::value;
             floatx4 sr = {0.f, 0.f, 0.f, 0.f}, si = {0.f, 0.f, 0.f, 0.f};
             const int an = tr_base(nt);
 #pragma unroll
@@ -548,18 +588,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 hr[nt][r] = nr;
                 hi[nt][r] = ni;
             }
+        };
+        // WAVES = 8: this half's two tiles, handed to the other half through LDS
+        auto give = [&](auto nt0) {
+            constexpr int T0 = decltype(nt0)::value;
+            float4* dst = reinterpret_cast<float4*>(&l_hx[W8 ? wv : 0][0][lane][0]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                dst[(2 * j) * 64] = float4{hr[T0 + j][0], hr[T0 + j][1], hr[T0 + j][2], hr[T0 + j][3]};
+                dst[(2 * j + 1) * 64] = float4{hi[T0 + j][0], hi[T0 + j][1], hi[T0 + j][2], hi[T0 + j][3]};
+            }
+        };
+        if (!W8) {
+            update(std::integral_constant<int, 0>());
+            update(std::integral_constant<int, 1>());
+            update(std::integral_constant<int, 2>());
+            update(std::integral_constant<int, 3>());
+        } else if (hv == 0) {
+            update(std::integral_constant<int, 0>());
+            update(std::integral_constant<int, 1>());
+            if (c + 1 < a.nC) give(std::integral_constant<int, 0>());
+        } else {
+            update(std::integral_constant<int, 2>());
+            update(std::integral_constant<int, 3>());
+            if (c + 1 < a.nC) give(std::integral_constant<int, 2>());
         }
     }
     if (a.hT_re != nullptr) {
+        // WAVES = 8: each half stores the tiles it updated last
         const BufRes r1 = make_buf(a.hT_re + bh * (int64_t)N * D, N * D * 4);
         const BufRes i1 = make_buf(a.hT_im + bh * (int64_t)N * D, N * D * 4);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt) {
+            if (W8 && (nt >> 1) != hv) continue;  // wave-uniform
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 buf_store_f32(hr[nt][r], r1, soff + (16 * nt + r) * D);
                 buf_store_f32(hi[nt][r], i1, soff + (16 * nt + r) * D);
             }
+        }
     }
 }
 
@@ -584,7 +651,14 @@ hipError_t launch_scan_fused(const FwdArgs& f, hipStream_t s) {
     int cus = 0;
     if (device_cu_count(&cus) != hipSuccess) cus = 0;
     a.late = (cus > 0 && nseq > cus && nseq <= 2 * (int64_t)cus) ? cus : (1 << 30);
-    hipLaunchKernelGGL(k_scan_fused_bf16, dim3((unsigned)(f.B * f.H)), dim3(256), 0, s, a);
+    // eight waves when every sequence gets a CU of its own (T 2048, H 48, B 1:
+    // 0.126 ms against 0.159 with four; B 4: 0.166 against 0.194); four otherwise
+    // (B 8 with eight waves, in two rounds of one workgroup a CU: 0.310 ms against
+    // 0.277 with four and the priority swap)
+    if (cus > 0 && nseq <= cus)
+        hipLaunchKernelGGL(k_scan_fused_bf16<8>, dim3((unsigned)nseq), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_scan_fused_bf16<4>, dim3((unsigned)nseq), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
