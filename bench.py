@@ -246,6 +246,7 @@ def forward_entry(inp, steps, warmup, dev, cpu_budget_s=None):
     """One forward workload: tokens/s, ms per step (profiler off), the per-kernel
     averages (profiled pass), the chunk-scan kernel's roofline object, the whole
     forward's fractions and, with a budget, the oracle on the host beside it."""
+    import torch
     sh = inp.shape
     B, T, H, D, N, C = sh["B"], sh["T"], sh["H"], sh["D"], sh["N"], sh["C"]
     dtype = "bf16" if inp.in_dtype == "bf16" else "f32"
@@ -261,10 +262,14 @@ def forward_entry(inp, steps, warmup, dev, cpu_budget_s=None):
         f_ms = kern["k_scan_fused"]
         f_bytes = scan_fused_hbm_bytes(B, T, H, D, N, in_bytes)
         f_gbs = f_bytes / (f_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_scan_fused", "symbol": "k_scan_fused_bf16",
+        # eight-wave workgroups when every sequence has a CU of its own, as the
+        # library's launcher chooses
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        fsym = "k_scan_fused_bf16<8>" if B * H <= cus else "k_scan_fused_bf16<4>"
+        roof = {"bound": "hbm", "kernel": "k_scan_fused", "symbol": fsym,
                 "achieved": round(f_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(f_gbs / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic("k_scan_fused_bf16"),
+                "traffic": load_traffic(fsym),
                 "algorithmic_bytes_per_launch": f_bytes, "avg_launch_ms": round(f_ms, 5),
                 "mfma_frac": round(fwd_flops / (f_ms * 1e-3) / 1e12 / peak, 4)}
     else:
