@@ -251,7 +251,10 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3 : 1))) void k_born_bf16(
     BornArgs a) {
     constexpr int NM = D / 16;          // MFMA steps over the features (per part)
-    constexpr int KS = 4 * D + 16;      // LDS key row stride (bytes): D/4 quads of 16 B, padded
+    // LDS key row stride (bytes): D/4 quads of 16 B, padded.  At D = 16 a read takes
+    // 16 rows at 4 quads; with 96-byte rows the bank-conflict counter reads none for
+    // it, with 80-byte rows 4 cycles an instruction (measured in isolation)
+    constexpr int KS = D == 16 ? 96 : 4 * D + 16;
     // LDS value row stride (bytes): [vr | vi] of one key, padded by 32 B so that the
     // four rows one transposing read takes (32 B each) fall in distinct banks
     constexpr int VS = 4 * D + 32;
