@@ -71,7 +71,10 @@ __global__ __launch_bounds__(256) void k_state_scan(
     constexpr bool PAIR = PW == 2 && ScanTune<In>::pair;
     constexpr int RING = DIST < KJ ? DIST : KJ;
     constexpr int WPL = (C + 63) / 64;  // weights per lane and plane when loading a chunk's w
-    __shared__ float lds_w[4][2 * C];  // per wave: w re, w im of the current chunk
+    // per wave: w re, w im of the current chunk, each in four groups of KJ steps (the
+    // k-steps of lane group g) padded to KJ + 1, so that the four addresses a step
+    // reads fall in distinct banks at C = 128 too
+    __shared__ float lds_w[4][2 * 4 * (C / 4 + 1)];
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
     const int wv = wave_id();
@@ -180,8 +183,8 @@ __global__ __launch_bounds__(256) void k_state_scan(
         for (int k = 0; k < WPL; ++k) {
             const int pos = lane + 64 * k;
             if (pos < C) {
-                lw[pos] = wn_r[k];
-                lw[C + pos] = wn_i[k];
+                lw[pos + pos / KJ] = wn_r[k];
+                lw[4 * (KJ + 1) + pos + pos / KJ] = wn_i[k];
             }
         }
         if (c + 1 < nC) load_w(c + 1);
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256) void k_state_scan(
             else if (c + 1 < nC)  // wave-uniform
                 load(c + 1, jn - KJ, ring[j % RING]);
             __builtin_amdgcn_sched_barrier(0);
-            const float wr = lw[KJ * g + j], wi = lw[C + KJ * g + j];
+            const float wr = lw[(KJ + 1) * g + j], wi = lw[4 * (KJ + 1) + (KJ + 1) * g + j];
             const float pr = wr * o.br - wi * o.bi;  // (w B)[l, n]
             const float pi = wr * o.bi + wi * o.br;
             const float ps = pr + pi;
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     constexpr int WPL = (C + 63) / 64;
     constexpr int SPLIT = 4;  // chunks per round = waves per workgroup
     static_assert(!(PW == 2 && ScanTune<In>::pair), "paired X columns are not used here");
-    __shared__ float lds_w[SPLIT][2 * C];                // per wave: w of its current chunk
+    __shared__ float lds_w[SPLIT][2 * 4 * (C / 4 + 1)];  // per wave: w of its current chunk (padded as above)
     __shared__ floatx4 lds_s[2][SPLIT][2 * PW][64];      // [round parity][wave][tile re/im][lane]
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
@@ -340,8 +343,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             for (int k = 0; k < WPL; ++k) {
                 const int pos = lane + 64 * k;
                 if (pos < C) {
-                    lw[pos] = wn_r[k];
-                    lw[C + pos] = wn_i[k];
+                    lw[pos + pos / KJ] = wn_r[k];
+                    lw[4 * (KJ + 1) + pos + pos / KJ] = wn_i[k];
                 }
             }
             const int cn = c + SPLIT;  // this wave's next chunk
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 else if (cn < nC)  // wave-uniform
                     load(cn, jn - KJ, ring[j % RING]);
                 __builtin_amdgcn_sched_barrier(0);
-                const float wr = lw[KJ * g + j], wi = lw[C + KJ * g + j];
+                const float wr = lw[(KJ + 1) * g + j], wi = lw[4 * (KJ + 1) + (KJ + 1) * g + j];
                 const float pr = wr * o.br - wi * o.bi;  // (w B)[l, n]
                 const float pi = wr * o.bi + wi * o.br;
                 const float ps = pr + pi;
