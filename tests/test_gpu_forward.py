@@ -320,6 +320,23 @@ def test_bf16_more_sequences_than_cus():
         assert rel_err(y[b, :, h, :], yr) <= yb and rel_err(hT[b, h], hr) <= hb, (b, h)
 
 
+def test_bf16_one_sequence_per_cu():
+    """bf16 inputs at N = D = C = 64 with as many sequences as the device has CUs:
+    the largest grid of eight-wave workgroups (two halves exchanging state tiles
+    through LDS).  Sampled sequences, first, middle and last, within the path's
+    bounds of the oracle on the rounded inputs."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    inp = wl.random_forward(13, 1, 200, cus, 64, 64, 64, with_h0=True, with_dskip=True,
+                            in_dtype="bf16", name="onepercu")
+    pairs = [(0, 0), (0, cus // 2), (0, cus - 1)]
+    y, hT = _check_sampled(inp, pairs, TOL_BF16)
+    yb, hb = bf16_diagnostic_bounds(64, 64, 64)
+    ref = sampled_oracle(inp, pairs)
+    for (b, h), (yr, hr) in ref.items():
+        assert rel_err(y[b, :, h, :], yr) <= yb and rel_err(hT[b, h], hr) <= hb, (b, h)
+
+
 def test_config2_long_sampled():
     inp = wl.config2()
     _check_sampled(inp, [(0, 0), (0, 13), (0, 29), (0, 47)], TOL_F32)
