@@ -12,15 +12,16 @@
 // states and the chunk-to-chunk recurrence taken in its sequential form; the
 // skip term follows the burn-mamba step_constant readout).  The discretisation
 // and the chunk-local cumsum (acs, e = exp(acs), w = exp(acs[C-1] - acs),
-// cd = exp(acs[C-1])) are done here too, one chunk ahead, by the wave with the
-// fewest score tiles.
+// cd = exp(acs[C-1])) are done here too, one chunk ahead, by wave 0 (which takes
+// one score tile of the ten with four waves, none with eight).
 //
 // Every product runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  That
 // instruction takes A[i][k] from lane i + 16 (k / 8), slot k % 8, B[k][j] from
 // lane j + 16 (k / 8), slot k % 8, and leaves D[4g + r][j] in register r of lane
-// j + 16 g.  Wave w of the four owns the 16 columns p = 16 w + (lane % 16) of y
-// and of the state; its part of H sits in the accumulator layout of the
-// chunk-state product: tile nt, register r of lane p + 16 g <-> n = 16 nt + 4 g + r.
+// j + 16 g.  Wave w (of four; with eight, waves w and w + 4, see the kernel) owns
+// the 16 columns p = 16 w + (lane % 16) of y and of the state; its part of H sits
+// in the accumulator layout of the chunk-state product: tile nt, register r of lane
+// p + 16 g <-> n = 16 nt + 4 g + r.
 //  * y is formed transposed, y^T = H_c^T C^T (scaled by exp(acs)) + X^T M^T, so
 //    that register r of lane l + 16 g holds y[l][16 w + 4 g + r]: four adjacent
 //    columns of one row, stored with one 16-byte store per plane.
@@ -47,9 +48,9 @@
 // pieces) while the current chunk is computed, then written to LDS with the
 // pieces XOR-swizzled by the row; w B is formed from the same B pieces in fp32
 // and rounded to bf16 on the way.  The M tiles overwrite the B rows once the
-// scores are done.  65 KB of LDS: two workgroups per CU.  Rows of a partial last
-// chunk past the sequence read as zero through the buffer extents and their
-// stores are dropped.
+// scores are done.  69 KB of LDS with four waves (two workgroups per CU), 102 KB
+// with eight (one).  Rows of a partial last chunk past the sequence read as zero
+// through the buffer extents and their stores are dropped.
 #include <type_traits>
 
 #include "cssd_device.h"
