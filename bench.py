@@ -444,12 +444,16 @@ def time_backward(inp, steps, warmup, dev, seed=9, saved=False):
     r = math.sqrt(0.5)
     dy = [torch.randn((Bsz, T, H, D), generator=g, device=dev) * r for _ in range(2)]
     dhT = [torch.randn((Bsz, H, N, D), generator=g, device=dev) * r for _ in range(2)]
-    ws = torch.empty(cssd.cssd_backward_workspace_size(Bsz, T, H, D, N, inp.chunk),
+    code = cssd.CSSD_BF16 if inp.in_dtype == "bf16" else cssd.CSSD_F32
+    ws = torch.empty(cssd.cssd_backward_workspace_size(Bsz, T, H, D, N, inp.chunk, code),
                      dtype=torch.uint8, device=dev)
     ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
            d["A_im"], d["Dskip"], d["h0"])
-    out = cssd.cssd_forward(*ins, chunk=inp.chunk, workspace=ws)
-    y, hT = out[:2], out[2:]
+    if code == cssd.CSSD_BF16:
+        y, hT = None, None  # recomputed in fp32 inside the call
+    else:
+        out = cssd.cssd_forward(*ins, chunk=inp.chunk, workspace=ws)
+        y, hT = out[:2], out[2:]
     stream = torch.cuda.current_stream(dev)
 
     def run():
@@ -747,6 +751,13 @@ def main():
                                        / PEAK_FP32_MFMA_TFLOPS, 4),
                          "algorithmic_flops_per_launch": bfl,
                          "avg_launch_ms": round(bk["k_bwd_dx"], 5)}}
+        progress("timing the backward pass with bf16 inputs")
+        inp16 = wl.config1("bf16")
+        b16ms, b16k = time_backward(inp16, max(3, args.steps // 2), 2, dev)
+        del inp16
+        extra["backward_B8_T2048_H48_D64_N64_C64_bf16_inputs"] = {
+            "tokens_per_s": round(tokens / (b16ms * 1e-3), 1), "ms_per_step": round(b16ms, 4),
+            "kernels_avg_ms": {k: round(v, 5) for k, v in b16k.items()}}
         progress("timing the backward pass on the forward's saved states")
         sms, sk = time_backward(inp, max(3, args.steps // 2), 2, dev, saved=True)
         extra["backward_saved_states_B8_T2048_H48_D64_N64_C64_f32"] = {

@@ -24,7 +24,7 @@ CSSD_F32, CSSD_BF16 = 0, 1
 KERNEL_NAMES = ("k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
                 "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
                 "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db",
-                "k_state_scan", "k_state_scan_adj", "k_fill", "k_scan_fused")
+                "k_state_scan", "k_state_scan_adj", "k_fill", "k_scan_fused", "k_widen")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +63,8 @@ def load_library(path: Optional[str] = None):
             + [_vp] * 2 + [_vp] * 4 + [_vp]
         lib.cssd_backward_workspace_size.restype = ctypes.c_int
         lib.cssd_backward_workspace_size.argtypes = [_i64] * 6 + [ctypes.POINTER(_sz)]
+        lib.cssd_backward_workspace_size_dtype.restype = ctypes.c_int
+        lib.cssd_backward_workspace_size_dtype.argtypes = [_i64] * 6 + [_i32, ctypes.POINTER(_sz)]
         lib.cssd_backward.restype = ctypes.c_int
         lib.cssd_backward.argtypes = [_i64] * 6 + [_i32] + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 \
             + [_vp] * 2 + [_vp] * 4 + [_vp] * 6 + [_vp] * 4 + [_vp] * 2 + [_vp, _sz, _vp]
@@ -116,12 +118,14 @@ def cssd_forward_workspace_size(batch: int, seqlen: int, nheads: int, headdim: i
 
 
 def cssd_backward_workspace_size(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
-                                 chunk: int) -> int:
+                                 chunk: int, in_dtype: int = CSSD_F32) -> int:
+    """Workspace bytes of cssd_backward with x, B, C of in_dtype (CSSD_F32 or
+    CSSD_BF16: the latter adds the fp32 copies the inputs are widened into)."""
     out = _sz(0)
-    st = load_library().cssd_backward_workspace_size(batch, seqlen, nheads, headdim, dstate, chunk,
-                                                     ctypes.byref(out))
+    st = load_library().cssd_backward_workspace_size_dtype(batch, seqlen, nheads, headdim, dstate,
+                                                           chunk, in_dtype, ctypes.byref(out))
     if st != CSSD_OK:
-        raise CSSDError(st, "cssd_backward_workspace_size")
+        raise CSSDError(st, "cssd_backward_workspace_size_dtype")
     return int(out.value)
 
 
@@ -280,8 +284,11 @@ def cssd_backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0,
                   *, chunk: int, want_dh0: bool = True, workspace=None, stream=None):
     """Gradients of cssd_forward (see include/cssd.h): planar (dL/dRe, dL/dIm) pairs.
 
-    The first arguments are the forward inputs (float32); h0 as in cssd_forward;
-    y = (y_re, y_im) is the forward output for these inputs, dy = (dy_re, dy_im)
+    The first arguments are the forward inputs (x, B, C float32 or bfloat16, the
+    rest float32; bfloat16 planes are widened once into the workspace); h0 as in
+    cssd_forward;
+    y = (y_re, y_im), the forward output, is not read and may be None (the
+    gradients need only the inputs), dy = (dy_re, dy_im)
     its upstream gradient, dhT = (dhT_re, dhT_im) that of the final state or None.
     Returns a dict of float32 tensors: dx_re, dx_im, dB_re, dB_im, dC_re, dC_im,
     ddt, dA_re, dA_im, dD (None without Dskip), dh0_re, dh0_im (None unless
@@ -312,14 +319,25 @@ def _backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, 
     Bsz, T, H, D = x_re.shape
     N = B_re.shape[-1]
     f32 = (torch.float32,)
+    # bf16 x, B, C: cssd_backward widens them (cssd_backward_saved takes fp32 only)
+    if x_re.dtype == torch.bfloat16 and saved is None:
+        code, okd = CSSD_BF16, (torch.bfloat16,)
+    else:
+        code, okd = CSSD_F32, f32
     p = {}
-    for name, t, shp in (("x_re", x_re, (Bsz, T, H, D)), ("x_im", x_im, (Bsz, T, H, D)),
-                         ("B_re", B_re, (Bsz, T, H, N)), ("B_im", B_im, (Bsz, T, H, N)),
-                         ("C_re", C_re, (Bsz, T, H, N)), ("C_im", C_im, (Bsz, T, H, N)),
-                         ("dt", dt, (Bsz, T, H)), ("A_re", A_re, (H,)), ("A_im", A_im, (H,)),
-                         ("y_re", y[0], (Bsz, T, H, D)), ("y_im", y[1], (Bsz, T, H, D)),
-                         ("dy_re", dy[0], (Bsz, T, H, D)), ("dy_im", dy[1], (Bsz, T, H, D))):
-        p[name] = _check(t, name, shp, f32, dev)
+    for name, t, shp, dts in (("x_re", x_re, (Bsz, T, H, D), okd), ("x_im", x_im, (Bsz, T, H, D), okd),
+                              ("B_re", B_re, (Bsz, T, H, N), okd), ("B_im", B_im, (Bsz, T, H, N), okd),
+                              ("C_re", C_re, (Bsz, T, H, N), okd), ("C_im", C_im, (Bsz, T, H, N), okd),
+                              ("dt", dt, (Bsz, T, H), f32), ("A_re", A_re, (H,), f32),
+                              ("A_im", A_im, (H,), f32),
+                              ("dy_re", dy[0], (Bsz, T, H, D), f32), ("dy_im", dy[1], (Bsz, T, H, D), f32)):
+        p[name] = _check(t, name, shp, dts, dev)
+    # y is not read by the library; a given y is still checked for its shape
+    if y is None:
+        p["y_re"] = p["y_im"] = None
+    else:
+        for name, t in (("y_re", y[0]), ("y_im", y[1])):
+            p[name] = _check(t, name, (Bsz, T, H, D), f32, dev)
     p["Dskip"] = None if Dskip is None else _check(Dskip, "Dskip", (H,), f32, dev)
     hT = None if saved is None else saved[0]
     for key, pair, shp in (("h0", h0, (Bsz, H, N, D)), ("dhT", dhT, (Bsz, H, N, D)),
@@ -333,14 +351,14 @@ def _backward(x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0, y, 
          "dD": e(H) if Dskip is not None else None,
          "dh0_re": e(Bsz, H, N, D) if want_dh0 else None,
          "dh0_im": e(Bsz, H, N, D) if want_dh0 else None}
-    need = cssd_backward_workspace_size(Bsz, T, H, D, N, chunk)
+    need = cssd_backward_workspace_size(Bsz, T, H, D, N, chunk, code)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the same device")
     ws_bytes = workspace.numel() * workspace.element_size()
     ptr = lambda t: None if t is None else t.data_ptr()
-    head = (Bsz, T, H, D, N, int(chunk), CSSD_F32,
+    head = (Bsz, T, H, D, N, int(chunk), code,
             p["x_re"], p["x_im"], p["B_re"], p["B_im"], p["C_re"], p["C_im"],
             p["dt"], p["A_re"], p["A_im"], p["Dskip"], p["h0_re"], p["h0_im"], p["y_re"], p["y_im"])
     tail = (p["dy_re"], p["dy_im"], p["dhT_re"], p["dhT_im"],

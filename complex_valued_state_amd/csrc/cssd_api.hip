@@ -155,6 +155,13 @@ struct BwdLayout {
     size_t r_re, r_im, q1_re, q1_im, q2_re, q2_im, ddp, hT_re, hT_im, z_re, z_im, pa, total;
 };
 
+// bytes of the fp32 copies of bf16 x, B, C (two planes each) that cssd_backward
+// widens into its workspace after the backward's own layout
+size_t widen_bytes(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N) {
+    return 2 * round_up((size_t)(B * T * H * D) * sizeof(float)) +
+           4 * round_up((size_t)(B * T * H * N) * sizeof(float));
+}
+
 BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t N, int64_t C) {
     BwdLayout l;
     l.fwd = layout(B, T, H, D, N, C);
@@ -394,6 +401,17 @@ int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, 
     return CSSD_OK;
 }
 
+int cssd_backward_workspace_size_dtype(int64_t batch, int64_t seqlen, int64_t nheads,
+                                       int64_t headdim, int64_t dstate, int64_t chunk,
+                                       int32_t in_dtype, size_t* bytes) {
+    if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
+    const int st = cssd_backward_workspace_size(batch, seqlen, nheads, headdim, dstate, chunk,
+                                                bytes);
+    if (st != CSSD_OK || in_dtype == CSSD_F32 || *bytes == 0) return st;
+    *bytes += widen_bytes(batch, seqlen, nheads, headdim, dstate);
+    return CSSD_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -414,17 +432,24 @@ int backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int
     const int st = check_shape(batch, seqlen, nheads, headdim, dstate, chunk);
     if (st != CSSD_OK) return st;
     if (in_dtype != CSSD_F32 && in_dtype != CSSD_BF16) return CSSD_ERR_INVALID_ARG;
-    if (in_dtype != CSSD_F32) return CSSD_ERR_UNSUPPORTED;
+    // bf16 inputs: cssd_backward widens them (below); the saved form would need the
+    // chunk states of a bf16 forward, which the one-kernel bf16 path never stores
+    if (in_dtype == CSSD_BF16 && saved) return CSSD_ERR_UNSUPPORTED;
     if (empty_problem(batch, seqlen, nheads))
         return empty_backward(nheads, batch * nheads * dstate * headdim, dhT_re, dhT_im, dA_re,
                               dA_im, dD, dh0_re, dh0_im, stream);
+    // y is not read (the log-decay gradient takes conj(C) . dC in its place), so
+    // it is not checked either
+    (void)y_re;
+    (void)y_im;
+    const bool wide = in_dtype == CSSD_BF16;
     // row-vector reads need 16 bytes; the gradients are written element-wise
-    const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, y_re, y_im,
+    const void* req[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im,
                          dy_re, dy_im, dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt,
                          dA_re, dA_im};
-    const uintptr_t req_al[] = {16, 16, 16, 16, 16, 16, 4, 4, 4, 16, 16,
+    const uintptr_t req_al[] = {16, 16, 16, 16, 16, 16, 4, 4, 4,
                                 16, 16, 4, 4, 4, 4, 4, 4, 4, 4, 4};
-    for (int i = 0; i < 22; ++i)
+    for (int i = 0; i < 20; ++i)
         if (req[i] == nullptr || !aligned(req[i], req_al[i])) return CSSD_ERR_INVALID_ARG;
     if ((h0_re == nullptr) != (h0_im == nullptr) || (dhT_re == nullptr) != (dhT_im == nullptr) ||
         (dh0_re == nullptr) != (dh0_im == nullptr))
@@ -442,7 +467,7 @@ int backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int
         fhT_re = fhT_im = nullptr;
     }
     const void* ins[] = {x_re, x_im, B_re, B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re,
-                         h0_im, y_re, y_im, dy_re, dy_im, dhT_re, dhT_im, fhT_re, fhT_im};
+                         h0_im, dy_re, dy_im, dhT_re, dhT_im, fhT_re, fhT_im};
     const void* outs[] = {dx_re, dx_im, dB_re, dB_im, dC_re, dC_im, ddt, dA_re, dA_im, dD,
                           dh0_re, dh0_im};
     for (int i = 0; i < 12; ++i) {
@@ -454,17 +479,39 @@ int backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int
     }
 
     const BwdLayout L = bwd_layout(batch, seqlen, nheads, headdim, dstate, chunk);
-    if (workspace == nullptr || workspace_bytes < L.total ||
+    const size_t extra = wide ? widen_bytes(batch, seqlen, nheads, headdim, dstate) : 0;
+    if (workspace == nullptr || workspace_bytes < L.total + extra ||
         (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return CSSD_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (wide) {
+        // the bf16 planes widened once, after the backward's own layout; the fp32
+        // kernels then run on exactly the rounded values
+        const int64_t nx = batch * seqlen * nheads * headdim, nb = batch * seqlen * nheads * dstate;
+        const void* src[6] = {x_re, x_im, B_re, B_im, C_re, C_im};
+        const void* dst[6];
+        size_t off = L.total;
+        for (int i = 0; i < 6; ++i) {
+            const int64_t n = i < 2 ? nx : nb;
+            float* d = reinterpret_cast<float*>(ws + off);
+            if (timed(cssd::K_WIDEN, s, [&] {
+                    return cssd::launch_widen(static_cast<const uint16_t*>(src[i]), d, n, s);
+                }) != hipSuccess)
+                return CSSD_ERR_HIP;
+            dst[i] = d;
+            off += round_up((size_t)n * 4);
+        }
+        x_re = dst[0]; x_im = dst[1]; B_re = dst[2]; B_im = dst[3]; C_re = dst[4]; C_im = dst[5];
+        in_dtype = CSSD_F32;
+    }
     cssd::BwdArgs a;
     // the recomputed forward writes its final state into the workspace, not y
     a.f = fwd_args(batch, seqlen, nheads, headdim, dstate, chunk, in_dtype, x_re, x_im, B_re,
                    B_im, C_re, C_im, dt, A_re, A_im, Dskip, h0_re, h0_im, nullptr, nullptr,
                    reinterpret_cast<float*>(ws + L.hT_re), reinterpret_cast<float*>(ws + L.hT_im),
                    ws, L.fwd);
-    a.y_re = y_re; a.y_im = y_im; a.dy_re = dy_re; a.dy_im = dy_im;
+    a.dy_re = dy_re; a.dy_im = dy_im;
     a.dhT_re = dhT_re; a.dhT_im = dhT_im;
     a.dx_re = dx_re; a.dx_im = dx_im; a.db_re = dB_re; a.db_im = dB_im;
     a.dc_re = dC_re; a.dc_im = dC_im; a.ddt = ddt; a.da_re = dA_re; a.da_im = dA_im; a.dd = dD;
@@ -482,7 +529,6 @@ int backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int
     a.z_im = reinterpret_cast<double*>(ws + L.z_im);
     a.pa = reinterpret_cast<double*>(ws + L.pa);
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     // forward recomputation: cumsums, chunk states, carry-in states H_c and hT
     if (!saved) {
         if (timed(cssd::K_CUMSUM, s, [&] { return cssd::launch_cumsum(a.f, s); }) != hipSuccess)
@@ -898,7 +944,7 @@ const char* cssd_kernel_name(int kernel_id) {
         "k_cumsum", "k_chunk_state", "k_state_pass", "k_chunk_scan", "k_step",
         "k_step_infinite", "k_bwd_dx", "k_bwd_dc", "k_bwd_dz",
         "k_phase_summary", "k_phase_carry", "k_phase_out", "k_born", "k_bwd_db",
-        "k_state_scan", "k_state_scan_adj", "k_fill", "k_scan_fused"};
+        "k_state_scan", "k_state_scan_adj", "k_fill", "k_scan_fused", "k_widen"};
     if (kernel_id < 0 || kernel_id >= cssd::K_COUNT) return nullptr;
     return names[kernel_id];
 }

@@ -10,7 +10,7 @@ enum KernelId { K_CUMSUM = 0, K_CHUNK_STATE = 1, K_STATE_PASS = 2, K_CHUNK_SCAN 
                 K_STEP_INFINITE = 5, K_BWD_DX = 6, K_BWD_DC = 7, K_BWD_DZ = 8,
                 K_PHASE_SUMMARY = 9, K_PHASE_CARRY = 10, K_PHASE_OUT = 11, K_BORN = 12,
                 K_BWD_DB = 13, K_STATE_SCAN = 14, K_STATE_SCAN_ADJ = 15, K_FILL = 16,
-                K_SCAN_FUSED = 17, K_COUNT = 18 };
+                K_SCAN_FUSED = 17, K_WIDEN = 18, K_COUNT = 19 };
 
 struct FwdArgs {
     int64_t B, T, H, D, N, C, nC;
@@ -27,14 +27,13 @@ struct FwdArgs {
 // output and upstream gradients, the gradients, and the extra workspace.
 struct BwdArgs {
     FwdArgs f;
-    const float *y_re, *y_im;                // forward output
     const float *dy_re, *dy_im;              // dL/dy
     const float *dhT_re, *dhT_im;            // dL/dhT or NULL
     float *dx_re, *dx_im, *db_re, *db_im, *dc_re, *dc_im, *ddt, *da_re, *da_im, *dd;
     float *dh0_re, *dh0_im;                  // or NULL
     // workspace
     float *r_re, *r_im;                      // adjoint chunk states Q_c, then R_{c+1}
-    float *q1_re, *q1_im, *q2_re, *q2_im;    // per position: the dx and y halves of q
+    float *q1_re, *q1_im, *q2_re, *q2_im;    // per position: the dx and dC halves of q
     float *ddp;                              // per position: Re(dy . conj(x))
     const float *hT_re, *hT_im;              // the forward's final state (read only)
     double *z_re, *z_im;                     // per chunk, two partials: <R_{c+1}, H_{c+1}>
@@ -74,6 +73,8 @@ hipError_t device_cu_count(int* cus);
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_cumsum(const FwdArgs& a, hipStream_t stream);
+// n bf16 values (16-byte aligned) widened to fp32 (16-byte aligned)
+hipError_t launch_widen(const uint16_t* src, float* dst, int64_t n, hipStream_t stream);
 // chunk states and the chunk-to-chunk pass fused (forward): writes H_c and hT
 hipError_t launch_state_scan(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t stream);

@@ -23,7 +23,10 @@
 // recurrence for G_t . conj(h_t) telescopes to
 //   dz_t = sum_{l >= t} q_l + <dhT, hT>,
 //   q_l  = sum_p dy_l[p] conj(y_l[p] - D x_l[p]) - conj(x_l[p]) (dx_l[p] - D dy_l[p])
-// (z_t = softplus(dt_t) A, <u, v> = sum u conj(v)), and the part of that sum from
+// (z_t = softplus(dt_t) A, <u, v> = sum u conj(v)).  As y_l - D x_l = C_l . h_l and
+// dC_l = dy_l conj(h_l), the first sum is conj(C_l) . dC_l, which the dC kernels
+// form from their own output: y is never read, and q does not take the rounding
+// of whatever forward produced y.  The part of the sum for dz_t from
 // the start of chunk c + 1 onwards is <R_{c+1}, H_{c+1}> (the same telescoping
 // stopped at a chunk boundary).  So for t in chunk c
 //   dz_t = sum_{l >= t, l in chunk c} q_l + <R_{c+1}, H_{c+1}>,
@@ -78,6 +81,22 @@ __device__ __forceinline__ void seg_exp(const double* ar, const double* ai, int 
     double dv = ai[t] - ai[s];
     dv -= rint(dv);
     cexp_scaled((float)d2, (float)(conj ? -dv : dv), lr, li);
+}
+
+// sum over the 16 lanes of a lane group, complete in the group's last lane
+// (lane % 16 == 15): inclusive prefix sums by DPP row shifts of 1, 2, 4, 8, whose
+// out-of-row sources read 0; the moves stay in the vector unit
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_total(float v) {
+    v += dpp_f32<0x111>(v);  // row_shr:1
+    v += dpp_f32<0x112>(v);  // row_shr:2
+    v += dpp_f32<0x114>(v);  // row_shr:4
+    v += dpp_f32<0x118>(v);  // row_shr:8
+    return v;
 }
 
 // sum over the 16 lanes of a lane group (lane % 16 varies, lane / 16 fixed)
@@ -633,12 +652,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // The chunk's dY and X rows go to LDS; each wave loads its column blocks of
 // conj(H_c) (element-wise from the fragments) and conj(B) into registers.
 //  1. state term dY H_c^H on the wave's columns, rows scaled by conj(e[t]);
-//     wave w also forms q2 and the dD partial of rows [16 w, 16 w + 16).
+//     wave w also forms the dD partial of rows [16 w, 16 w + 16).
 //  2. the causal tiles of P^T = conj(X) dY^T (t tile >= l tile) split over the
 //     waves; K = conj(L) P comes out with register r holding
 //     [t = t0 + lane%16][l = l0 + 4 (lane/16) + r], the A-operand layout of
 //     the product with conj(B) rows; exchanged through LDS (over the X rows).
-//  3. dC[t, n] += sum_l K[t, l] conj(B[l, n]).
+//  3. dC[t, n] += sum_l K[t, l] conj(B[l, n]); then q2[t] = conj(C[t]) . dC[t].
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dc_lds(
     BwdArgs a) {
@@ -649,7 +668,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     constexpr int PLANE = C * D, IPP = PLANE / 256;
     constexpr int XPLANE = PLANE / 2, XIPP = XPLANE / 256;  // half of the X rows
     // The X rows are staged in halves: rows 0-31 for the seven tiles with lt < 2
-    // (and the q2 rows of waves 0 and 1), then rows 32-63 for the other three
+    // (and the dD rows of waves 0 and 1), then rows 32-63 for the other three
     // (and waves 2 and 3): 52 KB of LDS, three workgroups per CU.
     __shared__ floatx4 lds_g4[2 * PLANE / 4];   // dY rows, later the K tiles
     __shared__ floatx4 lds_x4[2 * XPLANE / 4];  // X rows, half at a time
@@ -710,51 +729,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const BufRes rb_r = make_buf(static_cast<const float*>(f.b_re) + v.row0 * N, v.extN * 4);
     const BufRes rb_i = make_buf(static_cast<const float*>(f.b_im) + v.row0 * N, v.extN * 4);
     float cb_r[NLT][4], cb_i[NLT][4];
-    // y rows 16 w + li for q2
-    const BufRes ry_r = make_buf(a.y_re + v.row0 * D, v.extD * 4);
-    const BufRes ry_i = make_buf(a.y_im + v.row0 * D, v.extD * 4);
-    floatx4 yq_r[PT], yq_i[PT];
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-        yq_r[k] = buf_f32x4(ry_r, (uint32_t)(16 * w + li) * v.sD + 16 * k + 4 * g);
-        yq_i[k] = buf_f32x4(ry_i, (uint32_t)(16 * w + li) * v.sD + 16 * k + 4 * g);
-    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
 
     auto row4 = [&](const float* plane, int row, int ch) -> floatx4 {
         return *reinterpret_cast<const floatx4*>(plane + row * D + 4 * lds_swz<D>(row, ch));
     };
-    const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
 
-    // ---- the y half of q and the dD partial for row t = 16 w + li, with the X
-    // rows staged from row x0 on (called in the phase that holds row t)
-    auto q2_row = [&](int x0) {
+    // ---- the dD partial Re(dy . conj(x)) for row t = 16 w + li, with the X rows
+    // staged from row x0 on (called in the phase that holds row t)
+    auto dd_row = [&](int x0) {
         const int t = 16 * w + li;
-        float qr = 0.f, qi = 0.f, dd = 0.f;
+        float dd = 0.f;
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
             const floatx4 gr = row4(ldg, t, 4 * k + g), gi = row4(ldg + PLANE, t, 4 * k + g);
             const floatx4 xr = row4(ldx, t - x0, 4 * k + g);
             const floatx4 xi = row4(ldx + XPLANE, t - x0, 4 * k + g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float ur = yq_r[k][e] - dk * xr[e], ui = yq_i[k][e] - dk * xi[e];
-                qr += gr[e] * ur + gi[e] * ui;  // dy conj(y - D x)
-                qi += gi[e] * ur - gr[e] * ui;
-                dd += gr[e] * xr[e] + gi[e] * xi[e];
-            }
+            for (int e = 0; e < 4; ++e) dd += gr[e] * xr[e] + gi[e] * xi[e];
         }
-        qr = sum_groups(qr);
-        qi = sum_groups(qi);
         dd = sum_groups(dd);
-        if (g == 0) {
-            a.q2_re[v.pbase + t] = qr;
-            a.q2_im[v.pbase + t] = qi;
-            a.ddp[v.pbase + t] = dd;
-        }
+        if (g == 0) a.ddp[v.pbase + t] = dd;
     };
-    if (w < 2) q2_row(0);
+    if (w < 2) dd_row(0);
 
     // ---- 1. state term dY H_c^H, then the row factor conj(e[t])
     CTile acc[NLT];
@@ -832,7 +830,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     stage_plane(f.x_im, ldx + XPLANE, XIPP % W, C / 2, XIPP);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (w >= 2) q2_row(C / 2);
+    if (w >= 2) dd_row(C / 2);
 #pragma unroll
     for (int j = 0; j < MQ; ++j)
         if (j < nq && second_half(qs[j])) score_tile(qs[j], C / 2, m_r[j], m_i[j]);
@@ -857,9 +855,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
     __syncthreads();
 
-    // ---- 3. dC[tt] += K(tt, lt) conj(B)[lt rows, this wave's columns], lt <= tt
+    // ---- 3. dC[tt] += K(tt, lt) conj(B)[lt rows, this wave's columns], lt <= tt.
+    // Row tile lt of dC is complete after step lt (it sums the tiles lt' <= lt):
+    // it is stored there, and its part of q2[t] = conj(C[t]) . dC[t] (this wave's
+    // 16 columns, summed over the lane group) goes to LDS, where the cumsums and e
+    // are no longer read (two barriers since step 2); the C values are loaded at
+    // the top of the step, ahead of its matrix products.
+    const BufRes rdc_r = make_buf(a.dc_re + v.row0 * N, v.extN * 4);
+    const BufRes rdc_i = make_buf(a.dc_im + v.row0 * N, v.extN * 4);
+    const BufRes rc_r = make_buf(static_cast<const float*>(f.c_re) + v.row0 * N, v.extN * 4);
+    const BufRes rc_i = make_buf(static_cast<const float*>(f.c_im) + v.row0 * N, v.extN * 4);
+    float* const lq = lda;  // [W][C][2]
 #pragma unroll
     for (int lt = 0; lt < NLT; ++lt) {
+        float qc_r[4], qc_i[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (uint32_t)(lt * 16 + 4 * g + r) * v.sN + 16 * w + li;
+            qc_r[r] = buf_f32(rc_r, off);
+            qc_i[r] = buf_f32(rc_i, off);
+        }
         float bs[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) bs[r] = cb_r[lt][r] + cb_i[lt][r];
@@ -872,23 +887,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             for (int r = 0; r < 4; ++r)
                 ctile_mac(acc[tt], mr[r], mi[r], mr[r] + mi[r], cb_r[lt][r], cb_i[lt][r], bs[r]);
         }
-    }
-
-    // ---- stores; register r <-> row t = 16 tt + 4g + r, column n = 16w + li
-    const BufRes rdc_r = make_buf(a.dc_re + v.row0 * N, v.extN * 4);
-    const BufRes rdc_i = make_buf(a.dc_im + v.row0 * N, v.extN * 4);
-#pragma unroll
-    for (int tt = 0; tt < NLT; ++tt)
+        // stores and q2 part of row tile lt; register r <-> row t = 16 lt + 4g + r,
+        // column n = 16w + li
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const uint32_t off = (uint32_t)(tt * 16 + 4 * g + r) * v.sN + 16 * w + li;
-            buf_store_f32(ctile_re(acc[tt], r), rdc_r, off);
-            buf_store_f32(ctile_im(acc[tt], r), rdc_i, off);
+            const int t = lt * 16 + 4 * g + r;
+            const uint32_t off = (uint32_t)t * v.sN + 16 * w + li;
+            const float dr = ctile_re(acc[lt], r), di = ctile_im(acc[lt], r);
+            buf_store_f32(dr, rdc_r, off);
+            buf_store_f32(di, rdc_i, off);
+            const float pr = row_total(qc_r[r] * dr + qc_i[r] * di);
+            const float pi = row_total(qc_r[r] * di - qc_i[r] * dr);
+            if (li == 15) {
+                lq[(w * C + t) * 2] = pr;
+                lq[(w * C + t) * 2 + 1] = pi;
+            }
         }
+    }
+    __syncthreads();
+    if (threadIdx.x < C) {
+        const int t = threadIdx.x;
+        float qr = 0.f, qi = 0.f;
+#pragma unroll
+        for (int u = 0; u < W; ++u) {
+            qr += lq[(u * C + t) * 2];
+            qi += lq[(u * C + t) * 2 + 1];
+        }
+        a.q2_re[v.pbase + t] = qr;
+        a.q2_im[v.pbase + t] = qi;
+    }
 }
 
 // ----------------------------------------------------------------------------
-// dC for row tile tt of one chunk, plus the y half of q and the dD partials
+// dC for row tile tt of one chunk, plus the dC half of q and the dD partials
 // ----------------------------------------------------------------------------
 template <int C, int N, int D>
 __device__ __forceinline__ void dc_tile(const BwdArgs& a, int64_t chunk, int tt) {
@@ -903,15 +934,12 @@ __device__ __forceinline__ void dc_tile(const BwdArgs& a, int64_t chunk, int tt)
     const BufRes rb_i = make_buf(static_cast<const float*>(f.b_im) + v.row0 * N, v.extN * 4);
     const BufRes rx_r = make_buf(static_cast<const float*>(f.x_re) + v.row0 * D, v.extD * 4);
     const BufRes rx_i = make_buf(static_cast<const float*>(f.x_im) + v.row0 * D, v.extD * 4);
-    const BufRes ry_r = make_buf(a.y_re + v.row0 * D, v.extD * 4);
-    const BufRes ry_i = make_buf(a.y_im + v.row0 * D, v.extD * 4);
     const BufRes rg_r = make_buf(a.dy_re + v.row0 * D, v.extD * 4);
     const BufRes rg_i = make_buf(a.dy_im + v.row0 * D, v.extD * 4);
     const BufRes rh_r = make_buf(f.st_re + chunk * (int64_t)N * D, N * D * 4);
     const BufRes rh_i = make_buf(f.st_im + chunk * (int64_t)N * D, N * D * 4);
     const double* __restrict__ ar = f.acs_re + v.pbase;
     const double* __restrict__ ai = f.acs_im + v.pbase;
-    const float dk = f.dskip != nullptr ? f.dskip[v.h] : 0.f;
 
     // rows t0 + li of dY, as A-operand (over p) and as B-operand of conj(X) dY^T
     floatx4 gq_r[PT], gq_i[PT];
@@ -921,30 +949,18 @@ __device__ __forceinline__ void dc_tile(const BwdArgs& a, int64_t chunk, int tt)
         gq_i[k] = buf_f32x4(rg_i, (uint32_t)(t0 + li) * v.sD + 16 * k + 4 * g);
     }
 
-    // ---- the y half of q and the dD partial for rows t = t0 + li
+    // ---- the dD partial Re(dy . conj(x)) for rows t = t0 + li
     {
-        float qr = 0.f, qi = 0.f, dd = 0.f;
+        float dd = 0.f;
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
             const uint32_t off = (uint32_t)(t0 + li) * v.sD + 16 * k + 4 * g;
-            const floatx4 yr = buf_f32x4(ry_r, off), yi = buf_f32x4(ry_i, off);
             const floatx4 xr = buf_f32x4(rx_r, off), xi = buf_f32x4(rx_i, off);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float ur = yr[e] - dk * xr[e], ui = yi[e] - dk * xi[e];
-                qr += gq_r[k][e] * ur + gq_i[k][e] * ui;  // dy conj(y - D x)
-                qi += gq_i[k][e] * ur - gq_r[k][e] * ui;
-                dd += gq_r[k][e] * xr[e] + gq_i[k][e] * xi[e];
-            }
+            for (int e = 0; e < 4; ++e) dd += gq_r[k][e] * xr[e] + gq_i[k][e] * xi[e];
         }
-        qr = sum_groups(qr);
-        qi = sum_groups(qi);
         dd = sum_groups(dd);
-        if (g == 0) {
-            a.q2_re[v.pbase + t0 + li] = qr;
-            a.q2_im[v.pbase + t0 + li] = qi;
-            a.ddp[v.pbase + t0 + li] = dd;
-        }
+        if (g == 0) a.ddp[v.pbase + t0 + li] = dd;
     }
 
     // accumulators: register r <-> row t = t0 + 4g + r, column n = 16 nt + li
@@ -1026,6 +1042,29 @@ __device__ __forceinline__ void dc_tile(const BwdArgs& a, int64_t chunk, int tt)
         for (int nt = 0; nt < NK; ++nt) {
             buf_store_f32(ctile_re(dc[nt], r), rdc_r, trow * v.sN + 16 * nt + li);
             buf_store_f32(ctile_im(dc[nt], r), rdc_i, trow * v.sN + 16 * nt + li);
+        }
+    }
+
+    // ---- the dC half of q, conj(C[t]) . dC[t], for rows t = t0 + 4g + r
+    const BufRes rc_r = make_buf(static_cast<const float*>(f.c_re) + v.row0 * N, v.extN * 4);
+    const BufRes rc_i = make_buf(static_cast<const float*>(f.c_im) + v.row0 * N, v.extN * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t trow = (uint32_t)(t0 + 4 * g + r);
+        float pr = 0.f, pi = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NK; ++nt) {
+            const float cr = buf_f32(rc_r, trow * v.sN + 16 * nt + li);
+            const float ci = buf_f32(rc_i, trow * v.sN + 16 * nt + li);
+            const float dr = ctile_re(dc[nt], r), di = ctile_im(dc[nt], r);
+            pr += cr * dr + ci * di;
+            pi += cr * di - ci * dr;
+        }
+        pr = row_total(pr);
+        pi = row_total(pi);
+        if (li == 15) {
+            a.q2_re[v.pbase + trow] = pr;
+            a.q2_im[v.pbase + trow] = pi;
         }
     }
 }

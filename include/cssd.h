@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define CSSD_VERSION 107 /* major*100 + minor */
+#define CSSD_VERSION 108 /* major*100 + minor */
 
 typedef enum cssd_status {
     CSSD_OK = 0,
@@ -222,11 +222,23 @@ int cssd_step(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
               float *y_re, float *y_im, void *stream);
 
 /*
- * Workspace bytes cssd_backward needs for this shape (at least the forward's).
+ * Workspace bytes cssd_backward needs for this shape (at least the forward's),
+ * with fp32 inputs.
  */
 int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
                                  int64_t headdim, int64_t dstate, int64_t chunk,
                                  size_t *bytes);
+
+/*
+ * Workspace bytes cssd_backward needs for this shape with inputs of in_dtype:
+ * for CSSD_F32 as cssd_backward_workspace_size; for CSSD_BF16 that plus the fp32
+ * copies of x, B, C it widens the inputs into (4 bytes an element, 2 planes each,
+ * each rounded up to 256 bytes).  Returns CSSD_ERR_INVALID_ARG for another
+ * in_dtype or a NULL bytes, and the shape checks of cssd_backward_workspace_size.
+ */
+int cssd_backward_workspace_size_dtype(int64_t batch, int64_t seqlen, int64_t nheads,
+                                       int64_t headdim, int64_t dstate, int64_t chunk,
+                                       int32_t in_dtype, size_t *bytes);
 
 /*
  * Gradients of cssd_forward (the pages train the scan by automatic
@@ -239,11 +251,16 @@ int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
  * x, B, C), ddt [B,T,H], dA [H] and dDskip [H] (summed over batch and time), and
  * dh0 [B,H,N,D].
  *
- *   x_* .. h0_*      exactly the inputs of the cssd_forward call (fp32 only:
- *                    in_dtype must be CSSD_F32, else CSSD_ERR_UNSUPPORTED)
- *   y_re, y_im       that call's output y [B,T,H,D]; it enters the gradient of
- *                    the log-decay (see below), so it must be the output for
- *                    these inputs
+ *   x_* .. h0_*      exactly the inputs of the cssd_forward call.  With
+ *                    in_dtype CSSD_BF16 (the bf16-input setting of the pages'
+ *                    training: the phase-state paper, §7, training protocol)
+ *                    x, B, C are bf16 planes: they are widened to fp32 once into
+ *                    the workspace (which must then hold
+ *                    cssd_backward_workspace_size_dtype bytes) and the gradients
+ *                    are those of the scan at exactly the rounded values, in fp32
+ *   y_re, y_im       not read, may be NULL (that call's output y has a place in
+ *                    the signature; the gradients need only the inputs, see
+ *                    below)
  *   dy_re, dy_im     [B,T,H,D] upstream gradient of y
  *   dhT_re, dhT_im   [B,H,N,D] upstream gradient of the final state, or both
  *                    NULL (zero)
@@ -257,9 +274,15 @@ int cssd_backward_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
  * dz_t (z_t = softplus(dt_t) A) uses the identity
  *   dz_t = sum_{l>=t} [dy_l . conj(y_l - D x_l) - conj(x_l) . (dx_l - D dy_l)]
  *          + <dhT, hT>,
- * obtained by summing the reverse recurrence of dL/dh_t (<u, v> = sum u conj(v)).
- * Alignment: x, B, C, y, dy (and h0, dhT, dh0) 16 bytes, the rest their
- * element size.  Outputs may not alias inputs or each other.
+ * obtained by summing the reverse recurrence of dL/dh_t (<u, v> = sum u conj(v)),
+ * with dy_l . conj(y_l - D x_l) taken as conj(C_l) . dC_l (y_l - D x_l = C_l h_l,
+ * dC_l = dy_l conj(h_l)).  So y is never read, and the gradients do not take the
+ * rounding of the forward that produced it: those sums cancel, and a bf16
+ * forward's y would make ddt and dA several percent wrong.
+ * Alignment: x, B, C, dy (and h0, dhT, dh0) 16 bytes (bf16 planes too), the
+ * rest their element size.  Outputs may not alias inputs or each other.
+ * Launches with bf16 inputs: six widen launches, then the kernels of the fp32
+ * call.
  */
 int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                   int64_t dstate, int64_t chunk, int32_t in_dtype,
@@ -288,10 +311,13 @@ int cssd_backward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim
  * way: Mamba-3-Lite docs, "SSD Theory", autograd notes), which saves the
  * recomputation's launches (ids 0 and 14).  The gradients are bit-identical to
  * cssd_backward's for the same inputs.
+ *   y_re, y_im     not read, may be NULL (as in cssd_backward)
  *   hT_re, hT_im   [B,H,N,D] the forward's final state; required when dhT is
  *                  given (it enters <dhT, hT>), else may be NULL
- * Every other argument as cssd_backward.  A workspace that does not hold that
- * forward's results gives undefined gradients (this is not detected).
+ * Every other argument as cssd_backward, except that in_dtype must be CSSD_F32
+ * (else CSSD_ERR_UNSUPPORTED: the bf16-input forward keeps no chunk states).  A
+ * workspace that does not hold that forward's results gives undefined gradients
+ * (this is not detected).
  */
 int cssd_backward_saved(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                         int64_t dstate, int64_t chunk, int32_t in_dtype,
@@ -440,7 +466,9 @@ int cssd_born_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
  * cssd_backward_saved does not; both then run 15 state_scan_adj, the adjoint chunk states and pass fused, where
  * dstate = headdim = chunk = 64, else 1 and 2 in their adjoint modes), 9 phase_summary,
  * 10 phase_carry, 11 phase_out (cssd_phase_scan), 12 born (cssd_born_attention),
- * 16 fill (the states and zeroed sums of an empty problem, one launch per plane).
+ * 16 fill (the states and zeroed sums of an empty problem, one launch per plane),
+ * 17 scan_fused (cssd_forward with bf16 inputs at headdim = dstate = chunk = 64),
+ * 18 widen (cssd_backward with bf16 inputs: one launch per widened plane).
  * cssd_kernel_name(k) gives the device symbol stem of each id (NULL if out of
  * range).
  * Launches on a stream that is being captured into a HIP graph are not

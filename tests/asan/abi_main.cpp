@@ -173,14 +173,49 @@ int main() {
                     want += "bwd_dx bwd_db bwd_dc bwd_dz ";
                     EXPECT(calls() == want, "backward sequence %s", calls().c_str());
                 }
+                // bf16 inputs: the fp32-size workspace is too small; with the bf16 size
+                // the six planes are widened inside it, then the fp32 sequence runs;
+                // the saved-state form takes fp32 only
+                Fwd fb(B, T, H, D, N, C, CSSD_BF16);
+                size_t bbytes = 0;
+                EXPECT(cssd_backward_workspace_size_dtype(B, T, H, D, N, C, CSSD_BF16, &bbytes) ==
+                           CSSD_OK, "bws bf16");
+                EXPECT(bbytes > bytes, "bf16 workspace %zu against %zu", bbytes, bytes);
+                Buf wsb(bbytes);
+                // (y is not read: NULL here)
+                auto bf16_backward = [&](size_t nbytes) {
+                    return cssd_backward(B, T, H, D, N, C, CSSD_BF16, fb.x_re.p, fb.x_im.p,
+                                         fb.b_re.p, fb.b_im.p, fb.c_re.p, fb.c_im.p, fb.dtb.f(),
+                                         fb.a_re.f(), fb.a_im.f(), nullptr, nullptr, nullptr,
+                                         nullptr, nullptr, dy_re.f(), dy_im.f(), nullptr,
+                                         nullptr, g[0].f(), g[1].f(), g[2].f(), g[3].f(),
+                                         g[4].f(), g[5].f(), g[6].f(), g[7].f(), g[8].f(),
+                                         nullptr, nullptr, nullptr, wsb.p, nbytes, nullptr);
+                };
+                stub_register_workspace(wsb.p, bbytes);
                 stub_reset();
-                EXPECT(cssd_backward(B, T, H, D, N, C, CSSD_BF16, f.x_re.p, f.x_im.p, f.b_re.p,
-                                     f.b_im.p, f.c_re.p, f.c_im.p, f.dtb.f(), f.a_re.f(),
-                                     f.a_im.f(), nullptr, nullptr, nullptr, f.y_re.f(), f.y_im.f(),
-                                     dy_re.f(), dy_im.f(), nullptr, nullptr, g[0].f(), g[1].f(),
-                                     g[2].f(), g[3].f(), g[4].f(), g[5].f(), g[6].f(), g[7].f(),
-                                     g[8].f(), nullptr, nullptr, nullptr, ws.p, bytes,
-                                     nullptr) == CSSD_ERR_UNSUPPORTED, "bf16 backward");
+                EXPECT(bf16_backward(bytes) == CSSD_ERR_WORKSPACE, "bf16 backward, fp32 workspace");
+                EXPECT(calls().empty(), "bf16 backward refused, launched %s", calls().c_str());
+                stub_reset();
+                EXPECT(bf16_backward(bbytes) == CSSD_OK, "bf16 backward");
+                EXPECT(stub_bad() == 0, "bf16 backward workspace regions");
+                {
+                    const bool fused = D == 64 && N == 64 && C == 64;
+                    std::string want = "widen widen widen widen widen widen cumsum state_scan ";
+                    want += fused ? "state_scan_adj " : "chunk_state_adjoint state_pass_adjoint ";
+                    want += "bwd_dx bwd_db bwd_dc bwd_dz ";
+                    EXPECT(calls() == want, "bf16 backward sequence %s", calls().c_str());
+                }
+                stub_reset();
+                EXPECT(cssd_backward_saved(B, T, H, D, N, C, CSSD_BF16, fb.x_re.p, fb.x_im.p,
+                                           fb.b_re.p, fb.b_im.p, fb.c_re.p, fb.c_im.p, fb.dtb.f(),
+                                           fb.a_re.f(), fb.a_im.f(), nullptr, nullptr, nullptr,
+                                           fb.y_re.f(), fb.y_im.f(), fb.hT_re.f(), fb.hT_im.f(),
+                                           dy_re.f(), dy_im.f(), nullptr, nullptr, g[0].f(),
+                                           g[1].f(), g[2].f(), g[3].f(), g[4].f(), g[5].f(),
+                                           g[6].f(), g[7].f(), g[8].f(), nullptr, nullptr, nullptr,
+                                           wsb.p, bbytes, nullptr) == CSSD_ERR_UNSUPPORTED,
+                       "bf16 saved backward");
             }
     // ---- decode step and the constant-input calls
     {

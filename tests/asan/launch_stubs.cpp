@@ -60,6 +60,11 @@ hipError_t device_cu_count(int* cus) {
     *cus = 256;
     return hipSuccess;
 }
+hipError_t launch_widen(const uint16_t*, float* dst, int64_t n, hipStream_t) {
+    stub::check(dst, (size_t)n * 4, "widened plane");
+    stub::calls.push_back("widen");
+    return hipSuccess;
+}
 hipError_t launch_cumsum(const FwdArgs& a, hipStream_t) {
     stub::check_fwd(a);
     stub::calls.push_back("cumsum");

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("cssd_forward", "cssd_backward", "cssd_backward_saved",
-                     "cssd_backward_workspace_size",
+                     "cssd_backward_workspace_size", "cssd_backward_workspace_size_dtype",
                      "cssd_step", "cssd_step_n", "cssd_step_infinite", "cssd_phase_scan",
                      "cssd_phase_scan_workspace_size", "cssd_born_attention",
                      "cssd_forward_workspace_size", "cssd_status_string", "cssd_version"):
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cssd_version() == 107
+    assert lib.cssd_version() == 108
     for st in range(6):
         assert lib.cssd_status_string(st)
     assert b"unknown" in lib.cssd_status_string(99)
@@ -184,7 +184,20 @@ def test_backward_validation(lib):
         *shape, dt, *ins, None, None, *g, ws, 1 << 30, None)
     assert lib.cssd_backward(*args(grads)) == 1          # dh0_re without dh0_im
     good = p[20:30] + [None, None]
-    assert lib.cssd_backward(*args(good, dt=1)) == 2     # bf16 inputs not supported
+    # bf16 inputs need the widened copies in the workspace: a workspace of exactly
+    # the fp32 size is refused before anything is launched
+    fsz, bsz = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.cssd_backward_workspace_size_dtype(1, 64, 2, 16, 16, 16, 0, ctypes.byref(fsz)) == 0
+    assert lib.cssd_backward_workspace_size_dtype(1, 64, 2, 16, 16, 16, 1, ctypes.byref(bsz)) == 0
+    assert lib.cssd_backward_workspace_size_dtype(1, 64, 2, 16, 16, 16, 2, ctypes.byref(bsz)) == 1
+    short = lambda g: (1, 64, 2, 16, 16, 16, 1, *ins, None, None, *g, ws, fsz.value, None)
+    assert lib.cssd_backward(*short(good)) == 3           # CSSD_ERR_WORKSPACE
+    # y is not read and may be NULL: the pointer checks pass and the short
+    # workspace is what is refused (nothing launched)
+    noy = ins[:12] + [None, None] + ins[14:]
+    for dt in (0, 1):
+        assert lib.cssd_backward(1, 64, 2, 16, 16, 16, dt, *noy, None, None, *good, ws, 256,
+                                 None) == 3
     assert lib.cssd_backward(*args(good, shape=(1, 64, 2, 16, 24, 16))) == 2
     bad = list(good); bad[0] = ins[0]                     # dx aliases x
     assert lib.cssd_backward(*args(bad)) == 1
@@ -201,6 +214,27 @@ def test_backward_validation(lib):
     bad = list(good); bad[0] = hT[0]                      # dx aliases hT
     assert lib.cssd_backward_saved(*sargs(bad)) == 1
     assert lib.cssd_backward_saved(*sargs(good, shape=(1, 64, 2, 16, 24, 16))) == 2
+    bf = lambda g: (1, 64, 2, 16, 16, 16, 1, *ins[:14], *hT, *ins[14:], None, None, *g, ws,
+                    1 << 30, None)
+    assert lib.cssd_backward_saved(*bf(good)) == 2        # bf16: no saved chunk states
+
+
+def test_backward_workspace_size_dtype(lib):
+    """bf16 inputs add the fp32 copies of x, B, C (two planes each, each rounded
+    up to 256 bytes) to the fp32 workspace."""
+    up = lambda v: (v + 255) // 256 * 256
+    for shape in ((1, 64, 2, 16, 16, 16), (2, 100, 3, 32, 64, 16), (1, 257, 2, 64, 128, 64)):
+        B, T, H, D, N, C = shape
+        f, b, plain = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert lib.cssd_backward_workspace_size(*shape, ctypes.byref(plain)) == 0
+        assert lib.cssd_backward_workspace_size_dtype(*shape, 0, ctypes.byref(f)) == 0
+        assert lib.cssd_backward_workspace_size_dtype(*shape, 1, ctypes.byref(b)) == 0
+        assert f.value == plain.value
+        assert b.value == f.value + 2 * up(4 * B * T * H * D) + 4 * up(4 * B * T * H * N)
+    z = ctypes.c_size_t(7)
+    assert lib.cssd_backward_workspace_size_dtype(0, 64, 2, 16, 16, 16, 1, ctypes.byref(z)) == 0
+    assert z.value == 0                                  # an empty problem needs none
+    assert lib.cssd_backward_workspace_size_dtype(1, 64, 2, 16, 16, 16, 1, None) == 1
 
 
 def _phase_ws(lib, *shape):
@@ -281,7 +315,8 @@ def test_profiler_without_launches(lib):
         pass
     assert set(prof.ms) == set(cssd.KERNEL_NAMES)
     assert all(v == 0 for v in prof.launches.values())
-    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(18) is None
+    assert lib.cssd_kernel_name(3) == b"k_chunk_scan" and lib.cssd_kernel_name(19) is None
+    assert lib.cssd_kernel_name(17) == b"k_scan_fused" and lib.cssd_kernel_name(18) == b"k_widen"
     assert lib.cssd_kernel_name(16) == b"k_fill"
     assert lib.cssd_kernel_name(14) == b"k_state_scan"
     assert lib.cssd_kernel_name(15) == b"k_state_scan_adj"
@@ -315,7 +350,7 @@ def test_empty_problems_validate_and_enqueue_nothing(lib):
     # backward: no heads -> nothing at all; heads but no dA -> invalid
     assert lib.cssd_backward(2, 64, 0, 16, 16, 16, 0, *[n] * 18, *[n] * 12, n, 0, n) == 0
     assert lib.cssd_backward(2, 0, 3, 16, 16, 16, 0, *[n] * 18, *[n] * 12, n, 0, n) == 1
-    assert lib.cssd_backward(2, 0, 3, 16, 16, 16, 1, *[n] * 18, *[n] * 12, n, 0, n) == 2
+    assert lib.cssd_backward(2, 0, 3, 16, 16, 16, 1, *[n] * 18, *[n] * 12, n, 0, n) == 1  # bf16 alike
     # decode with no rows or heads; nsteps is still checked
     assert lib.cssd_step(0, 2, 16, 16, *[n] * 14, n) == 0
     assert lib.cssd_step_n(3, 0, 16, 16, 4, *[n] * 14, n) == 0

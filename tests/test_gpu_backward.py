@@ -164,6 +164,77 @@ def test_backward_saved_states(case):
     _check(got, want, skip_dD=not with_d)
 
 
+TOL_BF16 = 2e-2
+
+BF16_BWD = [
+    # (B, T, H, D, N, C, with_h0, with_dskip, with_dhT)
+    (2, 130, 2, 64, 64, 64, True, True, True),    # bf16 matrix-core forward, fused adjoint pass
+    (1, 100, 3, 32, 64, 32, False, True, False),  # register-operand forward, ragged tail
+    (1, 70, 2, 32, 32, 64, True, False, True),    # matrix-core forward at N = D = 32
+]
+
+
+@pytest.mark.parametrize("case", BF16_BWD, ids=lambda c: "B{}T{}H{}D{}N{}C{}{}{}{}".format(
+    *c[:6], "_h0" if c[6] else "", "_D" if c[7] else "", "_dhT" if c[8] else ""))
+def test_backward_bf16_inputs(case):
+    """bf16 x, B, C into cssd_backward.  The widening to fp32 is exact and y is
+    not read (the log-decay gradient takes conj(C) . dC in its place), so the
+    gradients equal those of the fp32 call on the rounded values bit for bit,
+    whichever forward's y is passed, or none; every gradient meets the fp32 bar
+    against the oracle on the rounded inputs, and the bf16-input bar against the
+    oracle on the pre-rounding inputs."""
+    import torch
+    import complex_valued_state_amd as cssd
+    Bsz, T, H, D, N, C, with_h0, with_d, with_dhT = case
+    log(f"backward bf16 inputs {case}")
+    kw = dict(with_h0=with_h0, with_dskip=with_d, name="bwd_bf16")
+    inp32 = wl.random_forward(71 + T, Bsz, T, H, D, N, C, **kw)
+    inp16 = wl.random_forward(71 + T, Bsz, T, H, D, N, C, in_dtype="bf16", **kw)
+    d16 = dev_inputs(inp16)
+    # the same rounded values as fp32 device planes
+    d32 = dict(d16)
+    for k in ("x_re", "x_im", "B_re", "B_im", "C_re", "C_im"):
+        d32[k] = d16[k].float()
+    rng = np.random.default_rng(72)
+    cz = lambda *s: (np.sqrt(0.5) * (rng.standard_normal(s) + 1j * rng.standard_normal(s))
+                     ).astype(np.complex64)
+    gy = cz(Bsz, T, H, D)
+    ghT = cz(Bsz, H, N, D) if with_dhT else None
+    pl = lambda a: (_dev(a.real.copy()), _dev(a.imag.copy()))
+    ins = lambda d: (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"],
+                     d["A_re"], d["A_im"], d["Dskip"], d["h0"])
+    dyt, dhTt = pl(gy), None if ghT is None else pl(ghT)
+    n = lambda t: None if t is None else t.double().cpu().numpy()
+
+    # the fp32 call on the rounded values, given the fp32 forward's y of them
+    y32 = cssd.cssd_forward(*ins(d32), chunk=C, return_state=False)[:2]
+    g32 = cssd.cssd_backward(*ins(d32), y32, dyt, dhTt, chunk=C)
+    # the bf16 call: y not passed, and the bf16 forward's y passed
+    g16 = cssd.cssd_backward(*ins(d16), None, dyt, dhTt, chunk=C)
+    y16 = cssd.cssd_forward(*ins(d16), chunk=C, return_state=False)[:2]
+    g16y = cssd.cssd_backward(*ins(d16), y16, dyt, dhTt, chunk=C)
+    torch.cuda.synchronize()
+    for k, v in g32.items():
+        if v is not None:
+            assert torch.equal(g16[k], v), k
+            assert torch.equal(g16y[k], v), k
+
+    got = {"dx": n(g16["dx_re"]) + 1j * n(g16["dx_im"]),
+           "dB": n(g16["dB_re"]) + 1j * n(g16["dB_im"]),
+           "dC": n(g16["dC_re"]) + 1j * n(g16["dC_im"]), "ddt": n(g16["ddt"]),
+           "dA": n(g16["dA_re"]) + 1j * n(g16["dA_im"]), "dD": n(g16["dD"]),
+           "dh0": n(g16["dh0_re"]) + 1j * n(g16["dh0_im"])}
+    gyc = gy.astype(np.complex128)
+    ghc = None if ghT is None else ghT.astype(np.complex128)
+    want16 = oracle.backward(*inp16.complex(), gyc, ghc)
+    want32 = oracle.backward(*inp32.complex(), gyc, ghc)
+    for k in ("dx", "dB", "dC", "ddt", "dA", "dh0") + (("dD",) if with_d else ()):
+        err, err32 = rel_err(got[k], want16[k]), rel_err(got[k], want32[k])
+        log(f"    {k}: rel err {err:.2e} vs the rounded inputs, {err32:.2e} vs pre-rounding")
+        assert err <= TOL, (k, err)
+        assert err32 <= TOL_BF16, (k, err32)
+
+
 def test_backward_maximum_size_sampled():
     """The gradient pass at the largest size the entry points accept at
     D = N = C = 64 with 64 heads, taken as B64 T8191 H64 (2^31 - 2^18 elements
