@@ -171,6 +171,8 @@ BF16_BWD = [
     (2, 130, 2, 64, 64, 64, True, True, True),    # bf16 matrix-core forward, fused adjoint pass
     (1, 100, 3, 32, 64, 32, False, True, False),  # register-operand forward, ragged tail
     (1, 70, 2, 32, 32, 64, True, False, True),    # matrix-core forward at N = D = 32
+    (1, 300, 2, 16, 128, 128, True, True, True),  # largest N and C (tile kernels)
+    (2, 50, 2, 128, 16, 32, False, True, True),   # largest D, ragged tail
 ]
 
 
@@ -233,6 +235,31 @@ def test_backward_bf16_inputs(case):
         log(f"    {k}: rel err {err:.2e} vs the rounded inputs, {err32:.2e} vs pre-rounding")
         assert err <= TOL, (k, err)
         assert err32 <= TOL_BF16, (k, err32)
+
+
+def test_backward_ignores_y():
+    """y is not read by either backward entry point: with fp32 inputs, passing no
+    y, the forward's y or an unrelated tensor gives the same gradients bit for
+    bit, on the staged (N = D = C = 64) and the tile kernels."""
+    import torch
+    import complex_valued_state_amd as cssd
+    for (Bsz, T, H, D, N, C) in ((2, 130, 2, 64, 64, 64), (1, 100, 3, 32, 64, 16)):
+        log(f"backward without y B{Bsz} T{T} H{H} D{D} N{N} C{C}")
+        inp = wl.random_forward(81 + T, Bsz, T, H, D, N, C, with_h0=True, name="bwd_noy")
+        d = dev_inputs(inp)
+        ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"],
+               d["A_re"], d["A_im"], d["Dskip"], d["h0"])
+        g = torch.Generator(device="cuda:0").manual_seed(82)
+        pl = lambda *s: tuple(torch.randn(s, generator=g, device="cuda:0") for _ in range(2))
+        dy, dhT, junk = pl(Bsz, T, H, D), pl(Bsz, H, N, D), pl(Bsz, T, H, D)
+        y = cssd.cssd_forward(*ins, chunk=C, return_state=False)[:2]
+        ref = cssd.cssd_backward(*ins, y, dy, dhT, chunk=C)
+        for other in (None, junk):
+            got = cssd.cssd_backward(*ins, other, dy, dhT, chunk=C)
+            torch.cuda.synchronize()
+            for k, v in ref.items():
+                if v is not None:
+                    assert torch.equal(got[k], v), k
 
 
 def test_backward_maximum_size_sampled():
