@@ -64,7 +64,7 @@ KERNEL_SRC = {"k_chunk_scan": _SCAN_SRC, "k_chunk_scan_lds": _SCAN_SRC, "k_chunk
               "k_born_bf16": ("k_born.hip",), "k_state_scan": ("k_state_scan.hip",),
               "k_state_scan_lds": ("k_state_scan.hip",), "k_state_scan_mm": ("k_state_scan.hip",),
               "k_state_scan_cp": ("k_state_scan.hip",),
-              "k_scan_fused_bf16": ("k_scan_fused_bf16.hip",)}
+              "k_scan_fused_bf16": ("k_scan_fused_bf16.hip",), "k_widen": ("k_widen.hip",)}
 
 
 # ---------------------------------------------------------------------------
