@@ -247,7 +247,10 @@ struct BoolTag {
     static constexpr bool value = B;
 };
 
-template <int D>
+// SMALL: every row a workgroup addresses (up to the end of the last 128-row query
+// block, past T) lies within 2 GB of its (b, h)'s first row, so loads and stores go
+// through buffer views with 32-bit offsets (the launcher checks it)
+template <int D, bool SMALL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3 : 1))) void k_born_bf16(
     BornArgs a) {
     constexpr int NM = D / 16;          // MFMA steps over the features (per part)
@@ -274,10 +277,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int64_t rs = a.H * D;
     const int64_t base = (b * a.T * a.H + h) * D;
-    // every row a workgroup addresses (up to the end of the last 128-row query
-    // block, past T) lies within 2 GB of this (b, h)'s first row: stores through
-    // 32-bit buffer offsets
-    const bool small = ((a.T + 2 * kBornBlock) * rs + D) * 4 < ((int64_t)1 << 31);
     const uint16_t* qr_p = reinterpret_cast<const uint16_t*>(a.q_re);
     const uint16_t* qi_p = reinterpret_cast<const uint16_t*>(a.q_im);
     const uint16_t* kr_p = reinterpret_cast<const uint16_t*>(a.k_re);
@@ -290,7 +289,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
     constexpr int QBR = 2 * kBornBlock;
     const int nblk = pair == a.nqb - 1 - pair ? 1 : 2;
     for (int which = 0; which < nblk; ++which) {
-        const int64_t qb = which == 0 ? pair : a.nqb - 1 - pair;
+        const int qb = (int)(which == 0 ? pair : a.nqb - 1 - pair);
         // B operands: [qr quad, qi quad] and [-qr quad, qi quad], scaled by 1/sqrt(D tau)
         bf16x8 bre[2][NM], bim[2][NM];
 #pragma unroll
@@ -339,7 +338,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
         // is used): KQ key quads (real 8 B + imaginary 8 B) and VQ value chunks (16 B)
         uint2 skr[RD][KQ], ski[RD][KQ];
         uint4 sv[RD][VQ];
-        auto fetch = [&](int64_t kb, int set) {
+        auto fetch = [&](int kb, int set) {
+            if constexpr (SMALL) {
+                // the block's rows through views that end at the sequence's last row:
+                // rows past it read as zero; the lane offsets are the same every block
+                const int first = kb * kBornBlock;
+                const int64_t left = a.T - first;
+                const uint32_t ext = left > 0 ? (uint32_t)(((left - 1) * rs + D) * 2) : 0u;
+                const int64_t off = base + (int64_t)first * rs;
+                const BufRes rkr = make_buf(kr_p + off, ext), rki = make_buf(ki_p + off, ext);
+#pragma unroll
+                for (int i = 0; i < KQ; ++i) {
+                    const int idx = i * 256 + tid, row = idx / (D / 4), q = idx % (D / 4);
+                    const uint32_t vo = (uint32_t)((row * rs + 4 * q) * 2);
+                    skr[set][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rkr, vo, 0, 0));
+                    ski[set][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rki, vo, 0, 0));
+                }
+#pragma unroll
+                for (int i = 0; i < VQ; ++i) {
+                    // a plane is a multiple of 64 chunks, so the plane is the wave's
+                    const int idx = i * 256 + tid;
+                    const int pl = (i * 256 + 64 * w) / (kBornBlock * D / 8);
+                    const int rem = idx % (kBornBlock * D / 8), row = rem / (D / 8), c8 = rem % (D / 8);
+                    const BufRes rv = make_buf((pl == 0 ? vr_p : vi_p) + off, ext);
+                    sv[set][i] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (uint32_t)((row * rs + 8 * c8) * 2), 0, 0));
+                }
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < KQ; ++i) {
                 const int idx = i * 256 + tid, row = idx / (D / 4), q = idx % (D / 4);
@@ -385,7 +411,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
         // key blocks of 64 up to the end of this query block; block b's loads go to
         // register set b % RD and are written to LDS buffer b % 2 at the end of block
         // b - 1, after which the set takes block b + RD
-        const int64_t nkb = 2 * qb + 2;
+        const int nkb = 2 * qb + 2;
         fetch(0, 0);
         __syncthreads();  // the previous query block is done with the LDS buffers
         commit(0, 0);
@@ -395,12 +421,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
         __syncthreads();
         // a block wholly before the query block (kb < 2 qb) has no masked or empty
         // score tile for any wave; only the two blocks on the diagonal need the checks
-        auto step = [&](int64_t kb, int set_next, auto full_tag) {
+        auto step = [&](int kb, int set_next, auto full_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
             const int buf = kb & 1;
             // key tile t of this block starts kd = 64 kb + 16 t - (128 qb + 32 w + 16 u)
             // rows after query tile u: kd < 0 unmasked, kd = 0 the diagonal tile, kd > 0 empty
-            const int kd0 = (int)(64 * kb - QBR * qb) - 32 * w;
+            const int kd0 = 64 * kb - QBR * qb - 32 * w;
             // per 32-key step s2 (key tiles 2 s2, 2 s2 + 1): the scores of both query
             // tiles, packed to bf16 where the matrix core leaves them, then
             // O += P . [vr | vi] and the row sums
@@ -466,20 +492,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
             __syncthreads();
         };
         static_assert(RD == 1 || RD == 2, "2 qb must be a multiple of RD");
-        for (int64_t kb0 = 0; kb0 < 2 * qb; kb0 += RD) {
+        for (int kb0 = 0; kb0 < 2 * qb; kb0 += RD) {
 #pragma unroll
             for (int j = 0; j < RD; ++j) step(kb0 + j, (j + 1) % RD, BoolTag<true>());
         }
         step(2 * qb, 1 % RD, BoolTag<false>());
         step(2 * qb + 1, 0, BoolTag<false>());
-        if (small) {
+        if constexpr (SMALL) {
             // through views of this (b, h)'s rows: 32-bit offsets, rows past the
             // sequence dropped by the extent
             const uint32_t ext = (uint32_t)(((a.T - 1) * rs + D) * 4);
             const BufRes vre = make_buf(a.out_re + base, ext), vim = make_buf(a.out_im + base, ext);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                uint32_t vo = (uint32_t)(((qb * QBR + 32 * w + 16 * u + 4 * lg) * rs + lr) * 4);
+                uint32_t vo = (uint32_t)(((int64_t)(qb * QBR + 32 * w + 16 * u + 4 * lg) * rs + lr) * 4);
                 asm volatile("" : "+v"(vo));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -499,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
                 for (int r = 0; r < 4; ++r) {
                     const int qloc = 4 * lg + r;
                     const float den = den4[u][r];
-                    const int64_t row = qb * QBR + 32 * w + 16 * u + qloc;
+                    const int64_t row = (int64_t)qb * QBR + 32 * w + 16 * u + qloc;
                     if (row >= a.T) continue;
                     const float inv = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;  // about 1 ulp
                     const int64_t at = base + row * rs;
@@ -519,10 +545,16 @@ hipError_t launch_born(const BornArgs& a, hipStream_t s) {
     const int64_t per_xcd = (groups + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(kXcds * per_xcd * a.hpl * a.npair)), block(256);
     if (a.in_dtype == 1) {
-        switch (a.D) {
-            case 16: hipLaunchKernelGGL(k_born_bf16<16>, grid, block, 0, s, a); break;
-            case 32: hipLaunchKernelGGL(k_born_bf16<32>, grid, block, 0, s, a); break;
-            case 64: hipLaunchKernelGGL(k_born_bf16<64>, grid, block, 0, s, a); break;
+        // the rows one workgroup can address, up to the end of its last 128-row
+        // query block, within 2 GB of its (b, h)'s first row
+        const bool small = ((a.T + 2 * kBornBlock) * a.H * a.D + a.D) * 4 < ((int64_t)1 << 31);
+        switch (a.D * 2 + (small ? 1 : 0)) {
+            case 33: hipLaunchKernelGGL((k_born_bf16<16, true>), grid, block, 0, s, a); break;
+            case 32: hipLaunchKernelGGL((k_born_bf16<16, false>), grid, block, 0, s, a); break;
+            case 65: hipLaunchKernelGGL((k_born_bf16<32, true>), grid, block, 0, s, a); break;
+            case 64: hipLaunchKernelGGL((k_born_bf16<32, false>), grid, block, 0, s, a); break;
+            case 129: hipLaunchKernelGGL((k_born_bf16<64, true>), grid, block, 0, s, a); break;
+            case 128: hipLaunchKernelGGL((k_born_bf16<64, false>), grid, block, 0, s, a); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();

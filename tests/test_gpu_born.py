@@ -176,3 +176,40 @@ def test_born_bf16_layer_shape_sampled_rows():
     sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
     assert rel_err(sel, want) <= TOL16, rel_err(sel, want)
     assert np.all(np.isfinite(got))
+
+
+def test_born_bf16_wide_span_sampled_rows():
+    """bf16 inputs where the rows one (b, h) addresses span 2 GB or more (B1 T4096
+    H8192 D16, 2^29 elements a plane), so the kernel takes its 64-bit addressing
+    path rather than the 32-bit buffer views.  Inputs are drawn on the device
+    (torch's seeded generator, the layer-shape distributions); the oracle runs on
+    three heads, the last among them, sliced out (rows of different heads do not
+    interact), at sampled rows."""
+    import math
+    import torch
+    import complex_valued_state_amd as cssd
+    B, T, H, D = 1, 4096, 8192, 16
+    assert ((T + 256) * H * D + D) * 4 >= 1 << 31
+    log(f"  born bf16 wide span B{B} T{T} H{H} D{D}: drawing inputs on the device")
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(98)
+    r = math.sqrt(0.5)
+    pl = lambda: (torch.randn((B, T, H, D), generator=g, device=dev) * r).to(torch.bfloat16)
+    q, k, v = (pl(), pl()), (pl(), pl()), (pl(), pl())
+    tau = 0.5 + 1.5 * torch.rand((B, T, H), generator=g, device=dev)
+    o = cssd.cssd_born_attention(*q, *k, *v, tau)
+    torch.cuda.synchronize()
+    heads = [0, 4097, H - 1]
+    sl = lambda t: t[:, :, heads].double().cpu().numpy()
+    rng = np.random.default_rng(99)
+    ts = np.concatenate([[0, 1, 63, 64, 127, 128, T - 1], rng.integers(0, T, 60)])
+    rows = np.stack([np.zeros(3 * ts.size, np.int64), np.tile(ts, 3),
+                     np.repeat(np.arange(3), ts.size)], axis=1)
+    log("  born bf16 wide span: oracle on three heads")
+    want = oracle.born_attention_rows((sl(q[0]), sl(q[1])), (sl(k[0]), sl(k[1])),
+                                      (sl(v[0]), sl(v[1])), sl(tau), rows)
+    got_re, got_im = sl(o[0]), sl(o[1])
+    sel = got_re[0, rows[:, 1], rows[:, 2]] + 1j * got_im[0, rows[:, 1], rows[:, 2]]
+    assert rel_err(sel, want) <= TOL16, rel_err(sel, want)
+    del q, k, v, tau, o
+    torch.cuda.empty_cache()
