@@ -283,6 +283,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
     const uint16_t* ki_p = reinterpret_cast<const uint16_t*>(a.k_im);
     const uint16_t* vr_p = reinterpret_cast<const uint16_t*>(a.v_re);
     const uint16_t* vi_p = reinterpret_cast<const uint16_t*>(a.v_im);
+    // SMALL: views of this (b, h)'s key and value rows, ending at its last row
+    const uint32_t ext_bh = SMALL ? (uint32_t)(((a.T - 1) * rs + D) * 2) : 0u;
+    const BufRes vkr = make_buf(kr_p + base, ext_bh), vki = make_buf(ki_p + base, ext_bh);
+    const BufRes vvr = make_buf(vr_p + base, ext_bh), vvi = make_buf(vi_p + base, ext_bh);
 
     // query blocks of 128 rows: wave w owns query tiles u = 0, 1 (rows 32w + 16u of
     // the block), so every key and value operand read from LDS serves two score tiles
@@ -340,19 +344,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
         uint4 sv[RD][VQ];
         auto fetch = [&](int kb, int set) {
             if constexpr (SMALL) {
-                // the block's rows through views that end at the sequence's last row:
-                // rows past it read as zero; the lane offsets are the same every block
-                const int first = kb * kBornBlock;
-                const int64_t left = a.T - first;
-                const uint32_t ext = left > 0 ? (uint32_t)(((left - 1) * rs + D) * 2) : 0u;
-                const int64_t off = base + (int64_t)first * rs;
-                const BufRes rkr = make_buf(kr_p + off, ext), rki = make_buf(ki_p + off, ext);
+                // through the views of this (b, h)'s rows: the block's offset joins
+                // the lane's constant one, rows past the sequence read as zero
+                const uint32_t boff = (uint32_t)kb * (uint32_t)(kBornBlock * rs * 2);
 #pragma unroll
                 for (int i = 0; i < KQ; ++i) {
                     const int idx = i * 256 + tid, row = idx / (D / 4), q = idx % (D / 4);
-                    const uint32_t vo = (uint32_t)((row * rs + 4 * q) * 2);
-                    skr[set][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rkr, vo, 0, 0));
-                    ski[set][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rki, vo, 0, 0));
+                    const uint32_t vo = (uint32_t)((row * rs + 4 * q) * 2) + boff;
+                    skr[set][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vkr, vo, 0, 0));
+                    ski[set][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vki, vo, 0, 0));
                 }
 #pragma unroll
                 for (int i = 0; i < VQ; ++i) {
@@ -360,9 +360,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 3
                     const int idx = i * 256 + tid;
                     const int pl = (i * 256 + 64 * w) / (kBornBlock * D / 8);
                     const int rem = idx % (kBornBlock * D / 8), row = rem / (D / 8), c8 = rem % (D / 8);
-                    const BufRes rv = make_buf((pl == 0 ? vr_p : vi_p) + off, ext);
+                    const uint32_t vo = (uint32_t)((row * rs + 8 * c8) * 2) + boff;
                     sv[set][i] = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (uint32_t)((row * rs + 8 * c8) * 2), 0, 0));
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(pl == 0 ? vvr : vvi, vo, 0, 0));
                 }
                 return;
             }
