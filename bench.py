@@ -614,10 +614,13 @@ def born_entry(steps, dev, bf16):
     fl = born_flops(bb, bt, bhd, bd)
     kern = "k_born_bf16" if bf16 else "k_born"
     peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    # the bf16 kernel's 32-bit-view instance serves rows that span under 2 GB per (b, h)
+    small = ((bt + 2 * 64) * bhd * bd + bd) * 4 < (1 << 31)
+    sym = f"{kern}<{bd}, {'true' if small else 'false'}>" if bf16 else f"{kern}<{bd}>"
     return {
         "tokens_per_s": round(bb * bt / (ms * 1e-3), 1), "ms_per_call": round(ms, 5),
-        "roofline": {"bound": "mfma", "kernel": kern, "symbol": f"{kern}<{bd}>",
-                     "traffic": load_traffic(f"{kern}<{bd}>"),
+        "roofline": {"bound": "mfma", "kernel": kern, "symbol": sym,
+                     "traffic": load_traffic(sym),
                      "achieved": round(fl / (kms * 1e-3) / 1e12, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(fl / (kms * 1e-3) / 1e12 / peak, 4),
