@@ -79,25 +79,30 @@ def test_forward_no_rows_or_heads(shape):
     assert y_re.shape == (Bsz, T, H, D) and hT_re.shape == (Bsz, H, N, D)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("with_dhT", [True, False])
-def test_backward_zero_steps(with_dhT):
+def test_backward_zero_steps(with_dhT, bf16):
+    """T = 0: dh0 = dhT, dA and dDskip are empty sums; with bf16 x, B, C (and no
+    y, which the backward does not read) nothing is widened either."""
     import torch
     import complex_valued_state_amd as cssd
     import oracle
     Bsz, T, H, D, N, C = 2, 0, 3, 64, 64, 64
-    log(f"backward T=0 dhT={with_dhT}")
+    log(f"backward T=0 dhT={with_dhT} bf16={bf16}")
     x, Bm, Cm, dt, A, Dk, h0 = _problem(12, Bsz, T, H, D, N)
     rng = np.random.default_rng(13)
     dhT = (rng.standard_normal((Bsz, H, N, D)) + 1j * rng.standard_normal((Bsz, H, N, D))
            ).astype(np.complex64)
     pl = lambda a: (_dev(a.real), _dev(a.imag))
+    io = (lambda a: tuple(t.to(torch.bfloat16) for t in pl(a))) if bf16 else pl
     dy = np.zeros((Bsz, T, H, D), np.complex64)
     with cssd.profile() as prof:
-        g = cssd.cssd_backward(*pl(x), *pl(Bm), *pl(Cm), _dev(dt), _dev(A.real), _dev(A.imag),
-                               _dev(Dk), pl(h0), pl(dy), pl(dy), pl(dhT) if with_dhT else None,
-                               chunk=C)
+        g = cssd.cssd_backward(*io(x), *io(Bm), *io(Cm), _dev(dt), _dev(A.real), _dev(A.imag),
+                               _dev(Dk), pl(h0), None if bf16 else pl(dy), pl(dy),
+                               pl(dhT) if with_dhT else None, chunk=C)
         torch.cuda.synchronize()
     assert prof.launches["k_fill"] == 5 and prof.launches["k_bwd_dx"] == 0
+    assert prof.launches["k_widen"] == 0
     w = oracle.backward(x.astype(np.complex128), Bm.astype(np.complex128),
                         Cm.astype(np.complex128), dt.astype(np.float64), A.astype(np.complex128),
                         Dk.astype(np.float64), h0.astype(np.complex128), dy.astype(np.complex128),
