@@ -72,6 +72,57 @@ def test_training_step_graph_replays():
             assert torch.equal(got[k], v), (rep, k)
 
 
+def test_bf16_training_step_graph_replays():
+    """bf16 x, B, C: the one-kernel forward, then the backward, which widens the
+    bf16 planes in its workspace and reads no y: one captured graph, replayed."""
+    import torch
+    import complex_valued_state_amd as cssd
+    Bsz, T, H, D, N, C = 2, 300, 3, 64, 64, 64
+    log("graph: bf16 forward + backward")
+    inp = wl.random_forward(83, Bsz, T, H, D, N, C, with_h0=True, in_dtype="bf16")
+    d = dev_inputs(inp)
+    ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
+           d["A_im"], d["Dskip"], d["h0"])
+    g = torch.Generator(device="cuda:0").manual_seed(84)
+    dy = [torch.randn((Bsz, T, H, D), generator=g, device="cuda:0") for _ in range(2)]
+    dhT = [torch.randn((Bsz, H, N, D), generator=g, device="cuda:0") for _ in range(2)]
+    ws_f = torch.empty(cssd.cssd_forward_workspace_size(Bsz, T, H, D, N, C), dtype=torch.uint8,
+                       device="cuda:0")
+    ws_b = torch.empty(cssd.cssd_backward_workspace_size(Bsz, T, H, D, N, C, cssd.CSSD_BF16),
+                       dtype=torch.uint8, device="cuda:0")
+    y = [torch.empty((Bsz, T, H, D), device="cuda:0") for _ in range(2)]
+    hT = [torch.empty((Bsz, H, N, D), device="cuda:0") for _ in range(2)]
+
+    def step():
+        cssd.cssd_forward(*ins, chunk=C, out=(*y, *hT), workspace=ws_f)
+        return cssd.cssd_backward(*ins, None, dy, dhT, chunk=C, workspace=ws_b)
+
+    ref_g = step()
+    torch.cuda.synchronize()
+    ref = {"y_re": y[0].clone(), "y_im": y[1].clone(), "hT_re": hT[0].clone(),
+           "hT_im": hT[1].clone(), **{k: v.clone() for k, v in ref_g.items() if v is not None}}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gg = step()
+    for rep in range(REPLAYS):
+        for t in (*y, *hT, *(v for v in gg.values() if v is not None)):
+            t.fill_(float("nan"))
+        ws_b.fill_(255)  # the widened planes are rewritten by every replay
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {"y_re": y[0], "y_im": y[1], "hT_re": hT[0], "hT_im": hT[1],
+               **{k: v for k, v in gg.items() if v is not None}}
+        for k, v in ref.items():
+            assert torch.equal(got[k], v), (rep, k)
+
+
 def test_decode_step_graph_replays():
     """cssd_step updates its state in place: the state is reset eagerly before
     each replay, and the replay must give the eager step's state and output."""
