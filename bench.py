@@ -262,14 +262,22 @@ def forward_entry(inp, steps, warmup, dev, cpu_budget_s=None):
         f_ms = kern["k_scan_fused"]
         f_bytes = scan_fused_hbm_bytes(B, T, H, D, N, in_bytes)
         f_gbs = f_bytes / (f_ms * 1e-3) / 1e9
-        # eight-wave workgroups when every sequence has a CU of its own, as the
-        # library's launcher chooses
+        # the launch shapes the library's launcher chooses: eight-wave workgroups
+        # when every sequence has a CU of its own; up to two sequences a CU, whole
+        # four-wave workgroups beside half-width ones on a second stream (the
+        # profiler's time and the traffic cover both kernels); else four waves
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        fsym = "k_scan_fused_bf16<8>" if B * H <= cus else "k_scan_fused_bf16<4>"
-        roof = {"bound": "hbm", "kernel": "k_scan_fused", "symbol": fsym,
+        if B * H <= cus:
+            fsyms = ["k_scan_fused_bf16<8, false>"]
+        elif B * H <= 2 * cus:
+            fsyms = ["k_scan_fused_bf16<4, false>", "k_scan_fused_bf16<4, true>"]
+        else:
+            fsyms = ["k_scan_fused_bf16<4, false>"]
+        tr = [load_traffic(x) for x in fsyms]
+        roof = {"bound": "hbm", "kernel": "k_scan_fused", "symbol": " + ".join(fsyms),
                 "achieved": round(f_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(f_gbs / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic(fsym),
+                "traffic": None if None in tr else sum(tr),
                 "algorithmic_bytes_per_launch": f_bytes, "avg_launch_ms": round(f_ms, 5),
                 "mfma_frac": round(fwd_flops / (f_ms * 1e-3) / 1e12 / peak, 4)}
     else:

@@ -48,9 +48,16 @@
 // pieces) while the current chunk is computed, then written to LDS with the
 // pieces XOR-swizzled by the row; w B is formed from the same B pieces in fp32
 // and rounded to bf16 on the way.  The M tiles overwrite the B rows once the
-// scores are done.  69 KB of LDS with four waves (two workgroups per CU), 102 KB
-// with eight (one).  Rows of a partial last chunk past the sequence read as zero
-// through the buffer extents and their stores are dropped.
+// scores are done.  69 KB of LDS with four waves, 84 KB for a half-width
+// workgroup, 102 KB with eight.  Rows of a partial last chunk past the sequence
+// read as zero through the buffer extents and their stores are dropped.
+//
+// Launch shapes by the number of sequences B H against the CU count: up to one a
+// CU, one eight-wave workgroup each; up to two a CU, one four-wave workgroup for
+// each of the first (CU count), and two half-width workgroups for each of the
+// rest on a second stream, so every CU holds one whole sequence and one half;
+// beyond that, four-wave workgroups in rounds.
+#include <mutex>
 #include <type_traits>
 
 #include "cssd_device.h"
@@ -124,6 +131,11 @@ struct FusedArgs {
     // (late = CU count when there are more sequences than CUs, but no more than
     // twice as many; otherwise no workgroup is late and priorities stay default)
     int late;
+    // the chunk at which late workgroups give up their priority (and, in the same
+    // launch, the others take it)
+    int swap_at;
+    // the half-width launch: sequences hbase .. hbase + hcount - 1, two workgroups each
+    int64_t hbase, hcount;
 };
 
 // one chunk's inputs in flight in registers: KP 16-byte pieces a thread of each
@@ -143,14 +155,22 @@ struct Pre {
 // updated tiles pass to the other through LDS, read after the next chunk's first
 // barrier.  One eight-wave workgroup per CU (101 KB of LDS); its per-chunk time is
 // about half that of a four-wave workgroup alone.
-template <int WAVES>
+// HALF (four waves): two workgroups share one sequence, each taking two of the four
+// column blocks (the columns of y and of the state are independent), split between
+// its waves as the eight-wave form splits one: wave v takes column block
+// 2 half + (v & 1) and half hv = v / 2, and the partner wave v ^ 2 holds the other
+// half's tiles.  Each repeats the scores G.  84 KB of LDS, so a CU holds one such
+// workgroup next to one whole four-wave one (69 KB) and never two of them.
+template <int WAVES, bool HALF>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_fused_bf16(
     FusedArgs a) {
     static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
+    static_assert(!HALF || WAVES == 4, "half-width workgroups have four waves");
     constexpr int C = 64, N = 64, D = 64;
     constexpr int NT = 64 * WAVES;       // threads
     constexpr int KP = 512 / NT;         // 16-byte pieces a thread of each staged plane
     constexpr bool W8 = WAVES == 8;
+    constexpr bool SPL = W8 || HALF;  // row and state tiles split between two halves
     // C rows (re, im).  The planes are 16 bytes more than a multiple of the bank
     // window apart: 8-byte reads of the two planes at one offset, which the compiler
     // merges into one two-address read, then fall in different banks (0 instead of 8
@@ -168,14 +188,26 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
     __shared__ __align__(16) float l_e[2][2][C];
     __shared__ __align__(16) float l_w[2][2][C];
     __shared__ float l_cd[2][2];
-    // WAVES = 8: each wave's two updated state tiles, [wave][4 floats][lane] x 4
-    __shared__ __align__(16) float l_hx[W8 ? 8 : 1][4][64][4];
+    // split forms: each wave's two updated state tiles, [wave][4 floats][lane] x 4
+    __shared__ __align__(16) float l_hx[SPL ? WAVES : 1][4][64][4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int li = lane & 15, g = lane >> 4;
     const int wv = wave_id();
-    const int w = wv & 3, hv = wv >> 2;  // column block, half (WAVES = 8)
-    const int64_t bh = blockIdx.x;
+    int64_t bh = blockIdx.x;
+    int cg = 0;  // HALF: which two column blocks
+    if constexpr (HALF) {
+        // both workgroups of a sequence on one XCD (dispatch is round-robin over 8),
+        // so its B and C rows are fetched into one L2
+        const int64_t e = blockIdx.x, k = e / 16, x8 = e % 8;
+        cg = (int)((e / 8) & 1);
+        if (8 * k + x8 >= a.hcount) return;  // workgroup-uniform, before any barrier
+        bh = a.hbase + 8 * k + x8;
+    }
+    // column block, half (split forms), and the wave holding the other half's tiles
+    const int w = HALF ? 2 * cg + (wv & 1) : (wv & 3);
+    const int hv = HALF ? wv >> 1 : wv >> 2;
+    const int partner = HALF ? wv ^ 2 : wv ^ 4;
     const int h = (int)(bh % a.H);
     const int64_t b = bh / a.H;
     const uint32_t sN = (uint32_t)a.H * N, sD = (uint32_t)a.H * D;
@@ -321,7 +353,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
     // extent 0 (all dropped).  The compiler's waits for a prefetch then count the operations
     // issued after it exactly, also across the loop's back edge, instead of
     // waiting for the output stores or for the loads just issued.
-    constexpr int NLT = W8 ? 2 : 4;  // row tiles of y a wave
+    constexpr int NLT = SPL ? 2 : 4;  // row tiles of y a wave
     Pre<KP> P;
     load(0, P);
     const float dt0 = load_dt(0);
@@ -335,15 +367,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
     if (wv == 0) cumsum(0, dt0);
     // Wave priority.  Of two workgroups on one CU, the one dispatched first wins
     // instruction arbitration and the other falls behind (measured: 14.1K against
-    // 17.2K clocks a chunk), and the kernel waits for the one behind.  So the late
-    // workgroup takes priority for the first 9/16 of its chunks and the early one
-    // for the rest: from the rates while ahead and while behind, both then finish
-    // at about the same time (measured at B 8, T 2048, H 48: 0.292 ms with default
-    // priorities, 0.281 switching at one half, 0.277 at 9/16 and at 5/8).
+    // 17.2K clocks a chunk), and the kernel waits for the one behind.  So a late
+    // workgroup (a.late) takes priority up to chunk a.swap_at and, where the
+    // early ones are in the same launch, gives it to them from there (two whole
+    // workgroups on a CU, measured at B 8, T 2048, H 48: 0.292 ms with default
+    // priorities, 0.281 switching at one half, 0.277 at 9/16 and at 5/8; the
+    // launcher now splits that case into whole and half-width workgroups).
     const bool late = (int)blockIdx.x >= a.late;  // wave-uniform
     if (late) __builtin_amdgcn_s_setprio(1);
     for (int c = 0; c < a.nC; ++c) {
-        if (c == (9 * a.nC) / 16 && a.late < (1 << 30)) {
+        if (c == a.swap_at && a.late < (1 << 30)) {
             if (late) __builtin_amdgcn_s_setprio(0);
             else __builtin_amdgcn_s_setprio(1);
         }
@@ -358,9 +391,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
         const float* const le_i = l_e[slot][1];
 
         __syncthreads();  // every wave is done with the previous chunk's LDS
-        if (W8 && c > 0) {
+        if (SPL && c > 0) {
             // the other half's two updated state tiles (2 (1 - hv), 2 (1 - hv) + 1)
-            const float4* src = reinterpret_cast<const float4*>(&l_hx[W8 ? (wv ^ 4) : 0][0][lane][0]);
+            const float4* src = reinterpret_cast<const float4*>(&l_hx[SPL ? partner : 0][0][lane][0]);
             auto take = [&](auto nt0) {
                 constexpr int T0 = decltype(nt0)::value;
 #pragma unroll
@@ -519,7 +552,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
             const BufRes ry_i = make_buf(a.y_im + row0 * D, extD * 4);
 #pragma unroll
             for (int jt = 0; jt < NLT; ++jt) {
-                const int lt = W8 ? (hv == 0 ? 3 * jt : 1 + jt) : jt;  // wave-uniform
+                const int lt = SPL ? (hv == 0 ? 3 * jt : 1 + jt) : jt;  // wave-uniform
                 floatx4 yr = {0.f, 0.f, 0.f, 0.f}, yi = {0.f, 0.f, 0.f, 0.f};
                 const int l = 16 * lt + li;
 #pragma unroll
@@ -590,17 +623,17 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
                 hi[nt][r] = ni;
             }
         };
-        // WAVES = 8: this half's two tiles, handed to the other half through LDS
+        // split forms: this half's two tiles, handed to the other half through LDS
         auto give = [&](auto nt0) {
             constexpr int T0 = decltype(nt0)::value;
-            float4* dst = reinterpret_cast<float4*>(&l_hx[W8 ? wv : 0][0][lane][0]);
+            float4* dst = reinterpret_cast<float4*>(&l_hx[SPL ? wv : 0][0][lane][0]);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 dst[(2 * j) * 64] = float4{hr[T0 + j][0], hr[T0 + j][1], hr[T0 + j][2], hr[T0 + j][3]};
                 dst[(2 * j + 1) * 64] = float4{hi[T0 + j][0], hi[T0 + j][1], hi[T0 + j][2], hi[T0 + j][3]};
             }
         };
-        if (!W8) {
+        if (!SPL) {
             update(std::integral_constant<int, 0>());
             update(std::integral_constant<int, 1>());
             update(std::integral_constant<int, 2>());
@@ -616,12 +649,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
         }
     }
     if (a.hT_re != nullptr) {
-        // WAVES = 8: each half stores the tiles it updated last
+        // split forms: each half stores the tiles it updated last
         const BufRes r1 = make_buf(a.hT_re + bh * (int64_t)N * D, N * D * 4);
         const BufRes i1 = make_buf(a.hT_im + bh * (int64_t)N * D, N * D * 4);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            if (W8 && (nt >> 1) != hv) continue;  // wave-uniform
+            if (SPL && (nt >> 1) != hv) continue;  // wave-uniform
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 buf_store_f32(hr[nt][r], r1, soff + (16 * nt + r) * D);
@@ -630,6 +663,31 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
         }
     }
 }
+
+namespace {
+
+// The second stream of the split launch, one per device, created on first use with
+// the default priority; launches on it follow the caller's stream through events.
+hipError_t side_stream(hipStream_t* out) {
+    static std::mutex m;
+    static hipStream_t streams[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(m);
+    if (streams[dev] == nullptr) {
+        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            streams[dev] = nullptr;
+            return e;
+        }
+    }
+    *out = streams[dev];
+    return hipSuccess;
+}
+
+}  // namespace
 
 bool scan_fused(const FwdArgs& f) {
     return f.in_dtype == 1 && f.C == 64 && f.N == 64 && f.D == 64;
@@ -648,18 +706,66 @@ hipError_t launch_scan_fused(const FwdArgs& f, hipStream_t s) {
     a.h0_re = f.h0_re; a.h0_im = f.h0_im;
     a.y_re = f.y_re; a.y_im = f.y_im; a.hT_re = f.hT_re; a.hT_im = f.hT_im;
     a.T = f.T; a.H = (int)f.H; a.nC = (int)f.nC;
+    a.hbase = 0;
+    a.hcount = 0;
     const int64_t nseq = f.B * f.H;
     int cus = 0;
     if (device_cu_count(&cus) != hipSuccess) cus = 0;
-    a.late = (cus > 0 && nseq > cus && nseq <= 2 * (int64_t)cus) ? cus : (1 << 30);
+    a.late = 1 << 30;
+    a.swap_at = a.nC;
     // eight waves when every sequence gets a CU of its own (T 2048, H 48, B 1:
-    // 0.126 ms against 0.159 with four; B 4: 0.166 against 0.194); four otherwise
-    // (B 8 with eight waves, in two rounds of one workgroup a CU: 0.310 ms against
-    // 0.277 with four and the priority swap)
-    if (cus > 0 && nseq <= cus)
-        hipLaunchKernelGGL(k_scan_fused_bf16<8>, dim3((unsigned)nseq), dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_scan_fused_bf16<4>, dim3((unsigned)nseq), dim3(256), 0, s, a);
+    // 0.126 ms against 0.159 with four; B 4: 0.166 against 0.194)
+    if (cus > 0 && nseq <= cus) {
+        hipLaunchKernelGGL((k_scan_fused_bf16<8, false>), dim3((unsigned)nseq), dim3(512), 0, s, a);
+        return hipGetLastError();
+    }
+    if (cus > 0 && nseq <= 2 * (int64_t)cus) {
+        // more sequences than CUs, at most twice as many: the first `cus` run whole,
+        // one four-wave workgroup each, and the rest as two half-width workgroups
+        // each, launched beside them on a second stream.  LDS admits one whole and
+        // one half on a CU, never two halves, so each CU carries about 1.6
+        // sequences' work instead of two whole ones on half the CUs.
+        hipStream_t s2;
+        hipError_t e = side_stream(&s2);
+        if (e != hipSuccess) return e;
+        hipEvent_t fork, join;
+        if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) != hipSuccess) {
+            (void)hipEventDestroy(fork);
+            return e;
+        }
+        FusedArgs hb = a;
+        hb.hbase = cus;
+        hb.hcount = nseq - cus;
+        // the halves are dispatched after the whole workgroups they share CUs with,
+        // which then win instruction arbitration (the halves took 0.246 ms, the
+        // wholes 0.216, at B 8, T 2048, H 48): the halves take wave priority for
+        // the first 9/16 of their chunks (measured with the switch at 0, 6, 8, 10,
+        // 12 and 16 sixteenths: 0.269, 0.263, 0.260, 0.261, 0.265 and 0.272 ms)
+        hb.late = 0;
+        hb.swap_at = (9 * a.nC) / 16;
+        const int64_t hblocks = 16 * ((hb.hcount + 7) / 8);
+        e = hipEventRecord(fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s2, fork, 0);
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL((k_scan_fused_bf16<4, false>), dim3((unsigned)cus), dim3(256), 0, s, a);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL((k_scan_fused_bf16<4, true>), dim3((unsigned)hblocks), dim3(256), 0, s2,
+                               hb);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) e = hipEventRecord(join, s2);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, join, 0);
+        // events still pending are released once they complete
+        (void)hipEventDestroy(fork);
+        (void)hipEventDestroy(join);
+        return e;
+    }
+    // more than twice as many sequences as CUs (or no CU count): four waves, in
+    // rounds of two workgroups a CU
+    hipLaunchKernelGGL((k_scan_fused_bf16<4, false>), dim3((unsigned)nseq), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -123,6 +123,54 @@ def test_bf16_training_step_graph_replays():
             assert torch.equal(got[k], v), (rep, k)
 
 
+def test_bf16_forward_two_stream_split_graph_replays():
+    """bf16 inputs with more sequences than CUs (and at most twice as many): the
+    forward runs whole and half-width workgroups on the caller's stream and a
+    second stream joined through events.  Captured into a graph and replayed, it
+    gives the eager result bit for bit, and the eager result meets the oracle."""
+    import torch
+    import complex_valued_state_amd as cssd
+    from gpu_util import oracle_forward, rel_err
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Bsz, T, H, D, N, C = 1, 100, cus + 9, 64, 64, 64
+    log(f"graph: bf16 forward, {Bsz * H} sequences on {cus} CUs")
+    inp = wl.random_forward(85, Bsz, T, H, D, N, C, with_h0=True, in_dtype="bf16")
+    d = dev_inputs(inp)
+    ins = (d["x_re"], d["x_im"], d["B_re"], d["B_im"], d["C_re"], d["C_im"], d["dt"], d["A_re"],
+           d["A_im"], d["Dskip"], d["h0"])
+    ws = torch.empty(cssd.cssd_forward_workspace_size(Bsz, T, H, D, N, C), dtype=torch.uint8,
+                     device="cuda:0")
+    y = [torch.empty((Bsz, T, H, D), device="cuda:0") for _ in range(2)]
+    hT = [torch.empty((Bsz, H, N, D), device="cuda:0") for _ in range(2)]
+
+    def step():
+        cssd.cssd_forward(*ins, chunk=C, out=(*y, *hT), workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (*y, *hT)]
+    yr, hr = oracle_forward(inp)
+    to = lambda a, b: a.double().cpu().numpy() + 1j * b.double().cpu().numpy()
+    assert rel_err(to(y[0], y[1]), yr) <= 2e-2 and rel_err(to(hT[0], hT[1]), hr) <= 2e-2
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(REPLAYS):
+        for t in (*y, *hT):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((*y, *hT), ref):
+            assert torch.equal(t, r), rep
+
+
 def test_decode_step_graph_replays():
     """cssd_step updates its state in place: the state is reset eagerly before
     each replay, and the replay must give the eager step's state and output."""
