@@ -666,24 +666,43 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 
 namespace {
 
-// The second stream of the split launch, one per device, created on first use with
-// the default priority; launches on it follow the caller's stream through events.
-hipError_t side_stream(hipStream_t* out) {
-    static std::mutex m;
-    static hipStream_t streams[64] = {};
+// The second stream of the split launch and its fork and join events, one set per
+// device, created on the first split launch on that device (default priority,
+// timing off) and kept until the process ends.  The launcher enqueues under the
+// set's lock, so each wait binds to the record of the same call also when several
+// host threads launch at once.
+struct SideSet {
+    std::mutex m;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+hipError_t side_set(SideSet** out) {
+    static SideSet sets[64];
+    static std::mutex init;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(m);
-    if (streams[dev] == nullptr) {
-        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    SideSet& ss = sets[dev];
+    std::lock_guard<std::mutex> lock(init);
+    if (ss.s == nullptr) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
         if (e != hipSuccess) {
-            streams[dev] = nullptr;
+            if (j != nullptr) (void)hipEventDestroy(j);
+            if (f != nullptr) (void)hipEventDestroy(f);
+            if (st != nullptr) (void)hipStreamDestroy(st);
             return e;
         }
+        ss.fork = f;
+        ss.join = j;
+        ss.s = st;
     }
-    *out = streams[dev];
+    *out = &ss;
     return hipSuccess;
 }
 
@@ -723,17 +742,12 @@ hipError_t launch_scan_fused(const FwdArgs& f, hipStream_t s) {
         // more sequences than CUs, at most twice as many: the first `cus` run whole,
         // one four-wave workgroup each, and the rest as two half-width workgroups
         // each, launched beside them on a second stream.  LDS admits one whole and
-        // one half on a CU, never two halves, so each CU carries about 1.6
-        // sequences' work instead of two whole ones on half the CUs.
-        hipStream_t s2;
-        hipError_t e = side_stream(&s2);
+        // one half on a CU, never two halves, so the work spreads over every CU
+        // instead of two whole sequences on half of them (a half costs nearly a
+        // whole's vector work: 0.257-0.260 ms against 0.277 at B 8, T 2048, H 48).
+        SideSet* ss = nullptr;
+        hipError_t e = side_set(&ss);
         if (e != hipSuccess) return e;
-        hipEvent_t fork, join;
-        if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) != hipSuccess) {
-            (void)hipEventDestroy(fork);
-            return e;
-        }
         FusedArgs hb = a;
         hb.hbase = cus;
         hb.hcount = nseq - cus;
@@ -745,22 +759,20 @@ hipError_t launch_scan_fused(const FwdArgs& f, hipStream_t s) {
         hb.late = 0;
         hb.swap_at = (9 * a.nC) / 16;
         const int64_t hblocks = 16 * ((hb.hcount + 7) / 8);
-        e = hipEventRecord(fork, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(s2, fork, 0);
+        std::lock_guard<std::mutex> lock(ss->m);
+        e = hipEventRecord(ss->fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
         if (e == hipSuccess) {
             hipLaunchKernelGGL((k_scan_fused_bf16<4, false>), dim3((unsigned)cus), dim3(256), 0, s, a);
             e = hipGetLastError();
         }
         if (e == hipSuccess) {
-            hipLaunchKernelGGL((k_scan_fused_bf16<4, true>), dim3((unsigned)hblocks), dim3(256), 0, s2,
-                               hb);
+            hipLaunchKernelGGL((k_scan_fused_bf16<4, true>), dim3((unsigned)hblocks), dim3(256), 0,
+                               ss->s, hb);
             e = hipGetLastError();
         }
-        if (e == hipSuccess) e = hipEventRecord(join, s2);
-        if (e == hipSuccess) e = hipStreamWaitEvent(s, join, 0);
-        // events still pending are released once they complete
-        (void)hipEventDestroy(fork);
-        (void)hipEventDestroy(join);
+        if (e == hipSuccess) e = hipEventRecord(ss->join, ss->s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
         return e;
     }
     // more than twice as many sequences as CUs (or no CU count): four waves, in

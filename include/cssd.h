@@ -25,9 +25,16 @@
  *    or written as vectors (cssd_forward: B_*, C_*, h0_*, hT_*; cssd_step: x_*,
  *    h_*, y_*) to 16 bytes (8 bytes for bf16 B_*, C_*), every other array to
  *    its element size.  The library
- *    never allocates, frees or synchronises; all work is enqueued on `stream`
- *    (a hipStream_t passed as void*; NULL = the legacy default stream) and is
- *    complete when that stream is.  Outputs are valid only after that point.
+ *    never allocates device memory, frees or synchronises; all work is enqueued
+ *    on `stream` (a hipStream_t passed as void*; NULL = the legacy default
+ *    stream) and is complete when that stream is.  Outputs are valid only after
+ *    that point.  One exception to "on `stream`": a bf16-input cssd_forward at
+ *    headdim = dstate = chunk = 64 with more (b, h) sequences than the GPU has
+ *    CUs, but at most twice as many, runs part of its work on a second stream of
+ *    the library's, which waits for `stream` before it starts, and which `stream`
+ *    waits for afterwards (events), so the result is still complete when
+ *    `stream` is, and graph capture of `stream` takes both in.  That stream and
+ *    its two events are created on the first such call on a GPU and kept.
  *  - Validation is synchronous and host-side: bad arguments return an error
  *    status before anything is enqueued, and the library never reads device
  *    memory from the host.  Launch failures return CSSD_ERR_HIP.  No C++
@@ -173,7 +180,9 @@ int cssd_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
  * a fixed device array of CSSD_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
  * library, one per GPU, held from the first call on that GPU until the process
  * ends.  The call allocates nothing itself (its first call on a GPU looks the
- * array's address up once); the caller still owns every input and output.
+ * array's address up once, and the first bf16 call in the two-stream shape
+ * described above creates that stream and its events); the caller still owns
+ * every input and output.
  * A problem whose cssd_forward_workspace_size exceeds the array returns
  * CSSD_ERR_TOO_LARGE before anything is enqueued (at D = N = chunk = 64 the
  * array holds about 1,900 chunks, batch * nheads * ceil(seqlen / chunk)).
