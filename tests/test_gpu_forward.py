@@ -306,13 +306,35 @@ def test_config1_bf16_sampled():
 
 def test_bf16_more_sequences_than_cus():
     """bf16 inputs at N = D = C = 64 with more sequences than CUs (at most twice as
-    many): the workgroups dispatched onto occupied CUs change wave priority
-    halfway, which must leave the results alone.  257 sequences with a ragged
-    tail: sampled early and late workgroups, and the last sequence, within the
-    path's bounds of the oracle on the rounded inputs."""
+    many): the first sequences run as whole workgroups, the rest as pairs of
+    half-width workgroups on a second stream that take wave priority for part of
+    the run.  257 sequences with a ragged tail (on a 256-CU device one sequence
+    in halves, most of its 16 half-width slots empty): sampled whole sequences
+    and the last one, within the path's bounds of the oracle on the rounded
+    inputs."""
     inp = wl.random_forward(11, 1, 130, 257, 64, 64, 64, with_h0=True, with_dskip=True,
                             in_dtype="bf16", name="manyseq")
     pairs = [(0, 0), (0, 1), (0, 128), (0, 254), (0, 255), (0, 256)]
+    y, hT = _check_sampled(inp, pairs, TOL_BF16)
+    yb, hb = bf16_diagnostic_bounds(64, 64, 64)
+    ref = sampled_oracle(inp, pairs)
+    for (b, h), (yr, hr) in ref.items():
+        assert rel_err(y[b, :, h, :], yr) <= yb and rel_err(hT[b, h], hr) <= hb, (b, h)
+
+
+@pytest.mark.parametrize("extra", [0, 1], ids=["twice_cus", "twice_cus_plus_one"])
+def test_bf16_twice_as_many_sequences_as_cus(extra):
+    """bf16 inputs at N = D = C = 64 at the edges of the split launch: exactly
+    twice as many sequences as CUs (the most half-width workgroups, one per CU
+    beside one whole sequence) and one more (four-wave workgroups in rounds).
+    Sampled sequences on both sides of the split and the last one, within the
+    path's bounds of the oracle on the rounded inputs."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H = 2 * cus + extra
+    inp = wl.random_forward(17 + extra, 1, 70, H, 64, 64, 64, with_h0=True, with_dskip=True,
+                            in_dtype="bf16", name="twicecus")
+    pairs = [(0, 0), (0, cus - 1), (0, cus), (0, cus + 7), (0, cus + 8), (0, H - 1)]
     y, hT = _check_sampled(inp, pairs, TOL_BF16)
     yb, hb = bf16_diagnostic_bounds(64, 64, 64)
     ref = sampled_oracle(inp, pairs)
