@@ -636,10 +636,11 @@ def born_entry(steps, dev, bf16):
 
 
 # the workloads --only can time alone: name -> (generator function, argument) for the
-# forward ones; the Born attention ones take no inputs from here
+# forward and backward ones; the Born attention ones take no inputs from here
 ONLY = {"forward_f32": ("config1", "f32"), "forward_bf16": ("config1", "bf16"),
         "forward_tiny": ("config0", None), "forward_long": ("config2", None),
-        "forward_pam": ("config3", "re"), "born_f32": None, "born_bf16": None}
+        "forward_pam": ("config3", "re"), "born_f32": None, "born_bf16": None,
+        "backward_f32": ("config1", "f32"), "backward_bf16": ("config1", "bf16")}
 
 
 def only_inputs(name):
@@ -672,8 +673,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
     ap.add_argument("--only", choices=sorted(ONLY), default=None,
-                    help="time one forward workload alone and print its figures (for "
-                         "profiler runs); not the benchmark line")
+                    help="time one workload alone (a forward, the backward or the Born "
+                         "attention) and print its figures (for profiler runs); not the "
+                         "benchmark line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy a 1 GiB buffer three times (the reference kernel that scales "
                          "the HBM byte counters) and exit")
@@ -696,6 +698,9 @@ def main():
         progress(f"timing {args.only} alone")
         if args.only.startswith("born_"):
             e = born_entry(args.steps, dev, bf16=args.only == "born_bf16")
+        elif args.only.startswith("backward_"):
+            bms, bk = time_backward(only_inputs(args.only), max(3, args.steps // 2), 2, dev)
+            e = {"ms_per_step": round(bms, 4), "kernels_avg_ms": {k: round(v, 5) for k, v in bk.items()}}
         else:
             e = forward_entry(only_inputs(args.only), args.steps, args.warmup, dev)
         print(json.dumps({"workload": args.only, **e}), flush=True)

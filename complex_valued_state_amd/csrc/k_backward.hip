@@ -1251,20 +1251,33 @@ __global__ __launch_bounds__(256) void k_bwd_dz(BwdArgs a) {
 
 // dA[h], dDskip[h]: the per-span partials summed over b and the spans in a fixed order.
 __global__ __launch_bounds__(256) void k_bwd_reduce(BwdArgs a) {
-    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (h >= a.f.H) return;
+    // one wave per head: lane l sums spans l, l + 64, ... of every batch row in
+    // order, then a butterfly over the 64 lanes adds the lane sums, the same order
+    // on every run (one thread per head, summing all its partials in a row, took
+    // 0.040 ms at B 8, T 2048, H 48: 256 dependent loads a head)
+    const int64_t h = (int64_t)blockIdx.x * 4 + wave_id();
+    if (h >= a.f.H) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
     const int64_t nsp = dz_spans(a.f.nC, a.f.C);
     double sr = 0.0, si = 0.0, sd = 0.0;
     for (int64_t b = 0; b < a.f.B; ++b)
-        for (int64_t sp = 0; sp < nsp; ++sp) {
+        for (int64_t sp = lane; sp < nsp; sp += 64) {
             const int64_t u = (b * a.f.H + h) * nsp + sp;
             sr += a.pa[3 * u];
             si += a.pa[3 * u + 1];
             sd += a.pa[3 * u + 2];
         }
-    a.da_re[h] = (float)sr;
-    a.da_im[h] = (float)si;
-    if (a.dd != nullptr) a.dd[h] = (float)sd;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        sr += __shfl_xor(sr, off, 64);
+        si += __shfl_xor(si, off, 64);
+        sd += __shfl_xor(sd, off, 64);
+    }
+    if (lane == 0) {
+        a.da_re[h] = (float)sr;
+        a.da_im[h] = (float)si;
+        if (a.dd != nullptr) a.dd[h] = (float)sd;
+    }
 }
 
 template <int C, int N, int PART>
@@ -1336,7 +1349,7 @@ hipError_t launch_bwd_dz(const BwdArgs& a, bool with_zbound, hipStream_t s) {
     hipLaunchKernelGGL(k_bwd_dz, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((a.f.H + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)((a.f.H + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
