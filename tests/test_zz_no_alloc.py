@@ -47,6 +47,29 @@ def test_noalloc_matches_forward_on_two_calls():
         assert ey <= TOL and eh <= TOL
 
 
+def test_noalloc_bf16_two_stream_split():
+    """bf16 inputs with more sequences than CUs (at most twice as many): the
+    forward runs part of its work on the library's second stream, set up once on
+    the first such call (possibly this one), and the no-alloc entry point gives
+    cssd_forward's result bit for bit, on two calls in a row."""
+    import torch
+    import complex_valued_state_amd as cssd
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for rep, (T, H) in enumerate(((100, cus + 9), (70, 2 * cus))):
+        B, D, N, C = 1, 64, 64, 64
+        assert cssd.cssd_forward_workspace_size(B, T, H, D, N, C) <= cssd.CSSD_NOALLOC_SCRATCH_BYTES
+        inp = wl.random_forward(511 + rep, B, T, H, D, N, C, with_h0=True, in_dtype="bf16")
+        d = dev_inputs(inp)
+        log(f"  noalloc bf16 B{B} T{T} H{H} ({B * H} sequences, {cus} CUs)")
+        out = [torch.full((B, T, H, D), float("nan"), device="cuda:0") for _ in range(2)] + \
+              [torch.full((B, H, N, D), float("nan"), device="cuda:0") for _ in range(2)]
+        cssd.cssd_forward_noalloc(*_ins(d), chunk=C, out=tuple(out))
+        ref = cssd.cssd_forward(*_ins(d), chunk=C)
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(out, ref)):
+            assert torch.equal(a, b), (rep, k)
+
+
 def test_noalloc_refuses_a_problem_too_large_for_its_array():
     import torch
     import complex_valued_state_amd as cssd
