@@ -6,10 +6,12 @@
 // in one pass over the key blocks with fp32 accumulation on the matrix cores.
 //
 // Both contractions are dense, so both run on v_mfma_f32_16x16x4_f32:
-//  * the overlap, as real products over the 2D features [re | im]: with
+//  * the overlap in Gauss form, three real products over the D features: with
 //    q~ = q / sqrt(D tau) (which folds the page's 1/(D tau) into the query),
-//      Re <q~|k> = [kr | ki] . [qr | qi],   Im <q~|k> = -[ki | kr] . [-qr | qi],
-//    so the imaginary part reuses the real part's key registers, halves swapped;
+//      P1 = kr . qr,  P2 = ki . qi,  P3 = (kr - ki) . (qr + qi),
+//      Re <q~|k> = P1 + P2,   -Im <q~|k> = P3 - P1 + P2,
+//    three quarters of the matrix work of the four products (kr - ki is formed
+//    from the staged key operands, qr + qi once per query block);
 //  * the weighted sum, S . [vr | vi], with the row sums of S formed alongside.
 // Each wave computes the transposed score tile (keys x queries): the matrix
 // core leaves key 4g + r of query q in register r of lane q + 16g, which is
@@ -78,7 +80,8 @@ __global__ __launch_bounds__(256) void k_born(BornArgs a) {
         const int64_t qb = which == 0 ? pair : a.nqb - 1 - pair;
         // this lane's query row (as the B operand) and its scaled features
         const int64_t qrow = qb * kBornBlock + 16 * w + lr;
-        float bre[NS], bim[NS];
+        // B operands: the scaled query features [qr | qi] and the sums qr + qi
+        float bre[NS], bsum[Q4];
         {
             float4 qr[Q4 / 4], qi[Q4 / 4];
             float scale = 0.f;
@@ -101,8 +104,7 @@ __global__ __launch_bounds__(256) void k_born(BornArgs a) {
                 const float i = pick4(qi[s / 4], s % 4) * scale;
                 bre[s] = r;
                 bre[s + Q4] = i;
-                bim[s] = -r;
-                bim[s + Q4] = i;
+                bsum[s] = r + i;
             }
         }
         floatx4 o[NCT];
@@ -153,17 +155,23 @@ __global__ __launch_bounds__(256) void k_born(BornArgs a) {
                     are[Q4 + 4 * c + 0] = y.x; are[Q4 + 4 * c + 1] = y.y;
                     are[Q4 + 4 * c + 2] = y.z; are[Q4 + 4 * c + 3] = y.w;
                 }
-                floatx4 sre = {0.f, 0.f, 0.f, 0.f}, sim = {0.f, 0.f, 0.f, 0.f};
+                // the overlap in Gauss form, three products over the D features:
+                // P1 = kr . qr, P2 = ki . qi, P3 = (kr - ki) . (qr + qi); then
+                // Re = P1 + P2 and P3 - P1 + P2 = -Im (the sign drops out of |.|^2)
+                floatx4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+                floatx4 p3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    sre = __builtin_amdgcn_mfma_f32_16x16x4f32(are[s], bre[s], sre, 0, 0, 0);
-                    sim = __builtin_amdgcn_mfma_f32_16x16x4f32(are[(s + Q4) % NS], bim[s], sim, 0, 0, 0);
+                for (int s = 0; s < Q4; ++s) {
+                    p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(are[s], bre[s], p1, 0, 0, 0);
+                    p2 = __builtin_amdgcn_mfma_f32_16x16x4f32(are[Q4 + s], bre[Q4 + s], p2, 0, 0, 0);
+                    p3 = __builtin_amdgcn_mfma_f32_16x16x4f32(are[s] - are[Q4 + s], bsum[s], p3, 0, 0, 0);
                 }
                 // scores of query lr, keys 16t + 4lg + r
                 float sc[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = sre[r] * sre[r] + sim[r] * sim[r];
+                    const float re = p1[r] + p2[r], im = p3[r] - p1[r] + p2[r];
+                    float v = re * re + im * im;
                     if (diag && 16 * t + 4 * lg + r > 16 * w + lr) v = 0.f;
                     sc[r] = v;
                     lsum += v;
